@@ -1,0 +1,304 @@
+"""Plain CPU reference for the MoE expert feed-forward layer (test infrastructure only).
+
+Source: "Efficient MoE Training for Biological Foundation Models"
+  * Challenge 1 (Fragmented expert kernels): the Hugging Face baseline walks the
+    experts in a Python loop; for each expert it finds the (token, slot) pairs
+    routed to it, gathers those hidden_states rows, runs the expert, multiplies
+    by routing_weights[token, slot] and index-adds the result into
+    final_hidden_states. GroupedLinear takes per-expert token counts
+    (split_sizes) and the experts' gate_up weights are [2*intermediate, hidden].
+  * Challenge 3: ScaledSwiGLU multiplies the routing probability into the
+    SwiGLU output, and the grouped MLP is GroupedLinear(gate_up) ->
+    ScaledSwiGLU -> GroupedLinear(down), with a matching backward.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes):
+  * routing: softmax over the experts, keep the k largest, renormalise the k
+    kept probabilities to sum to 1; selection compares the logits, larger
+    first, lower expert index first on equal logits;
+  * rows of an expert are ordered by ascending token (the order the loop
+    visits them when the routing mask is laid out [token, slot]);
+  * gate is rows [0, I) of the gate_up weight, up is rows [I, 2I);
+    SwiGLU(g, u) = silu(g) * u with silu(g) = g / (1 + exp(-g)); no biases;
+  * the probability is applied once: after the expert here (as the loop does),
+    inside ScaledSwiGLU in the grouped form; both are equal in exact arithmetic.
+
+All arithmetic is float64; inputs are upcast exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .mxfp8 import mxfp8_qdq
+
+__all__ = [
+    "route_topk", "permute", "silu", "expert_ffn", "moe_ffn_forward",
+    "grouped_mlp_forward", "grouped_mlp_forward_mxfp8", "unpermute_combine",
+    "grouped_mlp_backward", "moe_ffn_backward", "gather_rows",
+]
+
+f64 = np.float64
+
+
+def silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def _sigmoid(g):
+    return 1.0 / (1.0 + np.exp(-g))
+
+
+# ---------------------------------------------------------------------------
+# Router gating: routing_weights [T, k] and the chosen experts [T, k]
+# ---------------------------------------------------------------------------
+
+def route_topk(logits, k: int, renormalize: bool = True):
+    """Top-k router gating.
+
+    Returns (topk_idx int32 [T, k], topk_prob float64 [T, k]). Slot j holds the
+    j-th largest logit (ties: lower expert index first). With ``renormalize``
+    the k probabilities are the softmax restricted to the chosen experts;
+    otherwise they are the full softmax's entries for those experts.
+    """
+    l = np.asarray(logits, dtype=f64)
+    T, E = l.shape
+    assert 1 <= k <= E
+    # a stable sort of the negated logits keeps equal logits in index order
+    order = np.argsort(-l, axis=1, kind="stable")[:, :k]
+    sel = np.take_along_axis(l, order, axis=1)
+    m = sel[:, :1]                                    # the largest logit of the row
+    num = np.exp(sel - m)
+    if renormalize:
+        den = num.sum(axis=1, keepdims=True)
+    else:
+        den = np.exp(l - m).sum(axis=1, keepdims=True)
+    return order.astype(np.int32), num / den
+
+
+# ---------------------------------------------------------------------------
+# Token permutation into per-expert groups (split_sizes)
+# ---------------------------------------------------------------------------
+
+def permute(topk_idx, E: int):
+    """Group the T*k (token, slot) pairs by expert.
+
+    Expert by expert, as the baseline loop does, the pairs routed to expert e
+    are listed in ascending token order; concatenating the lists gives the
+    permuted rows. Returns dict with
+      split_sizes [E], offsets [E+1], row_id_map [T*k] ((t, j) -> row),
+      src_token [T*k] (row -> t), src_slot [T*k] (row -> j).
+    """
+    idx = np.asarray(topk_idx)
+    T, k = idx.shape
+    split_sizes = np.zeros(E, np.int64)
+    row_id_map = np.full(T * k, -1, np.int64)
+    src_token = np.empty(T * k, np.int64)
+    src_slot = np.empty(T * k, np.int64)
+    row = 0
+    for e in range(E):
+        top_x, slot = np.nonzero(idx == e)          # row-major: ascending token
+        n = top_x.size
+        split_sizes[e] = n
+        rows = np.arange(row, row + n)
+        row_id_map[top_x * k + slot] = rows
+        src_token[rows] = top_x
+        src_slot[rows] = slot
+        row += n
+    offsets = np.concatenate([[0], np.cumsum(split_sizes)])
+    return dict(split_sizes=split_sizes, offsets=offsets, row_id_map=row_id_map,
+                src_token=src_token, src_slot=src_slot)
+
+
+def gather_rows(x, src_token):
+    """x_perm[r] = x[src_token[r]]."""
+    return np.asarray(x)[np.asarray(src_token)]
+
+
+# ---------------------------------------------------------------------------
+# The expert MLP and the per-expert loop
+# ---------------------------------------------------------------------------
+
+def expert_ffn(X, w_gate_up, w_down):
+    """One expert: Z = X W1^T, A = silu(Z[:, :I]) * Z[:, I:], Y = A W2^T.
+    Returns (Y, Z, A), all float64."""
+    X = np.asarray(X, dtype=f64)
+    W1 = np.asarray(w_gate_up, dtype=f64)
+    W2 = np.asarray(w_down, dtype=f64)
+    I = W1.shape[0] // 2
+    Z = X @ W1.T
+    A = silu(Z[:, :I]) * Z[:, I:]
+    return A @ W2.T, Z, A
+
+
+def moe_ffn_forward(hidden_states, w_gate_up, w_down, topk_idx, routing_weights):
+    """final_hidden_states [T, H] by the per-expert loop (float64).
+
+    w_gate_up [E, 2I, H], w_down [E, H, I]."""
+    x = np.asarray(hidden_states, dtype=f64)
+    idx = np.asarray(topk_idx)
+    p = np.asarray(routing_weights, dtype=f64)
+    T, H = x.shape
+    E = w_gate_up.shape[0]
+    final_hidden_states = np.zeros((T, H), f64)
+    for e in range(E):
+        top_x, slot = np.nonzero(idx == e)
+        if top_x.size == 0:
+            continue
+        Y, _, _ = expert_ffn(x[top_x], w_gate_up[e], w_down[e])
+        np.add.at(final_hidden_states, top_x, Y * p[top_x, slot][:, None])
+    return final_hidden_states
+
+
+def grouped_mlp_forward(x_perm, w_gate_up, w_down, offsets, prob_perm):
+    """The grouped form on permuted rows: for expert e, rows
+    [offsets[e], offsets[e+1]) go through gate_up, ScaledSwiGLU (probability
+    folded in) and down.
+
+    Returns (y_perm [R, H], z [R, 2I], h [R, I]) in float64, where
+    h = silu(gate) * up * prob and y_perm = h W2^T.
+    """
+    x = np.asarray(x_perm, dtype=f64)
+    p = np.asarray(prob_perm, dtype=f64)
+    off = np.asarray(offsets, dtype=np.int64)
+    E, twoI, H = w_gate_up.shape
+    I = twoI // 2
+    R = x.shape[0]
+    y = np.zeros((R, H), f64)
+    z = np.zeros((R, twoI), f64)
+    h = np.zeros((R, I), f64)
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        W1 = np.asarray(w_gate_up[e], dtype=f64)
+        W2 = np.asarray(w_down[e], dtype=f64)
+        Z = x[a:b] @ W1.T
+        Hs = silu(Z[:, :I]) * Z[:, I:] * p[a:b, None]
+        y[a:b] = Hs @ W2.T
+        z[a:b] = Z
+        h[a:b] = Hs
+    return y, z, h
+
+
+def grouped_mlp_forward_mxfp8(x_perm, w_gate_up, w_down, offsets, prob_perm):
+    """Grouped MLP with the naive quantise -> dequantise steps of Challenge 3
+    around both GEMMs: x (along H), W1 (along H), h (along I) and W2 (along I)
+    each pass through MXFP8 before their GEMM; gate_up accumulators stay
+    unrounded. Returns (y_perm, h_before_quantisation) in float64."""
+    x = mxfp8_qdq(np.asarray(x_perm, dtype=f64)) if len(x_perm) else np.zeros((0, w_gate_up.shape[2]))
+    p = np.asarray(prob_perm, dtype=f64)
+    off = np.asarray(offsets, dtype=np.int64)
+    E, twoI, H = w_gate_up.shape
+    I = twoI // 2
+    R = x.shape[0]
+    y = np.zeros((R, H), f64)
+    h = np.zeros((R, I), f64)
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        W1 = mxfp8_qdq(np.asarray(w_gate_up[e], dtype=f64))
+        W2 = mxfp8_qdq(np.asarray(w_down[e], dtype=f64))
+        Z = x[a:b] @ W1.T
+        Hs = silu(Z[:, :I]) * Z[:, I:] * p[a:b, None]
+        h[a:b] = Hs
+        y[a:b] = mxfp8_qdq(Hs) @ W2.T
+    return y, h
+
+
+def unpermute_combine(y_perm, row_id_map, T: int, k: int, weights=None):
+    """out[t] = sum over slots j (ascending) of w[t, j] * y_perm[row_id_map[t*k + j]];
+    w = 1 when the probability was already folded in (weights=None)."""
+    y = np.asarray(y_perm, dtype=f64)
+    rmap = np.asarray(row_id_map).reshape(T, k)
+    out = np.zeros((T, y.shape[1]), f64)
+    for j in range(k):
+        contrib = y[rmap[:, j]]
+        if weights is not None:
+            contrib = contrib * np.asarray(weights, dtype=f64).reshape(T, k)[:, j:j + 1]
+        out += contrib
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Backward (the "matching fused backward" of Challenge 3, as explicit formulas)
+# ---------------------------------------------------------------------------
+
+def grouped_mlp_backward(dy_perm, x_perm, w_gate_up, w_down, offsets, prob_perm):
+    """Gradients of y_perm = (silu(G) * U * p) W2^T with (G, U) = x W1^T, per expert.
+
+    dy_perm [R, H] is the upstream gradient on the permuted rows. Returns dict
+    dx_perm [R, H], dw_gate_up [E, 2I, H], dw_down [E, H, I], dprob_perm [R].
+    Experts with no rows get exactly zero weight gradients.
+    """
+    dy = np.asarray(dy_perm, dtype=f64)
+    x = np.asarray(x_perm, dtype=f64)
+    p = np.asarray(prob_perm, dtype=f64)
+    off = np.asarray(offsets, dtype=np.int64)
+    E, twoI, H = w_gate_up.shape
+    I = twoI // 2
+    R = x.shape[0]
+    dx = np.zeros((R, H), f64)
+    dw1 = np.zeros((E, twoI, H), f64)
+    dw2 = np.zeros((E, H, I), f64)
+    dprob = np.zeros(R, f64)
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        W1 = np.asarray(w_gate_up[e], dtype=f64)
+        W2 = np.asarray(w_down[e], dtype=f64)
+        X, dY, pe = x[a:b], dy[a:b], p[a:b, None]
+        Z = X @ W1.T
+        G, U = Z[:, :I], Z[:, I:]
+        sg = _sigmoid(G)
+        A = G * sg * U                      # SwiGLU before the probability
+        Hs = A * pe
+        dw2[e] = dY.T @ Hs
+        dHs = dY @ W2
+        dprob[a:b] = (dHs * A).sum(axis=1)
+        dA = dHs * pe
+        dG = dA * U * sg * (1.0 + G * (1.0 - sg))
+        dU = dA * G * sg
+        dZ = np.concatenate([dG, dU], axis=1)
+        dx[a:b] = dZ @ W1
+        dw1[e] = dZ.T @ X
+    return dict(dx_perm=dx, dw_gate_up=dw1, dw_down=dw2, dprob_perm=dprob)
+
+
+def moe_ffn_backward(hidden_states, w_gate_up, w_down, topk_idx, routing_weights, d_out):
+    """Gradients of moe_ffn_forward's output against d_out, walking the same
+    per-expert loop backwards. Returns dict dx [T, H], dw_gate_up, dw_down,
+    drouting_weights [T, k] (gradient w.r.t. the routing weights themselves)."""
+    x = np.asarray(hidden_states, dtype=f64)
+    idx = np.asarray(topk_idx)
+    p = np.asarray(routing_weights, dtype=f64)
+    g = np.asarray(d_out, dtype=f64)
+    T, H = x.shape
+    E, twoI, _ = w_gate_up.shape
+    I = twoI // 2
+    dx = np.zeros((T, H), f64)
+    dw1 = np.zeros((E, twoI, H), f64)
+    dw2 = np.zeros((E, H, I), f64)
+    dp = np.zeros_like(p)
+    for e in range(E):
+        top_x, slot = np.nonzero(idx == e)
+        if top_x.size == 0:
+            continue
+        W1 = np.asarray(w_gate_up[e], dtype=f64)
+        W2 = np.asarray(w_down[e], dtype=f64)
+        Y, Z, A = expert_ffn(x[top_x], W1, W2)
+        pw = p[top_x, slot][:, None]
+        gY = g[top_x]                                # index_add_ scatters, so its grad gathers
+        dp[top_x, slot] = (gY * Y).sum(axis=1)
+        dY = gY * pw
+        dw2[e] = dY.T @ A
+        dA = dY @ W2
+        G, U = Z[:, :I], Z[:, I:]
+        sg = _sigmoid(G)
+        dG = dA * U * sg * (1.0 + G * (1.0 - sg))
+        dU = dA * G * sg
+        dZ = np.concatenate([dG, dU], axis=1)
+        np.add.at(dx, top_x, dZ @ W1)
+        dw1[e] = dZ.T @ x[top_x]
+    return dict(dx=dx, dw_gate_up=dw1, dw_down=dw2, drouting_weights=dp)

@@ -1,0 +1,152 @@
+"""Pins for the oracle's MXFP8 quantiser (CPU only): fixed E4M3 code points,
+a brute-force nearest-codebook search, the scale rule's bounds, scale
+equivariance, exact round trips and idempotence."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from moe_inputs import bf16_bits_to_f32, f32_to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _codebook():
+    """All finite E4M3 values from the bit fields: sign, exponent (bias 7), mantissa."""
+    vals = {}
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            continue
+        mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+        vals[c] = -mag if s else mag
+    return vals
+
+
+def test_e4m3_fixed_points():
+    g = json.load(open(os.path.join(GOLDEN, "e4m3_codes.json")))
+    for case in g["codes"]:
+        assert int(oracle.e4m3_encode(case["value"])) == case["code"], case
+        assert float(oracle.e4m3_decode(case["code"])) == case["value"]
+    for c in g["nan_codes"]:
+        assert np.isnan(oracle.e4m3_decode(c))
+
+
+def test_e4m3_decode_matches_codebook():
+    cb = _codebook()
+    codes = np.array(sorted(cb), np.uint8)
+    np.testing.assert_array_equal(oracle.e4m3_decode(codes), [cb[int(c)] for c in codes])
+
+
+def test_e4m3_encode_brute_force_nearest_ties_to_even():
+    cb = _codebook()
+    pos = sorted((v, c) for c, v in cb.items() if c < 128)      # non-negative codes
+    grid = set(np.linspace(0, 448, 20001).tolist())
+    for (a, _), (b, _) in zip(pos, pos[1:]):
+        grid.update([(a + b) / 2, a, b, np.nextafter((a + b) / 2, 0), np.nextafter((a + b) / 2, 1e9)])
+    grid = np.array(sorted(grid))
+    vals = np.array([v for v, _ in pos])
+    codes = np.array([c for _, c in pos])
+    expect = []
+    for x in grid:
+        d = np.abs(vals - x)
+        best = np.flatnonzero(d == d.min())
+        if len(best) > 1:                       # a tie: the even mantissa wins
+            best = [b for b in best if codes[b] % 2 == 0]
+        expect.append(codes[best[0]])
+    got = oracle.e4m3_encode(grid)
+    np.testing.assert_array_equal(got, expect)
+    np.testing.assert_array_equal(oracle.e4m3_encode(-grid[1:]), np.array(expect[1:]) | 0x80)
+
+
+def test_e8m0_scale_brute_force():
+    rng = np.random.default_rng(0)
+    amax = np.concatenate([np.exp2(rng.uniform(-140, 125, 3000)),
+                           448 * np.exp2(np.arange(-20, 20, dtype=np.float64)),
+                           np.nextafter(448 * np.exp2(np.arange(-5, 5.0)), np.inf)])
+    s = oracle.e8m0_scale_exponent(amax)
+    for a, si in zip(amax, s):
+        want = next(t for t in range(-127, 128) if a <= 448 * 2.0 ** t) if a <= 448 * 2.0 ** 127 else 127
+        assert si == want
+    assert oracle.e8m0_scale_exponent(0.0) == -127
+
+
+def _bf16_blocks(rows=64, cols=256, seed=0, spread=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    if spread:
+        x *= np.exp2(rng.integers(-30, 30, (rows, cols // 32))).repeat(32, 1).astype(np.float32)
+    return bf16_bits_to_f32(f32_to_bf16_bits(x))
+
+
+def test_quantize_scale_bounds_and_zero_block():
+    x = _bf16_blocks()
+    x[3, 32:64] = 0.0
+    codes, scales = oracle.mxfp8_quantize(x)
+    amax = np.abs(x.reshape(64, 8, 32)).max(2)
+    scale = np.exp2(scales.astype(np.float64) - 127)
+    nz = amax > 0
+    assert (amax[nz] / scale[nz] <= 448).all()
+    assert (amax[nz] / scale[nz] > 224).all()            # smallest such power of two
+    assert scales[3, 1] == 0 and not codes[3, 32:64].any()
+    # no code is NaN and the largest element of each block lands in the top binade
+    assert not np.isnan(oracle.e4m3_decode(codes)).any()
+
+
+def test_quantize_equivariance_roundtrip_idempotence():
+    x = _bf16_blocks(seed=1)
+    codes, scales = oracle.mxfp8_quantize(x)
+    for j in (-7, 1, 12):
+        c2, s2 = oracle.mxfp8_quantize(x * 2.0 ** j)
+        np.testing.assert_array_equal(c2, codes)
+        np.testing.assert_array_equal(s2.astype(int), scales.astype(int) + j)
+    dq = oracle.mxfp8_dequantize(codes, scales)
+    # already representable: the values survive a second pass unchanged; the codes
+    # too, except where the block maximum rounded down to 224 * scale, which moves
+    # the block one binade down (same values, scale one smaller)
+    c3, s3 = oracle.mxfp8_quantize(dq)
+    np.testing.assert_array_equal(oracle.mxfp8_dequantize(c3, s3), dq)
+    amax_dq = np.abs(dq.reshape(dq.shape[0], -1, 32)).max(2)
+    same = amax_dq > 224 * np.exp2(scales.astype(np.float64) - 127)
+    np.testing.assert_array_equal(s3[same], scales[same])
+    np.testing.assert_array_equal(s3[~same].astype(int), scales[~same].astype(int) - 1)
+    np.testing.assert_array_equal(c3.reshape(dq.shape[0], -1, 32)[same], codes.reshape(dq.shape[0], -1, 32)[same])
+    np.testing.assert_array_equal(oracle.mxfp8_qdq(dq), dq)
+    # relative error of a normal-range element is at most half an E4M3 ulp (2^-4)
+    big = np.abs(dq) >= np.exp2(scales.astype(float) - 127 - 6).repeat(32, 1)
+    rel = np.abs(dq - x)[big] / np.abs(x)[big]
+    assert rel.max() <= 2.0 ** -4 + 1e-12
+
+
+def test_quantize_commutes_with_row_permutation():
+    x = _bf16_blocks(seed=2)
+    perm = np.random.default_rng(3).permutation(x.shape[0])
+    c, s = oracle.mxfp8_quantize(x)
+    cp, sp = oracle.mxfp8_quantize(x[perm])
+    np.testing.assert_array_equal(cp, c[perm])
+    np.testing.assert_array_equal(sp, s[perm])
+
+
+def test_mxfp8_mlp_equals_exact_mlp_on_representable_inputs():
+    """With x, W1, W2 already MX-representable only h is rounded: the MXFP8
+    reference then equals the exact MLP run on the rounded h."""
+    from moe_inputs import WORKLOADS, make_inputs, scaled
+    inp = make_inputs(scaled(WORKLOADS["tiny"], T=40, H=64, I=64, E=4, k=2, seed=3, dtype="bf16"))
+    x = oracle.mxfp8_qdq(inp.x)
+    w1 = np.stack([oracle.mxfp8_qdq(w) for w in inp.w1])
+    w2 = np.stack([oracle.mxfp8_qdq(w) for w in inp.w2])
+    idx, p = oracle.route_topk(inp.logits, 2)
+    m = oracle.permute(idx, 4)
+    xp = oracle.gather_rows(x, m["src_token"])
+    pp = p.ravel()[m["src_token"] * 2 + m["src_slot"]]
+    y8, h = oracle.grouped_mlp_forward_mxfp8(xp, w1, w2, m["offsets"], pp)
+    _, _, h_exact = oracle.grouped_mlp_forward(xp, w1, w2, m["offsets"], pp)
+    np.testing.assert_allclose(h, h_exact, rtol=1e-13, atol=1e-16)
+    y_ref = np.zeros_like(y8)
+    hq = oracle.mxfp8_qdq(h)
+    for e in range(4):
+        a, b = m["offsets"][e], m["offsets"][e + 1]
+        y_ref[a:b] = hq[a:b] @ w2[e].T
+    np.testing.assert_allclose(y8, y_ref, rtol=1e-12, atol=1e-14)
