@@ -1,0 +1,211 @@
+"""MoE expert feed-forward hot path on AMD MI355X (gfx950): Python binding.
+
+Thin argument marshalling over the C ABI of include/moe.h: every step runs in
+the HIP kernels of libmoe.so; torch only provides device memory and the
+current stream. The functions carry the C entry points' names.
+
+Path (per "Efficient MoE Training for Biological Foundation Models",
+Challenges 1-3): moe_route_topk -> moe_permute -> moe_grouped_mlp_fwd
+(gate_up grouped GEMM + ScaledSwiGLU, down grouped GEMM) ->
+moe_unpermute_combine; moe_grouped_mlp_bwd for the backward; mxfp8_quantize
+for MXFP8 block quantisation.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import MOE_BF16, MOE_F32, MOE_MXFP8, MlpDesc, MoeError, check, lib, ptr_table
+
+__all__ = [
+    "moe_route_topk", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
+    "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "workspace_size", "MoeError", "lib",
+    "MOE_F32", "MOE_BF16", "MOE_MXFP8",
+]
+
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.uint8: MOE_MXFP8}
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def workspace_size(op, desc=None, R=0, T=0, E=1, k=1):
+    n = ctypes.c_size_t(0)
+    check("moe_workspace_size", lib().moe_workspace_size(op, ctypes.byref(desc) if desc is not None else None,
+                                                         R, T, E, k, ctypes.byref(n)))
+    return n.value
+
+
+def moe_route_topk(logits: torch.Tensor, k: int, renormalize: bool = True):
+    """logits [T, E] float32 -> (topk_idx int32 [T, k], topk_prob float32 [T, k])."""
+    _need_cuda(logits)
+    T, E = logits.shape
+    idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    prob = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    check("moe_route_topk", lib().moe_route_topk(_p(logits), T, E, k, int(renormalize), _p(idx), _p(prob),
+                                                 _stream(logits.device)))
+    return idx, prob
+
+
+def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torch.Tensor | None, E: int,
+                x_scale: torch.Tensor | None = None, row_id_map: torch.Tensor | None = None):
+    """Group the (token, slot) pairs by expert.
+
+    Returns a dict with x_perm [R, H], x_perm_scale (MXFP8 only), prob_perm [R],
+    split_sizes [E], offsets [E+1], row_id_map [T*k], src_token [R].
+    With ``row_id_map`` given, only x is gathered with that map (topk_idx gives k).
+    """
+    _need_cuda(x, topk_idx, topk_prob, x_scale, row_id_map)
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    R = T * k
+    dt = _DT[x.dtype]
+    dev = x.device
+    x_perm = torch.empty((R, H), dtype=x.dtype, device=dev)
+    xps = torch.empty((R, H // 32), dtype=torch.uint8, device=dev) if dt == MOE_MXFP8 else None
+    if row_id_map is not None:
+        check("moe_permute", lib().moe_permute(_p(x), _p(x_scale), dt, T, H, E, k, None, None, 1, _p(x_perm),
+                                               _p(xps), None, None, None, _p(row_id_map), None, None, 0,
+                                               _stream(dev)))
+        return dict(x_perm=x_perm, x_perm_scale=xps)
+    prob_perm = torch.empty(R, dtype=torch.float32, device=dev) if topk_prob is not None else None
+    split = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    rmap = torch.empty(R, dtype=torch.int32, device=dev)
+    src = torch.empty(R, dtype=torch.int32, device=dev)
+    ws = _workspace(workspace_size(_lib.MOE_OP_PERMUTE, None, 0, T, E, k), dev)
+    check("moe_permute", lib().moe_permute(_p(x), _p(x_scale), dt, T, H, E, k, _p(topk_idx), _p(topk_prob), 0,
+                                           _p(x_perm), _p(xps), _p(prob_perm), _p(split), _p(offsets), _p(rmap),
+                                           _p(src), _p(ws), ws.numel(), _stream(dev)))
+    return dict(x_perm=x_perm, x_perm_scale=xps, prob_perm=prob_perm, split_sizes=split, offsets=offsets,
+                row_id_map=rmap, src_token=src)
+
+
+def moe_unpermute_combine(y_perm: torch.Tensor, row_id_map: torch.Tensor, T: int, k: int,
+                          weights: torch.Tensor | None = None):
+    """out[t] = sum_j w[t, j] * y_perm[row_id_map[t*k + j]] (w = 1 without weights)."""
+    _need_cuda(y_perm, row_id_map, weights)
+    H = y_perm.shape[1]
+    out = torch.empty((T, H), dtype=y_perm.dtype, device=y_perm.device)
+    check("moe_unpermute_combine", lib().moe_unpermute_combine(_p(y_perm), _DT[y_perm.dtype], _p(row_id_map),
+                                                               _p(weights), T, H, k, _p(out),
+                                                               _stream(y_perm.device)))
+    return out
+
+
+def mxfp8_quantize(x: torch.Tensor):
+    """bf16 [rows, cols] -> (E4M3 codes uint8 [rows, cols], E8M0 scales uint8 [rows, cols/32])."""
+    _need_cuda(x)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("mxfp8_quantize takes bfloat16")
+    x2 = x.reshape(-1, x.shape[-1])
+    rows, cols = x2.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    check("mxfp8_quantize", lib().mxfp8_quantize(_p(x2), rows, cols, _p(codes), _p(scales), _stream(x.device)))
+    return codes.reshape(x.shape), scales.reshape(*x.shape[:-1], cols // 32)
+
+
+def _experts(w):
+    """A [E, ...] tensor or a list of per-expert tensors -> list of per-expert tensors."""
+    if isinstance(w, torch.Tensor):
+        return [w[e] for e in range(w.shape[0])]
+    return list(w)
+
+
+_COMPUTE = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
+
+
+def moe_grouped_mlp_fwd(x_perm: torch.Tensor, w_gate_up, w_down, offsets: torch.Tensor, prob_perm: torch.Tensor,
+                        compute: str = "bf16", save_for_bwd: bool = False, x_perm_scale=None,
+                        w_gate_up_scale=None, w_down_scale=None, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None):
+    """Grouped MLP forward on permuted rows. Returns y_perm, or (y_perm, z, h) with save_for_bwd.
+
+    compute: "f32", "bf16" or "mxfp8". For mxfp8, x_perm may be bf16 (quantised in
+    the call) or uint8 codes with x_perm_scale; weights may be bf16 master weights
+    (quantised in the call) or uint8 codes with per-expert scale tensors.
+    """
+    w1 = _experts(w_gate_up)
+    w2 = _experts(w_down)
+    E = len(w1)
+    twoI, H = w1[0].shape
+    I = twoI // 2
+    R = x_perm.shape[0]
+    dev = x_perm.device
+    _need_cuda(x_perm, offsets, prob_perm, x_perm_scale, *w1, *w2)
+    c = _COMPUTE[compute]
+    act = _DT[x_perm.dtype]
+    wt = _DT[w1[0].dtype]
+    desc = MlpDesc(E, H, I, c, act, wt, int(save_for_bwd))
+    out_dtype = torch.float32 if c == MOE_F32 else torch.bfloat16
+    y = out if out is not None else torch.empty((R, H), dtype=out_dtype, device=dev)
+    z = torch.empty((R, 2 * I), dtype=out_dtype, device=dev) if save_for_bwd else None
+    h = torch.empty((R, I), dtype=out_dtype, device=dev) if save_for_bwd else None
+    need = workspace_size(_lib.MOE_OP_MLP_FWD, desc, R)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    t1, k1 = ptr_table([t.data_ptr() for t in w1])
+    t2, k2 = ptr_table([t.data_ptr() for t in w2])
+    s1 = s2 = None
+    keep = []
+    if w_gate_up_scale is not None:
+        s1, a = ptr_table([t.data_ptr() for t in _experts(w_gate_up_scale)])
+        keep.append(a)
+        s2, a = ptr_table([t.data_ptr() for t in _experts(w_down_scale)])
+        keep.append(a)
+    check("moe_grouped_mlp_fwd", lib().moe_grouped_mlp_fwd(
+        ctypes.byref(desc), R, _p(x_perm), _p(x_perm_scale), t1, t2, s1, s2, _p(offsets), _p(prob_perm), _p(y),
+        _p(z), _p(h), _p(ws), ws.numel(), _stream(dev)))
+    del k1, k2, keep
+    return (y, z, h) if save_for_bwd else y
+
+
+def moe_grouped_mlp_bwd(dy_perm, x_perm, z, h, prob_perm, w_gate_up, w_down, offsets, compute: str = "bf16",
+                        dw_gate_up=None, dw_down=None, workspace: torch.Tensor | None = None):
+    """Grouped MLP backward. Returns (dx_perm, dw_gate_up [E, 2I, H], dw_down [E, H, I], dprob_perm [R])."""
+    w1 = _experts(w_gate_up)
+    w2 = _experts(w_down)
+    E = len(w1)
+    twoI, H = w1[0].shape
+    I = twoI // 2
+    R = x_perm.shape[0]
+    dev = x_perm.device
+    _need_cuda(dy_perm, x_perm, z, h, prob_perm, offsets, *w1, *w2)
+    c = _COMPUTE[compute]
+    dt = torch.float32 if c == MOE_F32 else torch.bfloat16
+    desc = MlpDesc(E, H, I, c, _DT[x_perm.dtype], _DT[w1[0].dtype], 1)
+    dx = torch.empty((R, H), dtype=dt, device=dev)
+    dw1 = dw_gate_up if dw_gate_up is not None else torch.empty((E, twoI, H), dtype=dt, device=dev)
+    dw2 = dw_down if dw_down is not None else torch.empty((E, H, I), dtype=dt, device=dev)
+    dprob = torch.empty(R, dtype=torch.float32, device=dev)
+    need = workspace_size(_lib.MOE_OP_MLP_BWD, desc, R)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    t1, k1 = ptr_table([t.data_ptr() for t in w1])
+    t2, k2 = ptr_table([t.data_ptr() for t in w2])
+    d1, k3 = ptr_table([t.data_ptr() for t in _experts(dw1)])
+    d2, k4 = ptr_table([t.data_ptr() for t in _experts(dw2)])
+    check("moe_grouped_mlp_bwd", lib().moe_grouped_mlp_bwd(
+        ctypes.byref(desc), R, _p(dy_perm), _p(x_perm), _p(z), _p(h), _p(prob_perm), t1, t2, _p(offsets), _p(dx),
+        d1, d2, _p(dprob), _p(ws), ws.numel(), _stream(dev)))
+    del k1, k2, k3, k4
+    return dx, dw1, dw2, dprob

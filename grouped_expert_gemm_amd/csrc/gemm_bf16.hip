@@ -1,0 +1,448 @@
+// Persistent grouped GEMM on bf16 MFMA (gfx950 v_mfma_f32_32x32x16_bf16), float32
+// accumulation, with the epilogues of the grouped MLP fused in.
+//
+// Source: GroupedLinear of "Efficient MoE Training for Biological Foundation Models",
+// Challenge 1 (one submission for all local experts, per-expert token counts), and
+// the fused GroupedLinear -> ScaledSwiGLU -> GroupedLinear path of Challenge 3 with
+// its matching backward. The pages' own fused kernel targets another GPU; this is a
+// design for CDNA4: 64-wide wavefronts, 160 KiB LDS, 8 XCDs with private L2.
+//
+// Computes C[m][n] = sum_k Q(m, k) * P(n, k) tile by tile:
+//   P (MFMA A operand) indexes the output column n, Q (MFMA B operand) the row m, so
+//   a lane of the 32x32 accumulator holds one row m and 4 consecutive columns n per
+//   4 registers: epilogue stores are 8-byte row-contiguous and the SwiGLU gate/up
+//   pair of a column sits in the same lane.
+// Grouping:
+//   GROUP_M: rows m are token rows; expert e owns rows [offsets[e], offsets[e+1]) and
+//            its own P (the expert's weight); K is fixed. Forward and data gradients.
+//   GROUP_K: the reduction runs over expert e's token rows (K = its row count, may be
+//            0); M and N are fixed and each expert writes its own C. Weight gradients.
+// Operand layouts: KCONTIG = rows of K-contiguous elements ([rows][K]); MNCONTIG =
+//   K is the row index and m/n is contiguous ([K][cols]); the loader transposes
+//   8x8 bf16 blocks in registers so LDS always holds [m or n][k].
+// Tiles: 256 x 256 x 64, 4 wavefronts (2 x 2), each 128 x 128 = 4 x 4 MFMA blocks
+//   held in 256 accumulator registers; 2 LDS stages of 64 KiB; one barrier per K
+//   step. LDS rows are 128 bytes (8 chunks of 16 bytes) and chunk c of row r lives
+//   at c ^ ((r ^ (r >> 3)) & 7), which keeps straight loads, transposed stores and
+//   MFMA fragment reads free of bank conflicts.
+// Scheduling: one workgroup per CU loops over tiles (persistent); tile ids are
+//   remapped so that each XCD (workgroup id mod 8) works on a contiguous run of
+//   tiles. Inside an expert, tiles run m-fastest, so a run covers a few weight
+//   panels and all of the expert's token panels, and concurrent runs share them
+//   through L2 and the Infinity Cache.
+#include "common.h"
+#include "gemm_bf16.h"
+#include "internal.h"
+
+namespace moe {
+namespace gemm {
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+__device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
+  return (uint32_t)(row * 128 + ((chunk ^ swz(row)) << 4));
+}
+
+// column offset of MFMA sub-tile s (0..3) of wavefront column wn inside the 256-wide
+// tile: sub-tiles 0,1 cover [wn*64, wn*64+64), sub-tiles 2,3 the same span + 128.
+__device__ __forceinline__ int sub_n(int s, int wn) { return (s >> 1) * 128 + wn * 64 + (s & 1) * 32; }
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// 8 rows (k) x 8 bf16 (mn) -> 8 vectors (mn) x 8 bf16 (k)
+__device__ __forceinline__ void transpose8(const uint4 in[8], uint4 out[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint4 a = in[2 * p], b = in[2 * p + 1];
+      const uint32_t wa = (j >> 1) == 0 ? a.x : (j >> 1) == 1 ? a.y : (j >> 1) == 2 ? a.z : a.w;
+      const uint32_t wb = (j >> 1) == 0 ? b.x : (j >> 1) == 1 ? b.y : (j >> 1) == 2 ? b.z : b.w;
+      w[p] = perm(wb, wa, sel);
+    }
+    out[j] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// wait until this wavefront's global -> LDS copies have landed (vmcnt(0))
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+
+template <int PL, int QL, int G, int EP>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_kernel(const Params prm) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int32_t s_tstart[MOE_MAX_EXPERTS + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int E = prm.E;
+
+  for (int e = tid; e <= E; e += 256) s_off[e] = prm.offsets[e];
+  __syncthreads();
+  if (tid == 0) {  // make the offsets a nondecreasing sequence inside [0, R]: no access leaves the tensors
+    int prev = 0;
+    for (int e = 0; e <= E; ++e) {
+      int v = s_off[e];
+      v = v < prev ? prev : v;
+      v = v > (int)prm.R ? (int)prm.R : v;
+      s_off[e] = v;
+      prev = v;
+    }
+    s_off[0] = 0;
+  }
+  __syncthreads();
+  int total;
+  if constexpr (G == GROUP_M) {
+    if (tid == 0) {
+      int run = 0;
+      for (int e = 0; e < E; ++e) {
+        s_tstart[e] = run;
+        const int me = s_off[e + 1] - s_off[e];
+        run += ((me + kBM - 1) / kBM) * prm.n_tiles;
+      }
+      s_tstart[E] = run;
+    }
+    __syncthreads();
+    total = s_tstart[E];
+  } else {
+    total = E * (prm.M / kBM) * prm.n_tiles;
+  }
+
+  const int nwg = gridDim.x;
+  const int logical = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+
+  uint8_t* const ldsP = lds;               // stage s at + s * kStageBytes
+  uint8_t* const ldsQ = lds + kTileBytes;
+
+  for (int t = logical; t < total; t += nwg) {
+    // ---------------- tile decode ----------------
+    int e, mt, nt;
+    if constexpr (G == GROUP_M) {
+      int lo = 0, hi = E;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tstart[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+      const int me = s_off[e + 1] - s_off[e];
+      const int mte = (me + kBM - 1) / kBM;
+      const int local = t - s_tstart[e];
+      mt = local % mte;
+      nt = local / mte;
+    } else {
+      const int mtiles = prm.M / kBM;
+      const int per = mtiles * prm.n_tiles;
+      e = t / per;
+      const int local = t - e * per;
+      mt = local % mtiles;
+      nt = local / mtiles;
+    }
+    // tile coordinates are wavefront-uniform: keep them in scalar registers
+    e = __builtin_amdgcn_readfirstlane(e);
+    mt = __builtin_amdgcn_readfirstlane(mt);
+    nt = __builtin_amdgcn_readfirstlane(nt);
+    const int row_beg = __builtin_amdgcn_readfirstlane(s_off[e]);
+    const int row_end = __builtin_amdgcn_readfirstlane(s_off[e + 1]);
+
+    // ---------------- operand addressing ----------------
+    // K-contiguous operands are copied global -> LDS directly (global_load_lds_dwordx4:
+    // lane l of a wavefront lands at the wave's LDS base + 16 * l). Round i of wave w
+    // fills LDS rows i*32 + w*8 .. +8; lane l takes row + (l >> 3) and physical chunk
+    // l & 7, i.e. logical chunk (l & 7) ^ swz(row) of that row.
+    // MN-contiguous operands go through registers and an 8x8 transpose.
+    const int dma_row0 = wave * 8 + (lane >> 3);
+    const bf16_t* pbase;
+    if constexpr (G == GROUP_M) pbase = reinterpret_cast<const bf16_t*>(prm.tab[e]);
+    else pbase = prm.p;
+    // KCONTIG: a uniform tile base plus, per round, this lane's 32-bit byte offset
+    const char* p_tile = nullptr;
+    uint32_t p_off[8];
+    int64_t p_col = 0;       // MNCONTIG: this thread's 8-column chunk
+    if constexpr (PL == KCONTIG) {
+      if constexpr (EP == EPI_SWIGLU) p_tile = reinterpret_cast<const char*>(pbase + (int64_t)nt * 128 * prm.p_ld);
+      else p_tile = reinterpret_cast<const char*>(pbase + (int64_t)nt * kBN * prm.p_ld);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = i * 32 + dma_row0;
+        int n;  // row of P relative to the tile base
+        if constexpr (EP == EPI_SWIGLU) n = (r < 128) ? r : prm.I + (r - 128);
+        else n = r;
+        p_off[i] = (uint32_t)(((int64_t)n * prm.p_ld + (((lane & 7) ^ swz(r)) * 8)) * 2);
+      }
+    } else {
+      p_col = (int64_t)nt * kBN + (tid & 31) * 8;
+    }
+    const char* q_tile = nullptr;
+    uint32_t q_off[8];
+    int64_t q_col = 0;
+    if constexpr (QL == KCONTIG) {
+      const int tile_row = row_beg + mt * kBM;
+      q_tile = reinterpret_cast<const char*>(prm.q + (int64_t)tile_row * prm.q_ld);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = i * 32 + dma_row0;
+        int row = tile_row + r;
+        row = row < row_end ? row : row_end - 1;  // rows past the expert: any valid row, discarded
+        q_off[i] = (uint32_t)(((int64_t)(row - tile_row) * prm.q_ld + (((lane & 7) ^ swz(r)) * 8)) * 2);
+      }
+    } else {
+      q_col = (int64_t)mt * kBM + (tid & 31) * 8;
+    }
+    // K range
+    int nk;
+    int64_t kbeg;  // GROUP_K: first token row; GROUP_M: 0
+    if constexpr (G == GROUP_M) {
+      nk = prm.K / kBK;
+      kbeg = 0;
+    } else {
+      nk = (row_end - row_beg + kBK - 1) / kBK;
+      kbeg = row_beg;
+    }
+    const int kg = tid >> 5;  // MNCONTIG: k group of 8 rows
+
+    uint4 pr[8], qr[8];
+    // start moving K step kt into LDS stage `stage`
+    auto issue_tile = [&](int kt, int stage) {
+      const int64_t k0 = (int64_t)kt * kBK;
+      if constexpr (PL == KCONTIG) {
+        uint8_t* P = ldsP + stage * kStageBytes + (wave * 8) * 128;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          __builtin_amdgcn_global_load_lds((const void*)(p_tile + k0 * 2 + p_off[i]), (lds_ptr_t)(P + i * 32 * 128), 16, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int64_t kr = kbeg + k0 + kg * 8 + i;
+          bool ok = true;
+          if constexpr (G == GROUP_K) ok = kr < row_end;
+          pr[i] = ok ? *reinterpret_cast<const uint4*>(pbase + kr * prm.p_ld + p_col) : make_uint4(0, 0, 0, 0);
+        }
+      }
+      if constexpr (QL == KCONTIG) {
+        uint8_t* Q = ldsQ + stage * kStageBytes + (wave * 8) * 128;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          __builtin_amdgcn_global_load_lds((const void*)(q_tile + k0 * 2 + q_off[i]), (lds_ptr_t)(Q + i * 32 * 128), 16, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int64_t kr = kbeg + k0 + kg * 8 + i;
+          bool ok = true;
+          if constexpr (G == GROUP_K) ok = kr < row_end;
+          qr[i] = ok ? *reinterpret_cast<const uint4*>(prm.q + kr * prm.q_ld + q_col) : make_uint4(0, 0, 0, 0);
+        }
+      }
+    };
+    // finish the register-staged (transposed) operands of stage `stage`
+    auto commit_tile = [&](int stage) {
+      if constexpr (PL == MNCONTIG) {
+        uint8_t* P = ldsP + stage * kStageBytes;
+        uint4 tr[8];
+        transpose8(pr, tr);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(P + lds_off((tid & 31) * 8 + j, kg)) = tr[j];
+      }
+      if constexpr (QL == MNCONTIG) {
+        uint8_t* Q = ldsQ + stage * kStageBytes;
+        uint4 tr[8];
+        transpose8(qr, tr);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(Q + lds_off((tid & 31) * 8 + j, kg)) = tr[j];
+      }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+    if (nk > 0) {
+      issue_tile(0, 0);
+      commit_tile(0);
+    }
+    wait_vmem();
+    __syncthreads();
+
+    const int l32 = lane & 31, lhi = lane >> 5;
+    // Fragment addresses. Sub-tile s of either operand starts at a row that is a
+    // multiple of 32, odd multiples for odd s, so swz(row) = swz(l32) ^ 4 * (s & 1);
+    // the rest of the row offset is a compile-time constant per s.
+    const uint32_t fragP = (uint32_t)((wn * 64 + l32) * 128);
+    const uint32_t fragQ = (uint32_t)((wm * 128 + l32) * 128);
+    const int sw = swz(l32);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) issue_tile(kt + 1, cur ^ 1);
+      const uint8_t* P = ldsP + cur * kStageBytes + fragP;
+      const uint8_t* Q = ldsQ + cur * kStageBytes + fragQ;
+      bf16x8 fa[2][4], fb[2][4];
+      auto load_frags = [&](int kk, int buf) {
+        const uint32_t c0 = (uint32_t)(((kk * 2 + lhi) ^ sw) << 4);
+        const uint32_t c1 = c0 ^ 64u;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          fa[buf][s] = *reinterpret_cast<const bf16x8*>(P + ((s >> 1) * 128 + (s & 1) * 32) * 128 + ((s & 1) ? c1 : c0));
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          fb[buf][s] = *reinterpret_cast<const bf16x8*>(Q + (s * 32) * 128 + ((s & 1) ? c1 : c0));
+      };
+      load_frags(0, 0);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk < 3) load_frags(kk + 1, (kk + 1) & 1);
+#pragma unroll
+        for (int sn = 0; sn < 4; ++sn)
+#pragma unroll
+          for (int sm = 0; sm < 4; ++sm)
+            acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][sn], fb[kk & 1][sm], acc[sn][sm], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kt + 1 < nk) commit_tile(cur ^ 1);
+      wait_vmem();
+      __syncthreads();
+    }
+
+    // ---------------- epilogue ----------------
+#pragma unroll
+    for (int sm = 0; sm < 4; ++sm) {
+      const int m_local = wm * 128 + sm * 32 + l32;
+      if constexpr (G == GROUP_K) {
+        bf16_t* C = reinterpret_cast<bf16_t*>(const_cast<void*>(prm.tab[e]));
+        const int64_t m = (int64_t)mt * kBM + m_local;
+#pragma unroll
+        for (int sn = 0; sn < 4; ++sn)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int64_t col = (int64_t)nt * kBN + sub_n(sn, wn) + i4 * 8 + lhi * 4;
+            uint2 v;
+            v.x = pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]);
+            v.y = pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]);
+            *reinterpret_cast<uint2*>(C + m * prm.c_ld + col) = v;
+          }
+      } else {
+        const int64_t mg = (int64_t)row_beg + mt * kBM + m_local;
+        const bool valid = mg < row_end;
+        if constexpr (EP == EPI_STORE) {
+          if (valid) {
+#pragma unroll
+            for (int sn = 0; sn < 4; ++sn)
+#pragma unroll
+              for (int i4 = 0; i4 < 4; ++i4) {
+                const int64_t col = (int64_t)nt * kBN + sub_n(sn, wn) + i4 * 8 + lhi * 4;
+                uint2 v;
+                v.x = pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]);
+                v.y = pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]);
+                *reinterpret_cast<uint2*>(prm.c + mg * prm.c_ld + col) = v;
+              }
+          }
+        } else if constexpr (EP == EPI_SWIGLU) {
+          if (valid) {
+            const float p = prm.prob[mg];
+            const int64_t I = prm.I;
+#pragma unroll
+            for (int sn = 0; sn < 2; ++sn)
+#pragma unroll
+              for (int i4 = 0; i4 < 4; ++i4) {
+                const int64_t col = (int64_t)nt * 128 + wn * 64 + sn * 32 + i4 * 8 + lhi * 4;
+                float h[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                  const float g = acc[sn][sm][i4 * 4 + v];
+                  const float u = acc[sn + 2][sm][i4 * 4 + v];
+                  h[v] = silu_f(g) * u * p;
+                }
+                *reinterpret_cast<uint2*>(prm.c + mg * prm.c_ld + col) =
+                    make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+                if (prm.zout) {
+                  bf16_t* z = prm.zout + mg * (2 * I);
+                  *reinterpret_cast<uint2*>(z + col) =
+                      make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]),
+                                 pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]));
+                  *reinterpret_cast<uint2*>(z + I + col) =
+                      make_uint2(pack_bf16x2(acc[sn + 2][sm][i4 * 4 + 0], acc[sn + 2][sm][i4 * 4 + 1]),
+                                 pack_bf16x2(acc[sn + 2][sm][i4 * 4 + 2], acc[sn + 2][sm][i4 * 4 + 3]));
+                }
+              }
+          }
+        } else {  // EPI_DSWIGLU: acc holds dH for intermediate columns
+          float part = 0.f;
+          if (valid) {
+            const float p = prm.prob[mg];
+            const int64_t I = prm.I;
+            const bf16_t* z = prm.zin + mg * (2 * I);
+            bf16_t* dz = prm.c + mg * prm.c_ld;
+#pragma unroll
+            for (int sn = 0; sn < 4; ++sn)
+#pragma unroll
+              for (int i4 = 0; i4 < 4; ++i4) {
+                const int64_t col = (int64_t)nt * kBN + sub_n(sn, wn) + i4 * 8 + lhi * 4;
+                const uint2 gz = *reinterpret_cast<const uint2*>(z + col);
+                const uint2 uz = *reinterpret_cast<const uint2*>(z + I + col);
+                const float gv[4] = {bf16_to_f32(gz.x & 0xFFFFu), bf16_to_f32(gz.x >> 16),
+                                     bf16_to_f32(gz.y & 0xFFFFu), bf16_to_f32(gz.y >> 16)};
+                const float uv[4] = {bf16_to_f32(uz.x & 0xFFFFu), bf16_to_f32(uz.x >> 16),
+                                     bf16_to_f32(uz.y & 0xFFFFu), bf16_to_f32(uz.y >> 16)};
+                float dg[4], du[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                  const float dh = acc[sn][sm][i4 * 4 + v];
+                  const float g = gv[v], u = uv[v];
+                  const float sg = 1.f / (1.f + __expf(-g));
+                  const float sl = g * sg;
+                  part += dh * sl * u;
+                  const float da = dh * p;
+                  dg[v] = da * u * sg * (1.f + g * (1.f - sg));
+                  du[v] = da * sl;
+                }
+                *reinterpret_cast<uint2*>(dz + col) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+                *reinterpret_cast<uint2*>(dz + I + col) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+              }
+          }
+          part += __shfl_xor(part, 32);
+          if (valid && lhi == 0) prm.part[(int64_t)(nt * 2 + wn) * prm.R + mg] = part;
+        }
+      }
+    }
+  }
+}
+
+template <int PL, int QL, int G, int EP>
+static moe_status launch(const Params& p, int64_t max_tiles, hipStream_t s, const char* what) {
+  if (max_tiles <= 0) return MOE_OK;
+  int64_t grid = num_cus();
+  if (max_tiles < grid) grid = max_tiles;
+  hipLaunchKernelGGL((grouped_gemm_kernel<PL, QL, G, EP>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  return check_launch(what);
+}
+
+moe_status run(const Params& p, int pl, int ql, int g, int ep, int64_t max_tiles, hipStream_t s,
+               const char* what) {
+  if (pl == KCONTIG && ql == KCONTIG && g == GROUP_M && ep == EPI_SWIGLU)
+    return launch<KCONTIG, KCONTIG, GROUP_M, EPI_SWIGLU>(p, max_tiles, s, what);
+  if (pl == KCONTIG && ql == KCONTIG && g == GROUP_M && ep == EPI_STORE)
+    return launch<KCONTIG, KCONTIG, GROUP_M, EPI_STORE>(p, max_tiles, s, what);
+  if (pl == MNCONTIG && ql == KCONTIG && g == GROUP_M && ep == EPI_DSWIGLU)
+    return launch<MNCONTIG, KCONTIG, GROUP_M, EPI_DSWIGLU>(p, max_tiles, s, what);
+  if (pl == MNCONTIG && ql == KCONTIG && g == GROUP_M && ep == EPI_STORE)
+    return launch<MNCONTIG, KCONTIG, GROUP_M, EPI_STORE>(p, max_tiles, s, what);
+  if (pl == MNCONTIG && ql == MNCONTIG && g == GROUP_K && ep == EPI_STORE)
+    return launch<MNCONTIG, MNCONTIG, GROUP_K, EPI_STORE>(p, max_tiles, s, what);
+  return fail(MOE_ERR_UNSUPPORTED, std::string(what) + ": no kernel for this operand combination");
+}
+
+}  // namespace gemm
+}  // namespace moe

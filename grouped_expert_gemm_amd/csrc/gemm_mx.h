@@ -1,0 +1,15 @@
+// MXFP8 grouped MLP forward (MX-scaled fp8 MFMA).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+namespace mx {
+
+moe_status forward(const moe_mlp_desc& d, int64_t R, const void* x_perm, const uint8_t* x_perm_scale,
+                   const void* const* w_gate_up, const void* const* w_down, const uint8_t* const* w_gate_up_scale,
+                   const uint8_t* const* w_down_scale, const int32_t* offsets, const float* prob_perm,
+                   void* y_perm, uint8_t* workspace, hipStream_t s);
+
+}  // namespace mx
+}  // namespace moe

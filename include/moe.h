@@ -1,0 +1,206 @@
+/*
+ * moe.h -- C ABI of the MoE expert feed-forward hot path on one AMD MI355X (gfx950).
+ *
+ * The path, as "Efficient MoE Training for Biological Foundation Models" describes
+ * it (Challenge 1: Fragmented expert kernels; Challenge 3: Quantization overhead):
+ * router top-k gating -> token permutation into per-expert groups (split_sizes) ->
+ * grouped GEMM gate_up -> ScaledSwiGLU (routing probability folded in) -> grouped
+ * GEMM down -> unpermute with combine; plus the matching backward and MXFP8 block
+ * quantisation (one scale per 32 consecutive values, Challenge 2).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers unless marked [host]. The caller owns all memory,
+ *    including workspaces; the library keeps no pointer after a call returns.
+ *  - Every call only enqueues work on `stream` (a hipStream_t passed as void*, NULL
+ *    for the null stream) and returns: no host<->device synchronisation and no
+ *    device allocation. Results are ready once the stream reaches them.
+ *  - Tensors are row-major and densely packed. bf16 tensors are raw 16-bit patterns.
+ *    Expert weights follow the [out_features, in_features] convention: gate_up is
+ *    [2I, H] with the gate rows first ([0, I)) and the up rows after ([I, 2I));
+ *    down is [H, I]. Each expert's weight is its own tensor, passed in a [host]
+ *    array of E device pointers.
+ *  - Arguments are checked before anything is launched. A bad argument returns
+ *    MOE_ERR_INVALID_ARG, a shape the kernels do not implement MOE_ERR_UNSUPPORTED,
+ *    a workspace that is too small MOE_ERR_WORKSPACE, and a failed launch
+ *    MOE_ERR_LAUNCH; nothing is launched in the first three cases. moe_last_error()
+ *    returns a description of the last failure on the calling thread. The library
+ *    never aborts the process.
+ *  - T = 0 and experts that receive no tokens are legal.
+ *  - Results are deterministic: the same inputs give the same bits.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_LAUNCH = 4
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,   /* float32 */
+  MOE_BF16 = 1,  /* bfloat16 bit patterns */
+  MOE_MXFP8 = 2  /* E4M3 codes (uint8) + one E8M0 scale byte per 32 consecutive values */
+} moe_dtype;
+
+/* Largest expert count the library accepts. */
+#define MOE_MAX_EXPERTS 256
+
+/*
+ * Router top-k gating. Source: routing_weights of the Hugging Face per-expert loop
+ * (Challenge 1). The pages show no router; the rule implemented is softmax over
+ * the E logits, keep the k largest, and (renormalize != 0) rescale the kept
+ * probabilities to sum to 1; with renormalize == 0 they are the full softmax's
+ * entries. Selection compares the float32 logits: slot 0 holds the largest; on
+ * equal logits the lower expert index comes first.
+ *   logits    [T, E] float32
+ *   topk_idx  [T, k] int32   (out) expert of each slot
+ *   topk_prob [T, k] float32 (out) routing weight of each slot
+ * Limits: 1 <= k <= E <= MOE_MAX_EXPERTS, k <= 16.
+ */
+moe_status moe_route_topk(const float* logits, int64_t T, int E, int k, int renormalize,
+                          int32_t* topk_idx, float* topk_prob, void* stream);
+
+/*
+ * Token permutation into per-expert groups. Source: split_sizes of GroupedLinear
+ * (Challenge 1) and the per-expert row gather of the baseline loop; token
+ * permutation before the grouped GEMM is also named in the PyTorch-native MoE
+ * library article (DeepEP dispatcher with permute/unpermute fusion).
+ * The R = T*k (token, slot) pairs are grouped by expert in ascending expert
+ * order; inside a group rows are in ascending token order. Row r of the result
+ * holds x[src_token[r]].
+ *   x            [T, H] in dtype dt (F32 or BF16; MXFP8: codes, with x_scale [T, H/32])
+ *   topk_idx     [T, k] int32, topk_prob [T, k] float32 (may be NULL: prob_perm not written)
+ *   x_perm       [R, H] (out), x_perm_scale [R, H/32] (out, MXFP8 only)
+ *   prob_perm    [R] float32 (out, may be NULL) routing weight of each row
+ *   split_sizes  [E] int32 (out) rows per expert; offsets [E+1] int32 (out) prefix sums
+ *   row_id_map   [T*k] int32 (out) row of pair (t, j) at index t*k + j
+ *   src_token    [R] int32 (out) token of each row
+ * reuse_map != 0: the maps are INPUTS from an earlier call with the same routing;
+ * only x is gathered into x_perm (used to gather the output gradient).
+ * workspace: moe_workspace_size(MOE_OP_PERMUTE, ...) bytes, 256-byte aligned.
+ */
+moe_status moe_permute(const void* x, const uint8_t* x_scale, moe_dtype dt, int64_t T, int H,
+                       int E, int k, const int32_t* topk_idx, const float* topk_prob,
+                       int reuse_map, void* x_perm, uint8_t* x_perm_scale, float* prob_perm,
+                       int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
+                       int32_t* src_token, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * Unpermute with combine. Source: the index_add_ into final_hidden_states of the
+ * baseline loop (Challenge 1).
+ *   out[t] = sum over j = 0..k-1 (in that order, float32) of w[t, j] * y_perm[row_id_map[t*k + j]]
+ * with w = weights [T, k] float32, or w = 1 when weights is NULL (the routing
+ * probability already folded into ScaledSwiGLU). y_perm [T*k, H] and out [T, H]
+ * are both dtype dt (F32 or BF16; bf16 output is rounded to nearest even).
+ */
+moe_status moe_unpermute_combine(const void* y_perm, moe_dtype dt, const int32_t* row_id_map,
+                                 const float* weights, int64_t T, int H, int k, void* out,
+                                 void* stream);
+
+/*
+ * MXFP8 block quantisation of a bf16 matrix along its rows. Source: Challenge 2
+ * (one scaling factor per block of 32 consecutive values, 8-bit values) and
+ * Challenge 3 (bf16 -> MXFP8 before the low-precision GEMM).
+ * For each block of 32 consecutive elements of a row: s = the smallest integer
+ * with max|block| <= 448 * 2^s, clamped to [-127, 127] (s = -127 for an all-zero
+ * block); the scale byte is s + 127 (E8M0); each element becomes the OCP E4M3
+ * code of x / 2^s, rounded to nearest with ties to even, keeping x's sign bit.
+ *   in [rows, cols] bf16 (cols % 32 == 0), e4m3 [rows, cols] uint8 (out),
+ *   e8m0 [rows, cols/32] uint8 (out).
+ */
+moe_status mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,
+                          uint8_t* e8m0, void* stream);
+
+/* Description of one grouped MLP layer (the experts' shapes and precisions). */
+typedef struct {
+  int E;             /* experts, 1..MOE_MAX_EXPERTS */
+  int H;             /* hidden size (GEMM K of gate_up, N of down) */
+  int I;             /* intermediate size (gate_up has 2I outputs) */
+  moe_dtype compute; /* GEMM input precision: MOE_F32, MOE_BF16 or MOE_MXFP8 */
+  moe_dtype act;     /* storage of x_perm: F32 (compute F32), BF16, or MXFP8 (codes + x_perm_scale) */
+  moe_dtype wt;      /* storage of weights: F32 (compute F32), BF16 (for MXFP8 compute: master
+                        weights quantised inside the call), or MXFP8 (codes + scale tables) */
+  int save_for_bwd;  /* nonzero: write z_save and h_save for moe_grouped_mlp_bwd */
+} moe_mlp_desc;
+
+/*
+ * Grouped MLP forward: GroupedLinear(gate_up) -> ScaledSwiGLU -> GroupedLinear(down)
+ * over the permuted rows. Source: Challenge 3 (the Sequential of the three ops and
+ * its fused forward: SwiGLU and probability scaling inside the grouped path, some
+ * intermediates never materialised; with MXFP8, quantisation fused before the
+ * down projection, Figure 4).
+ * For expert e and its rows r in [offsets[e], offsets[e+1]):
+ *   z = x_perm[r] W1_e^T  (2I values; float32 accumulation)
+ *   h = silu(z[0:I]) * z[I:2I] * prob_perm[r]      (silu(g) = g / (1 + exp(-g)))
+ *   y_perm[r] = h W2_e^T
+ * With compute = MXFP8, x_perm (along H), W1_e (along H), h (along I) and W2_e
+ * (along I) enter their GEMMs as MXFP8 (rule of mxfp8_quantize); h is quantised in
+ * the gate_up epilogue from its float32 value. Outputs: y_perm [R, H] (bf16, or
+ * float32 when compute = F32). With save_for_bwd: z_save [R, 2I] and h_save [R, I]
+ * (bf16, or float32 when compute = F32); otherwise both may be NULL.
+ *   w_gate_up [host] E pointers to [2I, H]; w_down [host] E pointers to [H, I]
+ *   w_gate_up_scale / w_down_scale [host] E pointers to [2I, H/32] / [H, I/32]
+ *       E8M0 scales, only when wt = MXFP8 (else NULL)
+ *   offsets [E+1] int32 (device), prob_perm [R] float32
+ * Shapes the GEMM kernels implement: BF16/MXFP8 need H % 256 == 0 and I % 128 == 0;
+ * F32 needs H % 4 == 0.
+ */
+moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, const void* x_perm,
+                               const uint8_t* x_perm_scale, const void* const* w_gate_up,
+                               const void* const* w_down, const uint8_t* const* w_gate_up_scale,
+                               const uint8_t* const* w_down_scale, const int32_t* offsets,
+                               const float* prob_perm, void* y_perm, void* z_save, void* h_save,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped MLP backward (the "matching fused backward" of Challenge 3), compute
+ * BF16 or F32. With dY = dy_perm (gradient of y_perm), G, U = the halves of z_save,
+ * A = silu(G) * U, p = prob_perm, per expert e:
+ *   dW2_e    = dY^T h_save                          -> dw_down[e]    [H, I]
+ *   dH       = dY W2_e
+ *   dprob[r] = sum_i dH[r, i] * A[r, i]             -> dprob_perm    [R] float32
+ *   dA       = dH * p
+ *   dG       = dA * U * sig(G) * (1 + G * (1 - sig(G))),  dU = dA * silu(G)
+ *   dx_perm  = [dG, dU] W1_e                         -> dx_perm       [R, H]
+ *   dW1_e    = [dG, dU]^T x_perm                     -> dw_gate_up[e] [2I, H]
+ * Experts without rows get all-zero weight gradients. Weight gradients have the
+ * weights' dtype (bf16 or float32) and are overwritten, not accumulated.
+ */
+moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, const void* dy_perm,
+                               const void* x_perm, const void* z_save, const void* h_save,
+                               const float* prob_perm, const void* const* w_gate_up,
+                               const void* const* w_down, const int32_t* offsets,
+                               void* dx_perm, void* const* dw_gate_up, void* const* dw_down,
+                               float* dprob_perm, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Operations for moe_workspace_size. */
+typedef enum {
+  MOE_OP_PERMUTE = 0,  /* T = token count, E, k used; desc may be NULL */
+  MOE_OP_MLP_FWD = 1,  /* desc and R used */
+  MOE_OP_MLP_BWD = 2   /* desc and R used */
+} moe_op;
+
+/* Workspace bytes an operation needs (0 is possible). bytes is a [host] pointer. */
+moe_status moe_workspace_size(moe_op op, const moe_mlp_desc* desc, int64_t R, int64_t T, int E,
+                              int k, size_t* bytes);
+
+const char* moe_status_str(moe_status s);
+/* Description of the last failure on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

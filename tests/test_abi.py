@@ -1,0 +1,92 @@
+"""The C-ABI library (CPU only, no compute calls): it loads, exports every entry
+point include/moe.h declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from grouped_expert_gemm_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from grouped_expert_gemm_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^(?:moe_status|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for n in ("moe_route_topk", "moe_permute", "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd",
+              "moe_unpermute_combine", "mxfp8_quantize"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    from grouped_expert_gemm_amd import _lib
+    names = declared_functions()
+    assert sorted(names) == sorted(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.moe_status_str(s)
+
+
+def test_argument_errors_before_launch(L):
+    from grouped_expert_gemm_amd import _lib
+    INV, UNS, WS = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED, _lib.MOE_ERR_WORKSPACE
+    assert L.moe_route_topk(None, 10, 0, 1, 1, None, None, None) == INV        # E = 0
+    assert L.moe_route_topk(None, 10, 8, 9, 1, None, None, None) == INV        # k > E
+    assert L.moe_route_topk(None, 10, 32, 17, 1, None, None, None) == UNS      # k > 16
+    assert L.moe_route_topk(None, 0, 8, 2, 1, None, None, None) == 0           # T = 0: nothing to do
+    assert L.moe_route_topk(None, 5, 8, 2, 1, None, None, None) == INV         # NULL
+    assert b"NULL" in L.moe_last_error()
+    assert L.mxfp8_quantize(None, 4, 33, None, None, None) == INV              # cols % 32
+    assert L.moe_unpermute_combine(None, 2, None, None, 4, 8, 2, None, None) == UNS  # MXFP8 rows
+    # permute: undersized workspace is reported before any launch
+    dummy = ctypes.c_void_p(256)
+    assert L.moe_permute(dummy, None, 1, 1000, 64, 8, 2, dummy, dummy, 0, dummy, None, dummy, dummy, dummy,
+                         dummy, dummy, dummy, 16, None) == WS
+    assert L.moe_permute(dummy, None, 1, 10, 64, 300, 2, dummy, dummy, 0, dummy, None, dummy, dummy, dummy,
+                         dummy, dummy, dummy, 1 << 20, None) == INV             # E > 256
+
+
+def test_mlp_descriptor_checks(L):
+    from grouped_expert_gemm_amd import _lib
+    n = ctypes.c_size_t()
+    D = _lib.MlpDesc
+    ok = D(8, 4096, 14336, 1, 1, 1, 0)
+    assert L.moe_workspace_size(1, ctypes.byref(ok), 16384, 0, 0, 0, ctypes.byref(n)) == 0
+    assert n.value >= 16384 * 14336 * 2
+    assert L.moe_workspace_size(2, ctypes.byref(ok), 8192, 0, 0, 0, ctypes.byref(n)) == 0
+    assert L.moe_workspace_size(1, ctypes.byref(D(8, 100, 14336, 1, 1, 1, 0)), 1, 0, 0, 0,
+                                ctypes.byref(n)) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, 2, 1, 1, 0)), 1, 0, 0, 0,
+                                ctypes.byref(n)) == _lib.MOE_ERR_UNSUPPORTED    # MXFP8 backward
+    assert L.moe_workspace_size(1, ctypes.byref(D(0, 256, 128, 1, 1, 1, 0)), 1, 0, 0, 0,
+                                ctypes.byref(n)) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_size(1, ctypes.byref(D(8, 256, 128, 1, 0, 1, 0)), 1, 0, 0, 0,
+                                ctypes.byref(n)) == _lib.MOE_ERR_INVALID_ARG    # f32 storage, bf16 compute
+    assert L.moe_grouped_mlp_fwd(None, 1, None, None, None, None, None, None, None, None, None, None, None,
+                                 None, 0, None) == _lib.MOE_ERR_INVALID_ARG
+    # a NULL expert pointer is caught before launch
+    ptrs = (ctypes.c_void_p * 8)(*([4096] * 7 + [0]))
+    pp = ctypes.cast(ptrs, _lib.PP)
+    d = D(8, 256, 128, 1, 1, 1, 0)
+    st = L.moe_grouped_mlp_fwd(ctypes.byref(d), 64, ctypes.c_void_p(4096), None, pp, pp, None, None,
+                               ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096), None, None,
+                               ctypes.c_void_p(4096), 1 << 30, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG and b"expert 7" in L.moe_last_error()

@@ -1,0 +1,142 @@
+"""GPU parity of the grouped MLP (forward, backward) and of the whole layer
+against the CPU oracle, at multi-tile shapes with ragged expert groups, empty
+experts, and the tiny float32 workload. Tolerance: max|a-b| / max|b| <= 2e-2
+for bf16 outputs with float32 accumulation (the float32 path is held to 1e-4)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import max_rel_err
+from moe_inputs import WORKLOADS, make_grad, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_expert_gemm_amd as g
+    g.lib()
+    return g
+
+
+from gpu_util import dev_bf16, dev_f32, host, oracle_perm  # noqa: E402
+
+
+def _setup(w, zero_experts=()):
+    inp = make_inputs(w)
+    if zero_experts:
+        inp.logits[:, list(zero_experts)] -= 100.0
+    idx, p, m, pp = oracle_perm(inp, w.k, w.E)
+    for e in zero_experts:
+        assert m["split_sizes"][e] == 0
+    return inp, idx, p, m, pp
+
+
+def _dev_inputs(inp, m, pp):
+    xp_bits = inp.bits["x"][m["src_token"]]
+    return (dev_bf16(xp_bits), dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"]),
+            torch.from_numpy(m["offsets"].astype(np.int32)).cuda(), dev_f32(pp.astype(np.float32)))
+
+
+FWD_SHAPES = [
+    # name, T, H, I, E, k, zipf, empty experts
+    ("ragged", 1500, 512, 384, 4, 2, 0.0, ()),
+    ("skewed", 1200, 256, 128, 16, 4, 1.2, (3, 9)),
+    ("one_expert", 300, 256, 256, 1, 1, 0.0, ()),
+    ("tiny_groups", 37, 256, 128, 8, 2, 0.0, (0,)),
+]
+
+
+@pytest.mark.parametrize("shape", FWD_SHAPES, ids=[s[0] for s in FWD_SHAPES])
+def test_grouped_mlp_fwd_bf16(moe, shape):
+    name, T, H, I, E, k, zipf, empty = shape
+    w = scaled(WORKLOADS["mixtral_fwd"], T=T, H=H, I=I, E=E, k=k, zipf=zipf, seed=11)
+    inp, idx, p, m, pp = _setup(w, empty)
+    xp, w1, w2, off, prob = _dev_inputs(inp, m, pp)
+    print(f"mlp fwd bf16 {name}: R={T * k} H={H} I={I} E={E}", flush=True)
+    y, z, h = moe.moe_grouped_mlp_fwd(xp, w1, w2, off, prob, compute="bf16", save_for_bwd=True)
+    y2 = moe.moe_grouped_mlp_fwd(xp, w1, w2, off, prob, compute="bf16")
+    torch.cuda.synchronize()
+    ry, rz, rh = oracle.grouped_mlp_forward(inp.x[m["src_token"]], inp.w1, inp.w2, m["offsets"], pp)
+    assert max_rel_err(host(y), ry) <= BF16_TOL
+    assert max_rel_err(host(z), rz) <= BF16_TOL
+    assert max_rel_err(host(h), rh) <= BF16_TOL
+    assert torch.equal(y, y2), "saving z/h must not change y"
+
+
+BWD_SHAPES = [
+    ("ragged", 700, 512, 256, 4, 2, 0.0, ()),
+    ("skewed_empty", 900, 256, 256, 8, 2, 1.2, (5,)),
+]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=[s[0] for s in BWD_SHAPES])
+def test_grouped_mlp_bwd_bf16(moe, shape):
+    name, T, H, I, E, k, zipf, empty = shape
+    w = scaled(WORKLOADS["mixtral_fwd_bwd"], T=T, H=H, I=I, E=E, k=k, zipf=zipf, seed=12)
+    inp, idx, p, m, pp = _setup(w, empty)
+    xp, w1, w2, off, prob = _dev_inputs(inp, m, pp)
+    R = T * k
+    dyf, dyb = make_grad((R, H), 99)
+    print(f"mlp bwd bf16 {name}: R={R} H={H} I={I} E={E}", flush=True)
+    y, z, h = moe.moe_grouped_mlp_fwd(xp, w1, w2, off, prob, compute="bf16", save_for_bwd=True)
+    dx, dw1, dw2, dprob = moe.moe_grouped_mlp_bwd(dev_bf16(dyb), xp, z, h, prob, w1, w2, off)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_mlp_backward(dyf, inp.x[m["src_token"]], inp.w1, inp.w2, m["offsets"], pp)
+    assert max_rel_err(host(dx), ref["dx_perm"]) <= BF16_TOL
+    assert max_rel_err(host(dw1), ref["dw_gate_up"]) <= BF16_TOL
+    assert max_rel_err(host(dw2), ref["dw_down"]) <= BF16_TOL
+    assert max_rel_err(dprob.cpu().numpy(), ref["dprob_perm"]) <= BF16_TOL
+    for e in empty:
+        assert not host(dw1)[e].any() and not host(dw2)[e].any(), "idle expert must get zero weight gradients"
+
+
+def test_tiny_layer_f32_forward_and_backward(moe):
+    """The tiny workload end to end in float32: route -> permute -> grouped MLP -> combine,
+    against the per-expert loop; then the backward against the loop's backward."""
+    w = WORKLOADS["tiny"]
+    inp = make_inputs(w)
+    T, H, E, k = w.T, w.H, w.E, w.k
+    idx, p = moe.moe_route_topk(dev_f32(inp.logits), k)
+    x = dev_f32(inp.x)
+    r = moe.moe_permute(x, idx, p, E)
+    w1, w2 = dev_f32(inp.w1), dev_f32(inp.w2)
+    y, z, h = moe.moe_grouped_mlp_fwd(r["x_perm"], w1, w2, r["offsets"], r["prob_perm"], compute="f32",
+                                      save_for_bwd=True)
+    out = moe.moe_unpermute_combine(y, r["row_id_map"], T, k)
+    ridx, rp = oracle.route_topk(inp.logits, k)
+    ref = oracle.moe_ffn_forward(inp.x, inp.w1, inp.w2, ridx, rp)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert max_rel_err(out.cpu().numpy(), ref) <= F32_TOL
+
+    dout = np.random.default_rng(7).standard_normal((T, H)).astype(np.float32)
+    dyp = moe.moe_permute(dev_f32(dout), idx, None, E, row_id_map=r["row_id_map"])["x_perm"]
+    dx_perm, dw1, dw2, dprob_perm = moe.moe_grouped_mlp_bwd(dyp, r["x_perm"], z, h, r["prob_perm"], w1, w2,
+                                                            r["offsets"], compute="f32")
+    dx = moe.moe_unpermute_combine(dx_perm, r["row_id_map"], T, k)
+    g = oracle.moe_ffn_backward(inp.x, inp.w1, inp.w2, ridx, rp, dout)
+    assert max_rel_err(dx.cpu().numpy(), g["dx"]) <= F32_TOL
+    assert max_rel_err(dw1.cpu().numpy(), g["dw_gate_up"]) <= F32_TOL
+    assert max_rel_err(dw2.cpu().numpy(), g["dw_down"]) <= F32_TOL
+    dprob = dprob_perm.cpu().numpy()[r["row_id_map"].cpu().numpy()].reshape(T, k)
+    assert max_rel_err(dprob, g["drouting_weights"]) <= F32_TOL
+
+
+def test_layer_bf16_end_to_end(moe):
+    """route -> permute -> grouped MLP -> combine in bf16 against the per-expert loop."""
+    w = scaled(WORKLOADS["qwen3_fwd"], T=2000, H=512, I=256, E=32, k=4, seed=21)
+    inp = make_inputs(w)
+    idx, p = moe.moe_route_topk(dev_f32(inp.logits), w.k)
+    r = moe.moe_permute(dev_bf16(inp.bits["x"]), idx, p, w.E)
+    y = moe.moe_grouped_mlp_fwd(r["x_perm"], dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"]), r["offsets"],
+                                r["prob_perm"], compute="bf16")
+    out = moe.moe_unpermute_combine(y, r["row_id_map"], w.T, w.k)
+    ridx, rp = oracle.route_topk(inp.logits, w.k)
+    ref = oracle.moe_ffn_forward(inp.x, inp.w1, inp.w2, ridx, rp)
+    assert max_rel_err(host(out), ref) <= BF16_TOL

@@ -1,0 +1,178 @@
+"""GPU parity of each C-ABI entry point against the CPU oracle, at sizes that span
+several tiles with ragged tails, plus edge cases (empty experts, one expert
+taking every token, T = 1, k = E). Integer and byte outputs must match exactly;
+floating outputs within the stated tolerances (max|a-b| / max|b|)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import max_rel_err
+from moe_inputs import WORKLOADS, f32_to_bf16_bits, bf16_bits_to_f32, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2     # bf16 outputs with float32 accumulation
+PROB_TOL = 1e-6     # float32 routing weights
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_expert_gemm_amd as g
+    g.lib()
+    return g
+
+
+from gpu_util import bf16_bits, dev_bf16, dev_f32, host, oracle_perm  # noqa: E402
+
+
+# ---------------------------------------------------------------------------
+# router
+# ---------------------------------------------------------------------------
+
+def _route_case(moe, logits, k, renorm=True):
+    idx, p = moe.moe_route_topk(dev_f32(logits), k, renorm)
+    ridx, rp = oracle.route_topk(logits, k, renorm)
+    print(f"route T={logits.shape[0]} E={logits.shape[1]} k={k}", flush=True)
+    assert np.array_equal(idx.cpu().numpy(), ridx), "top-k indices differ"
+    np.testing.assert_allclose(p.cpu().numpy(), rp, rtol=PROB_TOL, atol=1e-7)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_fwd", "mixtral_fwd"])
+def test_route_workloads(moe, name):
+    w = WORKLOADS[name]
+    inp = make_inputs(scaled(w, H=32, I=32, E=w.E), want_float=False)  # logits do not depend on H, I
+    _route_case(moe, inp.logits, w.k)
+
+
+def test_route_edges(moe):
+    rng = np.random.default_rng(0)
+    ties = np.round(rng.standard_normal((333, 16))).astype(np.float32)   # many exact ties
+    _route_case(moe, ties, 4)
+    _route_case(moe, rng.standard_normal((1, 8)).astype(np.float32), 2)  # T = 1
+    _route_case(moe, rng.standard_normal((100, 6)).astype(np.float32), 6)  # k = E
+    _route_case(moe, rng.standard_normal((100, 256)).astype(np.float32), 16)
+    _route_case(moe, rng.standard_normal((77, 32)).astype(np.float32), 3, renorm=False)
+
+
+# ---------------------------------------------------------------------------
+# permutation and combine
+# ---------------------------------------------------------------------------
+
+def _permute_case(moe, T, H, E, k, idx, p, dtype="bf16"):
+    rng = np.random.default_rng(T + E)
+    xf = rng.standard_normal((T, H)).astype(np.float32)
+    xb = f32_to_bf16_bits(xf)
+    x = dev_bf16(xb) if dtype == "bf16" else dev_f32(xf)
+    r = moe.moe_permute(x, torch.from_numpy(idx.astype(np.int32)).cuda(), dev_f32(p), E)
+    m = oracle.permute(idx, E)
+    print(f"permute T={T} H={H} E={E} k={k}", flush=True)
+    for key in ("split_sizes", "offsets", "row_id_map", "src_token"):
+        assert np.array_equal(r[key].cpu().numpy(), m[key]), key
+    pp = p.ravel()[m["src_token"] * k + m["src_slot"]].astype(np.float32)
+    assert np.array_equal(r["prob_perm"].cpu().numpy(), pp)
+    if dtype == "bf16":
+        assert np.array_equal(bf16_bits(r["x_perm"]), xb[m["src_token"]])
+    else:
+        assert np.array_equal(r["x_perm"].cpu().numpy(), xf[m["src_token"]])
+    return r, m, x
+
+
+def test_permute_workloads(moe):
+    for name in ("tiny", "qwen3_fwd"):
+        w = WORKLOADS[name]
+        inp = make_inputs(scaled(w, H=32, I=32), want_float=False)
+        idx, p = oracle.route_topk(inp.logits, w.k)
+        sizes = np.bincount(idx.ravel(), minlength=w.E)
+        if name == "qwen3_fwd":
+            assert (sizes == 0).any()
+        _permute_case(moe, w.T, 256, w.E, w.k, idx, p.astype(np.float32))
+
+
+def test_permute_edges(moe):
+    rng = np.random.default_rng(1)
+    # every token to expert 3 (k = 1), the others empty
+    idx = np.full((1000, 1), 3, np.int32)
+    _permute_case(moe, 1000, 64, 8, 1, idx, np.ones((1000, 1), np.float32))
+    # T = 1, k = E
+    idx, p = oracle.route_topk(rng.standard_normal((1, 5)).astype(np.float32), 5)
+    _permute_case(moe, 1, 40, 5, 5, idx, p.astype(np.float32))
+    # odd row width (byte-wise copies), float32 rows, many blocks
+    idx, p = oracle.route_topk(rng.standard_normal((2049, 256)).astype(np.float32), 16)
+    _permute_case(moe, 2049, 3, 256, 16, idx, p.astype(np.float32), dtype="f32")
+
+
+def test_permute_reuse_map_and_mxfp8_rows(moe):
+    rng = np.random.default_rng(2)
+    T, H, E, k = 777, 128, 8, 2
+    idx, p = oracle.route_topk(rng.standard_normal((T, E)).astype(np.float32), k)
+    r, m, _ = _permute_case(moe, T, H, E, k, idx, p.astype(np.float32))
+    g = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    out = moe.moe_permute(dev_bf16(g), torch.from_numpy(idx).cuda(), None, E, row_id_map=r["row_id_map"])
+    assert np.array_equal(bf16_bits(out["x_perm"]), g[m["src_token"]])
+    codes = torch.from_numpy(rng.integers(0, 255, (T, H), dtype=np.uint8)).cuda()
+    sc = torch.from_numpy(rng.integers(0, 255, (T, H // 32), dtype=np.uint8)).cuda()
+    q = moe.moe_permute(codes, torch.from_numpy(idx).cuda(), dev_f32(p), E, x_scale=sc)
+    assert np.array_equal(q["x_perm"].cpu().numpy(), codes.cpu().numpy()[m["src_token"]])
+    assert np.array_equal(q["x_perm_scale"].cpu().numpy(), sc.cpu().numpy()[m["src_token"]])
+
+
+def test_combine(moe):
+    rng = np.random.default_rng(3)
+    T, H, E, k = 1500, 512, 8, 2
+    idx, p = oracle.route_topk(rng.standard_normal((T, E)).astype(np.float32), k)
+    m = oracle.permute(idx, E)
+    yb = f32_to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
+    rmap = torch.from_numpy(m["row_id_map"].astype(np.int32)).cuda()
+    out = moe.moe_unpermute_combine(dev_bf16(yb), rmap, T, k)
+    ref = oracle.unpermute_combine(bf16_bits_to_f32(yb), m["row_id_map"], T, k)
+    assert max_rel_err(host(out), ref) <= 2.0 ** -8
+    outw = moe.moe_unpermute_combine(dev_bf16(yb), rmap, T, k, dev_f32(p.astype(np.float32)))
+    refw = oracle.unpermute_combine(bf16_bits_to_f32(yb), m["row_id_map"], T, k, weights=p)
+    assert max_rel_err(host(outw), refw) <= 2.0 ** -8
+    # k = 1, unit weights: the inverse permutation, bit for bit
+    idx1, _ = oracle.route_topk(rng.standard_normal((T, E)).astype(np.float32), 1)
+    m1 = oracle.permute(idx1, E)
+    xb = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    back = moe.moe_unpermute_combine(dev_bf16(xb[m1["src_token"]]),
+                                     torch.from_numpy(m1["row_id_map"].astype(np.int32)).cuda(), T, 1)
+    assert np.array_equal(bf16_bits(back), xb)
+    # float32 rows, odd width
+    yf = rng.standard_normal((T * k, 7)).astype(np.float32)
+    outf = moe.moe_unpermute_combine(dev_f32(yf), rmap, T, k)
+    np.testing.assert_allclose(outf.cpu().numpy(), oracle.unpermute_combine(yf, m["row_id_map"], T, k),
+                               rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 quantisation: bit-exact
+# ---------------------------------------------------------------------------
+
+def test_mxfp8_quantize_bit_exact(moe):
+    rng = np.random.default_rng(4)
+    rows, cols = 300, 1024
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x *= np.exp2(rng.integers(-40, 40, (rows, cols // 32))).repeat(32, 1).astype(np.float32)
+    x[5, 64:96] = 0.0                                       # zero block
+    x[6, :32] = -0.0                                        # negative zeros
+    x[7, 32:64] = rng.standard_normal(32) * 1e-39           # bf16 subnormals
+    x[8, 64:96] = 448.0 * 2.0 ** 5                          # exactly on the scale boundary
+    x[9, :] = rng.standard_normal(cols) * 3e38 / 4          # near the top of the range
+    xb = f32_to_bf16_bits(x)
+    codes, scales = moe.mxfp8_quantize(dev_bf16(xb))
+    rc, rs = oracle.mxfp8_quantize(bf16_bits_to_f32(xb))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_mxfp8_quantize_weight_shape(moe):
+    """A Mixtral gate_up weight slice: one expert's first 2048 rows x 4096."""
+    w = WORKLOADS["mixtral_fwd"]
+    g = np.random.default_rng(np.random.SeedSequence(w.seed).spawn(6)[1])
+    xb = f32_to_bf16_bits(np.float32(0.02) * g.standard_normal((2048, 4096), np.float32))
+    codes, scales = moe.mxfp8_quantize(dev_bf16(xb))
+    rc, rs = oracle.mxfp8_quantize(bf16_bits_to_f32(xb))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
