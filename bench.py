@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert feed-forward layer on one MI355X.
+
+One step = the whole forward hot path over one batch of synthetic tokens:
+router top-k -> permutation into expert groups -> grouped gate_up GEMM with
+ScaledSwiGLU -> grouped down GEMM -> unpermute/combine, at the Mixtral-8x7B
+layer shape (T=8192, H=4096, I=14336, E=8, top-2, bf16). A second measurement
+runs forward + backward at T=4096. Throughput is the algorithmic GEMM work
+(6*R*H*I per forward, twice that per backward) over the wall time of the
+timed steps, inputs already resident in HBM.
+
+Prints one JSON line. The oracle's CPU time on a bounded sample of the same
+workload is reported beside it (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+METRIC = "grouped-MLP TFLOP/s fwd and fwd+bwd, Mixtral-8x7B layer; % MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "grouped_expert_gemm_amd", "csrc", "gemm_bf16.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev_bf16(torch, np, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Layer:
+    """Device buffers and the C calls of one forward (and optionally backward) step."""
+
+    def __init__(self, w, inp, backward: bool):
+        import numpy as np
+        import torch
+
+        import grouped_expert_gemm_amd as moe
+        from grouped_expert_gemm_amd import _lib
+
+        self.torch, self.moe, self.L = torch, moe, moe.lib()
+        self.w = w
+        T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
+        R = T * k
+        self.R = R
+        dev = torch.device("cuda", 0)
+        bf = torch.bfloat16
+        self.logits = torch.from_numpy(inp.logits).cuda()
+        self.x = dev_bf16(torch, np, inp.bits["x"])
+        self.w1 = dev_bf16(torch, np, inp.bits["w1"])
+        self.w2 = dev_bf16(torch, np, inp.bits["w2"])
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.prob = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.x_perm = torch.empty((R, H), dtype=bf, device=dev)
+        self.prob_perm = torch.empty(R, dtype=torch.float32, device=dev)
+        self.split = torch.empty(E, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.rmap = torch.empty(R, dtype=torch.int32, device=dev)
+        self.src = torch.empty(R, dtype=torch.int32, device=dev)
+        self.ws_perm = torch.empty(max(1, moe.workspace_size(_lib.MOE_OP_PERMUTE, None, 0, T, E, k)),
+                                   dtype=torch.uint8, device=dev)
+        self.h = torch.empty((R, I), dtype=bf, device=dev)
+        self.z = torch.empty((R, 2 * I), dtype=bf, device=dev) if backward else None
+        self.y = torch.empty((R, H), dtype=bf, device=dev)
+        self.out = torch.empty((T, H), dtype=bf, device=dev)
+        self.t1, self._k1 = _lib.ptr_table([self.w1[e].data_ptr() for e in range(E)])
+        self.t2, self._k2 = _lib.ptr_table([self.w2[e].data_ptr() for e in range(E)])
+        self.backward = backward
+        if backward:
+            self.dout = dev_bf16(torch, np, inp.bits["dout"])
+            self.dy = torch.empty((R, H), dtype=bf, device=dev)
+            self.dx_perm = torch.empty((R, H), dtype=bf, device=dev)
+            self.dx = torch.empty((T, H), dtype=bf, device=dev)
+            self.dw1 = torch.empty_like(self.w1)
+            self.dw2 = torch.empty_like(self.w2)
+            self.dprob_perm = torch.empty(R, dtype=torch.float32, device=dev)
+            self.dprob = torch.empty(R, dtype=torch.float32, device=dev)
+            self.d1, self._k3 = _lib.ptr_table([self.dw1[e].data_ptr() for e in range(E)])
+            self.d2, self._k4 = _lib.ptr_table([self.dw2[e].data_ptr() for e in range(E)])
+            self.desc = _lib.MlpDesc(E, H, I, _lib.MOE_BF16, _lib.MOE_BF16, _lib.MOE_BF16, 1)
+            self.ws_bwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_BWD, self.desc, R), dtype=torch.uint8,
+                                      device=dev)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.ev = []
+
+    def step(self, time_gate_up=False):
+        from grouped_expert_gemm_amd import _lib
+        L, w, s, p = self.L, self.w, self.stream, (lambda t: ctypes.c_void_p(t.data_ptr()))
+        T, H, I, E, k, R = w.T, w.H, w.I, w.E, w.k, self.R
+        BF = _lib.MOE_BF16
+        c = _lib.check
+        c("route", L.moe_route_topk(p(self.logits), T, E, k, 1, p(self.idx), p(self.prob), s))
+        c("permute", L.moe_permute(p(self.x), None, BF, T, H, E, k, p(self.idx), p(self.prob), 0, p(self.x_perm),
+                                   None, p(self.prob_perm), p(self.split), p(self.offsets), p(self.rmap),
+                                   p(self.src), p(self.ws_perm), self.ws_perm.numel(), s))
+        if time_gate_up:
+            e0 = self.torch.cuda.Event(enable_timing=True)
+            e1 = self.torch.cuda.Event(enable_timing=True)
+            e0.record()
+        c("gate_up", L.moe_grouped_gate_up_swiglu(E, R, H, I, BF, p(self.x_perm), None, self.t1, None,
+                                                  p(self.offsets), p(self.prob_perm), p(self.h), None,
+                                                  p(self.z) if self.z is not None else None, s))
+        if time_gate_up:
+            e1.record()
+            self.ev.append((e0, e1))
+        c("down", L.moe_grouped_linear(E, R, I, H, BF, p(self.h), self.t2, p(self.offsets), p(self.y), s))
+        c("combine", L.moe_unpermute_combine(p(self.y), BF, p(self.rmap), None, T, H, k, p(self.out), s))
+        if self.backward:
+            c("dOut gather", L.moe_permute(p(self.dout), None, BF, T, H, E, k, None, None, 1, p(self.dy), None,
+                                           None, None, None, p(self.rmap), None, None, 0, s))
+            c("mlp bwd", L.moe_grouped_mlp_bwd(ctypes.byref(self.desc), R, p(self.dy), p(self.x_perm), p(self.z),
+                                               p(self.h), p(self.prob_perm), self.t1, self.t2, p(self.offsets),
+                                               p(self.dx_perm), self.d1, self.d2, p(self.dprob_perm),
+                                               p(self.ws_bwd), self.ws_bwd.numel(), s))
+            c("dx combine", L.moe_unpermute_combine(p(self.dx_perm), BF, p(self.rmap), None, T, H, k, p(self.dx),
+                                                    s))
+            # dprob[t, j] = dprob_perm[row_id_map[t*k + j]]: a gather, i.e. a combine with k = 1
+            c("dprob gather", L.moe_unpermute_combine(p(self.dprob_perm), _lib.MOE_F32, p(self.rmap), None, R, 1,
+                                                      1, p(self.dprob), s))
+
+    def gate_up_ms(self):
+        self.torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in self.ev]
+        return sum(ts) / len(ts)
+
+
+def time_steps(layer, steps, warmup):
+    torch = layer.torch
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.step(time_gate_up=True)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def traffic_record():
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter runs, or None
+    if they were taken on a different version of the kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if rec.get("kernel_sha256") != sha:
+            return None
+        return rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, w, seconds):
+    """The oracle (float64 numpy, per-expert loop) on the first rows of expert 0 of the
+    same workload, sized to take roughly `seconds` of host time."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from moe_inputs import bf16_bits_to_f32
+
+    idx, p = oracle.route_topk(inp.logits, w.k)
+    m = oracle.permute(idx, w.E)
+    rows = m["src_token"][m["offsets"][0]:m["offsets"][1]]
+    pp = p.ravel()[m["src_token"] * w.k + m["src_slot"]][m["offsets"][0]:m["offsets"][1]]
+    w1 = bf16_bits_to_f32(inp.bits["w1"][0:1])
+    w2 = bf16_bits_to_f32(inp.bits["w2"][0:1])
+    x = bf16_bits_to_f32(inp.bits["x"][rows])
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.grouped_mlp_forward(x[:n], w1, w2, np.array([0, n]), pp[:n])
+        return time.perf_counter() - t0
+
+    n0 = 32
+    t_small = run(n0)
+    n = int(max(n0, min(len(rows), n0 * seconds / max(t_small, 1e-3))))
+    t = run(n)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    flop = 6.0 * n * w.H * w.I
+    return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 numpy oracle forward (gate_up, ScaledSwiGLU, down) on {n} rows of expert 0 of the "
+                      f"{w.name} workload (H={w.H}, I={w.I}); {t:.1f} s wall, {os.cpu_count()} host CPUs visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-fwd-bwd", action="store_true", help="skip the forward+backward measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the MoE layer here runs all experts on a single MI355X "
+              "(no expert parallelism across GPUs is built); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from moe_inputs import WORKLOADS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    w = WORKLOADS["mixtral_fwd"]
+    t0 = time.perf_counter()
+    inp = make_inputs(w, want_float=False)
+    log(f"inputs {w.name}: {time.perf_counter() - t0:.1f} s")
+    layer = Layer(w, inp, backward=False)
+    ms = time_steps(layer, args.steps, args.warmup)
+    gate_ms = layer.gate_up_ms()
+    flop = w.gemm_flop_fwd()
+    value = flop / (ms * 1e-3) / 1e12
+    R = w.R
+    gate_flop = 4.0 * R * w.H * w.I
+    achieved = gate_flop / (gate_ms * 1e-3) / 1e12
+    log(f"fwd step {ms:.3f} ms -> {value:.1f} TFLOP/s; gate_up {gate_ms:.3f} ms -> {achieved:.1f} TFLOP/s")
+    traffic = traffic_record()
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "mixtral_fwd", "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k,
+                   "step": "route + permute + gate_up/ScaledSwiGLU + down + combine (forward)",
+                   "flop_per_step": flop},
+        "pct_of_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
+        "roofline": {"kernel": "grouped gate_up + ScaledSwiGLU (grouped_gemm_kernel<K,K,GROUP_M,SWIGLU>)",
+                     "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "avg_launch_ms": round(gate_ms, 4), "traffic": traffic},
+    }
+    del layer
+    torch.cuda.empty_cache()
+
+    if not args.no_fwd_bwd:
+        wb = WORKLOADS["mixtral_fwd_bwd"]
+        t0 = time.perf_counter()
+        inpb = make_inputs(wb, want_float=False)
+        log(f"inputs {wb.name}: {time.perf_counter() - t0:.1f} s")
+        lb = Layer(wb, inpb, backward=True)
+        msb = time_steps(lb, max(3, args.steps // 2), args.warmup)
+        flopb = 3.0 * wb.gemm_flop_fwd()
+        vb = flopb / (msb * 1e-3) / 1e12
+        log(f"fwd+bwd step {msb:.3f} ms -> {vb:.1f} TFLOP/s")
+        result["fwd_bwd"] = {"workload": "mixtral_fwd_bwd", "T": wb.T, "value": round(vb, 2), "unit": "TFLOP/s",
+                             "ms_per_step": round(msb, 4), "pct_of_bf16_peak": round(100 * vb / BF16_PEAK_TFLOPS, 2),
+                             "flop_per_step": flopb}
+        del lb, inpb
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds)
+        log(f"cpu baseline: {time.perf_counter() - t0:.1f} s")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

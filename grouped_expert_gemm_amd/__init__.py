@@ -21,7 +21,8 @@ from ._lib import MOE_BF16, MOE_F32, MOE_MXFP8, MlpDesc, MoeError, check, lib, p
 
 __all__ = [
     "moe_route_topk", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
-    "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "workspace_size", "MoeError", "lib",
+    "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu",
+    "workspace_size", "MoeError", "lib",
     "MOE_F32", "MOE_BF16", "MOE_MXFP8",
 ]
 
@@ -209,3 +210,53 @@ def moe_grouped_mlp_bwd(dy_perm, x_perm, z, h, prob_perm, w_gate_up, w_down, off
         d1, d2, _p(dprob), _p(ws), ws.numel(), _stream(dev)))
     del k1, k2, k3, k4
     return dx, dw1, dw2, dprob
+
+
+def moe_grouped_linear(x: torch.Tensor, w, offsets: torch.Tensor, out: torch.Tensor | None = None):
+    """GroupedLinear: y[r] = x[r] W_e^T for the rows of expert e. x [R, K], W_e [N, K] -> y [R, N]."""
+    ws = _experts(w)
+    E = len(ws)
+    N, K = ws[0].shape
+    R = x.shape[0]
+    _need_cuda(x, offsets, *ws)
+    y = out if out is not None else torch.empty((R, N), dtype=x.dtype, device=x.device)
+    t, keep = ptr_table([t.data_ptr() for t in ws])
+    check("moe_grouped_linear", lib().moe_grouped_linear(E, R, K, N, _DT[x.dtype], _p(x), t, _p(offsets), _p(y),
+                                                         _stream(x.device)))
+    del keep
+    return y
+
+
+def moe_grouped_gate_up_swiglu(x: torch.Tensor, w_gate_up, offsets: torch.Tensor, prob: torch.Tensor,
+                               save_z: bool = False, x_scale=None, w_scale=None, out: torch.Tensor | None = None,
+                               out_scale: torch.Tensor | None = None):
+    """GroupedLinear(gate_up) fused with ScaledSwiGLU: h = silu(x W_e[:I]^T) * (x W_e[I:]^T) * prob.
+
+    bf16/f32: returns h [R, I] (and z [R, 2I] with save_z). MXFP8 (x given as uint8 codes
+    with x_scale, weights as codes with w_scale): returns (h codes [R, I], h scales [R, I/32]).
+    """
+    ws = _experts(w_gate_up)
+    E = len(ws)
+    twoI, H = ws[0].shape
+    I = twoI // 2
+    R = x.shape[0]
+    dev = x.device
+    _need_cuda(x, offsets, prob, x_scale, *ws)
+    dt = _DT[x.dtype]
+    t, keep = ptr_table([t.data_ptr() for t in ws])
+    st = None
+    if dt == MOE_MXFP8:
+        st, keep2 = ptr_table([t.data_ptr() for t in _experts(w_scale)])
+        h = out if out is not None else torch.empty((R, I), dtype=torch.uint8, device=dev)
+        hs = out_scale if out_scale is not None else torch.empty((R, I // 32), dtype=torch.uint8, device=dev)
+        z = None
+    else:
+        h = out if out is not None else torch.empty((R, I), dtype=x.dtype, device=dev)
+        hs = None
+        z = torch.empty((R, twoI), dtype=x.dtype, device=dev) if save_z else None
+    check("moe_grouped_gate_up_swiglu", lib().moe_grouped_gate_up_swiglu(
+        E, R, H, I, dt, _p(x), _p(x_scale), t, st, _p(offsets), _p(prob), _p(h), _p(hs), _p(z), _stream(dev)))
+    del keep
+    if dt == MOE_MXFP8:
+        return h, hs
+    return (h, z) if save_z else h

@@ -19,7 +19,8 @@ MOE_MAX_EXPERTS = 256
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_route_topk", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
-    "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_workspace_size",
+    "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu",
+    "moe_workspace_size",
     "moe_status_str", "moe_last_error",
 )
 
@@ -58,6 +59,8 @@ def _declare(lib):
                                 sz, vp],
         "moe_grouped_mlp_bwd": [ctypes.POINTER(MlpDesc), i64, vp, vp, vp, vp, vp, PP, PP, vp, vp, PP, PP, vp,
                                 vp, sz, vp],
+        "moe_grouped_linear": [c_int, i64, c_int, c_int, c_int, vp, PP, vp, vp, vp],
+        "moe_grouped_gate_up_swiglu": [c_int, i64, c_int, c_int, c_int, vp, vp, PP, PP, vp, vp, vp, vp, vp, vp],
         "moe_workspace_size": [c_int, ctypes.POINTER(MlpDesc), i64, i64, c_int, c_int, ctypes.POINTER(sz)],
     }
     for name, args in sig.items():

@@ -8,10 +8,11 @@
 namespace moe {
 namespace gemm {
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kTileBytes = 256 * kBK * 2;     // one operand, one stage
+constexpr int kBM = 256, kBN = 256, kBK = 32;
+constexpr int kStages = 4;                    // LDS ring depth
+constexpr int kTileBytes = 256 * kBK * 2;     // one operand, one stage (16 KiB)
 constexpr int kStageBytes = 2 * kTileBytes;   // P and Q
-constexpr int kLdsBytes = 2 * kStageBytes;    // two stages
+constexpr int kLdsBytes = kStages * kStageBytes;
 
 enum { KCONTIG = 0, MNCONTIG = 1 };
 enum { GROUP_M = 0, GROUP_K = 1 };

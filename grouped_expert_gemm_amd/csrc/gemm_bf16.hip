@@ -20,16 +20,20 @@
 // Operand layouts: KCONTIG = rows of K-contiguous elements ([rows][K]); MNCONTIG =
 //   K is the row index and m/n is contiguous ([K][cols]); the loader transposes
 //   8x8 bf16 blocks in registers so LDS always holds [m or n][k].
-// Tiles: 256 x 256 x 64, 4 wavefronts (2 x 2), each 128 x 128 = 4 x 4 MFMA blocks
-//   held in 256 accumulator registers; 2 LDS stages of 64 KiB; one barrier per K
-//   step. LDS rows are 128 bytes (8 chunks of 16 bytes) and chunk c of row r lives
-//   at c ^ ((r ^ (r >> 3)) & 7), which keeps straight loads, transposed stores and
-//   MFMA fragment reads free of bank conflicts.
+// Tiles: 256 x 256 x 32 per K step, 4 wavefronts (2 x 2), each 128 x 128 = 4 x 4
+//   MFMA blocks held in 256 accumulator registers. LDS is a ring of 4 stages of
+//   32 KiB: K-contiguous operands are copied global -> LDS three steps ahead of the
+//   step being multiplied (partial vmcnt waits keep two steps in flight), which hides
+//   the latency of L2 misses; one barrier per K step. LDS rows are 64 bytes (4 chunks
+//   of 16 bytes) and chunk c of row r lives at c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3,
+//   which keeps MFMA fragment reads free of bank conflicts for 8- and 16-lane phases.
 // Scheduling: one workgroup per CU loops over tiles (persistent); tile ids are
 //   remapped so that each XCD (workgroup id mod 8) works on a contiguous run of
 //   tiles. Inside an expert, tiles run m-fastest, so a run covers a few weight
 //   panels and all of the expert's token panels, and concurrent runs share them
 //   through L2 and the Infinity Cache.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_bf16.h"
 #include "internal.h"
@@ -37,10 +41,10 @@
 namespace moe {
 namespace gemm {
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 __device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ swz(row)) << 4));
+  return (uint32_t)(row * 64 + ((chunk ^ swz(row)) << 4));
 }
 
 // column offset of MFMA sub-tile s (0..3) of wavefront column wn inside the 256-wide
@@ -51,34 +55,64 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// 8 rows (k) x 8 bf16 (mn) -> 8 vectors (mn) x 8 bf16 (k)
-__device__ __forceinline__ void transpose8(const uint4 in[8], uint4 out[8]) {
+// 4 rows (k) x 8 bf16 (mn) -> 8 vectors (mn) x 4 bf16 (k)
+__device__ __forceinline__ void transpose4x8(const uint4 in[4], uint2 out[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
     uint32_t w[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint4 a = in[2 * p], b = in[2 * p + 1];
-      const uint32_t wa = (j >> 1) == 0 ? a.x : (j >> 1) == 1 ? a.y : (j >> 1) == 2 ? a.z : a.w;
-      const uint32_t wb = (j >> 1) == 0 ? b.x : (j >> 1) == 1 ? b.y : (j >> 1) == 2 ? b.z : b.w;
-      w[p] = perm(wb, wa, sel);
+    for (int i = 0; i < 4; ++i) {
+      const uint4 a = in[i];
+      w[i] = (j >> 1) == 0 ? a.x : (j >> 1) == 1 ? a.y : (j >> 1) == 2 ? a.z : a.w;
     }
-    out[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    out[j] = make_uint2(perm(w[1], w[0], sel), perm(w[3], w[2], sel));
   }
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// wait until this wavefront's global -> LDS copies have landed (vmcnt(0))
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): at most N of this wavefront's vector memory operations
+// (loads, including global -> LDS copies, which complete in issue order) outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+// Workgroup barrier for the K loop. LDS stores of this wavefront are waited for
+// (lgkmcnt(0)); global -> LDS copies are NOT: the caller has already waited for the
+// ones the next step reads (wait_vm_le), and the others must stay in flight, which
+// __syncthreads() would not allow (its fence drains every outstanding copy). The
+// signal fences keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ void wait_vm_le(int n) {  // n: a multiple of 4 in [0, 24]
+  switch (n) {
+    case 24: wait_vm<24>(); break;
+    case 20: wait_vm<20>(); break;
+    case 16: wait_vm<16>(); break;
+    case 12: wait_vm<12>(); break;
+    case 8: wait_vm<8>(); break;
+    case 4: wait_vm<4>(); break;
+    default: wait_vm<0>(); break;
+  }
+}
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
 template <int PL, int QL, int G, int EP>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(const Params prm) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  // one array per ring slot and operand: every LDS access below names its array at
+  // compile time, so the compiler can tell a copy into one slot from reads of another
+  // and does not serialise the copies in flight with the fragment reads
+  __shared__ __attribute__((aligned(1024))) uint8_t sP0[kTileBytes], sP1[kTileBytes], sP2[kTileBytes], sP3[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ0[kTileBytes], sQ1[kTileBytes], sQ2[kTileBytes], sQ3[kTileBytes];
   __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int32_t s_tstart[MOE_MAX_EXPERTS + 1];
 
@@ -122,8 +156,18 @@ void grouped_gemm_kernel(const Params prm) {
   const int nwg = gridDim.x;
   const int logical = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
 
-  uint8_t* const ldsP = lds;               // stage s at + s * kStageBytes
-  uint8_t* const ldsQ = lds + kTileBytes;
+  auto slotP = [&](auto S) -> uint8_t* {
+    if constexpr (S.value == 0) return sP0;
+    else if constexpr (S.value == 1) return sP1;
+    else if constexpr (S.value == 2) return sP2;
+    else return sP3;
+  };
+  auto slotQ = [&](auto S) -> uint8_t* {
+    if constexpr (S.value == 0) return sQ0;
+    else if constexpr (S.value == 1) return sQ1;
+    else if constexpr (S.value == 2) return sQ2;
+    else return sQ3;
+  };
 
   for (int t = logical; t < total; t += nwg) {
     // ---------------- tile decode ----------------
@@ -158,43 +202,43 @@ void grouped_gemm_kernel(const Params prm) {
     // ---------------- operand addressing ----------------
     // K-contiguous operands are copied global -> LDS directly (global_load_lds_dwordx4:
     // lane l of a wavefront lands at the wave's LDS base + 16 * l). Round i of wave w
-    // fills LDS rows i*32 + w*8 .. +8; lane l takes row + (l >> 3) and physical chunk
-    // l & 7, i.e. logical chunk (l & 7) ^ swz(row) of that row.
-    // MN-contiguous operands go through registers and an 8x8 transpose.
-    const int dma_row0 = wave * 8 + (lane >> 3);
+    // fills the 16 LDS rows starting at (i*4 + w) * 16; lane l takes row + (l >> 2) and
+    // physical chunk l & 3, i.e. logical chunk (l & 3) ^ swz(row) of that row.
+    // MN-contiguous operands go through registers and a 4x8 transpose.
+    const int dma_row0 = wave * 16 + (lane >> 2);
     const bf16_t* pbase;
     if constexpr (G == GROUP_M) pbase = reinterpret_cast<const bf16_t*>(prm.tab[e]);
     else pbase = prm.p;
     // KCONTIG: a uniform tile base plus, per round, this lane's 32-bit byte offset
     const char* p_tile = nullptr;
-    uint32_t p_off[8];
-    int64_t p_col = 0;       // MNCONTIG: this thread's 8-column chunk
+    uint32_t p_off[4];
+    int64_t p_col = 0;  // MNCONTIG: this thread's 8-column chunk
     if constexpr (PL == KCONTIG) {
       if constexpr (EP == EPI_SWIGLU) p_tile = reinterpret_cast<const char*>(pbase + (int64_t)nt * 128 * prm.p_ld);
       else p_tile = reinterpret_cast<const char*>(pbase + (int64_t)nt * kBN * prm.p_ld);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = i * 32 + dma_row0;
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 64 + dma_row0;
         int n;  // row of P relative to the tile base
         if constexpr (EP == EPI_SWIGLU) n = (r < 128) ? r : prm.I + (r - 128);
         else n = r;
-        p_off[i] = (uint32_t)(((int64_t)n * prm.p_ld + (((lane & 7) ^ swz(r)) * 8)) * 2);
+        p_off[i] = (uint32_t)(((int64_t)n * prm.p_ld + (((lane & 3) ^ swz(r)) * 8)) * 2);
       }
     } else {
       p_col = (int64_t)nt * kBN + (tid & 31) * 8;
     }
     const char* q_tile = nullptr;
-    uint32_t q_off[8];
+    uint32_t q_off[4];
     int64_t q_col = 0;
     if constexpr (QL == KCONTIG) {
       const int tile_row = row_beg + mt * kBM;
       q_tile = reinterpret_cast<const char*>(prm.q + (int64_t)tile_row * prm.q_ld);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = i * 32 + dma_row0;
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 64 + dma_row0;
         int row = tile_row + r;
         row = row < row_end ? row : row_end - 1;  // rows past the expert: any valid row, discarded
-        q_off[i] = (uint32_t)(((int64_t)(row - tile_row) * prm.q_ld + (((lane & 7) ^ swz(r)) * 8)) * 2);
+        q_off[i] = (uint32_t)(((int64_t)(row - tile_row) * prm.q_ld + (((lane & 3) ^ swz(r)) * 8)) * 2);
       }
     } else {
       q_col = (int64_t)mt * kBM + (tid & 31) * 8;
@@ -209,56 +253,68 @@ void grouped_gemm_kernel(const Params prm) {
       nk = (row_end - row_beg + kBK - 1) / kBK;
       kbeg = row_beg;
     }
-    const int kg = tid >> 5;  // MNCONTIG: k group of 8 rows
+    const int kg = tid >> 5;  // MNCONTIG: k group of 4 rows
 
-    uint4 pr[8], qr[8];
-    // start moving K step kt into LDS stage `stage`
-    auto issue_tile = [&](int kt, int stage) {
-      const int64_t k0 = (int64_t)kt * kBK;
+    constexpr int kDma = (PL == KCONTIG ? 4 : 0) + (QL == KCONTIG ? 4 : 0);  // copies per stage per lane
+    constexpr bool kReg = PL == MNCONTIG || QL == MNCONTIG;
+
+    // global -> LDS copies of K step kt into ring slot S (= kt % kStages)
+    auto issue_dma = [&](int kt, auto S) {
+      const int64_t k0b = (int64_t)kt * kBK * 2;
       if constexpr (PL == KCONTIG) {
-        uint8_t* P = ldsP + stage * kStageBytes + (wave * 8) * 128;
+        uint8_t* P = slotP(S) + wave * 1024;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          __builtin_amdgcn_global_load_lds((const void*)(p_tile + k0 * 2 + p_off[i]), (lds_ptr_t)(P + i * 32 * 128), 16, 0, 0);
-      } else {
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_global_load_lds((const void*)(p_tile + k0b + p_off[i]), (lds_ptr_t)(P + i * 4096), 16, 0, 0);
+      }
+      if constexpr (QL == KCONTIG) {
+        uint8_t* Q = slotQ(S) + wave * 1024;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int64_t kr = kbeg + k0 + kg * 8 + i;
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_global_load_lds((const void*)(q_tile + k0b + q_off[i]), (lds_ptr_t)(Q + i * 4096), 16, 0, 0);
+      }
+    };
+    uint4 pr[4], qr[4];
+    // register loads of K step kt for the MN-contiguous operands
+    auto load_regs = [&](int kt) {
+      const int64_t k0 = (int64_t)kt * kBK;
+      if constexpr (PL == MNCONTIG) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t kr = kbeg + k0 + kg * 4 + i;
           bool ok = true;
           if constexpr (G == GROUP_K) ok = kr < row_end;
           pr[i] = ok ? *reinterpret_cast<const uint4*>(pbase + kr * prm.p_ld + p_col) : make_uint4(0, 0, 0, 0);
         }
       }
-      if constexpr (QL == KCONTIG) {
-        uint8_t* Q = ldsQ + stage * kStageBytes + (wave * 8) * 128;
+      if constexpr (QL == MNCONTIG) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          __builtin_amdgcn_global_load_lds((const void*)(q_tile + k0 * 2 + q_off[i]), (lds_ptr_t)(Q + i * 32 * 128), 16, 0, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int64_t kr = kbeg + k0 + kg * 8 + i;
+        for (int i = 0; i < 4; ++i) {
+          const int64_t kr = kbeg + k0 + kg * 4 + i;
           bool ok = true;
           if constexpr (G == GROUP_K) ok = kr < row_end;
           qr[i] = ok ? *reinterpret_cast<const uint4*>(prm.q + kr * prm.q_ld + q_col) : make_uint4(0, 0, 0, 0);
         }
       }
     };
-    // finish the register-staged (transposed) operands of stage `stage`
-    auto commit_tile = [&](int stage) {
+    // transpose the register-staged operands of K step kt and write them to LDS
+    auto commit_regs = [&](auto S) {
+      const uint32_t sub = (uint32_t)((kg & 1) * 8);
       if constexpr (PL == MNCONTIG) {
-        uint8_t* P = ldsP + stage * kStageBytes;
-        uint4 tr[8];
-        transpose8(pr, tr);
+        uint8_t* P = slotP(S);
+        uint2 tr[8];
+        transpose4x8(pr, tr);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(P + lds_off((tid & 31) * 8 + j, kg)) = tr[j];
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint2*>(P + lds_off((tid & 31) * 8 + j, kg >> 1) + sub) = tr[j];
       }
       if constexpr (QL == MNCONTIG) {
-        uint8_t* Q = ldsQ + stage * kStageBytes;
-        uint4 tr[8];
-        transpose8(qr, tr);
+        uint8_t* Q = slotQ(S);
+        uint2 tr[8];
+        transpose4x8(qr, tr);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(Q + lds_off((tid & 31) * 8 + j, kg)) = tr[j];
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint2*>(Q + lds_off((tid & 31) * 8 + j, kg >> 1) + sub) = tr[j];
       }
     };
 
@@ -270,51 +326,120 @@ void grouped_gemm_kernel(const Params prm) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-    if (nk > 0) {
-      issue_tile(0, 0);
-      commit_tile(0);
-    }
-    wait_vmem();
-    __syncthreads();
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
 
     const int l32 = lane & 31, lhi = lane >> 5;
-    // Fragment addresses. Sub-tile s of either operand starts at a row that is a
-    // multiple of 32, odd multiples for odd s, so swz(row) = swz(l32) ^ 4 * (s & 1);
-    // the rest of the row offset is a compile-time constant per s.
-    const uint32_t fragP = (uint32_t)((wn * 64 + l32) * 128);
-    const uint32_t fragQ = (uint32_t)((wm * 128 + l32) * 128);
-    const int sw = swz(l32);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) issue_tile(kt + 1, cur ^ 1);
-      const uint8_t* P = ldsP + cur * kStageBytes + fragP;
-      const uint8_t* Q = ldsQ + cur * kStageBytes + fragQ;
-      bf16x8 fa[2][4], fb[2][4];
-      auto load_frags = [&](int kk, int buf) {
-        const uint32_t c0 = (uint32_t)(((kk * 2 + lhi) ^ sw) << 4);
-        const uint32_t c1 = c0 ^ 64u;
+    // Fragment addresses: sub-tile rows start at multiples of 32, where swz depends on
+    // the lane's row within the sub-tile only; the rest of the offset is a constant.
+    const uint32_t fragP = (uint32_t)((wn * 64 + l32) * 64);
+    const uint32_t fragQ = (uint32_t)((wm * 128 + l32) * 64);
+    const uint32_t ck0 = (uint32_t)(((0 * 2 + lhi) ^ swz(l32)) << 4);
+    const uint32_t ck1 = (uint32_t)(((1 * 2 + lhi) ^ swz(l32)) << 4);
+    // fragments of one k16 slice: 4 of P (n sub-tiles), 4 of Q (m sub-tiles)
+    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    auto read_slice = [&](auto S, uint32_t ck, bf16x8* fa, bf16x8* fb) {
+      const uint8_t* P = slotP(S) + fragP + ck;
+      const uint8_t* Q = slotQ(S) + fragQ + ck;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          fa[buf][s] = *reinterpret_cast<const bf16x8*>(P + ((s >> 1) * 128 + (s & 1) * 32) * 128 + ((s & 1) ? c1 : c0));
+      for (int t = 0; t < 4; ++t) fa[t] = *reinterpret_cast<const bf16x8*>(P + ((t >> 1) * 128 + (t & 1) * 32) * 64);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          fb[buf][s] = *reinterpret_cast<const bf16x8*>(Q + (s * 32) * 128 + ((s & 1) ? c1 : c0));
-      };
-      load_frags(0, 0);
+      for (int t = 0; t < 4; ++t) fb[t] = *reinterpret_cast<const bf16x8*>(Q + (t * 32) * 64);
+    };
+    auto mfma_slice = [&](const bf16x8* fa, const bf16x8* fb) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if (kk < 3) load_frags(kk + 1, (kk + 1) & 1);
+      for (int sn = 0; sn < 4; ++sn)
 #pragma unroll
-        for (int sn = 0; sn < 4; ++sn)
+        for (int sm = 0; sm < 4; ++sm)
+          acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sn], fb[sm], acc[sn][sm], 0, 0, 0);
+    };
+    // 16 MFMAs with the 8 fragment reads of another slice threaded between them
+    auto interleave = [&]() {
 #pragma unroll
-          for (int sm = 0; sm < 4; ++sm)
-            acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][sn], fb[kk & 1][sm], acc[sn][sm], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      if (kt + 1 < nk) commit_tile(cur ^ 1);
-      wait_vmem();
-      __syncthreads();
+    };
+
+    // prologue: register loads of step 0, copies of steps 0..3, then step 1's registers
+    if (nk > 0) {
+      if constexpr (kReg) load_regs(0);
+      if constexpr (kDma > 0) {
+        issue_dma(0, S0{});
+        if (nk > 1) issue_dma(1, S1{});
+        if (nk > 2) issue_dma(2, S2{});
+        if (nk > 3) issue_dma(3, S3{});
+      }
+      const int later = (nk > 1) + (nk > 2) + (nk > 3);
+      wait_vm_le(later * kDma);  // step 0 complete
+      if constexpr (kReg) {
+        commit_regs(S0{});
+        if (nk > 1) load_regs(1);
+      }
     }
+    lds_barrier();
+    if (nk > 0) read_slice(S0{}, ck0, fa0, fb0);
+
+    // K step kt on ring slot S. On entry the first k16 slice of step kt is in fa0/fb0.
+    //   phase A: its 16 MFMAs while the second slice is read into fa1/fb1; then wait for
+    //            step kt+1 (copies, or register loads that are then written to LDS) and
+    //            meet at the barrier;
+    //   phase B: slot S is free now: start step kt+4's copies into it (register loads of
+    //            step kt+2 first), then the second slice's 16 MFMAs while step kt+1's
+    //            first slice is read into fa0/fb0.
+    // Copies land 3 steps after they are issued; vmcnt counts loads in issue order.
+    // FULL: steps kt+1..kt+4 all exist, so every branch below folds away and the step
+    // is one basic block the scheduler can interleave.
+    auto kstep = [&](int kt, auto S, auto FULL) {
+      constexpr int s = decltype(S)::value;
+      constexpr bool full = decltype(FULL)::value;
+      using SN = std::integral_constant<int, (s + 1) & 3>;
+      read_slice(S, ck1, fa1, fb1);
+      mfma_slice(fa0, fb0);
+      interleave();
+      if (kReg && (full || kt + 1 < nk)) {
+        wait_vm_le((full || kt + 3 < nk) ? kDma : 0);
+        commit_regs(SN{});
+      } else {
+        wait_vm_le(full ? 2 * kDma : ((kt + 2 < nk) + (kt + 3 < nk)) * kDma);
+      }
+      lds_barrier();
+      if (kReg && (full || kt + 2 < nk)) load_regs(kt + 2);
+      if constexpr (kDma > 0) {
+        if (full || kt + 4 < nk) issue_dma(kt + 4, S);
+      }
+      if (full || kt + 1 < nk) read_slice(SN{}, ck0, fa0, fb0);
+      mfma_slice(fa1, fb1);
+      // copies and next-slice reads threaded between the MFMAs, so the wavefront never
+      // waits behind a burst of copy instructions while the matrix core idles
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+    using Full = std::true_type;
+    using Tail = std::false_type;
+    int kt = 0;
+    for (; kt + 7 < nk; kt += 4) {  // steady state: kt+7 < nk covers the copies of all four steps
+      kstep(kt, S0{}, Full{});
+      kstep(kt + 1, S1{}, Full{});
+      kstep(kt + 2, S2{}, Full{});
+      kstep(kt + 3, S3{}, Full{});
+    }
+    for (; kt < nk; kt += 4) {
+      kstep(kt, S0{}, Tail{});
+      if (kt + 1 < nk) kstep(kt + 1, S1{}, Tail{});
+      if (kt + 2 < nk) kstep(kt + 2, S2{}, Tail{});
+      if (kt + 3 < nk) kstep(kt + 3, S3{}, Tail{});
+    }
+    // all waves are done with every slot before the next tile's prologue copies
+    lds_barrier();
 
     // ---------------- epilogue ----------------
 #pragma unroll

@@ -11,6 +11,11 @@ struct PtrTab {
 
 namespace f32 {
 
+moe_status gate_up(int E, int64_t R, int H, int I, const float* x, const PtrTab& w1, const int32_t* off,
+                   const float* prob, float* h, float* z, hipStream_t s);
+moe_status linear(int E, int64_t R, int K, int N, const float* x, const PtrTab& w, const int32_t* off, float* y,
+                  hipStream_t s);
+
 moe_status forward(const moe_mlp_desc& d, int64_t R, const float* x, const PtrTab& w1, const PtrTab& w2,
                    const int32_t* off, const float* prob, float* y, float* z, float* h, hipStream_t s);
 

@@ -119,6 +119,20 @@ __global__ __launch_bounds__(256) void wgrad(const float* __restrict__ a, int ld
 
 static unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
+moe_status gate_up(int E, int64_t R, int H, int I, const float* x, const PtrTab& w1, const int32_t* off,
+                   const float* prob, float* h, float* z, hipStream_t s) {
+  if (R == 0) return MOE_OK;
+  hipLaunchKernelGGL(gateup_swiglu, dim3(blocks_for(R * I)), dim3(256), 0, s, x, w1, off, prob, R, E, H, I, h, z);
+  return check_launch("grouped gate_up + ScaledSwiGLU (f32)");
+}
+
+moe_status linear(int E, int64_t R, int K, int N, const float* x, const PtrTab& w, const int32_t* off, float* y,
+                  hipStream_t s) {
+  if (R == 0) return MOE_OK;
+  hipLaunchKernelGGL(rows_times_wt, dim3(blocks_for(R * N)), dim3(256), 0, s, x, w, off, R, E, N, K, y);
+  return check_launch("grouped linear (f32)");
+}
+
 moe_status forward(const moe_mlp_desc& d, int64_t R, const float* x, const PtrTab& w1, const PtrTab& w2,
                    const int32_t* off, const float* prob, float* y, float* z, float* h, hipStream_t s) {
   if (R == 0) return MOE_OK;

@@ -11,5 +11,10 @@ moe_status forward(const moe_mlp_desc& d, int64_t R, const void* x_perm, const u
                    const uint8_t* const* w_down_scale, const int32_t* offsets, const float* prob_perm,
                    void* y_perm, uint8_t* workspace, hipStream_t s);
 
+// MXFP8 gate_up + ScaledSwiGLU on pre-quantised operands; h written as MXFP8
+moe_status gate_up(int E, int64_t R, int H, int I, const uint8_t* x, const uint8_t* x_scale, const void* const* w,
+                   const uint8_t* const* w_scale, const int32_t* offsets, const float* prob, uint8_t* h,
+                   uint8_t* h_scale, hipStream_t s);
+
 }  // namespace mx
 }  // namespace moe

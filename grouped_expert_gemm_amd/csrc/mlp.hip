@@ -93,6 +93,53 @@ __global__ __launch_bounds__(256) void reduce_partials(const float* __restrict__
   out[r] = s;
 }
 
+// bf16 GroupedLinear(gate_up) + ScaledSwiGLU: h [R, I] (and z [R, 2I] when z != NULL)
+static moe_status bf16_gate_up(int E, int64_t R, int H, int I, const bf16_t* x, const PtrTab& w,
+                               const int32_t* offsets, const float* prob, bf16_t* h, bf16_t* z, hipStream_t s) {
+  gemm::Params p;
+  std::memset(&p, 0, sizeof(p));
+  std::memcpy(p.tab, w.p, sizeof(p.tab));
+  p.q = x;
+  p.q_ld = H;
+  p.p_ld = H;
+  p.c = h;
+  p.c_ld = I;
+  p.offsets = offsets;
+  p.prob = prob;
+  p.zout = z;
+  p.R = R;
+  p.N = 2 * I;
+  p.K = H;
+  p.E = E;
+  p.I = I;
+  p.n_tiles = I / 128;
+  const int64_t mtiles = (R + gemm::kBM - 1) / gemm::kBM + E;
+  return gemm::run(p, gemm::KCONTIG, gemm::KCONTIG, gemm::GROUP_M, gemm::EPI_SWIGLU, mtiles * p.n_tiles, s,
+                   "grouped gate_up + ScaledSwiGLU");
+}
+
+// bf16 GroupedLinear: y [R, N] = x [R, K] W_e^T
+static moe_status bf16_linear(int E, int64_t R, int K, int N, const bf16_t* x, const PtrTab& w,
+                              const int32_t* offsets, bf16_t* y, hipStream_t s) {
+  gemm::Params q;
+  std::memset(&q, 0, sizeof(q));
+  std::memcpy(q.tab, w.p, sizeof(q.tab));
+  q.q = x;
+  q.q_ld = K;
+  q.p_ld = K;
+  q.c = y;
+  q.c_ld = N;
+  q.offsets = offsets;
+  q.R = R;
+  q.N = N;
+  q.K = K;
+  q.E = E;
+  q.n_tiles = N / gemm::kBN;
+  const int64_t mtiles = (R + gemm::kBM - 1) / gemm::kBM + E;
+  return gemm::run(q, gemm::KCONTIG, gemm::KCONTIG, gemm::GROUP_M, gemm::EPI_STORE, mtiles * q.n_tiles, s,
+                   "grouped linear");
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -146,45 +193,62 @@ extern "C" moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, c
 
   // bf16: gate_up + ScaledSwiGLU (h, optionally z), then down
   bf16_t* h = d.save_for_bwd ? (bf16_t*)h_save : (bf16_t*)workspace;
-  gemm::Params p;
-  std::memset(&p, 0, sizeof(p));
-  std::memcpy(p.tab, w1.p, sizeof(p.tab));
-  p.q = (const bf16_t*)x_perm;
-  p.q_ld = d.H;
-  p.p_ld = d.H;
-  p.c = h;
-  p.c_ld = d.I;
-  p.offsets = offsets;
-  p.prob = prob_perm;
-  p.zout = d.save_for_bwd ? (bf16_t*)z_save : nullptr;
-  p.R = R;
-  p.N = 2 * d.I;
-  p.K = d.H;
-  p.E = d.E;
-  p.I = d.I;
-  p.n_tiles = d.I / 128;
-  const int64_t mtiles = (R + gemm::kBM - 1) / gemm::kBM + d.E;
-  st = gemm::run(p, gemm::KCONTIG, gemm::KCONTIG, gemm::GROUP_M, gemm::EPI_SWIGLU, mtiles * p.n_tiles, s,
-                 "moe_grouped_mlp_fwd(gate_up)");
+  st = bf16_gate_up(d.E, R, d.H, d.I, (const bf16_t*)x_perm, w1, offsets, prob_perm, h,
+                    d.save_for_bwd ? (bf16_t*)z_save : nullptr, s);
   if (st != MOE_OK) return st;
+  return bf16_linear(d.E, R, d.I, d.H, h, w2, offsets, (bf16_t*)y_perm, s);
+}
 
-  gemm::Params q;
-  std::memset(&q, 0, sizeof(q));
-  std::memcpy(q.tab, w2.p, sizeof(q.tab));
-  q.q = h;
-  q.q_ld = d.I;
-  q.p_ld = d.I;
-  q.c = (bf16_t*)y_perm;
-  q.c_ld = d.H;
-  q.offsets = offsets;
-  q.R = R;
-  q.N = d.H;
-  q.K = d.I;
-  q.E = d.E;
-  q.I = d.I;
-  q.n_tiles = d.H / gemm::kBN;
-  return gemm::run(q, gemm::KCONTIG, gemm::KCONTIG, gemm::GROUP_M, gemm::EPI_STORE, mtiles * q.n_tiles, s,
-                   "moe_grouped_mlp_fwd(down)");
+extern "C" moe_status moe_grouped_linear(int E, int64_t R, int K, int N, moe_dtype dt, const void* x,
+                                         const void* const* w, const int32_t* offsets, void* y, void* stream) {
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_linear: E out of [1, 256]");
+  if (R < 0 || R > 0x7FFFFFFF || K < 1 || N < 1) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_linear: bad R/K/N");
+  if (dt != MOE_BF16 && dt != MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_linear: dtype must be BF16 or F32");
+  if (dt == MOE_BF16 && (N % 256 != 0 || K % 64 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_linear: bf16 needs N % 256 == 0 and K % 64 == 0");
+  if ((int64_t)N * K * 2 > 0x7FFFFFFFLL) return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_linear: weight exceeds 2^31 bytes");
+  if (R == 0) return MOE_OK;
+  const size_t align = dt == MOE_F32 ? 4 : 16;
+  if (!x || !y || !offsets) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_linear: NULL pointer");
+  if (!aligned(x, align) || !aligned(y, align)) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_linear: misaligned tensor");
+  moe_status st = check_table(w, E, align, "moe_grouped_linear(w)");
+  if (st != MOE_OK) return st;
+  const PtrTab tab = make_tab(w, E);
+  const hipStream_t s = as_stream(stream);
+  if (dt == MOE_F32) return f32::linear(E, R, K, N, (const float*)x, tab, offsets, (float*)y, s);
+  return bf16_linear(E, R, K, N, (const bf16_t*)x, tab, offsets, (bf16_t*)y, s);
+}
+
+extern "C" moe_status moe_grouped_gate_up_swiglu(int E, int64_t R, int H, int I, moe_dtype dt, const void* x,
+                                                 const uint8_t* x_scale, const void* const* w,
+                                                 const uint8_t* const* w_scale, const int32_t* offsets,
+                                                 const float* prob, void* h, uint8_t* h_scale, void* z_save,
+                                                 void* stream) {
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gate_up_swiglu: E out of [1, 256]");
+  if (R < 0 || R > 0x7FFFFFFF || H < 1 || I < 1) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gate_up_swiglu: bad R/H/I");
+  if (dt != MOE_BF16 && dt != MOE_F32 && dt != MOE_MXFP8)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gate_up_swiglu: bad dtype");
+  if (dt != MOE_F32 && (H % 256 != 0 || I % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_gate_up_swiglu: needs H % 256 == 0 and I % 128 == 0");
+  if ((int64_t)2 * I * H * 2 > 0x7FFFFFFFLL) return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_gate_up_swiglu: weight exceeds 2^31 bytes");
+  if (dt == MOE_MXFP8 && z_save) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gate_up_swiglu: z_save needs BF16 or F32");
+  if (R == 0) return MOE_OK;
+  const size_t align = dt == MOE_F32 ? 4 : 16;
+  if (!x || !h || !offsets || !prob) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gate_up_swiglu: NULL pointer");
+  if (!aligned(x, align) || !aligned(h, align) || (z_save && !aligned(z_save, align)))
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gate_up_swiglu: misaligned tensor");
+  moe_status st = check_table(w, E, align, "moe_grouped_gate_up_swiglu(w)");
+  if (st != MOE_OK) return st;
+  const hipStream_t s = as_stream(stream);
+  const PtrTab tab = make_tab(w, E);
+  if (dt == MOE_MXFP8) {
+    if (!x_scale || !h_scale) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gate_up_swiglu: MXFP8 needs x_scale and h_scale");
+    if ((st = check_table((const void* const*)w_scale, E, 4, "moe_grouped_gate_up_swiglu(w_scale)")) != MOE_OK) return st;
+    return mx::gate_up(E, R, H, I, (const uint8_t*)x, x_scale, w, w_scale, offsets, prob, (uint8_t*)h, h_scale, s);
+  }
+  if (dt == MOE_F32)
+    return f32::gate_up(E, R, H, I, (const float*)x, tab, offsets, prob, (float*)h, (float*)z_save, s);
+  return bf16_gate_up(E, R, H, I, (const bf16_t*)x, tab, offsets, prob, (bf16_t*)h, (bf16_t*)z_save, s);
 }
 
 extern "C" moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, const void* dy_perm,

@@ -185,6 +185,36 @@ moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, const void* 
                                float* dprob_perm, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/*
+ * GroupedLinear: one grouped GEMM submission over all local experts. Source:
+ * "Efficient MoE Training for Biological Foundation Models", Challenge 1 (GroupedLinear
+ * applies each expert's linear map to that expert's rows in one call, with per-expert
+ * token counts; bias=False).
+ *   y[r] = x[r] W_e^T  for r in [offsets[e], offsets[e+1]), float32 accumulation
+ *   x [R, K], W_e [N, K] ([host] array of E device pointers), y [R, N]; dt = F32 or BF16
+ *   (bf16 output rounded to nearest even).
+ * Shapes the kernels implement: BF16 needs N % 256 == 0 and K % 64 == 0.
+ */
+moe_status moe_grouped_linear(int E, int64_t R, int K, int N, moe_dtype dt, const void* x,
+                              const void* const* w, const int32_t* offsets, void* y, void* stream);
+
+/*
+ * GroupedLinear(gate_up) fused with ScaledSwiGLU (the first kernel of the fused grouped
+ * MLP, Challenge 3 and Figure 4). For the rows r of expert e:
+ *   z = x[r] W_e^T (2I values),  h[r] = silu(z[0:I]) * z[I:2I] * prob[r]
+ *   x [R, H], W_e [2I, H] ([host] array of E device pointers), prob [R] float32,
+ *   h [R, I] (out), z_save [R, 2I] (out, may be NULL); dt = F32 or BF16.
+ * With dt = MXFP8, x holds E4M3 codes with x_scale [R, H/32], W_e codes with
+ * w_scale[e] [2I, H/32], and h is written as E4M3 codes with h_scale [R, I/32]
+ * (quantised from the float32 value of h by the rule of mxfp8_quantize); z_save must
+ * be NULL. Shapes: H % 256 == 0 and I % 128 == 0 (BF16, MXFP8).
+ */
+moe_status moe_grouped_gate_up_swiglu(int E, int64_t R, int H, int I, moe_dtype dt, const void* x,
+                                      const uint8_t* x_scale, const void* const* w,
+                                      const uint8_t* const* w_scale, const int32_t* offsets,
+                                      const float* prob, void* h, uint8_t* h_scale, void* z_save,
+                                      void* stream);
+
 /* Operations for moe_workspace_size. */
 typedef enum {
   MOE_OP_PERMUTE = 0,  /* T = token count, E, k used; desc may be NULL */
