@@ -1,0 +1,107 @@
+"""GPU parity of the MXFP8 grouped MLP forward against the oracle's MXFP8-emulated
+reference (quantise -> dequantise around both GEMMs): tolerance 6e-2 on y.
+The fused path quantises bf16 activations and master weights inside the call; the
+pre-quantised path takes E4M3 codes + E8M0 scales made by mxfp8_quantize (bit-exact
+with the oracle's quantiser)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import max_rel_err
+from moe_inputs import WORKLOADS, bf16_bits_to_f32, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+MX_TOL = 6e-2
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_expert_gemm_amd as g
+    g.lib()
+    return g
+
+
+from gpu_util import dev_bf16, dev_f32, host, oracle_perm  # noqa: E402
+
+SHAPES = [
+    # name, T, H, I, E, k, zipf, empty experts
+    ("ragged", 1500, 512, 512, 4, 2, 0.0, ()),
+    ("skewed_empty", 900, 256, 256, 16, 4, 1.2, (2, 7)),
+]
+
+
+def _setup(name, T, H, I, E, k, zipf, empty):
+    w = scaled(WORKLOADS["mixtral_mxfp8_fwd"], T=T, H=H, I=I, E=E, k=k, zipf=zipf, seed=31)
+    inp = make_inputs(w)
+    if empty:
+        inp.logits[:, list(empty)] -= 100.0
+    idx, p, m, pp = oracle_perm(inp, k, E)
+    for e in empty:
+        assert m["split_sizes"][e] == 0
+    return w, inp, m, pp
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_mxfp8_fused_forward(moe, shape):
+    w, inp, m, pp = _setup(*shape)
+    xp = dev_bf16(inp.bits["x"][m["src_token"]])
+    off = torch.from_numpy(m["offsets"].astype(np.int32)).cuda()
+    print(f"mxfp8 fwd {shape[0]}: R={w.R} H={w.H} I={w.I} E={w.E}", flush=True)
+    y = moe.moe_grouped_mlp_fwd(xp, dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"]), off,
+                                dev_f32(pp.astype(np.float32)), compute="mxfp8")
+    torch.cuda.synchronize()
+    ref, _ = oracle.grouped_mlp_forward_mxfp8(inp.x[m["src_token"]], inp.w1, inp.w2, m["offsets"], pp)
+    err = max_rel_err(host(y), ref)
+    print(f"  max rel err {err:.3e}")
+    assert err <= MX_TOL
+
+
+def test_mxfp8_prequantised_operands_and_h(moe):
+    w, inp, m, pp = _setup(*SHAPES[0])
+    E, H, I = w.E, w.H, w.I
+    xp_bits = inp.bits["x"][m["src_token"]]
+    xq, xs = moe.mxfp8_quantize(dev_bf16(xp_bits))
+    w1q, w1s = moe.mxfp8_quantize(dev_bf16(inp.bits["w1"]).reshape(E * 2 * I, H))
+    w2q, w2s = moe.mxfp8_quantize(dev_bf16(inp.bits["w2"]).reshape(E * H, I))
+    w1q, w1s = w1q.reshape(E, 2 * I, H), w1s.reshape(E, 2 * I, H // 32)
+    w2q, w2s = w2q.reshape(E, H, I), w2s.reshape(E, H, I // 32)
+    off = torch.from_numpy(m["offsets"].astype(np.int32)).cuda()
+    prob = dev_f32(pp.astype(np.float32))
+    # quantised operands are bit-exact with the oracle's quantiser
+    rxq, rxs = oracle.mxfp8_quantize(bf16_bits_to_f32(xp_bits))
+    assert np.array_equal(xq.cpu().numpy(), rxq) and np.array_equal(xs.cpu().numpy(), rxs)
+    # gate_up + ScaledSwiGLU with h quantised in the epilogue
+    hq, hs = moe.moe_grouped_gate_up_swiglu(xq, w1q, off, prob, x_scale=xs, w_scale=w1s)
+    torch.cuda.synchronize()
+    x_dq = oracle.mxfp8_dequantize(rxq, rxs)
+    w1_dq = np.stack([oracle.mxfp8_qdq(inp.w1[e]) for e in range(E)])
+    _, _, h_ref = oracle.grouped_mlp_forward(x_dq, w1_dq, np.zeros((E, H, I)), m["offsets"], pp)
+    rhq, rhs = oracle.mxfp8_quantize(h_ref)
+    g_codes, g_scales = hq.cpu().numpy(), hs.cpu().numpy()
+    # The GPU rounds h from the matrix core's float32 sums, the oracle from float64.
+    # Elements that nearly cancel carry a sum error that is large next to themselves but
+    # tiny next to their block's maximum, which sets the block's scale: so codes may
+    # differ (rarely), and each difference stays within one E4M3 step of the top binade
+    # of its block (2^-3 of the block maximum).
+    assert (g_scales != rhs).mean() < 1e-2
+    diff = g_codes != rhq
+    print(f"  h codes differing: {diff.mean():.2e}, scales differing: {(g_scales != rhs).mean():.2e}")
+    assert diff.mean() < 1e-2
+    gv = oracle.mxfp8_dequantize(g_codes, g_scales)
+    rv = oracle.mxfp8_dequantize(rhq, rhs)
+    R = gv.shape[0]
+    bmax = np.abs(rv).reshape(R, -1, 32).max(axis=2)
+    bdiff = np.abs(gv - rv).reshape(R, -1, 32).max(axis=2)
+    assert np.all(bdiff <= 2.0 ** -3 * bmax)
+    assert max_rel_err(gv, rv) <= MX_TOL
+    # the whole forward on pre-quantised operands equals the fused path
+    y_pre = moe.moe_grouped_mlp_fwd(xq, w1q, w2q, off, prob, compute="mxfp8", x_perm_scale=xs,
+                                    w_gate_up_scale=w1s, w_down_scale=w2s)
+    y_fused = moe.moe_grouped_mlp_fwd(dev_bf16(xp_bits), dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"]),
+                                      off, prob, compute="mxfp8")
+    torch.cuda.synchronize()
+    assert torch.equal(y_pre, y_fused)
