@@ -147,6 +147,63 @@ def time_steps(layer, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
+
+
+def extra_forward(w, inp, steps, warmup, compute="bf16", prequant=False):
+    """One forward layer step through the Python binding (route, permute, grouped MLP,
+    combine) on another workload or precision; returns its throughput record."""
+    import numpy as np
+    import torch
+
+    import grouped_expert_gemm_amd as moe
+
+    dev_logits = torch.from_numpy(inp.logits).cuda()
+    x = dev_bf16(torch, np, inp.bits["x"])
+    w1 = dev_bf16(torch, np, inp.bits["w1"])
+    w2 = dev_bf16(torch, np, inp.bits["w2"])
+    s1 = s2 = None
+    if prequant:
+        # master weights quantised once, outside the timed steps
+        E, twoI, H = w1.shape
+        q1, s1 = moe.mxfp8_quantize(w1.reshape(E * twoI, H))
+        q2, s2 = moe.mxfp8_quantize(w2.reshape(E * H, w.I))
+        w1, s1 = q1.reshape(E, twoI, H), s1.reshape(E, twoI, H // 32)
+        w2, s2 = q2.reshape(E, H, w.I), s2.reshape(E, H, w.I // 32)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+
+    def step():
+        nonlocal ws
+        idx, p = moe.moe_route_topk(dev_logits, w.k)
+        r = moe.moe_permute(x, idx, p, w.E)
+        y = moe.moe_grouped_mlp_fwd(r["x_perm"], w1, w2, r["offsets"], r["prob_perm"], compute=compute,
+                                    w_gate_up_scale=s1, w_down_scale=s2, workspace=ws)
+        moe.moe_unpermute_combine(y, r["row_id_map"], w.T, w.k)
+
+    from grouped_expert_gemm_amd import _lib
+    desc = _lib.MlpDesc(w.E, w.H, w.I, moe._COMPUTE[compute], _lib.MOE_BF16,
+                        _lib.MOE_MXFP8 if prequant else _lib.MOE_BF16, 0)
+    ws = torch.empty(max(1, moe.workspace_size(_lib.MOE_OP_MLP_FWD, desc, w.R)), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    v = w.gemm_flop_fwd() / (ms * 1e-3) / 1e12
+    peak = FP8_PEAK_TFLOPS if compute == "mxfp8" else BF16_PEAK_TFLOPS
+    rec = {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k, "compute": compute,
+           "value": round(v, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
+           "pct_of_peak": round(100 * v / peak, 2), "peak": peak}
+    if compute == "mxfp8":
+        rec["weights"] = ("MXFP8, quantised once outside the step" if prequant
+                          else "bf16 master weights, quantised inside every step")
+    log(f"{w.name} {compute}{' prequant' if prequant else ''}: {ms:.3f} ms -> {v:.1f} TFLOP/s")
+    return rec
+
+
 def traffic_record():
     """HBM bytes per gate_up launch from the committed rocprofv3 counter runs, or None
     if they were taken on a different version of the kernel source."""
@@ -161,8 +218,9 @@ def traffic_record():
 
 
 def cpu_baseline(inp, w, seconds):
-    """The oracle (float64 numpy, per-expert loop) on the first rows of expert 0 of the
-    same workload, sized to take roughly `seconds` of host time."""
+    """The oracle (float64 numpy, per-expert loop) on the same workload, expert by expert
+    in index order until about `seconds` of host time have passed (at least one expert):
+    route, permute, then the grouped MLP of each expert on all of its rows."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -171,26 +229,28 @@ def cpu_baseline(inp, w, seconds):
 
     idx, p = oracle.route_topk(inp.logits, w.k)
     m = oracle.permute(idx, w.E)
-    rows = m["src_token"][m["offsets"][0]:m["offsets"][1]]
-    pp = p.ravel()[m["src_token"] * w.k + m["src_slot"]][m["offsets"][0]:m["offsets"][1]]
-    w1 = bf16_bits_to_f32(inp.bits["w1"][0:1])
-    w2 = bf16_bits_to_f32(inp.bits["w2"][0:1])
-    x = bf16_bits_to_f32(inp.bits["x"][rows])
-
-    def run(n):
+    pp = p.ravel()[m["src_token"] * w.k + m["src_slot"]]
+    t_all = 0.0
+    rows = 0
+    experts = 0
+    for e in range(w.E):
+        a, b = int(m["offsets"][e]), int(m["offsets"][e + 1])
+        x = bf16_bits_to_f32(inp.bits["x"][m["src_token"][a:b]])
+        w1 = bf16_bits_to_f32(inp.bits["w1"][e:e + 1])
+        w2 = bf16_bits_to_f32(inp.bits["w2"][e:e + 1])
         t0 = time.perf_counter()
-        oracle.grouped_mlp_forward(x[:n], w1, w2, np.array([0, n]), pp[:n])
-        return time.perf_counter() - t0
-
-    n0 = 32
-    t_small = run(n0)
-    n = int(max(n0, min(len(rows), n0 * seconds / max(t_small, 1e-3))))
-    t = run(n)
+        oracle.grouped_mlp_forward(x, w1, w2, np.array([0, b - a]), pp[a:b])
+        t_all += time.perf_counter() - t0
+        rows += b - a
+        experts += 1
+        if t_all >= seconds:
+            break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    flop = 6.0 * n * w.H * w.I
-    return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 numpy oracle forward (gate_up, ScaledSwiGLU, down) on {n} rows of expert 0 of the "
-                      f"{w.name} workload (H={w.H}, I={w.I}); {t:.1f} s wall, {os.cpu_count()} host CPUs visible"}
+    flop = 6.0 * rows * w.H * w.I
+    return {"value": round(flop / t_all / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 numpy oracle, grouped MLP forward (gate_up, ScaledSwiGLU, down) of experts "
+                      f"0..{experts - 1} of the {w.name} workload on all their rows ({rows} of {w.R} rows, "
+                      f"H={w.H}, I={w.I}); {t_all:.1f} s of oracle time, {os.cpu_count()} host CPUs visible"}
 
 
 def main():
@@ -199,6 +259,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-fwd-bwd", action="store_true", help="skip the forward+backward measurement")
+    ap.add_argument("--quick", action="store_true", help="skip the MXFP8 and Qwen3 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
@@ -243,6 +304,21 @@ def main():
     }
     del layer
     torch.cuda.empty_cache()
+
+    if not args.quick:
+        # MXFP8 on the same Mixtral tensors (the MXFP8 workload draws the same inputs)
+        w8 = WORKLOADS["mixtral_mxfp8_fwd"]
+        result["mxfp8_fwd"] = extra_forward(w8, inp, max(3, args.steps // 2), args.warmup, compute="mxfp8")
+        result["mxfp8_fwd_prequantised"] = extra_forward(w8, inp, max(3, args.steps // 2), args.warmup,
+                                                          compute="mxfp8", prequant=True)
+        torch.cuda.empty_cache()
+        wq = WORKLOADS["qwen3_fwd"]
+        t0 = time.perf_counter()
+        inpq = make_inputs(wq, want_float=False)
+        log(f"inputs {wq.name}: {time.perf_counter() - t0:.1f} s")
+        result["qwen3_fwd"] = extra_forward(wq, inpq, max(3, args.steps // 2), args.warmup)
+        del inpq
+        torch.cuda.empty_cache()
 
     if not args.no_fwd_bwd:
         wb = WORKLOADS["mixtral_fwd_bwd"]
