@@ -16,7 +16,8 @@
 // -- the two 16-byte chunks a bf16 step reads as its two k16 slices -- and supplies
 // the E8M0 scale of K block g (values [32g, 32g + 32)) of its row.
 // Scales: per 4-step group each lane loads 8 bytes (blocks 8g..8g+7) of its row per
-// sub-tile; op_sel picks the step's byte at compile time.
+// sub-tile and packs the 4 bytes of its own K half (block 2j + (l / 32) of step j) into
+// one word, so step j's MFMA selects byte j with op_sel, a compile-time immediate.
 #include <cstring>
 #include <type_traits>
 
@@ -170,7 +171,7 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
       qs_off[t2] = (uint32_t)((int64_t)(q_row(wm * 128 + t2 * 32 + l32) - tile_row) * kscale);
     }
     uint2 scl_next[8];
-    uint32_t sP[4][2], sQ[4][2];  // [sub-tile][word]: bytes 0 and 2 = this lane's block of steps 0..3
+    uint32_t sP[4], sQ[4];  // [sub-tile]: byte j = this lane's scale for step j of the group
     auto load_scales = [&](int g) {
 #pragma unroll
       for (int t2 = 0; t2 < 4; ++t2) {
@@ -182,9 +183,8 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
 #pragma unroll
       for (int t2 = 0; t2 < 8; ++t2) {
         const uint64_t raw = ((uint64_t)scl_next[t2].y << 32 | scl_next[t2].x) >> (8 * lhi);
-        uint32_t* dst = t2 < 4 ? sP[t2] : sQ[t2 - 4];
-        dst[0] = (uint32_t)raw;
-        dst[1] = (uint32_t)(raw >> 32);
+        const uint32_t packed = __builtin_amdgcn_perm((uint32_t)(raw >> 32), (uint32_t)raw, 0x06040200u);
+        if (t2 < 4) sP[t2] = packed; else sQ[t2 - 4] = packed;
       }
     };
 
@@ -210,7 +210,7 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
       const i32x4_t b = *reinterpret_cast<const i32x4_t*>(base + row * 64 + ck1);
       return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    i32x8_t Q[4], P01[2], P23[2];
+    i32x8_t QA[4], QB[4], P01[2], P23[2];
 
     // prologue
     load_scales(0);
@@ -225,23 +225,25 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
       const uint8_t* P = sP0 + fragP;
       const uint8_t* Qb = sQ0 + fragQ;
 #pragma unroll
-      for (int t2 = 0; t2 < 4; ++t2) Q[t2] = rd(Qb, t2 * 32);
+      for (int t2 = 0; t2 < 4; ++t2) QA[t2] = rd(Qb, t2 * 32);
       P01[0] = rd(P, 0);
       P01[1] = rd(P, 32);
     }
 
     // step kt on slot S (j = kt % 4 = S). On entry Q and P01 hold this step's Q
-    // fragments and P sub-tiles 0-1.
+    // fragments and P sub-tiles 0-1; Q alternates between two register sets by step
+    // parity, so every fragment register is written once and read once per step.
     //   phase A: MFMAs of P 0-1 while P 2-3 are read; wait for step kt+1; barrier;
     //   phase B: copies of step kt+4 into slot S (free now), the next group's scales,
-    //            the next step's P 0-1; MFMAs of P 2-3 in Q order, each Q fragment
-    //            replaced by the next step's as soon as its two MFMAs are issued.
+    //            the next step's P 0-1 and Q fragments (into the other Q set), threaded
+    //            through the MFMAs of P 2-3.
     auto kstep = [&](int kt, auto S, auto FULL) {
       constexpr int j = decltype(S)::value;
       constexpr bool full = decltype(FULL)::value;
+      // this step's Q fragments: QA on even steps, QB on odd; the next step's go to the other
+      auto& Q = [&]() -> i32x8_t (&)[4] { if constexpr (j & 1) return QB; else return QA; }();
+      auto& QN = [&]() -> i32x8_t (&)[4] { if constexpr (j & 1) return QA; else return QB; }();
       using SN = std::integral_constant<int, (j + 1) & 3>;
-      constexpr int w = j >> 1;            // scale word of this step
-      constexpr int os = (j & 1) * 2;      // and byte in it
       {
         const uint8_t* P = slotP(S) + fragP;
         P23[0] = rd(P, 128);
@@ -251,8 +253,8 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
       for (int sm = 0; sm < 4; ++sm)
 #pragma unroll
         for (int sn = 0; sn < 2; ++sn)
-          acc[sn][sm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(P01[sn], Q[sm], acc[sn][sm], 0, 0, os,
-                                                                          (int)sP[sn][w], os, (int)sQ[sm][w]);
+          acc[sn][sm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(P01[sn], Q[sm], acc[sn][sm], 0, 0, j,
+                                                                          (int)sP[sn], j, (int)sQ[sm]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -281,9 +283,9 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
       for (int sm = 0; sm < 4; ++sm) {
 #pragma unroll
         for (int sn = 2; sn < 4; ++sn)
-          acc[sn][sm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(P23[sn - 2], Q[sm], acc[sn][sm], 0, 0, os,
-                                                                          (int)sP[sn][w], os, (int)sQ[sm][w]);
-        if (next) Q[sm] = rd(Qn, sm * 32);
+          acc[sn][sm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(P23[sn - 2], Q[sm], acc[sn][sm], 0, 0, j,
+                                                                          (int)sP[sn], j, (int)sQ[sm]);
+        if (next) QN[sm] = rd(Qn, sm * 32);
       }
       if constexpr (full) {
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
