@@ -262,7 +262,18 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip the MXFP8 and Qwen3 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MoE layer here runs all experts on a single MI355X "
               "(no expert parallelism across GPUs is built); run it with --gpus 1", file=sys.stderr)
