@@ -18,15 +18,18 @@
 //   GROUP_K: the reduction runs over expert e's token rows (K = its row count, may be
 //            0); M and N are fixed and each expert writes its own C. Weight gradients.
 // Operand layouts: KCONTIG = rows of K-contiguous elements ([rows][K]); MNCONTIG =
-//   K is the row index and m/n is contiguous ([K][cols]); the loader transposes
-//   8x8 bf16 blocks in registers so LDS always holds [m or n][k].
+//   K is the row index and m/n is contiguous ([K][cols]). Both are copied to LDS in
+//   their global layout; MFMA fragments of an MNCONTIG operand (8 consecutive k of one
+//   m/n) come out of gfx950's transposing LDS read (ds_read_b64_tr_b16), so no operand
+//   passes through registers on its way to LDS.
 // Tiles: 256 x 256 x 32 per K step, 4 wavefronts (2 x 2), each 128 x 128 = 4 x 4
 //   MFMA blocks held in 256 accumulator registers. LDS is a ring of 4 stages of
-//   32 KiB: K-contiguous operands are copied global -> LDS three steps ahead of the
+//   32 KiB: operands are copied global -> LDS three steps ahead of the
 //   step being multiplied (partial vmcnt waits keep two steps in flight), which hides
 //   the latency of L2 misses; one barrier per K step. LDS rows are 64 bytes (4 chunks
 //   of 16 bytes) and chunk c of row r lives at c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3,
-//   which keeps MFMA fragment reads free of bank conflicts for 8- and 16-lane phases.
+//   which keeps MFMA fragment reads free of bank conflicts for 8- and 16-lane phases;
+//   MNCONTIG tiles are 32 rows of 512 bytes with their own chunk swizzle (mnswz).
 // Scheduling: one workgroup per CU loops over tiles (persistent); tile ids are
 //   remapped so that each XCD (workgroup id mod 8) works on a contiguous run of
 //   tiles. Inside an expert, tiles run m-fastest, so a run covers a few weight
@@ -41,6 +44,9 @@
 
 namespace moe {
 namespace gemm {
+
+// source of the copies of K rows past the end of a ragged K range
+static __device__ __attribute__((aligned(16))) uint4 g_zero16;
 
 template <int PL, int QL, int G, int EP>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
@@ -137,19 +143,35 @@ void grouped_gemm_kernel(const Params prm) {
     const int row_end = __builtin_amdgcn_readfirstlane(s_off[e + 1]);
 
     // ---------------- operand addressing ----------------
-    // K-contiguous operands are copied global -> LDS directly (global_load_lds_dwordx4:
-    // lane l of a wavefront lands at the wave's LDS base + 16 * l). Round i of wave w
-    // fills the 16 LDS rows starting at (i*4 + w) * 16; lane l takes row + (l >> 2) and
-    // physical chunk l & 3, i.e. logical chunk (l & 3) ^ swz(row) of that row.
-    // MN-contiguous operands go through registers and a 4x8 transpose.
+    // Every operand is copied global -> LDS directly (global_load_lds_dwordx4: lane l
+    // of a wavefront lands at the wave's LDS base + 16 * l), 4 copies per operand, lane
+    // and K step; round i of wave w fills LDS bytes [(4i + w) KiB, +1 KiB) of the slot.
+    //   KCONTIG: LDS rows of 64 bytes ([mn][k]); lane l takes row (4i + w) * 16 + (l >> 2)
+    //            and physical chunk l & 3, i.e. logical chunk (l & 3) ^ swz(row).
+    //   MNCONTIG: LDS rows of 512 bytes ([k][mn], the global layout); lane l takes k-row
+    //            r = 8i + 2w + (l >> 5) and physical chunk l & 31, i.e. the 8 columns of
+    //            logical chunk (l & 31) ^ mnswz(r & 3).
     const int dma_row0 = wave * 16 + (lane >> 2);
+    const int mn_row0 = 2 * wave + (lane >> 5);
     const bf16_t* pbase;
     if constexpr (G == GROUP_M) pbase = reinterpret_cast<const bf16_t*>(prm.tab[e]);
     else pbase = prm.p;
-    // KCONTIG: a uniform tile base plus, per round, this lane's 32-bit byte offset
-    const char* p_tile = nullptr;
+    // K range
+    int nk;
+    int kbeg;  // first K row of an MN-contiguous operand (GROUP_K: the expert's first token row)
+    if constexpr (G == GROUP_M) {
+      nk = prm.K / kBK;
+      kbeg = 0;
+    } else {
+      nk = (row_end - row_beg + kBK - 1) / kBK;
+      kbeg = row_beg;
+    }
+    const int kcount = (G == GROUP_M) ? prm.K : row_end - row_beg;
+    // a uniform tile base plus, per round, this lane's 32-bit byte offset; the tile base
+    // moves by p_step / q_step bytes per K step
+    const char* p_tile;
     uint32_t p_off[4];
-    int64_t p_col = 0;  // MNCONTIG: this thread's 8-column chunk
+    int64_t p_step;
     if constexpr (PL == KCONTIG) {
       if constexpr (EP == EPI_SWIGLU) p_tile = reinterpret_cast<const char*>(pbase + (int64_t)nt * 128 * prm.p_ld);
       else p_tile = reinterpret_cast<const char*>(pbase + (int64_t)nt * kBN * prm.p_ld);
@@ -161,12 +183,19 @@ void grouped_gemm_kernel(const Params prm) {
         else n = r;
         p_off[i] = (uint32_t)(((int64_t)n * prm.p_ld + (((lane & 3) ^ swz(r)) * 8)) * 2);
       }
+      p_step = kBK * 2;
     } else {
-      p_col = (int64_t)nt * kBN + (tid & 31) * 8;
+      p_tile = reinterpret_cast<const char*>(pbase + (int64_t)kbeg * prm.p_ld + (int64_t)nt * kBN);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 8 + mn_row0;
+        p_off[i] = (uint32_t)(((int64_t)r * prm.p_ld + (((lane & 31) ^ mnswz(r & 3)) * 8)) * 2);
+      }
+      p_step = (int64_t)kBK * prm.p_ld * 2;
     }
-    const char* q_tile = nullptr;
+    const char* q_tile;
     uint32_t q_off[4];
-    int64_t q_col = 0;
+    int64_t q_step;
     if constexpr (QL == KCONTIG) {
       const int tile_row = row_beg + mt * kBM;
       q_tile = reinterpret_cast<const char*>(prm.q + (int64_t)tile_row * prm.q_ld);
@@ -177,82 +206,36 @@ void grouped_gemm_kernel(const Params prm) {
         row = row < row_end ? row : row_end - 1;  // rows past the expert: any valid row, discarded
         q_off[i] = (uint32_t)(((int64_t)(row - tile_row) * prm.q_ld + (((lane & 3) ^ swz(r)) * 8)) * 2);
       }
+      q_step = kBK * 2;
     } else {
-      q_col = (int64_t)mt * kBM + (tid & 31) * 8;
+      q_tile = reinterpret_cast<const char*>(prm.q + (int64_t)kbeg * prm.q_ld + (int64_t)mt * kBM);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 8 + mn_row0;
+        q_off[i] = (uint32_t)(((int64_t)r * prm.q_ld + (((lane & 31) ^ mnswz(r & 3)) * 8)) * 2);
+      }
+      q_step = (int64_t)kBK * prm.q_ld * 2;
     }
-    // K range
-    int nk;
-    int64_t kbeg;  // GROUP_K: first token row; GROUP_M: 0
-    if constexpr (G == GROUP_M) {
-      nk = prm.K / kBK;
-      kbeg = 0;
-    } else {
-      nk = (row_end - row_beg + kBK - 1) / kBK;
-      kbeg = row_beg;
-    }
-    const int kg = tid >> 5;  // MNCONTIG: k group of 4 rows
 
-    constexpr int kDma = (PL == KCONTIG ? 4 : 0) + (QL == KCONTIG ? 4 : 0);  // copies per stage per lane
-    constexpr bool kReg = PL == MNCONTIG || QL == MNCONTIG;
+    constexpr int kDma = 8;  // copies per stage per lane
 
-    // global -> LDS copies of K step kt into ring slot S (= kt % kStages)
+    // global -> LDS copies of K step kt into ring slot S (= kt % kStages). K rows of an
+    // MN-contiguous operand past the end of the K range (the ragged last step of a
+    // GROUP_K expert) are copied from a zero block: they must add nothing to the sums.
     auto issue_dma = [&](int kt, auto S) {
-      const int64_t k0b = (int64_t)kt * kBK * 2;
-      if constexpr (PL == KCONTIG) {
-        uint8_t* P = slotP(S) + wave * 1024;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __builtin_amdgcn_global_load_lds((const void*)(p_tile + k0b + p_off[i]), (lds_ptr_t)(P + i * 4096), 16, 0, 0);
-      }
-      if constexpr (QL == KCONTIG) {
-        uint8_t* Q = slotQ(S) + wave * 1024;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __builtin_amdgcn_global_load_lds((const void*)(q_tile + k0b + q_off[i]), (lds_ptr_t)(Q + i * 4096), 16, 0, 0);
-      }
-    };
-    uint4 pr[4], qr[4];
-    // register loads of K step kt for the MN-contiguous operands
-    auto load_regs = [&](int kt) {
-      const int64_t k0 = (int64_t)kt * kBK;
-      if constexpr (PL == MNCONTIG) {
+      auto one = [&](const char* tile, const uint32_t* off, int64_t step, bool mn, uint8_t* dst) {
+        const char* base = tile + kt * step;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t kr = kbeg + k0 + kg * 4 + i;
-          bool ok = true;
-          if constexpr (G == GROUP_K) ok = kr < row_end;
-          pr[i] = ok ? *reinterpret_cast<const uint4*>(pbase + kr * prm.p_ld + p_col) : make_uint4(0, 0, 0, 0);
+          const char* src = base + off[i];
+          if (G == GROUP_K && mn) {
+            if (kt * kBK + i * 8 + mn_row0 >= kcount) src = reinterpret_cast<const char*>(&g_zero16);
+          }
+          __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(dst + i * 4096), 16, 0, 0);
         }
-      }
-      if constexpr (QL == MNCONTIG) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t kr = kbeg + k0 + kg * 4 + i;
-          bool ok = true;
-          if constexpr (G == GROUP_K) ok = kr < row_end;
-          qr[i] = ok ? *reinterpret_cast<const uint4*>(prm.q + kr * prm.q_ld + q_col) : make_uint4(0, 0, 0, 0);
-        }
-      }
-    };
-    // transpose the register-staged operands of K step kt and write them to LDS
-    auto commit_regs = [&](auto S) {
-      const uint32_t sub = (uint32_t)((kg & 1) * 8);
-      if constexpr (PL == MNCONTIG) {
-        uint8_t* P = slotP(S);
-        uint2 tr[8];
-        transpose4x8(pr, tr);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<uint2*>(P + lds_off((tid & 31) * 8 + j, kg >> 1) + sub) = tr[j];
-      }
-      if constexpr (QL == MNCONTIG) {
-        uint8_t* Q = slotQ(S);
-        uint2 tr[8];
-        transpose4x8(qr, tr);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<uint2*>(Q + lds_off((tid & 31) * 8 + j, kg >> 1) + sub) = tr[j];
-      }
+      };
+      one(p_tile, p_off, p_step, PL == MNCONTIG, slotP(S) + wave * 1024);
+      one(q_tile, q_off, q_step, QL == MNCONTIG, slotQ(S) + wave * 1024);
     };
 
     f32x16 acc[4][4];
@@ -269,21 +252,57 @@ void grouped_gemm_kernel(const Params prm) {
     using S3 = std::integral_constant<int, 3>;
 
     const int l32 = lane & 31, lhi = lane >> 5;
-    // Fragment addresses: sub-tile rows start at multiples of 32, where swz depends on
-    // the lane's row within the sub-tile only; the rest of the offset is a constant.
+    // KCONTIG fragment addresses: sub-tile rows start at multiples of 32, where swz
+    // depends on the lane's row within the sub-tile only; the rest is a constant.
     const uint32_t fragP = (uint32_t)((wn * 64 + l32) * 64);
     const uint32_t fragQ = (uint32_t)((wm * 128 + l32) * 64);
     const uint32_t ck0 = (uint32_t)(((0 * 2 + lhi) ^ swz(l32)) << 4);
     const uint32_t ck1 = (uint32_t)(((1 * 2 + lhi) ^ swz(l32)) << 4);
+    // MNCONTIG fragment addresses (transposing reads). A fragment is k 8*(l >> 5) .. +7
+    // of column l & 31 of a 32-column sub-tile; it takes two ds_read_b64_tr_b16, each
+    // covering 4 k-rows. In 16-lane group g = l >> 4 (columns (g & 1) * 16 .. +15, k-rows
+    // (g >> 1) * 8 + 4 * read .. +3), lane 4j + a supplies the 8 bytes of k-row j at
+    // columns 4a .. 4a+3, and the read hands lane i of the group column i of the 4 rows.
+    const int trj = (lane & 15) >> 2, tra = lane & 3;
+    const int tr_low = (lane >> 4 & 1) * 2 + (tra >> 1);             // chunk bits 0-1
+    const uint32_t tr_row = (uint32_t)((((lane >> 5) * 8) + trj) * 512 + (tra & 1) * 8);
+    const int tr_x = tr_low ^ mnswz(trj);
+    // P sub-tile t spans columns (t >> 1) * 128 + wn * 64 + (t & 1) * 32: chunk bit 4
+    // is (t >> 1), bit 3 wn, bit 2 (t & 1)
+    const uint32_t trP0 = tr_row + (uint32_t)(((wn * 8) ^ tr_x) << 4);
+    const uint32_t trP1 = tr_row + (uint32_t)(((wn * 8 + 4) ^ tr_x) << 4);
+    // Q sub-tile t spans columns wm * 128 + t * 32: chunk bit 4 is wm, bits 2-3 t
+    uint32_t trQ[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) trQ[t] = tr_row + (uint32_t)((((t * 4) ^ tr_x) + wm * 16) << 4);
+
+    auto read_tr = [&](const uint8_t* base, uint32_t off) -> bf16x8 {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(base + off));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(base + off + 4 * 512));
+      const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, v);
+    };
     // fragments of one k16 slice: 4 of P (n sub-tiles), 4 of Q (m sub-tiles)
     bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-    auto read_slice = [&](auto S, uint32_t ck, bf16x8* fa, bf16x8* fb) {
-      const uint8_t* P = slotP(S) + fragP + ck;
-      const uint8_t* Q = slotQ(S) + fragQ + ck;
+    auto read_slice = [&](auto S, int sl, bf16x8* fa, bf16x8* fb) {
+      if constexpr (PL == KCONTIG) {
+        const uint8_t* P = slotP(S) + fragP + (sl ? ck1 : ck0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) fa[t] = *reinterpret_cast<const bf16x8*>(P + ((t >> 1) * 128 + (t & 1) * 32) * 64);
+        for (int t = 0; t < 4; ++t) fa[t] = *reinterpret_cast<const bf16x8*>(P + ((t >> 1) * 128 + (t & 1) * 32) * 64);
+      } else {
+        const uint8_t* P = slotP(S) + sl * 16 * 512;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) fb[t] = *reinterpret_cast<const bf16x8*>(Q + (t * 32) * 64);
+        for (int t = 0; t < 4; ++t) fa[t] = read_tr(P, ((t & 1) ? trP1 : trP0) + (t >> 1) * 256);
+      }
+      if constexpr (QL == KCONTIG) {
+        const uint8_t* Q = slotQ(S) + fragQ + (sl ? ck1 : ck0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) fb[t] = *reinterpret_cast<const bf16x8*>(Q + (t * 32) * 64);
+      } else {
+        const uint8_t* Q = slotQ(S) + sl * 16 * 512;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) fb[t] = read_tr(Q, trQ[t]);
+      }
     };
     auto mfma_slice = [&](const bf16x8* fa, const bf16x8* fb) {
 #pragma unroll
@@ -292,41 +311,45 @@ void grouped_gemm_kernel(const Params prm) {
         for (int sm = 0; sm < 4; ++sm)
           acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sn], fb[sm], acc[sn][sm], 0, 0, 0);
     };
-    // 16 MFMAs with the 8 fragment reads of another slice threaded between them
-    auto interleave = [&]() {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+    // LDS read instructions per slice (a transposed fragment takes two)
+    constexpr int kReads = (PL == KCONTIG ? 4 : 8) + (QL == KCONTIG ? 4 : 8);
+    // 16 MFMAs with the fragment reads of another slice spread evenly between them
+    auto interleave_a = [&]() {
+      static_for<16>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int nr = ((i + 1) * kReads) / 16 - (i * kReads) / 16;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+      });
+    };
+    // 16 MFMAs with the next slice's reads and the 8 copies of a later step between them
+    auto interleave_b = [&]() {
+      static_for<16>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int nr = ((i + 1) * kReads) / 16 - (i * kReads) / 16;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+        if constexpr (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      });
     };
 
-    // prologue: register loads of step 0, copies of steps 0..3, then step 1's registers
+    // prologue: copies of steps 0..3
     if (nk > 0) {
-      if constexpr (kReg) load_regs(0);
-      if constexpr (kDma > 0) {
-        issue_dma(0, S0{});
-        if (nk > 1) issue_dma(1, S1{});
-        if (nk > 2) issue_dma(2, S2{});
-        if (nk > 3) issue_dma(3, S3{});
-      }
+      issue_dma(0, S0{});
+      if (nk > 1) issue_dma(1, S1{});
+      if (nk > 2) issue_dma(2, S2{});
+      if (nk > 3) issue_dma(3, S3{});
       const int later = (nk > 1) + (nk > 2) + (nk > 3);
       wait_vm_le(later * kDma);  // step 0 complete
-      if constexpr (kReg) {
-        commit_regs(S0{});
-        if (nk > 1) load_regs(1);
-      }
     }
     lds_barrier();
-    if (nk > 0) read_slice(S0{}, ck0, fa0, fb0);
+    if (nk > 0) read_slice(S0{}, 0, fa0, fb0);
 
     // K step kt on ring slot S. On entry the first k16 slice of step kt is in fa0/fb0.
     //   phase A: its 16 MFMAs while the second slice is read into fa1/fb1; then wait for
-    //            step kt+1 (copies, or register loads that are then written to LDS) and
-    //            meet at the barrier;
-    //   phase B: slot S is free now: start step kt+4's copies into it (register loads of
-    //            step kt+2 first), then the second slice's 16 MFMAs while step kt+1's
-    //            first slice is read into fa0/fb0.
+    //            step kt+1's copies and meet at the barrier;
+    //   phase B: slot S is free now: start step kt+4's copies into it, then the second
+    //            slice's 16 MFMAs while step kt+1's first slice is read into fa0/fb0.
     // Copies land 3 steps after they are issued; vmcnt counts loads in issue order.
     // FULL: steps kt+1..kt+4 all exist, so every branch below folds away and the step
     // is one basic block the scheduler can interleave.
@@ -334,31 +357,15 @@ void grouped_gemm_kernel(const Params prm) {
       constexpr int s = decltype(S)::value;
       constexpr bool full = decltype(FULL)::value;
       using SN = std::integral_constant<int, (s + 1) & 3>;
-      read_slice(S, ck1, fa1, fb1);
+      read_slice(S, 1, fa1, fb1);
       mfma_slice(fa0, fb0);
-      interleave();
-      if (kReg && (full || kt + 1 < nk)) {
-        wait_vm_le((full || kt + 3 < nk) ? kDma : 0);
-        commit_regs(SN{});
-      } else {
-        wait_vm_le(full ? 2 * kDma : ((kt + 2 < nk) + (kt + 3 < nk)) * kDma);
-      }
+      interleave_a();
+      wait_vm_le(full ? 2 * kDma : ((kt + 2 < nk) + (kt + 3 < nk)) * kDma);
       lds_barrier();
-      if (kReg && (full || kt + 2 < nk)) load_regs(kt + 2);
-      if constexpr (kDma > 0) {
-        if (full || kt + 4 < nk) issue_dma(kt + 4, S);
-      }
-      if (full || kt + 1 < nk) read_slice(SN{}, ck0, fa0, fb0);
+      if (full || kt + 4 < nk) issue_dma(kt + 4, S);
+      if (full || kt + 1 < nk) read_slice(SN{}, 0, fa0, fb0);
       mfma_slice(fa1, fb1);
-      // copies and next-slice reads threaded between the MFMAs, so the wavefront never
-      // waits behind a burst of copy instructions while the matrix core idles
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+      interleave_b();
     };
     using Full = std::true_type;
     using Tail = std::false_type;

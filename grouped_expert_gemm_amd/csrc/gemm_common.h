@@ -2,6 +2,8 @@
 // wait counters and the K-loop barrier.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -9,34 +11,29 @@ namespace gemm {
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-__device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-  return (uint32_t)(row * 64 + ((chunk ^ swz(row)) << 4));
-}
+// LDS layout of an MN-contiguous operand tile: 32 k-rows of 512 bytes (32 chunks of
+// 16 bytes); chunk c of k-row r sits at c ^ mnswz(r & 3). A transposing read touches,
+// per 16 lanes, 2 adjacent chunks of 4 consecutive k-rows and, per 32 lanes, 4 chunks of
+// the same rows; mnswz gives the 4 rows distinct chunk bits 1-2 and distinct bits 2-3,
+// so both sets fall on distinct banks.
+__device__ __forceinline__ int mnswz(int j) { return (j << 2) ^ (((j ^ (j >> 1)) & 1) << 1); }
 
 // column offset of MFMA sub-tile s (0..3) of wavefront column wn inside the 256-wide
 // tile: sub-tiles 0,1 cover [wn*64, wn*64+64), sub-tiles 2,3 the same span + 128.
 __device__ __forceinline__ int sub_n(int s, int wn) { return (s >> 1) * 128 + wn * 64 + (s & 1) * 32; }
 
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 
-// 4 rows (k) x 8 bf16 (mn) -> 8 vectors (mn) x 4 bf16 (k)
-__device__ __forceinline__ void transpose4x8(const uint4 in[4], uint2 out[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 a = in[i];
-      w[i] = (j >> 1) == 0 ? a.x : (j >> 1) == 1 ? a.y : (j >> 1) == 2 ? a.z : a.w;
-    }
-    out[j] = make_uint2(perm(w[1], w[0], sel), perm(w[3], w[2], sel));
+// f(integral_constant<0>) ... f(integral_constant<N-1>), unrolled at compile time
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
   }
 }
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // s_waitcnt vmcnt(N): at most N of this wavefront's vector memory operations
 // (loads, including global -> LDS copies, which complete in issue order) outstanding
