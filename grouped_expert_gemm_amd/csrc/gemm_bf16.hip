@@ -24,9 +24,10 @@
 //   passes through registers on its way to LDS.
 // Tiles: 256 x 256 x 32 per K step, 4 wavefronts (2 x 2), each 128 x 128 = 4 x 4
 //   MFMA blocks held in 256 accumulator registers. LDS is a ring of 4 stages of
-//   32 KiB: operands are copied global -> LDS three steps ahead of the
-//   step being multiplied (partial vmcnt waits keep two steps in flight), which hides
-//   the latency of L2 misses; one barrier per K step. LDS rows are 64 bytes (4 chunks
+//   32 KiB: operands are copied global -> LDS (buffer loads with the lds modifier)
+//   three steps ahead of the step being multiplied (a partial vmcnt wait keeps the
+//   next step's copies in flight), which hides the latency of L2 misses; one barrier
+//   per K step, which leaves the latest fragment reads in flight. LDS rows are 64 bytes (4 chunks
 //   of 16 bytes) and chunk c of row r lives at c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3,
 //   which keeps MFMA fragment reads free of bank conflicts for 8- and 16-lane phases;
 //   MNCONTIG tiles are 32 rows of 512 bytes with their own chunk swizzle (mnswz).
@@ -45,8 +46,8 @@
 namespace moe {
 namespace gemm {
 
-// source of the copies of K rows past the end of a ragged K range
-static __device__ __attribute__((aligned(16))) uint4 g_zero16;
+// word 3 of a raw buffer descriptor for dword loads (32-bit data format)
+constexpr int kBufferFlags = 0x00020000;
 
 template <int PL, int QL, int G, int EP>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
@@ -217,25 +218,36 @@ void grouped_gemm_kernel(const Params prm) {
       q_step = (int64_t)kBK * prm.q_ld * 2;
     }
 
+    // bytes addressable from each tile origin: GROUP_K token rows end at the expert's
+    // last row; every other operand stays inside its tensor by construction
+    constexpr int64_t kAll = 0xFFFFFFFFll;
+    const int64_t p_extent = (G == GROUP_K && PL == MNCONTIG) ? (int64_t)kcount * prm.p_ld * 2 : kAll;
+    const int64_t q_extent = (G == GROUP_K && QL == MNCONTIG) ? (int64_t)kcount * prm.q_ld * 2 : kAll;
     constexpr int kDma = 8;  // copies per stage per lane
+    // copies run kAhead K steps ahead of the step being multiplied: 4 refills the slot
+    // just consumed (the barrier must then wait for every fragment read of it), 3 the
+    // slot consumed one step earlier (the latest fragment reads stay in flight)
+    constexpr int kAhead = 3;
 
-    // global -> LDS copies of K step kt into ring slot S (= kt % kStages). K rows of an
-    // MN-contiguous operand past the end of the K range (the ragged last step of a
-    // GROUP_K expert) are copied from a zero block: they must add nothing to the sums.
+    // global -> LDS copies of K step kt into ring slot S (= kt % kStages), as
+    // buffer_load_dwordx4 ... lds through a buffer descriptor based at the step's tile
+    // origin. (The flat-encoded global_load_lds would make the compiler wait for every
+    // outstanding LDS read wherever it waits for one.) For the token rows of a GROUP_K
+    // operand the descriptor's record count ends at the expert's last row: the rows of
+    // the ragged last step past it fail the hardware range check and land as zeros.
     auto issue_dma = [&](int kt, auto S) {
-      auto one = [&](const char* tile, const uint32_t* off, int64_t step, bool mn, uint8_t* dst) {
-        const char* base = tile + kt * step;
+      auto one = [&](const char* tile, const uint32_t* off, int64_t step, int64_t extent, uint8_t* dst) {
+        const int64_t at = (int64_t)kt * step;
+        int64_t nrec = extent - at;
+        nrec = nrec < 0 ? 0 : (nrec > kAll ? kAll : nrec);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(tile + at), (short)0, (int)(uint32_t)nrec, kBufferFlags);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const char* src = base + off[i];
-          if (G == GROUP_K && mn) {
-            if (kt * kBK + i * 8 + mn_row0 >= kcount) src = reinterpret_cast<const char*>(&g_zero16);
-          }
-          __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(dst + i * 4096), 16, 0, 0);
-        }
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 4096), 16, off[i], 0, 0, 0);
       };
-      one(p_tile, p_off, p_step, PL == MNCONTIG, slotP(S) + wave * 1024);
-      one(q_tile, q_off, q_step, QL == MNCONTIG, slotQ(S) + wave * 1024);
+      one(p_tile, p_off, p_step, p_extent, slotP(S) + wave * 1024);
+      one(q_tile, q_off, q_step, q_extent, slotQ(S) + wave * 1024);
     };
 
     f32x16 acc[4][4];
@@ -333,26 +345,15 @@ void grouped_gemm_kernel(const Params prm) {
       });
     };
 
-    // prologue: copies of steps 0..3
-    if (nk > 0) {
-      issue_dma(0, S0{});
-      if (nk > 1) issue_dma(1, S1{});
-      if (nk > 2) issue_dma(2, S2{});
-      if (nk > 3) issue_dma(3, S3{});
-      const int later = (nk > 1) + (nk > 2) + (nk > 3);
-      wait_vm_le(later * kDma);  // step 0 complete
-    }
-    lds_barrier();
-    if (nk > 0) read_slice(S0{}, 0, fa0, fb0);
-
     // K step kt on ring slot S. On entry the first k16 slice of step kt is in fa0/fb0.
     //   phase A: its 16 MFMAs while the second slice is read into fa1/fb1; then wait for
     //            step kt+1's copies and meet at the barrier;
-    //   phase B: slot S is free now: start step kt+4's copies into it, then the second
-    //            slice's 16 MFMAs while step kt+1's first slice is read into fa0/fb0.
-    // Copies land 3 steps after they are issued; vmcnt counts loads in issue order.
-    // FULL: steps kt+1..kt+4 all exist, so every branch below folds away and the step
-    // is one basic block the scheduler can interleave.
+    //   phase B: start step kt+kAhead's copies into the slot read kt+kAhead-4 steps
+    //            ago, then the second slice's 16 MFMAs while step kt+1's first slice is
+    //            read into fa0/fb0.
+    // vmcnt counts loads in issue order, so a partial wait leaves the later steps' copies
+    // in flight. FULL: steps up to kt+kAhead all exist, so every branch below folds away
+    // and the step is one basic block the scheduler can interleave.
     auto kstep = [&](int kt, auto S, auto FULL) {
       constexpr int s = decltype(S)::value;
       constexpr bool full = decltype(FULL)::value;
@@ -360,21 +361,55 @@ void grouped_gemm_kernel(const Params prm) {
       read_slice(S, 1, fa1, fb1);
       mfma_slice(fa0, fb0);
       interleave_a();
-      wait_vm_le(full ? 2 * kDma : ((kt + 2 < nk) + (kt + 3 < nk)) * kDma);
-      lds_barrier();
-      if (full || kt + 4 < nk) issue_dma(kt + 4, S);
+      if constexpr (kAhead == 3) {
+        // step kt+1 landed (kt+2's copies may be in flight); slot (kt-1) % 4 was last
+        // read a step ago, so only this phase's reads of slot S may stay outstanding
+        wait_vm_le(full || kt + 2 < nk ? kDma : 0);
+        lds_barrier_keep<kReads>();
+        using SP = std::integral_constant<int, (s + 3) & 3>;
+        if (full || kt + 3 < nk) issue_dma(kt + 3, SP{});
+      } else {
+        wait_vm_le(full ? 2 * kDma : ((kt + 2 < nk) + (kt + 3 < nk)) * kDma);
+        lds_barrier();
+        if (full || kt + 4 < nk) issue_dma(kt + 4, S);
+      }
       if (full || kt + 1 < nk) read_slice(SN{}, 0, fa0, fb0);
       mfma_slice(fa1, fb1);
       interleave_b();
     };
     using Full = std::true_type;
     using Tail = std::false_type;
+    // The long-K path has a prologue without branches, so the compiler's model of the
+    // copies in flight at the top of the steady-state loop is exact and it adds no
+    // waits there; short K ranges (ragged experts of GROUP_K, small K) take the
+    // general prologue and go straight to the tail loop.
     int kt = 0;
-    for (; kt + 7 < nk; kt += 4) {  // steady state: kt+7 < nk covers the copies of all four steps
-      kstep(kt, S0{}, Full{});
-      kstep(kt + 1, S1{}, Full{});
-      kstep(kt + 2, S2{}, Full{});
-      kstep(kt + 3, S3{}, Full{});
+    if (nk >= kAhead + 4) {
+      issue_dma(0, S0{});
+      issue_dma(1, S1{});
+      issue_dma(2, S2{});
+      if constexpr (kAhead == 4) issue_dma(3, S3{});
+      wait_vm<(kAhead - 1) * kDma>();  // step 0 complete
+      lds_barrier();
+      read_slice(S0{}, 0, fa0, fb0);
+      for (; kt + kAhead + 3 < nk; kt += 4) {  // steady state: the copies of all four steps exist
+        kstep(kt, S0{}, Full{});
+        kstep(kt + 1, S1{}, Full{});
+        kstep(kt + 2, S2{}, Full{});
+        kstep(kt + 3, S3{}, Full{});
+      }
+    } else {
+      // copies of steps 0 .. min(nk, kAhead) - 1
+      if (nk > 0) {
+        issue_dma(0, S0{});
+        if (nk > 1) issue_dma(1, S1{});
+        if (nk > 2) issue_dma(2, S2{});
+        if (kAhead == 4 && nk > 3) issue_dma(3, S3{});
+        const int later = (nk > 1) + (nk > 2) + (kAhead == 4 && nk > 3);
+        wait_vm_le(later * kDma);  // step 0 complete
+      }
+      lds_barrier();
+      if (nk > 0) read_slice(S0{}, 0, fa0, fb0);
     }
     for (; kt < nk; kt += 4) {
       kstep(kt, S0{}, Tail{});

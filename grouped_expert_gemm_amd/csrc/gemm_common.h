@@ -54,6 +54,17 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// The same barrier, but the N most recent LDS operations of this wavefront may still be
+// in flight (LDS operations complete in order; N is capped at the counter's 15).
+template <int N>
+__device__ __forceinline__ void lds_barrier_keep() {
+  constexpr int n = N < 15 ? N : 15;
+  __builtin_amdgcn_s_waitcnt(0xC07F | (n << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ void wait_vm_le(int n) {  // n: a multiple of 4 in [0, 24]
   switch (n) {
     case 24: wait_vm<24>(); break;
