@@ -46,9 +46,6 @@
 namespace moe {
 namespace gemm {
 
-// word 3 of a raw buffer descriptor for dword loads (32-bit data format)
-constexpr int kBufferFlags = 0x00020000;
-
 template <int PL, int QL, int G, int EP>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(const Params prm) {

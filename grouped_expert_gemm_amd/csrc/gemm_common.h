@@ -23,6 +23,8 @@ __device__ __forceinline__ int mnswz(int j) { return (j << 2) ^ (((j ^ (j >> 1))
 __device__ __forceinline__ int sub_n(int s, int wn) { return (s >> 1) * 128 + wn * 64 + (s & 1) * 32; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// word 3 of a raw buffer descriptor for dword loads (32-bit data format)
+constexpr int kBufferFlags = 0x00020000;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 
