@@ -38,6 +38,9 @@ struct Params {
 
 moe_status run(const Params& p, int pl, int ql, int g, int ep, int64_t max_tiles, hipStream_t s,
                const char* what);
+// forward kernel (gemm_fwd.hip): GROUP_M, both operands KCONTIG, EPI_STORE or EPI_SWIGLU,
+// K a multiple of 64
+moe_status run_fwd(const Params& p, int ep, int64_t max_tiles, hipStream_t s, const char* what);
 
 }  // namespace gemm
 }  // namespace moe

@@ -532,6 +532,9 @@ static moe_status launch(const Params& p, int64_t max_tiles, hipStream_t s, cons
 
 moe_status run(const Params& p, int pl, int ql, int g, int ep, int64_t max_tiles, hipStream_t s,
                const char* what) {
+  // the forward projections take the 64-wide-K kernel built for K-contiguous operands
+  if (pl == KCONTIG && ql == KCONTIG && g == GROUP_M && (ep == EPI_SWIGLU || ep == EPI_STORE) && p.K % 64 == 0)
+    return run_fwd(p, ep, max_tiles, s, what);
   if (pl == KCONTIG && ql == KCONTIG && g == GROUP_M && ep == EPI_SWIGLU)
     return launch<KCONTIG, KCONTIG, GROUP_M, EPI_SWIGLU>(p, max_tiles, s, what);
   if (pl == KCONTIG && ql == KCONTIG && g == GROUP_M && ep == EPI_STORE)

@@ -11,6 +11,11 @@ namespace gemm {
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
+// LDS layout of a K-contiguous bf16 operand tile with 64-element K steps: 256 rows of
+// 128 bytes (8 chunks of 16 bytes); chunk c of row r sits at c ^ swz8(r). Any 16
+// consecutive rows then put a given logical chunk on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
 // LDS layout of an MN-contiguous operand tile: 32 k-rows of 512 bytes (32 chunks of
 // 16 bytes); chunk c of k-row r sits at c ^ mnswz(r & 3). A transposing read touches,
 // per 16 lanes, 2 adjacent chunks of 4 consecutive k-rows and, per 32 lanes, 4 chunks of

@@ -1,0 +1,349 @@
+// Persistent grouped GEMM for the forward projections: rows grouped by expert
+// (GROUP_M), both operands K-contiguous, bf16 MFMA with float32 accumulation, and the
+// plain-store or ScaledSwiGLU epilogue.
+//
+// Source: GroupedLinear and the fused GroupedLinear -> ScaledSwiGLU -> GroupedLinear
+// forward of "Efficient MoE Training for Biological Foundation Models", Challenges 1
+// and 3 (gate_up with the routing weight folded into the activation, then down).
+//
+// Same output tiling, wavefront layout, tile order and epilogues as the general kernel
+// in gemm_bf16.hip (256 x 256 tiles, 4 wavefronts of 128 x 128); what differs is the
+// copy pipeline, shaped for operands whose rows are K-contiguous:
+//   * K steps are 64 wide, so each row of a tile contributes one whole 128-byte cache
+//     line per step. Copying whole lines moves twice the bytes per cycle through a
+//     CU's global -> LDS path as copying half lines (measured on gfx950, L2-resident
+//     source), and at 32-wide steps that path runs close to full in this kernel.
+//   * LDS holds a ring of 5 half-slots of 32 KiB (all 160 KiB): step v keeps P in
+//     half-slot 2v mod 5 and Q in 2v+1 mod 5. When step kt is done with both of its
+//     half-slots, Q of step kt+2 and P of step kt+3 take them, so weight panels, which
+//     come from HBM, have about two steps to land and token panels, which other tiles
+//     have usually pulled into L2 already, one.
+//   * One barrier per step, after the third of its four k16 slices: it publishes step
+//     kt+1's copies and frees step kt's half-slots; the copies above are threaded
+//     through the fourth slice's MFMAs.
+// LDS rows are 128 bytes: chunk c of row r sits at c ^ swz8(r).
+#include <type_traits>
+
+#include "common.h"
+#include "gemm_bf16.h"
+#include "gemm_common.h"
+#include "internal.h"
+
+namespace moe {
+namespace gemm {
+
+namespace {
+constexpr int kWBK = 64;                      // K step
+constexpr int kWTile = kBM * kWBK * 2;        // one operand of one K step: a half-slot (32 KiB)
+}  // namespace
+
+template <int EP>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_fwd_kernel(const Params prm) {
+  // one array per half-slot: every LDS access names its array at compile time, so the
+  // compiler can tell a copy into one half-slot from reads of another
+  __shared__ __attribute__((aligned(1024))) uint8_t sH0[kWTile], sH1[kWTile], sH2[kWTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t sH3[kWTile], sH4[kWTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int E = prm.E;
+  const int R = (int)prm.R;
+
+  const int nwg = gridDim.x;
+  const int logical = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+
+  auto hslot = [&](auto H) -> uint8_t* {
+    if constexpr (H.value == 0) return sH0;
+    else if constexpr (H.value == 1) return sH1;
+    else if constexpr (H.value == 2) return sH2;
+    else if constexpr (H.value == 3) return sH3;
+    else return sH4;
+  };
+
+  // Tile order: expert-major, ceil(rows_e / 256) row tiles x n_tiles per expert, row
+  // tiles fastest. A workgroup's tiles only move forward, so it walks the expert
+  // offsets once (wavefront-uniform loads), making them a nondecreasing sequence inside
+  // [0, R] on the way: no access leaves the tensors.
+  auto clamp_off = [&](int v, int prev) -> int {
+    v = v < prev ? prev : v;
+    return v > R ? R : v;
+  };
+  int e_w = 0;
+  int ob = 0;
+  int oe = clamp_off(prm.offsets[1], 0);
+  int ts_w = 0;
+  int nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
+
+  const int l32 = lane & 31, lhi = lane >> 5;
+  // fragment addresses: sub-tile rows start at multiples of 32, where swz8 depends on
+  // the lane's row within the sub-tile only; k16 slice sl is logical chunk 2*sl + lhi
+  const uint32_t fragP = (uint32_t)((wn * 64 + l32) * 128);
+  const uint32_t fragQ = (uint32_t)((wm * 128 + l32) * 128);
+  uint32_t ck[4];
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) ck[sl] = (uint32_t)(((2 * sl + lhi) ^ swz8(l32)) << 4);
+  // copies: round i (0..7) of wavefront w fills LDS bytes [(4i + w) KiB, +1 KiB) of a
+  // half-slot: rows (4i + w) * 8 + (lane >> 3), physical chunk lane & 7, i.e. logical
+  // chunk (lane & 7) ^ swz8(row), which does not depend on the round
+  const int kc_row0 = wave * 8 + (lane >> 3);
+  const int kc_chunk = (lane & 7) ^ swz8(kc_row0);
+  const int nk = prm.K / kWBK;
+  constexpr int64_t kAll = 0xFFFFFFFFll;
+
+  for (int t = logical;; t += nwg) {
+    // ---------------- tile decode ----------------
+    while (e_w < E && t >= ts_w + nt_w) {
+      ts_w += nt_w;
+      ++e_w;
+      ob = oe;
+      if (e_w < E) {
+        oe = clamp_off(prm.offsets[e_w + 1], ob);
+        nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
+      }
+    }
+    if (e_w >= E) break;
+    int e = e_w, mt, nt;
+    {
+      const int local = t - ts_w;
+      const int mte = (oe - ob + kBM - 1) / kBM;
+      mt = local % mte;
+      nt = local / mte;
+    }
+    e = __builtin_amdgcn_readfirstlane(e);
+    mt = __builtin_amdgcn_readfirstlane(mt);
+    nt = __builtin_amdgcn_readfirstlane(nt);
+    const int row_beg = __builtin_amdgcn_readfirstlane(ob);
+    const int row_end = __builtin_amdgcn_readfirstlane(oe);
+    const int tile_row = row_beg + mt * kBM;
+
+    // ---------------- operands ----------------
+    // Each copy addresses the step's tile origin + this lane's offset + the round's
+    // wavefront-uniform row offset (the buffer instruction's scalar offset). Q's record
+    // count ends at the expert's last row: the rows past it fail the hardware range
+    // check (which covers the scalar offset) and land as zeros, discarded below.
+    const bf16_t* pbase = reinterpret_cast<const bf16_t*>(prm.tab[e]);
+    const char* p_tile;
+    if constexpr (EP == EPI_SWIGLU) p_tile = reinterpret_cast<const char*>(pbase + (int64_t)nt * 128 * prm.p_ld);
+    else p_tile = reinterpret_cast<const char*>(pbase + (int64_t)nt * kBN * prm.p_ld);
+    const char* q_tile = reinterpret_cast<const char*>(prm.q + (int64_t)tile_row * prm.q_ld);
+    const uint32_t p_off0 = (uint32_t)(((int64_t)kc_row0 * prm.p_ld + kc_chunk * 8) * 2);
+    const uint32_t q_off0 = (uint32_t)(((int64_t)kc_row0 * prm.q_ld + kc_chunk * 8) * 2);
+    const int64_t q_extent = (int64_t)(row_end - tile_row) * prm.q_ld * 2;
+    // SWIGLU: tile rows 128..255 of P are the up rows, I further down than the gate rows
+    const int p_up = (EP == EPI_SWIGLU) ? prm.I - 128 : 0;
+
+    // one operand of K step kt into a half-slot; round i's rows: i * 32 (+ up for i >= 4),
+    // below 2^32 bytes from the tile origin (one expert's weight)
+    auto copy_op = [&](const char* tile, uint32_t off0, int up, int64_t ld, int64_t extent, int kt, uint8_t* dst) {
+      const int64_t at = (int64_t)kt * kWBK * 2;
+      int64_t nrec = extent - at;
+      nrec = nrec < 0 ? 0 : (nrec > kAll ? kAll : nrec);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(tile + at), (short)0, (int)(uint32_t)nrec, kBufferFlags);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t rows = (uint32_t)(i * 32 + (i >= 4 ? up : 0));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 4096), 16, off0,
+                                                 (int)(rows * (uint32_t)ld * 2u), 0, 0);
+      }
+    };
+    auto copy_P = [&](int kt, auto H) { copy_op(p_tile, p_off0, p_up, prm.p_ld, kAll, kt, hslot(H) + wave * 1024); };
+    auto copy_Q = [&](int kt, auto H) { copy_op(q_tile, q_off0, 0, prm.q_ld, q_extent, kt, hslot(H) + wave * 1024); };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+    // fragments of one k16 slice: 4 of P (n sub-tiles), 4 of Q (m sub-tiles), read in
+    // the order the MFMAs consume them (P 0 with all of Q first)
+    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    auto read_slice = [&](auto HP, auto HQ, int sl, bf16x8* fa, bf16x8* fb) {
+      const uint8_t* P = hslot(HP) + fragP + ck[sl];
+      const uint8_t* Q = hslot(HQ) + fragQ + ck[sl];
+      fa[0] = *reinterpret_cast<const bf16x8*>(P);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fb[u] = *reinterpret_cast<const bf16x8*>(Q + (u * 32) * 128);
+#pragma unroll
+      for (int u = 1; u < 4; ++u) fa[u] = *reinterpret_cast<const bf16x8*>(P + ((u >> 1) * 128 + (u & 1) * 32) * 128);
+    };
+    auto mfma_slice = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+      for (int sn = 0; sn < 4; ++sn)
+#pragma unroll
+        for (int sm = 0; sm < 4; ++sm)
+          acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sn], fb[sm], acc[sn][sm], 0, 0, 0);
+    };
+    // 16 MFMAs with the 8 fragment reads of another slice between them
+    auto interleave_a = [&]() {
+      static_for<16>([&](auto I) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (decltype(I)::value & 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      });
+    };
+    // ... and the 16 copies of later steps as well
+    auto interleave_b = [&]() {
+      static_for<16>([&](auto I) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (decltype(I)::value & 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      });
+    };
+
+    // K step kt, V = kt % 5; on entry slice 0 is in fa0/fb0. Copies are issued in the
+    // order P0 Q0 P1 Q1 P2 | Q2 P3 | Q3 P4 | ..., so when step kt+1 must have landed only
+    // P of step kt+2 (the 8 most recent copies) may still be in flight.
+    // FULL: step kt+3 exists, so every branch folds away.
+    auto kstep = [&](int kt, auto V, auto FULL) {
+      constexpr int v = decltype(V)::value;
+      constexpr bool full = decltype(FULL)::value;
+      using HP = std::integral_constant<int, (2 * v) % 5>;
+      using HQ = std::integral_constant<int, (2 * v + 1) % 5>;
+      using HPn = std::integral_constant<int, (2 * v + 2) % 5>;
+      using HQn = std::integral_constant<int, (2 * v + 3) % 5>;
+      read_slice(HP{}, HQ{}, 1, fa1, fb1);
+      mfma_slice(fa0, fb0);
+      interleave_a();
+      read_slice(HP{}, HQ{}, 2, fa0, fb0);
+      mfma_slice(fa1, fb1);
+      interleave_a();
+      read_slice(HP{}, HQ{}, 3, fa1, fb1);
+      mfma_slice(fa0, fb0);
+      interleave_a();
+      if (full) wait_vm<8>();
+      else wait_vm_le(kt + 2 < nk ? 8 : 0);
+      lds_barrier();                                  // also waits for every read of step kt
+      if (full || kt + 2 < nk) copy_Q(kt + 2, HP{});  // Q of step kt+2: half-slot 2(kt+2)+1 = 2kt mod 5
+      if (full || kt + 3 < nk) copy_P(kt + 3, HQ{});  // P of step kt+3: half-slot 2(kt+3) = 2kt+1 mod 5
+      if (full || kt + 1 < nk) read_slice(HPn{}, HQn{}, 0, fa0, fb0);
+      mfma_slice(fa1, fb1);
+      interleave_b();
+    };
+    using V0 = std::integral_constant<int, 0>;
+    using V1 = std::integral_constant<int, 1>;
+    using V2 = std::integral_constant<int, 2>;
+    using V3 = std::integral_constant<int, 3>;
+    using V4 = std::integral_constant<int, 4>;
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    using H2 = std::integral_constant<int, 2>;
+    using H3 = std::integral_constant<int, 3>;
+    using H4 = std::integral_constant<int, 4>;
+    using Full = std::true_type;
+    using Tail = std::false_type;
+    // The long-K path has a prologue without branches, so the compiler's model of the
+    // copies in flight at the top of the steady-state loop is exact and it adds no
+    // waits there; short K ranges take the general prologue and the tail loop.
+    int kt = 0;
+    if (nk >= 8) {
+      copy_P(0, H0{});
+      copy_Q(0, H1{});
+      copy_P(1, H2{});
+      copy_Q(1, H3{});
+      copy_P(2, H4{});
+      wait_vm<24>();  // step 0 complete
+      lds_barrier();
+      read_slice(H0{}, H1{}, 0, fa0, fb0);
+      for (; kt + 7 < nk; kt += 5) {  // steady state: the copies of all five steps exist
+        kstep(kt, V0{}, Full{});
+        kstep(kt + 1, V1{}, Full{});
+        kstep(kt + 2, V2{}, Full{});
+        kstep(kt + 3, V3{}, Full{});
+        kstep(kt + 4, V4{}, Full{});
+      }
+    } else {
+      if (nk > 0) {
+        copy_P(0, H0{});
+        copy_Q(0, H1{});
+        if (nk > 1) {
+          copy_P(1, H2{});
+          copy_Q(1, H3{});
+        }
+        if (nk > 2) copy_P(2, H4{});
+        wait_vm_le((nk > 1) * 16 + (nk > 2) * 8);  // step 0 complete
+      }
+      lds_barrier();
+      if (nk > 0) read_slice(H0{}, H1{}, 0, fa0, fb0);
+    }
+    for (; kt < nk; kt += 5) {
+      kstep(kt, V0{}, Tail{});
+      if (kt + 1 < nk) kstep(kt + 1, V1{}, Tail{});
+      if (kt + 2 < nk) kstep(kt + 2, V2{}, Tail{});
+      if (kt + 3 < nk) kstep(kt + 3, V3{}, Tail{});
+      if (kt + 4 < nk) kstep(kt + 4, V4{}, Tail{});
+    }
+    // every wavefront is done with every half-slot before the next tile's copies
+    lds_barrier();
+
+    // ---------------- epilogue ----------------
+#pragma unroll
+    for (int sm = 0; sm < 4; ++sm) {
+      const int64_t mg = (int64_t)tile_row + wm * 128 + sm * 32 + l32;
+      if (mg >= row_end) continue;
+      if constexpr (EP == EPI_STORE) {
+#pragma unroll
+        for (int sn = 0; sn < 4; ++sn)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int64_t col = (int64_t)nt * kBN + sub_n(sn, wn) + i4 * 8 + lhi * 4;
+            uint2 vv;
+            vv.x = pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]);
+            vv.y = pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]);
+            *reinterpret_cast<uint2*>(prm.c + mg * prm.c_ld + col) = vv;
+          }
+      } else {  // EPI_SWIGLU: gate columns in sub-tiles 0-1, the matching up columns in 2-3
+        const float p = prm.prob[mg];
+        const int64_t I = prm.I;
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int64_t col = (int64_t)nt * 128 + wn * 64 + sn * 32 + i4 * 8 + lhi * 4;
+            float h[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              const float g = acc[sn][sm][i4 * 4 + x];
+              const float u = acc[sn + 2][sm][i4 * 4 + x];
+              h[x] = silu_f(g) * u * p;
+            }
+            *reinterpret_cast<uint2*>(prm.c + mg * prm.c_ld + col) =
+                make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+            if (prm.zout) {
+              bf16_t* z = prm.zout + mg * (2 * I);
+              *reinterpret_cast<uint2*>(z + col) =
+                  make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]),
+                             pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]));
+              *reinterpret_cast<uint2*>(z + I + col) =
+                  make_uint2(pack_bf16x2(acc[sn + 2][sm][i4 * 4 + 0], acc[sn + 2][sm][i4 * 4 + 1]),
+                             pack_bf16x2(acc[sn + 2][sm][i4 * 4 + 2], acc[sn + 2][sm][i4 * 4 + 3]));
+            }
+          }
+      }
+    }
+  }
+}
+
+template <int EP>
+static moe_status launch_fwd(const Params& p, int64_t max_tiles, hipStream_t s, const char* what) {
+  if (max_tiles <= 0) return MOE_OK;
+  int64_t grid = num_cus();
+  if (max_tiles < grid) grid = max_tiles;
+  hipLaunchKernelGGL((grouped_gemm_fwd_kernel<EP>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  return check_launch(what);
+}
+
+moe_status run_fwd(const Params& p, int ep, int64_t max_tiles, hipStream_t s, const char* what) {
+  if (p.K % kWBK != 0) return fail(MOE_ERR_UNSUPPORTED, std::string(what) + ": K must be a multiple of 64");
+  if (ep == EPI_SWIGLU) return launch_fwd<EPI_SWIGLU>(p, max_tiles, s, what);
+  if (ep == EPI_STORE) return launch_fwd<EPI_STORE>(p, max_tiles, s, what);
+  return fail(MOE_ERR_UNSUPPORTED, std::string(what) + ": no forward kernel for this epilogue");
+}
+
+}  // namespace gemm
+}  // namespace moe
