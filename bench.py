@@ -70,6 +70,7 @@ class Layer:
         self.src = torch.empty(R, dtype=torch.int32, device=dev)
         self.ws_perm = torch.empty(max(1, moe.workspace_size(_lib.MOE_OP_PERMUTE, None, 0, T, E, k)),
                                    dtype=torch.uint8, device=dev)
+        self.ws_gemm = moe.gemm_workspace(dev)
         self.h = torch.empty((R, I), dtype=bf, device=dev)
         self.z = torch.empty((R, 2 * I), dtype=bf, device=dev) if backward else None
         self.y = torch.empty((R, H), dtype=bf, device=dev)
@@ -110,11 +111,13 @@ class Layer:
             e0.record()
         c("gate_up", L.moe_grouped_gate_up_swiglu(E, R, H, I, BF, p(self.x_perm), None, self.t1, None,
                                                   p(self.offsets), p(self.prob_perm), p(self.h), None,
-                                                  p(self.z) if self.z is not None else None, s))
+                                                  p(self.z) if self.z is not None else None, p(self.ws_gemm),
+                                                  self.ws_gemm.numel(), s))
         if time_gate_up:
             e1.record()
             self.ev.append((e0, e1))
-        c("down", L.moe_grouped_linear(E, R, I, H, BF, p(self.h), self.t2, p(self.offsets), p(self.y), s))
+        c("down", L.moe_grouped_linear(E, R, I, H, BF, p(self.h), self.t2, p(self.offsets), p(self.y),
+                                       p(self.ws_gemm), self.ws_gemm.numel(), s))
         c("combine", L.moe_unpermute_combine(p(self.y), BF, p(self.rmap), None, T, H, k, p(self.out), s))
         if self.backward:
             c("dOut gather", L.moe_permute(p(self.dout), None, BF, T, H, E, k, None, None, 1, p(self.dy), None,

@@ -21,7 +21,7 @@ from ._lib import MOE_BF16, MOE_F32, MOE_MXFP8, MlpDesc, MoeError, check, lib, p
 
 __all__ = [
     "moe_route_topk", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
-    "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu",
+    "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu", "gemm_workspace",
     "workspace_size", "MoeError", "lib",
     "MOE_F32", "MOE_BF16", "MOE_MXFP8",
 ]
@@ -212,8 +212,17 @@ def moe_grouped_mlp_bwd(dy_perm, x_perm, z, h, prob_perm, w_gate_up, w_down, off
     return dx, dw1, dw2, dprob
 
 
-def moe_grouped_linear(x: torch.Tensor, w, offsets: torch.Tensor, out: torch.Tensor | None = None):
-    """GroupedLinear: y[r] = x[r] W_e^T for the rows of expert e. x [R, K], W_e [N, K] -> y [R, N]."""
+def gemm_workspace(device) -> torch.Tensor:
+    """A workspace for moe_grouped_linear / moe_grouped_gate_up_swiglu (split-K tail area)."""
+    return _workspace(workspace_size(_lib.MOE_OP_GROUPED_GEMM, None, 0), device)
+
+
+def moe_grouped_linear(x: torch.Tensor, w, offsets: torch.Tensor, out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None):
+    """GroupedLinear: y[r] = x[r] W_e^T for the rows of expert e. x [R, K], W_e [N, K] -> y [R, N].
+
+    workspace: optional (see gemm_workspace); without it no tile is split along K.
+    """
     ws = _experts(w)
     E = len(ws)
     N, K = ws[0].shape
@@ -221,15 +230,16 @@ def moe_grouped_linear(x: torch.Tensor, w, offsets: torch.Tensor, out: torch.Ten
     _need_cuda(x, offsets, *ws)
     y = out if out is not None else torch.empty((R, N), dtype=x.dtype, device=x.device)
     t, keep = ptr_table([t.data_ptr() for t in ws])
+    nws = workspace.numel() if workspace is not None else 0
     check("moe_grouped_linear", lib().moe_grouped_linear(E, R, K, N, _DT[x.dtype], _p(x), t, _p(offsets), _p(y),
-                                                         _stream(x.device)))
+                                                         _p(workspace), nws, _stream(x.device)))
     del keep
     return y
 
 
 def moe_grouped_gate_up_swiglu(x: torch.Tensor, w_gate_up, offsets: torch.Tensor, prob: torch.Tensor,
                                save_z: bool = False, x_scale=None, w_scale=None, out: torch.Tensor | None = None,
-                               out_scale: torch.Tensor | None = None):
+                               out_scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """GroupedLinear(gate_up) fused with ScaledSwiGLU: h = silu(x W_e[:I]^T) * (x W_e[I:]^T) * prob.
 
     bf16/f32: returns h [R, I] (and z [R, 2I] with save_z). MXFP8 (x given as uint8 codes
@@ -255,7 +265,8 @@ def moe_grouped_gate_up_swiglu(x: torch.Tensor, w_gate_up, offsets: torch.Tensor
         hs = None
         z = torch.empty((R, twoI), dtype=x.dtype, device=dev) if save_z else None
     check("moe_grouped_gate_up_swiglu", lib().moe_grouped_gate_up_swiglu(
-        E, R, H, I, dt, _p(x), _p(x_scale), t, st, _p(offsets), _p(prob), _p(h), _p(hs), _p(z), _stream(dev)))
+        E, R, H, I, dt, _p(x), _p(x_scale), t, st, _p(offsets), _p(prob), _p(h), _p(hs), _p(z), _p(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(dev)))
     del keep
     if dt == MOE_MXFP8:
         return h, hs

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = range(5)
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
-MOE_OP_PERMUTE, MOE_OP_MLP_FWD, MOE_OP_MLP_BWD = 0, 1, 2
+MOE_OP_PERMUTE, MOE_OP_MLP_FWD, MOE_OP_MLP_BWD, MOE_OP_GROUPED_GEMM = 0, 1, 2, 3
 MOE_MAX_EXPERTS = 256
 
 # every symbol include/moe.h declares
@@ -59,8 +59,9 @@ def _declare(lib):
                                 sz, vp],
         "moe_grouped_mlp_bwd": [ctypes.POINTER(MlpDesc), i64, vp, vp, vp, vp, vp, PP, PP, vp, vp, PP, PP, vp,
                                 vp, sz, vp],
-        "moe_grouped_linear": [c_int, i64, c_int, c_int, c_int, vp, PP, vp, vp, vp],
-        "moe_grouped_gate_up_swiglu": [c_int, i64, c_int, c_int, c_int, vp, vp, PP, PP, vp, vp, vp, vp, vp, vp],
+        "moe_grouped_linear": [c_int, i64, c_int, c_int, c_int, vp, PP, vp, vp, vp, sz, vp],
+        "moe_grouped_gate_up_swiglu": [c_int, i64, c_int, c_int, c_int, vp, vp, PP, PP, vp, vp, vp, vp, vp, vp, sz,
+                                       vp],
         "moe_workspace_size": [c_int, ctypes.POINTER(MlpDesc), i64, i64, c_int, c_int, ctypes.POINTER(sz)],
     }
     for name, args in sig.items():

@@ -77,6 +77,9 @@ extern "C" moe_status moe_workspace_size(moe_op op, const moe_mlp_desc* desc, in
       *bytes = op == MOE_OP_MLP_FWD ? mlp_fwd_workspace_bytes(*desc, R) : mlp_bwd_workspace_bytes(*desc, R);
       return MOE_OK;
     }
+    case MOE_OP_GROUPED_GEMM:
+      *bytes = grouped_gemm_workspace_bytes();
+      return MOE_OK;
   }
   return fail(MOE_ERR_INVALID_ARG, "moe_workspace_size: unknown op");
 }

@@ -37,7 +37,11 @@ constexpr int kWBK = 64;                      // K step
 constexpr int kWTile = kBM * kWBK * 2;        // one operand of one K step: a half-slot (32 KiB)
 }  // namespace
 
-template <int EP>
+// TAIL = false: the data-parallel tiles; TAIL = true: one K chunk of a split-K tail
+// tile per workgroup (launched after the first, same grid), written as a float32
+// partial tile. Two instantiations keep the chunk logic out of the main kernel's
+// register allocation.
+template <int EP, bool TAIL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_fwd_kernel(const Params prm) {
   // one array per half-slot: every LDS access names its array at compile time, so the
@@ -76,6 +80,39 @@ void grouped_gemm_fwd_kernel(const Params prm) {
   int oe = clamp_off(prm.offsets[1], 0);
   int ts_w = 0;
   int nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
+  const int nk = prm.K / kWBK;
+
+  // Split-K tail. All tiles are counted first; when the last round would leave at
+  // least half the workgroups idle, its `rem` tiles are cut into `split` K chunks, one
+  // per workgroup after the data-parallel rounds, each writing a float32 partial tile
+  // for run_tail_reduce to sum.
+  int total = 0;
+  {
+    int prev = 0;
+    for (int x = 0; x < E; ++x) {
+      const int en = clamp_off(prm.offsets[x + 1], prev);
+      total += ((en - prev + kBM - 1) / kBM) * prm.n_tiles;
+      prev = en;
+    }
+  }
+  const int rem = total % nwg;
+  int split = 0;
+  if (prm.tail_cap > 0 && rem > 0 && rem * 2 <= nwg) {
+    split = nwg / rem;
+    split = split > 16 ? 16 : split;
+    split = split > nk ? nk : split;
+    if (rem * split > prm.tail_cap) split = prm.tail_cap / rem;
+    if (split < 2) split = 0;
+  }
+  const int dp_total = split ? total - rem : total;
+  const int units = split ? rem * split : 0;
+  if (!TAIL && prm.tail_meta && blockIdx.x == 0 && tid == 0) {
+    prm.tail_meta[0] = split ? rem : 0;
+    prm.tail_meta[1] = split;
+    prm.tail_meta[2] = dp_total;
+    prm.tail_meta[3] = 0;
+  }
+  if (TAIL && logical >= units) return;
 
   const int l32 = lane & 31, lhi = lane >> 5;
   // fragment addresses: sub-tile rows start at multiples of 32, where swz8 depends on
@@ -90,10 +127,18 @@ void grouped_gemm_fwd_kernel(const Params prm) {
   // chunk (lane & 7) ^ swz8(row), which does not depend on the round
   const int kc_row0 = wave * 8 + (lane >> 3);
   const int kc_chunk = (lane & 7) ^ swz8(kc_row0);
-  const int nk = prm.K / kWBK;
   constexpr int64_t kAll = 0xFFFFFFFFll;
 
-  for (int t = logical;; t += nwg) {
+  // TAIL: the single work item of this workgroup is K chunk `unit % split` of tail
+  // tile `unit / split`
+  const int unit = TAIL ? logical : -1;
+  const int t_first = TAIL ? dp_total + unit / split : logical;
+  const int t_end = TAIL ? t_first + 1 : dp_total;
+  const int k0 = TAIL ? (int)((int64_t)nk * (unit % split) / split) : 0;
+  const int k1 = TAIL ? (int)((int64_t)nk * (unit % split + 1) / split) : nk;
+  const int nkl = k1 - k0;
+
+  for (int t = t_first; t < t_end; t += nwg) {
     // ---------------- tile decode ----------------
     while (e_w < E && t >= ts_w + nt_w) {
       ts_w += nt_w;
@@ -124,14 +169,18 @@ void grouped_gemm_fwd_kernel(const Params prm) {
     // wavefront-uniform row offset (the buffer instruction's scalar offset). Q's record
     // count ends at the expert's last row: the rows past it fail the hardware range
     // check (which covers the scalar offset) and land as zeros, discarded below.
+    // a K chunk [k0, k1) starts k0 steps into the rows: the tile origins move by k0
+    // steps, and Q's record count (measured from its origin) shrinks by as much
     const bf16_t* pbase = reinterpret_cast<const bf16_t*>(prm.tab[e]);
+    const int64_t kshift = (int64_t)k0 * kWBK * 2;
     const char* p_tile;
     if constexpr (EP == EPI_SWIGLU) p_tile = reinterpret_cast<const char*>(pbase + (int64_t)nt * 128 * prm.p_ld);
     else p_tile = reinterpret_cast<const char*>(pbase + (int64_t)nt * kBN * prm.p_ld);
-    const char* q_tile = reinterpret_cast<const char*>(prm.q + (int64_t)tile_row * prm.q_ld);
+    p_tile += kshift;
+    const char* q_tile = reinterpret_cast<const char*>(prm.q + (int64_t)tile_row * prm.q_ld) + kshift;
     const uint32_t p_off0 = (uint32_t)(((int64_t)kc_row0 * prm.p_ld + kc_chunk * 8) * 2);
     const uint32_t q_off0 = (uint32_t)(((int64_t)kc_row0 * prm.q_ld + kc_chunk * 8) * 2);
-    const int64_t q_extent = (int64_t)(row_end - tile_row) * prm.q_ld * 2;
+    const int64_t q_extent = (int64_t)(row_end - tile_row) * prm.q_ld * 2 - kshift;
     // SWIGLU: tile rows 128..255 of P are the up rows, I further down than the gate rows
     const int p_up = (EP == EPI_SWIGLU) ? prm.I - 128 : 0;
 
@@ -217,11 +266,11 @@ void grouped_gemm_fwd_kernel(const Params prm) {
       mfma_slice(fa0, fb0);
       interleave_a();
       if (full) wait_vm<8>();
-      else wait_vm_le(kt + 2 < nk ? 8 : 0);
+      else wait_vm_le(kt + 2 < nkl ? 8 : 0);
       lds_barrier();                                  // also waits for every read of step kt
-      if (full || kt + 2 < nk) copy_Q(kt + 2, HP{});  // Q of step kt+2: half-slot 2(kt+2)+1 = 2kt mod 5
-      if (full || kt + 3 < nk) copy_P(kt + 3, HQ{});  // P of step kt+3: half-slot 2(kt+3) = 2kt+1 mod 5
-      if (full || kt + 1 < nk) read_slice(HPn{}, HQn{}, 0, fa0, fb0);
+      if (full || kt + 2 < nkl) copy_Q(kt + 2, HP{});  // Q of step kt+2: half-slot 2(kt+2)+1 = 2kt mod 5
+      if (full || kt + 3 < nkl) copy_P(kt + 3, HQ{});  // P of step kt+3: half-slot 2(kt+3) = 2kt+1 mod 5
+      if (full || kt + 1 < nkl) read_slice(HPn{}, HQn{}, 0, fa0, fb0);
       mfma_slice(fa1, fb1);
       interleave_b();
     };
@@ -241,7 +290,7 @@ void grouped_gemm_fwd_kernel(const Params prm) {
     // copies in flight at the top of the steady-state loop is exact and it adds no
     // waits there; short K ranges take the general prologue and the tail loop.
     int kt = 0;
-    if (nk >= 8) {
+    if (nkl >= 8) {
       copy_P(0, H0{});
       copy_Q(0, H1{});
       copy_P(1, H2{});
@@ -250,7 +299,7 @@ void grouped_gemm_fwd_kernel(const Params prm) {
       wait_vm<24>();  // step 0 complete
       lds_barrier();
       read_slice(H0{}, H1{}, 0, fa0, fb0);
-      for (; kt + 7 < nk; kt += 5) {  // steady state: the copies of all five steps exist
+      for (; kt + 7 < nkl; kt += 5) {  // steady state: the copies of all five steps exist
         kstep(kt, V0{}, Full{});
         kstep(kt + 1, V1{}, Full{});
         kstep(kt + 2, V2{}, Full{});
@@ -258,30 +307,53 @@ void grouped_gemm_fwd_kernel(const Params prm) {
         kstep(kt + 4, V4{}, Full{});
       }
     } else {
-      if (nk > 0) {
+      if (nkl > 0) {
         copy_P(0, H0{});
         copy_Q(0, H1{});
-        if (nk > 1) {
+        if (nkl > 1) {
           copy_P(1, H2{});
           copy_Q(1, H3{});
         }
-        if (nk > 2) copy_P(2, H4{});
-        wait_vm_le((nk > 1) * 16 + (nk > 2) * 8);  // step 0 complete
+        if (nkl > 2) copy_P(2, H4{});
+        wait_vm_le((nkl > 1) * 16 + (nkl > 2) * 8);  // step 0 complete
       }
       lds_barrier();
-      if (nk > 0) read_slice(H0{}, H1{}, 0, fa0, fb0);
+      if (nkl > 0) read_slice(H0{}, H1{}, 0, fa0, fb0);
     }
-    for (; kt < nk; kt += 5) {
+    for (; kt < nkl; kt += 5) {
       kstep(kt, V0{}, Tail{});
-      if (kt + 1 < nk) kstep(kt + 1, V1{}, Tail{});
-      if (kt + 2 < nk) kstep(kt + 2, V2{}, Tail{});
-      if (kt + 3 < nk) kstep(kt + 3, V3{}, Tail{});
-      if (kt + 4 < nk) kstep(kt + 4, V4{}, Tail{});
+      if (kt + 1 < nkl) kstep(kt + 1, V1{}, Tail{});
+      if (kt + 2 < nkl) kstep(kt + 2, V2{}, Tail{});
+      if (kt + 3 < nkl) kstep(kt + 3, V3{}, Tail{});
+      if (kt + 4 < nkl) kstep(kt + 4, V4{}, Tail{});
     }
     // every wavefront is done with every half-slot before the next tile's copies
     lds_barrier();
 
     // ---------------- epilogue ----------------
+    if constexpr (TAIL) {  // K chunk of a tail tile: the float32 partial, all 256 rows, row-major
+      float* part = prm.tail + (int64_t)unit * (kBM * kBN);
+#pragma unroll
+      for (int sm = 0; sm < 4; ++sm)
+#pragma unroll
+        for (int sn = 0; sn < 4; ++sn)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int r = wm * 128 + sm * 32 + l32;
+            const int c = sub_n(sn, wn) + i4 * 8 + lhi * 4;
+            *reinterpret_cast<float4*>(part + r * kBN + c) =
+                make_float4(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1], acc[sn][sm][i4 * 4 + 2],
+                            acc[sn][sm][i4 * 4 + 3]);
+          }
+      if (unit % split == 0 && tid == 0) {
+        int32_t* m = prm.tail_meta + 4 + 4 * (unit / split);
+        m[0] = tile_row;
+        m[1] = row_end;
+        m[2] = nt;
+        m[3] = 0;
+      }
+      continue;
+    } else {
 #pragma unroll
     for (int sm = 0; sm < 4; ++sm) {
       const int64_t mg = (int64_t)tile_row + wm * 128 + sm * 32 + l32;
@@ -326,6 +398,57 @@ void grouped_gemm_fwd_kernel(const Params prm) {
           }
       }
     }
+    }
+  }
+}
+
+// Finishes the split-K tail: one thread sums the float32 partials of 4 consecutive
+// output columns of one row of a tail tile in chunk order and applies the epilogue.
+template <int EP>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const Params prm) {
+  const int32_t* meta = prm.tail_meta;
+  const int n_tail = meta[0];
+  const int split = meta[1];
+  constexpr int kCols = (EP == EPI_SWIGLU) ? 128 : kBN;  // output columns of a tile
+  constexpr int kThreadsPerRow = kCols / 4;
+  constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
+  constexpr int kBlocksPerTile = kBM / kRowsPerBlock;
+  const int tile_i = blockIdx.x / kBlocksPerTile;
+  if (tile_i >= n_tail) return;
+  const int32_t* m = meta + 4 + 4 * tile_i;
+  const int tile_row = m[0], row_end = m[1], nt = m[2];
+  const int r = (blockIdx.x % kBlocksPerTile) * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
+  const int64_t mg = (int64_t)tile_row + r;
+  if (mg >= row_end) return;
+  const int c = (threadIdx.x % kThreadsPerRow) * 4;
+  const float* part = prm.tail + (int64_t)tile_i * split * (kBM * kBN) + r * kBN;
+  auto sum4 = [&](int col) -> float4 {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < split; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)j * (kBM * kBN) + col);
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    return a;
+  };
+  if constexpr (EP == EPI_STORE) {
+    const float4 a = sum4(c);
+    *reinterpret_cast<uint2*>(prm.c + mg * prm.c_ld + (int64_t)nt * kBN + c) =
+        make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+  } else {  // tile columns c are gate, c + 128 the matching up
+    const float4 g = sum4(c), u = sum4(128 + c);
+    const float p = prm.prob[mg];
+    const int64_t col = (int64_t)nt * 128 + c;
+    *reinterpret_cast<uint2*>(prm.c + mg * prm.c_ld + col) =
+        make_uint2(pack_bf16x2(silu_f(g.x) * u.x * p, silu_f(g.y) * u.y * p),
+                   pack_bf16x2(silu_f(g.z) * u.z * p, silu_f(g.w) * u.w * p));
+    if (prm.zout) {
+      bf16_t* z = prm.zout + mg * (2 * (int64_t)prm.I);
+      *reinterpret_cast<uint2*>(z + col) = make_uint2(pack_bf16x2(g.x, g.y), pack_bf16x2(g.z, g.w));
+      *reinterpret_cast<uint2*>(z + prm.I + col) = make_uint2(pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w));
+    }
   }
 }
 
@@ -334,15 +457,37 @@ static moe_status launch_fwd(const Params& p, int64_t max_tiles, hipStream_t s, 
   if (max_tiles <= 0) return MOE_OK;
   int64_t grid = num_cus();
   if (max_tiles < grid) grid = max_tiles;
-  hipLaunchKernelGGL((grouped_gemm_fwd_kernel<EP>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((grouped_gemm_fwd_kernel<EP, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  moe_status st = check_launch(what);
+  if (st != MOE_OK || p.tail_cap <= 0) return st;
+  hipLaunchKernelGGL((grouped_gemm_fwd_kernel<EP, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return check_launch(what);
 }
 
 moe_status run_fwd(const Params& p, int ep, int64_t max_tiles, hipStream_t s, const char* what) {
   if (p.K % kWBK != 0) return fail(MOE_ERR_UNSUPPORTED, std::string(what) + ": K must be a multiple of 64");
-  if (ep == EPI_SWIGLU) return launch_fwd<EPI_SWIGLU>(p, max_tiles, s, what);
-  if (ep == EPI_STORE) return launch_fwd<EPI_STORE>(p, max_tiles, s, what);
-  return fail(MOE_ERR_UNSUPPORTED, std::string(what) + ": no forward kernel for this epilogue");
+  if (p.tail_cap > 0 && (!p.tail || !p.tail_meta))
+    return fail(MOE_ERR_INVALID_ARG, std::string(what) + ": split-K tail area missing");
+  moe_status st;
+  if (ep == EPI_SWIGLU) st = launch_fwd<EPI_SWIGLU>(p, max_tiles, s, what);
+  else if (ep == EPI_STORE) st = launch_fwd<EPI_STORE>(p, max_tiles, s, what);
+  else return fail(MOE_ERR_UNSUPPORTED, std::string(what) + ": no forward kernel for this epilogue");
+  if (st != MOE_OK || p.tail_cap <= 0 || max_tiles <= 0) return st;
+  return run_tail_reduce(p, ep, max_tiles, s, what);
+}
+
+moe_status run_tail_reduce(const Params& p, int ep, int64_t max_tiles, hipStream_t s, const char* what) {
+  // at most half a round of tiles is ever split: the grid covers that many
+  int64_t nwg = num_cus();
+  if (max_tiles < nwg) nwg = max_tiles;
+  const int64_t max_tail = nwg / 2;
+  if (max_tail <= 0) return MOE_OK;
+  if (ep == EPI_SWIGLU) {
+    hipLaunchKernelGGL((tail_reduce_kernel<EPI_SWIGLU>), dim3((unsigned)(max_tail * (kBM / 8))), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((tail_reduce_kernel<EPI_STORE>), dim3((unsigned)(max_tail * (kBM / 4))), dim3(256), 0, s, p);
+  }
+  return check_launch(what);
 }
 
 }  // namespace gemm

@@ -47,7 +47,7 @@ size_t mlp_fwd_workspace_bytes(const moe_mlp_desc& d, int64_t R) {
   const size_t I = d.I, H = d.H, E = d.E;
   switch (d.compute) {
     case MOE_F32: return d.save_for_bwd ? 0 : a256(R * I * 4);
-    case MOE_BF16: return d.save_for_bwd ? 0 : a256(R * I * 2);
+    case MOE_BF16: return (d.save_for_bwd ? 0 : a256(R * I * 2)) + grouped_gemm_workspace_bytes();
     case MOE_MXFP8: {
       size_t b = 0;
       if (d.act == MOE_BF16) b += a256(R * H) + a256(R * H / 32);
@@ -58,6 +58,8 @@ size_t mlp_fwd_workspace_bytes(const moe_mlp_desc& d, int64_t R) {
   }
   return 0;
 }
+
+size_t grouped_gemm_workspace_bytes() { return a256(gemm::tail_ws_bytes(num_cus())); }
 
 size_t mlp_bwd_workspace_bytes(const moe_mlp_desc& d, int64_t R) {
   const size_t I = d.I;
@@ -94,10 +96,32 @@ __global__ __launch_bounds__(256) void reduce_partials(const float* __restrict__
 }
 
 // bf16 GroupedLinear(gate_up) + ScaledSwiGLU: h [R, I] (and z [R, 2I] when z != NULL)
+// split-K tail area carved from a workspace (nullptr: the kernels never split)
+struct TailArea {
+  float* part = nullptr;
+  int32_t* meta = nullptr;
+  int cap = 0;
+};
+static TailArea tail_area(uint8_t* base) {
+  TailArea t;
+  if (!base) return t;
+  t.meta = reinterpret_cast<int32_t*>(base);
+  t.part = reinterpret_cast<float*>(base + gemm::kTailMetaSpace);
+  t.cap = num_cus();
+  return t;
+}
+static void set_tail(gemm::Params& p, const TailArea& t) {
+  p.tail = t.part;
+  p.tail_meta = t.meta;
+  p.tail_cap = t.cap;
+}
+
 static moe_status bf16_gate_up(int E, int64_t R, int H, int I, const bf16_t* x, const PtrTab& w,
-                               const int32_t* offsets, const float* prob, bf16_t* h, bf16_t* z, hipStream_t s) {
+                               const int32_t* offsets, const float* prob, bf16_t* h, bf16_t* z, hipStream_t s,
+                               const TailArea& tail = TailArea()) {
   gemm::Params p;
   std::memset(&p, 0, sizeof(p));
+  set_tail(p, tail);
   std::memcpy(p.tab, w.p, sizeof(p.tab));
   p.q = x;
   p.q_ld = H;
@@ -120,9 +144,10 @@ static moe_status bf16_gate_up(int E, int64_t R, int H, int I, const bf16_t* x, 
 
 // bf16 GroupedLinear: y [R, N] = x [R, K] W_e^T
 static moe_status bf16_linear(int E, int64_t R, int K, int N, const bf16_t* x, const PtrTab& w,
-                              const int32_t* offsets, bf16_t* y, hipStream_t s) {
+                              const int32_t* offsets, bf16_t* y, hipStream_t s, const TailArea& tail = TailArea()) {
   gemm::Params q;
   std::memset(&q, 0, sizeof(q));
+  set_tail(q, tail);
   std::memcpy(q.tab, w.p, sizeof(q.tab));
   q.q = x;
   q.q_ld = K;
@@ -191,16 +216,28 @@ extern "C" moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, c
                        prob_perm, y_perm, (uint8_t*)workspace, s);
   }
 
-  // bf16: gate_up + ScaledSwiGLU (h, optionally z), then down
+  // bf16: gate_up + ScaledSwiGLU (h, optionally z), then down; workspace: [h] [tail area]
   bf16_t* h = d.save_for_bwd ? (bf16_t*)h_save : (bf16_t*)workspace;
+  const TailArea tail = tail_area((uint8_t*)workspace + (d.save_for_bwd ? 0 : a256((size_t)R * d.I * 2)));
   st = bf16_gate_up(d.E, R, d.H, d.I, (const bf16_t*)x_perm, w1, offsets, prob_perm, h,
-                    d.save_for_bwd ? (bf16_t*)z_save : nullptr, s);
+                    d.save_for_bwd ? (bf16_t*)z_save : nullptr, s, tail);
   if (st != MOE_OK) return st;
-  return bf16_linear(d.E, R, d.I, d.H, h, w2, offsets, (bf16_t*)y_perm, s);
+  return bf16_linear(d.E, R, d.I, d.H, h, w2, offsets, (bf16_t*)y_perm, s, tail);
+}
+
+// the tail area of a caller's grouped-GEMM workspace (none if it is NULL); validated
+static moe_status gemm_workspace(void* ws, size_t bytes, const char* what, TailArea* out) {
+  *out = TailArea();
+  if (!ws) return MOE_OK;
+  if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, std::string(what) + ": workspace not 256-byte aligned");
+  if (bytes < grouped_gemm_workspace_bytes()) return fail(MOE_ERR_WORKSPACE, std::string(what) + ": workspace too small");
+  *out = tail_area((uint8_t*)ws);
+  return MOE_OK;
 }
 
 extern "C" moe_status moe_grouped_linear(int E, int64_t R, int K, int N, moe_dtype dt, const void* x,
-                                         const void* const* w, const int32_t* offsets, void* y, void* stream) {
+                                         const void* const* w, const int32_t* offsets, void* y, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
   if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_linear: E out of [1, 256]");
   if (R < 0 || R > 0x7FFFFFFF || K < 1 || N < 1) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_linear: bad R/K/N");
   if (dt != MOE_BF16 && dt != MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_linear: dtype must be BF16 or F32");
@@ -216,14 +253,16 @@ extern "C" moe_status moe_grouped_linear(int E, int64_t R, int K, int N, moe_dty
   const PtrTab tab = make_tab(w, E);
   const hipStream_t s = as_stream(stream);
   if (dt == MOE_F32) return f32::linear(E, R, K, N, (const float*)x, tab, offsets, (float*)y, s);
-  return bf16_linear(E, R, K, N, (const bf16_t*)x, tab, offsets, (bf16_t*)y, s);
+  TailArea tail;
+  if ((st = gemm_workspace(workspace, workspace_bytes, "moe_grouped_linear", &tail)) != MOE_OK) return st;
+  return bf16_linear(E, R, K, N, (const bf16_t*)x, tab, offsets, (bf16_t*)y, s, tail);
 }
 
 extern "C" moe_status moe_grouped_gate_up_swiglu(int E, int64_t R, int H, int I, moe_dtype dt, const void* x,
                                                  const uint8_t* x_scale, const void* const* w,
                                                  const uint8_t* const* w_scale, const int32_t* offsets,
                                                  const float* prob, void* h, uint8_t* h_scale, void* z_save,
-                                                 void* stream) {
+                                                 void* workspace, size_t workspace_bytes, void* stream) {
   if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gate_up_swiglu: E out of [1, 256]");
   if (R < 0 || R > 0x7FFFFFFF || H < 1 || I < 1) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gate_up_swiglu: bad R/H/I");
   if (dt != MOE_BF16 && dt != MOE_F32 && dt != MOE_MXFP8)
@@ -248,7 +287,9 @@ extern "C" moe_status moe_grouped_gate_up_swiglu(int E, int64_t R, int H, int I,
   }
   if (dt == MOE_F32)
     return f32::gate_up(E, R, H, I, (const float*)x, tab, offsets, prob, (float*)h, (float*)z_save, s);
-  return bf16_gate_up(E, R, H, I, (const bf16_t*)x, tab, offsets, prob, (bf16_t*)h, (bf16_t*)z_save, s);
+  TailArea tail;
+  if ((st = gemm_workspace(workspace, workspace_bytes, "moe_grouped_gate_up_swiglu", &tail)) != MOE_OK) return st;
+  return bf16_gate_up(E, R, H, I, (const bf16_t*)x, tab, offsets, prob, (bf16_t*)h, (bf16_t*)z_save, s, tail);
 }
 
 extern "C" moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, const void* dy_perm,

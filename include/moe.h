@@ -194,9 +194,16 @@ moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, const void* 
  *   x [R, K], W_e [N, K] ([host] array of E device pointers), y [R, N]; dt = F32 or BF16
  *   (bf16 output rounded to nearest even).
  * Shapes the kernels implement: BF16 needs N % 256 == 0 and K % 64 == 0.
+ * workspace: NULL (workspace_bytes ignored), or at least
+ *   moe_workspace_size(MOE_OP_GROUPED_GEMM, ...) bytes, 256-byte aligned, caller-owned,
+ *   contents need no initialisation; with it, a last round of tiles that would leave
+ *   most CUs idle is split along K into float32 partial tiles that a second kernel sums.
+ *   The result is the same sum in another association order. Calls sharing a workspace
+ *   must not overlap.
  */
 moe_status moe_grouped_linear(int E, int64_t R, int K, int N, moe_dtype dt, const void* x,
-                              const void* const* w, const int32_t* offsets, void* y, void* stream);
+                              const void* const* w, const int32_t* offsets, void* y, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /*
  * GroupedLinear(gate_up) fused with ScaledSwiGLU (the first kernel of the fused grouped
@@ -208,18 +215,20 @@ moe_status moe_grouped_linear(int E, int64_t R, int K, int N, moe_dtype dt, cons
  * w_scale[e] [2I, H/32], and h is written as E4M3 codes with h_scale [R, I/32]
  * (quantised from the float32 value of h by the rule of mxfp8_quantize); z_save must
  * be NULL. Shapes: H % 256 == 0 and I % 128 == 0 (BF16, MXFP8).
+ * workspace: as for moe_grouped_linear (used by BF16 only; NULL is always valid).
  */
 moe_status moe_grouped_gate_up_swiglu(int E, int64_t R, int H, int I, moe_dtype dt, const void* x,
                                       const uint8_t* x_scale, const void* const* w,
                                       const uint8_t* const* w_scale, const int32_t* offsets,
                                       const float* prob, void* h, uint8_t* h_scale, void* z_save,
-                                      void* stream);
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Operations for moe_workspace_size. */
 typedef enum {
   MOE_OP_PERMUTE = 0,  /* T = token count, E, k used; desc may be NULL */
   MOE_OP_MLP_FWD = 1,  /* desc and R used */
-  MOE_OP_MLP_BWD = 2   /* desc and R used */
+  MOE_OP_MLP_BWD = 2,  /* desc and R used */
+  MOE_OP_GROUPED_GEMM = 3  /* moe_grouped_linear / moe_grouped_gate_up_swiglu; no argument used */
 } moe_op;
 
 /* Workspace bytes an operation needs (0 is possible). bytes is a [host] pointer. */

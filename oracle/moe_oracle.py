@@ -33,7 +33,8 @@ from .mxfp8 import mxfp8_qdq
 
 __all__ = [
     "route_topk", "permute", "silu", "expert_ffn", "moe_ffn_forward",
-    "grouped_mlp_forward", "grouped_mlp_forward_mxfp8", "unpermute_combine",
+    "grouped_mlp_forward",
+    "grouped_linear", "grouped_mlp_forward_mxfp8", "unpermute_combine",
     "grouped_mlp_backward", "moe_ffn_backward", "gather_rows",
 ]
 
@@ -178,6 +179,20 @@ def grouped_mlp_forward(x_perm, w_gate_up, w_down, offsets, prob_perm):
         z[a:b] = Z
         h[a:b] = Hs
     return y, z, h
+
+
+def grouped_linear(x_perm, w, offsets):
+    """GroupedLinear (Challenge 1): for expert e, y[r] = x[r] W_e^T for the rows
+    r in [offsets[e], offsets[e+1]); one weight [N, K] per expert. float64."""
+    x = np.asarray(x_perm, dtype=f64)
+    off = np.asarray(offsets, dtype=np.int64)
+    E, N, K = w.shape
+    y = np.zeros((x.shape[0], N), f64)
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if a < b:
+            y[a:b] = x[a:b] @ np.asarray(w[e], dtype=f64).T
+    return y
 
 
 def grouped_mlp_forward_mxfp8(x_perm, w_gate_up, w_down, offsets, prob_perm):

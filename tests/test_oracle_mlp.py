@@ -221,3 +221,30 @@ def test_grouped_backward_equals_loop_backward():
     np.testing.assert_allclose(gb["dw_down"], gl["dw_down"], rtol=1e-11, atol=1e-13)
     dp = gb["dprob_perm"][m["row_id_map"]].reshape(T, k)
     np.testing.assert_allclose(dp, gl["drouting_weights"], rtol=1e-11, atol=1e-13)
+
+
+def test_grouped_linear_brute_force_and_down_projection():
+    """GroupedLinear: a triple loop on a tiny ragged case with an empty expert, and
+    the down projection inside the grouped MLP (y = h W2^T per expert)."""
+    rng = np.random.default_rng(7)
+    E, N, K = 3, 5, 4
+    sizes = [2, 0, 3]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    x = rng.standard_normal((off[-1], K))
+    w = rng.standard_normal((E, N, K))
+    y = oracle.grouped_linear(x, w, off)
+    for e in range(E):
+        for r in range(off[e], off[e + 1]):
+            for n in range(N):
+                acc = 0.0
+                for kk in range(K):
+                    acc += x[r, kk] * w[e, n, kk]
+                assert abs(y[r, n] - acc) <= 1e-12 * max(1.0, abs(acc))
+    inp = _tiny()
+    idx, p = oracle.route_topk(inp.logits, 2)
+    m = oracle.permute(idx, 6)
+    pp = p.ravel()[m["src_token"] * 2 + m["src_slot"]]
+    yf, z, h = oracle.grouped_mlp_forward(inp.x[m["src_token"]], inp.w1, inp.w2, m["offsets"], pp)
+    assert np.allclose(oracle.grouped_linear(h, inp.w2, m["offsets"]), yf, rtol=0, atol=1e-12)
+    # the gate_up projection is GroupedLinear with the [2I, H] weight
+    assert np.allclose(oracle.grouped_linear(inp.x[m["src_token"]], inp.w1, m["offsets"]), z, rtol=0, atol=1e-12)
