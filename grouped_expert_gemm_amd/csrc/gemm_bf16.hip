@@ -46,7 +46,10 @@
 namespace moe {
 namespace gemm {
 
-template <int PL, int QL, int G, int EP>
+// TAIL (GROUP_M, EPI_STORE only): one K chunk of a split-K tail tile per workgroup,
+// written as a float32 partial tile (see the forward kernel); launched after the
+// TAIL = false kernel, which skips those tiles.
+template <int PL, int QL, int G, int EP, bool TAIL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(const Params prm) {
   // one array per ring slot and operand: every LDS access below names its array at
@@ -97,6 +100,31 @@ void grouped_gemm_kernel(const Params prm) {
   const int nwg = gridDim.x;
   const int logical = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
 
+  // split-K tail (GROUP_M, EPI_STORE): the same rule as the forward kernel's
+  constexpr bool kCanSplit = G == GROUP_M && EP == EPI_STORE;
+  const int nk_all = (G == GROUP_M) ? prm.K / kBK : 0;
+  const int rem = total % nwg;
+  int split = 0;
+  if (kCanSplit && prm.tail_cap > 0 && rem > 0 && rem * 2 <= nwg) {
+    split = nwg / rem;
+    split = split > 16 ? 16 : split;
+    split = split > nk_all ? nk_all : split;
+    if (rem * split > prm.tail_cap) split = prm.tail_cap / rem;
+    if (split < 2) split = 0;
+  }
+  const int dp_total = split ? total - rem : total;
+  const int units = split ? rem * split : 0;
+  if (kCanSplit && !TAIL && prm.tail_meta && blockIdx.x == 0 && tid == 0) {
+    prm.tail_meta[0] = split ? rem : 0;
+    prm.tail_meta[1] = split;
+    prm.tail_meta[2] = dp_total;
+    prm.tail_meta[3] = 0;
+  }
+  if (TAIL && logical >= units) return;
+  const int unit = TAIL ? logical : -1;
+  const int t_first = TAIL ? dp_total + unit / split : logical;
+  const int t_end = TAIL ? t_first + 1 : dp_total;
+
   auto slotP = [&](auto S) -> uint8_t* {
     if constexpr (S.value == 0) return sP0;
     else if constexpr (S.value == 1) return sP1;
@@ -110,7 +138,7 @@ void grouped_gemm_kernel(const Params prm) {
     else return sQ3;
   };
 
-  for (int t = logical; t < total; t += nwg) {
+  for (int t = t_first; t < t_end; t += nwg) {
     // ---------------- tile decode ----------------
     int e, mt, nt;
     if constexpr (G == GROUP_M) {
@@ -157,8 +185,13 @@ void grouped_gemm_kernel(const Params prm) {
     // K range
     int nk;
     int kbeg;  // first K row of an MN-contiguous operand (GROUP_K: the expert's first token row)
+    int k0 = 0;  // TAIL: the chunk's first K step (the tile origins move there)
     if constexpr (G == GROUP_M) {
-      nk = prm.K / kBK;
+      nk = nk_all;
+      if constexpr (TAIL) {
+        k0 = (int)((int64_t)nk_all * (unit % split) / split);
+        nk = (int)((int64_t)nk_all * (unit % split + 1) / split) - k0;
+      }
       kbeg = 0;
     } else {
       nk = (row_end - row_beg + kBK - 1) / kBK;
@@ -213,6 +246,10 @@ void grouped_gemm_kernel(const Params prm) {
         q_off[i] = (uint32_t)(((int64_t)r * prm.q_ld + (((lane & 31) ^ mnswz(r & 3)) * 8)) * 2);
       }
       q_step = (int64_t)kBK * prm.q_ld * 2;
+    }
+    if constexpr (TAIL) {  // GROUP_M operands are not range-checked: moving the origins suffices
+      p_tile += (int64_t)k0 * p_step;
+      q_tile += (int64_t)k0 * q_step;
     }
 
     // bytes addressable from each tile origin: GROUP_K token rows end at the expert's
@@ -418,6 +455,29 @@ void grouped_gemm_kernel(const Params prm) {
     lds_barrier();
 
     // ---------------- epilogue ----------------
+    if constexpr (TAIL) {  // K chunk of a tail tile: the float32 partial, all 256 rows, row-major
+      float* part_tile = prm.tail + (int64_t)unit * (kBM * kBN);
+#pragma unroll
+      for (int sm = 0; sm < 4; ++sm)
+#pragma unroll
+        for (int sn = 0; sn < 4; ++sn)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int r = wm * 128 + sm * 32 + l32;
+            const int c = sub_n(sn, wn) + i4 * 8 + lhi * 4;
+            *reinterpret_cast<float4*>(part_tile + r * kBN + c) =
+                make_float4(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1], acc[sn][sm][i4 * 4 + 2],
+                            acc[sn][sm][i4 * 4 + 3]);
+          }
+      if (unit % split == 0 && tid == 0) {
+        int32_t* m = prm.tail_meta + 4 + 4 * (unit / split);
+        m[0] = row_beg + mt * kBM;
+        m[1] = row_end;
+        m[2] = nt;
+        m[3] = 0;
+      }
+      continue;
+    }
 #pragma unroll
     for (int sm = 0; sm < 4; ++sm) {
       const int m_local = wm * 128 + sm * 32 + l32;
@@ -526,8 +586,16 @@ static moe_status launch(const Params& p, int64_t max_tiles, hipStream_t s, cons
   if (max_tiles <= 0) return MOE_OK;
   int64_t grid = num_cus();
   if (max_tiles < grid) grid = max_tiles;
-  hipLaunchKernelGGL((grouped_gemm_kernel<PL, QL, G, EP>), dim3((unsigned)grid), dim3(256), 0, s, p);
-  return check_launch(what);
+  hipLaunchKernelGGL((grouped_gemm_kernel<PL, QL, G, EP, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  moe_status st = check_launch(what);
+  if constexpr (G == GROUP_M && EP == EPI_STORE) {
+    if (st != MOE_OK || p.tail_cap <= 0) return st;
+    if (!p.tail || !p.tail_meta) return fail(MOE_ERR_INVALID_ARG, std::string(what) + ": split-K tail area missing");
+    hipLaunchKernelGGL((grouped_gemm_kernel<PL, QL, G, EP, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    if ((st = check_launch(what)) != MOE_OK) return st;
+    return run_tail_reduce(p, EP, max_tiles, s, what);
+  }
+  return st;
 }
 
 moe_status run(const Params& p, int pl, int ql, int g, int ep, int64_t max_tiles, hipStream_t s,

@@ -64,7 +64,7 @@ size_t grouped_gemm_workspace_bytes() { return a256(gemm::tail_ws_bytes(num_cus(
 size_t mlp_bwd_workspace_bytes(const moe_mlp_desc& d, int64_t R) {
   const size_t I = d.I;
   if (d.compute == MOE_F32) return a256(4 * R * I * 4);
-  return a256(R * 2 * I * 2) + a256((size_t)2 * (I / 256) * R * 4);
+  return a256(R * 2 * I * 2) + a256((size_t)2 * (I / 256) * R * 4) + grouped_gemm_workspace_bytes();
 }
 
 static moe_status check_table(const void* const* t, int E, size_t align, const char* what) {
@@ -334,6 +334,8 @@ extern "C" moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, c
   bf16_t* dz = (bf16_t*)ws;
   ws += a256(R * 2 * I * 2);
   float* part = (float*)ws;
+  ws += a256((size_t)2 * (I / 256) * R * 4);
+  const TailArea tail = tail_area(ws);  // split-K tail of the gate_up dgrad
   const int64_t mtiles = (R + gemm::kBM - 1) / gemm::kBM + d.E;
 
   if (R > 0) {
@@ -379,6 +381,7 @@ extern "C" moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, c
     q.E = d.E;
     q.I = (int)I;
     q.n_tiles = (int)(H / gemm::kBN);
+    set_tail(q, tail);
     st = gemm::run(q, gemm::MNCONTIG, gemm::KCONTIG, gemm::GROUP_M, gemm::EPI_STORE, mtiles * q.n_tiles, s,
                    "moe_grouped_mlp_bwd(gate_up dgrad)");
     if (st != MOE_OK) return st;
