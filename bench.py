@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 METRIC = "grouped-MLP TFLOP/s fwd and fwd+bwd, Mixtral-8x7B layer; % MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "grouped_expert_gemm_amd", "csrc", "gemm_bf16.hip")
+KERNEL_SRC = os.path.join(ROOT, "grouped_expert_gemm_amd", "csrc", "gemm_fwd.hip")
 
 
 def log(*a):
@@ -311,7 +311,7 @@ def main():
                    "step": "route + permute + gate_up/ScaledSwiGLU + down + combine (forward)",
                    "flop_per_step": flop},
         "pct_of_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
-        "roofline": {"kernel": "grouped gate_up + ScaledSwiGLU (grouped_gemm_kernel<K,K,GROUP_M,SWIGLU>)",
+        "roofline": {"kernel": "grouped gate_up + ScaledSwiGLU (grouped_gemm_fwd_kernel<EPI_SWIGLU>)",
                      "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "avg_launch_ms": round(gate_ms, 4), "traffic": traffic},
