@@ -455,6 +455,126 @@ void grouped_gemm_kernel(const Params prm) {
     lds_barrier();
 
     // ---------------- epilogue ----------------
+    if constexpr (EP == EPI_DSWIGLU) {
+      // dSwiGLU through LDS (free after the K loop), in two passes over 128 of the 256
+      // columns: z's gate and up halves are copied in with coalesced 16-byte copies
+      // (rows of 256 bytes, chunk c of row r at c ^ (r & 15); gate rows r in sP[r / 64],
+      // up rows in sQ[r / 64]; rows past the expert read as zeros), every lane turns its
+      // accumulators and z values into dG, dU in place, and the tile leaves with
+      // coalesced 16-byte stores. In the accumulator layout each load would touch 32
+      // rows x 16 bytes, one latency-bound round trip per 8 bytes a lane needs.
+      // The lane offsets below do not change from tile to tile; computed from opaque
+      // copies of the lane and wavefront numbers they stay inside the epilogue instead
+      // of being hoisted out of the tile loop and held across the K loop, which has no
+      // registers to spare.
+      int ln = lane, wv = __builtin_amdgcn_readfirstlane(wave);
+      asm volatile("" : "+v"(ln));
+      asm volatile("" : "+s"(wv));
+      const int em = wv >> 1, en = wv & 1, e32 = ln & 31, ehi = ln >> 5;
+      const int tile_row = row_beg + mt * kBM;
+      const int valid_rows = min(row_end - tile_row, kBM);
+      const int64_t I = prm.I;
+      const int64_t zld = 2 * I;  // z and dz row length
+      float pr[4], dpart[4];
+#pragma unroll
+      for (int sm = 0; sm < 4; ++sm) {
+        const int64_t mg = (int64_t)tile_row + em * 128 + sm * 32 + e32;
+        pr[sm] = mg < row_end ? prm.prob[mg] : 0.f;
+        dpart[sm] = 0.f;
+      }
+      auto arrP = [&](int a) -> uint8_t* { return a == 0 ? sP0 : a == 1 ? sP1 : a == 2 ? sP2 : sP3; };
+      auto arrQ = [&](int a) -> uint8_t* { return a == 0 ? sQ0 : a == 1 ? sQ1 : a == 2 ? sQ2 : sQ3; };
+      const char* zt = reinterpret_cast<const char*>(prm.zin + (int64_t)tile_row * zld);
+      char* dzt = reinterpret_cast<char*>(prm.c + (int64_t)tile_row * prm.c_ld);
+      static_for<2>([&](auto CC) {
+        constexpr int c = decltype(CC)::value;
+        const int64_t col0 = (int64_t)nt * kBN + c * 128;  // first z column of the pass (gate half)
+        // copy in: wavefront w takes rows [64w, 64w + 64) of both halves, 4 rows per copy
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int64_t colb = (col0 + half * I) * 2;
+          const int64_t nrec = (int64_t)valid_rows * zld * 2 - colb;
+          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(zt + colb), (short)0, (int)(uint32_t)(nrec < 0 ? 0 : nrec), kBufferFlags);
+          uint8_t* dst = (half ? arrQ(wv) : arrP(wv));
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int rr = wv * 64 + 4 * i + (ln >> 4);
+            const int g = (ln & 15) ^ (rr & 15);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 1024), 16,
+                                                     (uint32_t)((ln >> 4) * zld * 2 + g * 16),
+                                                     (int)((uint32_t)(wv * 64 + 4 * i) * (uint32_t)(zld * 2)), 0, 0);
+          }
+        }
+        wait_vm<0>();
+        lds_barrier();
+        // dG, dU in place
+#pragma unroll
+        for (int sm = 0; sm < 4; ++sm) {
+          const int r = em * 128 + sm * 32 + e32;
+          uint8_t* gP = arrP(r >> 6) + (r & 63) * 256;
+          uint8_t* gQ = arrQ(r >> 6) + (r & 63) * 256;
+#pragma unroll
+          for (int sq = 0; sq < 2; ++sq) {
+            const int sn = 2 * c + sq;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const int ch = en * 8 + sq * 4 + i4;
+              const uint32_t off = (uint32_t)(((ch ^ (r & 15)) << 4) + ehi * 8);
+              const uint2 gz = *reinterpret_cast<const uint2*>(gP + off);
+              const uint2 uz = *reinterpret_cast<const uint2*>(gQ + off);
+              const float gv[4] = {bf16_to_f32(gz.x & 0xFFFFu), bf16_to_f32(gz.x >> 16),
+                                   bf16_to_f32(gz.y & 0xFFFFu), bf16_to_f32(gz.y >> 16)};
+              const float uv[4] = {bf16_to_f32(uz.x & 0xFFFFu), bf16_to_f32(uz.x >> 16),
+                                   bf16_to_f32(uz.y & 0xFFFFu), bf16_to_f32(uz.y >> 16)};
+              float dg[4], du[4];
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const float dh = acc[sn][sm][i4 * 4 + v];
+                const float gg = gv[v], u = uv[v];
+                const float sg = 1.f / (1.f + __expf(-gg));
+                const float sl = gg * sg;
+                dpart[sm] += dh * sl * u;
+                const float da = dh * pr[sm];
+                dg[v] = da * u * sg * (1.f + gg * (1.f - sg));
+                du[v] = da * sl;
+              }
+              *reinterpret_cast<uint2*>(gP + off) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+              *reinterpret_cast<uint2*>(gQ + off) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+            }
+          }
+          // the row's dprob sum is formed here, not deferred to its use after the stores
+          // with every product it needs kept live
+          asm volatile("" : "+v"(dpart[sm]));
+        }
+        lds_barrier();
+        // store out: wavefront w stores rows [64w, 64w + 64) of both halves
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint8_t* src = half ? arrQ(wv) : arrP(wv);
+          const int64_t colb = (col0 + half * I) * 2;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int rl = 4 * i + (ln >> 4);  // row within the wavefront's 64
+            const int rr = wv * 64 + rl;
+            const int pch = ln & 15;
+            const uint4 v = *reinterpret_cast<const uint4*>(src + rl * 256 + ((pch ^ (rr & 15)) << 4));
+            if (rr < valid_rows)
+              *reinterpret_cast<uint4*>(dzt + (int64_t)rr * prm.c_ld * 2 + colb + pch * 16) = v;
+          }
+        }
+        lds_barrier();  // every read of the staging area is done before it is reused
+      });
+      // dprob partial of each row: the 64 columns of this wavefront, both lanes of the row
+#pragma unroll
+      for (int sm = 0; sm < 4; ++sm) {
+        float pt = dpart[sm];
+        pt += __shfl_xor(pt, 32);
+        const int64_t mg = (int64_t)tile_row + em * 128 + sm * 32 + e32;
+        if (mg < row_end && ehi == 0) prm.part[(int64_t)(nt * 2 + en) * prm.R + mg] = pt;
+      }
+      continue;
+    }
     if constexpr (TAIL) {  // K chunk of a tail tile: the float32 partial, all 256 rows, row-major
       float* part_tile = prm.tail + (int64_t)unit * (kBM * kBN);
 #pragma unroll
@@ -539,42 +659,6 @@ void grouped_gemm_kernel(const Params prm) {
                 }
               }
           }
-        } else {  // EPI_DSWIGLU: acc holds dH for intermediate columns
-          float part = 0.f;
-          if (valid) {
-            const float p = prm.prob[mg];
-            const int64_t I = prm.I;
-            const bf16_t* z = prm.zin + mg * (2 * I);
-            bf16_t* dz = prm.c + mg * prm.c_ld;
-#pragma unroll
-            for (int sn = 0; sn < 4; ++sn)
-#pragma unroll
-              for (int i4 = 0; i4 < 4; ++i4) {
-                const int64_t col = (int64_t)nt * kBN + sub_n(sn, wn) + i4 * 8 + lhi * 4;
-                const uint2 gz = *reinterpret_cast<const uint2*>(z + col);
-                const uint2 uz = *reinterpret_cast<const uint2*>(z + I + col);
-                const float gv[4] = {bf16_to_f32(gz.x & 0xFFFFu), bf16_to_f32(gz.x >> 16),
-                                     bf16_to_f32(gz.y & 0xFFFFu), bf16_to_f32(gz.y >> 16)};
-                const float uv[4] = {bf16_to_f32(uz.x & 0xFFFFu), bf16_to_f32(uz.x >> 16),
-                                     bf16_to_f32(uz.y & 0xFFFFu), bf16_to_f32(uz.y >> 16)};
-                float dg[4], du[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                  const float dh = acc[sn][sm][i4 * 4 + v];
-                  const float g = gv[v], u = uv[v];
-                  const float sg = 1.f / (1.f + __expf(-g));
-                  const float sl = g * sg;
-                  part += dh * sl * u;
-                  const float da = dh * p;
-                  dg[v] = da * u * sg * (1.f + g * (1.f - sg));
-                  du[v] = da * sl;
-                }
-                *reinterpret_cast<uint2*>(dz + col) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-                *reinterpret_cast<uint2*>(dz + I + col) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-              }
-          }
-          part += __shfl_xor(part, 32);
-          if (valid && lhi == 0) prm.part[(int64_t)(nt * 2 + wn) * prm.R + mg] = part;
         }
       }
     }
