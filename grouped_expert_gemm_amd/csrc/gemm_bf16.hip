@@ -598,6 +598,47 @@ void grouped_gemm_kernel(const Params prm) {
       }
       continue;
     }
+    if constexpr (G == GROUP_K) {
+      // The weight-gradient tile (all 256 x 256 entries inside the output) leaves through
+      // LDS, idle after the K loop: 512-byte rows, chunk c of row r at c ^ (r & 31), rows
+      // 32a .. 32a + 31 in array a (sP0..sP3, then sQ0..sQ3). Written from the
+      // accumulators, each store instruction would touch 32 rows x 16 bytes; read back
+      // row-contiguous it touches 2 rows x 512 bytes, an eighth of the cache lines.
+      int ln = lane, wv = __builtin_amdgcn_readfirstlane(wave);
+      asm volatile("" : "+v"(ln));  // keep the lane offsets inside the epilogue
+      const int em = wv >> 1, en = wv & 1, e32 = ln & 31, ehi = ln >> 5;
+      auto arr = [&](int a) -> uint8_t* {
+        return a < 4 ? (a == 0 ? sP0 : a == 1 ? sP1 : a == 2 ? sP2 : sP3)
+                     : (a == 4 ? sQ0 : a == 5 ? sQ1 : a == 6 ? sQ2 : sQ3);
+      };
+#pragma unroll
+      for (int sm = 0; sm < 4; ++sm) {
+        uint8_t* rowp = arr(em * 4 + sm) + e32 * 512;
+#pragma unroll
+        for (int sn = 0; sn < 4; ++sn)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int ch = (sn >> 1) * 16 + en * 8 + (sn & 1) * 4 + i4;
+            uint2 v;
+            v.x = pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]);
+            v.y = pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]);
+            *reinterpret_cast<uint2*>(rowp + ((ch ^ e32) << 4) + ehi * 8) = v;
+          }
+      }
+      lds_barrier();
+      char* ct = reinterpret_cast<char*>(const_cast<void*>(prm.tab[e])) +
+                 ((int64_t)mt * kBM * prm.c_ld + (int64_t)nt * kBN) * 2;
+      const int64_t ldb = prm.c_ld * 2;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {  // wavefront w: rows [64w, 64w + 64), 2 per store
+        const int r = wv * 64 + 2 * i + ehi;
+        const uint4 v = *reinterpret_cast<const uint4*>(arr(wv * 2 + (i >> 4)) + (r & 31) * 512 +
+                                                         (((ln & 31) ^ (r & 31)) << 4));
+        *reinterpret_cast<uint4*>(ct + r * ldb + (ln & 31) * 16) = v;
+      }
+      lds_barrier();  // the staging area is read out before the next tile's copies land
+      continue;
+    }
 #pragma unroll
     for (int sm = 0; sm < 4; ++sm) {
       const int m_local = wm * 128 + sm * 32 + l32;
