@@ -32,6 +32,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kBufferFlags = 0x00020000;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 
 // f(integral_constant<0>) ... f(integral_constant<N-1>), unrolled at compile time
 template <int N, int I = 0, typename F>

@@ -354,50 +354,94 @@ void grouped_gemm_fwd_kernel(const Params prm) {
       }
       continue;
     } else {
+      // The output leaves through LDS, idle after the K loop, in blocks of 256 rows x 128
+      // columns of bf16: 256-byte rows, chunk c of row r at c ^ (r & 15), rows 0-127 in
+      // the first array of a pair and 128-255 in the second. Each wavefront writes its
+      // accumulator values (8 bytes per lane, 32 rows per instruction), and after a
+      // barrier reads back and stores 4 whole rows per instruction, 16 bytes per lane,
+      // skipping rows past the expert. Column block b of the accumulators is sub-tiles
+      // 2b and 2b + 1: chunk wn * 8 + (sn & 1) * 4 + i4 of the block.
+      int ln = lane, wv = __builtin_amdgcn_readfirstlane(wave);
+      asm volatile("" : "+v"(ln));  // keep the lane offsets inside the epilogue
+      const int em = wv >> 1, en = wv & 1, e32 = ln & 31, ehi = ln >> 5;
+      const int valid = min(row_end - tile_row, kBM);
+      // LDS byte offset of this lane's 8 bytes in row (em * 128 + sm * 32 + e32) & 127
+      auto put = [&](uint8_t* arr, int sm, int sq, int i4, uint2 v) {
+        const int rr = sm * 32 + e32;
+        const int ch = en * 8 + sq * 4 + i4;
+        *reinterpret_cast<uint2*>(arr + rr * 256 + ((ch ^ (rr & 15)) << 4) + ehi * 8) = v;
+      };
+      // 16 stores of 4 rows: wavefront w takes rows [64w, 64w + 64) of the block. Buffer
+      // stores: the row goes into the scalar offset, and rows past the expert fall
+      // outside the descriptor's range, where stores are dropped.
+      auto drain = [&](const uint8_t* arr, bf16_t* dst, int64_t ld) {
+        const int64_t ldb = ld * 2;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(dst + (int64_t)tile_row * ld), (short)0, (int)(uint32_t)(valid * ldb), kBufferFlags);
+        const int pc = ln & 15;
+        const uint32_t vo = (uint32_t)((ln >> 4) * ldb + pc * 16);
 #pragma unroll
-    for (int sm = 0; sm < 4; ++sm) {
-      const int64_t mg = (int64_t)tile_row + wm * 128 + sm * 32 + l32;
-      if (mg >= row_end) continue;
-      if constexpr (EP == EPI_STORE) {
+        for (int i = 0; i < 16; ++i) {
+          const int rl = (wv & 1) * 64 + 4 * i + (ln >> 4);  // row within the array
+          const v4u32 v = *reinterpret_cast<const v4u32*>(arr + rl * 256 + ((pc ^ (rl & 15)) << 4));
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, vo, (int)((wv * 64 + 4 * i) * ldb), 0);
+        }
+      };
+      auto acc_block = [&](int b, uint8_t* arr0, uint8_t* arr1) {
+        uint8_t* arr = em ? arr1 : arr0;
 #pragma unroll
-        for (int sn = 0; sn < 4; ++sn)
+        for (int sm = 0; sm < 4; ++sm)
 #pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const int64_t col = (int64_t)nt * kBN + sub_n(sn, wn) + i4 * 8 + lhi * 4;
-            uint2 vv;
-            vv.x = pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]);
-            vv.y = pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]);
-            *reinterpret_cast<uint2*>(prm.c + mg * prm.c_ld + col) = vv;
-          }
-      } else {  // EPI_SWIGLU: gate columns in sub-tiles 0-1, the matching up columns in 2-3
-        const float p = prm.prob[mg];
-        const int64_t I = prm.I;
+          for (int sq = 0; sq < 2; ++sq)
 #pragma unroll
-        for (int sn = 0; sn < 2; ++sn)
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const int64_t col = (int64_t)nt * 128 + wn * 64 + sn * 32 + i4 * 8 + lhi * 4;
-            float h[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              const float g = acc[sn][sm][i4 * 4 + x];
-              const float u = acc[sn + 2][sm][i4 * 4 + x];
-              h[x] = silu_f(g) * u * p;
-            }
-            *reinterpret_cast<uint2*>(prm.c + mg * prm.c_ld + col) =
-                make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-            if (prm.zout) {
-              bf16_t* z = prm.zout + mg * (2 * I);
-              *reinterpret_cast<uint2*>(z + col) =
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const int sn = 2 * b + sq;
+              put(arr, sm, sq, i4,
                   make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]),
-                             pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]));
-              *reinterpret_cast<uint2*>(z + I + col) =
-                  make_uint2(pack_bf16x2(acc[sn + 2][sm][i4 * 4 + 0], acc[sn + 2][sm][i4 * 4 + 1]),
-                             pack_bf16x2(acc[sn + 2][sm][i4 * 4 + 2], acc[sn + 2][sm][i4 * 4 + 3]));
+                             pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3])));
             }
-          }
+      };
+      if constexpr (EP == EPI_STORE) {
+        acc_block(0, sH0, sH1);
+        acc_block(1, sH2, sH3);
+        lds_barrier();
+        bf16_t* c0 = prm.c + (int64_t)nt * kBN;
+        drain(wv < 2 ? sH0 : sH1, c0, prm.c_ld);
+        drain(wv < 2 ? sH2 : sH3, c0 + 128, prm.c_ld);
+        lds_barrier();  // read out before the next tile's copies land
+      } else {  // EPI_SWIGLU: gate columns in block 0, the matching up columns in block 1
+        uint8_t* harr = em ? sH1 : sH0;
+#pragma unroll
+        for (int sm = 0; sm < 4; ++sm) {
+          const int mr = tile_row + em * 128 + sm * 32 + e32;
+          const float p = prm.prob[mr < row_end ? mr : row_end - 1];  // rows past the expert: not stored
+#pragma unroll
+          for (int sq = 0; sq < 2; ++sq)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              float h[4];
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                const float g = acc[sq][sm][i4 * 4 + x];
+                const float u = acc[sq + 2][sm][i4 * 4 + x];
+                h[x] = silu_f(g) * u * p;
+              }
+              put(harr, sm, sq, i4, make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])));
+            }
+        }
+        const int64_t I = prm.I;
+        if (prm.zout) acc_block(0, sH2, sH3);
+        lds_barrier();
+        drain(wv < 2 ? sH0 : sH1, prm.c + (int64_t)nt * 128, prm.c_ld);
+        if (prm.zout) {
+          drain(wv < 2 ? sH2 : sH3, prm.zout + (int64_t)nt * 128, 2 * I);
+          lds_barrier();
+          acc_block(1, sH0, sH1);
+          lds_barrier();
+          drain(wv < 2 ? sH0 : sH1, prm.zout + I + (int64_t)nt * 128, 2 * I);
+        }
+        lds_barrier();  // read out before the next tile's copies land
       }
-    }
     }
   }
 }
