@@ -72,35 +72,50 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(const int32_t* __rest
                                                            int E, int32_t* __restrict__ base,
                                                            int32_t* __restrict__ split_sizes,
                                                            int32_t* __restrict__ offsets) {
-  __shared__ int32_t tot[MOE_MAX_EXPERTS];
+  // counts [nb, E] pass through LDS in chunks of whole block rows, read and written
+  // coalesced; thread e runs down column e inside LDS (the running count stays in a
+  // register across chunks). A second coalesced pass adds the expert offsets.
+  constexpr int kChunk = 8192;  // LDS entries per chunk (32 KiB)
+  __shared__ int32_t buf[kChunk];
   __shared__ int32_t off[MOE_MAX_EXPERTS + 1];
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 256) {
-    int32_t run = 0;
-    for (int64_t b = 0; b < nb; ++b) {
-      int32_t c = counts[b * E + e];
-      base[b * E + e] = run;
-      run += c;
-    }
-    tot[e] = run;
+  const int64_t rows = kChunk / E;  // E <= 256, so at least 32 block rows per chunk
+  int32_t run = 0;
+  for (int64_t b0 = 0; b0 < nb; b0 += rows) {
+    const int64_t nr = nb - b0 < rows ? nb - b0 : rows;
+    const int n = (int)(nr * E);
+    const int32_t* src = counts + b0 * E;
+    for (int i = tid; i < n; i += 256) buf[i] = src[i];
+    __syncthreads();
+    if (tid < E)
+      for (int r = 0; r < (int)nr; ++r) {
+        const int32_t c = buf[r * E + tid];
+        buf[r * E + tid] = run;
+        run += c;
+      }
+    __syncthreads();
+    int32_t* dst = base + b0 * E;
+    for (int i = tid; i < n; i += 256) dst[i] = buf[i];
+    __syncthreads();
   }
+  if (tid < E) buf[tid] = run;  // per-expert totals
   __syncthreads();
   if (tid == 0) {
-    int32_t run = 0;
+    int32_t acc = 0;
     for (int e = 0; e < E; ++e) {
-      off[e] = run;
-      run += tot[e];
+      off[e] = acc;
+      acc += buf[e];
     }
-    off[E] = run;
+    off[E] = acc;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) {
-    split_sizes[e] = tot[e];
-    offsets[e] = off[e];
-    const int32_t o = off[e];
-    for (int64_t b = 0; b < nb; ++b) base[b * E + e] += o;
+  if (tid < E) {
+    split_sizes[tid] = buf[tid];
+    offsets[tid] = off[tid];
   }
   if (tid == 0) offsets[E] = off[E];
+  const int64_t all = nb * E;
+  for (int64_t i = tid; i < all; i += 256) base[i] += off[i % E];
 }
 
 template <typename U>

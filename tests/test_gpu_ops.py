@@ -55,6 +55,16 @@ def test_route_edges(moe):
     _route_case(moe, rng.standard_normal((100, 6)).astype(np.float32), 6)  # k = E
     _route_case(moe, rng.standard_normal((100, 256)).astype(np.float32), 16)
     _route_case(moe, rng.standard_normal((77, 32)).astype(np.float32), 3, renorm=False)
+    # every lane-group width: E = 1, 3 (a group of 4 with an empty lane), 65 and 200
+    # (two and four logits per lane, partly empty), odd token counts
+    _route_case(moe, rng.standard_normal((5, 1)).astype(np.float32), 1)
+    _route_case(moe, rng.standard_normal((37, 3)).astype(np.float32), 2)
+    _route_case(moe, rng.standard_normal((129, 65)).astype(np.float32), 7, renorm=False)
+    _route_case(moe, np.round(2 * rng.standard_normal((61, 200))).astype(np.float32), 9)
+    # -inf logits are ranked like any number (ties among them by index)
+    neg = rng.standard_normal((50, 16)).astype(np.float32)
+    neg[:, 3:] = -np.inf
+    _route_case(moe, neg, 5)
 
 
 # ---------------------------------------------------------------------------
