@@ -11,3 +11,4 @@ Foundation Models", Challenge 1: Fragmented expert kernels.
 """
 from .moe_oracle import *  # noqa: F401,F403
 from .mxfp8 import *  # noqa: F401,F403
+from .router import *  # noqa: F401,F403
