@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import MOE_BF16, MOE_F32, MOE_MXFP8, MlpDesc, MoeError, check, lib, ptr_table
 
 __all__ = [
-    "moe_route_topk", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
+    "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu", "gemm_workspace",
     "workspace_size", "MoeError", "lib",
     "MOE_F32", "MOE_BF16", "MOE_MXFP8",
@@ -66,6 +66,49 @@ def moe_route_topk(logits: torch.Tensor, k: int, renormalize: bool = True):
     check("moe_route_topk", lib().moe_route_topk(_p(logits), T, E, k, int(renormalize), _p(idx), _p(prob),
                                                  _stream(logits.device)))
     return idx, prob
+
+
+def moe_router_logits(x: torch.Tensor, w_router: torch.Tensor) -> torch.Tensor:
+    """x [T, H] bf16, w_router [E, H] bf16 -> logits [T, E] float32."""
+    _need_cuda(x, w_router)
+    T, H = x.shape
+    E = w_router.shape[0]
+    if x.dtype != torch.bfloat16 or w_router.dtype != torch.bfloat16 or w_router.shape[1] != H:
+        raise ValueError("moe_router_logits: x [T, H] and w_router [E, H] must be bfloat16")
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    check("moe_router_logits", lib().moe_router_logits(_p(x), _p(w_router), T, H, E, _p(logits),
+                                                       _stream(x.device)))
+    return logits
+
+
+def moe_route_topk_bwd(topk_idx: torch.Tensor, topk_prob: torch.Tensor, d_topk_prob: torch.Tensor, E: int,
+                       renormalize: bool = True, logits: torch.Tensor | None = None) -> torch.Tensor:
+    """Gradient of moe_route_topk's probabilities -> d_logits [T, E] float32
+    (``logits`` is needed only without renormalisation)."""
+    _need_cuda(topk_idx, topk_prob, d_topk_prob, logits)
+    T, k = topk_idx.shape
+    d = torch.empty((T, E), dtype=torch.float32, device=topk_idx.device)
+    check("moe_route_topk_bwd", lib().moe_route_topk_bwd(_p(logits), _p(topk_idx), _p(topk_prob), _p(d_topk_prob),
+                                                         T, E, k, int(renormalize), _p(d),
+                                                         _stream(topk_idx.device)))
+    return d
+
+
+def moe_router_bwd(x: torch.Tensor, w_router: torch.Tensor, d_logits: torch.Tensor,
+                   dx_in: torch.Tensor | None = None, dx: torch.Tensor | None = None):
+    """Backward of moe_router_logits -> (dx [T, H] bf16 = dx_in + d_logits w_router,
+    dw_router [E, H] float32 = d_logits^T x)."""
+    _need_cuda(x, w_router, d_logits, dx_in, dx)
+    T, H = x.shape
+    E = w_router.shape[0]
+    if dx is None:
+        dx = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    dw = torch.empty((E, H), dtype=torch.float32, device=x.device)
+    desc = MlpDesc(E, H, 1, 0, MOE_BF16, MOE_BF16, 0)
+    ws = _workspace(workspace_size(_lib.MOE_OP_ROUTER_BWD, desc, 0, T), x.device)
+    check("moe_router_bwd", lib().moe_router_bwd(_p(x), _p(w_router), _p(d_logits), _p(dx_in), T, H, E, _p(dx),
+                                                 _p(dw), _p(ws), ws.numel(), _stream(x.device)))
+    return dx, dw
 
 
 def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torch.Tensor | None, E: int,

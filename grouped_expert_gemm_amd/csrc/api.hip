@@ -80,6 +80,11 @@ extern "C" moe_status moe_workspace_size(moe_op op, const moe_mlp_desc* desc, in
     case MOE_OP_GROUPED_GEMM:
       *bytes = grouped_gemm_workspace_bytes();
       return MOE_OK;
+    case MOE_OP_ROUTER_BWD:
+      if (!desc || T < 0 || desc->E < 1 || desc->E > MOE_MAX_EXPERTS || desc->H < 1)
+        return fail(MOE_ERR_INVALID_ARG, "moe_workspace_size(ROUTER_BWD): desc NULL or bad T/E/H");
+      *bytes = router_bwd_workspace_bytes(T, desc->H, desc->E);
+      return MOE_OK;
   }
   return fail(MOE_ERR_INVALID_ARG, "moe_workspace_size: unknown op");
 }

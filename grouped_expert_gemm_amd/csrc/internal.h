@@ -16,6 +16,7 @@ moe_status validate_desc(const moe_mlp_desc& d, bool backward);
 size_t mlp_fwd_workspace_bytes(const moe_mlp_desc& d, int64_t R);
 size_t mlp_bwd_workspace_bytes(const moe_mlp_desc& d, int64_t R);
 size_t grouped_gemm_workspace_bytes();  // split-K tail area of one grouped GEMM call
+size_t router_bwd_workspace_bytes(int64_t T, int H, int E);  // dW token-chunk partials
 
 // mxfp8 quantisation launcher used by the forward (weights and activations)
 moe_status launch_mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,

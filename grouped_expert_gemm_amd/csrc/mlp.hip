@@ -85,14 +85,25 @@ static PtrTab make_tab(const void* const* t, int E) {
   return tab;
 }
 
-// dprob[r] = sum over j of part[j][r], j in increasing order (deterministic)
+// dprob[r] = sum over j of part[j][r] in a fixed order (deterministic): 8 threads per
+// row each add the partials j = q, q + 8, ... in increasing j, then the 8 sums are added
+// in q order. 32 rows per workgroup, consecutive threads on consecutive rows.
 __global__ __launch_bounds__(256) void reduce_partials(const float* __restrict__ part, int nparts, int64_t R,
                                                        float* __restrict__ out) {
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= R) return;
+  __shared__ float sums[8][32];
+  const int rl = threadIdx.x & 31, q = threadIdx.x >> 5;
+  const int64_t r = (int64_t)blockIdx.x * 32 + rl;
   float s = 0.f;
-  for (int j = 0; j < nparts; ++j) s += part[(int64_t)j * R + r];
-  out[r] = s;
+  if (r < R)
+    for (int j = q; j < nparts; j += 8) s += part[(int64_t)j * R + r];
+  sums[q][rl] = s;
+  __syncthreads();
+  if (q == 0 && r < R) {
+    float t = sums[0][rl];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) t += sums[i][rl];
+    out[r] = t;
+  }
 }
 
 // bf16 GroupedLinear(gate_up) + ScaledSwiGLU: h [R, I] (and z [R, 2I] when z != NULL)
@@ -361,7 +372,7 @@ extern "C" moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, c
     st = gemm::run(p, gemm::MNCONTIG, gemm::KCONTIG, gemm::GROUP_M, gemm::EPI_DSWIGLU, mtiles * p.n_tiles, s,
                    "moe_grouped_mlp_bwd(down dgrad)");
     if (st != MOE_OK) return st;
-    hipLaunchKernelGGL(reduce_partials, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, (const float*)part,
+    hipLaunchKernelGGL(reduce_partials, dim3((unsigned)((R + 31) / 32)), dim3(256), 0, s, (const float*)part,
                        2 * p.n_tiles, R, dprob_perm);
     if ((st = check_launch("moe_grouped_mlp_bwd(dprob)")) != MOE_OK) return st;
 

@@ -71,6 +71,52 @@ moe_status moe_route_topk(const float* logits, int64_t T, int E, int k, int reno
                           int32_t* topk_idx, float* topk_prob, void* stream);
 
 /*
+ * Router gate linear. Source: the router logits behind routing_weights of the
+ * Hugging Face per-expert loop (Challenge 1). The pages show no router; the gate is
+ * read as a bias-free linear map hidden -> E with an [E, H] weight (the [out, in]
+ * layout of the pages' GroupedLinear weights):
+ *   logits[t, e] = sum_h x[t, h] * w_router[e, h], bf16 products, float32 accumulation
+ *   x        [T, H] bf16, 16-byte aligned
+ *   w_router [E, H] bf16, 16-byte aligned
+ *   logits   [T, E] float32 (out)
+ * The four H quarters of each token are summed in a fixed order (deterministic).
+ * Limits: 1 <= E <= MOE_MAX_EXPERTS, H % 64 == 0.
+ */
+moe_status moe_router_logits(const void* x, const void* w_router, int64_t T, int H, int E,
+                             float* logits, void* stream);
+
+/*
+ * Backward of moe_route_topk (the selection is piecewise constant in the logits;
+ * only the probabilities carry a gradient). With g = d_topk_prob and p = topk_prob:
+ *   renormalize != 0: d_logits[t, idx[t, j]] = p[t, j] * (g[t, j] - sum_j' p[t, j'] g[t, j']),
+ *                     every other expert 0; logits may be NULL;
+ *   renormalize == 0: d_logits[t, e] = P[t, e] * (G[t, e] - sum_j p[t, j] g[t, j]) with P the
+ *                     softmax of the logits row and G[t, e] = g[t, j] where e = idx[t, j], else 0.
+ *   logits [T, E] float32 (renormalize == 0 only), topk_idx [T, k] int32,
+ *   topk_prob, d_topk_prob [T, k] float32, d_logits [T, E] float32 (out, every entry written)
+ * Limits: 1 <= k <= E <= MOE_MAX_EXPERTS, k <= 16.
+ */
+moe_status moe_route_topk_bwd(const float* logits, const int32_t* topk_idx, const float* topk_prob,
+                              const float* d_topk_prob, int64_t T, int E, int k, int renormalize,
+                              float* d_logits, void* stream);
+
+/*
+ * Backward of moe_router_logits:
+ *   dx[t, h]        = dx_in[t, h] + sum_e d_logits[t, e] * w_router[e, h]   (bf16 out; dx_in
+ *                     bf16 or NULL for 0, may equal dx: the expert path's input gradient
+ *                     plus the router's)
+ *   dw_router[e, h] = sum_t d_logits[t, e] * x[t, h]                        (float32 out)
+ * float32 arithmetic; dw_router adds chunks of 1024 tokens in order (deterministic).
+ * workspace: moe_workspace_size(MOE_OP_ROUTER_BWD, desc with E and H, R ignored, T)
+ * bytes (0 when T <= 1024), 16-byte aligned, caller-owned. T == 0 writes dw_router = 0.
+ * Limits: 1 <= E <= MOE_MAX_EXPERTS, H % 8 == 0; x, w_router, dx, dx_in, dw_router
+ * 16-byte aligned.
+ */
+moe_status moe_router_bwd(const void* x, const void* w_router, const float* d_logits, const void* dx_in,
+                          int64_t T, int H, int E, void* dx, float* dw_router, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * Token permutation into per-expert groups. Source: split_sizes of GroupedLinear
  * (Challenge 1) and the per-expert row gather of the baseline loop; token
  * permutation before the grouped GEMM is also named in the PyTorch-native MoE
@@ -228,7 +274,8 @@ typedef enum {
   MOE_OP_PERMUTE = 0,  /* T = token count, E, k used; desc may be NULL */
   MOE_OP_MLP_FWD = 1,  /* desc and R used */
   MOE_OP_MLP_BWD = 2,  /* desc and R used */
-  MOE_OP_GROUPED_GEMM = 3  /* moe_grouped_linear / moe_grouped_gate_up_swiglu; no argument used */
+  MOE_OP_GROUPED_GEMM = 3, /* moe_grouped_linear / moe_grouped_gate_up_swiglu; no argument used */
+  MOE_OP_ROUTER_BWD = 4    /* moe_router_bwd: desc (E, H) and T used */
 } moe_op;
 
 /* Workspace bytes an operation needs (0 is possible). bytes is a [host] pointer. */
