@@ -26,6 +26,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector, published
 METRIC = "grouped-MLP TFLOP/s fwd and fwd+bwd, Mixtral-8x7B layer; % MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "grouped_expert_gemm_amd", "csrc", "gemm_fwd.hip")
@@ -207,6 +209,62 @@ def extra_forward(w, inp, steps, warmup, compute="bf16", prequant=False):
     return rec
 
 
+def router_measure(w, inp, reps=20):
+    """The router gate linear (bf16 MFMA; HBM-bound at small E), the top-k gating
+    backward and the gate linear's backward (float32 VALU) at a workload's shape, each
+    timed with events over `reps` calls; returns one record per op with its roofline."""
+    import numpy as np
+    import torch
+
+    import grouped_expert_gemm_amd as moe
+
+    T, H, E, k = w.T, w.H, w.E, w.k
+    x = dev_bf16(torch, np, inp.bits["x"])
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    wr = (0.02 * torch.randn((E, H), generator=g, device="cuda")).to(torch.bfloat16)
+    logits = torch.from_numpy(inp.logits).cuda()
+    idx, prob = moe.moe_route_topk(logits, k)
+    dprob = torch.randn((T, k), generator=g, device="cuda")
+    dlog = moe.moe_route_topk_bwd(idx, prob, dprob, E)
+    dx = torch.empty_like(x)
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    out = {"workload": w.name, "T": T, "H": H, "E": E, "k": k}
+    ms = timed(lambda: moe.moe_router_logits(x, wr))
+    nbytes = T * H * 2 + E * H * 2 + T * E * 4
+    out["router_logits"] = {"ms": round(ms, 4), "bound": "hbm", "achieved_GBps": round(nbytes / ms / 1e6, 1),
+                            "peak_GBps": HBM_PEAK_GBPS, "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                            "tflops": round(2.0 * T * H * E / ms / 1e9, 2)}
+    ms = timed(lambda: moe.moe_route_topk_bwd(idx, prob, dprob, E))
+    nbytes = T * k * 12 + T * E * 4
+    out["route_topk_bwd"] = {"ms": round(ms, 4), "bound": "hbm", "achieved_GBps": round(nbytes / ms / 1e6, 1),
+                             "peak_GBps": HBM_PEAK_GBPS, "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+    ms = timed(lambda: moe.moe_router_bwd(x, wr, dlog, dx_in=dx, dx=dx))
+    # x read, dx read and written, d_logits read, dW written: whichever of the fp32
+    # vector rate and HBM takes longer bounds the op
+    flops = 4.0 * T * H * E
+    nbytes = 3 * T * H * 2 + T * E * 4 + E * H * 4
+    if flops / FP32_PEAK_TFLOPS / 1e12 >= nbytes / HBM_PEAK_GBPS / 1e9:
+        out["router_bwd"] = {"ms": round(ms, 4), "bound": "alu", "achieved_TFLOPs": round(flops / ms / 1e9, 2),
+                             "peak_TFLOPs": FP32_PEAK_TFLOPS, "frac": round(flops / ms / 1e9 / FP32_PEAK_TFLOPS, 4)}
+    else:
+        out["router_bwd"] = {"ms": round(ms, 4), "bound": "hbm", "achieved_GBps": round(nbytes / ms / 1e6, 1),
+                             "peak_GBps": HBM_PEAK_GBPS, "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+    log(f"router {w.name}: logits {out['router_logits']['ms']:.3f} ms, topk bwd {out['route_topk_bwd']['ms']:.3f} ms, "
+        f"gate bwd {out['router_bwd']['ms']:.3f} ms")
+    return out
+
+
 def traffic_record():
     """HBM bytes per gate_up launch from the committed rocprofv3 counter runs, or None
     if they were taken on a different version of the kernel source."""
@@ -331,6 +389,7 @@ def main():
         inpq = make_inputs(wq, want_float=False)
         log(f"inputs {wq.name}: {time.perf_counter() - t0:.1f} s")
         result["qwen3_fwd"] = extra_forward(wq, inpq, max(3, args.steps // 2), args.warmup)
+        result["router"] = [router_measure(w, inp), router_measure(wq, inpq)]
         del inpq
         torch.cuda.empty_cache()
 

@@ -13,8 +13,8 @@
 // route_topk_bwd_kernel: the token-per-lane-group layout of the router; a token's k
 //   slots are read by every lane of its group.
 // router_dx_kernel / router_dw_kernel: the gate linear's backward on fp32 VALU, blocks
-//   of 8 x 8 outputs per thread; dW sums token chunks into a workspace, then adds the
-//   chunks in order (deterministic).
+//   of 8 x 8 outputs per thread; dW sums token chunks (64 to 1024 tokens, enough for
+//   ~1024 workgroups) into a workspace, then adds the chunks in order (deterministic).
 #include <cmath>
 
 #include "common.h"
@@ -141,8 +141,16 @@ __global__ __launch_bounds__(256) void route_topk_bwd_kernel(const float* __rest
 }
 
 constexpr int kDxTokens = 8;    // tokens per dx workgroup
-constexpr int kDwChunk = 1024;  // tokens per dW partial
 constexpr int kHBlock = 2048;   // columns per workgroup (256 threads x 8)
+
+// tokens per dW partial: enough chunks for ~1024 workgroups, 64 .. 1024 tokens each
+int64_t dw_chunk(int64_t T, int H, int E) {
+  const int64_t other = (int64_t)((E + 7) / 8) * ((H + kHBlock - 1) / kHBlock);
+  int64_t want = (1024 + other - 1) / other;  // chunks wanted
+  int64_t c = 1024;
+  while (c > 64 && (T + c - 1) / c < want) c >>= 1;
+  return c;
+}
 
 // dx[t, h] = (dx_in[t, h]) + sum_e dl[t, e] w[e, h]; thread: 8 tokens x 8 columns
 __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict__ dl, const bf16_t* __restrict__ w,
@@ -195,9 +203,11 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict_
 }
 
 // part[c, e, h] = sum over tokens t of chunk c (in order) of dl[t, e] x[t, h];
-// thread: 8 experts x 8 columns
+// thread: 8 experts x 8 columns (VEC: E % 8 == 0, the 8 gradients come as two float4)
+template <bool VEC>
 __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ dl, const bf16_t* __restrict__ x,
-                                                        int64_t T, int H, int E, float* __restrict__ part) {
+                                                        int64_t T, int H, int E, int64_t chunk,
+                                                        float* __restrict__ part) {
   const int64_t c = blockIdx.x;
   const int e0 = blockIdx.y * 8;
   const int h = blockIdx.z * kHBlock + threadIdx.x * 8;
@@ -207,8 +217,8 @@ __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict_
   for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 8; ++b) acc[a][b] = 0.f;
-  const int64_t tb = c * kDwChunk;
-  const int64_t te = tb + kDwChunk < T ? tb + kDwChunk : T;
+  const int64_t tb = c * chunk;
+  const int64_t te = tb + chunk < T ? tb + chunk : T;
   for (int64_t t = tb; t < te; ++t) {
     const uint4 xv = *reinterpret_cast<const uint4*>(x + t * H + h);
     const uint32_t xb[4] = {xv.x, xv.y, xv.z, xv.w};
@@ -218,13 +228,20 @@ __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict_
       xf[2 * q] = bf16_to_f32(xb[q] & 0xFFFFu);
       xf[2 * q + 1] = bf16_to_f32(xb[q] >> 16);
     }
+    float gv[8];
+    if constexpr (VEC) {
+      const float4 g0 = *reinterpret_cast<const float4*>(dl + t * E + e0);
+      const float4 g1 = *reinterpret_cast<const float4*>(dl + t * E + e0 + 4);
+      gv[0] = g0.x; gv[1] = g0.y; gv[2] = g0.z; gv[3] = g0.w;
+      gv[4] = g1.x; gv[5] = g1.y; gv[6] = g1.z; gv[7] = g1.w;
+    } else {
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      const int e = e0 + a < E ? e0 + a : E - 1;
-      const float g = dl[t * E + e];
-#pragma unroll
-      for (int b = 0; b < 8; ++b) acc[a][b] = fmaf(g, xf[b], acc[a][b]);
+      for (int a = 0; a < 8; ++a) gv[a] = dl[t * E + (e0 + a < E ? e0 + a : E - 1)];
     }
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int b = 0; b < 8; ++b) acc[a][b] = fmaf(gv[a], xf[b], acc[a][b]);
   }
 #pragma unroll
   for (int a = 0; a < 8; ++a) {
@@ -263,7 +280,9 @@ void launch_bwd(const float* logits, const int32_t* idx, const float* prob, cons
 }  // namespace
 
 size_t router_bwd_workspace_bytes(int64_t T, int H, int E) {
-  const int64_t nchunks = (T + kDwChunk - 1) / kDwChunk;
+  if (T <= 0) return 0;
+  const int64_t ch = dw_chunk(T, H, E);
+  const int64_t nchunks = (T + ch - 1) / ch;
   return nchunks > 1 ? (size_t)(nchunks * E * (int64_t)H * 4) : 0;
 }
 
@@ -350,10 +369,16 @@ extern "C" moe_status moe_router_bwd(const void* x, const void* w_router, const 
                      static_cast<bf16_t*>(dx));
   moe_status st = check_launch("moe_router_bwd(dx)");
   if (st != MOE_OK) return st;
-  const int64_t nchunks = (T + kDwChunk - 1) / kDwChunk;
+  const int64_t ch = dw_chunk(T, H, E);
+  const int64_t nchunks = (T + ch - 1) / ch;
   float* part = nchunks > 1 ? static_cast<float*>(workspace) : dw_router;
-  hipLaunchKernelGGL(router_dw_kernel, dim3((unsigned)nchunks, (unsigned)((E + 7) / 8), hb), dim3(256), 0, s,
-                     d_logits, static_cast<const bf16_t*>(x), T, H, E, part);
+  const dim3 gdw((unsigned)nchunks, (unsigned)((E + 7) / 8), hb);
+  if (E % 8 == 0 && aligned(d_logits, 16))
+    hipLaunchKernelGGL(router_dw_kernel<true>, gdw, dim3(256), 0, s, d_logits, static_cast<const bf16_t*>(x), T, H,
+                       E, ch, part);
+  else
+    hipLaunchKernelGGL(router_dw_kernel<false>, gdw, dim3(256), 0, s, d_logits, static_cast<const bf16_t*>(x), T, H,
+                       E, ch, part);
   if ((st = check_launch("moe_router_bwd(dw)")) != MOE_OK) return st;
   if (nchunks > 1) {
     hipLaunchKernelGGL(router_dw_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)part,

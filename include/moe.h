@@ -106,9 +106,11 @@ moe_status moe_route_topk_bwd(const float* logits, const int32_t* topk_idx, cons
  *                     bf16 or NULL for 0, may equal dx: the expert path's input gradient
  *                     plus the router's)
  *   dw_router[e, h] = sum_t d_logits[t, e] * x[t, h]                        (float32 out)
- * float32 arithmetic; dw_router adds chunks of 1024 tokens in order (deterministic).
+ * float32 arithmetic; dw_router adds chunks of 64..1024 tokens (a function of T, H, E)
+ * in order (deterministic).
  * workspace: moe_workspace_size(MOE_OP_ROUTER_BWD, desc with E and H, R ignored, T)
- * bytes (0 when T <= 1024), 16-byte aligned, caller-owned. T == 0 writes dw_router = 0.
+ * bytes (0 when one chunk covers T), 16-byte aligned, caller-owned. T == 0 writes
+ * dw_router = 0.
  * Limits: 1 <= E <= MOE_MAX_EXPERTS, H % 8 == 0; x, w_router, dx, dx_in, dw_router
  * 16-byte aligned.
  */
