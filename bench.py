@@ -314,6 +314,42 @@ def cpu_baseline(inp, w, seconds):
                       f"H={w.H}, I={w.I}); {t_all:.1f} s of oracle time, {os.cpu_count()} host CPUs visible"}
 
 
+def fwd_bwd_measure(steps, warmup):
+    from moe_inputs import WORKLOADS, make_inputs
+
+    wb = WORKLOADS["mixtral_fwd_bwd"]
+    t0 = time.perf_counter()
+    inpb = make_inputs(wb, want_float=False)
+    log(f"inputs {wb.name}: {time.perf_counter() - t0:.1f} s")
+    lb = Layer(wb, inpb, backward=True)
+    msb = time_steps(lb, steps, warmup)
+    flopb = 3.0 * wb.gemm_flop_fwd()
+    vb = flopb / (msb * 1e-3) / 1e12
+    log(f"fwd+bwd step {msb:.3f} ms -> {vb:.1f} TFLOP/s")
+    return {"workload": "mixtral_fwd_bwd", "T": wb.T, "value": round(vb, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(msb, 4), "pct_of_bf16_peak": round(100 * vb / BF16_PEAK_TFLOPS, 2),
+            "flop_per_step": flopb}
+
+
+def only_measurement(which, steps, warmup):
+    """One measurement on its own (for kernel traces of that workload)."""
+    from moe_inputs import WORKLOADS, make_inputs
+
+    if which == "fwd_bwd":
+        return fwd_bwd_measure(steps, warmup)
+    if which == "qwen3":
+        wq = WORKLOADS["qwen3_fwd"]
+        return extra_forward(wq, make_inputs(wq, want_float=False), steps, warmup)
+    w = WORKLOADS["mixtral_fwd"]
+    inp = make_inputs(w, want_float=False)
+    if which == "mxfp8":
+        w8 = WORKLOADS["mixtral_mxfp8_fwd"]
+        return [extra_forward(w8, inp, steps, warmup, compute="mxfp8"),
+                extra_forward(w8, inp, steps, warmup, compute="mxfp8", prequant=True)]
+    wq = WORKLOADS["qwen3_fwd"]
+    return [router_measure(w, inp, steps), router_measure(wq, make_inputs(wq, want_float=False), steps)]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,6 +359,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip the MXFP8 and Qwen3 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=["fwd_bwd", "qwen3", "mxfp8", "router"],
+                    help="run one measurement and print its record (kernel traces of that workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -346,6 +384,10 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+
+    if args.only:
+        print(json.dumps(only_measurement(args.only, args.steps, args.warmup)), flush=True)
+        return
 
     w = WORKLOADS["mixtral_fwd"]
     t0 = time.perf_counter()
@@ -394,19 +436,7 @@ def main():
         torch.cuda.empty_cache()
 
     if not args.no_fwd_bwd:
-        wb = WORKLOADS["mixtral_fwd_bwd"]
-        t0 = time.perf_counter()
-        inpb = make_inputs(wb, want_float=False)
-        log(f"inputs {wb.name}: {time.perf_counter() - t0:.1f} s")
-        lb = Layer(wb, inpb, backward=True)
-        msb = time_steps(lb, max(3, args.steps // 2), args.warmup)
-        flopb = 3.0 * wb.gemm_flop_fwd()
-        vb = flopb / (msb * 1e-3) / 1e12
-        log(f"fwd+bwd step {msb:.3f} ms -> {vb:.1f} TFLOP/s")
-        result["fwd_bwd"] = {"workload": "mixtral_fwd_bwd", "T": wb.T, "value": round(vb, 2), "unit": "TFLOP/s",
-                             "ms_per_step": round(msb, 4), "pct_of_bf16_peak": round(100 * vb / BF16_PEAK_TFLOPS, 2),
-                             "flop_per_step": flopb}
-        del lb, inpb
+        result["fwd_bwd"] = fwd_bwd_measure(max(3, args.steps // 2), args.warmup)
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
