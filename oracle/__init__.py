@@ -12,3 +12,4 @@ Foundation Models", Challenge 1: Fragmented expert kernels.
 from .moe_oracle import *  # noqa: F401,F403
 from .mxfp8 import *  # noqa: F401,F403
 from .router import *  # noqa: F401,F403
+from .fp8_tensor import *  # noqa: F401,F403

@@ -1,0 +1,80 @@
+"""Per-tensor FP8 (E4M3) quantisation and the grouped MLP forward on it, as a plain CPU
+reference (test infrastructure only).
+
+"Efficient MoE Training for Biological Foundation Models", Challenge 2 contrasts FP8,
+where one scaling factor covers a whole tensor, with MXFP8's one factor per 32 values.
+The pages give no FP8 scale rule; the reading used here ("current scaling"):
+
+* the scale of a tensor is s = amax / 448 in float32 (amax = max |x| over the whole
+  tensor; s = 1 for an all-zero tensor), so the largest magnitude maps to E4M3's 448;
+* an element's code is the OCP E4M3 code (rule of mxfp8.e4m3_encode: round to nearest,
+  ties to even, saturating, sign kept) of the float32 quotient x / s;
+* in the grouped MLP forward, x_perm is one tensor and each expert's W1_e and W2_e is
+  one tensor; h is materialised in bf16 (its scale needs the whole tensor's amax first)
+  and quantised from that bf16 value as one tensor; GEMM products are exact, sums
+  float64 here; y = (h_q W2_e,q^T) s_h s_w2,e.
+
+All arithmetic is float64 except the float32 scale and quotient, which fix the codes.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .mxfp8 import E4M3_MAX, e4m3_decode, e4m3_encode
+
+__all__ = ["fp8_tensor_scale", "fp8_tensor_quantize", "fp8_tensor_qdq", "grouped_mlp_forward_fp8_tensor"]
+
+
+def fp8_tensor_scale(x) -> np.float32:
+    """float32 scale amax / 448 of a whole tensor (1 for an all-zero or empty tensor)."""
+    a = np.asarray(x, np.float32)
+    amax = np.float32(np.max(np.abs(a))) if a.size else np.float32(0.0)
+    return np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+
+
+def fp8_tensor_quantize(x):
+    """(codes uint8, scale float32) of a whole tensor."""
+    a = np.asarray(x, np.float32)
+    s = fp8_tensor_scale(a)
+    q = (a / s).astype(np.float32)      # the float32 quotient decides the code
+    return e4m3_encode(q.astype(np.float64)), s
+
+
+def fp8_tensor_qdq(x) -> np.ndarray:
+    codes, s = fp8_tensor_quantize(x)
+    return e4m3_decode(codes) * np.float64(s)
+
+
+def _bf16_round(a):
+    """float64 -> nearest bf16 value (ties to even), as float64."""
+    f = np.asarray(a, np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def grouped_mlp_forward_fp8_tensor(x_perm, w_gate_up, w_down, offsets, prob_perm):
+    """y_perm [R, H] of the grouped MLP with every GEMM operand quantised per tensor."""
+    x = np.asarray(x_perm, np.float64)
+    w1 = np.asarray(w_gate_up, np.float64)
+    w2 = np.asarray(w_down, np.float64)
+    p = np.asarray(prob_perm, np.float64)
+    E, twoI, H = w1.shape
+    I = twoI // 2
+    R = x.shape[0]
+    xq = fp8_tensor_qdq(x)
+    h = np.zeros((R, I))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue
+        z = xq[a:b] @ fp8_tensor_qdq(w1[e]).T
+        g, u = z[:, :I], z[:, I:]
+        h[a:b] = g / (1.0 + np.exp(-g)) * u * p[a:b, None]
+    hq = fp8_tensor_qdq(_bf16_round(h))
+    y = np.zeros((R, H))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            y[a:b] = hq[a:b] @ fp8_tensor_qdq(w2[e]).T
+    return y
