@@ -168,7 +168,13 @@ def extra_forward(w, inp, steps, warmup, compute="bf16", prequant=False):
     w1 = dev_bf16(torch, np, inp.bits["w1"])
     w2 = dev_bf16(torch, np, inp.bits["w2"])
     s1 = s2 = None
-    if prequant:
+    if prequant and compute == "fp8":
+        # master weights quantised once (one scale per expert weight), outside the timed steps
+        q1 = [moe.fp8_tensor_quantize(w1[e]) for e in range(w.E)]
+        q2 = [moe.fp8_tensor_quantize(w2[e]) for e in range(w.E)]
+        w1, s1 = [c for c, _ in q1], [sc for _, sc in q1]
+        w2, s2 = [c for c, _ in q2], [sc for _, sc in q2]
+    elif prequant:
         # master weights quantised once, outside the timed steps
         E, twoI, H = w1.shape
         q1, s1 = moe.mxfp8_quantize(w1.reshape(E * twoI, H))
@@ -187,7 +193,7 @@ def extra_forward(w, inp, steps, warmup, compute="bf16", prequant=False):
 
     from grouped_expert_gemm_amd import _lib
     desc = _lib.MlpDesc(w.E, w.H, w.I, moe._COMPUTE[compute], _lib.MOE_BF16,
-                        _lib.MOE_MXFP8 if prequant else _lib.MOE_BF16, 0)
+                        moe._COMPUTE[compute] if prequant else _lib.MOE_BF16, 0)
     ws = torch.empty(max(1, moe.workspace_size(_lib.MOE_OP_MLP_FWD, desc, w.R)), dtype=torch.uint8, device="cuda")
     for _ in range(warmup):
         step()
@@ -198,12 +204,12 @@ def extra_forward(w, inp, steps, warmup, compute="bf16", prequant=False):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     v = w.gemm_flop_fwd() / (ms * 1e-3) / 1e12
-    peak = FP8_PEAK_TFLOPS if compute == "mxfp8" else BF16_PEAK_TFLOPS
+    peak = FP8_PEAK_TFLOPS if compute in ("mxfp8", "fp8") else BF16_PEAK_TFLOPS
     rec = {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k, "compute": compute,
            "value": round(v, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
            "pct_of_peak": round(100 * v / peak, 2), "peak": peak}
-    if compute == "mxfp8":
-        rec["weights"] = ("MXFP8, quantised once outside the step" if prequant
+    if compute in ("mxfp8", "fp8"):
+        rec["weights"] = (f"{compute.upper()}, quantised once outside the step" if prequant
                           else "bf16 master weights, quantised inside every step")
     log(f"{w.name} {compute}{' prequant' if prequant else ''}: {ms:.3f} ms -> {v:.1f} TFLOP/s")
     return rec
@@ -346,6 +352,10 @@ def only_measurement(which, steps, warmup):
         w8 = WORKLOADS["mixtral_mxfp8_fwd"]
         return [extra_forward(w8, inp, steps, warmup, compute="mxfp8"),
                 extra_forward(w8, inp, steps, warmup, compute="mxfp8", prequant=True)]
+    if which == "fp8":
+        w8 = WORKLOADS["mixtral_mxfp8_fwd"]
+        return [extra_forward(w8, inp, steps, warmup, compute="fp8"),
+                extra_forward(w8, inp, steps, warmup, compute="fp8", prequant=True)]
     wq = WORKLOADS["qwen3_fwd"]
     return [router_measure(w, inp, steps), router_measure(wq, make_inputs(wq, want_float=False), steps)]
 
@@ -359,7 +369,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip the MXFP8 and Qwen3 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["fwd_bwd", "qwen3", "mxfp8", "router"],
+    ap.add_argument("--only", choices=["fwd_bwd", "qwen3", "mxfp8", "fp8", "router"],
                     help="run one measurement and print its record (kernel traces of that workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
@@ -425,6 +435,11 @@ def main():
         result["mxfp8_fwd"] = extra_forward(w8, inp, max(3, args.steps // 2), args.warmup, compute="mxfp8")
         result["mxfp8_fwd_prequantised"] = extra_forward(w8, inp, max(3, args.steps // 2), args.warmup,
                                                           compute="mxfp8", prequant=True)
+        torch.cuda.empty_cache()
+        # per-tensor FP8 on the same tensors (one scale per tensor; h goes through bf16)
+        result["fp8_tensor_fwd"] = extra_forward(w8, inp, max(3, args.steps // 2), args.warmup, compute="fp8")
+        result["fp8_tensor_fwd_prequantised"] = extra_forward(w8, inp, max(3, args.steps // 2), args.warmup,
+                                                              compute="fp8", prequant=True)
         torch.cuda.empty_cache()
         wq = WORKLOADS["qwen3_fwd"]
         t0 = time.perf_counter()

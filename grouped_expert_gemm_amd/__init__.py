@@ -17,13 +17,14 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import MOE_BF16, MOE_F32, MOE_MXFP8, MlpDesc, MoeError, check, lib, ptr_table
+from ._lib import MOE_BF16, MOE_F32, MOE_FP8, MOE_MXFP8, MlpDesc, MoeError, check, lib, ptr_table
 
 __all__ = [
     "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
+    "fp8_tensor_quantize",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu", "gemm_workspace",
     "workspace_size", "MoeError", "lib",
-    "MOE_F32", "MOE_BF16", "MOE_MXFP8",
+    "MOE_F32", "MOE_BF16", "MOE_MXFP8", "MOE_FP8",
 ]
 
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.uint8: MOE_MXFP8}
@@ -170,6 +171,19 @@ def mxfp8_quantize(x: torch.Tensor):
     return codes.reshape(x.shape), scales.reshape(*x.shape[:-1], cols // 32)
 
 
+def fp8_tensor_quantize(x: torch.Tensor):
+    """bf16 tensor -> (E4M3 codes uint8 of x's shape, float32 scale tensor of shape [1])."""
+    _need_cuda(x)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("fp8_tensor_quantize takes bfloat16")
+    x = x.contiguous()
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    check("fp8_tensor_quantize", lib().fp8_tensor_quantize(_p(x), x.numel(), _p(codes), _p(scale),
+                                                           _stream(x.device)))
+    return codes, scale
+
+
 def _experts(w):
     """A [E, ...] tensor or a list of per-expert tensors -> list of per-expert tensors."""
     if isinstance(w, torch.Tensor):
@@ -177,7 +191,7 @@ def _experts(w):
     return list(w)
 
 
-_COMPUTE = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
+_COMPUTE = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8, "fp8": MOE_FP8}
 
 
 def moe_grouped_mlp_fwd(x_perm: torch.Tensor, w_gate_up, w_down, offsets: torch.Tensor, prob_perm: torch.Tensor,
@@ -186,9 +200,10 @@ def moe_grouped_mlp_fwd(x_perm: torch.Tensor, w_gate_up, w_down, offsets: torch.
                         workspace: torch.Tensor | None = None):
     """Grouped MLP forward on permuted rows. Returns y_perm, or (y_perm, z, h) with save_for_bwd.
 
-    compute: "f32", "bf16" or "mxfp8". For mxfp8, x_perm may be bf16 (quantised in
-    the call) or uint8 codes with x_perm_scale; weights may be bf16 master weights
-    (quantised in the call) or uint8 codes with per-expert scale tensors.
+    compute: "f32", "bf16", "mxfp8" or "fp8" (per-tensor scales). For mxfp8 and fp8,
+    x_perm may be bf16 (quantised in the call) or uint8 codes with x_perm_scale; weights
+    may be bf16 master weights (quantised in the call) or uint8 codes with per-expert
+    scale tensors (fp8: one float32 scale tensor per expert weight).
     """
     w1 = _experts(w_gate_up)
     w2 = _experts(w_down)
@@ -199,8 +214,8 @@ def moe_grouped_mlp_fwd(x_perm: torch.Tensor, w_gate_up, w_down, offsets: torch.
     dev = x_perm.device
     _need_cuda(x_perm, offsets, prob_perm, x_perm_scale, *w1, *w2)
     c = _COMPUTE[compute]
-    act = _DT[x_perm.dtype]
-    wt = _DT[w1[0].dtype]
+    act = c if x_perm.dtype == torch.uint8 else _DT[x_perm.dtype]
+    wt = c if w1[0].dtype == torch.uint8 else _DT[w1[0].dtype]
     desc = MlpDesc(E, H, I, c, act, wt, int(save_for_bwd))
     out_dtype = torch.float32 if c == MOE_F32 else torch.bfloat16
     y = out if out is not None else torch.empty((R, H), dtype=out_dtype, device=dev)

@@ -12,14 +12,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = range(5)
-MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_MXFP8, MOE_FP8 = 0, 1, 2, 3
 MOE_OP_PERMUTE, MOE_OP_MLP_FWD, MOE_OP_MLP_BWD, MOE_OP_GROUPED_GEMM, MOE_OP_ROUTER_BWD = 0, 1, 2, 3, 4
 MOE_MAX_EXPERTS = 256
 
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd",
-    "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
+    "moe_permute", "moe_unpermute_combine", "mxfp8_quantize", "fp8_tensor_quantize",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu",
     "moe_workspace_size",
     "moe_status_str", "moe_last_error",
@@ -59,6 +59,7 @@ def _declare(lib):
                         vp, sz, vp],
         "moe_unpermute_combine": [vp, c_int, vp, vp, i64, c_int, c_int, vp, vp],
         "mxfp8_quantize": [vp, i64, i64, vp, vp, vp],
+        "fp8_tensor_quantize": [vp, i64, vp, vp, vp],
         "moe_grouped_mlp_fwd": [ctypes.POINTER(MlpDesc), i64, vp, vp, PP, PP, PP, PP, vp, vp, vp, vp, vp, vp,
                                 sz, vp],
         "moe_grouped_mlp_bwd": [ctypes.POINTER(MlpDesc), i64, vp, vp, vp, vp, vp, PP, PP, vp, vp, PP, PP, vp,

@@ -16,5 +16,13 @@ moe_status gate_up(int E, int64_t R, int H, int I, const uint8_t* x, const uint8
                    const uint8_t* const* w_scale, const int32_t* offsets, const float* prob, uint8_t* h,
                    uint8_t* h_scale, hipStream_t s);
 
+// per-tensor FP8 forward (E4M3 with one float32 scale per tensor: x_perm, each expert's
+// W1 and W2, and h, which is stored in bf16 before its scale is known)
+size_t fp8_tensor_workspace_bytes(const moe_mlp_desc& d, int64_t R);
+moe_status forward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const void* x_perm, const float* x_scale,
+                              const void* const* w_gate_up, const void* const* w_down, const float* const* w_gate_up_scale,
+                              const float* const* w_down_scale, const int32_t* offsets, const float* prob_perm,
+                              void* y_perm, uint8_t* ws, hipStream_t s);
+
 }  // namespace mx
 }  // namespace moe

@@ -39,11 +39,11 @@ enum { MX_STORE = 0, MX_SWIGLU = 1 };
 
 struct MxParams {
   const uint8_t* tab[kMaxE];     // per-expert P codes [N][K]
-  const uint8_t* tab_s[kMaxE];   // per-expert P scales [N][K/32]
+  const uint8_t* tab_s[kMaxE];   // per-expert P scales [N][K/32]; per-tensor mode: the expert's float32 scale
   const uint8_t* q;              // Q codes [R][K]
-  const uint8_t* q_s;            // Q scales [R][K/32]
-  void* c;                       // STORE: bf16 [R][N]; SWIGLU: h codes [R][I]
-  uint8_t* c_s;                  // SWIGLU: h scales [R][I/32]
+  const uint8_t* q_s;            // Q scales [R][K/32]; per-tensor mode: one float32 scale
+  void* c;                       // STORE: bf16 [R][N]; SWIGLU: h codes [R][I] (per-tensor mode: h bf16)
+  uint8_t* c_s;                  // SWIGLU: h scales [R][I/32]; per-tensor mode: h's amax word (float bits)
   const int32_t* offsets;
   const float* prob;
   int64_t R;
@@ -53,7 +53,11 @@ struct MxParams {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-template <int EP>
+// PT = false: MX block scales (E8M0 per 32 K values of every row of both operands).
+// PT = true: per-tensor FP8; the MFMA runs with unit block scales, the products are
+// scaled by (Q's scale x the expert's P scale) in the epilogue, and the SwiGLU
+// epilogue writes h in bf16 and raises h's amax word (its scale needs all of h).
+template <int EP, bool PT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_mx_kernel(const MxParams prm) {
   __shared__ __attribute__((aligned(1024))) uint8_t sP0[kTileBytes], sP1[kTileBytes], sP2[kTileBytes], sP3[kTileBytes];
@@ -173,6 +177,7 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
     uint2 scl_next[8];
     uint32_t sP[4], sQ[4];  // [sub-tile]: byte j = this lane's scale for step j of the group
     auto load_scales = [&](int g) {
+      if constexpr (PT) return;
 #pragma unroll
       for (int t2 = 0; t2 < 4; ++t2) {
         scl_next[t2] = *reinterpret_cast<const uint2*>(ps_base + ps_off[t2] + g * 8);
@@ -180,6 +185,11 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
       }
     };
     auto take_scales = [&]() {
+      if constexpr (PT) {
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2) sP[t2] = sQ[t2] = 0x7F7F7F7Fu;   // E8M0 127 = 1.0
+        return;
+      }
 #pragma unroll
       for (int t2 = 0; t2 < 8; ++t2) {
         const uint64_t raw = ((uint64_t)scl_next[t2].y << 32 | scl_next[t2].x) >> (8 * lhi);
@@ -263,7 +273,7 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
       // wait for step kt+1's copies (and, at the group's last step, the next group's
       // scales); loads complete in issue order
       if constexpr (full) {
-        wait_vm_le((j == 1 || j == 2) ? 2 * kDma + 8 : 2 * kDma);
+        wait_vm_le((!PT && (j == 1 || j == 2)) ? 2 * kDma + 8 : 2 * kDma);
       } else {
         wait_vm_le(((kt + 2 < nk) + (kt + 3 < nk)) * kDma);
       }
@@ -318,6 +328,10 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
     lds_barrier();
 
     // ---------------- epilogue ----------------
+    // per-tensor mode: the product of the two tensors' scales
+    const float alpha = PT ? *reinterpret_cast<const float*>(prm.q_s) * *reinterpret_cast<const float*>(prm.tab_s[e])
+                           : 1.f;
+    float hmax = 0.f;   // per-tensor SwiGLU: max |h| of this lane's values
 #pragma unroll
     for (int sm = 0; sm < 4; ++sm) {
       const int64_t mg = (int64_t)tile_row + wm * 128 + sm * 32 + l32;
@@ -331,9 +345,28 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
             for (int i4 = 0; i4 < 4; ++i4) {
               const int64_t col = (int64_t)nt * kBN + sub_n(sn, wn) + i4 * 8 + lhi * 4;
               *reinterpret_cast<uint2*>(C + col) =
-                  make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]),
-                             pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]));
+                  make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0] * alpha, acc[sn][sm][i4 * 4 + 1] * alpha),
+                             pack_bf16x2(acc[sn][sm][i4 * 4 + 2] * alpha, acc[sn][sm][i4 * 4 + 3] * alpha));
             }
+        }
+      } else if constexpr (PT) {
+        const float p = valid ? prm.prob[mg] : 0.f;
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn) {
+          const int64_t col0 = (int64_t)nt * 128 + wn * 64 + sn * 32;
+          float h[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            h[i] = silu_f(acc[sn][sm][i] * alpha) * (acc[sn + 2][sm][i] * alpha) * p;
+            hmax = fmaxf(hmax, fabsf(h[i]));
+          }
+          if (valid) {
+            bf16_t* C = reinterpret_cast<bf16_t*>(prm.c) + mg * prm.I + col0;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+              *reinterpret_cast<uint2*>(C + i4 * 8 + lhi * 4) =
+                  make_uint2(pack_bf16x2(h[i4 * 4 + 0], h[i4 * 4 + 1]), pack_bf16x2(h[i4 * 4 + 2], h[i4 * 4 + 3]));
+          }
         }
       } else {
         const float p = valid ? prm.prob[mg] : 0.f;
@@ -364,17 +397,26 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
         }
       }
     }
+    if constexpr (PT && EP == MX_SWIGLU) {
+      // h is stored in bf16, and rounding is monotone: the maximum of the stored
+      // magnitudes is the rounded maximum of the float32 ones
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, off));
+      if (lane == 0 && hmax > 0.f)
+        atomicMax(reinterpret_cast<uint32_t*>(prm.c_s), f32_to_bf16(hmax) << 16);
+    }
   }
 }
 
-static moe_status launch(int ep, const MxParams& p, int64_t max_tiles, hipStream_t s, const char* what) {
+static moe_status launch(int ep, bool pt, const MxParams& p, int64_t max_tiles, hipStream_t s, const char* what) {
   if (max_tiles <= 0) return MOE_OK;
   int64_t grid = num_cus();
   if (max_tiles < grid) grid = max_tiles;
-  if (ep == MX_SWIGLU)
-    hipLaunchKernelGGL(grouped_gemm_mx_kernel<MX_SWIGLU>, dim3((unsigned)grid), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(grouped_gemm_mx_kernel<MX_STORE>, dim3((unsigned)grid), dim3(256), 0, s, p);
+  const dim3 g((unsigned)grid), b(256);
+  if (ep == MX_SWIGLU && !pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU, false>), g, b, 0, s, p);
+  else if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU, true>), g, b, 0, s, p);
+  else if (!pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_STORE, false>), g, b, 0, s, p);
+  else hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_STORE, true>), g, b, 0, s, p);
   return check_launch(what);
 }
 
@@ -409,7 +451,7 @@ moe_status gate_up(int E, int64_t R, int H, int I, const uint8_t* x, const uint8
   p.I = I;
   p.n_tiles = I / 128;
   const int64_t mtiles = (R + kBM - 1) / kBM + E;
-  return launch(MX_SWIGLU, p, mtiles * p.n_tiles, s, "MXFP8 gate_up + ScaledSwiGLU");
+  return launch(MX_SWIGLU, false, p, mtiles * p.n_tiles, s, "MXFP8 gate_up + ScaledSwiGLU");
 }
 
 static moe_status down(int E, int64_t R, int H, int I, const uint8_t* h, const uint8_t* h_scale,
@@ -432,7 +474,7 @@ static moe_status down(int E, int64_t R, int H, int I, const uint8_t* h, const u
   p.I = I;
   p.n_tiles = H / kBN;
   const int64_t mtiles = (R + kBM - 1) / kBM + E;
-  return launch(MX_STORE, p, mtiles * p.n_tiles, s, "MXFP8 down");
+  return launch(MX_STORE, false, p, mtiles * p.n_tiles, s, "MXFP8 down");
 }
 
 static size_t a256(size_t x) { return align_up(x, 256); }
@@ -490,6 +532,112 @@ moe_status forward(const moe_mlp_desc& d, int64_t R, const void* x_perm, const u
   st = gate_up(E, R, H, I, xq, xs, reinterpret_cast<const void* const*>(w1q), w1s, offsets, prob_perm, hq, hs, s);
   if (st != MOE_OK) return st;
   return down(E, R, H, I, hq, hs, w2q, w2s, offsets, y_perm, s);
+}
+
+// Per-tensor FP8 forward. Workspace: scale words [x, W1 of each expert, W2 of each
+// expert, h], then the codes of whatever is given in bf16, then h in bf16 and its codes.
+size_t fp8_tensor_workspace_bytes(const moe_mlp_desc& d, int64_t R) {
+  const size_t I = d.I, H = d.H, E = d.E;
+  size_t b = a256((2 + 2 * E) * 4);
+  if (d.act == MOE_BF16) b += a256(R * H);
+  if (d.wt == MOE_BF16) b += E * (a256(2 * I * H) + a256(H * I));
+  return b + a256(R * I * 2) + a256(R * I);
+}
+
+moe_status forward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const void* x_perm, const float* x_scale,
+                              const void* const* w_gate_up, const void* const* w_down, const float* const* w_gate_up_scale,
+                              const float* const* w_down_scale, const int32_t* offsets, const float* prob_perm,
+                              void* y_perm, uint8_t* ws, hipStream_t s) {
+  const int E = d.E, H = d.H, I = d.I;
+  moe_status st = check_mx_shape(E, H, I, "moe_grouped_mlp_fwd");
+  if (st != MOE_OK) return st;
+  float* words = reinterpret_cast<float*>(ws);
+  ws += a256((2 + 2 * (size_t)E) * 4);
+  float* w1_word = words + 1;
+  float* w2_word = words + 1 + E;
+  float* h_word = words + 1 + 2 * E;
+  if ((st = fp8t_zero(words, 2 + 2 * E, s)) != MOE_OK) return st;
+
+  const uint8_t* xq = reinterpret_cast<const uint8_t*>(x_perm);
+  const float* xs = x_scale;
+  if (d.act == MOE_BF16) {
+    uint8_t* q = ws;
+    ws += a256((size_t)R * H);
+    const void* in[1] = {x_perm};
+    uint8_t* out[1] = {q};
+    if ((st = fp8t_amax(in, 1, R * H, words, s)) != MOE_OK) return st;
+    if ((st = fp8t_quantize(in, out, 1, R * H, words, s)) != MOE_OK) return st;
+    xq = q;
+    xs = words;
+  }
+  MxParams g, dn;
+  std::memset(&g, 0, sizeof(g));
+  std::memset(&dn, 0, sizeof(dn));
+  if (d.wt == MOE_BF16) {
+    uint8_t* q1[kMaxE];
+    uint8_t* q2[kMaxE];
+    for (int e = 0; e < E; ++e) {
+      q1[e] = ws;
+      ws += a256((size_t)2 * I * H);
+      q2[e] = ws;
+      ws += a256((size_t)H * I);
+    }
+    if ((st = fp8t_amax(w_gate_up, E, (int64_t)2 * I * H, w1_word, s)) != MOE_OK) return st;
+    if ((st = fp8t_quantize(w_gate_up, q1, E, (int64_t)2 * I * H, w1_word, s)) != MOE_OK) return st;
+    if ((st = fp8t_amax(w_down, E, (int64_t)H * I, w2_word, s)) != MOE_OK) return st;
+    if ((st = fp8t_quantize(w_down, q2, E, (int64_t)H * I, w2_word, s)) != MOE_OK) return st;
+    for (int e = 0; e < E; ++e) {
+      g.tab[e] = q1[e];
+      g.tab_s[e] = reinterpret_cast<const uint8_t*>(w1_word + e);
+      dn.tab[e] = q2[e];
+      dn.tab_s[e] = reinterpret_cast<const uint8_t*>(w2_word + e);
+    }
+  } else {
+    for (int e = 0; e < E; ++e) {
+      g.tab[e] = reinterpret_cast<const uint8_t*>(w_gate_up[e]);
+      g.tab_s[e] = reinterpret_cast<const uint8_t*>(w_gate_up_scale[e]);
+      dn.tab[e] = reinterpret_cast<const uint8_t*>(w_down[e]);
+      dn.tab_s[e] = reinterpret_cast<const uint8_t*>(w_down_scale[e]);
+    }
+  }
+  // amax words of x and the weights -> scales (h's word stays an amax accumulator)
+  if ((st = fp8t_finalize(words, 1 + 2 * E, s)) != MOE_OK) return st;
+
+  bf16_t* h = reinterpret_cast<bf16_t*>(ws);
+  ws += a256((size_t)R * I * 2);
+  uint8_t* hq = ws;
+  const int64_t mtiles = (R + kBM - 1) / kBM + E;
+
+  g.q = xq;
+  g.q_s = reinterpret_cast<const uint8_t*>(xs);
+  g.c = h;
+  g.c_s = reinterpret_cast<uint8_t*>(h_word);
+  g.offsets = offsets;
+  g.prob = prob_perm;
+  g.R = R;
+  g.K = H;
+  g.N = 2 * I;
+  g.E = E;
+  g.I = I;
+  g.n_tiles = I / 128;
+  if ((st = launch(MX_SWIGLU, true, g, mtiles * g.n_tiles, s, "FP8 gate_up + ScaledSwiGLU")) != MOE_OK) return st;
+
+  const void* hin[1] = {h};
+  uint8_t* hout[1] = {hq};
+  if ((st = fp8t_quantize(hin, hout, 1, R * I, h_word, s)) != MOE_OK) return st;
+  if ((st = fp8t_finalize(h_word, 1, s)) != MOE_OK) return st;
+
+  dn.q = hq;
+  dn.q_s = reinterpret_cast<const uint8_t*>(h_word);
+  dn.c = y_perm;
+  dn.offsets = offsets;
+  dn.R = R;
+  dn.K = I;
+  dn.N = H;
+  dn.E = E;
+  dn.I = I;
+  dn.n_tiles = H / kBN;
+  return launch(MX_STORE, true, dn, mtiles * dn.n_tiles, s, "FP8 down");
 }
 
 }  // namespace mx

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime.h>
+
 #include "moe.h"
 
 namespace moe {
@@ -21,5 +23,15 @@ size_t router_bwd_workspace_bytes(int64_t T, int H, int E);  // dW token-chunk p
 // mxfp8 quantisation launcher used by the forward (weights and activations)
 moe_status launch_mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,
                                  uint8_t* e8m0, void* stream);
+
+// per-tensor FP8 (one float32 scale per tensor). A tensor's word holds the float bits
+// of its amax between fp8t_amax and fp8t_finalize (cleared first by fp8t_zero), and
+// its scale amax / 448 (1 for amax = 0) after fp8t_finalize. n: elements per tensor,
+// a multiple of 8; inputs bf16 16-byte aligned, codes 8-byte aligned.
+moe_status fp8t_zero(float* words, int n, hipStream_t s);
+moe_status fp8t_amax(const void* const* in, int ntensors, int64_t n, float* words, hipStream_t s);
+moe_status fp8t_quantize(const void* const* in, uint8_t* const* out, int ntensors, int64_t n, const float* words,
+                         hipStream_t s);
+moe_status fp8t_finalize(float* words, int n, hipStream_t s);
 
 }  // namespace moe

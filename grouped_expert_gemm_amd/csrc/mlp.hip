@@ -18,6 +18,7 @@ static bool is_act_ok(const moe_mlp_desc& d) {
     case MOE_F32: return d.act == MOE_F32 && d.wt == MOE_F32;
     case MOE_BF16: return d.act == MOE_BF16 && d.wt == MOE_BF16;
     case MOE_MXFP8: return (d.act == MOE_BF16 || d.act == MOE_MXFP8) && (d.wt == MOE_BF16 || d.wt == MOE_MXFP8);
+    case MOE_FP8: return (d.act == MOE_BF16 || d.act == MOE_FP8) && (d.wt == MOE_BF16 || d.wt == MOE_FP8);
   }
   return false;
 }
@@ -25,19 +26,19 @@ static bool is_act_ok(const moe_mlp_desc& d) {
 moe_status validate_desc(const moe_mlp_desc& d, bool backward) {
   if (d.E < 1 || d.E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "grouped MLP: E out of [1, 256]");
   if (d.H < 1 || d.I < 1) return fail(MOE_ERR_INVALID_ARG, "grouped MLP: H and I must be positive");
-  if (d.compute != MOE_F32 && d.compute != MOE_BF16 && d.compute != MOE_MXFP8)
+  if (d.compute != MOE_F32 && d.compute != MOE_BF16 && d.compute != MOE_MXFP8 && d.compute != MOE_FP8)
     return fail(MOE_ERR_INVALID_ARG, "grouped MLP: bad compute dtype");
   if (!is_act_ok(d)) return fail(MOE_ERR_INVALID_ARG, "grouped MLP: act/wt storage does not match compute dtype");
   if ((int64_t)d.H * d.I * 2 > 0x7FFFFFFFLL)
     return fail(MOE_ERR_UNSUPPORTED, "grouped MLP: one expert's weight exceeds 2^31 bytes");
-  if (d.compute == MOE_BF16 || d.compute == MOE_MXFP8) {
+  if (d.compute == MOE_BF16 || d.compute == MOE_MXFP8 || d.compute == MOE_FP8) {
     if (d.H % 256 != 0 || d.I % 128 != 0)
-      return fail(MOE_ERR_UNSUPPORTED, "grouped MLP: bf16/MXFP8 kernels need H % 256 == 0 and I % 128 == 0");
+      return fail(MOE_ERR_UNSUPPORTED, "grouped MLP: bf16/fp8 kernels need H % 256 == 0 and I % 128 == 0");
     if (backward && d.I % 256 != 0)
       return fail(MOE_ERR_UNSUPPORTED, "grouped MLP backward: bf16 kernels need I % 256 == 0");
   }
-  if (backward && d.compute == MOE_MXFP8)
-    return fail(MOE_ERR_UNSUPPORTED, "grouped MLP backward: MXFP8 backward is not implemented (use BF16)");
+  if (backward && (d.compute == MOE_MXFP8 || d.compute == MOE_FP8))
+    return fail(MOE_ERR_UNSUPPORTED, "grouped MLP backward: FP8 / MXFP8 backward is not implemented (use BF16)");
   return MOE_OK;
 }
 
@@ -55,6 +56,7 @@ size_t mlp_fwd_workspace_bytes(const moe_mlp_desc& d, int64_t R) {
       b += a256(R * I) + a256(R * I / 32);  // h as MXFP8
       return b;
     }
+    case MOE_FP8: return mx::fp8_tensor_workspace_bytes(d, R);
   }
   return 0;
 }
@@ -197,7 +199,8 @@ extern "C" moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, c
   if (!aligned(x_perm, align) || !aligned(y_perm, align))
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_mlp_fwd: x_perm / y_perm misaligned");
   if (d.save_for_bwd) {
-    if (d.compute == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_mlp_fwd: save_for_bwd needs BF16 or F32");
+    if (d.compute == MOE_MXFP8 || d.compute == MOE_FP8)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_mlp_fwd: save_for_bwd needs BF16 or F32");
     if (!z_save || !h_save) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_mlp_fwd: save_for_bwd needs z_save and h_save");
     if (!aligned(z_save, align) || !aligned(h_save, align))
       return fail(MOE_ERR_INVALID_ARG, "moe_grouped_mlp_fwd: z_save / h_save misaligned");
@@ -210,6 +213,12 @@ extern "C" moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, c
   }
   if (d.compute == MOE_MXFP8 && d.act == MOE_MXFP8 && (!x_perm_scale || !aligned(x_perm_scale, 4)))
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_mlp_fwd: MXFP8 activations need a 4-byte aligned x_perm_scale");
+  if (d.compute == MOE_FP8 && d.wt == MOE_FP8) {
+    if ((st = check_table((const void* const*)w_gate_up_scale, d.E, 4, "moe_grouped_mlp_fwd(w_gate_up_scale)")) != MOE_OK) return st;
+    if ((st = check_table((const void* const*)w_down_scale, d.E, 4, "moe_grouped_mlp_fwd(w_down_scale)")) != MOE_OK) return st;
+  }
+  if (d.compute == MOE_FP8 && d.act == MOE_FP8 && (!x_perm_scale || !aligned(x_perm_scale, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_mlp_fwd: FP8 activations need a 4-byte aligned x_perm_scale");
   const size_t need = mlp_fwd_workspace_bytes(d, R);
   if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_grouped_mlp_fwd: workspace too small");
   if (need > 0 && (!workspace || !aligned(workspace, 256)))
@@ -221,6 +230,12 @@ extern "C" moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, c
     float* h = d.save_for_bwd ? (float*)h_save : (float*)workspace;
     return f32::forward(d, R, (const float*)x_perm, w1, w2, offsets, prob_perm, (float*)y_perm,
                         d.save_for_bwd ? (float*)z_save : nullptr, h, s);
+  }
+  if (d.compute == MOE_FP8) {
+    return mx::forward_fp8_tensor(d, R, x_perm, reinterpret_cast<const float*>(x_perm_scale), w_gate_up, w_down,
+                                  reinterpret_cast<const float* const*>(w_gate_up_scale),
+                                  reinterpret_cast<const float* const*>(w_down_scale), offsets, prob_perm, y_perm,
+                                  (uint8_t*)workspace, s);
   }
   if (d.compute == MOE_MXFP8) {
     return mx::forward(d, R, x_perm, x_perm_scale, w_gate_up, w_down, w_gate_up_scale, w_down_scale, offsets,

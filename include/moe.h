@@ -49,7 +49,8 @@ typedef enum {
 typedef enum {
   MOE_F32 = 0,   /* float32 */
   MOE_BF16 = 1,  /* bfloat16 bit patterns */
-  MOE_MXFP8 = 2  /* E4M3 codes (uint8) + one E8M0 scale byte per 32 consecutive values */
+  MOE_MXFP8 = 2, /* E4M3 codes (uint8) + one E8M0 scale byte per 32 consecutive values */
+  MOE_FP8 = 3    /* E4M3 codes (uint8) + one float32 scale for the whole tensor (value = code x scale) */
 } moe_dtype;
 
 /* Largest expert count the library accepts. */
@@ -170,15 +171,32 @@ moe_status moe_unpermute_combine(const void* y_perm, moe_dtype dt, const int32_t
 moe_status mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,
                           uint8_t* e8m0, void* stream);
 
+/*
+ * Per-tensor FP8 quantisation of a bf16 tensor. Source: Challenge 2 (FP8 with one
+ * scaling factor for a whole tensor, the contrast to MXFP8's factor per 32 values).
+ * The pages give no scale rule; the one implemented ("current scaling"):
+ *   amax = max |in| over the n elements; scale = amax / 448 (float32 division,
+ *   rounded to nearest), or 1 when amax = 0;
+ *   e4m3[i] = the OCP E4M3 code of the float32 quotient in[i] / scale (rounded to
+ *   nearest even, saturating to +-448, sign kept).
+ *   in [n] bf16 (16-byte aligned), e4m3 [n] uint8 (out, 8-byte aligned),
+ *   scale: ONE float32 in device memory (out, 4-byte aligned; also used as the amax
+ *   accumulator while the call's kernels run).
+ * Limits: n % 8 == 0. n == 0 writes scale = 1.
+ */
+moe_status fp8_tensor_quantize(const void* in_bf16, int64_t n, uint8_t* e4m3, float* scale, void* stream);
+
 /* Description of one grouped MLP layer (the experts' shapes and precisions). */
 typedef struct {
   int E;             /* experts, 1..MOE_MAX_EXPERTS */
   int H;             /* hidden size (GEMM K of gate_up, N of down) */
   int I;             /* intermediate size (gate_up has 2I outputs) */
-  moe_dtype compute; /* GEMM input precision: MOE_F32, MOE_BF16 or MOE_MXFP8 */
-  moe_dtype act;     /* storage of x_perm: F32 (compute F32), BF16, or MXFP8 (codes + x_perm_scale) */
-  moe_dtype wt;      /* storage of weights: F32 (compute F32), BF16 (for MXFP8 compute: master
-                        weights quantised inside the call), or MXFP8 (codes + scale tables) */
+  moe_dtype compute; /* GEMM input precision: MOE_F32, MOE_BF16, MOE_MXFP8 or MOE_FP8 */
+  moe_dtype act;     /* storage of x_perm: F32 (compute F32), BF16, or the compute dtype's
+                        codes (MXFP8 / FP8: codes + x_perm_scale) */
+  moe_dtype wt;      /* storage of weights: F32 (compute F32), BF16 (for MXFP8 / FP8 compute:
+                        master weights quantised inside the call), or the compute dtype's
+                        codes (codes + scale tables) */
   int save_for_bwd;  /* nonzero: write z_save and h_save for moe_grouped_mlp_bwd */
 } moe_mlp_desc;
 
@@ -194,15 +212,22 @@ typedef struct {
  *   y_perm[r] = h W2_e^T
  * With compute = MXFP8, x_perm (along H), W1_e (along H), h (along I) and W2_e
  * (along I) enter their GEMMs as MXFP8 (rule of mxfp8_quantize); h is quantised in
- * the gate_up epilogue from its float32 value. Outputs: y_perm [R, H] (bf16, or
+ * the gate_up epilogue from its float32 value. With compute = FP8, x_perm (one
+ * tensor), each expert's W1_e and W2_e (one tensor each) and h (one tensor) enter their
+ * GEMMs as per-tensor FP8 (rule of fp8_tensor_quantize); h is first stored in bf16,
+ * since its scale needs the maximum over all of it, and quantised from those bf16
+ * values; the GEMM products are scaled by the product of the two tensors' scales.
+ * FP8 scale arguments are float32 scales in device memory reached through the same
+ * parameters: x_perm_scale -> one float (act = FP8), w_gate_up_scale[e] / w_down_scale[e]
+ * -> one float each (wt = FP8). Outputs: y_perm [R, H] (bf16, or
  * float32 when compute = F32). With save_for_bwd: z_save [R, 2I] and h_save [R, I]
  * (bf16, or float32 when compute = F32); otherwise both may be NULL.
  *   w_gate_up [host] E pointers to [2I, H]; w_down [host] E pointers to [H, I]
  *   w_gate_up_scale / w_down_scale [host] E pointers to [2I, H/32] / [H, I/32]
  *       E8M0 scales, only when wt = MXFP8 (else NULL)
  *   offsets [E+1] int32 (device), prob_perm [R] float32
- * Shapes the GEMM kernels implement: BF16/MXFP8 need H % 256 == 0 and I % 128 == 0;
- * F32 needs H % 4 == 0.
+ * Shapes the GEMM kernels implement: BF16 needs H % 256 == 0 and I % 128 == 0;
+ * MXFP8 and FP8 need H % 256 == 0, I % 256 == 0 and E <= 128; F32 needs H % 4 == 0.
  */
 moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, const void* x_perm,
                                const uint8_t* x_perm_scale, const void* const* w_gate_up,

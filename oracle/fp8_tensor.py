@@ -22,7 +22,7 @@ import numpy as np
 
 from .mxfp8 import E4M3_MAX, e4m3_decode, e4m3_encode
 
-__all__ = ["fp8_tensor_scale", "fp8_tensor_quantize", "fp8_tensor_qdq", "grouped_mlp_forward_fp8_tensor"]
+__all__ = ["fp8_tensor_scale", "fp8_tensor_quantize", "fp8_tensor_qdq", "bf16_round", "grouped_mlp_forward_fp8_tensor"]
 
 
 def fp8_tensor_scale(x) -> np.float32:
@@ -32,20 +32,21 @@ def fp8_tensor_scale(x) -> np.float32:
     return np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
 
 
-def fp8_tensor_quantize(x):
-    """(codes uint8, scale float32) of a whole tensor."""
+def fp8_tensor_quantize(x, scale=None):
+    """(codes uint8, scale float32) of a whole tensor; scale: use this float32 scale
+    instead of the tensor's own (for a part of a larger tensor)."""
     a = np.asarray(x, np.float32)
-    s = fp8_tensor_scale(a)
+    s = fp8_tensor_scale(a) if scale is None else np.float32(scale)
     q = (a / s).astype(np.float32)      # the float32 quotient decides the code
     return e4m3_encode(q.astype(np.float64)), s
 
 
-def fp8_tensor_qdq(x) -> np.ndarray:
-    codes, s = fp8_tensor_quantize(x)
+def fp8_tensor_qdq(x, scale=None) -> np.ndarray:
+    codes, s = fp8_tensor_quantize(x, scale)
     return e4m3_decode(codes) * np.float64(s)
 
 
-def _bf16_round(a):
+def bf16_round(a):
     """float64 -> nearest bf16 value (ties to even), as float64."""
     f = np.asarray(a, np.float32)
     u = f.view(np.uint32).astype(np.uint64)
@@ -53,8 +54,9 @@ def _bf16_round(a):
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
-def grouped_mlp_forward_fp8_tensor(x_perm, w_gate_up, w_down, offsets, prob_perm):
-    """y_perm [R, H] of the grouped MLP with every GEMM operand quantised per tensor."""
+def grouped_mlp_forward_fp8_tensor(x_perm, w_gate_up, w_down, offsets, prob_perm, x_scale=None):
+    """y_perm [R, H] of the grouped MLP with every GEMM operand quantised per tensor.
+    x_scale: x_perm's scale when x_perm is part of a larger tensor (default: its own)."""
     x = np.asarray(x_perm, np.float64)
     w1 = np.asarray(w_gate_up, np.float64)
     w2 = np.asarray(w_down, np.float64)
@@ -62,7 +64,7 @@ def grouped_mlp_forward_fp8_tensor(x_perm, w_gate_up, w_down, offsets, prob_perm
     E, twoI, H = w1.shape
     I = twoI // 2
     R = x.shape[0]
-    xq = fp8_tensor_qdq(x)
+    xq = fp8_tensor_qdq(x, x_scale)
     h = np.zeros((R, I))
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
@@ -71,7 +73,7 @@ def grouped_mlp_forward_fp8_tensor(x_perm, w_gate_up, w_down, offsets, prob_perm
         z = xq[a:b] @ fp8_tensor_qdq(w1[e]).T
         g, u = z[:, :I], z[:, I:]
         h[a:b] = g / (1.0 + np.exp(-g)) * u * p[a:b, None]
-    hq = fp8_tensor_qdq(_bf16_round(h))
+    hq = fp8_tensor_qdq(bf16_round(h))
     y = np.zeros((R, H))
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
