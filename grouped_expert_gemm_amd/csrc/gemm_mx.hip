@@ -1,23 +1,32 @@
-// MXFP8 grouped MLP forward on gfx950's MX-scaled fp8 MFMA
-// (v_mfma_scale_f32_32x32x64_f8f6f4: E4M3 operands, one E8M0 scale per 32 K values).
+// MXFP8 and per-tensor FP8 grouped GEMMs of the MLP forward on gfx950's scaled fp8
+// MFMA (v_mfma_scale_f32_32x32x64_f8f6f4: E4M3 operands, one E8M0 scale per 32 K values).
 //
 // Source: "Efficient MoE Training for Biological Foundation Models", Challenge 2 (MXFP8:
 // one scaling factor per 32 consecutive values, 8-bit values, dedicated low-precision
-// GEMM instructions) and Challenge 3 / Figure 4 (bf16 master weights and activations
-// quantised before the GEMMs; SwiGLU, the routing-probability scaling and the
-// quantisation of h fused into one kernel before the down projection).
+// GEMM instructions; FP8 with one factor per tensor as the contrast) and Challenge 3 /
+// Figure 4 (bf16 master weights and activations quantised before the GEMMs; SwiGLU,
+// the routing-probability scaling and the quantisation of h fused into one kernel
+// before the down projection).
 //
-// The kernel reuses the bf16 kernel's machinery: 256 x 256 tiles, 4 wavefronts of
-// 128 x 128, a 4-slot LDS ring filled by global -> LDS copies four K steps ahead, a
-// barrier in the middle of each step. One K step is 64 fp8 values = 64 bytes per row,
-// the same bytes as a bf16 step, so the LDS layout, swizzle and copy code are shared.
 // MFMA operand layout (measured): lane l holds row l % 32 and, for g = l / 32, the K
 // values [16g, 16g + 16) in bytes 0..15 and [32 + 16g, 32 + 16g + 16) in bytes 16..31
-// -- the two 16-byte chunks a bf16 step reads as its two k16 slices -- and supplies
-// the E8M0 scale of K block g (values [32g, 32g + 32)) of its row.
-// Scales: per 4-step group each lane loads 8 bytes (blocks 8g..8g+7) of its row per
-// sub-tile and packs the 4 bytes of its own K half (block 2j + (l / 32) of step j) into
-// one word, so step j's MFMA selects byte j with op_sel, a compile-time immediate.
+// of a 64-value slice, and supplies the E8M0 scale of K block g (values [32g, 32g + 32))
+// of its row.
+//
+// grouped_gemm_mx_kernel (MXFP8): 256 x 256 tiles, 4 wavefronts of 128 x 128, a 4-slot
+// LDS ring filled by global -> LDS copies four K steps ahead, a barrier in the middle
+// of each step. One K step is 64 fp8 values = 64 bytes per row (the two 16-byte chunks
+// a lane reads). Scales: per 4-step group each lane loads 8 bytes (blocks 8g..8g+7) of
+// its row per sub-tile and packs the 4 bytes of its own K half (block 2j + (l / 32) of
+// step j) into one word, so step j's MFMA selects byte j with op_sel, a compile-time
+// immediate.
+//
+// grouped_gemm_fp8t_kernel (per-tensor FP8) runs on the bf16 forward kernel's copy
+// pipeline instead: K steps of 128 fp8 values, so every row of a tile brings one whole
+// 128-byte line per step, a ring of five 32 KiB LDS half-slots (P of step v in
+// half-slot 2v mod 5, Q in 2v + 1) filled by range-checked buffer copies, and one
+// barrier per step between its two 64-value slices (slice s is LDS chunks 4s..4s+3 of
+// a row, so a lane reads logical chunks 4s + g and 4s + 2 + g).
 #include <cstring>
 #include <type_traits>
 
@@ -53,11 +62,7 @@ struct MxParams {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-// PT = false: MX block scales (E8M0 per 32 K values of every row of both operands).
-// PT = true: per-tensor FP8; the MFMA runs with unit block scales, the products are
-// scaled by (Q's scale x the expert's P scale) in the epilogue, and the SwiGLU
-// epilogue writes h in bf16 and raises h's amax word (its scale needs all of h).
-template <int EP, bool PT>
+template <int EP>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_mx_kernel(const MxParams prm) {
   __shared__ __attribute__((aligned(1024))) uint8_t sP0[kTileBytes], sP1[kTileBytes], sP2[kTileBytes], sP3[kTileBytes];
@@ -177,7 +182,6 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
     uint2 scl_next[8];
     uint32_t sP[4], sQ[4];  // [sub-tile]: byte j = this lane's scale for step j of the group
     auto load_scales = [&](int g) {
-      if constexpr (PT) return;
 #pragma unroll
       for (int t2 = 0; t2 < 4; ++t2) {
         scl_next[t2] = *reinterpret_cast<const uint2*>(ps_base + ps_off[t2] + g * 8);
@@ -185,11 +189,6 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
       }
     };
     auto take_scales = [&]() {
-      if constexpr (PT) {
-#pragma unroll
-        for (int t2 = 0; t2 < 4; ++t2) sP[t2] = sQ[t2] = 0x7F7F7F7Fu;   // E8M0 127 = 1.0
-        return;
-      }
 #pragma unroll
       for (int t2 = 0; t2 < 8; ++t2) {
         const uint64_t raw = ((uint64_t)scl_next[t2].y << 32 | scl_next[t2].x) >> (8 * lhi);
@@ -273,7 +272,7 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
       // wait for step kt+1's copies (and, at the group's last step, the next group's
       // scales); loads complete in issue order
       if constexpr (full) {
-        wait_vm_le((!PT && (j == 1 || j == 2)) ? 2 * kDma + 8 : 2 * kDma);
+        wait_vm_le((j == 1 || j == 2) ? 2 * kDma + 8 : 2 * kDma);
       } else {
         wait_vm_le(((kt + 2 < nk) + (kt + 3 < nk)) * kDma);
       }
@@ -328,10 +327,6 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
     lds_barrier();
 
     // ---------------- epilogue ----------------
-    // per-tensor mode: the product of the two tensors' scales
-    const float alpha = PT ? *reinterpret_cast<const float*>(prm.q_s) * *reinterpret_cast<const float*>(prm.tab_s[e])
-                           : 1.f;
-    float hmax = 0.f;   // per-tensor SwiGLU: max |h| of this lane's values
 #pragma unroll
     for (int sm = 0; sm < 4; ++sm) {
       const int64_t mg = (int64_t)tile_row + wm * 128 + sm * 32 + l32;
@@ -345,28 +340,9 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
             for (int i4 = 0; i4 < 4; ++i4) {
               const int64_t col = (int64_t)nt * kBN + sub_n(sn, wn) + i4 * 8 + lhi * 4;
               *reinterpret_cast<uint2*>(C + col) =
-                  make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0] * alpha, acc[sn][sm][i4 * 4 + 1] * alpha),
-                             pack_bf16x2(acc[sn][sm][i4 * 4 + 2] * alpha, acc[sn][sm][i4 * 4 + 3] * alpha));
+                  make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]),
+                             pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]));
             }
-        }
-      } else if constexpr (PT) {
-        const float p = valid ? prm.prob[mg] : 0.f;
-#pragma unroll
-        for (int sn = 0; sn < 2; ++sn) {
-          const int64_t col0 = (int64_t)nt * 128 + wn * 64 + sn * 32;
-          float h[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            h[i] = silu_f(acc[sn][sm][i] * alpha) * (acc[sn + 2][sm][i] * alpha) * p;
-            hmax = fmaxf(hmax, fabsf(h[i]));
-          }
-          if (valid) {
-            bf16_t* C = reinterpret_cast<bf16_t*>(prm.c) + mg * prm.I + col0;
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4)
-              *reinterpret_cast<uint2*>(C + i4 * 8 + lhi * 4) =
-                  make_uint2(pack_bf16x2(h[i4 * 4 + 0], h[i4 * 4 + 1]), pack_bf16x2(h[i4 * 4 + 2], h[i4 * 4 + 3]));
-          }
         }
       } else {
         const float p = valid ? prm.prob[mg] : 0.f;
@@ -397,13 +373,353 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
         }
       }
     }
-    if constexpr (PT && EP == MX_SWIGLU) {
+  }
+}
+
+namespace {
+constexpr int kXBK = 128;                 // K step: 128 fp8 values, 128 bytes per row
+constexpr int kXTile = kBM * kXBK;        // one operand of one step: a half-slot (32 KiB)
+}  // namespace
+
+// Per-tensor FP8 grouped GEMM on the bf16 forward kernel's copy pipeline (see the top
+// of this file): K steps of 128 fp8 values, a ring of five 32 KiB LDS half-slots, two
+// 64-value MFMA slices per step with the barrier between them. The MFMA runs with unit
+// block scales; the products are scaled by (Q's scale x the expert's P scale) in the
+// epilogue, and the SwiGLU epilogue writes h in bf16 and raises h's amax word (its
+// scale needs all of h). (An MX-scaled instantiation of this pipeline needs ~30 more
+// registers for the scales and spills inside the K loop; MXFP8 keeps the 64-byte-step
+// kernel above.)
+template <int EP>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_fp8t_kernel(const MxParams prm) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sH0[kXTile], sH1[kXTile], sH2[kXTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t sH3[kXTile], sH4[kXTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int E = prm.E;
+  const int R = (int)prm.R;
+  const int K = prm.K;
+  const int l32 = lane & 31, lhi = lane >> 5;
+
+  const int nwg = gridDim.x;
+  const int logical = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+
+  auto hslot = [&](auto H) -> uint8_t* {
+    if constexpr (H.value == 0) return sH0;
+    else if constexpr (H.value == 1) return sH1;
+    else if constexpr (H.value == 2) return sH2;
+    else if constexpr (H.value == 3) return sH3;
+    else return sH4;
+  };
+
+  // Tiles: expert-major, ceil(rows_e / 256) row tiles x n_tiles per expert, row tiles
+  // fastest. Expert offsets are walked once with wavefront-uniform loads and made a
+  // nondecreasing sequence inside [0, R] on the way.
+  auto clamp_off = [&](int v, int prev) -> int {
+    v = v < prev ? prev : v;
+    return v > R ? R : v;
+  };
+  int total = 0;
+  {
+    int prev = 0;
+    for (int x = 0; x < E; ++x) {
+      const int en = clamp_off(prm.offsets[x + 1], prev);
+      total += ((en - prev + kBM - 1) / kBM) * prm.n_tiles;
+      prev = en;
+    }
+  }
+  int e_w = 0;
+  int ob = 0;
+  int oe = clamp_off(prm.offsets[1], 0);
+  int ts_w = 0;
+  int nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
+  const int nk = K / kXBK;
+
+  // fragment addresses: sub-tile rows start at multiples of 32, where swz8 depends on
+  // the lane's row within the sub-tile only; half h of slice s is logical chunk
+  // 4s + 2h + lhi
+  const uint32_t fragP = (uint32_t)((wn * 64 + l32) * 128);
+  const uint32_t fragQ = (uint32_t)((wm * 128 + l32) * 128);
+  uint32_t ck[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) ck[c] = (uint32_t)(((2 * c + lhi) ^ swz8(l32)) << 4);
+  // copies: round i (0..7) of wavefront w fills LDS bytes [(4i + w) KiB, +1 KiB) of a
+  // half-slot: rows (4i + w) * 8 + (lane >> 3), physical chunk lane & 7
+  const int kc_row0 = wave * 8 + (lane >> 3);
+  const int kc_chunk = (lane & 7) ^ swz8(kc_row0);
+  constexpr int64_t kAll = 0xFFFFFFFFll;
+
+  for (int t = logical; t < total; t += nwg) {
+    // ---------------- tile decode ----------------
+    while (e_w < E && t >= ts_w + nt_w) {
+      ts_w += nt_w;
+      ++e_w;
+      ob = oe;
+      if (e_w < E) {
+        oe = clamp_off(prm.offsets[e_w + 1], ob);
+        nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
+      }
+    }
+    if (e_w >= E) break;
+    int e = e_w, mt, nt;
+    {
+      const int local = t - ts_w;
+      const int mte = (oe - ob + kBM - 1) / kBM;
+      mt = local % mte;
+      nt = local / mte;
+    }
+    e = __builtin_amdgcn_readfirstlane(e);
+    mt = __builtin_amdgcn_readfirstlane(mt);
+    nt = __builtin_amdgcn_readfirstlane(nt);
+    const int row_beg = __builtin_amdgcn_readfirstlane(ob);
+    const int row_end = __builtin_amdgcn_readfirstlane(oe);
+    const int tile_row = row_beg + mt * kBM;
+
+    // P row of local tile row r (SWIGLU: gate rows, then the up rows of the same columns)
+    auto p_row = [&](int r) -> int {
+      if constexpr (EP == MX_SWIGLU) return (r < 128) ? nt * 128 + r : prm.I + nt * 128 + (r - 128);
+      else return nt * kBN + r;
+    };
+
+    // ---------------- operands ----------------
+    // Q's record count ends at the expert's last row: rows past it fail the range check
+    // and land as zero codes, discarded in the epilogue.
+    const uint8_t* p_tile = prm.tab[e] + (int64_t)p_row(0) * K;
+    const uint8_t* q_tile = prm.q + (int64_t)tile_row * K;
+    const uint32_t off0 = (uint32_t)((int64_t)kc_row0 * K + kc_chunk * 16);
+    const int64_t q_extent = (int64_t)(row_end - tile_row) * K;
+    const int p_up = (EP == MX_SWIGLU) ? prm.I - 128 : 0;
+    auto copy_op = [&](const uint8_t* tile, int up, int64_t extent, int kt, uint8_t* dst) {
+      const int64_t at = (int64_t)kt * kXBK;
+      int64_t nrec = extent - at;
+      nrec = nrec < 0 ? 0 : (nrec > kAll ? kAll : nrec);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(tile + at), (short)0, (int)(uint32_t)nrec, kBufferFlags);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t rows = (uint32_t)(i * 32 + (i >= 4 ? up : 0));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 4096), 16, off0, (int)(rows * (uint32_t)K),
+                                                 0, 0);
+      }
+    };
+    // the LDS destination (M0) is wavefront-uniform: keep it in scalar registers
+    auto copy_P = [&](int kt, auto H) { copy_op(p_tile, p_up, kAll, kt, hslot(H) + wave_u * 1024); };
+    auto copy_Q = [&](int kt, auto H) { copy_op(q_tile, 0, q_extent, kt, hslot(H) + wave_u * 1024); };
+
+    const uint32_t kUnit = 0x7F7F7F7Fu;  // E8M0 127 = 1.0 in every byte
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+    // fragments: Q of both slices of a step (fb0, fb1), and one set of P that is refilled
+    // sub-tile by sub-tile as soon as its four MFMAs have been issued
+    i32x8_t fa[4], fb0[4], fb1[4];
+    // Lane parts of the fragment addresses: P chunk c at fragP + ck[c], Q at fragQ +
+    // ck[c]. A step takes them through an empty asm, so the compiler adds the half-slot
+    // base inside the step instead of holding all 40 (half-slot, operand, chunk) sums
+    // across the loop; sub-tile offsets are the reads' immediate offsets.
+    auto rd = [&](const uint8_t* base, int s) -> i32x8_t {
+      const i32x4_t a = *reinterpret_cast<const i32x4_t*>(base + ck[2 * s]);
+      const i32x4_t b = *reinterpret_cast<const i32x4_t*>(base + ck[2 * s + 1]);
+      return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto read_q = [&](auto HQ, int s, i32x8_t* fb) {
+      const uint8_t* Q = hslot(HQ) + fragQ;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fb[u] = rd(Q + (u * 32) * 128, s);
+    };
+    auto read_p = [&](auto HP, int s, int sn) -> i32x8_t {
+      return rd(hslot(HP) + fragP + ((sn >> 1) * 128 + (sn & 1) * 32) * 128, s);
+    };
+    // the 16 MFMAs of one slice with Q fragments fb, P sub-tile by sub-tile; after the
+    // MFMAs of sub-tile sn, fa[sn] takes P sub-tile sn of slice s_next of half-slot HPn
+    auto mfma_slice = [&](const i32x8_t* fb, auto OPSEL, bool refill, auto HPn, int s_next) {
+      constexpr int os = decltype(OPSEL)::value;
+#pragma unroll
+      for (int sn = 0; sn < 4; ++sn) {
+#pragma unroll
+        for (int sm = 0; sm < 4; ++sm)
+          acc[sn][sm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[sn], fb[sm], acc[sn][sm], 0, 0, os,
+                                                                          (int)kUnit, os, (int)kUnit);
+        if (refill) fa[sn] = read_p(HPn, s_next, sn);
+      }
+    };
+    // 16 MFMAs with the 16 fragment reads (8 fragments, two 16-byte halves each) between them
+    auto interleave_a = [&]() {
+      static_for<16>([&](auto I) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      });
+    };
+    // ... and the 16 copies of later steps as well
+    auto interleave_b = [&]() {
+      static_for<16>([&](auto I) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      });
+    };
+
+    // K step kt, V = kt % 5 (the half-slot ring); on entry fa and fb0 hold slice 0.
+    // Per step the copies are issued in the order Q of step kt+2, P of step kt+3, so
+    // when step kt+1 must have landed only P of step kt+2 (the 8 most recent) may be
+    // in flight.
+    auto kstep = [&](int kt, auto V, auto FULL) {
+      constexpr int v = decltype(V)::value;
+      constexpr bool full = decltype(FULL)::value;
+      using HP = std::integral_constant<int, (2 * v) % 5>;
+      using HQ = std::integral_constant<int, (2 * v + 1) % 5>;
+      using HPn = std::integral_constant<int, (2 * v + 2) % 5>;
+      using HQn = std::integral_constant<int, (2 * v + 3) % 5>;
+      read_q(HQ{}, 1, fb1);
+      mfma_slice(fb0, std::integral_constant<int, 0>{}, true, HP{}, 1);
+      interleave_a();
+      if (full) wait_vm<8>();
+      else wait_vm_le(kt + 2 < nk ? 8 : 0);
+      lds_barrier();                                  // also waits for every read of step kt
+      if (full || kt + 2 < nk) copy_Q(kt + 2, HP{});  // Q of step kt+2: half-slot 2(kt+2)+1 = 2kt mod 5
+      if (full || kt + 3 < nk) copy_P(kt + 3, HQ{});  // P of step kt+3: half-slot 2(kt+3) = 2kt+1 mod 5
+      const bool next = full || kt + 1 < nk;
+      if (next) read_q(HQn{}, 0, fb0);
+      mfma_slice(fb1, std::integral_constant<int, 0>{}, next, HPn{}, 0);
+      interleave_b();
+    };
+    auto read_first = [&](auto HP, auto HQ) {
+      read_q(HQ, 0, fb0);
+#pragma unroll
+      for (int sn = 0; sn < 4; ++sn) fa[sn] = read_p(HP, 0, sn);
+    };
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    using H2 = std::integral_constant<int, 2>;
+    using H3 = std::integral_constant<int, 3>;
+    using H4 = std::integral_constant<int, 4>;
+    using Full = std::true_type;
+    using Tail = std::false_type;
+    auto steps5 = [&](int kt0, auto FULL) {
+      static_for<5>([&](auto V) {
+        constexpr int v = decltype(V)::value;
+        if (decltype(FULL)::value || kt0 + v < nk) kstep(kt0 + v, V, FULL);
+      });
+    };
+    int kt = 0;
+    if (nk >= 8) {
+      copy_P(0, H0{});
+      copy_Q(0, H1{});
+      copy_P(1, H2{});
+      copy_Q(1, H3{});
+      copy_P(2, H4{});
+      wait_vm<24>();  // step 0 complete
+      lds_barrier();
+      read_first(H0{}, H1{});
+      for (; kt + 7 < nk; kt += 5) steps5(kt, Full{});  // the copies of all five steps exist
+    } else {
+      copy_P(0, H0{});
+      copy_Q(0, H1{});
+      if (nk > 1) {
+        copy_P(1, H2{});
+        copy_Q(1, H3{});
+      }
+      if (nk > 2) copy_P(2, H4{});
+      wait_vm_le((nk > 1) * 16 + (nk > 2) * 8);  // step 0 complete
+      lds_barrier();
+      read_first(H0{}, H1{});
+    }
+    for (; kt < nk; kt += 5) steps5(kt, Tail{});
+    // every wavefront is done with every half-slot before the epilogue uses LDS
+    lds_barrier();
+
+    // ---------------- epilogue ----------------
+    // the product of the two tensors' scales
+    const float alpha = *reinterpret_cast<const float*>(prm.q_s) * *reinterpret_cast<const float*>(prm.tab_s[e]);
+    if constexpr (EP == MX_STORE) {
+      // bf16 rows through LDS (idle after the K loop), as in the bf16 forward kernel:
+      // blocks of 256 rows x 128 columns, 256-byte rows, chunk c of row r at
+      // c ^ (r & 15), rows 0-127 in the first array of a pair and 128-255 in the second;
+      // each wavefront writes its accumulators (8 bytes per lane), then 4 whole rows
+      // leave per store instruction, rows past the expert dropped by the range check.
+      int ln = lane, wv = __builtin_amdgcn_readfirstlane(wave);
+      asm volatile("" : "+v"(ln));  // keep the lane offsets inside the epilogue
+      const int em = wv >> 1, en = wv & 1, e32 = ln & 31, ehi = ln >> 5;
+      const int valid = min(row_end - tile_row, kBM);
+      auto put = [&](uint8_t* arr, int sm, int sq, int i4, uint2 v) {
+        const int rr = sm * 32 + e32;
+        const int ch = en * 8 + sq * 4 + i4;
+        *reinterpret_cast<uint2*>(arr + rr * 256 + ((ch ^ (rr & 15)) << 4) + ehi * 8) = v;
+      };
+      auto drain = [&](const uint8_t* arr, bf16_t* dst, int64_t ld) {
+        const int64_t ldb = ld * 2;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(dst + (int64_t)tile_row * ld), (short)0, (int)(uint32_t)(valid * ldb), kBufferFlags);
+        const int pc = ln & 15;
+        const uint32_t vo = (uint32_t)((ln >> 4) * ldb + pc * 16);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int rl = (wv & 1) * 64 + 4 * i + (ln >> 4);
+          const v4u32 val = *reinterpret_cast<const v4u32*>(arr + rl * 256 + ((pc ^ (rl & 15)) << 4));
+          __builtin_amdgcn_raw_buffer_store_b128(val, rs, vo, (int)((wv * 64 + 4 * i) * ldb), 0);
+        }
+      };
+      auto acc_block = [&](int b, uint8_t* arr0, uint8_t* arr1) {
+        uint8_t* arr = em ? arr1 : arr0;
+#pragma unroll
+        for (int sm = 0; sm < 4; ++sm)
+#pragma unroll
+          for (int sq = 0; sq < 2; ++sq)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const int sn = 2 * b + sq;
+              put(arr, sm, sq, i4,
+                  make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0] * alpha, acc[sn][sm][i4 * 4 + 1] * alpha),
+                             pack_bf16x2(acc[sn][sm][i4 * 4 + 2] * alpha, acc[sn][sm][i4 * 4 + 3] * alpha)));
+            }
+      };
+      acc_block(0, sH0, sH1);
+      acc_block(1, sH2, sH3);
+      lds_barrier();
+      bf16_t* c0 = reinterpret_cast<bf16_t*>(prm.c) + (int64_t)nt * kBN;
+      drain(wv < 2 ? sH0 : sH1, c0, prm.N);
+      drain(wv < 2 ? sH2 : sH3, c0 + 128, prm.N);
+      lds_barrier();  // read out before the next tile's copies land
+    } else {
+      float hmax = 0.f;   // max |h| of this lane's values
+#pragma unroll
+      for (int sm = 0; sm < 4; ++sm) {
+        const int64_t mg = (int64_t)tile_row + wm * 128 + sm * 32 + l32;
+        const bool valid = mg < row_end;
+        const float p = prm.prob[valid ? mg : row_end - 1];
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn) {
+          const int64_t col0 = (int64_t)nt * 128 + wn * 64 + sn * 32;
+          float h[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            h[i] = silu_f(acc[sn][sm][i] * alpha) * (acc[sn + 2][sm][i] * alpha) * p;
+            if (valid) hmax = fmaxf(hmax, fabsf(h[i]));
+          }
+          if (valid) {
+            bf16_t* C = reinterpret_cast<bf16_t*>(prm.c) + mg * prm.I + col0;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+              *reinterpret_cast<uint2*>(C + i4 * 8 + lhi * 4) =
+                  make_uint2(pack_bf16x2(h[i4 * 4 + 0], h[i4 * 4 + 1]), pack_bf16x2(h[i4 * 4 + 2], h[i4 * 4 + 3]));
+          }
+        }
+      }
       // h is stored in bf16, and rounding is monotone: the maximum of the stored
       // magnitudes is the rounded maximum of the float32 ones
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, off));
-      if (lane == 0 && hmax > 0.f)
-        atomicMax(reinterpret_cast<uint32_t*>(prm.c_s), f32_to_bf16(hmax) << 16);
+      if (lane == 0 && hmax > 0.f) atomicMax(reinterpret_cast<uint32_t*>(prm.c_s), f32_to_bf16(hmax) << 16);
     }
   }
 }
@@ -413,10 +729,10 @@ static moe_status launch(int ep, bool pt, const MxParams& p, int64_t max_tiles, 
   int64_t grid = num_cus();
   if (max_tiles < grid) grid = max_tiles;
   const dim3 g((unsigned)grid), b(256);
-  if (ep == MX_SWIGLU && !pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU, false>), g, b, 0, s, p);
-  else if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU, true>), g, b, 0, s, p);
-  else if (!pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_STORE, false>), g, b, 0, s, p);
-  else hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_STORE, true>), g, b, 0, s, p);
+  if (ep == MX_SWIGLU && !pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU>), g, b, 0, s, p);
+  else if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_SWIGLU>), g, b, 0, s, p);
+  else if (!pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_STORE>), g, b, 0, s, p);
+  else hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_STORE>), g, b, 0, s, p);
   return check_launch(what);
 }
 
