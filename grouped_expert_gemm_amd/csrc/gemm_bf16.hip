@@ -63,6 +63,7 @@ void grouped_gemm_kernel(const Params prm) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave >> 1, wn = wave & 1;
   const int E = prm.E;
 
@@ -280,8 +281,9 @@ void grouped_gemm_kernel(const Params prm) {
         for (int i = 0; i < 4; ++i)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 4096), 16, off[i], 0, 0, 0);
       };
-      one(p_tile, p_off, p_step, p_extent, slotP(S) + wave * 1024);
-      one(q_tile, q_off, q_step, q_extent, slotQ(S) + wave * 1024);
+      // the LDS destination (M0) is wavefront-uniform: computed in scalar registers
+      one(p_tile, p_off, p_step, p_extent, slotP(S) + wave_u * 1024);
+      one(q_tile, q_off, q_step, q_extent, slotQ(S) + wave_u * 1024);
     };
 
     f32x16 acc[4][4];

@@ -52,6 +52,7 @@ void grouped_gemm_fwd_kernel(const Params prm) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave >> 1, wn = wave & 1;
   const int E = prm.E;
   const int R = (int)prm.R;
@@ -199,8 +200,9 @@ void grouped_gemm_fwd_kernel(const Params prm) {
                                                  (int)(rows * (uint32_t)ld * 2u), 0, 0);
       }
     };
-    auto copy_P = [&](int kt, auto H) { copy_op(p_tile, p_off0, p_up, prm.p_ld, kAll, kt, hslot(H) + wave * 1024); };
-    auto copy_Q = [&](int kt, auto H) { copy_op(q_tile, q_off0, 0, prm.q_ld, q_extent, kt, hslot(H) + wave * 1024); };
+    // the LDS destination (M0) is wavefront-uniform: computed in scalar registers
+    auto copy_P = [&](int kt, auto H) { copy_op(p_tile, p_off0, p_up, prm.p_ld, kAll, kt, hslot(H) + wave_u * 1024); };
+    auto copy_Q = [&](int kt, auto H) { copy_op(q_tile, q_off0, 0, prm.q_ld, q_extent, kt, hslot(H) + wave_u * 1024); };
 
     f32x16 acc[4][4];
 #pragma unroll
