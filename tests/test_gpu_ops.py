@@ -129,6 +129,29 @@ def test_permute_reuse_map_and_mxfp8_rows(moe):
     assert np.array_equal(q["x_perm_scale"].cpu().numpy(), sc.cpu().numpy()[m["src_token"]])
 
 
+@pytest.mark.parametrize("T,H,E,k", [(700, 1096, 16, 6), (300, 2048, 128, 8), (129, 8, 4, 3)])
+def test_combine_shapes(moe, T, H, E, k):
+    """bf16 combine: row widths with a partial last group of chunks per lane, slot counts
+    with a partial group of four slots, weighted and unweighted."""
+    rng = np.random.default_rng(T + H + k)
+    idx, p = oracle.route_topk(rng.standard_normal((T, E)).astype(np.float32), k)
+    m = oracle.permute(idx, E)
+    yb = f32_to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
+    rmap = torch.from_numpy(m["row_id_map"].astype(np.int32)).cuda()
+    print(f"combine T={T} H={H} k={k}", flush=True)
+    out = moe.moe_unpermute_combine(dev_bf16(yb), rmap, T, k)
+    ref = oracle.unpermute_combine(bf16_bits_to_f32(yb), m["row_id_map"], T, k)
+    assert max_rel_err(host(out), ref) <= 2.0 ** -8
+    outw = moe.moe_unpermute_combine(dev_bf16(yb), rmap, T, k, dev_f32(p.astype(np.float32)))
+    refw = oracle.unpermute_combine(bf16_bits_to_f32(yb), m["row_id_map"], T, k, weights=p)
+    assert max_rel_err(host(outw), refw) <= 2.0 ** -8
+    # permutation of the same rows: bit-exact gather into each of the k rows
+    xb = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    r = moe.moe_permute(dev_bf16(xb), torch.from_numpy(idx.astype(np.int32)).cuda(),
+                        dev_f32(p.astype(np.float32)), E)
+    assert np.array_equal(bf16_bits(r["x_perm"]), xb[m["src_token"]])
+
+
 def test_combine(moe):
     rng = np.random.default_rng(3)
     T, H, E, k = 1500, 512, 8, 2
