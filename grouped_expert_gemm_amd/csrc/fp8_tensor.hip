@@ -61,22 +61,44 @@ __device__ __forceinline__ float scale_of_amax(uint32_t bits) {
   return amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
 }
 
-__global__ __launch_bounds__(256) void fp8t_quantize_kernel(const Fp8Tab tab, int64_t n8, const uint32_t* words) {
-  const uint4* in = tab.in[blockIdx.y];
-  uint2* out = tab.out[blockIdx.y];
-  const float s = scale_of_amax(words[blockIdx.y]);
+// The quotient x / s rounded to nearest, with r = 1/s rounded to nearest computed once:
+// q1 = x r is within one ulp of x / s, the residual x - q1 s is exact as an fma, and
+// q1 + residual * r (one fma) is the correctly rounded quotient (Markstein's theorem;
+// it needs s and r in the normal range, checked per tensor). Quotients below the
+// float32 normal range, where the theorem does not hold, are far below E4M3's smallest
+// step and get code 0 either way.
+template <bool kRecip>
+__device__ __forceinline__ float quotient(float x, float s, float r) {
+  if constexpr (!kRecip) return __fdiv_rn(x, s);
+  const float q1 = x * r;
+  const float e = __builtin_fmaf(-q1, s, x);
+  return __builtin_fmaf(e, r, q1);
+}
+
+template <bool kRecip>
+__device__ __forceinline__ void quantize_range(const uint4* in, uint2* out, int64_t n8, float s, float r) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
     const uint4 v = in[i];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t c[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      c[2 * j] = e4m3_encode(__fdiv_rn(bf16_to_f32(w[j] & 0xFFFFu), s));
-      c[2 * j + 1] = e4m3_encode(__fdiv_rn(bf16_to_f32(w[j] >> 16), s));
+      c[2 * j] = e4m3_encode(quotient<kRecip>(bf16_to_f32(w[j] & 0xFFFFu), s, r));
+      c[2 * j + 1] = e4m3_encode(quotient<kRecip>(bf16_to_f32(w[j] >> 16), s, r));
     }
     out[i] = make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
                         c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
   }
+}
+
+__global__ __launch_bounds__(256) void fp8t_quantize_kernel(const Fp8Tab tab, int64_t n8, const uint32_t* words) {
+  const float s = scale_of_amax(words[blockIdx.y]);
+  const float r = __fdiv_rn(1.f, s);
+  const float kMinNormal = 1.17549435e-38f, kMaxNormal = 3.40282347e+38f;
+  if (s >= kMinNormal && r >= kMinNormal && r <= kMaxNormal)
+    quantize_range<true>(tab.in[blockIdx.y], tab.out[blockIdx.y], n8, s, r);
+  else
+    quantize_range<false>(tab.in[blockIdx.y], tab.out[blockIdx.y], n8, s, r);
 }
 
 __global__ __launch_bounds__(256) void fp8t_finalize_kernel(uint32_t* words, int n) {

@@ -90,3 +90,34 @@ def test_mlp_descriptor_checks(L):
                                ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096), None, None,
                                ctypes.c_void_p(4096), 1 << 30, None)
     assert st == _lib.MOE_ERR_INVALID_ARG and b"expert 7" in L.moe_last_error()
+
+
+def test_fp8_tensor_argument_checks(L):
+    """Per-tensor FP8: size and pointer checks before any launch; descriptor rules of the
+    FP8 forward (storage matching the compute dtype, no backward, no saved tensors)."""
+    from grouped_expert_gemm_amd import _lib
+    INV, UNS = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED
+    scale = ctypes.c_void_p(4096)
+    assert L.fp8_tensor_quantize(None, 12, None, scale, None) == INV                  # n % 8
+    assert L.fp8_tensor_quantize(None, -8, None, scale, None) == INV                  # negative
+    assert L.fp8_tensor_quantize(None, 16, None, None, None) == INV                   # NULL scale
+    assert L.fp8_tensor_quantize(None, 16, None, ctypes.c_void_p(4098), None) == INV  # scale misaligned
+    assert L.fp8_tensor_quantize(None, 16, None, scale, None) == INV                  # NULL input
+    n = ctypes.c_size_t()
+    D = _lib.MlpDesc
+    FP8, BF16, MX = _lib.MOE_FP8, _lib.MOE_BF16, _lib.MOE_MXFP8
+    assert L.moe_workspace_size(1, ctypes.byref(D(8, 4096, 14336, FP8, BF16, BF16, 0)), 16384, 0, 0, 0,
+                                ctypes.byref(n)) == 0
+    # scale words, x codes, both weights' codes of 8 experts, h in bf16 and its codes
+    assert n.value >= 16384 * 4096 + 8 * 3 * 14336 * 4096 + 16384 * 14336 * 3
+    assert L.moe_workspace_size(1, ctypes.byref(D(8, 4096, 14336, FP8, MX, BF16, 0)), 1, 0, 0, 0,
+                                ctypes.byref(n)) == INV                                # MXFP8 storage, FP8 compute
+    assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, FP8, BF16, BF16, 0)), 1, 0, 0, 0,
+                                ctypes.byref(n)) == UNS                                # FP8 backward
+    ptrs = (ctypes.c_void_p * 8)(*([4096] * 8))
+    pp = ctypes.cast(ptrs, _lib.PP)
+    d = D(8, 256, 256, FP8, BF16, BF16, 1)
+    st = L.moe_grouped_mlp_fwd(ctypes.byref(d), 64, ctypes.c_void_p(4096), None, pp, pp, None, None,
+                               ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
+                               ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096), 1 << 40, None)
+    assert st == UNS and b"save_for_bwd" in L.moe_last_error()

@@ -33,7 +33,8 @@ def moe():
 from gpu_util import dev_bf16, dev_f32, host, oracle_perm  # noqa: E402
 
 
-@pytest.mark.parametrize("shape,mag", [((1000, 136), 1.0), ((3, 8), 1e-30), ((4096, 520), 3e4)])
+@pytest.mark.parametrize("shape,mag", [((1000, 136), 1.0), ((3, 8), 1e-30), ((4096, 520), 3e4), ((64, 40), 2e-38),
+                                       ((8192, 512), 2.0 ** 100)])
 def test_quantize_bit_exact(moe, shape, mag):
     rng = np.random.default_rng(7)
     x = (rng.standard_normal(shape) * mag).astype(np.float32)
