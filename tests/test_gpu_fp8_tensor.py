@@ -99,6 +99,12 @@ def test_fp8_forward(moe, shape):
                                     w_down_scale=[s for _, s in q2])
     torch.cuda.synchronize()
     assert torch.equal(y_pre, y)
+    # mixed storage: codes for x with bf16 master weights, and bf16 x with weight codes
+    y_xq = moe.moe_grouped_mlp_fwd(xq, w1b, w2b, off, prob, compute="fp8", x_perm_scale=xs)
+    y_wq = moe.moe_grouped_mlp_fwd(dev_bf16(xp_bits), [c for c, _ in q1], [c for c, _ in q2], off, prob,
+                                   compute="fp8", w_gate_up_scale=[s for _, s in q1], w_down_scale=[s for _, s in q2])
+    torch.cuda.synchronize()
+    assert torch.equal(y_xq, y) and torch.equal(y_wq, y)
     # a second call on the same inputs: same bits (the h maximum is an order-free max)
     y2 = moe.moe_grouped_mlp_fwd(dev_bf16(xp_bits), w1b, w2b, off, prob, compute="fp8")
     torch.cuda.synchronize()
