@@ -61,6 +61,7 @@ SHAPES = [
     # name, T, H, I, E, k, zipf, empty experts
     ("ragged", 1500, 512, 512, 4, 2, 0.0, ()),
     ("skewed_empty", 900, 256, 256, 16, 4, 1.2, (2, 7)),
+    ("many_experts", 700, 256, 256, 80, 4, 1.2, (3, 70)),   # expert tables in two launches of 64
 ]
 
 
