@@ -73,6 +73,10 @@ def test_grouped_mlp_fwd_bf16(moe, shape):
 BWD_SHAPES = [
     ("ragged", 700, 512, 256, 4, 2, 0.0, ()),
     ("skewed_empty", 900, 256, 256, 8, 2, 1.2, (5,)),
+    # more weight-gradient tiles than CUs (dW1: 16 experts x 8 x 4 tiles): each workgroup
+    # runs several, issuing the next tile's first copies before its stores; skewed
+    # expert sizes give both long and short K loops, and idle experts in the chain
+    ("many_tiles", 1200, 1024, 1024, 16, 2, 1.2, (4, 11)),
 ]
 
 
