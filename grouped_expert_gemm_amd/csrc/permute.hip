@@ -72,14 +72,17 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(const int32_t* __rest
                                                            int E, int32_t* __restrict__ base,
                                                            int32_t* __restrict__ split_sizes,
                                                            int32_t* __restrict__ offsets) {
-  // counts [nb, E] pass through LDS in chunks of whole block rows, read and written
-  // coalesced; thread e runs down column e inside LDS (the running count stays in a
-  // register across chunks). A second coalesced pass adds the expert offsets.
+  // counts [nb, E] pass through LDS in chunks of whole block rows, read coalesced;
+  // thread e runs down column e inside LDS (the running count stays in a register
+  // across chunks). The expert totals are scanned in parallel (Hillis-Steele over 256
+  // entries). When every block row fits in one chunk the expert offsets are added as
+  // the chunk is written out; otherwise a second coalesced pass adds them.
   constexpr int kChunk = 8192;  // LDS entries per chunk (32 KiB)
   __shared__ int32_t buf[kChunk];
-  __shared__ int32_t off[MOE_MAX_EXPERTS + 1];
+  __shared__ int32_t sc[2][256];
   const int tid = threadIdx.x;
   const int64_t rows = kChunk / E;  // E <= 256, so at least 32 block rows per chunk
+  const bool one_chunk = nb <= rows;
   int32_t run = 0;
   for (int64_t b0 = 0; b0 < nb; b0 += rows) {
     const int64_t nr = nb - b0 < rows ? nb - b0 : rows;
@@ -94,28 +97,44 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(const int32_t* __rest
         run += c;
       }
     __syncthreads();
-    int32_t* dst = base + b0 * E;
-    for (int i = tid; i < n; i += 256) dst[i] = buf[i];
-    __syncthreads();
-  }
-  if (tid < E) buf[tid] = run;  // per-expert totals
-  __syncthreads();
-  if (tid == 0) {
-    int32_t acc = 0;
-    for (int e = 0; e < E; ++e) {
-      off[e] = acc;
-      acc += buf[e];
+    if (!one_chunk) {
+      int32_t* dst = base + b0 * E;
+      for (int i = tid; i < n; i += 256) dst[i] = buf[i];
+      __syncthreads();
     }
-    off[E] = acc;
   }
+  // per-expert totals -> exclusive offsets
+  const int32_t total = tid < E ? run : 0;
+  sc[0][tid] = total;
   __syncthreads();
-  if (tid < E) {
-    split_sizes[tid] = buf[tid];
-    offsets[tid] = off[tid];
+  int cur = 0;
+  for (int d = 1; d < 256; d <<= 1) {
+    int32_t x = sc[cur][tid];
+    if (tid >= d) x += sc[cur][tid - d];
+    sc[cur ^ 1][tid] = x;
+    __syncthreads();
+    cur ^= 1;
   }
-  if (tid == 0) offsets[E] = off[E];
-  const int64_t all = nb * E;
-  for (int64_t i = tid; i < all; i += 256) base[i] += off[i % E];
+  const int32_t incl = sc[cur][tid];
+  if (tid < E) {
+    split_sizes[tid] = total;
+    offsets[tid] = incl - total;
+  }
+  if (tid == E - 1) offsets[E] = incl;
+  sc[cur ^ 1][tid] = incl - total;  // exclusive offset of expert tid
+  __syncthreads();
+  const int32_t* off = sc[cur ^ 1];
+  // thread tid adds to column tid % E of every (256 / E)-th row, starting at row tid / E
+  const int per = 256 / E;
+  const int c = tid % E, r0 = tid / E;
+  if (r0 < per) {
+    const int32_t o = off[c];
+    if (one_chunk) {
+      for (int64_t r = r0; r < nb; r += per) base[r * E + c] = buf[r * E + c] + o;
+    } else {
+      for (int64_t r = r0; r < nb; r += per) base[r * E + c] += o;
+    }
+  }
 }
 
 template <typename U>

@@ -112,6 +112,12 @@ def test_permute_edges(moe):
     # odd row width (byte-wise copies), float32 rows, many blocks
     idx, p = oracle.route_topk(rng.standard_normal((2049, 256)).astype(np.float32), 16)
     _permute_case(moe, 2049, 3, 256, 16, idx, p.astype(np.float32), dtype="f32")
+    # block counts over more than one LDS chunk of the scan (E = 256: 32 block rows per chunk)
+    idx, p = oracle.route_topk(rng.standard_normal((9000, 256)).astype(np.float32), 2)
+    _permute_case(moe, 9000, 16, 256, 2, idx, p.astype(np.float32))
+    # an expert count that does not divide the scan's 256 threads
+    idx, p = oracle.route_topk(rng.standard_normal((3000, 200)).astype(np.float32), 3)
+    _permute_case(moe, 3000, 16, 200, 3, idx, p.astype(np.float32))
 
 
 def test_permute_reuse_map_and_mxfp8_rows(moe):
