@@ -73,6 +73,7 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave >> 1, wn = wave & 1;
   const int E = prm.E;
   const int l32 = lane & 31, lhi = lane >> 5;
@@ -159,8 +160,9 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
     }
     auto issue_dma = [&](int kt, auto S) {
       const int64_t k0 = (int64_t)kt * kStepK;
-      uint8_t* P = slotP(S) + wave * 1024;
-      uint8_t* Q = slotQ(S) + wave * 1024;
+      // the LDS destination (M0) is wavefront-uniform: computed in scalar registers
+      uint8_t* P = slotP(S) + wave_u * 1024;
+      uint8_t* Q = slotQ(S) + wave_u * 1024;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(pbase + k0 + p_off[i]), (lds_ptr_t)(P + i * 4096), 16, 0, 0);
