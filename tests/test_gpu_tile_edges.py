@@ -87,3 +87,29 @@ def test_gate_up_swiglu_tile_edges(moe, use_ws):
         if b > a:
             assert max_rel_err(hh[a:b], rh[a:b]) <= BF16_TOL, (e, SIZES[e])
             assert max_rel_err(zh[a:b], rz[a:b]) <= BF16_TOL, (e, SIZES[e])
+
+
+@pytest.mark.parametrize("compute", ["mxfp8", "fp8"])
+def test_fp8_forward_tile_edges(moe, compute):
+    """The MXFP8 and per-tensor FP8 grouped MLP forwards at the same expert sizes, against
+    the oracle's quantise -> dequantise forwards (max rel error <= 6e-2)."""
+    rng = np.random.default_rng(13)
+    E, H, I = len(SIZES), 256, 256
+    off = _offsets(SIZES)
+    R = int(off[-1])
+    xb, x = _bf16(rng, (R, H), 1.0)
+    w1b, w1 = _bf16(rng, (E, 2 * I, H), 0.02)
+    w2b, w2 = _bf16(rng, (E, H, I), 0.02)
+    prob = rng.uniform(0.1, 1.0, R)
+    print(f"{compute} forward tile edges: R={R} H={H} I={I} E={E}", flush=True)
+    if compute == "mxfp8":
+        ref, _ = oracle.grouped_mlp_forward_mxfp8(x, w1, w2, off, prob)
+    else:
+        ref = oracle.grouped_mlp_forward_fp8_tensor(x, w1, w2, off, prob)
+    y = torch.full((R, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_mlp_fwd(dev_bf16(xb), dev_bf16(w1b), dev_bf16(w2b), torch.from_numpy(off).cuda(),
+                            dev_f32(prob), compute=compute, out=y)
+    torch.cuda.synchronize()
+    yh = host(y)
+    assert not np.isnan(yh).any()
+    assert max_rel_err(yh, ref) <= 6e-2
