@@ -21,7 +21,7 @@ from ._lib import MOE_BF16, MOE_F32, MOE_FP8, MOE_MXFP8, MlpDesc, MoeError, chec
 
 __all__ = [
     "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
-    "fp8_tensor_quantize",
+    "fp8_tensor_quantize", "mxfp8_quantize_colwise",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu", "gemm_workspace",
     "workspace_size", "MoeError", "lib",
     "MOE_F32", "MOE_BF16", "MOE_MXFP8", "MOE_FP8",
@@ -182,6 +182,26 @@ def fp8_tensor_quantize(x: torch.Tensor):
     check("fp8_tensor_quantize", lib().fp8_tensor_quantize(_p(x), x.numel(), _p(codes), _p(scale),
                                                            _stream(x.device)))
     return codes, scale
+
+
+def mxfp8_quantize_colwise(x: torch.Tensor, offsets: torch.Tensor, pad: int = 32):
+    """bf16 [R, C] with expert row offsets [E+1] -> (E4M3 codes [C, kcap], E8M0 scales
+    [C, kcap/32], padded offsets kofs [E+1]) with kcap = R + E * (pad - 1) rounded up to
+    32: each expert's rows, zero-padded to a multiple of pad, quantised along the token
+    axis as columns [kofs[e], kofs[e+1])."""
+    _need_cuda(x, offsets)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("mxfp8_quantize_colwise takes bfloat16")
+    x = x.contiguous()
+    R, C = x.shape
+    E = offsets.numel() - 1
+    kcap = (R + E * (pad - 1) + 31) // 32 * 32
+    codes = torch.zeros((C, kcap), dtype=torch.uint8, device=x.device)
+    scales = torch.zeros((C, kcap // 32), dtype=torch.uint8, device=x.device)
+    kofs = torch.empty(E + 1, dtype=torch.int32, device=x.device)
+    check("mxfp8_quantize_colwise", lib().mxfp8_quantize_colwise(_p(x), R, C, E, _p(offsets), pad, kcap, _p(codes),
+                                                                 _p(scales), _p(kofs), _stream(x.device)))
+    return codes, scales, kofs
 
 
 def _experts(w):

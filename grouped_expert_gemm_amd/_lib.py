@@ -19,7 +19,7 @@ MOE_MAX_EXPERTS = 256
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd",
-    "moe_permute", "moe_unpermute_combine", "mxfp8_quantize", "fp8_tensor_quantize",
+    "moe_permute", "moe_unpermute_combine", "mxfp8_quantize", "fp8_tensor_quantize", "mxfp8_quantize_colwise",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu",
     "moe_workspace_size",
     "moe_status_str", "moe_last_error",
@@ -60,6 +60,7 @@ def _declare(lib):
         "moe_unpermute_combine": [vp, c_int, vp, vp, i64, c_int, c_int, vp, vp],
         "mxfp8_quantize": [vp, i64, i64, vp, vp, vp],
         "fp8_tensor_quantize": [vp, i64, vp, vp, vp],
+        "mxfp8_quantize_colwise": [vp, i64, i64, c_int, vp, c_int, i64, vp, vp, vp, vp],
         "moe_grouped_mlp_fwd": [ctypes.POINTER(MlpDesc), i64, vp, vp, PP, PP, PP, PP, vp, vp, vp, vp, vp, vp,
                                 sz, vp],
         "moe_grouped_mlp_bwd": [ctypes.POINTER(MlpDesc), i64, vp, vp, vp, vp, vp, PP, PP, vp, vp, PP, PP, vp,

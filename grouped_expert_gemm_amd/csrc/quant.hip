@@ -60,9 +60,117 @@ moe_status launch_mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols
   return check_launch("mxfp8_quantize");
 }
 
+// Column-wise (per expert, along the token axis) MXFP8: a workgroup takes 32 rows x 64
+// columns of one expert's zero-padded row range. The rows come in with coalesced 16-byte
+// loads (8 lanes per 128-byte row segment, rows past the expert read as zeros) into an
+// LDS tile; four lanes per column reduce the block maximum over the 32 rows, and each
+// writes its 8 codes as one 8-byte store into the column's output row.
+__global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint16_t* __restrict__ x, int64_t R,
+                                                                     int C, int E, const int32_t* __restrict__ offsets,
+                                                                     int pad, int64_t kcap, uint8_t* __restrict__ codes,
+                                                                     uint8_t* __restrict__ scales,
+                                                                     int32_t* __restrict__ kofs_out) {
+  __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int32_t s_kofs[MOE_MAX_EXPERTS + 1];
+  __shared__ int32_t s_item[MOE_MAX_EXPERTS + 1];
+  __shared__ float tile[32][65];
+  __shared__ float red[4][64];
+  const int tid = threadIdx.x;
+  const int ncb = C / 64;
+  if (tid == 0) {  // offsets made nondecreasing inside [0, R]; padded offsets; work items per expert
+    int prev = 0, kacc = 0, iacc = 0;
+    for (int e = 0; e <= E; ++e) {
+      int v = e == 0 ? 0 : offsets[e];
+      v = v < prev ? prev : v;
+      v = v > (int)R ? (int)R : v;
+      if (e > 0) {
+        const int m = v - prev;
+        const int kp = (m + pad - 1) / pad * pad;
+        s_kofs[e - 1] = kacc;
+        s_item[e - 1] = iacc;
+        kacc += kp;
+        iacc += (kp / 32) * ncb;
+      }
+      s_off[e] = v;
+      prev = v;
+    }
+    s_kofs[E] = kacc;
+    s_item[E] = iacc;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = tid; e <= E; e += 256) kofs_out[e] = s_kofs[e];
+  const int total = s_item[E];
+  const int r = tid >> 3, c8 = (tid & 7) * 8;  // load: row r of the block, columns c8 .. c8 + 7
+  const int cc = tid & 63, q = tid >> 6;        // reduce and encode: column cc, rows 8q .. 8q + 7
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_item[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int local = item - s_item[e];
+    const int b = local / ncb, cb = local - b * ncb;
+    const int64_t row = (int64_t)s_off[e] + b * 32 + r;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < s_off[e + 1]) v = *reinterpret_cast<const uint4*>(x + row * C + cb * 64 + c8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[r][c8 + 2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+      tile[r][c8 + 2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    }
+    __syncthreads();
+    float f[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f[i] = tile[8 * q + i][cc];
+      amax = fmaxf(amax, fabsf(f[i]));
+    }
+    red[q][cc] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0][cc], red[1][cc]), fmaxf(red[2][cc], red[3][cc]));
+    const int sx = mx_scale_exponent(amax);
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = e4m3_encode(ldexpf(f[i], -sx));
+    const int64_t col = (int64_t)cb * 64 + cc;
+    const int64_t k = (int64_t)s_kofs[e] + b * 32;
+    *reinterpret_cast<uint2*>(codes + col * kcap + k + 8 * q) =
+        make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+    if (q == 0) scales[col * (kcap / 32) + k / 32] = (uint8_t)(sx + 127);
+    __syncthreads();  // the tile and the partial maxima are reused by the next item
+  }
+}
+
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" moe_status mxfp8_quantize_colwise(const void* x_bf16, int64_t R, int64_t C, int E, const int32_t* offsets,
+                                             int pad, int64_t kcap, uint8_t* e4m3_t, uint8_t* e8m0_t, int32_t* kofs,
+                                             void* stream) {
+  if (R < 0 || C < 0) return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_colwise: negative size");
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_colwise: E out of [1, 256]");
+  if (pad <= 0 || pad % 32 != 0) return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_colwise: pad must be a positive multiple of 32");
+  if (C % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "mxfp8_quantize_colwise: C % 64 != 0");
+  if (kcap % 32 != 0 || kcap < R + (int64_t)E * (pad - 1))
+    return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_colwise: kcap must be a multiple of 32 and >= R + E * (pad - 1)");
+  if (R > 0x7FFFFFFF || kcap > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "mxfp8_quantize_colwise: R or kcap >= 2^31");
+  if (!offsets || !kofs || (C > 0 && (!e4m3_t || !e8m0_t)) || (R > 0 && C > 0 && !x_bf16))
+    return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_colwise: NULL pointer");
+  if (!aligned(offsets, 4) || !aligned(kofs, 4) || (x_bf16 && !aligned(x_bf16, 16)) || (e4m3_t && !aligned(e4m3_t, 8)))
+    return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_colwise: x must be 16-byte, codes 8-byte and offsets 4-byte aligned");
+  const int64_t items = (kcap / 32) * (C / 64);
+  int64_t grid = (int64_t)num_cus() * 8;
+  if (items < grid) grid = items;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(mxfp8_quantize_colwise_kernel, dim3((unsigned)grid), dim3(256), 0, as_stream(stream),
+                     (const uint16_t*)x_bf16, R, (int)C, E, offsets, pad, kcap, e4m3_t, e8m0_t, kofs);
+  return check_launch("mxfp8_quantize_colwise");
+}
 
 extern "C" moe_status mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,
                                      uint8_t* e8m0, void* stream) {

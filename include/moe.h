@@ -172,6 +172,26 @@ moe_status mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8
                           uint8_t* e8m0, void* stream);
 
 /*
+ * Column-wise MXFP8 quantisation, expert by expert, along the token axis: the operand
+ * layout of the weight-gradient GEMMs of an MXFP8 backward, whose reduction runs over
+ * each expert's rows. Source: Challenge 2 (one scaling factor per 32 consecutive
+ * values) with Challenge 3's matching backward taking its GEMM operands in MXFP8 along
+ * each GEMM's own reduction axis (the pages show no layout; this is the reading).
+ * Expert e owns rows [offsets[e], offsets[e+1]) of x; those rows, zero-padded to a
+ * multiple of `pad`, become columns [kofs[e], kofs[e+1]) of the transposed output,
+ * quantised in blocks of 32 along that axis by the rule of mxfp8_quantize (blocks that
+ * are all padding get scale byte 0 and codes 0).
+ *   x       [R, C] bf16 (16-byte aligned), offsets [E+1] int32 (device)
+ *   e4m3_t  [C, kcap] uint8 (out, 8-byte aligned), e8m0_t [C, kcap/32] uint8 (out)
+ *   kofs    [E+1] int32 (out, device): the padded column offsets; columns at and past
+ *           kofs[E] are not written
+ * Limits: C % 64 == 0, pad a positive multiple of 32, kcap a multiple of 32 with
+ * kcap >= R + E * (pad - 1) (room for every expert's padding), 1 <= E <= MOE_MAX_EXPERTS.
+ */
+moe_status mxfp8_quantize_colwise(const void* x_bf16, int64_t R, int64_t C, int E, const int32_t* offsets, int pad,
+                                  int64_t kcap, uint8_t* e4m3_t, uint8_t* e8m0_t, int32_t* kofs, void* stream);
+
+/*
  * Per-tensor FP8 quantisation of a bf16 tensor. Source: Challenge 2 (FP8 with one
  * scaling factor for a whole tensor, the contrast to MXFP8's factor per 32 values).
  * The pages give no scale rule; the one implemented ("current scaling"):

@@ -23,7 +23,7 @@ import numpy as np
 
 __all__ = [
     "E4M3_MAX", "e4m3_encode", "e4m3_decode", "e8m0_scale_exponent",
-    "mxfp8_quantize", "mxfp8_dequantize", "mxfp8_qdq",
+    "mxfp8_quantize", "mxfp8_dequantize", "mxfp8_qdq", "mxfp8_quantize_colwise",
 ]
 
 E4M3_MAX = 448.0
@@ -100,3 +100,40 @@ def mxfp8_dequantize(codes, scales) -> np.ndarray:
 def mxfp8_qdq(x) -> np.ndarray:
     """Quantise then dequantise (the naive separate-op path of Challenge 3)."""
     return mxfp8_dequantize(*mxfp8_quantize(x))
+
+
+def mxfp8_quantize_colwise(x, offsets, pad, kcap):
+    """MXFP8 along the token axis, expert by expert: the operand layout of a weight
+    gradient, whose reduction runs over each expert's rows (the backward GEMMs take
+    their operands in MXFP8 along their own K axis, Challenge 3's matching backward).
+
+    x [R, C]; expert e owns rows [offsets[e], offsets[e+1]). Its rows, zero-padded to a
+    multiple of `pad` (a multiple of 32), become columns [kofs[e], kofs[e+1]) of the
+    transposed output and are quantised in blocks of 32 along that axis by the rule of
+    mxfp8_quantize (all-padding blocks: scale byte 0, codes 0).
+    Returns (codes [C, kcap] uint8, scales [C, kcap / 32] uint8, kofs [E + 1] int32);
+    entries at and past kofs[E] are 0.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    R, C = x.shape
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E = len(offsets) - 1
+    assert pad % _BLOCK == 0 and kcap % _BLOCK == 0
+    kofs = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        m = int(offsets[e + 1] - offsets[e])
+        kofs[e + 1] = kofs[e] + -(-m // pad) * pad
+    assert kofs[E] <= kcap
+    codes = np.zeros((C, kcap), dtype=np.uint8)
+    scales = np.zeros((C, kcap // _BLOCK), dtype=np.uint8)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        kp = int(kofs[e + 1] - kofs[e])
+        if kp == 0:
+            continue
+        seg = np.zeros((kp, C))
+        seg[: b - a] = x[a:b]
+        cq, sq = mxfp8_quantize(seg.T)
+        codes[:, kofs[e]:kofs[e + 1]] = cq
+        scales[:, kofs[e] // _BLOCK:kofs[e + 1] // _BLOCK] = sq
+    return codes, scales, kofs.astype(np.int32)

@@ -121,3 +121,15 @@ def test_fp8_tensor_argument_checks(L):
                                ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
                                ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096), 1 << 40, None)
     assert st == UNS and b"save_for_bwd" in L.moe_last_error()
+
+
+def test_mxfp8_colwise_argument_checks(L):
+    from grouped_expert_gemm_amd import _lib
+    INV, UNS = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED
+    d = ctypes.c_void_p(4096)
+    assert L.mxfp8_quantize_colwise(d, 100, 96, 4, d, 32, 256, d, d, d, None) == UNS     # C % 64
+    assert L.mxfp8_quantize_colwise(d, 100, 64, 4, d, 48, 256, d, d, d, None) == INV     # pad % 32
+    assert L.mxfp8_quantize_colwise(d, 100, 64, 4, d, 32, 192, d, d, d, None) == INV     # kcap < R + E (pad - 1)
+    assert L.mxfp8_quantize_colwise(d, 100, 64, 0, d, 32, 256, d, d, d, None) == INV     # E = 0
+    assert L.mxfp8_quantize_colwise(d, 100, 64, 4, None, 32, 256, d, d, d, None) == INV  # NULL offsets
+    assert b"kcap" in L.moe_last_error() or b"NULL" in L.moe_last_error()

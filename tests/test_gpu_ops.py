@@ -189,6 +189,35 @@ def test_combine(moe):
 # MXFP8 quantisation: bit-exact
 # ---------------------------------------------------------------------------
 
+COLWISE = [
+    # name, expert sizes, C, pad
+    ("ragged_idle", [37, 0, 100, 1, 162], 128, 32),
+    ("gemm_pad", [300, 5, 0, 257], 64, 256),
+    ("mixtral_bwd_dY", None, 4096, 256),   # the T=4096 backward's dY: 8192 rows, 8 experts
+]
+
+
+@pytest.mark.parametrize("case", COLWISE, ids=[c[0] for c in COLWISE])
+def test_mxfp8_quantize_colwise_bit_exact(moe, case):
+    name, sizes, C, pad = case
+    rng = np.random.default_rng(21)
+    if sizes is None:
+        w = WORKLOADS["mixtral_fwd_bwd"]
+        idx, _ = oracle.route_topk(make_inputs(scaled(w, H=32, I=32), want_float=False).logits, w.k)
+        sizes = list(np.bincount(idx.ravel(), minlength=w.E))
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(off[-1])
+    xb = f32_to_bf16_bits((rng.standard_normal((R, C)) * np.exp2(rng.integers(-6, 6, (R, 1)))).astype(np.float32))
+    print(f"mxfp8 colwise {name}: R={R} C={C} E={len(sizes)} pad={pad}", flush=True)
+    codes, scales, kofs = moe.mxfp8_quantize_colwise(dev_bf16(xb), torch.from_numpy(off).cuda(), pad)
+    torch.cuda.synchronize()
+    kcap = codes.shape[1]
+    rc, rs, rk = oracle.mxfp8_quantize_colwise(bf16_bits_to_f32(xb), off, pad, kcap)
+    assert np.array_equal(kofs.cpu().numpy(), rk)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+
+
 def test_mxfp8_quantize_bit_exact(moe):
     rng = np.random.default_rng(4)
     rows, cols = 300, 1024

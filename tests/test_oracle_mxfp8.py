@@ -150,3 +150,51 @@ def test_mxfp8_mlp_equals_exact_mlp_on_representable_inputs():
         a, b = m["offsets"][e], m["offsets"][e + 1]
         y_ref[a:b] = hq[a:b] @ w2[e].T
     np.testing.assert_allclose(y8, y_ref, rtol=1e-12, atol=1e-14)
+
+
+def test_colwise_brute_force_tiny():
+    """Column-wise (per expert, along the token axis) quantisation against a direct
+    per-element construction: blocks of 32 along each expert's zero-padded rows, the
+    scale by search over exponents, every code by the nearest codebook value."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((45, 3)) * np.exp2(rng.integers(-8, 8, (45, 3)))).astype(np.float32)
+    x[10, 1] = -0.0
+    off = np.array([0, 7, 7, 45])
+    codes, scales, kofs = oracle.mxfp8_quantize_colwise(x, off, 32, 128)
+    assert list(kofs) == [0, 32, 32, 96]      # 7 and 38 rows padded to 32 and 64
+    cb = _codebook()
+    items = sorted(cb.items())
+    for c in range(3):
+        for e in range(3):
+            col = np.zeros(int(kofs[e + 1] - kofs[e]))
+            col[: off[e + 1] - off[e]] = x[off[e]:off[e + 1], c]
+            for blk in range(len(col) // 32):
+                v = col[32 * blk: 32 * blk + 32]
+                a = np.abs(v).max()
+                s = -127 if a == 0 else next(t for t in range(-127, 128) if a <= 448 * 2.0 ** t)
+                assert scales[c, kofs[e] // 32 + blk] == s + 127
+                for i, xv in enumerate(v):
+                    q = xv / 2.0 ** s
+                    d = [(abs(val - q), code) for code, val in items if (code >> 7) == (1 if np.signbit(xv) else 0)]
+                    dmin = min(dd for dd, _ in d)
+                    best = [code for dd, code in d if dd == dmin]
+                    if len(best) > 1:
+                        best = [b for b in best if b % 2 == 0]
+                    assert codes[c, kofs[e] + 32 * blk + i] == best[0], (c, e, blk, i)
+    assert not codes[:, 96:].any() and not scales[:, 3:].any()
+
+
+def test_colwise_padding_and_segment_independence():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((300, 64)).astype(np.float32)
+    off = np.array([0, 40, 40, 300])
+    codes, scales, kofs = oracle.mxfp8_quantize_colwise(x, off, 256, 1024)
+    assert list(kofs) == [0, 256, 256, 768]   # 40 and 260 rows padded to 256 and 512
+    # expert 0 has 40 rows: blocks 2..7 of its padded range are all padding
+    assert not scales[:, 2:8].any() and not codes[:, 64:256].any()
+    assert not codes[:, 40:64].any()          # the padded tail of block 1 is code 0
+    # changing expert 0's rows leaves expert 2's columns alone
+    y = x.copy()
+    y[:40] *= 3.0
+    c2, s2, _ = oracle.mxfp8_quantize_colwise(y, off, 256, 1024)
+    assert np.array_equal(c2[:, 256:], codes[:, 256:]) and np.array_equal(s2[:, 8:], scales[:, 8:])
