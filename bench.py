@@ -271,6 +271,48 @@ def router_measure(w, inp, reps=20):
     return out
 
 
+def colwise_measure(reps=20):
+    """Column-wise MXFP8 quantisation (per expert, along the token axis; the operand
+    layout of MXFP8 weight gradients) of the Mixtral backward's dY [R, H] and h [R, I]
+    (T=4096, top-2), pad 256, timed with events over `reps` calls: HBM-bound."""
+    import torch
+
+    import grouped_expert_gemm_amd as moe
+    from moe_inputs import WORKLOADS, make_inputs, scaled
+
+    w = WORKLOADS["mixtral_fwd_bwd"]
+    inp = make_inputs(scaled(w, H=32, I=32), want_float=False)  # the routing depends on the logits only
+    idx, p = moe.moe_route_topk(torch.from_numpy(inp.logits).cuda(), w.k)
+    r = moe.moe_permute(torch.zeros((w.T, 32), dtype=torch.bfloat16, device="cuda"), idx, p, w.E)
+    off = r["offsets"]
+    R = w.T * w.k
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    recs = []
+    for name, C in (("dY", w.H), ("h", w.I)):
+        x = torch.randn((R, C), generator=g, device="cuda").to(torch.bfloat16)
+        codes, scales, kofs = moe.mxfp8_quantize_colwise(x, off, 256)  # allocates the outputs once
+        kcap = codes.shape[1]
+        L = moe.lib()
+        vp = ctypes.c_void_p
+        args = (vp(x.data_ptr()), R, C, w.E, vp(off.data_ptr()), 256, kcap, vp(codes.data_ptr()),
+                vp(scales.data_ptr()), vp(kofs.data_ptr()), vp(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):   # the C entry point on the same buffers: no allocation or fill in the loop
+            L.mxfp8_quantize_colwise(*args)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        ktot = int(kofs[-1].item())
+        nbytes = R * C * 2 + C * ktot + C * ktot // 32
+        recs.append({"tensor": name, "rows": R, "cols": C, "padded_rows": ktot, "ms": round(ms, 4), "bound": "hbm",
+                     "achieved_GBps": round(nbytes / ms / 1e6, 1), "peak_GBps": HBM_PEAK_GBPS,
+                     "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 4)})
+        log(f"mxfp8 colwise {name} [{R}, {C}]: {ms:.3f} ms -> {nbytes / ms / 1e6:.0f} GB/s")
+    return recs
+
+
 def traffic_record():
     """HBM bytes per gate_up launch from the committed rocprofv3 counter runs, or None
     if they were taken on a different version of the kernel source."""
@@ -352,6 +394,8 @@ def only_measurement(which, steps, warmup):
         w8 = WORKLOADS["mixtral_mxfp8_fwd"]
         return [extra_forward(w8, inp, steps, warmup, compute="mxfp8"),
                 extra_forward(w8, inp, steps, warmup, compute="mxfp8", prequant=True)]
+    if which == "colwise":
+        return colwise_measure(steps)
     if which == "fp8":
         w8 = WORKLOADS["mixtral_mxfp8_fwd"]
         return [extra_forward(w8, inp, steps, warmup, compute="fp8"),
@@ -369,7 +413,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip the MXFP8 and Qwen3 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["fwd_bwd", "qwen3", "mxfp8", "fp8", "router"],
+    ap.add_argument("--only", choices=["fwd_bwd", "qwen3", "mxfp8", "fp8", "router", "colwise"],
                     help="run one measurement and print its record (kernel traces of that workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
@@ -447,6 +491,7 @@ def main():
         log(f"inputs {wq.name}: {time.perf_counter() - t0:.1f} s")
         result["qwen3_fwd"] = extra_forward(wq, inpq, max(3, args.steps // 2), args.warmup)
         result["router"] = [router_measure(w, inp), router_measure(wq, inpq)]
+        result["mxfp8_colwise"] = colwise_measure()
         del inpq
         torch.cuda.empty_cache()
 

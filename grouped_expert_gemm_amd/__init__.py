@@ -187,15 +187,15 @@ def fp8_tensor_quantize(x: torch.Tensor):
 def mxfp8_quantize_colwise(x: torch.Tensor, offsets: torch.Tensor, pad: int = 32):
     """bf16 [R, C] with expert row offsets [E+1] -> (E4M3 codes [C, kcap], E8M0 scales
     [C, kcap/32], padded offsets kofs [E+1]) with kcap = R + E * (pad - 1) rounded up to
-    32: each expert's rows, zero-padded to a multiple of pad, quantised along the token
-    axis as columns [kofs[e], kofs[e+1])."""
+    128 (whole cache lines per output row): each expert's rows, zero-padded to a
+    multiple of pad, quantised along the token axis as columns [kofs[e], kofs[e+1])."""
     _need_cuda(x, offsets)
     if x.dtype != torch.bfloat16:
         raise ValueError("mxfp8_quantize_colwise takes bfloat16")
     x = x.contiguous()
     R, C = x.shape
     E = offsets.numel() - 1
-    kcap = (R + E * (pad - 1) + 31) // 32 * 32
+    kcap = (R + E * (pad - 1) + 127) // 128 * 128
     codes = torch.zeros((C, kcap), dtype=torch.uint8, device=x.device)
     scales = torch.zeros((C, kcap // 32), dtype=torch.uint8, device=x.device)
     kofs = torch.empty(E + 1, dtype=torch.int32, device=x.device)

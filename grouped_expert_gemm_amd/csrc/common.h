@@ -90,4 +90,15 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
   return sign | code;
 }
 
+// Four E4M3 codes packed into a word (a in the low byte) by the hardware conversion,
+// which rounds to nearest, ties to even, into gfx950's OCP E4M3 (FN) format and keeps
+// subnormal results and the sign of zero: the same codes as e4m3_encode for every
+// |v| < 464, which covers each value that reaches it here (x * 2^-s with s from
+// mx_scale_exponent is at most 448).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 }  // namespace moe

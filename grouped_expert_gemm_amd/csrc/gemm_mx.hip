@@ -365,10 +365,9 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
             uint8_t* C = reinterpret_cast<uint8_t*>(prm.c) + mg * prm.I + col0;
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-              uint32_t wv = 0;
-#pragma unroll
-              for (int v = 0; v < 4; ++v) wv |= e4m3_encode(ldexpf(h[i4 * 4 + v], -sx)) << (8 * v);
-              *reinterpret_cast<uint32_t*>(C + i4 * 8 + lhi * 4) = wv;
+              *reinterpret_cast<uint32_t*>(C + i4 * 8 + lhi * 4) =
+                  e4m3_pack4(ldexpf(h[i4 * 4], -sx), ldexpf(h[i4 * 4 + 1], -sx), ldexpf(h[i4 * 4 + 2], -sx),
+                             ldexpf(h[i4 * 4 + 3], -sx));
             }
             if (lhi == 0) prm.c_s[mg * (prm.I / 32) + col0 / 32] = (uint8_t)(sx + 127);
           }

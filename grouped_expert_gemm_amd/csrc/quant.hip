@@ -36,12 +36,9 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint4* __rest
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     amax = fmaxf(amax, __shfl_xor(amax, 2));
     const int s = mx_scale_exponent(amax);
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = e4m3_encode(ldexpf(f[i], -s));
     if (live) {
-      codes[q] = make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                            c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+      codes[q] = make_uint2(e4m3_pack4(ldexpf(f[0], -s), ldexpf(f[1], -s), ldexpf(f[2], -s), ldexpf(f[3], -s)),
+                            e4m3_pack4(ldexpf(f[4], -s), ldexpf(f[5], -s), ldexpf(f[6], -s), ldexpf(f[7], -s)));
       if ((q & 3) == 0) scales[q >> 2] = (uint8_t)(s + 127);
     }
   }
@@ -60,11 +57,12 @@ moe_status launch_mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols
   return check_launch("mxfp8_quantize");
 }
 
-// Column-wise (per expert, along the token axis) MXFP8: a workgroup takes 32 rows x 64
-// columns of one expert's zero-padded row range. The rows come in with coalesced 16-byte
-// loads (8 lanes per 128-byte row segment, rows past the expert read as zeros) into an
-// LDS tile; four lanes per column reduce the block maximum over the 32 rows, and each
-// writes its 8 codes as one 8-byte store into the column's output row.
+// Column-wise (per expert, along the token axis) MXFP8: a workgroup takes up to four
+// 32-row blocks (128 rows) x 64 columns of one expert's zero-padded row range. The rows
+// come in with coalesced 16-byte loads (8 lanes per 128-byte row segment; rows past the
+// expert read as zeros) into an LDS tile; lane (q, c) then owns block q of column c:
+// its maximum, scale byte and 32 codes, stored as two 16-byte stores, so the four
+// blocks of a column leave as one whole 128-byte line of the output row.
 __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint16_t* __restrict__ x, int64_t R,
                                                                      int C, int E, const int32_t* __restrict__ offsets,
                                                                      int pad, int64_t kcap, uint8_t* __restrict__ codes,
@@ -73,8 +71,7 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
   __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int32_t s_kofs[MOE_MAX_EXPERTS + 1];
   __shared__ int32_t s_item[MOE_MAX_EXPERTS + 1];
-  __shared__ float tile[32][65];
-  __shared__ float red[4][64];
+  __shared__ float tile[128][65];
   const int tid = threadIdx.x;
   const int ncb = C / 64;
   if (tid == 0) {  // offsets made nondecreasing inside [0, R]; padded offsets; work items per expert
@@ -89,7 +86,7 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
         s_kofs[e - 1] = kacc;
         s_item[e - 1] = iacc;
         kacc += kp;
-        iacc += (kp / 32) * ncb;
+        iacc += ((kp / 32 + 3) / 4) * ncb;
       }
       s_off[e] = v;
       prev = v;
@@ -101,8 +98,8 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
   if (blockIdx.x == 0)
     for (int e = tid; e <= E; e += 256) kofs_out[e] = s_kofs[e];
   const int total = s_item[E];
-  const int r = tid >> 3, c8 = (tid & 7) * 8;  // load: row r of the block, columns c8 .. c8 + 7
-  const int cc = tid & 63, q = tid >> 6;        // reduce and encode: column cc, rows 8q .. 8q + 7
+  const int r = tid >> 3, c8 = (tid & 7) * 8;  // load: rows r + 32i, columns c8 .. c8 + 7
+  const int cc = tid & 63, q = tid >> 6;        // encode: block q of column cc
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     int lo = 0, hi = E - 1;
     while (lo < hi) {
@@ -111,37 +108,42 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
     }
     const int e = lo;
     const int local = item - s_item[e];
-    const int b = local / ncb, cb = local - b * ncb;
-    const int64_t row = (int64_t)s_off[e] + b * 32 + r;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < s_off[e + 1]) v = *reinterpret_cast<const uint4*>(x + row * C + cb * 64 + c8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const int j = local / ncb, cb = local - j * ncb;
+    const int nblk = (s_kofs[e + 1] - s_kofs[e]) / 32;        // blocks in the expert's padded range
+    const int blocks = nblk - 4 * j < 4 ? nblk - 4 * j : 4;   // blocks of this item
+    const int64_t row0 = (int64_t)s_off[e] + 128 * j;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      tile[r][c8 + 2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
-      tile[r][c8 + 2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = row0 + r + 32 * i;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < s_off[e + 1]) v = *reinterpret_cast<const uint4*>(x + row * C + cb * 64 + c8);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        tile[r + 32 * i][c8 + 2 * h] = bf16_to_f32(w[h] & 0xFFFFu);
+        tile[r + 32 * i][c8 + 2 * h + 1] = bf16_to_f32(w[h] >> 16);
+      }
     }
     __syncthreads();
-    float f[8];
-    float amax = 0.f;
+    if (q < blocks) {
+      float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      f[i] = tile[8 * q + i][cc];
-      amax = fmaxf(amax, fabsf(f[i]));
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(tile[32 * q + i][cc]));
+      const int sx = mx_scale_exponent(amax);
+      uint32_t wd[8];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const float* t = &tile[32 * q + 4 * g][cc];
+        wd[g] = e4m3_pack4(ldexpf(t[0], -sx), ldexpf(t[65], -sx), ldexpf(t[130], -sx), ldexpf(t[195], -sx));
+      }
+      const int64_t col = (int64_t)cb * 64 + cc;
+      const int64_t k = (int64_t)s_kofs[e] + 128 * j + 32 * q;
+      uint4* dst = reinterpret_cast<uint4*>(codes + col * kcap + k);
+      dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+      scales[col * (kcap / 32) + k / 32] = (uint8_t)(sx + 127);
     }
-    red[q][cc] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0][cc], red[1][cc]), fmaxf(red[2][cc], red[3][cc]));
-    const int sx = mx_scale_exponent(amax);
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = e4m3_encode(ldexpf(f[i], -sx));
-    const int64_t col = (int64_t)cb * 64 + cc;
-    const int64_t k = (int64_t)s_kofs[e] + b * 32;
-    *reinterpret_cast<uint2*>(codes + col * kcap + k + 8 * q) =
-        make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
-    if (q == 0) scales[col * (kcap / 32) + k / 32] = (uint8_t)(sx + 127);
-    __syncthreads();  // the tile and the partial maxima are reused by the next item
+    __syncthreads();  // the tile is reused by the next item
   }
 }
 
@@ -161,9 +163,9 @@ extern "C" moe_status mxfp8_quantize_colwise(const void* x_bf16, int64_t R, int6
   if (R > 0x7FFFFFFF || kcap > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "mxfp8_quantize_colwise: R or kcap >= 2^31");
   if (!offsets || !kofs || (C > 0 && (!e4m3_t || !e8m0_t)) || (R > 0 && C > 0 && !x_bf16))
     return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_colwise: NULL pointer");
-  if (!aligned(offsets, 4) || !aligned(kofs, 4) || (x_bf16 && !aligned(x_bf16, 16)) || (e4m3_t && !aligned(e4m3_t, 8)))
-    return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_colwise: x must be 16-byte, codes 8-byte and offsets 4-byte aligned");
-  const int64_t items = (kcap / 32) * (C / 64);
+  if (!aligned(offsets, 4) || !aligned(kofs, 4) || (x_bf16 && !aligned(x_bf16, 16)) || (e4m3_t && !aligned(e4m3_t, 16)))
+    return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_colwise: x and codes must be 16-byte and offsets 4-byte aligned");
+  const int64_t items = (kcap / 32 + 3 * E) / 4 * (C / 64) + E * (C / 64);
   int64_t grid = (int64_t)num_cus() * 8;
   if (items < grid) grid = items;
   if (grid < 1) grid = 1;

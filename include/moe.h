@@ -182,7 +182,7 @@ moe_status mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8
  * quantised in blocks of 32 along that axis by the rule of mxfp8_quantize (blocks that
  * are all padding get scale byte 0 and codes 0).
  *   x       [R, C] bf16 (16-byte aligned), offsets [E+1] int32 (device)
- *   e4m3_t  [C, kcap] uint8 (out, 8-byte aligned), e8m0_t [C, kcap/32] uint8 (out)
+ *   e4m3_t  [C, kcap] uint8 (out, 16-byte aligned), e8m0_t [C, kcap/32] uint8 (out)
  *   kofs    [E+1] int32 (out, device): the padded column offsets; columns at and past
  *           kofs[E] are not written
  * Limits: C % 64 == 0, pad a positive multiple of 32, kcap a multiple of 32 with

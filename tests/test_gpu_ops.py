@@ -218,6 +218,34 @@ def test_mxfp8_quantize_colwise_bit_exact(moe, case):
     assert np.array_equal(scales.cpu().numpy(), rs)
 
 
+def test_mxfp8_quantize_colwise_special_values(moe):
+    """Blocks along the token axis holding zeros, negative zeros, bf16 subnormals, a block
+    whose maximum sits on a scale boundary, values near the top of the float range, values
+    below 2^-126, one large value over ones (the rest land on subnormal codes) and a
+    ramp through zero; three experts, the middle one empty."""
+    rng = np.random.default_rng(3)
+    R, C = 320, 128
+    x = rng.standard_normal((R, C)).astype(np.float32)
+    x *= np.exp2(rng.integers(-40, 40, (R // 32, C))).repeat(32, 0).astype(np.float32)
+    x[0:32, 0] = 0.0
+    x[32:64, 1] = -0.0
+    x[64:96, 2] = rng.standard_normal(32) * 1e-39
+    x[96:128, 3] = 448.0 * 2.0 ** 5
+    x[128:160, 4] = rng.standard_normal(32) * 3e38 / 4
+    x[160:192, 5] = rng.standard_normal(32) * 2.0 ** -130
+    x[192:224, 6] = 1.0
+    x[192, 6] = 2.0 ** 20
+    x[224:256, 7] = np.linspace(-1, 1, 32) * 2.0 ** -7
+    xb = f32_to_bf16_bits(x)
+    off = np.array([0, 100, 100, 320], np.int32)
+    codes, scales, kofs = moe.mxfp8_quantize_colwise(dev_bf16(xb), torch.from_numpy(off).cuda(), 32)
+    torch.cuda.synchronize()
+    rc, rs, rk = oracle.mxfp8_quantize_colwise(bf16_bits_to_f32(xb), off, 32, codes.shape[1])
+    assert np.array_equal(kofs.cpu().numpy(), rk)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+
+
 def test_mxfp8_quantize_bit_exact(moe):
     rng = np.random.default_rng(4)
     rows, cols = 300, 1024
