@@ -35,7 +35,7 @@ __all__ = [
     "route_topk", "permute", "silu", "expert_ffn", "moe_ffn_forward",
     "grouped_mlp_forward",
     "grouped_linear", "grouped_mlp_forward_mxfp8", "unpermute_combine",
-    "grouped_mlp_backward", "moe_ffn_backward", "gather_rows",
+    "grouped_mlp_backward", "moe_ffn_backward", "gather_rows", "grouped_mlp_backward_mxfp8",
 ]
 
 f64 = np.float64
@@ -317,3 +317,66 @@ def moe_ffn_backward(hidden_states, w_gate_up, w_down, topk_idx, routing_weights
         np.add.at(dx, top_x, dZ @ W1)
         dw1[e] = dZ.T @ x[top_x]
     return dict(dx=dx, dw_gate_up=dw1, dw_down=dw2, drouting_weights=dp)
+
+
+def _qdq_rows_per_expert(x, a, b):
+    """x[a:b] quantised through MXFP8 along the token axis: 32-row blocks starting at the
+    expert's first row, the last block zero-padded (padding rows do not change a block's
+    maximum and are dropped again)."""
+    seg = np.asarray(x, dtype=f64)[a:b]
+    m = b - a
+    padded = np.zeros((-(-m // 32) * 32, seg.shape[1]), f64)
+    padded[:m] = seg
+    return mxfp8_qdq(padded.T).T[:m]
+
+
+def grouped_mlp_backward_mxfp8(dy_perm, x_perm, z_save, h_save, w_gate_up, w_down, offsets, prob_perm,
+                               quantize=True):
+    """The grouped MLP backward with every GEMM operand passed through MXFP8 along that
+    GEMM's own reduction (K) axis (Challenge 2's 32-value blocks; Challenge 3 puts the
+    backward GEMMs in MXFP8 as it does the forward ones):
+
+      dH     = Q_H(dY) Q_H(W2_e)                      (K = H: dY along its rows' H, W2 along H)
+      dprob, dA, dG, dU from dH, the saved z = [G, U] and prob, as in grouped_mlp_backward
+      dx     = Q_2I(dZ) Q_2I(W1_e)                    (K = 2I)
+      dW2_e  = Q_tok(dY_e)^T Q_tok(h_e)               (K = the expert's rows)
+      dW1_e  = Q_tok(dZ_e)^T Q_tok(x_e)
+
+    Q_tok blocks start at each expert's first row (the padded layout of
+    mxfp8_quantize_colwise). z_save [R, 2I] and h_save [R, I] are the forward's saved
+    tensors, taken as given. quantize=False drops every Q and gives the bf16 backward's
+    formulas evaluated on the saved z and h."""
+    q = mxfp8_qdq if quantize else (lambda t: np.asarray(t, dtype=f64))
+    qt = _qdq_rows_per_expert if quantize else (lambda t, a, b: np.asarray(t, dtype=f64)[a:b])
+    dy = np.asarray(dy_perm, dtype=f64)
+    x = np.asarray(x_perm, dtype=f64)
+    z = np.asarray(z_save, dtype=f64)
+    h = np.asarray(h_save, dtype=f64)
+    p = np.asarray(prob_perm, dtype=f64)
+    off = np.asarray(offsets, dtype=np.int64)
+    E, twoI, H = w_gate_up.shape
+    I = twoI // 2
+    R = x.shape[0]
+    dx = np.zeros((R, H), f64)
+    dw1 = np.zeros((E, twoI, H), f64)
+    dw2 = np.zeros((E, H, I), f64)
+    dprob = np.zeros(R, f64)
+    dyq = q(dy) if R else dy
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        W1 = np.asarray(w_gate_up[e], dtype=f64)
+        W2 = np.asarray(w_down[e], dtype=f64)
+        G, U = z[a:b, :I], z[a:b, I:]
+        sg = _sigmoid(G)
+        A = G * sg * U
+        pe = p[a:b, None]
+        dHs = dyq[a:b] @ q(W2.T).T
+        dprob[a:b] = (dHs * A).sum(axis=1)
+        dA = dHs * pe
+        dZ = np.concatenate([dA * U * sg * (1.0 + G * (1.0 - sg)), dA * G * sg], axis=1)
+        dx[a:b] = q(dZ) @ q(W1.T).T
+        dw2[e] = qt(dy, a, b).T @ qt(h, a, b)
+        dw1[e] = qt(dZ, 0, b - a).T @ qt(x, a, b)
+    return dict(dx_perm=dx, dw_gate_up=dw1, dw_down=dw2, dprob_perm=dprob)

@@ -198,3 +198,94 @@ def test_colwise_padding_and_segment_independence():
     y[:40] *= 3.0
     c2, s2, _ = oracle.mxfp8_quantize_colwise(y, off, 256, 1024)
     assert np.array_equal(c2[:, 256:], codes[:, 256:]) and np.array_equal(s2[:, 8:], scales[:, 8:])
+
+
+def _bwd_case(seed=5, sizes=(37, 0, 70), H=64, I=64):
+    """Small backward inputs: saved z = x W1^T and h = silu(G) U p from the exact forward."""
+    rng = np.random.default_rng(seed)
+    E = len(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    R = int(off[-1])
+    x = rng.standard_normal((R, H))
+    w1 = 0.1 * rng.standard_normal((E, 2 * I, H))
+    w2 = 0.1 * rng.standard_normal((E, H, I))
+    p = rng.uniform(0.1, 1.0, R)
+    dy = rng.standard_normal((R, H))
+    _, z, h = oracle.grouped_mlp_forward(x, w1, w2, off, p)
+    return dict(dy_perm=dy, x_perm=x, z_save=z, h_save=h, w_gate_up=w1, w_down=w2, offsets=off, prob_perm=p)
+
+
+def test_mxfp8_backward_without_quantisation_is_the_exact_backward():
+    """Dropping every quantiser leaves the bf16 backward's formulas (which recompute z
+    from x and W1): the two must agree to float64 round-off, with zero weight gradients
+    for the empty expert."""
+    c = _bwd_case()
+    got = oracle.grouped_mlp_backward_mxfp8(**c, quantize=False)
+    ref = oracle.grouped_mlp_backward(c["dy_perm"], c["x_perm"], c["w_gate_up"], c["w_down"], c["offsets"],
+                                      c["prob_perm"])
+    for k in ref:
+        np.testing.assert_allclose(got[k], ref[k], rtol=1e-11, atol=1e-12)
+    assert not got["dw_gate_up"][1].any() and not got["dw_down"][1].any()
+
+
+def test_mxfp8_backward_quantises_each_gemm_along_its_reduction_axis():
+    """Power-of-two rescalings that MX quantisation along the stated axis carries through
+    exactly (a block's scale absorbs them) but quantisation along the other axis would
+    not: K-blocks of the dH GEMM (dY's columns and W2's rows in one 32-block of H, in
+    opposite directions), one column of W1 (the dx GEMM quantises W1 along 2I), one
+    column of x, dY or h (the weight-gradient GEMMs quantise along the expert's rows)."""
+    c = _bwd_case()
+    base = oracle.grouped_mlp_backward_mxfp8(**c)
+    # 1. dH = Q_H(dY) Q_H(W2): a 32-block of H scaled by 2^5 in dY and 2^-5 in W2
+    c1 = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in c.items()}
+    c1["dy_perm"][:, 32:64] *= 2.0 ** 5
+    c1["w_down"][:, 32:64, :] *= 2.0 ** -5
+    r1 = oracle.grouped_mlp_backward_mxfp8(**c1)
+    np.testing.assert_array_equal(r1["dprob_perm"], base["dprob_perm"])
+    np.testing.assert_array_equal(r1["dx_perm"], base["dx_perm"])
+    np.testing.assert_array_equal(r1["dw_gate_up"], base["dw_gate_up"])
+    # the same rescaling over a block that straddles two K-blocks does change dH
+    c1b = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in c.items()}
+    c1b["dy_perm"][:, 16:48] *= 2.0 ** 5
+    c1b["w_down"][:, 16:48, :] *= 2.0 ** -5
+    assert not np.array_equal(oracle.grouped_mlp_backward_mxfp8(**c1b)["dprob_perm"], base["dprob_perm"])
+    # 2. dx = Q_2I(dZ) Q_2I(W1): column 7 of every W1 scaled by 2^3 scales column 7 of dx
+    c2 = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in c.items()}
+    c2["w_gate_up"][:, :, 7] *= 8.0
+    r2 = oracle.grouped_mlp_backward_mxfp8(**c2)
+    want = base["dx_perm"].copy()
+    want[:, 7] *= 8.0
+    np.testing.assert_array_equal(r2["dx_perm"], want)
+    # 3. dW1 = Q_tok(dZ)^T Q_tok(x): column 5 of x scaled by 2^4 scales column 5 of dW1
+    c3 = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in c.items()}
+    c3["x_perm"][:, 5] *= 16.0
+    r3 = oracle.grouped_mlp_backward_mxfp8(**c3)
+    want = base["dw_gate_up"].copy()
+    want[:, :, 5] *= 16.0
+    np.testing.assert_array_equal(r3["dw_gate_up"], want)
+    # 4. dW2 = Q_tok(dY)^T Q_tok(h): column 9 of h scales column 9 of dW2; column 3 of dY
+    #    scales row 3 of dW2 (dY also feeds dH, whose blocks it changes: not checked here)
+    c4 = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in c.items()}
+    c4["h_save"][:, 9] *= 4.0
+    c4["dy_perm"][:, 3] *= 0.5
+    r4 = oracle.grouped_mlp_backward_mxfp8(**c4)
+    want = base["dw_down"].copy()
+    want[:, :, 9] *= 4.0
+    want[:, 3, :] *= 0.5
+    np.testing.assert_array_equal(r4["dw_down"], want)
+
+
+def test_mxfp8_backward_token_blocks_start_at_each_expert():
+    """The token-axis blocks of the weight gradients restart at every expert's first
+    row: moving rows from expert 0 to expert 2's range through an empty expert must not
+    change expert 2's gradient when its own rows and their order are unchanged, and an
+    expert's gradient equals a one-expert call on its rows alone."""
+    c = _bwd_case(sizes=(37, 0, 70))
+    base = oracle.grouped_mlp_backward_mxfp8(**c)
+    a, b = 37, 107
+    solo = {k: (v[a:b] if k in ("dy_perm", "x_perm", "z_save", "h_save", "prob_perm") else v)
+            for k, v in c.items()}
+    solo["offsets"] = np.array([0, 0, 0, b - a])
+    r = oracle.grouped_mlp_backward_mxfp8(**solo)
+    np.testing.assert_array_equal(r["dw_down"][2], base["dw_down"][2])
+    np.testing.assert_array_equal(r["dw_gate_up"][2], base["dw_gate_up"][2])
