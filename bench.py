@@ -379,12 +379,58 @@ def fwd_bwd_measure(steps, warmup):
             "flop_per_step": flopb}
 
 
+def bwd_measure(reps=10):
+    """The grouped MLP backward call alone at the Mixtral fwd+bwd shape (T=4096, top-2),
+    bf16 and MXFP8, on the saved z and h of one bf16 forward. Work: the four backward
+    GEMMs, 2x the forward's GEMM flop."""
+    import torch
+    from grouped_expert_gemm_amd import _lib
+    import grouped_expert_gemm_amd as moe
+    from moe_inputs import WORKLOADS, make_inputs
+
+    wb = WORKLOADS["mixtral_fwd_bwd"]
+    lb = Layer(wb, make_inputs(wb, want_float=False), backward=True)
+    lb.step()
+    torch.cuda.synchronize()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    flop = 2.0 * wb.gemm_flop_fwd()
+    out = []
+    for name, comp in (("bf16", _lib.MOE_BF16), ("mxfp8", _lib.MOE_MXFP8)):
+        desc = _lib.MlpDesc(wb.E, wb.H, wb.I, comp, _lib.MOE_BF16, _lib.MOE_BF16, 1)
+        ws = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_BWD, desc, lb.R), dtype=torch.uint8, device="cuda")
+
+        def call():
+            _lib.check("mlp bwd", lb.L.moe_grouped_mlp_bwd(
+                ctypes.byref(desc), lb.R, p(lb.dy), p(lb.x_perm), p(lb.z), p(lb.h), p(lb.prob_perm), lb.t1, lb.t2,
+                p(lb.offsets), p(lb.dx_perm), lb.d1, lb.d2, p(lb.dprob_perm), p(ws), ws.numel(), lb.stream))
+
+        for _ in range(2):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        v = flop / (ms * 1e-3) / 1e12
+        peak = BF16_PEAK_TFLOPS if name == "bf16" else 2 * BF16_PEAK_TFLOPS
+        log(f"grouped MLP backward {name}: {ms:.3f} ms -> {v:.1f} TFLOP/s ({100 * v / peak:.1f}% of {peak:.0f})")
+        out.append({"workload": "mixtral_fwd_bwd", "compute": name, "ms": round(ms, 4), "value": round(v, 2),
+                    "unit": "TFLOP/s", "pct_of_peak": round(100 * v / peak, 2), "flop": flop})
+        del ws
+    return out
+
+
 def only_measurement(which, steps, warmup):
     """One measurement on its own (for kernel traces of that workload)."""
     from moe_inputs import WORKLOADS, make_inputs
 
     if which == "fwd_bwd":
         return fwd_bwd_measure(steps, warmup)
+    if which == "bwd":
+        return bwd_measure(steps)
     if which == "qwen3":
         wq = WORKLOADS["qwen3_fwd"]
         return extra_forward(wq, make_inputs(wq, want_float=False), steps, warmup)
@@ -413,7 +459,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip the MXFP8 and Qwen3 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["fwd_bwd", "qwen3", "mxfp8", "fp8", "router", "colwise"],
+    ap.add_argument("--only", choices=["fwd_bwd", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise"],
                     help="run one measurement and print its record (kernel traces of that workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
@@ -497,6 +543,8 @@ def main():
 
     if not args.no_fwd_bwd:
         result["fwd_bwd"] = fwd_bwd_measure(max(3, args.steps // 2), args.warmup)
+        torch.cuda.empty_cache()
+        result["mlp_bwd"] = bwd_measure()
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

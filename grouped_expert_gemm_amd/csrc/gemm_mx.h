@@ -24,5 +24,12 @@ moe_status forward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const void* x_pe
                               const float* const* w_down_scale, const int32_t* offsets, const float* prob_perm,
                               void* y_perm, uint8_t* ws, hipStream_t s);
 
+// MXFP8 backward (bf16 inputs and outputs, every GEMM operand quantised along its K axis)
+size_t bwd_workspace_bytes(const moe_mlp_desc& d, int64_t R);
+moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf16_t* x, const bf16_t* z,
+                    const bf16_t* h, const float* prob, const void* const* w_gate_up, const void* const* w_down,
+                    const int32_t* offsets, bf16_t* dx, void* const* dw_gate_up, void* const* dw_down, float* dprob,
+                    uint8_t* ws, hipStream_t s);
+
 }  // namespace mx
 }  // namespace moe

@@ -44,7 +44,7 @@ constexpr int kMaxE = 128;   // experts per MXFP8 call (two pointer tables in th
 constexpr int kBM = 256, kBN = 256, kStepK = 64;
 constexpr int kTileBytes = 256 * kStepK;   // 16 KiB: one operand, one slot
 
-enum { MX_STORE = 0, MX_SWIGLU = 1 };
+enum { MX_STORE = 0, MX_SWIGLU = 1, MX_WGRAD = 2 };
 
 struct MxParams {
   const uint8_t* tab[kMaxE];     // per-expert P codes [N][K]
@@ -59,12 +59,22 @@ struct MxParams {
   int K, N, E, I, n_tiles;
 };
 
+// MX_WGRAD (a weight gradient per expert, K = the expert's padded token count): P =
+// tab[0] and Q = q are token-axis (column-wise) layouts [N][ld] and [R][ld] whose expert
+// e occupies columns [kofs[e], kofs[e+1]); the result goes to ctab[e] [R][N] in bf16,
+// all zeros for an expert without rows. Only this kernel takes the larger argument block.
+struct MxWgradParams : MxParams {
+  int ld;  // row stride of both token-axis code layouts (scales: ld / 32)
+  const int32_t* kofs;
+  void* ctab[kMaxE];
+};
+
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-template <int EP>
+template <int EP, typename Params>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_mx_kernel(const MxParams prm) {
+void grouped_gemm_mx_kernel(const Params prm) {
   __shared__ __attribute__((aligned(1024))) uint8_t sP0[kTileBytes], sP1[kTileBytes], sP2[kTileBytes], sP3[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sQ0[kTileBytes], sQ1[kTileBytes], sQ2[kTileBytes], sQ3[kTileBytes];
   __shared__ int32_t s_off[kMaxE + 1];
@@ -78,9 +88,16 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
   const int E = prm.E;
   const int l32 = lane & 31, lhi = lane >> 5;
 
-  for (int e = tid; e <= E; e += 256) s_off[e] = prm.offsets[e];
+  for (int e = tid; e <= E; e += 256) {
+    if constexpr (EP == MX_WGRAD) s_off[e] = prm.kofs[e];
+    else s_off[e] = prm.offsets[e];
+  }
   __syncthreads();
-  if (tid == 0) {  // nondecreasing offsets inside [0, R]; per-expert tile starts
+  if (EP == MX_WGRAD && tid == 0) {  // every expert: the whole [R, N] output; s_off holds the K offsets
+    const int per = (int)(prm.R / kBM) * prm.n_tiles;
+    for (int e = 0; e <= E; ++e) s_tstart[e] = e * per;
+  }
+  if (EP != MX_WGRAD && tid == 0) {  // nondecreasing offsets inside [0, R]; per-expert tile starts
     int prev = 0, run = 0;
     for (int e = 0; e <= E; ++e) {
       int v = s_off[e];
@@ -114,8 +131,10 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
     else return sQ3;
   };
 
-  const int nk = prm.K / kStepK;  // a multiple of 4 (K % 256 == 0)
-  const int64_t kscale = prm.K / 32;
+  int ld = prm.K;  // code row stride of P and Q (K-contiguous operands)
+  if constexpr (EP == MX_WGRAD) ld = prm.ld;
+  const int64_t kscale = ld / 32;
+  const int nk_all = prm.K / kStepK;  // a multiple of 4 (K % 256 == 0)
 
   for (int t = logical; t < total; t += nwg) {
     int lo = 0, hi = E;
@@ -124,7 +143,7 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
       if (s_tstart[mid] <= t) lo = mid; else hi = mid - 1;
     }
     int e = lo;
-    const int me = s_off[e + 1] - s_off[e];
+    const int me = (EP == MX_WGRAD) ? (int)prm.R : s_off[e + 1] - s_off[e];
     const int mte = (me + kBM - 1) / kBM;
     const int local = t - s_tstart[e];
     int mt = local % mte;
@@ -132,9 +151,12 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
     e = __builtin_amdgcn_readfirstlane(e);
     mt = __builtin_amdgcn_readfirstlane(mt);
     nt = __builtin_amdgcn_readfirstlane(nt);
-    const int row_beg = __builtin_amdgcn_readfirstlane(s_off[e]);
-    const int row_end = __builtin_amdgcn_readfirstlane(s_off[e + 1]);
+    const int row_beg = (EP == MX_WGRAD) ? 0 : __builtin_amdgcn_readfirstlane(s_off[e]);
+    const int row_end = (EP == MX_WGRAD) ? (int)prm.R : __builtin_amdgcn_readfirstlane(s_off[e + 1]);
     const int tile_row = row_beg + mt * kBM;
+    // K steps of 64 values, a multiple of 4 (K % 256 == 0; the expert's padded rows for MX_WGRAD)
+    const int nk = (EP == MX_WGRAD) ? __builtin_amdgcn_readfirstlane((s_off[e + 1] - s_off[e]) / kStepK) : nk_all;
+    const int k_beg = (EP == MX_WGRAD) ? __builtin_amdgcn_readfirstlane(s_off[e]) : 0;
 
     // P row of local tile row r (SWIGLU: gate rows then up rows of the same columns)
     auto p_row = [&](int r) -> int {
@@ -148,15 +170,15 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
 
     // ---- copies: identical lane mapping to the bf16 kernel (64-byte rows) ----
     const int dma_row0 = wave * 16 + (lane >> 2);
-    const uint8_t* pbase = prm.tab[e];
+    const uint8_t* pbase = ((EP == MX_WGRAD) ? prm.tab[0] : prm.tab[e]) + k_beg;
     uint32_t p_off[4], q_off[4];
-    const uint8_t* q_tile = prm.q + (int64_t)tile_row * prm.K;
+    const uint8_t* q_tile = prm.q + (int64_t)tile_row * ld + k_beg;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = i * 64 + dma_row0;
       const int chunk = (lane & 3) ^ swz(r);
-      p_off[i] = (uint32_t)((int64_t)p_row(r) * prm.K + chunk * 16);
-      q_off[i] = (uint32_t)((int64_t)(q_row(r) - tile_row) * prm.K + chunk * 16);
+      p_off[i] = (uint32_t)((int64_t)p_row(r) * ld + chunk * 16);
+      q_off[i] = (uint32_t)((int64_t)(q_row(r) - tile_row) * ld + chunk * 16);
     }
     auto issue_dma = [&](int kt, auto S) {
       const int64_t k0 = (int64_t)kt * kStepK;
@@ -173,8 +195,8 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
     constexpr int kDma = 8;
 
     // ---- scales: per sub-tile, this lane's row; 8 bytes per 4-step group ----
-    const uint8_t* ps_base = prm.tab_s[e];
-    const uint8_t* qs_base = prm.q_s + (int64_t)tile_row * kscale;
+    const uint8_t* ps_base = ((EP == MX_WGRAD) ? prm.tab_s[0] : prm.tab_s[e]) + k_beg / 32;
+    const uint8_t* qs_base = prm.q_s + (int64_t)tile_row * kscale + k_beg / 32;
     uint32_t ps_off[4], qs_off[4];
 #pragma unroll
     for (int t2 = 0; t2 < 4; ++t2) {
@@ -223,16 +245,16 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
     };
     i32x8_t QA[4], QB[4], P01[2], P23[2];
 
-    // prologue
-    load_scales(0);
-    issue_dma(0, S0{});
-    if (nk > 1) issue_dma(1, S1{});
-    if (nk > 2) issue_dma(2, S2{});
-    if (nk > 3) issue_dma(3, S3{});
-    wait_vm_le(((nk > 1) + (nk > 2) + (nk > 3)) * kDma);
-    take_scales();
-    lds_barrier();
-    {
+    // prologue (none for an expert without rows in MX_WGRAD: its gradient is zero)
+    if (EP != MX_WGRAD || nk > 0) {
+      load_scales(0);
+      issue_dma(0, S0{});
+      if (nk > 1) issue_dma(1, S1{});
+      if (nk > 2) issue_dma(2, S2{});
+      if (nk > 3) issue_dma(3, S3{});
+      wait_vm_le(((nk > 1) + (nk > 2) + (nk > 3)) * kDma);
+      take_scales();
+      lds_barrier();
       const uint8_t* P = sP0 + fragP;
       const uint8_t* Qb = sQ0 + fragQ;
 #pragma unroll
@@ -333,9 +355,12 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
     for (int sm = 0; sm < 4; ++sm) {
       const int64_t mg = (int64_t)tile_row + wm * 128 + sm * 32 + l32;
       const bool valid = mg < row_end;
-      if constexpr (EP == MX_STORE) {
+      if constexpr (EP == MX_STORE || EP == MX_WGRAD) {
         if (valid) {
-          bf16_t* C = reinterpret_cast<bf16_t*>(prm.c) + mg * prm.N;
+          void* cbase;
+          if constexpr (EP == MX_WGRAD) cbase = prm.ctab[e];
+          else cbase = prm.c;
+          bf16_t* C = reinterpret_cast<bf16_t*>(cbase) + mg * prm.N;
 #pragma unroll
           for (int sn = 0; sn < 4; ++sn)
 #pragma unroll
@@ -730,10 +755,18 @@ static moe_status launch(int ep, bool pt, const MxParams& p, int64_t max_tiles, 
   int64_t grid = num_cus();
   if (max_tiles < grid) grid = max_tiles;
   const dim3 g((unsigned)grid), b(256);
-  if (ep == MX_SWIGLU && !pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU>), g, b, 0, s, p);
+  if (ep == MX_SWIGLU && !pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU, MxParams>), g, b, 0, s, p);
   else if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_SWIGLU>), g, b, 0, s, p);
-  else if (!pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_STORE>), g, b, 0, s, p);
+  else if (!pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_STORE, MxParams>), g, b, 0, s, p);
   else hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_STORE>), g, b, 0, s, p);
+  return check_launch(what);
+}
+
+static moe_status launch_wgrad(const MxWgradParams& p, int64_t max_tiles, hipStream_t s, const char* what) {
+  if (max_tiles <= 0) return MOE_OK;
+  int64_t grid = num_cus();
+  if (max_tiles < grid) grid = max_tiles;
+  hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_WGRAD, MxWgradParams>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return check_launch(what);
 }
 
@@ -955,6 +988,198 @@ moe_status forward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const void* x_pe
   dn.I = I;
   dn.n_tiles = H / kBN;
   return launch(MX_STORE, true, dn, mtiles * dn.n_tiles, s, "FP8 down");
+}
+
+// ---------------------------------------------------------------------------------
+// MXFP8 backward: every GEMM takes its operands in MXFP8 along that GEMM's own K axis.
+//   dH  = dY W2_e      : dY by rows (along H), W2_e along H (column-wise, per expert)
+//   dZ  = dSwiGLU(dH, z, prob), dprob   (float32 from bf16 dH and z; dZ stored in bf16)
+//   dx  = dZ W1_e      : dZ by rows (along 2I), W1_e along 2I
+//   dW2 = dY_e^T h_e   : both along the expert's rows (token-axis layout, experts padded
+//   dW1 = dZ_e^T x_e     to whole 256-row K steps; empty experts give zero gradients)
+// ---------------------------------------------------------------------------------
+
+namespace {
+
+// dH [R, I] and z = [G, U] [R, 2I] (bf16) -> dZ = [dG, dU] (bf16), dprob[r] = sum dH * A
+// with A = silu(G) U (the probability's gradient), dA = dH p. One workgroup per row.
+__global__ __launch_bounds__(256) void mx_dswiglu_kernel(const bf16_t* __restrict__ dh, const bf16_t* __restrict__ z,
+                                                         const float* __restrict__ prob, bf16_t* __restrict__ dz,
+                                                         float* __restrict__ dprob, int I) {
+  const int64_t r = blockIdx.x;
+  const float p = prob[r];
+  const bf16_t* dhr = dh + r * I;
+  const bf16_t* zr = z + r * 2 * I;
+  bf16_t* dzr = dz + r * 2 * I;
+  float acc = 0.f;
+  for (int c = threadIdx.x * 8; c < I; c += 256 * 8) {
+    const uint4 dv = *reinterpret_cast<const uint4*>(dhr + c);
+    const uint4 gv = *reinterpret_cast<const uint4*>(zr + c);
+    const uint4 uv = *reinterpret_cast<const uint4*>(zr + I + c);
+    const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+    uint32_t og[4], ou[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float dg2[2], du2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float d = bf16_to_f32(h ? dw[j] >> 16 : dw[j] & 0xFFFFu);
+        const float G = bf16_to_f32(h ? gw[j] >> 16 : gw[j] & 0xFFFFu);
+        const float U = bf16_to_f32(h ? uw[j] >> 16 : uw[j] & 0xFFFFu);
+        const float sg = 1.f / (1.f + expf(-G));
+        acc += d * (G * sg * U);
+        const float dA = d * p;
+        dg2[h] = dA * U * sg * (1.f + G * (1.f - sg));
+        du2[h] = dA * G * sg;
+      }
+      og[j] = pack_bf16x2(dg2[0], dg2[1]);
+      ou[j] = pack_bf16x2(du2[0], du2[1]);
+    }
+    *reinterpret_cast<uint4*>(dzr + c) = make_uint4(og[0], og[1], og[2], og[3]);
+    *reinterpret_cast<uint4*>(dzr + I + c) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) dprob[r] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// token-axis layout: every expert padded to whole 256-row K steps of the GEMM
+int64_t bwd_kcap(int64_t R, int E) { return (R + (int64_t)E * 255 + 255) / 256 * 256; }
+
+struct BwdLayout {
+  size_t dyq, dys, w2c, w2s, w1c, w1s, dh, dz, dzq, dzs, dyc, dycs, hc, hcs, dzc, dzcs, xc, xcs, kofs, total;
+};
+
+BwdLayout bwd_layout(const moe_mlp_desc& d, int64_t R) {
+  const size_t H = d.H, I = d.I, E = d.E, kc = (size_t)bwd_kcap(R, d.E);
+  BwdLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += a256(bytes); return at; };
+  L.dyq = take(R * H);
+  L.dys = take(R * H / 32);
+  L.w2c = take(E * I * H);
+  L.w2s = take(E * I * H / 32);
+  L.w1c = take(E * H * 2 * I);
+  L.w1s = take(E * H * 2 * I / 32);
+  L.dh = take(R * I * 2);
+  L.dz = take(R * 2 * I * 2);
+  L.dzq = take(R * 2 * I);
+  L.dzs = take(R * 2 * I / 32);
+  L.dyc = take(H * kc);
+  L.dycs = take(H * kc / 32);
+  L.hc = take(I * kc);
+  L.hcs = take(I * kc / 32);
+  L.dzc = take(2 * I * kc);
+  L.dzcs = take(2 * I * kc / 32);
+  L.xc = take(H * kc);
+  L.xcs = take(H * kc / 32);
+  L.kofs = take((E + 1) * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(const moe_mlp_desc& d, int64_t R) { return bwd_layout(d, R).total; }
+
+moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf16_t* x, const bf16_t* z,
+                    const bf16_t* h, const float* prob, const void* const* w_gate_up, const void* const* w_down,
+                    const int32_t* offsets, bf16_t* dx, void* const* dw_gate_up, void* const* dw_down, float* dprob,
+                    uint8_t* ws, hipStream_t s) {
+  const int E = d.E, H = d.H, I = d.I;
+  moe_status st = check_mx_shape(E, H, I, "moe_grouped_mlp_bwd");
+  if (st != MOE_OK) return st;
+  const int64_t kc = bwd_kcap(R, E);
+  if ((int64_t)2 * I * kc > 0x7FFFFFFFLL || (int64_t)H * kc > 0x7FFFFFFFLL)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_mlp_bwd: MXFP8 token-axis operands exceed 2^31 bytes");
+  const BwdLayout L = bwd_layout(d, R);
+  uint8_t *dyq = ws + L.dyq, *dys = ws + L.dys, *dzq = ws + L.dzq, *dzs = ws + L.dzs;
+  bf16_t *dh = (bf16_t*)(ws + L.dh), *dz = (bf16_t*)(ws + L.dz);
+  int32_t* kofs = (int32_t*)(ws + L.kofs);
+  const size_t w2n = (size_t)I * H, w1n = (size_t)H * 2 * I;
+  const int64_t mtiles = (R + kBM - 1) / kBM + E;
+
+  // dH = dY W2_e
+  if ((st = launch_mxfp8_quantize(dy, R, H, dyq, dys, s)) != MOE_OK) return st;
+  for (int e = 0; e < E; ++e)
+    if ((st = launch_mxfp8_colwise(w_down[e], H, I, 1, nullptr, 32, H, ws + L.w2c + e * w2n,
+                                   ws + L.w2s + e * w2n / 32, nullptr, s)) != MOE_OK)
+      return st;
+  MxParams p;
+  std::memset(&p, 0, sizeof(p));
+  for (int e = 0; e < E; ++e) {
+    p.tab[e] = ws + L.w2c + e * w2n;
+    p.tab_s[e] = ws + L.w2s + e * w2n / 32;
+  }
+  p.q = dyq;
+  p.q_s = dys;
+  p.c = dh;
+  p.offsets = offsets;
+  p.R = R;
+  p.K = H;
+  p.N = I;
+  p.E = E;
+  p.I = I;
+  p.n_tiles = I / kBN;
+  if ((st = launch(MX_STORE, false, p, mtiles * p.n_tiles, s, "MXFP8 down dgrad")) != MOE_OK) return st;
+
+  // dZ, dprob
+  if (R > 0) {
+    hipLaunchKernelGGL(mx_dswiglu_kernel, dim3((unsigned)R), dim3(256), 0, s, dh, z, prob, dz, dprob, I);
+    if ((st = check_launch("MXFP8 dSwiGLU")) != MOE_OK) return st;
+  }
+
+  // dx = dZ W1_e
+  if ((st = launch_mxfp8_quantize(dz, R, 2 * I, dzq, dzs, s)) != MOE_OK) return st;
+  for (int e = 0; e < E; ++e)
+    if ((st = launch_mxfp8_colwise(w_gate_up[e], 2 * I, H, 1, nullptr, 32, 2 * I, ws + L.w1c + e * w1n,
+                                   ws + L.w1s + e * w1n / 32, nullptr, s)) != MOE_OK)
+      return st;
+  for (int e = 0; e < E; ++e) {
+    p.tab[e] = ws + L.w1c + e * w1n;
+    p.tab_s[e] = ws + L.w1s + e * w1n / 32;
+  }
+  p.q = dzq;
+  p.q_s = dzs;
+  p.c = dx;
+  p.K = 2 * I;
+  p.N = H;
+  p.n_tiles = H / kBN;
+  if ((st = launch(MX_STORE, false, p, mtiles * p.n_tiles, s, "MXFP8 gate_up dgrad")) != MOE_OK) return st;
+
+  // weight gradients on the token-axis layouts
+  if ((st = launch_mxfp8_colwise(dy, R, H, E, offsets, 256, kc, ws + L.dyc, ws + L.dycs, kofs, s)) != MOE_OK) return st;
+  if ((st = launch_mxfp8_colwise(h, R, I, E, offsets, 256, kc, ws + L.hc, ws + L.hcs, nullptr, s)) != MOE_OK) return st;
+  MxWgradParams w;
+  std::memset(&w, 0, sizeof(w));
+  w.kofs = kofs;
+  w.E = E;
+  w.ld = (int)kc;
+  w.q = ws + L.dyc;
+  w.q_s = ws + L.dycs;
+  w.tab[0] = ws + L.hc;
+  w.tab_s[0] = ws + L.hcs;
+  for (int e = 0; e < E; ++e) w.ctab[e] = dw_down[e];
+  w.R = H;
+  w.N = I;
+  w.I = I;
+  w.n_tiles = I / kBN;
+  if ((st = launch_wgrad(w, (int64_t)E * (H / kBM) * w.n_tiles, s, "MXFP8 down wgrad")) != MOE_OK) return st;
+  if ((st = launch_mxfp8_colwise(dz, R, 2 * I, E, offsets, 256, kc, ws + L.dzc, ws + L.dzcs, nullptr, s)) != MOE_OK)
+    return st;
+  if ((st = launch_mxfp8_colwise(x, R, H, E, offsets, 256, kc, ws + L.xc, ws + L.xcs, nullptr, s)) != MOE_OK) return st;
+  w.q = ws + L.dzc;
+  w.q_s = ws + L.dzcs;
+  w.tab[0] = ws + L.xc;
+  w.tab_s[0] = ws + L.xcs;
+  for (int e = 0; e < E; ++e) w.ctab[e] = dw_gate_up[e];
+  w.R = 2 * I;
+  w.N = H;
+  w.n_tiles = H / kBN;
+  return launch_wgrad(w, (int64_t)E * (2 * I / kBM) * w.n_tiles, s, "MXFP8 gate_up wgrad");
 }
 
 }  // namespace mx

@@ -24,6 +24,13 @@ size_t router_bwd_workspace_bytes(int64_t T, int H, int E);  // dW token-chunk p
 moe_status launch_mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,
                                  uint8_t* e8m0, void* stream);
 
+// column-wise (token-axis) MXFP8 of x [R, C] per expert (rule of mxfp8_quantize_colwise);
+// offsets NULL: one expert of R rows; kofs NULL: the padded offsets are not written.
+// The caller guarantees C % 64 == 0, pad % 32 == 0, kcap % 32 == 0, kcap >= the padded
+// row total, 16-byte aligned x and codes.
+moe_status launch_mxfp8_colwise(const void* x_bf16, int64_t R, int C, int E, const int32_t* offsets, int pad,
+                                int64_t kcap, uint8_t* codes, uint8_t* scales, int32_t* kofs, hipStream_t s);
+
 // per-tensor FP8 (one float32 scale per tensor). A tensor's word holds the float bits
 // of its amax between fp8t_amax and fp8t_finalize (cleared first by fp8t_zero), and
 // its scale amax / 448 (1 for amax = 0) after fp8t_finalize. n: elements per tensor,

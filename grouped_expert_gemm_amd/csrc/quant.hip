@@ -74,10 +74,10 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
   __shared__ float tile[128][65];
   const int tid = threadIdx.x;
   const int ncb = C / 64;
-  if (tid == 0) {  // offsets made nondecreasing inside [0, R]; padded offsets; work items per expert
+  if (tid == 0) {  // offsets made nondecreasing inside [0, R] (none: one expert of R rows); padded offsets
     int prev = 0, kacc = 0, iacc = 0;
     for (int e = 0; e <= E; ++e) {
-      int v = e == 0 ? 0 : offsets[e];
+      int v = e == 0 ? 0 : (offsets ? offsets[e] : (int)R);
       v = v < prev ? prev : v;
       v = v > (int)R ? (int)R : v;
       if (e > 0) {
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
     s_item[E] = iacc;
   }
   __syncthreads();
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0 && kofs_out)
     for (int e = tid; e <= E; e += 256) kofs_out[e] = s_kofs[e];
   const int total = s_item[E];
   const int r = tid >> 3, c8 = (tid & 7) * 8;  // load: rows r + 32i, columns c8 .. c8 + 7
@@ -151,6 +151,17 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
 
 using namespace moe;
 
+moe_status moe::launch_mxfp8_colwise(const void* x_bf16, int64_t R, int C, int E, const int32_t* offsets, int pad,
+                                int64_t kcap, uint8_t* codes, uint8_t* scales, int32_t* kofs, hipStream_t s) {
+  const int64_t items = (kcap / 32 + 3 * E) / 4 * (C / 64) + E * (C / 64);
+  int64_t grid = (int64_t)num_cus() * 8;
+  if (items < grid) grid = items;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(mxfp8_quantize_colwise_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const uint16_t*)x_bf16,
+                     R, C, E, offsets, pad, kcap, codes, scales, kofs);
+  return check_launch("mxfp8_quantize_colwise");
+}
+
 extern "C" moe_status mxfp8_quantize_colwise(const void* x_bf16, int64_t R, int64_t C, int E, const int32_t* offsets,
                                              int pad, int64_t kcap, uint8_t* e4m3_t, uint8_t* e8m0_t, int32_t* kofs,
                                              void* stream) {
@@ -165,13 +176,7 @@ extern "C" moe_status mxfp8_quantize_colwise(const void* x_bf16, int64_t R, int6
     return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_colwise: NULL pointer");
   if (!aligned(offsets, 4) || !aligned(kofs, 4) || (x_bf16 && !aligned(x_bf16, 16)) || (e4m3_t && !aligned(e4m3_t, 16)))
     return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_colwise: x and codes must be 16-byte and offsets 4-byte aligned");
-  const int64_t items = (kcap / 32 + 3 * E) / 4 * (C / 64) + E * (C / 64);
-  int64_t grid = (int64_t)num_cus() * 8;
-  if (items < grid) grid = items;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(mxfp8_quantize_colwise_kernel, dim3((unsigned)grid), dim3(256), 0, as_stream(stream),
-                     (const uint16_t*)x_bf16, R, (int)C, E, offsets, pad, kcap, e4m3_t, e8m0_t, kofs);
-  return check_launch("mxfp8_quantize_colwise");
+  return launch_mxfp8_colwise(x_bf16, R, (int)C, E, offsets, pad, kcap, e4m3_t, e8m0_t, kofs, as_stream(stream));
 }
 
 extern "C" moe_status mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,

@@ -29,6 +29,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .fp8_tensor import bf16_round
 from .mxfp8 import mxfp8_qdq
 
 __all__ = [
@@ -343,10 +344,14 @@ def grouped_mlp_backward_mxfp8(dy_perm, x_perm, z_save, h_save, w_gate_up, w_dow
       dW1_e  = Q_tok(dZ_e)^T Q_tok(x_e)
 
     Q_tok blocks start at each expert's first row (the padded layout of
-    mxfp8_quantize_colwise). z_save [R, 2I] and h_save [R, I] are the forward's saved
-    tensors, taken as given. quantize=False drops every Q and gives the bf16 backward's
-    formulas evaluated on the saved z and h."""
+    mxfp8_quantize_colwise). The recipe of Challenge 3 converts a low-precision GEMM's
+    result back to bf16 and keeps activations (and so their gradients) in bf16: dH and
+    dZ are rounded to bf16 (nearest, ties to even) before they are used. z_save [R, 2I]
+    and h_save [R, I] are the forward's saved tensors, taken as given. quantize=False
+    drops every Q and both roundings and gives the bf16 backward's formulas evaluated on
+    the saved z and h."""
     q = mxfp8_qdq if quantize else (lambda t: np.asarray(t, dtype=f64))
+    rnd = bf16_round if quantize else (lambda t: t)
     qt = _qdq_rows_per_expert if quantize else (lambda t, a, b: np.asarray(t, dtype=f64)[a:b])
     dy = np.asarray(dy_perm, dtype=f64)
     x = np.asarray(x_perm, dtype=f64)
@@ -372,10 +377,10 @@ def grouped_mlp_backward_mxfp8(dy_perm, x_perm, z_save, h_save, w_gate_up, w_dow
         sg = _sigmoid(G)
         A = G * sg * U
         pe = p[a:b, None]
-        dHs = dyq[a:b] @ q(W2.T).T
+        dHs = rnd(dyq[a:b] @ q(W2.T).T)
         dprob[a:b] = (dHs * A).sum(axis=1)
         dA = dHs * pe
-        dZ = np.concatenate([dA * U * sg * (1.0 + G * (1.0 - sg)), dA * G * sg], axis=1)
+        dZ = rnd(np.concatenate([dA * U * sg * (1.0 + G * (1.0 - sg)), dA * G * sg], axis=1))
         dx[a:b] = q(dZ) @ q(W1.T).T
         dw2[e] = qt(dy, a, b).T @ qt(h, a, b)
         dw1[e] = qt(dZ, 0, b - a).T @ qt(x, a, b)

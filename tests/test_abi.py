@@ -74,8 +74,13 @@ def test_mlp_descriptor_checks(L):
     assert L.moe_workspace_size(2, ctypes.byref(ok), 8192, 0, 0, 0, ctypes.byref(n)) == 0
     assert L.moe_workspace_size(1, ctypes.byref(D(8, 100, 14336, 1, 1, 1, 0)), 1, 0, 0, 0,
                                 ctypes.byref(n)) == _lib.MOE_ERR_UNSUPPORTED
-    assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, 2, 1, 1, 0)), 1, 0, 0, 0,
-                                ctypes.byref(n)) == _lib.MOE_ERR_UNSUPPORTED    # MXFP8 backward
+    assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, 2, 1, 1, 0)), 8192, 0, 0, 0,
+                                ctypes.byref(n)) == 0                           # MXFP8 backward
+    assert n.value >= 8192 * (4096 + 2 * 14336 + 14336 * 2 + 2 * 14336 * 2)     # its quantised operands
+    assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, 2, 2, 1, 0)), 1, 0, 0, 0,
+                                ctypes.byref(n)) == _lib.MOE_ERR_INVALID_ARG    # MXFP8 backward: bf16 activations
+    assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, 3, 1, 1, 0)), 1, 0, 0, 0,
+                                ctypes.byref(n)) == _lib.MOE_ERR_UNSUPPORTED    # per-tensor FP8 backward
     assert L.moe_workspace_size(1, ctypes.byref(D(0, 256, 128, 1, 1, 1, 0)), 1, 0, 0, 0,
                                 ctypes.byref(n)) == _lib.MOE_ERR_INVALID_ARG
     assert L.moe_workspace_size(1, ctypes.byref(D(8, 256, 128, 1, 0, 1, 0)), 1, 0, 0, 0,

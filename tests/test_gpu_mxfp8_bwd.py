@@ -1,0 +1,81 @@
+"""GPU parity of the MXFP8 grouped MLP backward against the oracle's MXFP8 backward
+(every GEMM operand quantised along that GEMM's reduction axis; the weight gradients
+along each expert's rows). Tolerance 6e-2, the MXFP8 forward's bound, on dx, dW1, dW2
+and dprob; experts without rows get exactly zero weight gradients.
+
+The saved forward tensors z and h are the oracle's exact forward rounded to bf16: both
+sides take the same bits. Both round dH and dZ to bf16 before quantising them; the
+library computes them in float32, the oracle in float64, so an element whose value
+sits on a bf16 or E4M3 rounding boundary can take the neighbouring code."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import max_rel_err
+from moe_inputs import WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, make_grad, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+MX_TOL = 6e-2
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_expert_gemm_amd as g
+    g.lib()
+    return g
+
+
+from gpu_util import dev_bf16, dev_f32, host, oracle_perm  # noqa: E402
+
+SHAPES = [
+    # name, T, H, I, E, k, zipf, empty experts
+    ("ragged", 700, 512, 256, 4, 2, 0.0, ()),
+    ("skewed_empty", 900, 256, 512, 8, 2, 1.2, (5,)),
+    # several 256-row K steps per expert, more weight-gradient tiles than CUs
+    ("many_tiles", 1500, 1024, 1024, 16, 2, 1.2, (4, 11)),
+]
+
+
+def _bits(a):
+    return f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_mxfp8_backward(moe, shape):
+    name, T, H, I, E, k, zipf, empty = shape
+    w = scaled(WORKLOADS["mixtral_fwd_bwd"], T=T, H=H, I=I, E=E, k=k, zipf=zipf, seed=41)
+    inp = make_inputs(w)
+    if empty:
+        inp.logits[:, list(empty)] -= 100.0
+    idx, p, m, pp = oracle_perm(inp, k, E)
+    for e in empty:
+        assert m["split_sizes"][e] == 0
+    R = T * k
+    xp_bits = inp.bits["x"][m["src_token"]]
+    xp = bf16_bits_to_f32(xp_bits)
+    _, z, h = oracle.grouped_mlp_forward(xp, inp.w1, inp.w2, m["offsets"], pp)
+    z_bits, h_bits = _bits(z), _bits(h)
+    dyf, dyb = make_grad((R, H), 77)
+    off = torch.from_numpy(m["offsets"].astype(np.int32)).cuda()
+    print(f"mxfp8 bwd {name}: R={R} H={H} I={I} E={E}", flush=True)
+    dx, dw1, dw2, dprob = moe.moe_grouped_mlp_bwd(
+        dev_bf16(dyb), dev_bf16(xp_bits), dev_bf16(z_bits), dev_bf16(h_bits), dev_f32(pp.astype(np.float32)),
+        dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"]), off, compute="mxfp8")
+    torch.cuda.synchronize()
+    ref = oracle.grouped_mlp_backward_mxfp8(dyf, xp, bf16_bits_to_f32(z_bits), bf16_bits_to_f32(h_bits), inp.w1,
+                                            inp.w2, m["offsets"], pp)
+    errs = dict(dx=max_rel_err(host(dx), ref["dx_perm"]), dw1=max_rel_err(host(dw1), ref["dw_gate_up"]),
+                dw2=max_rel_err(host(dw2), ref["dw_down"]), dprob=max_rel_err(dprob.cpu().numpy(), ref["dprob_perm"]))
+    print("  max rel err " + " ".join(f"{k2} {v:.2e}" for k2, v in errs.items()), flush=True)
+    for k2, v in errs.items():
+        assert v <= MX_TOL, k2
+    for e in empty:
+        assert not host(dw1)[e].any() and not host(dw2)[e].any(), "idle expert must get zero weight gradients"
+    # the quantisation is visible: the result is not the exact bf16-free backward
+    exact = oracle.grouped_mlp_backward_mxfp8(dyf, xp, bf16_bits_to_f32(z_bits), bf16_bits_to_f32(h_bits), inp.w1,
+                                              inp.w2, m["offsets"], pp, quantize=False)
+    assert max_rel_err(ref["dw_down"], exact["dw_down"]) > 1e-3
