@@ -351,27 +351,70 @@ void grouped_gemm_mx_kernel(const Params prm) {
     lds_barrier();
 
     // ---------------- epilogue ----------------
+    if constexpr (EP == MX_STORE || EP == MX_WGRAD) {
+      // bf16 rows through the copy slots (idle after the K loop): the tile as two blocks
+      // of 256 rows x 128 columns (block b in sP* for b = 0, sQ* for b = 1), each slot 64
+      // rows of 256 bytes with chunk c of local row r at c ^ (r & 15). Every wavefront
+      // writes its accumulators (8 bytes per lane), then drains its own 64 rows of each
+      // block, 4 whole rows per store instruction; rows past the expert are dropped by
+      // the buffer range check.
+      int ln = lane, wv = __builtin_amdgcn_readfirstlane(wave);
+      asm volatile("" : "+v"(ln));  // keep the lane offsets inside the epilogue
+      const int em = wv >> 1, en = wv & 1, e32 = ln & 31, ehi = ln >> 5;
+      const int valid = min(row_end - tile_row, kBM);
+      void* cbase;
+      if constexpr (EP == MX_WGRAD) cbase = prm.ctab[e];
+      else cbase = prm.c;
+      bf16_t* c0 = reinterpret_cast<bf16_t*>(cbase) + (int64_t)nt * kBN;
+      const int64_t ldb = (int64_t)prm.N * 2;
+      auto put_block = [&](auto B) {
+        constexpr int b = decltype(B)::value;
 #pragma unroll
-    for (int sm = 0; sm < 4; ++sm) {
-      const int64_t mg = (int64_t)tile_row + wm * 128 + sm * 32 + l32;
-      const bool valid = mg < row_end;
-      if constexpr (EP == MX_STORE || EP == MX_WGRAD) {
-        if (valid) {
-          void* cbase;
-          if constexpr (EP == MX_WGRAD) cbase = prm.ctab[e];
-          else cbase = prm.c;
-          bf16_t* C = reinterpret_cast<bf16_t*>(cbase) + mg * prm.N;
+        for (int sm = 0; sm < 4; ++sm) {
+          uint8_t* arr;
+          if constexpr (b == 0) arr = (sm < 2) ? (em ? sP2 : sP0) : (em ? sP3 : sP1);
+          else arr = (sm < 2) ? (em ? sQ2 : sQ0) : (em ? sQ3 : sQ1);
+          const int rl = (sm & 1) * 32 + e32;
 #pragma unroll
-          for (int sn = 0; sn < 4; ++sn)
+          for (int sq = 0; sq < 2; ++sq)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-              const int64_t col = (int64_t)nt * kBN + sub_n(sn, wn) + i4 * 8 + lhi * 4;
-              *reinterpret_cast<uint2*>(C + col) =
+              const int sn = 2 * b + sq;
+              const int ch = en * 8 + sq * 4 + i4;
+              *reinterpret_cast<uint2*>(arr + rl * 256 + ((ch ^ (rl & 15)) << 4) + ehi * 8) =
                   make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]),
                              pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]));
             }
         }
-      } else {
+      };
+      auto drain_block = [&](auto B) {
+        constexpr int b = decltype(B)::value;
+        const uint8_t* arr;
+        if constexpr (b == 0) arr = wv == 0 ? sP0 : wv == 1 ? sP1 : wv == 2 ? sP2 : sP3;
+        else arr = wv == 0 ? sQ0 : wv == 1 ? sQ1 : wv == 2 ? sQ2 : sQ3;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(c0 + b * 128 + (int64_t)tile_row * prm.N), (short)0, (int)(uint32_t)(valid * ldb), kBufferFlags);
+        const int pc = ln & 15;
+        const uint32_t vo = (uint32_t)((ln >> 4) * ldb + pc * 16);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int rl = 4 * i + (ln >> 4);
+          const v4u32 val = *reinterpret_cast<const v4u32*>(arr + rl * 256 + ((pc ^ (rl & 15)) << 4));
+          __builtin_amdgcn_raw_buffer_store_b128(val, rs, vo, (int)((wv * 64 + 4 * i) * ldb), 0);
+        }
+      };
+      put_block(std::integral_constant<int, 0>{});
+      put_block(std::integral_constant<int, 1>{});
+      lds_barrier();
+      drain_block(std::integral_constant<int, 0>{});
+      drain_block(std::integral_constant<int, 1>{});
+      lds_barrier();  // read out before the next tile's copies land
+    } else {
+#pragma unroll
+    for (int sm = 0; sm < 4; ++sm) {
+      const int64_t mg = (int64_t)tile_row + wm * 128 + sm * 32 + l32;
+      const bool valid = mg < row_end;
+      {
         const float p = valid ? prm.prob[mg] : 0.f;
 #pragma unroll
         for (int sn = 0; sn < 2; ++sn) {
@@ -398,6 +441,7 @@ void grouped_gemm_mx_kernel(const Params prm) {
           }
         }
       }
+    }
     }
   }
 }
