@@ -9,12 +9,14 @@ namespace mx {
 moe_status forward(const moe_mlp_desc& d, int64_t R, const void* x_perm, const uint8_t* x_perm_scale,
                    const void* const* w_gate_up, const void* const* w_down, const uint8_t* const* w_gate_up_scale,
                    const uint8_t* const* w_down_scale, const int32_t* offsets, const float* prob_perm,
-                   void* y_perm, uint8_t* workspace, hipStream_t s);
+                   void* y_perm, uint8_t* workspace, hipStream_t s, void* z_save = nullptr,
+                   void* h_save = nullptr);
 
-// MXFP8 gate_up + ScaledSwiGLU on pre-quantised operands; h written as MXFP8
+// MXFP8 gate_up + ScaledSwiGLU on pre-quantised operands; h written as MXFP8, and
+// optionally z [R, 2I] and h [R, I] in bf16 for the backward
 moe_status gate_up(int E, int64_t R, int H, int I, const uint8_t* x, const uint8_t* x_scale, const void* const* w,
                    const uint8_t* const* w_scale, const int32_t* offsets, const float* prob, uint8_t* h,
-                   uint8_t* h_scale, hipStream_t s);
+                   uint8_t* h_scale, hipStream_t s, void* z_save = nullptr, void* h_save = nullptr);
 
 // per-tensor FP8 forward (E4M3 with one float32 scale per tensor: x_perm, each expert's
 // W1 and W2, and h, which is stored in bf16 before its scale is known)

@@ -44,7 +44,7 @@ constexpr int kMaxE = 128;   // experts per MXFP8 call (two pointer tables in th
 constexpr int kBM = 256, kBN = 256, kStepK = 64;
 constexpr int kTileBytes = 256 * kStepK;   // 16 KiB: one operand, one slot
 
-enum { MX_STORE = 0, MX_SWIGLU = 1, MX_WGRAD = 2 };
+enum { MX_STORE = 0, MX_SWIGLU = 1, MX_WGRAD = 2, MX_SWIGLU_SAVE = 3 };  // SAVE: SWIGLU + bf16 z and h
 
 struct MxParams {
   const uint8_t* tab[kMaxE];     // per-expert P codes [N][K]
@@ -57,6 +57,8 @@ struct MxParams {
   const float* prob;
   int64_t R;
   int K, N, E, I, n_tiles;
+  void* z_save;                  // MXFP8 SWIGLU: NULL, or z [R][2I] in bf16 (gate, then up) and
+  void* h_save;                  //   h [R][I] in bf16 (before its quantisation), both written
 };
 
 // MX_WGRAD (a weight gradient per expert, K = the expert's padded token count): P =
@@ -160,7 +162,7 @@ void grouped_gemm_mx_kernel(const Params prm) {
 
     // P row of local tile row r (SWIGLU: gate rows then up rows of the same columns)
     auto p_row = [&](int r) -> int {
-      if constexpr (EP == MX_SWIGLU) return (r < 128) ? nt * 128 + r : prm.I + nt * 128 + (r - 128);
+      if constexpr (EP == MX_SWIGLU || EP == MX_SWIGLU_SAVE) return (r < 128) ? nt * 128 + r : prm.I + nt * 128 + (r - 128);
       else return nt * kBN + r;
     };
     auto q_row = [&](int r) -> int {
@@ -429,6 +431,25 @@ void grouped_gemm_mx_kernel(const Params prm) {
           amax = fmaxf(amax, __shfl_xor(amax, 32));
           const int sx = mx_scale_exponent(amax);
           const int64_t col0 = (int64_t)nt * 128 + wn * 64 + sn * 32;
+          if (EP == MX_SWIGLU_SAVE && valid) {  // the saved pre-activation: gate, then up at column I
+            bf16_t* Z = reinterpret_cast<bf16_t*>(prm.z_save) + mg * 2 * prm.I + col0;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              *reinterpret_cast<uint2*>(Z + i4 * 8 + lhi * 4) =
+                  make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]),
+                             pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]));
+              *reinterpret_cast<uint2*>(Z + prm.I + i4 * 8 + lhi * 4) =
+                  make_uint2(pack_bf16x2(acc[sn + 2][sm][i4 * 4 + 0], acc[sn + 2][sm][i4 * 4 + 1]),
+                             pack_bf16x2(acc[sn + 2][sm][i4 * 4 + 2], acc[sn + 2][sm][i4 * 4 + 3]));
+            }
+          }
+          if (EP == MX_SWIGLU_SAVE && valid) {
+            bf16_t* Hs = reinterpret_cast<bf16_t*>(prm.h_save) + mg * prm.I + col0;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+              *reinterpret_cast<uint2*>(Hs + i4 * 8 + lhi * 4) =
+                  make_uint2(pack_bf16x2(h[i4 * 4 + 0], h[i4 * 4 + 1]), pack_bf16x2(h[i4 * 4 + 2], h[i4 * 4 + 3]));
+          }
           if (valid) {
             uint8_t* C = reinterpret_cast<uint8_t*>(prm.c) + mg * prm.I + col0;
 #pragma unroll
@@ -799,7 +820,8 @@ static moe_status launch(int ep, bool pt, const MxParams& p, int64_t max_tiles, 
   int64_t grid = num_cus();
   if (max_tiles < grid) grid = max_tiles;
   const dim3 g((unsigned)grid), b(256);
-  if (ep == MX_SWIGLU && !pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU, MxParams>), g, b, 0, s, p);
+  if (ep == MX_SWIGLU && !pt && p.z_save) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU_SAVE, MxParams>), g, b, 0, s, p);
+  else if (ep == MX_SWIGLU && !pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU, MxParams>), g, b, 0, s, p);
   else if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_SWIGLU>), g, b, 0, s, p);
   else if (!pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_STORE, MxParams>), g, b, 0, s, p);
   else hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_STORE>), g, b, 0, s, p);
@@ -823,7 +845,7 @@ static moe_status check_mx_shape(int E, int H, int I, const char* what) {
 
 moe_status gate_up(int E, int64_t R, int H, int I, const uint8_t* x, const uint8_t* x_scale, const void* const* w,
                    const uint8_t* const* w_scale, const int32_t* offsets, const float* prob, uint8_t* h,
-                   uint8_t* h_scale, hipStream_t s) {
+                   uint8_t* h_scale, hipStream_t s, void* z_save, void* h_save) {
   moe_status st = check_mx_shape(E, H, I, "moe_grouped_gate_up_swiglu");
   if (st != MOE_OK) return st;
   MxParams p;
@@ -844,6 +866,8 @@ moe_status gate_up(int E, int64_t R, int H, int I, const uint8_t* x, const uint8
   p.E = E;
   p.I = I;
   p.n_tiles = I / 128;
+  p.z_save = z_save;
+  p.h_save = h_save;
   const int64_t mtiles = (R + kBM - 1) / kBM + E;
   return launch(MX_SWIGLU, false, p, mtiles * p.n_tiles, s, "MXFP8 gate_up + ScaledSwiGLU");
 }
@@ -876,7 +900,8 @@ static size_t a256(size_t x) { return align_up(x, 256); }
 moe_status forward(const moe_mlp_desc& d, int64_t R, const void* x_perm, const uint8_t* x_perm_scale,
                    const void* const* w_gate_up, const void* const* w_down, const uint8_t* const* w_gate_up_scale,
                    const uint8_t* const* w_down_scale, const int32_t* offsets, const float* prob_perm,
-                   void* y_perm, uint8_t* ws, hipStream_t s) {
+                   void* y_perm, uint8_t* ws, hipStream_t s, void* z_save,
+                   void* h_save) {
   const int E = d.E, H = d.H, I = d.I;
   moe_status st = check_mx_shape(E, H, I, "moe_grouped_mlp_fwd");
   if (st != MOE_OK) return st;
@@ -923,7 +948,8 @@ moe_status forward(const moe_mlp_desc& d, int64_t R, const void* x_perm, const u
   uint8_t* hq = ws;
   ws += a256((size_t)R * I);
   uint8_t* hs = ws;
-  st = gate_up(E, R, H, I, xq, xs, reinterpret_cast<const void* const*>(w1q), w1s, offsets, prob_perm, hq, hs, s);
+  st = gate_up(E, R, H, I, xq, xs, reinterpret_cast<const void* const*>(w1q), w1s, offsets, prob_perm, hq, hs, s,
+               z_save, h_save);
   if (st != MOE_OK) return st;
   return down(E, R, H, I, hq, hs, w2q, w2s, offsets, y_perm, s);
 }

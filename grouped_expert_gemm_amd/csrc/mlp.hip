@@ -202,8 +202,8 @@ extern "C" moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, c
   if (!aligned(x_perm, align) || !aligned(y_perm, align))
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_mlp_fwd: x_perm / y_perm misaligned");
   if (d.save_for_bwd) {
-    if (d.compute == MOE_MXFP8 || d.compute == MOE_FP8)
-      return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_mlp_fwd: save_for_bwd needs BF16 or F32");
+    if (d.compute == MOE_FP8)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_mlp_fwd: save_for_bwd needs BF16, F32 or MXFP8");
     if (!z_save || !h_save) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_mlp_fwd: save_for_bwd needs z_save and h_save");
     if (!aligned(z_save, align) || !aligned(h_save, align))
       return fail(MOE_ERR_INVALID_ARG, "moe_grouped_mlp_fwd: z_save / h_save misaligned");
@@ -242,7 +242,8 @@ extern "C" moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, c
   }
   if (d.compute == MOE_MXFP8) {
     return mx::forward(d, R, x_perm, x_perm_scale, w_gate_up, w_down, w_gate_up_scale, w_down_scale, offsets,
-                       prob_perm, y_perm, (uint8_t*)workspace, s);
+                       prob_perm, y_perm, (uint8_t*)workspace, s, d.save_for_bwd ? z_save : nullptr,
+                       d.save_for_bwd ? h_save : nullptr);
   }
 
   // bf16: gate_up + ScaledSwiGLU (h, optionally z), then down; workspace: [h] [tail area]

@@ -241,7 +241,9 @@ typedef struct {
  * parameters: x_perm_scale -> one float (act = FP8), w_gate_up_scale[e] / w_down_scale[e]
  * -> one float each (wt = FP8). Outputs: y_perm [R, H] (bf16, or
  * float32 when compute = F32). With save_for_bwd: z_save [R, 2I] and h_save [R, I]
- * (bf16, or float32 when compute = F32); otherwise both may be NULL.
+ * (bf16, or float32 when compute = F32; with MXFP8, z is the gate_up product of the
+ * MXFP8 operands and h its ScaledSwiGLU before quantisation, both rounded to bf16);
+ * otherwise both may be NULL. save_for_bwd is not available with compute = FP8.
  *   w_gate_up [host] E pointers to [2I, H]; w_down [host] E pointers to [H, I]
  *   w_gate_up_scale / w_down_scale [host] E pointers to [2I, H/32] / [H, I/32]
  *       E8M0 scales, only when wt = MXFP8 (else NULL)
@@ -258,7 +260,7 @@ moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, const void* 
 
 /*
  * Grouped MLP backward (the "matching fused backward" of Challenge 3), compute
- * BF16 or F32. With dY = dy_perm (gradient of y_perm), G, U = the halves of z_save,
+ * BF16, F32 or MXFP8. With dY = dy_perm (gradient of y_perm), G, U = the halves of z_save,
  * A = silu(G) * U, p = prob_perm, per expert e:
  *   dW2_e    = dY^T h_save                          -> dw_down[e]    [H, I]
  *   dH       = dY W2_e
@@ -269,6 +271,13 @@ moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, const void* 
  *   dW1_e    = [dG, dU]^T x_perm                     -> dw_gate_up[e] [2I, H]
  * Experts without rows get all-zero weight gradients. Weight gradients have the
  * weights' dtype (bf16 or float32) and are overwritten, not accumulated.
+ * compute = MXFP8 (act and wt BF16: every tensor in and out is bf16): each of the four
+ * GEMMs takes both operands as MXFP8 along its own reduction axis (Challenge 2's
+ * 32-value blocks, Challenge 3's recipe): dY and dZ = [dG, dU] by rows, W2_e along H,
+ * W1_e along 2I, and dY, h_save, dZ, x_perm along each expert's rows (blocks starting
+ * at the expert's first row, zero-padded). dH and dZ are rounded to bf16 before use, as
+ * the recipe returns a low-precision GEMM's result to bf16. Needs H % 256 == 0,
+ * I % 256 == 0, E <= 128.
  */
 moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, const void* dy_perm,
                                const void* x_perm, const void* z_save, const void* h_save,

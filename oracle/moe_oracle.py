@@ -196,11 +196,12 @@ def grouped_linear(x_perm, w, offsets):
     return y
 
 
-def grouped_mlp_forward_mxfp8(x_perm, w_gate_up, w_down, offsets, prob_perm):
+def grouped_mlp_forward_mxfp8(x_perm, w_gate_up, w_down, offsets, prob_perm, return_z=False):
     """Grouped MLP with the naive quantise -> dequantise steps of Challenge 3
     around both GEMMs: x (along H), W1 (along H), h (along I) and W2 (along I)
     each pass through MXFP8 before their GEMM; gate_up accumulators stay
-    unrounded. Returns (y_perm, h_before_quantisation) in float64."""
+    unrounded. Returns (y_perm, h_before_quantisation) in float64, and the
+    gate_up product z [R, 2I] as a third value with return_z."""
     x = mxfp8_qdq(np.asarray(x_perm, dtype=f64)) if len(x_perm) else np.zeros((0, w_gate_up.shape[2]))
     p = np.asarray(prob_perm, dtype=f64)
     off = np.asarray(offsets, dtype=np.int64)
@@ -209,6 +210,7 @@ def grouped_mlp_forward_mxfp8(x_perm, w_gate_up, w_down, offsets, prob_perm):
     R = x.shape[0]
     y = np.zeros((R, H), f64)
     h = np.zeros((R, I), f64)
+    z = np.zeros((R, 2 * I), f64)
     for e in range(E):
         a, b = int(off[e]), int(off[e + 1])
         if a == b:
@@ -216,10 +218,11 @@ def grouped_mlp_forward_mxfp8(x_perm, w_gate_up, w_down, offsets, prob_perm):
         W1 = mxfp8_qdq(np.asarray(w_gate_up[e], dtype=f64))
         W2 = mxfp8_qdq(np.asarray(w_down[e], dtype=f64))
         Z = x[a:b] @ W1.T
+        z[a:b] = Z
         Hs = silu(Z[:, :I]) * Z[:, I:] * p[a:b, None]
         h[a:b] = Hs
         y[a:b] = mxfp8_qdq(Hs) @ W2.T
-    return y, h
+    return (y, h, z) if return_z else (y, h)
 
 
 def unpermute_combine(y_perm, row_id_map, T: int, k: int, weights=None):

@@ -79,3 +79,42 @@ def test_mxfp8_backward(moe, shape):
     exact = oracle.grouped_mlp_backward_mxfp8(dyf, xp, bf16_bits_to_f32(z_bits), bf16_bits_to_f32(h_bits), inp.w1,
                                               inp.w2, m["offsets"], pp, quantize=False)
     assert max_rel_err(ref["dw_down"], exact["dw_down"]) > 1e-3
+
+
+def test_mxfp8_training_step(moe):
+    """An MXFP8 forward that saves z and h, then the MXFP8 backward on them, against the
+    oracle's MXFP8 forward (its z and h rounded to bf16) and MXFP8 backward. Saving does
+    not change y; the saved tensors match the oracle's to bf16-level error (the GEMM of
+    identical MX operands, float32 against float64 accumulation)."""
+    T, H, I, E, k = 900, 512, 256, 8, 2
+    w = scaled(WORKLOADS["mixtral_fwd_bwd"], T=T, H=H, I=I, E=E, k=k, zipf=1.2, seed=43)
+    inp = make_inputs(w)
+    inp.logits[:, [6]] -= 100.0
+    idx, p, m, pp = oracle_perm(inp, k, E)
+    assert m["split_sizes"][6] == 0
+    R = T * k
+    xp_bits = inp.bits["x"][m["src_token"]]
+    xp = bf16_bits_to_f32(xp_bits)
+    off = torch.from_numpy(m["offsets"].astype(np.int32)).cuda()
+    prob = dev_f32(pp.astype(np.float32))
+    w1, w2 = dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"])
+    print(f"mxfp8 training step: R={R} H={H} I={I} E={E}", flush=True)
+    y, z, h = moe.moe_grouped_mlp_fwd(dev_bf16(xp_bits), w1, w2, off, prob, compute="mxfp8", save_for_bwd=True)
+    y0 = moe.moe_grouped_mlp_fwd(dev_bf16(xp_bits), w1, w2, off, prob, compute="mxfp8")
+    dyf, dyb = make_grad((R, H), 78)
+    dx, dw1, dw2, dprob = moe.moe_grouped_mlp_bwd(dev_bf16(dyb), dev_bf16(xp_bits), z, h, prob, w1, w2, off,
+                                                  compute="mxfp8")
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0), "saving z and h must not change y"
+    y_ref, h_ref, z_ref = oracle.grouped_mlp_forward_mxfp8(xp, inp.w1, inp.w2, m["offsets"], pp, return_z=True)
+    ez, eh = max_rel_err(host(z), z_ref), max_rel_err(host(h), h_ref)
+    print(f"  saved z {ez:.2e}, saved h {eh:.2e}", flush=True)
+    assert ez <= 1e-2 and eh <= 1e-2
+    zb, hb = bf16_bits_to_f32(_bits(z_ref)), bf16_bits_to_f32(_bits(h_ref))
+    ref = oracle.grouped_mlp_backward_mxfp8(dyf, xp, zb, hb, inp.w1, inp.w2, m["offsets"], pp)
+    errs = dict(dx=max_rel_err(host(dx), ref["dx_perm"]), dw1=max_rel_err(host(dw1), ref["dw_gate_up"]),
+                dw2=max_rel_err(host(dw2), ref["dw_down"]), dprob=max_rel_err(dprob.cpu().numpy(), ref["dprob_perm"]))
+    print("  max rel err " + " ".join(f"{k2} {v:.2e}" for k2, v in errs.items()), flush=True)
+    for k2, v in errs.items():
+        assert v <= MX_TOL, k2
+    assert not host(dw1)[6].any() and not host(dw2)[6].any()
