@@ -44,7 +44,7 @@ def dev_bf16(torch, np, bits):
 class Layer:
     """Device buffers and the C calls of one forward (and optionally backward) step."""
 
-    def __init__(self, w, inp, backward: bool):
+    def __init__(self, w, inp, backward: bool, mx: bool = False):
         import numpy as np
         import torch
 
@@ -91,8 +91,14 @@ class Layer:
             self.dprob = torch.empty(R, dtype=torch.float32, device=dev)
             self.d1, self._k3 = _lib.ptr_table([self.dw1[e].data_ptr() for e in range(E)])
             self.d2, self._k4 = _lib.ptr_table([self.dw2[e].data_ptr() for e in range(E)])
-            self.desc = _lib.MlpDesc(E, H, I, _lib.MOE_BF16, _lib.MOE_BF16, _lib.MOE_BF16, 1)
+            comp = _lib.MOE_MXFP8 if mx else _lib.MOE_BF16
+            self.desc = _lib.MlpDesc(E, H, I, comp, _lib.MOE_BF16, _lib.MOE_BF16, 1)
             self.ws_bwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_BWD, self.desc, R), dtype=torch.uint8,
+                                      device=dev)
+        self.mx = mx
+        if mx:  # the whole grouped MLP forward in MXFP8 (one call), saving z and h when backward
+            self.desc_fwd = _lib.MlpDesc(E, H, I, _lib.MOE_MXFP8, _lib.MOE_BF16, _lib.MOE_BF16, int(backward))
+            self.ws_fwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_FWD, self.desc_fwd, R), dtype=torch.uint8,
                                       device=dev)
         self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self.ev = []
@@ -107,19 +113,25 @@ class Layer:
         c("permute", L.moe_permute(p(self.x), None, BF, T, H, E, k, p(self.idx), p(self.prob), 0, p(self.x_perm),
                                    None, p(self.prob_perm), p(self.split), p(self.offsets), p(self.rmap),
                                    p(self.src), p(self.ws_perm), self.ws_perm.numel(), s))
-        if time_gate_up:
-            e0 = self.torch.cuda.Event(enable_timing=True)
-            e1 = self.torch.cuda.Event(enable_timing=True)
-            e0.record()
-        c("gate_up", L.moe_grouped_gate_up_swiglu(E, R, H, I, BF, p(self.x_perm), None, self.t1, None,
-                                                  p(self.offsets), p(self.prob_perm), p(self.h), None,
-                                                  p(self.z) if self.z is not None else None, p(self.ws_gemm),
-                                                  self.ws_gemm.numel(), s))
-        if time_gate_up:
-            e1.record()
-            self.ev.append((e0, e1))
-        c("down", L.moe_grouped_linear(E, R, I, H, BF, p(self.h), self.t2, p(self.offsets), p(self.y),
-                                       p(self.ws_gemm), self.ws_gemm.numel(), s))
+        if self.mx:
+            c("mlp fwd", L.moe_grouped_mlp_fwd(ctypes.byref(self.desc_fwd), R, p(self.x_perm), None, self.t1, self.t2,
+                                               None, None, p(self.offsets), p(self.prob_perm), p(self.y),
+                                               p(self.z) if self.z is not None else None, p(self.h),
+                                               p(self.ws_fwd), self.ws_fwd.numel(), s))
+        else:
+            if time_gate_up:
+                e0 = self.torch.cuda.Event(enable_timing=True)
+                e1 = self.torch.cuda.Event(enable_timing=True)
+                e0.record()
+            c("gate_up", L.moe_grouped_gate_up_swiglu(E, R, H, I, BF, p(self.x_perm), None, self.t1, None,
+                                                      p(self.offsets), p(self.prob_perm), p(self.h), None,
+                                                      p(self.z) if self.z is not None else None, p(self.ws_gemm),
+                                                      self.ws_gemm.numel(), s))
+            if time_gate_up:
+                e1.record()
+                self.ev.append((e0, e1))
+            c("down", L.moe_grouped_linear(E, R, I, H, BF, p(self.h), self.t2, p(self.offsets), p(self.y),
+                                           p(self.ws_gemm), self.ws_gemm.numel(), s))
         c("combine", L.moe_unpermute_combine(p(self.y), BF, p(self.rmap), None, T, H, k, p(self.out), s))
         if self.backward:
             c("dOut gather", L.moe_permute(p(self.dout), None, BF, T, H, E, k, None, None, 1, p(self.dy), None,
@@ -362,21 +374,29 @@ def cpu_baseline(inp, w, seconds):
                       f"H={w.H}, I={w.I}); {t_all:.1f} s of oracle time, {os.cpu_count()} host CPUs visible"}
 
 
-def fwd_bwd_measure(steps, warmup):
+def fwd_bwd_measure(steps, warmup, mx=False):
+    """The whole layer forward + backward step (route ... combine, dOut gather, grouped
+    MLP backward, dx combine, dprob gather) at the Mixtral fwd+bwd shape; mx: the grouped
+    MLP forward and backward in MXFP8 (the forward saving z and h in bf16)."""
     from moe_inputs import WORKLOADS, make_inputs
 
     wb = WORKLOADS["mixtral_fwd_bwd"]
     t0 = time.perf_counter()
     inpb = make_inputs(wb, want_float=False)
     log(f"inputs {wb.name}: {time.perf_counter() - t0:.1f} s")
-    lb = Layer(wb, inpb, backward=True)
+    lb = Layer(wb, inpb, backward=True, mx=mx)
     msb = time_steps(lb, steps, warmup)
     flopb = 3.0 * wb.gemm_flop_fwd()
     vb = flopb / (msb * 1e-3) / 1e12
-    log(f"fwd+bwd step {msb:.3f} ms -> {vb:.1f} TFLOP/s")
-    return {"workload": "mixtral_fwd_bwd", "T": wb.T, "value": round(vb, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(msb, 4), "pct_of_bf16_peak": round(100 * vb / BF16_PEAK_TFLOPS, 2),
-            "flop_per_step": flopb}
+    peak = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
+    log(f"fwd+bwd step{' (MXFP8)' if mx else ''} {msb:.3f} ms -> {vb:.1f} TFLOP/s")
+    rec = {"workload": "mixtral_fwd_bwd", "T": wb.T, "value": round(vb, 2), "unit": "TFLOP/s",
+           "ms_per_step": round(msb, 4), "flop_per_step": flopb}
+    if mx:
+        rec.update(compute="mxfp8", pct_of_fp8_peak=round(100 * vb / peak, 2))
+    else:
+        rec["pct_of_bf16_peak"] = round(100 * vb / peak, 2)
+    return rec
 
 
 def bwd_measure(reps=10):
@@ -429,6 +449,8 @@ def only_measurement(which, steps, warmup):
 
     if which == "fwd_bwd":
         return fwd_bwd_measure(steps, warmup)
+    if which == "mx_fwd_bwd":
+        return fwd_bwd_measure(steps, warmup, mx=True)
     if which == "bwd":
         return bwd_measure(steps)
     if which == "qwen3":
@@ -459,7 +481,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip the MXFP8 and Qwen3 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["fwd_bwd", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise"],
+    ap.add_argument("--only", choices=["fwd_bwd", "mx_fwd_bwd", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise"],
                     help="run one measurement and print its record (kernel traces of that workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
@@ -543,6 +565,8 @@ def main():
 
     if not args.no_fwd_bwd:
         result["fwd_bwd"] = fwd_bwd_measure(max(3, args.steps // 2), args.warmup)
+        torch.cuda.empty_cache()
+        result["mxfp8_fwd_bwd"] = fwd_bwd_measure(max(3, args.steps // 2), args.warmup, mx=True)
         torch.cuda.empty_cache()
         result["mlp_bwd"] = bwd_measure()
         torch.cuda.empty_cache()
