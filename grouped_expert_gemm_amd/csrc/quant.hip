@@ -100,24 +100,41 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
   const int total = s_item[E];
   const int r = tid >> 3, c8 = (tid & 7) * 8;  // load: rows r + 32i, columns c8 .. c8 + 7
   const int cc = tid & 63, q = tid >> 6;        // encode: block q of column cc
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  // item -> expert, 128-row group j, 64-column block cb
+  auto locate = [&](int item, int& e, int& j, int& cb) {
     int lo = 0, hi = E - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_item[mid] <= item) lo = mid; else hi = mid - 1;
     }
-    const int e = lo;
+    e = lo;
     const int local = item - s_item[e];
-    const int j = local / ncb, cb = local - j * ncb;
-    const int nblk = (s_kofs[e + 1] - s_kofs[e]) / 32;        // blocks in the expert's padded range
-    const int blocks = nblk - 4 * j < 4 ? nblk - 4 * j : 4;   // blocks of this item
+    j = local / ncb;
+    cb = local - j * ncb;
+  };
+  // an item's rows in registers (rows past the expert as zeros): the next item's loads
+  // are in flight while the current one is encoded
+  uint4 v[4];
+  auto fetch = [&](int item) {
+    int e, j, cb;
+    locate(item, e, j, cb);
     const int64_t row0 = (int64_t)s_off[e] + 128 * j;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = row0 + r + 32 * i;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < s_off[e + 1]) v = *reinterpret_cast<const uint4*>(x + row * C + cb * 64 + c8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (row < s_off[e + 1]) v[i] = *reinterpret_cast<const uint4*>(x + row * C + cb * 64 + c8);
+    }
+  };
+  if ((int)blockIdx.x < total) fetch(blockIdx.x);
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    int e, j, cb;
+    locate(item, e, j, cb);
+    const int nblk = (s_kofs[e + 1] - s_kofs[e]) / 32;        // blocks in the expert's padded range
+    const int blocks = nblk - 4 * j < 4 ? nblk - 4 * j : 4;   // blocks of this item
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         tile[r + 32 * i][c8 + 2 * h] = bf16_to_f32(w[h] & 0xFFFFu);
@@ -125,6 +142,7 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
       }
     }
     __syncthreads();
+    if (item + (int)gridDim.x < total) fetch(item + gridDim.x);
     if (q < blocks) {
       float amax = 0.f;
 #pragma unroll
