@@ -141,3 +141,43 @@ def test_forward_backward_full_size(moe):
         for k, v in errs.items():
             assert v <= BF16_TOL, k
     assert np.isfinite(host(dx)).all()
+
+
+def test_mxfp8_backward_full_size(moe):
+    """The MXFP8 grouped MLP backward at the Mixtral fwd+bwd shape (R = 8192), in the
+    benchmark's launch configuration, on the real routing and permutation. The saved z
+    and h are seeded bf16 draws (the backward takes them as inputs). The largest
+    expert's gradients (dx and dprob rows, dW1, dW2) against the oracle's MXFP8 backward
+    on that expert's rows (a one-expert call gives the same expert results as the whole
+    call: the token-axis blocks restart at each expert)."""
+    from moe_inputs import make_grad
+    w = WORKLOADS["mixtral_fwd_bwd"]
+    inp = make_inputs(w, want_float=False)
+    R = w.T * w.k
+    print(f"mixtral_fwd_bwd MXFP8 backward: R={R} H={w.H} I={w.I}", flush=True)
+    idx, p = moe.moe_route_topk(dev_f32(inp.logits), w.k)
+    r = moe.moe_permute(dev_bf16(inp.bits["x"]), idx, p, w.E)
+    m, pp = _check_routing(idx, r, inp, w)
+    _, zbits = make_grad((R, 2 * w.I), 501)
+    _, hbits = make_grad((R, w.I), 502)
+    w1, w2 = dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"])
+    dyp = moe.moe_permute(dev_bf16(inp.bits["dout"]), idx, None, w.E, row_id_map=r["row_id_map"])["x_perm"]
+    dxp, dw1, dw2, dprob = moe.moe_grouped_mlp_bwd(dyp, r["x_perm"], dev_bf16(zbits), dev_bf16(hbits), r["prob_perm"],
+                                                   w1, w2, r["offsets"], compute="mxfp8")
+    torch.cuda.synchronize()
+    e = int(np.argmax(np.diff(m["offsets"])))
+    a, b, x, pe = _expert_rows(inp, m, pp, e)
+    dy = bf16_bits_to_f32(inp.bits["dout"][m["src_token"][a:b]])
+    W1 = bf16_bits_to_f32(inp.bits["w1"][e:e + 1])
+    W2 = bf16_bits_to_f32(inp.bits["w2"][e:e + 1])
+    g = oracle.grouped_mlp_backward_mxfp8(dy, x, bf16_bits_to_f32(zbits[a:b]), bf16_bits_to_f32(hbits[a:b]), W1, W2,
+                                          np.array([0, b - a]), pe)
+    errs = {
+        "dx_perm": max_rel_err(host(dxp)[a:b], g["dx_perm"]),
+        "dprob": max_rel_err(dprob.cpu().numpy()[a:b], g["dprob_perm"]),
+        "dw_gate_up": max_rel_err(host(dw1[e]), g["dw_gate_up"][0]),
+        "dw_down": max_rel_err(host(dw2[e]), g["dw_down"][0]),
+    }
+    print(f"  expert {e}: rows {b - a}, " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= MX_TOL, k
