@@ -118,3 +118,47 @@ def test_mxfp8_training_step(moe):
     for k2, v in errs.items():
         assert v <= MX_TOL, k2
     assert not host(dw1)[6].any() and not host(dw2)[6].any()
+
+
+def test_mxfp8_backward_degenerate(moe):
+    """No routed rows at all (every weight gradient exactly zero, weights prefilled with
+    NaN to show they are written), and every row on one expert of four."""
+    E, H, I = 4, 256, 256
+    rng = np.random.default_rng(5)
+    w1b = _bits(0.02 * rng.standard_normal((E, 2 * I, H)))
+    w2b = _bits(0.02 * rng.standard_normal((E, H, I)))
+    w1, w2 = dev_bf16(w1b), dev_bf16(w2b)
+    dev = torch.device("cuda")
+    empty = lambda *shape: torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    dw1 = torch.full((E, 2 * I, H), float("nan"), dtype=torch.bfloat16, device=dev)
+    dw2 = torch.full((E, H, I), float("nan"), dtype=torch.bfloat16, device=dev)
+    off = torch.zeros(E + 1, dtype=torch.int32, device=dev)
+    print("mxfp8 bwd: R = 0", flush=True)
+    dx, dw1, dw2, dprob = moe.moe_grouped_mlp_bwd(empty(0, H), empty(0, H), empty(0, 2 * I), empty(0, I),
+                                                  torch.empty(0, dtype=torch.float32, device=dev), w1, w2, off,
+                                                  compute="mxfp8", dw_gate_up=dw1, dw_down=dw2)
+    torch.cuda.synchronize()
+    assert dx.shape == (0, H) and dprob.numel() == 0
+    assert not host(dw1).any() and not host(dw2).any()
+    # all rows on expert 2
+    R = 300
+    xb = _bits(rng.standard_normal((R, H)))
+    dyb = _bits(rng.standard_normal((R, H)))
+    zb = _bits(rng.standard_normal((R, 2 * I)))
+    hb = _bits(0.3 * rng.standard_normal((R, I)))
+    pp = rng.uniform(0.2, 1.0, R).astype(np.float32)
+    offs = np.array([0, 0, 0, R, R], np.int32)
+    print("mxfp8 bwd: one busy expert", flush=True)
+    dx, dw1, dw2, dprob = moe.moe_grouped_mlp_bwd(dev_bf16(dyb), dev_bf16(xb), dev_bf16(zb), dev_bf16(hb), dev_f32(pp),
+                                                  w1, w2, torch.from_numpy(offs).cuda(), compute="mxfp8")
+    torch.cuda.synchronize()
+    ref = oracle.grouped_mlp_backward_mxfp8(bf16_bits_to_f32(dyb), bf16_bits_to_f32(xb), bf16_bits_to_f32(zb),
+                                            bf16_bits_to_f32(hb), bf16_bits_to_f32(w1b), bf16_bits_to_f32(w2b), offs,
+                                            pp)
+    for k2, got in (("dx_perm", host(dx)), ("dw_gate_up", host(dw1)), ("dw_down", host(dw2)),
+                    ("dprob_perm", dprob.cpu().numpy())):
+        err = max_rel_err(got, ref[k2])
+        print(f"  {k2} {err:.2e}", flush=True)
+        assert err <= MX_TOL, k2
+    for e in (0, 1, 3):
+        assert not host(dw1)[e].any() and not host(dw2)[e].any()
