@@ -148,8 +148,21 @@ void grouped_gemm_mx_kernel(const Params prm) {
     const int me = (EP == MX_WGRAD) ? (int)prm.R : s_off[e + 1] - s_off[e];
     const int mte = (me + kBM - 1) / kBM;
     const int local = t - s_tstart[e];
-    int mt = local % mte;
-    int nt = local / mte;
+    int mt, nt;
+    if constexpr (EP == MX_WGRAD) {
+      // groups of 8 m-tiles, n fastest over the group: the 32 consecutive tiles one XCD
+      // runs at a time form an 8 x 4 block whose operand slabs (~3.4 MB at K = 1100)
+      // stay in its L2; m fastest over all m-tiles re-read every Q slab once per n-tile
+      constexpr int GM = 8;
+      const int span = GM * prm.n_tiles;
+      const int grp = local / span, rem = local - grp * span;
+      const int gm = min(GM, mte - grp * GM);
+      mt = grp * GM + rem % gm;
+      nt = rem / gm;
+    } else {
+      mt = local % mte;
+      nt = local / mte;
+    }
     e = __builtin_amdgcn_readfirstlane(e);
     mt = __builtin_amdgcn_readfirstlane(mt);
     nt = __builtin_amdgcn_readfirstlane(nt);
