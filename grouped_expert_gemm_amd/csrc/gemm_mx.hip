@@ -366,65 +366,80 @@ void grouped_gemm_mx_kernel(const Params prm) {
     lds_barrier();
 
     // ---------------- epilogue ----------------
+    // bf16 rows through the copy slots (idle after the K loop): a tile as two blocks of
+    // 256 rows x 128 columns (block 0 in sP*, block 1 in sQ*), each slot 64 rows of 256
+    // bytes with chunk c of local row r at c ^ (r & 15). Every wavefront writes its
+    // values (8 bytes per lane), then drains its own 64 rows of a block, 4 whole rows per
+    // store instruction; rows past the expert are dropped by the buffer range check.
+    int ln = lane, wv = __builtin_amdgcn_readfirstlane(wave);
+    if constexpr (EP != MX_SWIGLU) asm volatile("" : "+v"(ln));  // keep the lane offsets inside the epilogue
+    const int em = wv >> 1, en = wv & 1, e32 = ln & 31, ehi = ln >> 5;
+    const int valid_rows = min(row_end - tile_row, kBM);
+    // sub-tile (sm, sq) of block b: 4 x 8 bytes of this lane's row
+    auto put = [&](auto B, int sm, int sq, int i4, uint2 v) {
+      constexpr int b = decltype(B)::value;
+      uint8_t* arr;
+      if constexpr (b == 0) arr = (sm < 2) ? (em ? sP2 : sP0) : (em ? sP3 : sP1);
+      else arr = (sm < 2) ? (em ? sQ2 : sQ0) : (em ? sQ3 : sQ1);
+      const int rl = (sm & 1) * 32 + e32;
+      const int ch = en * 8 + sq * 4 + i4;
+      *reinterpret_cast<uint2*>(arr + rl * 256 + ((ch ^ (rl & 15)) << 4) + ehi * 8) = v;
+    };
+    auto put_acc = [&](auto B) {
+      constexpr int b = decltype(B)::value;
+#pragma unroll
+      for (int sm = 0; sm < 4; ++sm)
+#pragma unroll
+        for (int sq = 0; sq < 2; ++sq)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int sn = 2 * b + sq;
+            put(B, sm, sq, i4,
+                make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]),
+                           pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3])));
+          }
+    };
+    // block b to rows [tile_row, tile_row + valid_rows) of dst (its 128 columns), ld elements per row
+    auto drain = [&](auto B, bf16_t* dst, int64_t ld) {
+      constexpr int b = decltype(B)::value;
+      const uint8_t* arr;
+      if constexpr (b == 0) arr = wv == 0 ? sP0 : wv == 1 ? sP1 : wv == 2 ? sP2 : sP3;
+      else arr = wv == 0 ? sQ0 : wv == 1 ? sQ1 : wv == 2 ? sQ2 : sQ3;
+      const int64_t ldb = ld * 2;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(dst + (int64_t)tile_row * ld), (short)0, (int)(uint32_t)(valid_rows * ldb), kBufferFlags);
+      const int pc = ln & 15;
+      const uint32_t vo = (uint32_t)((ln >> 4) * ldb + pc * 16);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = 4 * i + (ln >> 4);
+        const v4u32 val = *reinterpret_cast<const v4u32*>(arr + rl * 256 + ((pc ^ (rl & 15)) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(val, rs, vo, (int)((wv * 64 + 4 * i) * ldb), 0);
+      }
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
     if constexpr (EP == MX_STORE || EP == MX_WGRAD) {
-      // bf16 rows through the copy slots (idle after the K loop): the tile as two blocks
-      // of 256 rows x 128 columns (block b in sP* for b = 0, sQ* for b = 1), each slot 64
-      // rows of 256 bytes with chunk c of local row r at c ^ (r & 15). Every wavefront
-      // writes its accumulators (8 bytes per lane), then drains its own 64 rows of each
-      // block, 4 whole rows per store instruction; rows past the expert are dropped by
-      // the buffer range check.
-      int ln = lane, wv = __builtin_amdgcn_readfirstlane(wave);
-      asm volatile("" : "+v"(ln));  // keep the lane offsets inside the epilogue
-      const int em = wv >> 1, en = wv & 1, e32 = ln & 31, ehi = ln >> 5;
-      const int valid = min(row_end - tile_row, kBM);
       void* cbase;
       if constexpr (EP == MX_WGRAD) cbase = prm.ctab[e];
       else cbase = prm.c;
       bf16_t* c0 = reinterpret_cast<bf16_t*>(cbase) + (int64_t)nt * kBN;
-      const int64_t ldb = (int64_t)prm.N * 2;
-      auto put_block = [&](auto B) {
-        constexpr int b = decltype(B)::value;
-#pragma unroll
-        for (int sm = 0; sm < 4; ++sm) {
-          uint8_t* arr;
-          if constexpr (b == 0) arr = (sm < 2) ? (em ? sP2 : sP0) : (em ? sP3 : sP1);
-          else arr = (sm < 2) ? (em ? sQ2 : sQ0) : (em ? sQ3 : sQ1);
-          const int rl = (sm & 1) * 32 + e32;
-#pragma unroll
-          for (int sq = 0; sq < 2; ++sq)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              const int sn = 2 * b + sq;
-              const int ch = en * 8 + sq * 4 + i4;
-              *reinterpret_cast<uint2*>(arr + rl * 256 + ((ch ^ (rl & 15)) << 4) + ehi * 8) =
-                  make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]),
-                             pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]));
-            }
-        }
-      };
-      auto drain_block = [&](auto B) {
-        constexpr int b = decltype(B)::value;
-        const uint8_t* arr;
-        if constexpr (b == 0) arr = wv == 0 ? sP0 : wv == 1 ? sP1 : wv == 2 ? sP2 : sP3;
-        else arr = wv == 0 ? sQ0 : wv == 1 ? sQ1 : wv == 2 ? sQ2 : sQ3;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(c0 + b * 128 + (int64_t)tile_row * prm.N), (short)0, (int)(uint32_t)(valid * ldb), kBufferFlags);
-        const int pc = ln & 15;
-        const uint32_t vo = (uint32_t)((ln >> 4) * ldb + pc * 16);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int rl = 4 * i + (ln >> 4);
-          const v4u32 val = *reinterpret_cast<const v4u32*>(arr + rl * 256 + ((pc ^ (rl & 15)) << 4));
-          __builtin_amdgcn_raw_buffer_store_b128(val, rs, vo, (int)((wv * 64 + 4 * i) * ldb), 0);
-        }
-      };
-      put_block(std::integral_constant<int, 0>{});
-      put_block(std::integral_constant<int, 1>{});
+      put_acc(B0{});
+      put_acc(B1{});
       lds_barrier();
-      drain_block(std::integral_constant<int, 0>{});
-      drain_block(std::integral_constant<int, 1>{});
+      drain(B0{}, c0, prm.N);
+      drain(B1{}, c0 + 128, prm.N);
       lds_barrier();  // read out before the next tile's copies land
     } else {
+    if constexpr (EP == MX_SWIGLU_SAVE) {  // z: gate columns (block 0), up columns (block 1)
+      bf16_t* z0 = reinterpret_cast<bf16_t*>(prm.z_save) + (int64_t)nt * 128;
+      put_acc(B0{});
+      put_acc(B1{});
+      lds_barrier();
+      drain(B0{}, z0, 2 * prm.I);
+      drain(B1{}, z0 + prm.I, 2 * prm.I);
+      lds_barrier();
+    }
 #pragma unroll
     for (int sm = 0; sm < 4; ++sm) {
       const int64_t mg = (int64_t)tile_row + wm * 128 + sm * 32 + l32;
@@ -444,24 +459,11 @@ void grouped_gemm_mx_kernel(const Params prm) {
           amax = fmaxf(amax, __shfl_xor(amax, 32));
           const int sx = mx_scale_exponent(amax);
           const int64_t col0 = (int64_t)nt * 128 + wn * 64 + sn * 32;
-          if (EP == MX_SWIGLU_SAVE && valid) {  // the saved pre-activation: gate, then up at column I
-            bf16_t* Z = reinterpret_cast<bf16_t*>(prm.z_save) + mg * 2 * prm.I + col0;
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              *reinterpret_cast<uint2*>(Z + i4 * 8 + lhi * 4) =
-                  make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]),
-                             pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3]));
-              *reinterpret_cast<uint2*>(Z + prm.I + i4 * 8 + lhi * 4) =
-                  make_uint2(pack_bf16x2(acc[sn + 2][sm][i4 * 4 + 0], acc[sn + 2][sm][i4 * 4 + 1]),
-                             pack_bf16x2(acc[sn + 2][sm][i4 * 4 + 2], acc[sn + 2][sm][i4 * 4 + 3]));
-            }
-          }
-          if (EP == MX_SWIGLU_SAVE && valid) {
-            bf16_t* Hs = reinterpret_cast<bf16_t*>(prm.h_save) + mg * prm.I + col0;
+          if constexpr (EP == MX_SWIGLU_SAVE) {  // h in bf16, block-0 layout (its 128 columns)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4)
-              *reinterpret_cast<uint2*>(Hs + i4 * 8 + lhi * 4) =
-                  make_uint2(pack_bf16x2(h[i4 * 4 + 0], h[i4 * 4 + 1]), pack_bf16x2(h[i4 * 4 + 2], h[i4 * 4 + 3]));
+              put(B0{}, sm, sn, i4,
+                  make_uint2(pack_bf16x2(h[i4 * 4 + 0], h[i4 * 4 + 1]), pack_bf16x2(h[i4 * 4 + 2], h[i4 * 4 + 3])));
           }
           if (valid) {
             uint8_t* C = reinterpret_cast<uint8_t*>(prm.c) + mg * prm.I + col0;
@@ -475,6 +477,11 @@ void grouped_gemm_mx_kernel(const Params prm) {
           }
         }
       }
+    }
+    if constexpr (EP == MX_SWIGLU_SAVE) {
+      lds_barrier();
+      drain(B0{}, reinterpret_cast<bf16_t*>(prm.h_save) + (int64_t)nt * 128, prm.I);
+      lds_barrier();  // read out before the next tile's copies land
     }
     }
   }
