@@ -142,8 +142,13 @@ def test_mxfp8_mlp_equals_exact_mlp_on_representable_inputs():
     xp = oracle.gather_rows(x, m["src_token"])
     pp = p.ravel()[m["src_token"] * 2 + m["src_slot"]]
     y8, h = oracle.grouped_mlp_forward_mxfp8(xp, w1, w2, m["offsets"], pp)
-    _, _, h_exact = oracle.grouped_mlp_forward(xp, w1, w2, m["offsets"], pp)
+    _, z_exact, h_exact = oracle.grouped_mlp_forward(xp, w1, w2, m["offsets"], pp)
     np.testing.assert_allclose(h, h_exact, rtol=1e-13, atol=1e-16)
+    # the gate_up product it returns on request is the exact one too, and asking for it
+    # changes nothing else
+    y8z, hz, z8 = oracle.grouped_mlp_forward_mxfp8(xp, w1, w2, m["offsets"], pp, return_z=True)
+    np.testing.assert_allclose(z8, z_exact, rtol=1e-13, atol=1e-14)
+    assert np.array_equal(y8z, y8) and np.array_equal(hz, h)
     y_ref = np.zeros_like(y8)
     hq = oracle.mxfp8_qdq(h)
     for e in range(4):
