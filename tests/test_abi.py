@@ -126,6 +126,12 @@ def test_fp8_tensor_argument_checks(L):
                                ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
                                ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096), 1 << 40, None)
     assert st == UNS and b"save_for_bwd" in L.moe_last_error()
+    # MXFP8 saves z and h for the backward, and needs both buffers to do it
+    d = D(8, 256, 256, MX, BF16, BF16, 1)
+    st = L.moe_grouped_mlp_fwd(ctypes.byref(d), 64, ctypes.c_void_p(4096), None, pp, pp, None, None,
+                               ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
+                               None, None, ctypes.c_void_p(4096), 1 << 40, None)
+    assert st == INV and b"z_save" in L.moe_last_error()
 
 
 def test_mxfp8_colwise_argument_checks(L):
