@@ -277,7 +277,11 @@ moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, const void* 
  * W1_e along 2I, and dY, h_save, dZ, x_perm along each expert's rows (blocks starting
  * at the expert's first row, zero-padded). dH and dZ are rounded to bf16 before use, as
  * the recipe returns a low-precision GEMM's result to bf16. Needs H % 256 == 0,
- * I % 256 == 0, E <= 128.
+ * I % 256 == 0, E <= 128. Its workspace (moe_workspace_size(MOE_OP_MLP_BWD, ...))
+ * holds every quantised operand, the column-wise weight copies and dH, dZ in bf16:
+ * about R (3.1 H + 11.2 I) + 3.1 E H I bytes, plus (2H + 3I) bytes per padding row
+ * of the token-axis layouts (3.0 GB at R = 8192, H = 4096, I = 14336, E = 8). Calls
+ * sharing a workspace must not overlap.
  */
 moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, const void* dy_perm,
                                const void* x_perm, const void* z_save, const void* h_save,
