@@ -172,7 +172,7 @@ using namespace moe;
 moe_status moe::launch_mxfp8_colwise(const void* x_bf16, int64_t R, int C, int E, const int32_t* offsets, int pad,
                                 int64_t kcap, uint8_t* codes, uint8_t* scales, int32_t* kofs, hipStream_t s) {
   const int64_t items = (kcap / 32 + 3 * E) / 4 * (C / 64) + E * (C / 64);
-  int64_t grid = (int64_t)num_cus() * 16;  // ~4 resident per CU (33 KB of LDS each), the rest balance the tail
+  int64_t grid = (int64_t)num_cus() * 32;  // ~4 resident per CU (33 KB of LDS each), the rest balance the tail
   if (items < grid) grid = items;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(mxfp8_quantize_colwise_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const uint16_t*)x_bf16,
