@@ -22,7 +22,7 @@ import numpy as np
 
 from .mxfp8 import E4M3_MAX, e4m3_decode, e4m3_encode
 
-__all__ = ["fp8_tensor_scale", "fp8_tensor_quantize", "fp8_tensor_qdq", "bf16_round", "grouped_mlp_forward_fp8_tensor"]
+__all__ = ["fp8_tensor_scale", "fp8_tensor_quantize", "fp8_tensor_qdq", "bf16_round", "BF16_MAX", "grouped_mlp_forward_fp8_tensor"]
 
 
 def fp8_tensor_scale(x) -> np.float32:
@@ -46,12 +46,30 @@ def fp8_tensor_qdq(x, scale=None) -> np.ndarray:
     return e4m3_decode(codes) * np.float64(s)
 
 
+BF16_MAX = float.fromhex("0x1.fep127")   # largest finite bfloat16: (2 - 2^-7) * 2^127
+
+
 def bf16_round(a):
-    """float64 -> nearest bf16 value (ties to even), as float64."""
-    f = np.asarray(a, np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+    """float64 -> the nearest bfloat16 value, ties to the even significand, as float64.
+
+    bfloat16 keeps 8 significant bits and float32's exponent range: values in
+    [2^e, 2^(e+1)) with e >= -126 are spaced 2^(e-7), values below 2^-126 are
+    multiples of 2^-133 (subnormals). The value is divided by its spacing (exact: a
+    power of two), rounded half to even by np.rint, and scaled back (exact). Results
+    beyond the largest finite value become +-inf (IEEE rounding of an overflow);
+    zeros, infinities and NaN pass through. There is no float32 step in between, so
+    no double rounding."""
+    a = np.asarray(a, np.float64)
+    out = np.array(a, dtype=np.float64, copy=True)
+    fin = np.isfinite(a) & (a != 0)
+    v = a[fin]
+    _, ex = np.frexp(np.abs(v))              # |v| = m * 2^ex, m in [0.5, 1)
+    e = np.maximum(ex - 1, -126)             # exponent of the binade, subnormals at -126
+    step = np.ldexp(1.0, e - 7)
+    r = np.rint(v / step) * step
+    r = np.where(np.abs(r) > BF16_MAX, np.copysign(np.inf, r), r)
+    out[fin] = r
+    return out
 
 
 def grouped_mlp_forward_fp8_tensor(x_perm, w_gate_up, w_down, offsets, prob_perm, x_scale=None):

@@ -1,12 +1,12 @@
 """Plain CPU reference for the MoE expert feed-forward layer (test infrastructure only).
 
 Source: "Efficient MoE Training for Biological Foundation Models"
-  * Challenge 1 (Fragmented expert kernels): the Hugging Face baseline walks the
-    experts in a Python loop; for each expert it finds the (token, slot) pairs
-    routed to it, gathers those hidden_states rows, runs the expert, multiplies
-    by routing_weights[token, slot] and index-adds the result into
-    final_hidden_states. GroupedLinear takes per-expert token counts
-    (split_sizes) and the experts' gate_up weights are [2*intermediate, hidden].
+  * Challenge 1 (Fragmented expert kernels): the naive baseline visits the experts
+    one after another; each expert takes the (token, slot) pairs the router sent to
+    it, runs its MLP on those tokens, scales each result by the pair's routing
+    weight and adds it into the token's output. GroupedLinear instead takes
+    per-expert token counts (split_sizes), and each expert's gate_up weight is
+    [2 * intermediate, hidden].
   * Challenge 3: ScaledSwiGLU multiplies the routing probability into the
     SwiGLU output, and the grouped MLP is GroupedLinear(gate_up) ->
     ScaledSwiGLU -> GroupedLinear(down), with a matching backward.
@@ -84,28 +84,28 @@ def route_topk(logits, k: int, renormalize: bool = True):
 def permute(topk_idx, E: int):
     """Group the T*k (token, slot) pairs by expert.
 
-    Expert by expert, as the baseline loop does, the pairs routed to expert e
-    are listed in ascending token order; concatenating the lists gives the
-    permuted rows. Returns dict with
-      split_sizes [E], offsets [E+1], row_id_map [T*k] ((t, j) -> row),
-      src_token [T*k] (row -> t), src_slot [T*k] (row -> j).
+    Expert e's pairs are listed in ascending token order (the order a row-major scan
+    of the [T, k] choice table meets them); the lists of experts 0..E-1 are laid end
+    to end. Returns dict with
+      split_sizes [E], offsets [E+1], row_id_map [T*k] ((t, j) -> row; -1 for a pair
+      that names no expert in [0, E)), src_token [T*k] (row -> t), src_slot [T*k]
+      (row -> j); only the first offsets[E] entries of the last two are filled.
     """
-    idx = np.asarray(topk_idx)
-    T, k = idx.shape
+    choice = np.asarray(topk_idx)
+    T, k = choice.shape
     split_sizes = np.zeros(E, np.int64)
     row_id_map = np.full(T * k, -1, np.int64)
     src_token = np.empty(T * k, np.int64)
     src_slot = np.empty(T * k, np.int64)
-    row = 0
+    next_row = 0
     for e in range(E):
-        top_x, slot = np.nonzero(idx == e)          # row-major: ascending token
-        n = top_x.size
-        split_sizes[e] = n
-        rows = np.arange(row, row + n)
-        row_id_map[top_x * k + slot] = rows
-        src_token[rows] = top_x
+        tok, slot = np.nonzero(choice == e)          # row-major: ascending token
+        rows = next_row + np.arange(tok.size)
+        split_sizes[e] = tok.size
+        row_id_map[tok * k + slot] = rows
+        src_token[rows] = tok
         src_slot[rows] = slot
-        row += n
+        next_row += tok.size
     offsets = np.concatenate([[0], np.cumsum(split_sizes)])
     return dict(split_sizes=split_sizes, offsets=offsets, row_id_map=row_id_map,
                 src_token=src_token, src_slot=src_slot)
@@ -132,23 +132,23 @@ def expert_ffn(X, w_gate_up, w_down):
     return A @ W2.T, Z, A
 
 
-def moe_ffn_forward(hidden_states, w_gate_up, w_down, topk_idx, routing_weights):
-    """final_hidden_states [T, H] by the per-expert loop (float64).
+def moe_ffn_forward(x, w_gate_up, w_down, topk_idx, topk_prob):
+    """Layer output [T, H] by the naive per-expert loop (float64).
 
-    w_gate_up [E, 2I, H], w_down [E, H, I]."""
-    x = np.asarray(hidden_states, dtype=f64)
-    idx = np.asarray(topk_idx)
-    p = np.asarray(routing_weights, dtype=f64)
+    For each expert in turn: the tokens that chose it, their expert MLP output, each
+    weighted by the probability of the slot that chose the expert, accumulated into
+    those tokens' outputs. w_gate_up [E, 2I, H], w_down [E, H, I]."""
+    x = np.asarray(x, dtype=f64)
+    choice = np.asarray(topk_idx)
+    prob = np.asarray(topk_prob, dtype=f64)
     T, H = x.shape
-    E = w_gate_up.shape[0]
-    final_hidden_states = np.zeros((T, H), f64)
-    for e in range(E):
-        top_x, slot = np.nonzero(idx == e)
-        if top_x.size == 0:
-            continue
-        Y, _, _ = expert_ffn(x[top_x], w_gate_up[e], w_down[e])
-        np.add.at(final_hidden_states, top_x, Y * p[top_x, slot][:, None])
-    return final_hidden_states
+    out = np.zeros((T, H), f64)
+    for e in range(w_gate_up.shape[0]):
+        tok, slot = np.nonzero(choice == e)
+        if tok.size:
+            y_e, _, _ = expert_ffn(x[tok], w_gate_up[e], w_down[e])
+            np.add.at(out, tok, prob[tok, slot][:, None] * y_e)
+    return out
 
 
 def grouped_mlp_forward(x_perm, w_gate_up, w_down, offsets, prob_perm):
@@ -285,42 +285,38 @@ def grouped_mlp_backward(dy_perm, x_perm, w_gate_up, w_down, offsets, prob_perm)
     return dict(dx_perm=dx, dw_gate_up=dw1, dw_down=dw2, dprob_perm=dprob)
 
 
-def moe_ffn_backward(hidden_states, w_gate_up, w_down, topk_idx, routing_weights, d_out):
-    """Gradients of moe_ffn_forward's output against d_out, walking the same
-    per-expert loop backwards. Returns dict dx [T, H], dw_gate_up, dw_down,
-    drouting_weights [T, k] (gradient w.r.t. the routing weights themselves)."""
-    x = np.asarray(hidden_states, dtype=f64)
-    idx = np.asarray(topk_idx)
-    p = np.asarray(routing_weights, dtype=f64)
+def moe_ffn_backward(x, w_gate_up, w_down, topk_idx, topk_prob, d_out):
+    """Gradients of moe_ffn_forward's output against d_out, by the same per-expert loop
+    run backwards. Returns dict dx [T, H], dw_gate_up, dw_down, drouting_weights [T, k]
+    (gradient w.r.t. the routing probabilities themselves)."""
+    x = np.asarray(x, dtype=f64)
+    choice = np.asarray(topk_idx)
+    prob = np.asarray(topk_prob, dtype=f64)
     g = np.asarray(d_out, dtype=f64)
-    T, H = x.shape
-    E, twoI, _ = w_gate_up.shape
+    E, twoI, H = w_gate_up.shape
     I = twoI // 2
-    dx = np.zeros((T, H), f64)
+    dx = np.zeros_like(x)
     dw1 = np.zeros((E, twoI, H), f64)
     dw2 = np.zeros((E, H, I), f64)
-    dp = np.zeros_like(p)
+    dprob = np.zeros_like(prob)
     for e in range(E):
-        top_x, slot = np.nonzero(idx == e)
-        if top_x.size == 0:
+        tok, slot = np.nonzero(choice == e)
+        if tok.size == 0:
             continue
         W1 = np.asarray(w_gate_up[e], dtype=f64)
         W2 = np.asarray(w_down[e], dtype=f64)
-        Y, Z, A = expert_ffn(x[top_x], W1, W2)
-        pw = p[top_x, slot][:, None]
-        gY = g[top_x]                                # index_add_ scatters, so its grad gathers
-        dp[top_x, slot] = (gY * Y).sum(axis=1)
-        dY = gY * pw
+        y_e, Z, A = expert_ffn(x[tok], W1, W2)
+        g_e = g[tok]                                 # the forward accumulated into these tokens
+        dprob[tok, slot] = (g_e * y_e).sum(axis=1)
+        dY = g_e * prob[tok, slot][:, None]
         dw2[e] = dY.T @ A
         dA = dY @ W2
         G, U = Z[:, :I], Z[:, I:]
         sg = _sigmoid(G)
-        dG = dA * U * sg * (1.0 + G * (1.0 - sg))
-        dU = dA * G * sg
-        dZ = np.concatenate([dG, dU], axis=1)
-        np.add.at(dx, top_x, dZ @ W1)
-        dw1[e] = dZ.T @ x[top_x]
-    return dict(dx=dx, dw_gate_up=dw1, dw_down=dw2, drouting_weights=dp)
+        dZ = np.concatenate([dA * U * sg * (1.0 + G * (1.0 - sg)), dA * G * sg], axis=1)
+        np.add.at(dx, tok, dZ @ W1)
+        dw1[e] = dZ.T @ x[tok]
+    return dict(dx=dx, dw_gate_up=dw1, dw_down=dw2, drouting_weights=dprob)
 
 
 def _qdq_rows_per_expert(x, a, b):
@@ -335,7 +331,7 @@ def _qdq_rows_per_expert(x, a, b):
 
 
 def grouped_mlp_backward_mxfp8(dy_perm, x_perm, z_save, h_save, w_gate_up, w_down, offsets, prob_perm,
-                               quantize=True):
+                               quantize=True, round_bf16=True):
     """The grouped MLP backward with every GEMM operand passed through MXFP8 along that
     GEMM's own reduction (K) axis (Challenge 2's 32-value blocks; Challenge 3 puts the
     backward GEMMs in MXFP8 as it does the forward ones):
@@ -352,9 +348,10 @@ def grouped_mlp_backward_mxfp8(dy_perm, x_perm, z_save, h_save, w_gate_up, w_dow
     dZ are rounded to bf16 (nearest, ties to even) before they are used. z_save [R, 2I]
     and h_save [R, I] are the forward's saved tensors, taken as given. quantize=False
     drops every Q and both roundings and gives the bf16 backward's formulas evaluated on
-    the saved z and h."""
+    the saved z and h; round_bf16=False keeps every Q but drops the two bf16 roundings
+    (dH and dZ enter dprob, dSwiGLU and their quantisers unrounded)."""
     q = mxfp8_qdq if quantize else (lambda t: np.asarray(t, dtype=f64))
-    rnd = bf16_round if quantize else (lambda t: t)
+    rnd = bf16_round if (quantize and round_bf16) else (lambda t: t)
     qt = _qdq_rows_per_expert if quantize else (lambda t, a, b: np.asarray(t, dtype=f64)[a:b])
     dy = np.asarray(dy_perm, dtype=f64)
     x = np.asarray(x_perm, dtype=f64)
