@@ -165,6 +165,32 @@ def time_steps(layer, steps, warmup):
 
 
 FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
+FLUSH_BYTES = 512 << 20     # twice the 256 MB Infinity Cache
+
+
+_flush_buf = None
+
+
+def timed_flushed(f, reps):
+    """Average time of f() (ms) over `reps` calls, each timed alone with events on the
+    current stream right after a 512 MB device write, which evicts the Infinity Cache
+    and L2: a memory-bound call then reads its inputs from HBM, not from a cache that
+    the previous call warmed."""
+    import torch
+    global _flush_buf
+    if _flush_buf is None:
+        _flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    f()
+    total = 0.0
+    for i in range(reps):
+        _flush_buf.fill_(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        f()
+        b.record()
+        b.synchronize()
+        total += a.elapsed_time(b)
+    return total / reps
 
 
 def extra_forward(w, inp, steps, warmup, compute="bf16", prequant=False):
@@ -230,7 +256,8 @@ def extra_forward(w, inp, steps, warmup, compute="bf16", prequant=False):
 def router_measure(w, inp, reps=20):
     """The router gate linear (bf16 MFMA; HBM-bound at small E), the top-k gating
     backward and the gate linear's backward (float32 VALU) at a workload's shape, each
-    timed with events over `reps` calls; returns one record per op with its roofline."""
+    timed with events around single calls after a cache flush (timed_flushed); returns
+    one record per op with its roofline."""
     import numpy as np
     import torch
 
@@ -247,15 +274,7 @@ def router_measure(w, inp, reps=20):
     dx = torch.empty_like(x)
 
     def timed(f):
-        f()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            f()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        return timed_flushed(f, reps)
 
     out = {"workload": w.name, "T": T, "H": H, "E": E, "k": k}
     ms = timed(lambda: moe.moe_router_logits(x, wr))
@@ -286,7 +305,7 @@ def router_measure(w, inp, reps=20):
 def colwise_measure(reps=20):
     """Column-wise MXFP8 quantisation (per expert, along the token axis; the operand
     layout of MXFP8 weight gradients) of the Mixtral backward's dY [R, H] and h [R, I]
-    (T=4096, top-2), pad 256, timed with events over `reps` calls: HBM-bound."""
+    (T=4096, top-2), pad 256, each call timed after a cache flush: HBM-bound."""
     import torch
 
     import grouped_expert_gemm_amd as moe
@@ -308,14 +327,8 @@ def colwise_measure(reps=20):
         vp = ctypes.c_void_p
         args = (vp(x.data_ptr()), R, C, w.E, vp(off.data_ptr()), 256, kcap, vp(codes.data_ptr()),
                 vp(scales.data_ptr()), vp(kofs.data_ptr()), vp(torch.cuda.current_stream().cuda_stream))
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):   # the C entry point on the same buffers: no allocation or fill in the loop
-            L.mxfp8_quantize_colwise(*args)
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / reps
+        # the C entry point on the same buffers (no allocation), each call after a cache flush
+        ms = timed_flushed(lambda: L.mxfp8_quantize_colwise(*args), reps)
         ktot = int(kofs[-1].item())
         nbytes = R * C * 2 + C * ktot + C * ktot // 32
         recs.append({"tensor": name, "rows": R, "cols": C, "padded_rows": ktot, "ms": round(ms, 4), "bound": "hbm",
@@ -323,6 +336,61 @@ def colwise_measure(reps=20):
                      "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 4)})
         log(f"mxfp8 colwise {name} [{R}, {C}]: {ms:.3f} ms -> {nbytes / ms / 1e6:.0f} GB/s")
     return recs
+
+
+def memory_bound_measure(w, inp, reps=20):
+    """The permutation (count, scan and gather of x into expert order, with the maps)
+    and the combine at a forward workload's shape, each call timed alone after a cache
+    flush. Algorithmic bytes: permute T*H*2 (x) + R*H*2 (x_perm) + T*k*8 (ids and
+    probabilities) + R*16 (four maps and prob_perm); combine R*H*2 + T*H*2 + T*k*4."""
+    import numpy as np
+    import torch
+
+    import grouped_expert_gemm_amd as moe
+    from grouped_expert_gemm_amd import _lib
+
+    T, H, E, k = w.T, w.H, w.E, w.k
+    R = T * k
+    x = dev_bf16(torch, np, inp.bits["x"])
+    idx, prob = moe.moe_route_topk(torch.from_numpy(inp.logits).cuda(), k)
+    r = moe.moe_permute(x, idx, prob, E)
+    y = torch.randn((R, H), device="cuda").to(torch.bfloat16)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(1, moe.workspace_size(_lib.MOE_OP_PERMUTE, None, 0, T, E, k)), dtype=torch.uint8,
+                     device="cuda")
+    L = moe.lib()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def permute():
+        _lib.check("permute", L.moe_permute(vp(x), None, _lib.MOE_BF16, T, H, E, k, vp(idx), vp(prob), 0,
+                                            vp(r["x_perm"]), None, vp(r["prob_perm"]), vp(r["split_sizes"]),
+                                            vp(r["offsets"]), vp(r["row_id_map"]), vp(r["src_token"]), vp(ws),
+                                            ws.numel(), s))
+
+    def combine():
+        _lib.check("combine", L.moe_unpermute_combine(vp(y), _lib.MOE_BF16, vp(r["row_id_map"]), None, T, H, k,
+                                                      vp(out), s))
+
+    recs = {"workload": w.name, "T": T, "H": H, "E": E, "k": k, "cache": "flushed (512 MB write) before each call"}
+    for name, f, nbytes in (("permute", permute, T * H * 2 + R * H * 2 + T * k * 8 + R * 16),
+                            ("combine", combine, R * H * 2 + T * H * 2 + T * k * 4)):
+        ms = timed_flushed(f, reps)
+        recs[name] = {"ms": round(ms, 4), "bound": "hbm", "achieved_GBps": round(nbytes / ms / 1e6, 1),
+                      "peak_GBps": HBM_PEAK_GBPS, "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                      "bytes": nbytes}
+        log(f"{name} {w.name}: {ms:.4f} ms -> {nbytes / ms / 1e6:.0f} GB/s")
+    return recs
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def traffic_record():
@@ -369,6 +437,7 @@ def cpu_baseline(inp, w, seconds):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     flop = 6.0 * rows * w.H * w.I
     return {"value": round(flop / t_all / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"float64 numpy oracle, grouped MLP forward (gate_up, ScaledSwiGLU, down) of experts "
                       f"0..{experts - 1} of the {w.name} workload on all their rows ({rows} of {w.R} rows, "
                       f"H={w.H}, I={w.I}); {t_all:.1f} s of oracle time, {os.cpu_count()} host CPUs visible"}
@@ -464,6 +533,9 @@ def only_measurement(which, steps, warmup):
                 extra_forward(w8, inp, steps, warmup, compute="mxfp8", prequant=True)]
     if which == "colwise":
         return colwise_measure(steps)
+    if which == "permute":
+        wq = WORKLOADS["qwen3_fwd"]
+        return [memory_bound_measure(w, inp, steps), memory_bound_measure(wq, make_inputs(wq, want_float=False), steps)]
     if which == "fp8":
         w8 = WORKLOADS["mixtral_mxfp8_fwd"]
         return [extra_forward(w8, inp, steps, warmup, compute="fp8"),
@@ -481,7 +553,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip the MXFP8 and Qwen3 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["fwd_bwd", "mx_fwd_bwd", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise"],
+    ap.add_argument("--only", choices=["fwd_bwd", "mx_fwd_bwd", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise", "permute"],
                     help="run one measurement and print its record (kernel traces of that workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
@@ -559,6 +631,7 @@ def main():
         log(f"inputs {wq.name}: {time.perf_counter() - t0:.1f} s")
         result["qwen3_fwd"] = extra_forward(wq, inpq, max(3, args.steps // 2), args.warmup)
         result["router"] = [router_measure(w, inp), router_measure(wq, inpq)]
+        result["permute_combine"] = [memory_bound_measure(w, inp), memory_bound_measure(wq, inpq)]
         result["mxfp8_colwise"] = colwise_measure()
         del inpq
         torch.cuda.empty_cache()

@@ -30,6 +30,17 @@ size_t permute_workspace_bytes(int64_t T, int E, int k) {
   return b;
 }
 
+// expert of slot j of a token whose k ids are in e[0..k): -1 when the id is out of
+// [0, E) or repeats the id of an earlier slot (such a pair is dropped)
+__device__ __forceinline__ int slot_expert(const int* e, int j, int E) {
+  const int x = e[j];
+  bool ok = (unsigned)x < (unsigned)E;
+#pragma unroll
+  for (int i = 0; i < kMaxK; ++i)
+    if (i < j && e[i] == x) ok = false;
+  return ok ? x : -1;
+}
+
 __global__ __launch_bounds__(kPermBlock) void permute_count_kernel(const int32_t* __restrict__ idx,
                                                                    int64_t T, int E, int k,
                                                                    int32_t* __restrict__ counts,
@@ -41,19 +52,27 @@ __global__ __launch_bounds__(kPermBlock) void permute_count_kernel(const int32_t
   const int64_t t = (int64_t)blockIdx.x * kPermBlock + tid;
   const int w = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
+  int ids[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) ids[j] = (t < T && j < k) ? idx[t * k + j] : -1;
   if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      int e = idx[t * k + j];
-      if ((unsigned)e < (unsigned)E) atomicOr(&flags[e * (kPermBlock / 32) + w], bit);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) break;
+      const int e = slot_expert(ids, j, E);
+      if (e >= 0) atomicOr(&flags[e * (kPermBlock / 32) + w], bit);
     }
   }
   __syncthreads();
   if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      int e = idx[t * k + j];
-      int r = 0;
-      if ((unsigned)e < (unsigned)E) {
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) break;
+      const int e = slot_expert(ids, j, E);
+      int r = -1;
+      if (e >= 0) {
         const uint32_t* f = &flags[e * (kPermBlock / 32)];
+        r = 0;
         for (int ww = 0; ww < w; ++ww) r += __popc(f[ww]);
         r += __popc(f[w] & (bit - 1u));
       }
@@ -182,8 +201,9 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
       if (reuse) {
         r = row_id_map[t * k + j];
       } else {
-        int e = idx[t * k + j];
-        r = ((unsigned)e < (unsigned)E) ? base[(t / kPermBlock) * E + e] + rank_local[t * k + j] : -1;
+        const int e = idx[t * k + j];
+        const int rl = rank_local[t * k + j];  // -1: a dropped pair
+        r = ((unsigned)e < (unsigned)E && rl >= 0) ? base[(t / kPermBlock) * E + e] + rl : -1;
       }
       rows[j] = (r >= 0 && r < R) ? r : -1;
       if (!reuse && lane == j) {

@@ -137,6 +137,12 @@ moe_status moe_router_bwd(const void* x, const void* w_router, const float* d_lo
  * reuse_map != 0: the maps are INPUTS from an earlier call with the same routing;
  * only x is gathered into x_perm (used to gather the output gradient).
  * workspace: moe_workspace_size(MOE_OP_PERMUTE, ...) bytes, 256-byte aligned.
+ * Input contract: each token's k expert ids are distinct and in [0, E), as
+ * moe_route_topk produces them. A (token, slot) pair whose id is out of range, or
+ * repeats the id of an earlier slot of the same token, is dropped: its row_id_map
+ * entry is -1, split_sizes does not count it, and only the first offsets[E] rows of
+ * x_perm, prob_perm and src_token are written (T*k - offsets[E] pairs were dropped).
+ * moe_unpermute_combine skips -1 entries, so a dropped pair contributes nothing.
  */
 moe_status moe_permute(const void* x, const uint8_t* x_scale, moe_dtype dt, int64_t T, int H,
                        int E, int k, const int32_t* topk_idx, const float* topk_prob,

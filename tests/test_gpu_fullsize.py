@@ -1,11 +1,15 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark
-times: the whole layer runs on the GPU; the oracle computes every output of a sample
-of experts (all their rows), which it can finish in seconds on the host.
+times. Each workload's layer runs once on the GPU and its results are kept on the host;
+then the oracle checks EVERY expert, one expert (or, for the 128-expert workload, one
+group of experts) per test, and a last test per workload checks every token after the
+GPU's combine.
 
   * routing indices and the permutation: bit-exact for all tokens;
-  * bf16 outputs: max|a-b| / max|b| <= 2e-2 over each sampled expert's rows;
+  * bf16 outputs: max|a-b| / max|b| <= 2e-2 per expert and over all tokens;
   * MXFP8 outputs: <= 6e-2 against the oracle's quantise/dequantise reference;
-  * backward: dx, dprob rows and both weight gradients of the sampled experts.
+  * backward: y, dx and dprob rows and both weight gradients of every expert; dx and the
+    GPU's dprob gather ([T, k], the gradient w.r.t. the routing probabilities) over all
+    tokens.
 """
 import numpy as np
 import pytest
@@ -13,6 +17,7 @@ import torch
 
 import oracle
 from conftest import max_rel_err
+from gpu_util import bf16_bits, dev_bf16, dev_f32
 from moe_inputs import WORKLOADS, bf16_bits_to_f32, make_inputs
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -30,154 +35,286 @@ def moe():
     return g
 
 
-from gpu_util import dev_bf16, dev_f32, host  # noqa: E402
+_INPUTS = {}   # the last workload's inputs (one slot: the Mixtral weights are 2.8 GB of bits)
+_RUNS = {}     # GPU results on the host, per workload run
 
 
-def _layer_forward(moe, inp, w, compute="bf16", save=False):
+def _inputs(name):
+    w = WORKLOADS[name]
+    key = (w.seed, w.T, w.H, w.I, w.E, w.k, w.zipf, w.backward)
+    if key not in _INPUTS:
+        _INPUTS.clear()
+        _INPUTS[key] = make_inputs(w, want_float=False)
+    return _INPUTS[key]
+
+
+def _h32(t):
+    """Device tensor -> float32 numpy (bf16 through its bits, exactly)."""
+    if t.dtype == torch.bfloat16:
+        return bf16_bits_to_f32(bf16_bits(t))
+    return t.detach().cpu().numpy().astype(np.float32)
+
+
+def _done_with_gpu():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _route_and_permute(moe, inp, w):
     idx, p = moe.moe_route_topk(dev_f32(inp.logits), w.k)
     r = moe.moe_permute(dev_bf16(inp.bits["x"]), idx, p, w.E)
-    w1, w2 = dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"])
-    res = moe.moe_grouped_mlp_fwd(r["x_perm"], w1, w2, r["offsets"], r["prob_perm"], compute=compute,
-                                  save_for_bwd=save)
-    y = res[0] if save else res
-    out = moe.moe_unpermute_combine(y, r["row_id_map"], w.T, w.k)
     torch.cuda.synchronize()
-    return idx, p, r, w1, w2, res, out
-
-
-def _check_routing(idx, r, inp, w):
+    # routing indices and the whole permutation are graded bit-exact
     ridx, rp = oracle.route_topk(inp.logits, w.k)
     assert np.array_equal(idx.cpu().numpy(), ridx)
     m = oracle.permute(ridx, w.E)
     for key in ("split_sizes", "offsets", "row_id_map", "src_token"):
         assert np.array_equal(r[key].cpu().numpy(), m[key]), key
     pp = rp.ravel()[m["src_token"] * w.k + m["src_slot"]]
-    return m, pp
+    return idx, r, m, pp
 
 
-def _expert_rows(inp, m, pp, e, bits="x"):
+def _expert(run, e):
+    """Rows [a, b) of expert e, its x rows (float32), routing weights and weights."""
+    inp, m, pp = run["inp"], run["m"], run["pp"]
     a, b = int(m["offsets"][e]), int(m["offsets"][e + 1])
-    x = bf16_bits_to_f32(inp.bits[bits][m["src_token"][a:b]])
-    return a, b, x, pp[a:b]
-
-
-def _sample_experts(m, E, n):
-    sizes = np.diff(m["offsets"])
-    busy = [e for e in range(E) if sizes[e] > 0]
-    pick = sorted({busy[0], busy[-1], int(np.argmax(sizes))} | set(busy[:: max(1, len(busy) // n)][:n]))
-    return pick
-
-
-@pytest.mark.parametrize("name", ["mixtral_fwd", "qwen3_fwd"])
-def test_forward_full_size(moe, name):
-    w = WORKLOADS[name]
-    inp = make_inputs(w, want_float=False)
-    print(f"{name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.k}", flush=True)
-    idx, p, r, w1, w2, y, out = _layer_forward(moe, inp, w)
-    m, pp = _check_routing(idx, r, inp, w)
-    if name == "qwen3_fwd":
-        assert (np.diff(m["offsets"]) == 0).any(), "the skewed workload must leave experts idle"
-    yh = host(y)
-    ref_y = np.zeros_like(yh)
-    checked = np.zeros(w.R, bool)
-    for e in _sample_experts(m, w.E, 2 if w.E <= 8 else 6):
-        a, b, x, pe = _expert_rows(inp, m, pp, e)
-        W1 = bf16_bits_to_f32(inp.bits["w1"][e:e + 1])
-        W2 = bf16_bits_to_f32(inp.bits["w2"][e:e + 1])
-        ref_y[a:b], _, _ = oracle.grouped_mlp_forward(x, W1, W2, np.array([0, b - a]), pe)
-        checked[a:b] = True
-        err = max_rel_err(yh[a:b], ref_y[a:b])
-        print(f"  expert {e}: rows {b - a}, max rel err {err:.2e}", flush=True)
-        assert err <= BF16_TOL
-    # combine: tokens whose k rows were all checked above go through the oracle's combine
-    rmap = m["row_id_map"].reshape(w.T, w.k)
-    full = checked[rmap].all(axis=1)
-    if full.any():
-        ref_out = oracle.unpermute_combine(ref_y, m["row_id_map"], w.T, w.k)
-        assert max_rel_err(host(out)[full], ref_out[full]) <= BF16_TOL
-
-
-def test_mxfp8_forward_full_size(moe):
-    w = WORKLOADS["mixtral_mxfp8_fwd"]
-    inp = make_inputs(w, want_float=False)
-    print(f"mixtral_mxfp8_fwd: T={w.T} H={w.H} I={w.I}", flush=True)
-    idx, p, r, w1, w2, y, out = _layer_forward(moe, inp, w, compute="mxfp8")
-    m, pp = _check_routing(idx, r, inp, w)
-    yh = host(y)
-    e = int(np.argmax(np.diff(m["offsets"])))
-    a, b, x, pe = _expert_rows(inp, m, pp, e)
+    x = bf16_bits_to_f32(inp.bits["x"][m["src_token"][a:b]])
     W1 = bf16_bits_to_f32(inp.bits["w1"][e:e + 1])
     W2 = bf16_bits_to_f32(inp.bits["w2"][e:e + 1])
-    ref, _ = oracle.grouped_mlp_forward_mxfp8(x, W1, W2, np.array([0, b - a]), pe)
-    err = max_rel_err(yh[a:b], ref)
-    print(f"  expert {e}: rows {b - a}, max rel err {err:.2e}", flush=True)
-    assert err <= MX_TOL
+    return a, b, x, pp[a:b], W1, W2
 
 
-def test_forward_backward_full_size(moe):
+# ---------------------------------------------------------------------------
+# forward workloads: Mixtral bf16, Qwen3 bf16 (skewed, idle experts), Mixtral MXFP8
+# ---------------------------------------------------------------------------
+
+def _forward_run(moe, name):
+    if name in _RUNS:
+        return _RUNS[name]
+    _RUNS.clear()
+    w = WORKLOADS[name]
+    inp = _inputs(name)
+    compute = "mxfp8" if w.dtype == "mxfp8" else "bf16"
+    print(f"{name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.k} ({compute}), GPU layer", flush=True)
+    idx, r, m, pp = _route_and_permute(moe, inp, w)
+    if name == "qwen3_fwd":
+        assert (np.diff(m["offsets"]) == 0).any(), "the skewed workload must leave experts idle"
+    w1, w2 = dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"])
+    y = moe.moe_grouped_mlp_fwd(r["x_perm"], w1, w2, r["offsets"], r["prob_perm"], compute=compute)
+    out = moe.moe_unpermute_combine(y, r["row_id_map"], w.T, w.k)
+    run = dict(w=w, inp=inp, m=m, pp=pp, tol=MX_TOL if compute == "mxfp8" else BF16_TOL, y=_h32(y), out=_h32(out),
+               ref_y={})
+    del idx, r, w1, w2, y, out
+    _done_with_gpu()
+    _RUNS[name] = run
+    return run
+
+
+def _ref_forward(run, e):
+    if e not in run["ref_y"]:
+        a, b, x, pe, W1, W2 = _expert(run, e)
+        if run["w"].dtype == "mxfp8":
+            ref, _ = oracle.grouped_mlp_forward_mxfp8(x, W1, W2, np.array([0, b - a]), pe)
+        else:
+            ref, _, _ = oracle.grouped_mlp_forward(x, W1, W2, np.array([0, b - a]), pe)
+        run["ref_y"][e] = ref
+    return run["ref_y"][e]
+
+
+FWD_CASES = ([("mixtral_fwd", (e,)) for e in range(8)]
+             + [("qwen3_fwd", tuple(range(16 * g, 16 * g + 16))) for g in range(8)]
+             + [("mixtral_mxfp8_fwd", (e,)) for e in range(8)])
+
+
+@pytest.mark.parametrize("name,experts", FWD_CASES,
+                         ids=[f"{n}-e{x[0]}" + (f"-{x[-1]}" if len(x) > 1 else "") for n, x in FWD_CASES])
+def test_forward_full_size_experts(moe, name, experts):
+    run = _forward_run(moe, name)
+    for e in experts:
+        a, b = int(run["m"]["offsets"][e]), int(run["m"]["offsets"][e + 1])
+        if a == b:
+            print(f"  expert {e}: no rows", flush=True)
+            continue
+        err = max_rel_err(run["y"][a:b], _ref_forward(run, e))
+        print(f"  expert {e}: rows {b - a}, y max rel err {err:.2e}", flush=True)
+        assert err <= run["tol"], e
+
+
+@pytest.mark.parametrize("name", ["mixtral_fwd", "qwen3_fwd", "mixtral_mxfp8_fwd"])
+def test_forward_full_size_combine(moe, name):
+    """Every token's output after the GPU combine, against the oracle's combine of the
+    oracle's per-expert results."""
+    run = _forward_run(moe, name)
+    w, m = run["w"], run["m"]
+    ref_y = np.zeros((w.R, w.H))
+    for e in range(w.E):
+        a, b = int(m["offsets"][e]), int(m["offsets"][e + 1])
+        if b > a:
+            ref_y[a:b] = _ref_forward(run, e)
+    ref_out = oracle.unpermute_combine(ref_y, m["row_id_map"], w.T, w.k)
+    err = max_rel_err(run["out"], ref_out)
+    print(f"{name}: out over all {w.T} tokens, max rel err {err:.2e}", flush=True)
+    assert err <= run["tol"]
+    _RUNS.clear()
+
+
+# ---------------------------------------------------------------------------
+# Mixtral forward + backward (T = 4096), bf16
+# ---------------------------------------------------------------------------
+
+def _fwd_bwd_run(moe):
+    name = "mixtral_fwd_bwd/bf16"
+    if name in _RUNS:
+        return _RUNS[name]
+    _RUNS.clear()
     w = WORKLOADS["mixtral_fwd_bwd"]
-    inp = make_inputs(w, want_float=False)
-    print(f"mixtral_fwd_bwd: T={w.T} H={w.H} I={w.I}", flush=True)
-    idx, p, r, w1, w2, (y, z, h), out = _layer_forward(moe, inp, w, save=True)
-    m, pp = _check_routing(idx, r, inp, w)
+    inp = _inputs("mixtral_fwd_bwd")
+    print(f"mixtral_fwd_bwd: T={w.T} H={w.H} I={w.I}, GPU layer forward + backward (bf16)", flush=True)
+    idx, r, m, pp = _route_and_permute(moe, inp, w)
+    w1, w2 = dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"])
+    y, z, h = moe.moe_grouped_mlp_fwd(r["x_perm"], w1, w2, r["offsets"], r["prob_perm"], save_for_bwd=True)
+    out = moe.moe_unpermute_combine(y, r["row_id_map"], w.T, w.k)
     dyp = moe.moe_permute(dev_bf16(inp.bits["dout"]), idx, None, w.E, row_id_map=r["row_id_map"])["x_perm"]
     dxp, dw1, dw2, dprob = moe.moe_grouped_mlp_bwd(dyp, r["x_perm"], z, h, r["prob_perm"], w1, w2, r["offsets"])
     dx = moe.moe_unpermute_combine(dxp, r["row_id_map"], w.T, w.k)
-    torch.cuda.synchronize()
-    dxph, dprobh = host(dxp), dprob.cpu().numpy()
-    for e in _sample_experts(m, w.E, 1):
-        a, b, x, pe = _expert_rows(inp, m, pp, e)
-        dy = bf16_bits_to_f32(inp.bits["dout"][m["src_token"][a:b]])
-        W1 = bf16_bits_to_f32(inp.bits["w1"][e:e + 1])
-        W2 = bf16_bits_to_f32(inp.bits["w2"][e:e + 1])
+    # the gradient w.r.t. the routing probabilities: dprob[t, j] = dprob_perm[row_id_map[t*k + j]],
+    # gathered on the GPU as a one-slot combine of one-column rows
+    dprob_tk = moe.moe_unpermute_combine(dprob.view(w.R, 1), r["row_id_map"], w.R, 1).view(w.T, w.k)
+    run = dict(w=w, inp=inp, m=m, pp=pp, y=_h32(y), out=_h32(out), dxp=_h32(dxp), dx=_h32(dx),
+               dprob_perm=dprob.cpu().numpy(), dprob=dprob_tk.cpu().numpy(), dw1=bf16_bits(dw1), dw2=bf16_bits(dw2),
+               ref={})
+    del idx, r, w1, w2, y, z, h, out, dyp, dxp, dw1, dw2, dprob, dx, dprob_tk
+    _done_with_gpu()
+    _RUNS[name] = run
+    return run
+
+
+def _ref_fwd_bwd(run, e):
+    if e not in run["ref"]:
+        a, b, x, pe, W1, W2 = _expert(run, e)
+        dy = bf16_bits_to_f32(run["inp"].bits["dout"][run["m"]["src_token"][a:b]])
+        y, _, _ = oracle.grouped_mlp_forward(x, W1, W2, np.array([0, b - a]), pe)
         g = oracle.grouped_mlp_backward(dy, x, W1, W2, np.array([0, b - a]), pe)
-        errs = {
-            "dx_perm": max_rel_err(dxph[a:b], g["dx_perm"]),
-            "dprob": max_rel_err(dprobh[a:b], g["dprob_perm"]),
-            "dw_gate_up": max_rel_err(host(dw1[e]), g["dw_gate_up"][0]),
-            "dw_down": max_rel_err(host(dw2[e]), g["dw_down"][0]),
-        }
-        print(f"  expert {e}: rows {b - a}, " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
-        for k, v in errs.items():
-            assert v <= BF16_TOL, k
-    assert np.isfinite(host(dx)).all()
+        run["ref"][e] = dict(y=y, dx_perm=g["dx_perm"], dprob_perm=g["dprob_perm"], dw1=g["dw_gate_up"][0],
+                             dw2=g["dw_down"][0])
+    return run["ref"][e]
 
 
-def test_mxfp8_backward_full_size(moe):
-    """The MXFP8 grouped MLP backward at the Mixtral fwd+bwd shape (R = 8192), in the
-    benchmark's launch configuration, on the real routing and permutation. The saved z
-    and h are seeded bf16 draws (the backward takes them as inputs). The largest
-    expert's gradients (dx and dprob rows, dW1, dW2) against the oracle's MXFP8 backward
-    on that expert's rows (a one-expert call gives the same expert results as the whole
-    call: the token-axis blocks restart at each expert)."""
-    from moe_inputs import make_grad
-    w = WORKLOADS["mixtral_fwd_bwd"]
-    inp = make_inputs(w, want_float=False)
-    R = w.T * w.k
-    print(f"mixtral_fwd_bwd MXFP8 backward: R={R} H={w.H} I={w.I}", flush=True)
-    idx, p = moe.moe_route_topk(dev_f32(inp.logits), w.k)
-    r = moe.moe_permute(dev_bf16(inp.bits["x"]), idx, p, w.E)
-    m, pp = _check_routing(idx, r, inp, w)
-    _, zbits = make_grad((R, 2 * w.I), 501)
-    _, hbits = make_grad((R, w.I), 502)
-    w1, w2 = dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"])
-    dyp = moe.moe_permute(dev_bf16(inp.bits["dout"]), idx, None, w.E, row_id_map=r["row_id_map"])["x_perm"]
-    dxp, dw1, dw2, dprob = moe.moe_grouped_mlp_bwd(dyp, r["x_perm"], dev_bf16(zbits), dev_bf16(hbits), r["prob_perm"],
-                                                   w1, w2, r["offsets"], compute="mxfp8")
-    torch.cuda.synchronize()
-    e = int(np.argmax(np.diff(m["offsets"])))
-    a, b, x, pe = _expert_rows(inp, m, pp, e)
-    dy = bf16_bits_to_f32(inp.bits["dout"][m["src_token"][a:b]])
-    W1 = bf16_bits_to_f32(inp.bits["w1"][e:e + 1])
-    W2 = bf16_bits_to_f32(inp.bits["w2"][e:e + 1])
-    g = oracle.grouped_mlp_backward_mxfp8(dy, x, bf16_bits_to_f32(zbits[a:b]), bf16_bits_to_f32(hbits[a:b]), W1, W2,
-                                          np.array([0, b - a]), pe)
+@pytest.mark.parametrize("e", range(8))
+def test_forward_backward_full_size_expert(moe, e):
+    run = _fwd_bwd_run(moe)
+    a, b = int(run["m"]["offsets"][e]), int(run["m"]["offsets"][e + 1])
+    ref = _ref_fwd_bwd(run, e)
     errs = {
-        "dx_perm": max_rel_err(host(dxp)[a:b], g["dx_perm"]),
-        "dprob": max_rel_err(dprob.cpu().numpy()[a:b], g["dprob_perm"]),
-        "dw_gate_up": max_rel_err(host(dw1[e]), g["dw_gate_up"][0]),
-        "dw_down": max_rel_err(host(dw2[e]), g["dw_down"][0]),
+        "y": max_rel_err(run["y"][a:b], ref["y"]),
+        "dx_perm": max_rel_err(run["dxp"][a:b], ref["dx_perm"]),
+        "dprob": max_rel_err(run["dprob_perm"][a:b], ref["dprob_perm"]),
+        "dw_gate_up": max_rel_err(bf16_bits_to_f32(run["dw1"][e]), ref["dw1"]),
+        "dw_down": max_rel_err(bf16_bits_to_f32(run["dw2"][e]), ref["dw2"]),
     }
     print(f"  expert {e}: rows {b - a}, " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     for k, v in errs.items():
-        assert v <= MX_TOL, k
+        assert v <= BF16_TOL, k
+
+
+def test_forward_backward_full_size_tokens(moe):
+    """out, dx (after the GPU combine) and dprob [T, k] (the GPU gather) for every token."""
+    run = _fwd_bwd_run(moe)
+    w, m = run["w"], run["m"]
+    ref_y = np.zeros((w.R, w.H))
+    ref_dxp = np.zeros((w.R, w.H))
+    ref_dprob = np.zeros(w.R)
+    for e in range(w.E):
+        a, b = int(m["offsets"][e]), int(m["offsets"][e + 1])
+        ref = _ref_fwd_bwd(run, e)
+        ref_y[a:b], ref_dxp[a:b], ref_dprob[a:b] = ref["y"], ref["dx_perm"], ref["dprob_perm"]
+    errs = {
+        "out": max_rel_err(run["out"], oracle.unpermute_combine(ref_y, m["row_id_map"], w.T, w.k)),
+        "dx": max_rel_err(run["dx"], oracle.unpermute_combine(ref_dxp, m["row_id_map"], w.T, w.k)),
+        "dprob": max_rel_err(run["dprob"], ref_dprob[m["row_id_map"]].reshape(w.T, w.k)),
+    }
+    print(f"mixtral_fwd_bwd all {w.T} tokens: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= BF16_TOL, k
+    # the gather itself moves bits: dprob[t, j] is exactly the GPU's dprob_perm of its row
+    assert np.array_equal(run["dprob"].ravel(), run["dprob_perm"][m["row_id_map"]])
+    _RUNS.clear()
+
+
+# ---------------------------------------------------------------------------
+# Mixtral forward + backward (T = 4096), grouped MLP in MXFP8
+# ---------------------------------------------------------------------------
+
+def _mx_fwd_bwd_run(moe):
+    name = "mixtral_fwd_bwd/mxfp8"
+    if name in _RUNS:
+        return _RUNS[name]
+    _RUNS.clear()
+    w = WORKLOADS["mixtral_fwd_bwd"]
+    inp = _inputs("mixtral_fwd_bwd")
+    print(f"mixtral_fwd_bwd: T={w.T} H={w.H} I={w.I}, GPU layer forward + backward (MXFP8)", flush=True)
+    idx, r, m, pp = _route_and_permute(moe, inp, w)
+    w1, w2 = dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"])
+    y, z, h = moe.moe_grouped_mlp_fwd(r["x_perm"], w1, w2, r["offsets"], r["prob_perm"], compute="mxfp8",
+                                      save_for_bwd=True)
+    dyp = moe.moe_permute(dev_bf16(inp.bits["dout"]), idx, None, w.E, row_id_map=r["row_id_map"])["x_perm"]
+    dxp, dw1, dw2, dprob = moe.moe_grouped_mlp_bwd(dyp, r["x_perm"], z, h, r["prob_perm"], w1, w2, r["offsets"],
+                                                   compute="mxfp8")
+    dx = moe.moe_unpermute_combine(dxp, r["row_id_map"], w.T, w.k)
+    run = dict(w=w, inp=inp, m=m, pp=pp, y=_h32(y), z=bf16_bits(z), h=bf16_bits(h), dxp=_h32(dxp), dx=_h32(dx),
+               dprob_perm=dprob.cpu().numpy(), dw1=bf16_bits(dw1), dw2=bf16_bits(dw2), ref={})
+    del idx, r, w1, w2, y, z, h, dyp, dxp, dw1, dw2, dprob, dx
+    _done_with_gpu()
+    _RUNS[name] = run
+    return run
+
+
+@pytest.mark.parametrize("e", range(8))
+def test_mxfp8_forward_backward_full_size_expert(moe, e):
+    """Expert e of the MXFP8 training step: y, and the saved z and h, against the
+    oracle's MXFP8 forward; dx, dprob, dW1, dW2 against the oracle's MXFP8 backward on
+    the GPU's saved z and h (the backward's inputs, taken as given), both with the bf16
+    roundings of dH and dZ that the recipe's return to bf16 implies and without them."""
+    run = _mx_fwd_bwd_run(moe)
+    a, b, x, pe, W1, W2 = _expert(run, e)
+    offs = np.array([0, b - a])
+    y, h_ref, z_ref = oracle.grouped_mlp_forward_mxfp8(x, W1, W2, offs, pe, return_z=True)
+    fwd = {"y": max_rel_err(run["y"][a:b], y), "z": max_rel_err(bf16_bits_to_f32(run["z"][a:b]), z_ref),
+           "h": max_rel_err(bf16_bits_to_f32(run["h"][a:b]), h_ref)}
+    dy = bf16_bits_to_f32(run["inp"].bits["dout"][run["m"]["src_token"][a:b]])
+    zs, hs = bf16_bits_to_f32(run["z"][a:b]), bf16_bits_to_f32(run["h"][a:b])
+    got = {"dx_perm": run["dxp"][a:b], "dprob_perm": run["dprob_perm"][a:b],
+           "dw_gate_up": bf16_bits_to_f32(run["dw1"][e]), "dw_down": bf16_bits_to_f32(run["dw2"][e])}
+    errs = {}
+    for rounded in (True, False):
+        g = oracle.grouped_mlp_backward_mxfp8(dy, x, zs, hs, W1, W2, offs, pe, round_bf16=rounded)
+        for k in got:
+            errs[(k, rounded)] = max_rel_err(got[k], g[k] if k == "dx_perm" or k == "dprob_perm" else g[k][0])
+        if rounded:
+            run["ref"][e] = dict(dx_perm=g["dx_perm"])
+    print(f"  expert {e}: rows {b - a}, " + ", ".join(f"{k} {v:.2e}" for k, v in fwd.items()) + "; "
+          + ", ".join(f"{k} {v:.2e}/{errs[(k, False)]:.2e}" for (k, r), v in errs.items() if r)
+          + " (with/without the dH, dZ bf16 roundings)", flush=True)
+    assert fwd["y"] <= MX_TOL and fwd["z"] <= 1e-2 and fwd["h"] <= 1e-2
+    for (k, rounded), v in errs.items():
+        assert v <= MX_TOL, (k, rounded)
+
+
+def test_mxfp8_forward_backward_full_size_tokens(moe):
+    """dx after the GPU combine for every token of the MXFP8 training step."""
+    run = _mx_fwd_bwd_run(moe)
+    w, m = run["w"], run["m"]
+    ref_dxp = np.zeros((w.R, w.H))
+    for e in range(w.E):
+        a, b, x, pe, W1, W2 = _expert(run, e)
+        if e not in run["ref"]:
+            dy = bf16_bits_to_f32(run["inp"].bits["dout"][m["src_token"][a:b]])
+            g = oracle.grouped_mlp_backward_mxfp8(dy, x, bf16_bits_to_f32(run["z"][a:b]),
+                                                  bf16_bits_to_f32(run["h"][a:b]), W1, W2, np.array([0, b - a]), pe)
+            run["ref"][e] = dict(dx_perm=g["dx_perm"])
+        ref_dxp[a:b] = run["ref"][e]["dx_perm"]
+    err = max_rel_err(run["dx"], oracle.unpermute_combine(ref_dxp, m["row_id_map"], w.T, w.k))
+    print(f"mixtral_fwd_bwd MXFP8: dx over all {w.T} tokens, max rel err {err:.2e}", flush=True)
+    assert err <= MX_TOL
+    _RUNS.clear()
+    _INPUTS.clear()

@@ -128,8 +128,9 @@ def test_tiny_layer_f32_forward_and_backward(moe):
     assert max_rel_err(dx.cpu().numpy(), g["dx"]) <= F32_TOL
     assert max_rel_err(dw1.cpu().numpy(), g["dw_gate_up"]) <= F32_TOL
     assert max_rel_err(dw2.cpu().numpy(), g["dw_down"]) <= F32_TOL
-    dprob = dprob_perm.cpu().numpy()[r["row_id_map"].cpu().numpy()].reshape(T, k)
-    assert max_rel_err(dprob, g["drouting_weights"]) <= F32_TOL
+    # dprob [T, k] gathered on the GPU (a one-slot combine of one-column rows)
+    dprob = moe.moe_unpermute_combine(dprob_perm.view(T * k, 1), r["row_id_map"], T * k, 1).view(T, k)
+    assert max_rel_err(dprob.cpu().numpy(), g["drouting_weights"]) <= F32_TOL
 
 
 def test_layer_bf16_end_to_end(moe):
@@ -144,3 +145,40 @@ def test_layer_bf16_end_to_end(moe):
     ridx, rp = oracle.route_topk(inp.logits, w.k)
     ref = oracle.moe_ffn_forward(inp.x, inp.w1, inp.w2, ridx, rp)
     assert max_rel_err(host(out), ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("shape", [("mixtral_like", 600, 512, 256, 8, 2, 0.0), ("qwen_like", 700, 256, 256, 32, 8, 1.2)],
+                         ids=["mixtral_like", "qwen_like"])
+def test_layer_bf16_forward_backward_with_gpu_gathers(moe, shape):
+    """The bf16 layer forward and backward exactly as the benchmark runs it: the output
+    gradient gathered onto the routed rows, the grouped MLP backward, dx combined over
+    each token's k rows and dprob [T, k] gathered from the routed rows, all on the GPU;
+    against the per-expert loop's backward (dx, the weight gradients, and the gradient
+    w.r.t. the routing probabilities)."""
+    name, T, H, I, E, k, zipf = shape
+    w = scaled(WORKLOADS["mixtral_fwd_bwd"], T=T, H=H, I=I, E=E, k=k, zipf=zipf, seed=13)
+    inp = make_inputs(w)
+    R = T * k
+    print(f"layer bf16 fwd+bwd {name}: T={T} H={H} I={I} E={E} k={k}", flush=True)
+    idx, p = moe.moe_route_topk(dev_f32(inp.logits), k)
+    r = moe.moe_permute(dev_bf16(inp.bits["x"]), idx, p, E)
+    w1, w2 = dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"])
+    y, z, h = moe.moe_grouped_mlp_fwd(r["x_perm"], w1, w2, r["offsets"], r["prob_perm"], save_for_bwd=True)
+    out = moe.moe_unpermute_combine(y, r["row_id_map"], T, k)
+    dyp = moe.moe_permute(dev_bf16(inp.bits["dout"]), idx, None, E, row_id_map=r["row_id_map"])["x_perm"]
+    dxp, dw1, dw2, dprob_perm = moe.moe_grouped_mlp_bwd(dyp, r["x_perm"], z, h, r["prob_perm"], w1, w2, r["offsets"])
+    dx = moe.moe_unpermute_combine(dxp, r["row_id_map"], T, k)
+    dprob = moe.moe_unpermute_combine(dprob_perm.view(R, 1), r["row_id_map"], R, 1).view(T, k)
+    torch.cuda.synchronize()
+    ridx, rp = oracle.route_topk(inp.logits, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    ref = oracle.moe_ffn_forward(inp.x, inp.w1, inp.w2, ridx, rp)
+    g = oracle.moe_ffn_backward(inp.x, inp.w1, inp.w2, ridx, rp, inp.dout)
+    errs = dict(out=max_rel_err(host(out), ref), dx=max_rel_err(host(dx), g["dx"]),
+                dw_gate_up=max_rel_err(host(dw1), g["dw_gate_up"]), dw_down=max_rel_err(host(dw2), g["dw_down"]),
+                dprob=max_rel_err(dprob.cpu().numpy(), g["drouting_weights"]))
+    print("  " + ", ".join(f"{k2} {v:.2e}" for k2, v in errs.items()), flush=True)
+    for k2, v in errs.items():
+        assert v <= BF16_TOL, k2
+    # the gather moves bits: each dprob[t, j] is the dprob_perm entry of its row
+    assert torch.equal(dprob.view(-1), dprob_perm[r["row_id_map"].long()])

@@ -120,6 +120,47 @@ def test_permute_edges(moe):
     _permute_case(moe, 3000, 16, 200, 3, idx, p.astype(np.float32))
 
 
+def test_permute_drops_repeated_and_out_of_range_ids(moe):
+    """The input contract of moe_permute: a (token, slot) pair whose expert id is out of
+    [0, E) or repeats an earlier slot's id is dropped (row -1, not counted); the rest
+    are permuted exactly as if the dropped pairs were absent, and the combine skips them."""
+    rng = np.random.default_rng(3)
+    T, H, E, k = 1100, 64, 8, 3
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    idx[rng.choice(T, 60, replace=False), 2] = idx[:, 0][rng.choice(T, 60, replace=False)]  # some repeats
+    rep = rng.choice(T, 40, replace=False)
+    idx[rep, 2] = idx[rep, 1]                                                                   # repeats
+    bad = rng.choice(T, 40, replace=False)
+    idx[bad, 1] = rng.choice([-1, -7, E, E + 3, 1 << 30], 40)                                 # out of range
+    keep = np.ones_like(idx, bool)
+    for j in range(k):
+        keep[:, j] &= (idx[:, j] >= 0) & (idx[:, j] < E)
+        for i in range(j):
+            keep[:, j] &= idx[:, j] != idx[:, i]
+    assert (~keep).sum() > 50
+    clean = np.where(keep, idx, -1)
+    p = rng.uniform(0.1, 1, (T, k)).astype(np.float32)
+    xb = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    print(f"permute with dropped pairs: T={T} E={E} k={k}, {(~keep).sum()} dropped", flush=True)
+    r = moe.moe_permute(dev_bf16(xb), torch.from_numpy(idx).cuda(), dev_f32(p), E)
+    m = oracle.permute(clean, E)
+    n = int(m["offsets"][E])
+    assert n == keep.sum()
+    for key in ("split_sizes", "offsets", "row_id_map"):
+        assert np.array_equal(r[key].cpu().numpy(), m[key]), key
+    assert np.array_equal(r["src_token"].cpu().numpy()[:n], m["src_token"][:n])
+    assert np.array_equal(bf16_bits(r["x_perm"])[:n], xb[m["src_token"][:n]])
+    pp = p.ravel()[m["src_token"][:n] * k + m["src_slot"][:n]]
+    assert np.array_equal(r["prob_perm"].cpu().numpy()[:n], pp)
+    # the combine adds only the kept pairs of each token
+    y = torch.zeros((T * k, H), dtype=torch.float32, device="cuda")
+    y[:n] = torch.from_numpy(rng.standard_normal((n, H)).astype(np.float32)).cuda()
+    out = moe.moe_unpermute_combine(y, r["row_id_map"], T, k).cpu().numpy()
+    ref = oracle.unpermute_combine(np.concatenate([y[:n].cpu().numpy(), np.zeros((1, H))]),
+                                   np.where(m["row_id_map"] < 0, n, m["row_id_map"]), T, k)
+    assert np.abs(out - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
 def test_permute_reuse_map_and_mxfp8_rows(moe):
     rng = np.random.default_rng(2)
     T, H, E, k = 777, 128, 8, 2

@@ -294,3 +294,16 @@ def test_mxfp8_backward_token_blocks_start_at_each_expert():
     r = oracle.grouped_mlp_backward_mxfp8(**solo)
     np.testing.assert_array_equal(r["dw_down"][2], base["dw_down"][2])
     np.testing.assert_array_equal(r["dw_gate_up"][2], base["dw_gate_up"][2])
+
+
+def test_qdq_row_chunks_give_the_same_bits():
+    # quantisation blocks lie within rows: the threaded row-chunked qdq must equal one
+    # pass over the whole array, bit for bit (negative zeros and all-zero blocks included)
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((300, 96)) * np.exp2(rng.integers(-20, 20, (300, 1)))
+    x[5] = 0.0
+    x[7, :32] = -0.0
+    whole = oracle.mxfp8_qdq(x, rows_per_chunk=1 << 30)
+    for chunk in (1, 7, 64, 299):
+        got = oracle.mxfp8_qdq(x, rows_per_chunk=chunk)
+        assert np.array_equal(got.view(np.uint64), whole.view(np.uint64)), chunk
