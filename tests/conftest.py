@@ -28,3 +28,24 @@ def max_rel_err(a, b):
 @pytest.fixture
 def rel_err():
     return max_rel_err
+
+
+# Largest error seen per (group, tensor) over the cases a run checked; printed at the end
+# of every run (also with -q, and when every test passes) so the parity margins of a
+# GPU run are visible in its log.
+_PARITY = {}
+
+
+def record_parity(group, **errs):
+    d = _PARITY.setdefault(group, {})
+    for k, v in errs.items():
+        d[k] = max(d.get(k, 0.0), float(v))
+
+
+def pytest_terminal_summary(terminalreporter):
+    if not _PARITY:
+        return
+    terminalreporter.write_line("parity summary (largest max|a-b|/max|b| over the checked cases):")
+    for group in sorted(_PARITY):
+        errs = _PARITY[group]
+        terminalreporter.write_line(f"  {group}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from conftest import max_rel_err
+from conftest import max_rel_err, record_parity
 from gpu_util import bf16_bits, dev_bf16, dev_f32
 from moe_inputs import WORKLOADS, bf16_bits_to_f32, make_inputs
 
@@ -137,6 +137,7 @@ def test_forward_full_size_experts(moe, name, experts):
             continue
         err = max_rel_err(run["y"][a:b], _ref_forward(run, e))
         print(f"  expert {e}: rows {b - a}, y max rel err {err:.2e}", flush=True)
+        record_parity(f"full size {name} per expert", y=err)
         assert err <= run["tol"], e
 
 
@@ -154,6 +155,7 @@ def test_forward_full_size_combine(moe, name):
     ref_out = oracle.unpermute_combine(ref_y, m["row_id_map"], w.T, w.k)
     err = max_rel_err(run["out"], ref_out)
     print(f"{name}: out over all {w.T} tokens, max rel err {err:.2e}", flush=True)
+    record_parity(f"full size {name} all tokens", out=err)
     assert err <= run["tol"]
     _RUNS.clear()
 
@@ -213,6 +215,7 @@ def test_forward_backward_full_size_expert(moe, e):
         "dw_down": max_rel_err(bf16_bits_to_f32(run["dw2"][e]), ref["dw2"]),
     }
     print(f"  expert {e}: rows {b - a}, " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    record_parity("full size mixtral_fwd_bwd bf16 per expert", **errs)
     for k, v in errs.items():
         assert v <= BF16_TOL, k
 
@@ -234,6 +237,7 @@ def test_forward_backward_full_size_tokens(moe):
         "dprob": max_rel_err(run["dprob"], ref_dprob[m["row_id_map"]].reshape(w.T, w.k)),
     }
     print(f"mixtral_fwd_bwd all {w.T} tokens: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    record_parity("full size mixtral_fwd_bwd bf16 all tokens", **errs)
     for k, v in errs.items():
         assert v <= BF16_TOL, k
     # the gather itself moves bits: dprob[t, j] is exactly the GPU's dprob_perm of its row
@@ -295,6 +299,11 @@ def test_mxfp8_forward_backward_full_size_expert(moe, e):
     print(f"  expert {e}: rows {b - a}, " + ", ".join(f"{k} {v:.2e}" for k, v in fwd.items()) + "; "
           + ", ".join(f"{k} {v:.2e}/{errs[(k, False)]:.2e}" for (k, r), v in errs.items() if r)
           + " (with/without the dH, dZ bf16 roundings)", flush=True)
+    record_parity("full size mixtral_fwd_bwd MXFP8 forward per expert", **fwd)
+    record_parity("full size mixtral_fwd_bwd MXFP8 backward per expert, dH/dZ rounded to bf16",
+                  **{k: v for (k, r), v in errs.items() if r})
+    record_parity("full size mixtral_fwd_bwd MXFP8 backward per expert, no dH/dZ rounding",
+                  **{k: v for (k, r), v in errs.items() if not r})
     assert fwd["y"] <= MX_TOL and fwd["z"] <= 1e-2 and fwd["h"] <= 1e-2
     for (k, rounded), v in errs.items():
         assert v <= MX_TOL, (k, rounded)
@@ -315,6 +324,7 @@ def test_mxfp8_forward_backward_full_size_tokens(moe):
         ref_dxp[a:b] = run["ref"][e]["dx_perm"]
     err = max_rel_err(run["dx"], oracle.unpermute_combine(ref_dxp, m["row_id_map"], w.T, w.k))
     print(f"mixtral_fwd_bwd MXFP8: dx over all {w.T} tokens, max rel err {err:.2e}", flush=True)
+    record_parity("full size mixtral_fwd_bwd MXFP8 all tokens", dx=err)
     assert err <= MX_TOL
     _RUNS.clear()
     _INPUTS.clear()

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from conftest import max_rel_err
+from conftest import max_rel_err, record_parity
 from moe_inputs import WORKLOADS, make_grad, make_inputs, scaled
 
 pytestmark = pytest.mark.gpu
@@ -178,6 +178,7 @@ def test_layer_bf16_forward_backward_with_gpu_gathers(moe, shape):
                 dw_gate_up=max_rel_err(host(dw1), g["dw_gate_up"]), dw_down=max_rel_err(host(dw2), g["dw_down"]),
                 dprob=max_rel_err(dprob.cpu().numpy(), g["drouting_weights"]))
     print("  " + ", ".join(f"{k2} {v:.2e}" for k2, v in errs.items()), flush=True)
+    record_parity("layer bf16 fwd+bwd with GPU gathers", **errs)
     for k2, v in errs.items():
         assert v <= BF16_TOL, k2
     # the gather moves bits: each dprob[t, j] is the dprob_perm entry of its row

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from conftest import max_rel_err
+from conftest import max_rel_err, record_parity
 from moe_inputs import WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, make_grad, make_inputs, scaled
 
 pytestmark = pytest.mark.gpu
@@ -55,6 +55,8 @@ def _check_both_readings(got, dy, x, z, h, w1, w2, offsets, pp):
                     dw2=max_rel_err(got["dw2"], ref["dw_down"]), dprob=max_rel_err(got["dprob"], ref["dprob_perm"]))
         print(f"  max rel err ({'with' if rounded else 'without'} the dH, dZ bf16 roundings) "
               + " ".join(f"{k2} {v:.2e}" for k2, v in errs.items()), flush=True)
+        record_parity("MXFP8 backward small shapes, " + ("dH/dZ rounded to bf16" if rounded else "no dH/dZ rounding"),
+                      **errs)
         for k2, v in errs.items():
             assert v <= MX_TOL, (k2, rounded)
 
