@@ -13,6 +13,8 @@
 //             and each block's first row per expert;
 //   scatter : one wavefront per token reads its row once (16-byte lanes) and writes
 //             it to its k destination rows, plus the maps and the row weights.
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 
@@ -383,4 +385,64 @@ extern "C" moe_status moe_unpermute_combine(const void* y_perm, moe_dtype dt, co
                          weights, T, H, k, out);
   }
   return check_launch("moe_unpermute_combine");
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free permutation: the count/scan scratch lives in a static device array
+// ---------------------------------------------------------------------------
+
+namespace moe {
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+constexpr int kMaxDevices = 64;
+
+// One copy per GPU, held until the process ends. In host code this name is only a
+// stand-in for the symbol: kernels get the device address that hipGetSymbolAddress
+// returns for the current device.
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per device.
+moe_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_LAUNCH, "moe_permute_noalloc: no current device (or device index >= 64)");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_LAUNCH, std::string("moe_permute_noalloc: hipGetSymbolAddress failed: ") + hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_permute_noalloc(const void* x, const uint8_t* x_scale, moe_dtype dt, int64_t T, int H,
+                                          int E, int k, const int32_t* topk_idx, const float* topk_prob,
+                                          int reuse_map, void* x_perm, uint8_t* x_perm_scale, float* prob_perm,
+                                          int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
+                                          int32_t* src_token, void* stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute_noalloc: T < 0, E out of [1, 256] or k out of [1, E]");
+  if (!reuse_map) {
+    const size_t need = permute_workspace_bytes(T, E, k);
+    if (need > kNoAllocScratchBytes)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_permute_noalloc: T = " + std::to_string(T) + ", E = " + std::to_string(E) +
+                                           ", k = " + std::to_string(k) + " need " + std::to_string(need) +
+                                           " bytes of scratch, more than the 8 MiB static area");
+  }
+  void* ws = nullptr;
+  if (!reuse_map && T > 0) {
+    const moe_status st = scratch_address(&ws);
+    if (st != MOE_OK) return st;
+  }
+  return moe_permute(x, x_scale, dt, T, H, E, k, topk_idx, topk_prob, reuse_map, x_perm, x_perm_scale, prob_perm,
+                     split_sizes, offsets, row_id_map, src_token, ws, ws ? kNoAllocScratchBytes : 0, stream);
 }

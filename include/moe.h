@@ -152,6 +152,25 @@ moe_status moe_permute(const void* x, const uint8_t* x_scale, moe_dtype dt, int6
                        void* stream);
 
 /*
+ * moe_permute without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops or harnesses that forbid
+ * hipMalloc). Same arguments (minus the workspace), semantics and outputs as
+ * moe_permute. Its count/scan scratch is a static 8 MiB device array inside the
+ * library: one per GPU, held until the process ends, its address looked up once per
+ * device on the first call. Sizes whose scratch (moe_workspace_size(MOE_OP_PERMUTE,
+ * ...)) exceeds 8 MiB return MOE_ERR_UNSUPPORTED before anything is launched (T*k up
+ * to about two million pairs at E = 8). The call allocates nothing. Every call on one
+ * GPU shares that GPU's array and no entry of it needs clearing (each call writes
+ * what it reads); calls that overlap in time on one GPU (other streams or threads)
+ * race on it and must be serialised by the caller.
+ */
+moe_status moe_permute_noalloc(const void* x, const uint8_t* x_scale, moe_dtype dt, int64_t T, int H,
+                               int E, int k, const int32_t* topk_idx, const float* topk_prob,
+                               int reuse_map, void* x_perm, uint8_t* x_perm_scale, float* prob_perm,
+                               int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
+                               int32_t* src_token, void* stream);
+
+/*
  * Unpermute with combine. Source: the index_add_ into final_hidden_states of the
  * baseline loop (Challenge 1).
  *   out[t] = sum over j = 0..k-1 (in that order, float32) of w[t, j] * y_perm[row_id_map[t*k + j]]

@@ -144,3 +144,16 @@ def test_mxfp8_colwise_argument_checks(L):
     assert L.mxfp8_quantize_colwise(d, 100, 64, 0, d, 32, 256, d, d, d, None) == INV     # E = 0
     assert L.mxfp8_quantize_colwise(d, 100, 64, 4, None, 32, 256, d, d, d, None) == INV  # NULL offsets
     assert b"kcap" in L.moe_last_error() or b"NULL" in L.moe_last_error()
+
+
+def test_noalloc_permute_rejects_sizes_beyond_its_scratch(L):
+    """moe_permute_noalloc checks its fixed 8 MiB scratch against the request before it
+    touches any device: a size that would need more is refused with UNSUPPORTED."""
+    from grouped_expert_gemm_amd import _lib
+    dummy = ctypes.c_void_p(256)
+    T, E, k = 1 << 20, 8, 4          # rank table alone: T * k * 4 = 16 MiB
+    assert L.moe_permute_noalloc(dummy, None, 1, T, 64, E, k, dummy, dummy, 0, dummy, None, dummy, dummy, dummy,
+                                 dummy, dummy, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert b"8 MiB" in L.moe_last_error()
+    assert L.moe_permute_noalloc(dummy, None, 1, 10, 64, 0, 1, dummy, dummy, 0, dummy, None, dummy, dummy, dummy,
+                                 dummy, dummy, None) == _lib.MOE_ERR_INVALID_ARG     # E = 0
