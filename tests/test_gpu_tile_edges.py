@@ -1,5 +1,6 @@
 """GPU parity of the forward grouped GEMM at expert sizes on every row-tile boundary:
-0, 1, a 32-row sub-tile, 64 / 65, 128 / 129 rows past a multiple of the 256-row tile,
+0, 1, a 32-row sub-tile, 64 / 65, 128 / 129, 192 / 193 rows past a multiple of the 256-row tile
+(the boundaries of the forward kernel's active row sub-tile counts 1-4),
 and whole tiles (the last tile of an expert is mostly rows past it, which the copies'
 range check turns into zeros and the stores skip). Outputs start as NaN so a row no
 kernel writes fails the check; both the plain-store (GroupedLinear) and the ScaledSwiGLU
@@ -19,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 BF16_TOL = 2e-2
 
-SIZES = [0, 1, 31, 64, 65, 100, 128, 129, 255, 256, 257, 300, 384, 385, 576]
+SIZES = [0, 1, 31, 64, 65, 100, 128, 129, 192, 193, 255, 256, 257, 300, 384, 385, 449, 576]
 
 
 @pytest.fixture(scope="module")
