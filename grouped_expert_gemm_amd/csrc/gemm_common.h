@@ -73,8 +73,10 @@ __device__ __forceinline__ void lds_barrier_keep() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-__device__ __forceinline__ void wait_vm_le(int n) {  // n: a multiple of 4 in [0, 24]
+__device__ __forceinline__ void wait_vm_le(int n) {  // n: a multiple of 4 in [0, 32]
   switch (n) {
+    case 32: wait_vm<32>(); break;
+    case 28: wait_vm<28>(); break;
     case 24: wait_vm<24>(); break;
     case 20: wait_vm<20>(); break;
     case 16: wait_vm<16>(); break;

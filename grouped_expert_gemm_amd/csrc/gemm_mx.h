@@ -13,10 +13,13 @@ moe_status forward(const moe_mlp_desc& d, int64_t R, const void* x_perm, const u
                    void* h_save = nullptr);
 
 // MXFP8 gate_up + ScaledSwiGLU on pre-quantised operands; h written as MXFP8, and
-// optionally z [R, 2I] and h [R, I] in bf16 for the backward
+// optionally z [R, 2I] and h [R, I] in bf16 for the backward. step_major: every scale
+// array (x's, the weights', h's) in the step-major layout of launch_mxfp8_quantize_step_major
+// (the wide-step kernel), else in the public row-major layout.
 moe_status gate_up(int E, int64_t R, int H, int I, const uint8_t* x, const uint8_t* x_scale, const void* const* w,
                    const uint8_t* const* w_scale, const int32_t* offsets, const float* prob, uint8_t* h,
-                   uint8_t* h_scale, hipStream_t s, void* z_save = nullptr, void* h_save = nullptr);
+                   uint8_t* h_scale, hipStream_t s, void* z_save = nullptr, void* h_save = nullptr,
+                   bool step_major = false);
 
 // per-tensor FP8 forward (E4M3 with one float32 scale per tensor: x_perm, each expert's
 // W1 and W2, and h, which is stored in bf16 before its scale is known)

@@ -835,16 +835,434 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
   }
 }
 
-static moe_status launch(int ep, bool pt, const MxParams& p, int64_t max_tiles, hipStream_t s, const char* what) {
+// MXFP8 grouped GEMM on the same wide-step copy pipeline as grouped_gemm_fp8t_kernel:
+// K steps of 128 fp8 values (a whole 128-byte line per row), the five-half-slot LDS
+// ring, two 64-value MFMA slices per step with the barrier between them. What it adds
+// are the block scales: a step covers 4 E8M0 blocks of each row, one 32-bit word. The
+// scales come step-major (word k * rows + r for step k of row r: the 32 rows of a
+// sub-tile are one 128-byte run; the row-major public layout puts each row on its own
+// cache line, and loading those cost a fifth of the kernel's time). The forward's
+// quantisers write this layout; the gate_up epilogue writes h's scales in it. P's
+// scale array has prm.N rows, Q's prm.R. Each lane loads the words of its 4 P rows and 4 Q rows with
+// buffer loads two steps ahead (issued ahead of that step's copies, so the copy waits
+// need not count them; one load covers two sub-tiles, fanned out across the wavefront's
+// halves with a lane swap), and shifts them right by 8 bits x its K half g: byte 0 is then block g
+// (slice 0) and byte 2 block 2 + g (slice 1), so the MFMA's byte select is the
+// compile-time 0 / 2 for every lane.
+// Epilogues: MX_STORE (bf16 rows through LDS), MX_SWIGLU (h = silu(G) U p quantised to
+// MXFP8 along I: a 32-value block is one sub-tile column span of a row, 16 values in
+// lane l and 16 in lane l ^ 32) and MX_SWIGLU_SAVE (also z and h in bf16, through LDS).
+template <int EP>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_mxw_kernel(const MxParams prm) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sH0[kXTile], sH1[kXTile], sH2[kXTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t sH3[kXTile], sH4[kXTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int E = prm.E;
+  const int R = (int)prm.R;
+  const int K = prm.K;
+  const int l32 = lane & 31, lhi = lane >> 5;
+
+  const int nwg = gridDim.x;
+  const int logical = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+
+  auto hslot = [&](auto H) -> uint8_t* {
+    if constexpr (H.value == 0) return sH0;
+    else if constexpr (H.value == 1) return sH1;
+    else if constexpr (H.value == 2) return sH2;
+    else if constexpr (H.value == 3) return sH3;
+    else return sH4;
+  };
+
+  // Tiles: expert-major, ceil(rows_e / 256) row tiles x n_tiles per expert, row tiles
+  // fastest. Expert offsets are walked once with wavefront-uniform loads and made a
+  // nondecreasing sequence inside [0, R] on the way.
+  auto clamp_off = [&](int v, int prev) -> int {
+    v = v < prev ? prev : v;
+    return v > R ? R : v;
+  };
+  int total = 0;
+  {
+    int prev = 0;
+    for (int x = 0; x < E; ++x) {
+      const int en = clamp_off(prm.offsets[x + 1], prev);
+      total += ((en - prev + kBM - 1) / kBM) * prm.n_tiles;
+      prev = en;
+    }
+  }
+  int e_w = 0;
+  int ob = 0;
+  int oe = clamp_off(prm.offsets[1], 0);
+  int ts_w = 0;
+  int nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
+  const int nk = K / kXBK;
+
+  const uint32_t fragP = (uint32_t)((wn * 64 + l32) * 128);
+  const uint32_t fragQ = (uint32_t)((wm * 128 + l32) * 128);
+  uint32_t ck[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) ck[c] = (uint32_t)(((2 * c + lhi) ^ swz8(l32)) << 4);
+  const int kc_row0 = wave * 8 + (lane >> 3);
+  const int kc_chunk = (lane & 7) ^ swz8(kc_row0);
+  constexpr int64_t kAll = 0xFFFFFFFFll;
+  const uint32_t gshift = 8u * (uint32_t)lhi;
+
+  for (int t = logical; t < total; t += nwg) {
+    // ---------------- tile decode ----------------
+    while (e_w < E && t >= ts_w + nt_w) {
+      ts_w += nt_w;
+      ++e_w;
+      ob = oe;
+      if (e_w < E) {
+        oe = clamp_off(prm.offsets[e_w + 1], ob);
+        nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
+      }
+    }
+    if (e_w >= E) break;
+    int e = e_w, mt, nt;
+    {
+      const int local = t - ts_w;
+      const int mte = (oe - ob + kBM - 1) / kBM;
+      mt = local % mte;
+      nt = local / mte;
+    }
+    e = __builtin_amdgcn_readfirstlane(e);
+    mt = __builtin_amdgcn_readfirstlane(mt);
+    nt = __builtin_amdgcn_readfirstlane(nt);
+    const int row_beg = __builtin_amdgcn_readfirstlane(ob);
+    const int row_end = __builtin_amdgcn_readfirstlane(oe);
+    const int tile_row = row_beg + mt * kBM;
+
+    auto p_row = [&](int r) -> int {
+      if constexpr (EP == MX_SWIGLU || EP == MX_SWIGLU_SAVE) return (r < 128) ? nt * 128 + r : prm.I + nt * 128 + (r - 128);
+      else return nt * kBN + r;
+    };
+
+    // ---------------- operands ----------------
+    const uint8_t* p_tile = prm.tab[e] + (int64_t)p_row(0) * K;
+    const uint8_t* q_tile = prm.q + (int64_t)tile_row * K;
+    const uint32_t off0 = (uint32_t)((int64_t)kc_row0 * K + kc_chunk * 16);
+    const int64_t q_extent = (int64_t)(row_end - tile_row) * K;
+    const int p_up = (EP == MX_SWIGLU || EP == MX_SWIGLU_SAVE) ? prm.I - 128 : 0;
+    auto copy_op = [&](const uint8_t* tile, int up, int64_t extent, int kt, uint8_t* dst) {
+      const int64_t at = (int64_t)kt * kXBK;
+      int64_t nrec = extent - at;
+      nrec = nrec < 0 ? 0 : (nrec > kAll ? kAll : nrec);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(tile + at), (short)0, (int)(uint32_t)nrec, kBufferFlags);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t rows = (uint32_t)(i * 32 + (i >= 4 ? up : 0));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 4096), 16, off0, (int)(rows * (uint32_t)K),
+                                                 0, 0);
+      }
+    };
+    auto copy_P = [&](int kt, auto H) { copy_op(p_tile, p_up, kAll, kt, hslot(H) + wave_u * 1024); };
+    auto copy_Q = [&](int kt, auto H) { copy_op(q_tile, 0, q_extent, kt, hslot(H) + wave_u * 1024); };
+
+    // scale words (step-major): P sub-tile sn is tile rows sub_n(sn, wn) + [0, 32); Q
+    // sub-tile sm is wm * 128 + sm * 32 + [0, 32), rows past the expert clamped to its
+    // last row (their products are discarded). Step kt's words start kt * rows words in.
+    const __amdgpu_buffer_rsrc_t ps_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)prm.tab_s[e], (short)0, (int)0xFFFFFFFF, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t qs_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)prm.q_s, (short)0, (int)0xFFFFFFFF, kBufferFlags);
+    const int p_step = 4 * prm.N, q_step = 4 * R;  // bytes per K step of the two scale arrays
+    // One load serves two sub-tiles: lanes 0-31 read the row of sub-tile 2j, lanes 32-63
+    // that of sub-tile 2j + 1 (the same row index l32); raw word j of a step holds them.
+    uint32_t ps_off[2], qs_off[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      ps_off[j] = (uint32_t)(p_row(sub_n(2 * j + lhi, wn) + l32) * 4);
+      const int qr = wm * 128 + (2 * j + lhi) * 32 + l32;
+      qs_off[j] = (uint32_t)((tile_row + (qr < row_end - tile_row ? qr : row_end - tile_row - 1)) * 4);
+    }
+    // raw words of a step: [0, 1] P sub-tile pairs, [2, 3] Q sub-tile pairs
+    auto load_scales = [&](int kt, uint32_t* w) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(ps_rs, ps_off[j], kt * p_step, 0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) w[2 + j] = __builtin_amdgcn_raw_buffer_load_b32(qs_rs, qs_off[j], kt * q_step, 0);
+    };
+    // raw words -> the 8 scale words of a step ([0..3] P, [4..7] Q sub-tiles): the swap
+    // exchanges the upper half of one register with the lower half of the other, so a
+    // word and its copy give [lower, lower] (sub-tile 2j) and [upper, upper] (2j + 1);
+    // then the shift by 8 g puts block g of the step in byte 0 and 2 + g in byte 2
+    auto fan_out = [&](const uint32_t* w, uint32_t* sc) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const auto pr = __builtin_amdgcn_permlane32_swap(w[j], w[j], false, false);
+        const int base = (j < 2) ? 2 * j : 4 + 2 * (j - 2);
+        sc[base] = (uint32_t)pr[0] >> gshift;
+        sc[base + 1] = (uint32_t)pr[1] >> gshift;
+      }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+    i32x8_t fa[4], fb0[4], fb1[4];
+    auto rd = [&](const uint8_t* base, int s) -> i32x8_t {
+      const i32x4_t a = *reinterpret_cast<const i32x4_t*>(base + ck[2 * s]);
+      const i32x4_t b = *reinterpret_cast<const i32x4_t*>(base + ck[2 * s + 1]);
+      return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto read_q = [&](auto HQ, int s, i32x8_t* fb) {
+      const uint8_t* Q = hslot(HQ) + fragQ;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fb[u] = rd(Q + (u * 32) * 128, s);
+    };
+    auto read_p = [&](auto HP, int s, int sn) -> i32x8_t {
+      return rd(hslot(HP) + fragP + ((sn >> 1) * 128 + (sn & 1) * 32) * 128, s);
+    };
+    // the 16 MFMAs of slice SL with scale words sc (byte 2 SL of each); after the MFMAs of
+    // P sub-tile sn, fa[sn] takes P sub-tile sn of slice s_next of half-slot HPn
+    auto mfma_slice = [&](const i32x8_t* fb, const uint32_t* sc, auto SL, bool refill, auto HPn, int s_next) {
+      constexpr int os = 2 * decltype(SL)::value;
+#pragma unroll
+      for (int sn = 0; sn < 4; ++sn) {
+#pragma unroll
+        for (int sm = 0; sm < 4; ++sm)
+          acc[sn][sm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[sn], fb[sm], acc[sn][sm], 0, 0, os,
+                                                                          (int)sc[sn], os, (int)sc[4 + sm]);
+        if (refill) fa[sn] = read_p(HPn, s_next, sn);
+      }
+    };
+    auto interleave_a = [&]() {
+      static_for<16>([&](auto I) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      });
+    };
+    auto interleave_b = [&]() {
+      static_for<16>([&](auto I) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      });
+    };
+
+    // raw scale words of steps kt (r0) and kt+1 (r1) on entry to step kt
+    uint32_t r0[4], r1[4];
+    // K step kt, V = kt % 5. Per step the scale words of step kt+2 are loaded first, then
+    // the copies Q of step kt+2 and P of step kt+3, so when step kt+1 must have landed
+    // only P of step kt+2 (the 8 most recent operations) may be in flight, as in the
+    // per-tensor kernel. The scale loads are ordinary buffer loads, which the scheduler
+    // could otherwise move between the copies (those stay ordered among themselves
+    // through M0) and so break that count: a scheduling barrier keeps them ahead.
+    auto kstep = [&](int kt, auto V, auto FULL) {
+      constexpr int v = decltype(V)::value;
+      constexpr bool full = decltype(FULL)::value;
+      using HP = std::integral_constant<int, (2 * v) % 5>;
+      using HQ = std::integral_constant<int, (2 * v + 1) % 5>;
+      using HPn = std::integral_constant<int, (2 * v + 2) % 5>;
+      using HQn = std::integral_constant<int, (2 * v + 3) % 5>;
+      uint32_t sc[8];
+      fan_out(r0, sc);
+      read_q(HQ{}, 1, fb1);
+      mfma_slice(fb0, sc, std::integral_constant<int, 0>{}, true, HP{}, 1);
+      interleave_a();
+      if (full) wait_vm<8>();
+      else wait_vm_le(kt + 2 < nk ? 8 : 0);
+      lds_barrier();                                  // also waits for every read of step kt
+      uint32_t r2[4];
+      if (full || kt + 2 < nk) load_scales(kt + 2, r2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (full || kt + 2 < nk) copy_Q(kt + 2, HP{});  // Q of step kt+2: half-slot 2(kt+2)+1 = 2kt mod 5
+      if (full || kt + 3 < nk) copy_P(kt + 3, HQ{});  // P of step kt+3: half-slot 2(kt+3) = 2kt+1 mod 5
+      const bool next = full || kt + 1 < nk;
+      if (next) read_q(HQn{}, 0, fb0);
+      mfma_slice(fb1, sc, std::integral_constant<int, 1>{}, next, HPn{}, 0);
+      interleave_b();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r0[i] = r1[i];
+        r1[i] = r2[i];
+      }
+    };
+    auto read_first = [&](auto HP, auto HQ) {
+      read_q(HQ, 0, fb0);
+#pragma unroll
+      for (int sn = 0; sn < 4; ++sn) fa[sn] = read_p(HP, 0, sn);
+    };
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    using H2 = std::integral_constant<int, 2>;
+    using H3 = std::integral_constant<int, 3>;
+    using H4 = std::integral_constant<int, 4>;
+    using Full = std::true_type;
+    using Tail = std::false_type;
+    auto steps5 = [&](int kt0, auto FULL) {
+      static_for<5>([&](auto V) {
+        constexpr int v = decltype(V)::value;
+        if (decltype(FULL)::value || kt0 + v < nk) kstep(kt0 + v, V, FULL);
+      });
+    };
+    // Prologue: the scale words of steps 0 and 1 ahead of every copy, then the copies of
+    // steps 0-2, so that step 0's wait sees the steady state's pattern.
+    int kt = 0;
+    load_scales(0, r0);
+    if (nk > 1) load_scales(1, r1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nk >= 8) {
+      copy_P(0, H0{});
+      copy_Q(0, H1{});
+      copy_P(1, H2{});
+      copy_Q(1, H3{});
+      copy_P(2, H4{});
+      wait_vm<24>();  // the scale words and step 0's copies complete
+      lds_barrier();
+      read_first(H0{}, H1{});
+      for (; kt + 7 < nk; kt += 5) steps5(kt, Full{});  // the copies of all five steps exist
+    } else {
+      copy_P(0, H0{});
+      copy_Q(0, H1{});
+      if (nk > 1) {
+        copy_P(1, H2{});
+        copy_Q(1, H3{});
+      }
+      if (nk > 2) copy_P(2, H4{});
+      wait_vm_le((nk > 1) * 16 + (nk > 2) * 8);  // step 0 complete
+      lds_barrier();
+      read_first(H0{}, H1{});
+    }
+    for (; kt < nk; kt += 5) steps5(kt, Tail{});
+    // every wavefront is done with every half-slot before the epilogue uses LDS
+    lds_barrier();
+
+    // ---------------- epilogue ----------------
+    // bf16 blocks of 256 rows x 128 columns through LDS, as in the bf16 forward kernel:
+    // 256-byte rows, chunk c of row r at c ^ (r & 15), rows 0-127 in the first array of a
+    // pair and 128-255 in the second; 4 whole rows leave per store instruction, rows
+    // past the expert dropped by the range check.
+    int ln = lane, wv = __builtin_amdgcn_readfirstlane(wave);
+    asm volatile("" : "+v"(ln));  // keep the lane offsets inside the epilogue
+    const int em = wv >> 1, en = wv & 1, e32 = ln & 31, ehi = ln >> 5;
+    const int valid = min(row_end - tile_row, kBM);
+    auto put = [&](uint8_t* arr0, uint8_t* arr1, int sm, int sq, int i4, uint2 v) __attribute__((always_inline)) {
+      uint8_t* arr = em ? arr1 : arr0;
+      const int rr = sm * 32 + e32;
+      const int ch = en * 8 + sq * 4 + i4;
+      *reinterpret_cast<uint2*>(arr + rr * 256 + ((ch ^ (rr & 15)) << 4) + ehi * 8) = v;
+    };
+    auto drain = [&](const uint8_t* arr, bf16_t* dst, int64_t ld) __attribute__((always_inline)) {
+      const int64_t ldb = ld * 2;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(dst + (int64_t)tile_row * ld), (short)0, (int)(uint32_t)(valid * ldb), kBufferFlags);
+      const int pc = ln & 15;
+      const uint32_t vo = (uint32_t)((ln >> 4) * ldb + pc * 16);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = (wv & 1) * 64 + 4 * i + (ln >> 4);
+        const v4u32 val = *reinterpret_cast<const v4u32*>(arr + rl * 256 + ((pc ^ (rl & 15)) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(val, rs, vo, (int)((wv * 64 + 4 * i) * ldb), 0);
+      }
+    };
+    auto acc_block = [&](int b, uint8_t* arr0, uint8_t* arr1) __attribute__((always_inline)) {
+#pragma unroll
+      for (int sm = 0; sm < 4; ++sm)
+#pragma unroll
+        for (int sq = 0; sq < 2; ++sq)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int sn = 2 * b + sq;
+            put(arr0, arr1, sm, sq, i4,
+                make_uint2(pack_bf16x2(acc[sn][sm][i4 * 4 + 0], acc[sn][sm][i4 * 4 + 1]),
+                           pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3])));
+          }
+    };
+    if constexpr (EP == MX_STORE) {
+      acc_block(0, sH0, sH1);
+      acc_block(1, sH2, sH3);
+      lds_barrier();
+      bf16_t* c0 = reinterpret_cast<bf16_t*>(prm.c) + (int64_t)nt * kBN;
+      drain(wv < 2 ? sH0 : sH1, c0, prm.N);
+      drain(wv < 2 ? sH2 : sH3, c0 + 128, prm.N);
+      lds_barrier();  // read out before the next tile's copies land
+    } else {
+      constexpr bool save = EP == MX_SWIGLU_SAVE;
+#pragma unroll
+      for (int sm = 0; sm < 4; ++sm) {
+        const int64_t mg = (int64_t)tile_row + wm * 128 + sm * 32 + l32;
+        const bool live = mg < row_end;
+        const float p = prm.prob[live ? mg : row_end - 1];
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn) {
+          // h for the 32 columns of sub-tile sn: 16 values here, 16 in lane ^ 32
+          float h[16];
+          float amax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            h[i] = silu_f(acc[sn][sm][i]) * acc[sn + 2][sm][i] * p;
+            amax = fmaxf(amax, fabsf(h[i]));
+          }
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          const int sx = mx_scale_exponent(amax);
+          if constexpr (save) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+              put(sH0, sH1, sm, sn, i4,
+                  make_uint2(pack_bf16x2(h[i4 * 4 + 0], h[i4 * 4 + 1]), pack_bf16x2(h[i4 * 4 + 2], h[i4 * 4 + 3])));
+          }
+          if (live) {
+            const int64_t col0 = (int64_t)nt * 128 + wn * 64 + sn * 32;
+            uint8_t* C = reinterpret_cast<uint8_t*>(prm.c) + mg * prm.I + col0;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+              *reinterpret_cast<uint32_t*>(C + i4 * 8 + lhi * 4) =
+                  e4m3_pack4(ldexpf(h[i4 * 4], -sx), ldexpf(h[i4 * 4 + 1], -sx), ldexpf(h[i4 * 4 + 2], -sx),
+                             ldexpf(h[i4 * 4 + 3], -sx));
+            // step-major: word nt * R + mg (the down GEMM's K step nt), byte wn * 2 + sn
+            if (lhi == 0) prm.c_s[((int64_t)nt * R + mg) * 4 + wn * 2 + sn] = (uint8_t)(sx + 127);
+          }
+        }
+      }
+      if constexpr (save) {  // h (bf16, in sH0/sH1), z's gate half (sH2/sH3), then z's up half
+        const int64_t I2 = 2 * (int64_t)prm.I;
+        acc_block(0, sH2, sH3);
+        lds_barrier();
+        drain(wv < 2 ? sH0 : sH1, reinterpret_cast<bf16_t*>(prm.h_save) + (int64_t)nt * 128, prm.I);
+        drain(wv < 2 ? sH2 : sH3, reinterpret_cast<bf16_t*>(prm.z_save) + (int64_t)nt * 128, I2);
+        lds_barrier();
+        acc_block(1, sH0, sH1);
+        lds_barrier();
+        drain(wv < 2 ? sH0 : sH1, reinterpret_cast<bf16_t*>(prm.z_save) + prm.I + (int64_t)nt * 128, I2);
+      }
+      lds_barrier();  // read out before the next tile's copies land
+    }
+  }
+}
+
+// pt: per-tensor FP8; else MXFP8 with step-major scales (sm, the wide-step kernel) or
+// public-layout scales (the 64-value-step kernel)
+static moe_status launch(int ep, bool pt, const MxParams& p, int64_t max_tiles, hipStream_t s, const char* what,
+                         bool sm = false) {
   if (max_tiles <= 0) return MOE_OK;
   int64_t grid = num_cus();
   if (max_tiles < grid) grid = max_tiles;
   const dim3 g((unsigned)grid), b(256);
-  if (ep == MX_SWIGLU && !pt && p.z_save) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU_SAVE, MxParams>), g, b, 0, s, p);
-  else if (ep == MX_SWIGLU && !pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU, MxParams>), g, b, 0, s, p);
-  else if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_SWIGLU>), g, b, 0, s, p);
-  else if (!pt) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_STORE, MxParams>), g, b, 0, s, p);
-  else hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_STORE>), g, b, 0, s, p);
+  if (pt) {
+    if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_SWIGLU>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_STORE>), g, b, 0, s, p);
+  } else if (sm) {
+    if (ep == MX_SWIGLU && p.z_save) hipLaunchKernelGGL((grouped_gemm_mxw_kernel<MX_SWIGLU_SAVE>), g, b, 0, s, p);
+    else if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_mxw_kernel<MX_SWIGLU>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((grouped_gemm_mxw_kernel<MX_STORE>), g, b, 0, s, p);
+  } else {
+    if (ep == MX_SWIGLU && p.z_save) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU_SAVE, MxParams>), g, b, 0, s, p);
+    else if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU, MxParams>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_STORE, MxParams>), g, b, 0, s, p);
+  }
   return check_launch(what);
 }
 
@@ -865,7 +1283,7 @@ static moe_status check_mx_shape(int E, int H, int I, const char* what) {
 
 moe_status gate_up(int E, int64_t R, int H, int I, const uint8_t* x, const uint8_t* x_scale, const void* const* w,
                    const uint8_t* const* w_scale, const int32_t* offsets, const float* prob, uint8_t* h,
-                   uint8_t* h_scale, hipStream_t s, void* z_save, void* h_save) {
+                   uint8_t* h_scale, hipStream_t s, void* z_save, void* h_save, bool step_major) {
   moe_status st = check_mx_shape(E, H, I, "moe_grouped_gate_up_swiglu");
   if (st != MOE_OK) return st;
   MxParams p;
@@ -889,12 +1307,12 @@ moe_status gate_up(int E, int64_t R, int H, int I, const uint8_t* x, const uint8
   p.z_save = z_save;
   p.h_save = h_save;
   const int64_t mtiles = (R + kBM - 1) / kBM + E;
-  return launch(MX_SWIGLU, false, p, mtiles * p.n_tiles, s, "MXFP8 gate_up + ScaledSwiGLU");
+  return launch(MX_SWIGLU, false, p, mtiles * p.n_tiles, s, "MXFP8 gate_up + ScaledSwiGLU", step_major);
 }
 
 static moe_status down(int E, int64_t R, int H, int I, const uint8_t* h, const uint8_t* h_scale,
                        const uint8_t* const* w, const uint8_t* const* w_scale, const int32_t* offsets, void* y,
-                       hipStream_t s) {
+                       hipStream_t s, bool step_major) {
   MxParams p;
   std::memset(&p, 0, sizeof(p));
   for (int e = 0; e < E; ++e) {
@@ -912,11 +1330,14 @@ static moe_status down(int E, int64_t R, int H, int I, const uint8_t* h, const u
   p.I = I;
   p.n_tiles = H / kBN;
   const int64_t mtiles = (R + kBM - 1) / kBM + E;
-  return launch(MX_STORE, false, p, mtiles * p.n_tiles, s, "MXFP8 down");
+  return launch(MX_STORE, false, p, mtiles * p.n_tiles, s, "MXFP8 down", step_major);
 }
 
 static size_t a256(size_t x) { return align_up(x, 256); }
 
+// MXFP8 forward on the wide-step kernels, every scale array step-major. Workspace: x's
+// codes and scales (bf16 x) or its scales converted (MXFP8 x), the same per expert for
+// W1 and W2, then h's codes and scales.
 moe_status forward(const moe_mlp_desc& d, int64_t R, const void* x_perm, const uint8_t* x_perm_scale,
                    const void* const* w_gate_up, const void* const* w_down, const uint8_t* const* w_gate_up_scale,
                    const uint8_t* const* w_down_scale, const int32_t* offsets, const float* prob_perm,
@@ -925,53 +1346,61 @@ moe_status forward(const moe_mlp_desc& d, int64_t R, const void* x_perm, const u
   const int E = d.E, H = d.H, I = d.I;
   moe_status st = check_mx_shape(E, H, I, "moe_grouped_mlp_fwd");
   if (st != MOE_OK) return st;
-  // activations: quantised in the call when given as bf16
+  // activations: quantised in the call when given as bf16, else their scales converted
   const uint8_t* xq = reinterpret_cast<const uint8_t*>(x_perm);
-  const uint8_t* xs = x_perm_scale;
+  uint8_t* xs = nullptr;
   if (d.act == MOE_BF16) {
     uint8_t* q = ws;
     ws += a256((size_t)R * H);
-    uint8_t* qs = ws;
+    xs = ws;
     ws += a256((size_t)R * H / 32);
-    if ((st = launch_mxfp8_quantize(x_perm, R, H, q, qs, s)) != MOE_OK) return st;
+    if ((st = launch_mxfp8_quantize_step_major(x_perm, R, H, q, xs, s)) != MOE_OK) return st;
     xq = q;
-    xs = qs;
+  } else {
+    xs = ws;
+    ws += a256((size_t)R * H / 32);
+    uint8_t* dst[1] = {xs};
+    if ((st = launch_mx_scales_step_major(&x_perm_scale, dst, 1, R, H, s)) != MOE_OK) return st;
   }
-  // weights: bf16 master weights quantised in the call, or given as MXFP8
+  // weights: bf16 master weights quantised in the call, or MXFP8 with their scales converted
   const uint8_t* w1q[kMaxE];
-  const uint8_t* w1s[kMaxE];
+  uint8_t* w1s[kMaxE];
   const uint8_t* w2q[kMaxE];
-  const uint8_t* w2s[kMaxE];
+  uint8_t* w2s[kMaxE];
   for (int e = 0; e < E; ++e) {
     if (d.wt == MOE_BF16) {
       uint8_t* a = ws;
       ws += a256((size_t)2 * I * H);
-      uint8_t* as = ws;
+      w1s[e] = ws;
       ws += a256((size_t)2 * I * H / 32);
       uint8_t* b = ws;
       ws += a256((size_t)H * I);
-      uint8_t* bs = ws;
+      w2s[e] = ws;
       ws += a256((size_t)H * I / 32);
-      if ((st = launch_mxfp8_quantize(w_gate_up[e], 2 * I, H, a, as, s)) != MOE_OK) return st;
-      if ((st = launch_mxfp8_quantize(w_down[e], H, I, b, bs, s)) != MOE_OK) return st;
+      if ((st = launch_mxfp8_quantize_step_major(w_gate_up[e], 2 * I, H, a, w1s[e], s)) != MOE_OK) return st;
+      if ((st = launch_mxfp8_quantize_step_major(w_down[e], H, I, b, w2s[e], s)) != MOE_OK) return st;
       w1q[e] = a;
-      w1s[e] = as;
       w2q[e] = b;
-      w2s[e] = bs;
     } else {
       w1q[e] = reinterpret_cast<const uint8_t*>(w_gate_up[e]);
-      w1s[e] = w_gate_up_scale[e];
       w2q[e] = reinterpret_cast<const uint8_t*>(w_down[e]);
-      w2s[e] = w_down_scale[e];
+      w1s[e] = ws;
+      ws += a256((size_t)2 * I * H / 32);
+      w2s[e] = ws;
+      ws += a256((size_t)H * I / 32);
     }
+  }
+  if (d.wt != MOE_BF16) {
+    if ((st = launch_mx_scales_step_major(w_gate_up_scale, w1s, E, 2 * (int64_t)I, H, s)) != MOE_OK) return st;
+    if ((st = launch_mx_scales_step_major(w_down_scale, w2s, E, H, I, s)) != MOE_OK) return st;
   }
   uint8_t* hq = ws;
   ws += a256((size_t)R * I);
   uint8_t* hs = ws;
   st = gate_up(E, R, H, I, xq, xs, reinterpret_cast<const void* const*>(w1q), w1s, offsets, prob_perm, hq, hs, s,
-               z_save, h_save);
+               z_save, h_save, true);
   if (st != MOE_OK) return st;
-  return down(E, R, H, I, hq, hs, w2q, w2s, offsets, y_perm, s);
+  return down(E, R, H, I, hq, hs, w2q, w2s, offsets, y_perm, s, true);
 }
 
 // Per-tensor FP8 forward. Workspace: scale words [x, W1 of each expert, W2 of each

@@ -23,6 +23,15 @@ size_t router_bwd_workspace_bytes(int64_t T, int H, int E);  // dW token-chunk p
 // mxfp8 quantisation launcher used by the forward (weights and activations)
 moe_status launch_mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,
                                  uint8_t* e8m0, void* stream);
+// the same codes, scales written step-major: the 4 scale bytes of 128 values of row r
+// form one 32-bit word; the words of K step k of all rows are contiguous (word k * rows
+// + r). cols % 128 == 0. This is the scale layout the wide-step MXFP8 GEMM reads.
+moe_status launch_mxfp8_quantize_step_major(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,
+                                            uint8_t* e8m0, void* stream);
+// public-layout scales [rows][cols / 32] of n tensors of one shape -> step-major (4-byte
+// aligned pointers, n <= MOE_MAX_EXPERTS, cols % 128 == 0)
+moe_status launch_mx_scales_step_major(const uint8_t* const* src, uint8_t* const* dst, int n, int64_t rows,
+                                       int64_t cols, void* stream);
 
 // column-wise (token-axis) MXFP8 of x [R, C] per expert (rule of mxfp8_quantize_colwise);
 // offsets NULL: one expert of R rows; kofs NULL: the padded offsets are not written.

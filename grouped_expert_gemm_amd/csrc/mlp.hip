@@ -53,8 +53,9 @@ size_t mlp_fwd_workspace_bytes(const moe_mlp_desc& d, int64_t R) {
     case MOE_BF16: return (d.save_for_bwd ? 0 : a256(R * I * 2)) + grouped_gemm_workspace_bytes();
     case MOE_MXFP8: {
       size_t b = 0;
-      if (d.act == MOE_BF16) b += a256(R * H) + a256(R * H / 32);
-      if (d.wt == MOE_BF16) b += E * (a256(2 * I * H) + a256(2 * I * H / 32) + a256(H * I) + a256(H * I / 32));
+      // codes and step-major scales of what is given in bf16; converted scales otherwise
+      b += (d.act == MOE_BF16 ? a256(R * H) : 0) + a256(R * H / 32);
+      b += E * ((d.wt == MOE_BF16 ? a256(2 * I * H) + a256(H * I) : 0) + a256(2 * I * H / 32) + a256(H * I / 32));
       b += a256(R * I) + a256(R * I / 32);  // h as MXFP8
       return b;
     }

@@ -11,9 +11,14 @@
 
 namespace moe {
 
+// step_rows == 0: scale byte of block b of row r at r * cols32 + b (the public layout);
+// step_rows == rows: "step-major", the 4 blocks of 128 values of row r form one 32-bit
+// word, words of K step k (all rows) contiguous: byte ((b / 4) * rows + r) * 4 + b % 4
+// (the layout the wide-step MXFP8 GEMM reads, 32 rows of a sub-tile in one 128-byte run)
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint4* __restrict__ in, int64_t nblocks,
                                                              uint2* __restrict__ codes,
-                                                             uint8_t* __restrict__ scales) {
+                                                             uint8_t* __restrict__ scales, int64_t cols32,
+                                                             int64_t step_rows) {
   const int64_t lane_global = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   // the loop trip count is uniform across a wavefront (stride and the start differ by
@@ -39,13 +44,21 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint4* __rest
     if (live) {
       codes[q] = make_uint2(e4m3_pack4(ldexpf(f[0], -s), ldexpf(f[1], -s), ldexpf(f[2], -s), ldexpf(f[3], -s)),
                             e4m3_pack4(ldexpf(f[4], -s), ldexpf(f[5], -s), ldexpf(f[6], -s), ldexpf(f[7], -s)));
-      if ((q & 3) == 0) scales[q >> 2] = (uint8_t)(s + 127);
+      if ((q & 3) == 0) {
+        const int64_t b = q >> 2;
+        int64_t at = b;
+        if (step_rows) {
+          const int64_t r = b / cols32, c = b - r * cols32;
+          at = ((c >> 2) * step_rows + r) * 4 + (c & 3);
+        }
+        scales[at] = (uint8_t)(s + 127);
+      }
     }
   }
 }
 
-moe_status launch_mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,
-                                 uint8_t* e8m0, void* stream) {
+static moe_status quantize_rows(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3, uint8_t* e8m0,
+                                void* stream, bool step_major) {
   const int64_t nblocks = rows * (cols / 32);
   if (nblocks == 0) return MOE_OK;
   const int threads = 256;
@@ -53,8 +66,69 @@ moe_status launch_mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols
   const int64_t cap = (int64_t)num_cus() * 16;
   const unsigned grid = (unsigned)(want < cap ? want : cap);
   hipLaunchKernelGGL(mxfp8_quantize_kernel, dim3(grid), dim3(threads), 0, as_stream(stream),
-                     (const uint4*)in_bf16, nblocks, (uint2*)e4m3, e8m0);
+                     (const uint4*)in_bf16, nblocks, (uint2*)e4m3, e8m0, cols / 32, step_major ? rows : 0);
   return check_launch("mxfp8_quantize");
+}
+
+moe_status launch_mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,
+                                 uint8_t* e8m0, void* stream) {
+  return quantize_rows(in_bf16, rows, cols, e4m3, e8m0, stream, false);
+}
+
+moe_status launch_mxfp8_quantize_step_major(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,
+                                            uint8_t* e8m0, void* stream) {
+  if (cols % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "mxfp8 step-major scales need cols % 128 == 0");
+  return quantize_rows(in_bf16, rows, cols, e4m3, e8m0, stream, true);
+}
+
+// Public-layout scales [rows][cols / 32] -> step-major ([cols / 128][rows] 32-bit words),
+// for up to MOE_MAX_EXPERTS tensors of one shape (blockIdx.z): a transpose of a
+// [rows][steps] word matrix through a 64-row x 16-step LDS tile, read 64 bytes of a row
+// at a time and written 256 bytes of a step at a time.
+struct ScaleTables {
+  const uint32_t* src[MOE_MAX_EXPERTS];
+  uint32_t* dst[MOE_MAX_EXPERTS];
+};
+
+__global__ __launch_bounds__(256) void mx_scales_step_major_kernel(const ScaleTables tabs, int64_t rows,
+                                                                   int steps) {
+  __shared__ uint32_t tile[16][65];
+  const uint32_t* src = tabs.src[blockIdx.z];
+  uint32_t* dst = tabs.dst[blockIdx.z];
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int s0 = blockIdx.y * 16;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * 256 + tid;
+    const int r = idx >> 4, st = idx & 15;
+    if (r0 + r < rows && s0 + st < steps) tile[st][r] = src[(r0 + r) * steps + s0 + st];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * 256 + tid;
+    const int st = idx >> 6, r = idx & 63;
+    if (r0 + r < rows && s0 + st < steps) dst[(int64_t)(s0 + st) * rows + r0 + r] = tile[st][r];
+  }
+}
+
+moe_status launch_mx_scales_step_major(const uint8_t* const* src, uint8_t* const* dst, int n, int64_t rows,
+                                       int64_t cols, void* stream) {
+  if (cols % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "mxfp8 step-major scales need cols % 128 == 0");
+  if (n < 1 || n > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "mxfp8 scale conversion: bad tensor count");
+  if (rows == 0) return MOE_OK;
+  ScaleTables t;
+  for (int i = 0; i < n; ++i) {
+    if (!aligned(src[i], 4) || !aligned(dst[i], 4))
+      return fail(MOE_ERR_INVALID_ARG, "mxfp8 scale conversion: scales must be 4-byte aligned");
+    t.src[i] = reinterpret_cast<const uint32_t*>(src[i]);
+    t.dst[i] = reinterpret_cast<uint32_t*>(dst[i]);
+  }
+  const int steps = (int)(cols / 128);
+  const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((steps + 15) / 16), (unsigned)n);
+  hipLaunchKernelGGL(mx_scales_step_major_kernel, grid, dim3(256), 0, as_stream(stream), t, rows, steps);
+  return check_launch("mxfp8 scale conversion");
 }
 
 // Column-wise (per expert, along the token axis) MXFP8: a workgroup takes up to four
