@@ -44,7 +44,7 @@ def dev_bf16(torch, np, bits):
 class Layer:
     """Device buffers and the C calls of one forward (and optionally backward) step."""
 
-    def __init__(self, w, inp, backward: bool, mx: bool = False):
+    def __init__(self, w, inp, backward: bool, mx: bool = False, prequant: bool = False):
         import numpy as np
         import torch
 
@@ -96,10 +96,32 @@ class Layer:
             self.ws_bwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_BWD, self.desc, R), dtype=torch.uint8,
                                       device=dev)
         self.mx = mx
+        self.fs1 = self.fs2 = None
         if mx:  # the whole grouped MLP forward in MXFP8 (one call), saving z and h when backward
-            self.desc_fwd = _lib.MlpDesc(E, H, I, _lib.MOE_MXFP8, _lib.MOE_BF16, _lib.MOE_BF16, int(backward))
+            wt = _lib.MOE_BF16
+            if prequant:
+                # weights quantised once, outside the timed steps (as a training loop would once
+                # per optimizer step): row-wise for the forward, packed for the backward
+                wt = _lib.MOE_MXFP8
+                self.q1, self.qs1 = moe.mxfp8_quantize(self.w1)
+                self.q2, self.qs2 = moe.mxfp8_quantize(self.w2)
+                self.t1, self._k1 = _lib.ptr_table([self.q1[e].data_ptr() for e in range(E)])
+                self.t2, self._k2 = _lib.ptr_table([self.q2[e].data_ptr() for e in range(E)])
+                self.fs1, self._k5 = _lib.ptr_table([self.qs1[e].data_ptr() for e in range(E)])
+                self.fs2, self._k6 = _lib.ptr_table([self.qs2[e].data_ptr() for e in range(E)])
+                if backward:
+                    self.pk1 = [moe.mxfp8_pack_weight_bwd(self.w1[e]) for e in range(E)]
+                    self.pk2 = [moe.mxfp8_pack_weight_bwd(self.w2[e]) for e in range(E)]
+                    self.b1, self._k7 = _lib.ptr_table([t.data_ptr() for t in self.pk1])
+                    self.b2, self._k8 = _lib.ptr_table([t.data_ptr() for t in self.pk2])
+                    self.desc = _lib.MlpDesc(E, H, I, _lib.MOE_MXFP8, _lib.MOE_BF16, _lib.MOE_MXFP8, 1)
+                    self.ws_bwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_BWD, self.desc, R),
+                                              dtype=torch.uint8, device=dev)
+            self.desc_fwd = _lib.MlpDesc(E, H, I, _lib.MOE_MXFP8, _lib.MOE_BF16, wt, int(backward))
             self.ws_fwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_FWD, self.desc_fwd, R), dtype=torch.uint8,
                                       device=dev)
+        if not (mx and prequant and backward):
+            self.b1, self.b2 = self.t1, self.t2
         self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self.ev = []
 
@@ -115,7 +137,7 @@ class Layer:
                                    p(self.src), p(self.ws_perm), self.ws_perm.numel(), s))
         if self.mx:
             c("mlp fwd", L.moe_grouped_mlp_fwd(ctypes.byref(self.desc_fwd), R, p(self.x_perm), None, self.t1, self.t2,
-                                               None, None, p(self.offsets), p(self.prob_perm), p(self.y),
+                                               self.fs1, self.fs2, p(self.offsets), p(self.prob_perm), p(self.y),
                                                p(self.z) if self.z is not None else None, p(self.h),
                                                p(self.ws_fwd), self.ws_fwd.numel(), s))
         else:
@@ -137,7 +159,7 @@ class Layer:
             c("dOut gather", L.moe_permute(p(self.dout), None, BF, T, H, E, k, None, None, 1, p(self.dy), None,
                                            None, None, None, p(self.rmap), None, None, 0, s))
             c("mlp bwd", L.moe_grouped_mlp_bwd(ctypes.byref(self.desc), R, p(self.dy), p(self.x_perm), p(self.z),
-                                               p(self.h), p(self.prob_perm), self.t1, self.t2, p(self.offsets),
+                                               p(self.h), p(self.prob_perm), self.b1, self.b2, p(self.offsets),
                                                p(self.dx_perm), self.d1, self.d2, p(self.dprob_perm),
                                                p(self.ws_bwd), self.ws_bwd.numel(), s))
             c("dx combine", L.moe_unpermute_combine(p(self.dx_perm), BF, p(self.rmap), None, T, H, k, p(self.dx),
@@ -443,26 +465,29 @@ def cpu_baseline(inp, w, seconds):
                       f"H={w.H}, I={w.I}); {t_all:.1f} s of oracle time, {os.cpu_count()} host CPUs visible"}
 
 
-def fwd_bwd_measure(steps, warmup, mx=False):
+def fwd_bwd_measure(steps, warmup, mx=False, prequant=False):
     """The whole layer forward + backward step (route ... combine, dOut gather, grouped
     MLP backward, dx combine, dprob gather) at the Mixtral fwd+bwd shape; mx: the grouped
-    MLP forward and backward in MXFP8 (the forward saving z and h in bf16)."""
+    MLP forward and backward in MXFP8 (the forward saving z and h in bf16); prequant: the
+    MXFP8 weights quantised once outside the timed steps."""
     from moe_inputs import WORKLOADS, make_inputs
 
     wb = WORKLOADS["mixtral_fwd_bwd"]
     t0 = time.perf_counter()
     inpb = make_inputs(wb, want_float=False)
     log(f"inputs {wb.name}: {time.perf_counter() - t0:.1f} s")
-    lb = Layer(wb, inpb, backward=True, mx=mx)
+    lb = Layer(wb, inpb, backward=True, mx=mx, prequant=prequant)
     msb = time_steps(lb, steps, warmup)
     flopb = 3.0 * wb.gemm_flop_fwd()
     vb = flopb / (msb * 1e-3) / 1e12
     peak = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
-    log(f"fwd+bwd step{' (MXFP8)' if mx else ''} {msb:.3f} ms -> {vb:.1f} TFLOP/s")
+    log(f"fwd+bwd step{' (MXFP8)' if mx else ''}{' prequant' if prequant else ''} {msb:.3f} ms -> {vb:.1f} TFLOP/s")
     rec = {"workload": "mixtral_fwd_bwd", "T": wb.T, "value": round(vb, 2), "unit": "TFLOP/s",
            "ms_per_step": round(msb, 4), "flop_per_step": flopb}
     if mx:
-        rec.update(compute="mxfp8", pct_of_fp8_peak=round(100 * vb / peak, 2))
+        rec.update(compute="mxfp8", pct_of_fp8_peak=round(100 * vb / peak, 2),
+                   weights=("MXFP8, quantised once outside the step (row-wise for the forward, packed for the "
+                            "backward)" if prequant else "bf16 master weights, quantised inside every step"))
     else:
         rec["pct_of_bf16_peak"] = round(100 * vb / peak, 2)
     return rec
@@ -520,6 +545,8 @@ def only_measurement(which, steps, warmup):
         return fwd_bwd_measure(steps, warmup)
     if which == "mx_fwd_bwd":
         return fwd_bwd_measure(steps, warmup, mx=True)
+    if which == "mx_fwd_bwd_pre":
+        return fwd_bwd_measure(steps, warmup, mx=True, prequant=True)
     if which == "bwd":
         return bwd_measure(steps)
     if which == "qwen3":
@@ -553,7 +580,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip the MXFP8 and Qwen3 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["fwd_bwd", "mx_fwd_bwd", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise", "permute"],
+    ap.add_argument("--only", choices=["fwd_bwd", "mx_fwd_bwd", "mx_fwd_bwd_pre", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise", "permute"],
                     help="run one measurement and print its record (kernel traces of that workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
@@ -640,6 +667,9 @@ def main():
         result["fwd_bwd"] = fwd_bwd_measure(max(3, args.steps // 2), args.warmup)
         torch.cuda.empty_cache()
         result["mxfp8_fwd_bwd"] = fwd_bwd_measure(max(3, args.steps // 2), args.warmup, mx=True)
+        torch.cuda.empty_cache()
+        result["mxfp8_fwd_bwd_prequantised"] = fwd_bwd_measure(max(3, args.steps // 2), args.warmup, mx=True,
+                                                               prequant=True)
         torch.cuda.empty_cache()
         result["mlp_bwd"] = bwd_measure()
         torch.cuda.empty_cache()

@@ -21,7 +21,7 @@ from ._lib import MOE_BF16, MOE_F32, MOE_FP8, MOE_MXFP8, MlpDesc, MoeError, chec
 
 __all__ = [
     "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
-    "fp8_tensor_quantize", "mxfp8_quantize_colwise",
+    "fp8_tensor_quantize", "mxfp8_quantize_colwise", "mxfp8_pack_weight_bwd",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu", "gemm_workspace",
     "workspace_size", "MoeError", "lib",
     "MOE_F32", "MOE_BF16", "MOE_MXFP8", "MOE_FP8",
@@ -204,6 +204,18 @@ def mxfp8_quantize_colwise(x: torch.Tensor, offsets: torch.Tensor, pad: int = 32
     return codes, scales, kofs
 
 
+def mxfp8_pack_weight_bwd(w: torch.Tensor) -> torch.Tensor:
+    """bf16 weight [rows, cols] -> packed MXFP8 for moe_grouped_mlp_bwd (uint8, rows * cols
+    * 33 / 32 bytes: the codes of w^T quantised along rows, then the step-major scales)."""
+    _need_cuda(w)
+    if w.dtype != torch.bfloat16 or w.dim() != 2:
+        raise ValueError("mxfp8_pack_weight_bwd takes a 2-D bfloat16 weight")
+    rows, cols = w.shape
+    packed = torch.empty(rows * cols + rows * cols // 32, dtype=torch.uint8, device=w.device)
+    check("mxfp8_pack_weight_bwd", lib().mxfp8_pack_weight_bwd(_p(w), rows, cols, _p(packed), _stream(w.device)))
+    return packed
+
+
 def _experts(w):
     """A [E, ...] tensor or a list of per-expert tensors -> list of per-expert tensors."""
     if isinstance(w, torch.Tensor):
@@ -261,12 +273,15 @@ def moe_grouped_mlp_fwd(x_perm: torch.Tensor, w_gate_up, w_down, offsets: torch.
 
 def moe_grouped_mlp_bwd(dy_perm, x_perm, z, h, prob_perm, w_gate_up, w_down, offsets, compute: str = "bf16",
                         dw_gate_up=None, dw_down=None, workspace: torch.Tensor | None = None):
-    """Grouped MLP backward. Returns (dx_perm, dw_gate_up [E, 2I, H], dw_down [E, H, I], dprob_perm [R])."""
+    """Grouped MLP backward. Returns (dx_perm, dw_gate_up [E, 2I, H], dw_down [E, H, I], dprob_perm [R]).
+
+    With compute="mxfp8" the weights may be bf16 or packed by mxfp8_pack_weight_bwd (uint8)."""
     w1 = _experts(w_gate_up)
     w2 = _experts(w_down)
     E = len(w1)
-    twoI, H = w1[0].shape
-    I = twoI // 2
+    H = x_perm.shape[1]
+    I = z.shape[1] // 2
+    twoI = 2 * I
     R = x_perm.shape[0]
     dev = x_perm.device
     _need_cuda(dy_perm, x_perm, z, h, prob_perm, offsets, *w1, *w2)

@@ -1579,10 +1579,12 @@ BwdLayout bwd_layout(const moe_mlp_desc& d, int64_t R) {
   auto take = [&](size_t bytes) { const size_t at = o; o += a256(bytes); return at; };
   L.dyq = take(R * H);
   L.dys = take(R * H / 32);
-  L.w2c = take(E * I * H);
-  L.w2s = take(E * I * H / 32);
-  L.w1c = take(E * H * 2 * I);
-  L.w1s = take(E * H * 2 * I / 32);
+  if (d.wt == MOE_BF16) {  // column-wise weight copies (packed weights bring their own)
+    L.w2c = take(E * I * H);
+    L.w2s = take(E * I * H / 32);
+    L.w1c = take(E * H * 2 * I);
+    L.w1s = take(E * H * 2 * I / 32);
+  }
   L.dh = take(R * I * 2);
   L.dz = take(R * 2 * I * 2);
   L.dzq = take(R * 2 * I);
@@ -1621,17 +1623,28 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
   const size_t w2n = (size_t)I * H, w1n = (size_t)H * 2 * I;
   const int64_t mtiles = (R + kBM - 1) / kBM + E;
 
-  // dH = dY W2_e
-  if ((st = launch_mxfp8_quantize(dy, R, H, dyq, dys, s)) != MOE_OK) return st;
-  for (int e = 0; e < E; ++e)
-    if ((st = launch_mxfp8_colwise(w_down[e], H, I, 1, nullptr, 32, H, ws + L.w2c + e * w2n,
-                                   ws + L.w2s + e * w2n / 32, nullptr, s)) != MOE_OK)
-      return st;
+  // Weights along the data gradients' K axes: W2_e along H ([I][H] codes), W1_e along 2I
+  // ([H][2I]), step-major scales; quantised here from bf16 master weights, or packed by
+  // the caller (mxfp8_pack_weight_bwd: codes, then the scales).
+  const bool packed = d.wt == MOE_MXFP8;
+  auto w2_codes = [&](int e) -> const uint8_t* {
+    return packed ? reinterpret_cast<const uint8_t*>(w_down[e]) : ws + L.w2c + e * w2n;
+  };
+  auto w1_codes = [&](int e) -> const uint8_t* {
+    return packed ? reinterpret_cast<const uint8_t*>(w_gate_up[e]) : ws + L.w1c + e * w1n;
+  };
+  // dH = dY W2_e (the data gradients run on the wide-step kernel: step-major scales)
+  if ((st = launch_mxfp8_quantize_step_major(dy, R, H, dyq, dys, s)) != MOE_OK) return st;
+  if (!packed)
+    for (int e = 0; e < E; ++e)
+      if ((st = launch_mxfp8_colwise(w_down[e], H, I, 1, nullptr, 32, H, ws + L.w2c + e * w2n,
+                                     ws + L.w2s + e * w2n / 32, nullptr, s, true)) != MOE_OK)
+        return st;
   MxParams p;
   std::memset(&p, 0, sizeof(p));
   for (int e = 0; e < E; ++e) {
-    p.tab[e] = ws + L.w2c + e * w2n;
-    p.tab_s[e] = ws + L.w2s + e * w2n / 32;
+    p.tab[e] = w2_codes(e);
+    p.tab_s[e] = packed ? w2_codes(e) + w2n : ws + L.w2s + e * w2n / 32;
   }
   p.q = dyq;
   p.q_s = dys;
@@ -1643,7 +1656,7 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
   p.E = E;
   p.I = I;
   p.n_tiles = I / kBN;
-  if ((st = launch(MX_STORE, false, p, mtiles * p.n_tiles, s, "MXFP8 down dgrad")) != MOE_OK) return st;
+  if ((st = launch(MX_STORE, false, p, mtiles * p.n_tiles, s, "MXFP8 down dgrad", true)) != MOE_OK) return st;
 
   // dZ, dprob
   if (R > 0) {
@@ -1652,14 +1665,15 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
   }
 
   // dx = dZ W1_e
-  if ((st = launch_mxfp8_quantize(dz, R, 2 * I, dzq, dzs, s)) != MOE_OK) return st;
-  for (int e = 0; e < E; ++e)
-    if ((st = launch_mxfp8_colwise(w_gate_up[e], 2 * I, H, 1, nullptr, 32, 2 * I, ws + L.w1c + e * w1n,
-                                   ws + L.w1s + e * w1n / 32, nullptr, s)) != MOE_OK)
-      return st;
+  if ((st = launch_mxfp8_quantize_step_major(dz, R, 2 * I, dzq, dzs, s)) != MOE_OK) return st;
+  if (!packed)
+    for (int e = 0; e < E; ++e)
+      if ((st = launch_mxfp8_colwise(w_gate_up[e], 2 * I, H, 1, nullptr, 32, 2 * I, ws + L.w1c + e * w1n,
+                                     ws + L.w1s + e * w1n / 32, nullptr, s, true)) != MOE_OK)
+        return st;
   for (int e = 0; e < E; ++e) {
-    p.tab[e] = ws + L.w1c + e * w1n;
-    p.tab_s[e] = ws + L.w1s + e * w1n / 32;
+    p.tab[e] = w1_codes(e);
+    p.tab_s[e] = packed ? w1_codes(e) + w1n : ws + L.w1s + e * w1n / 32;
   }
   p.q = dzq;
   p.q_s = dzs;
@@ -1667,7 +1681,7 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
   p.K = 2 * I;
   p.N = H;
   p.n_tiles = H / kBN;
-  if ((st = launch(MX_STORE, false, p, mtiles * p.n_tiles, s, "MXFP8 gate_up dgrad")) != MOE_OK) return st;
+  if ((st = launch(MX_STORE, false, p, mtiles * p.n_tiles, s, "MXFP8 gate_up dgrad", true)) != MOE_OK) return st;
 
   // weight gradients on the token-axis layouts
   if ((st = launch_mxfp8_colwise(dy, R, H, E, offsets, 256, kc, ws + L.dyc, ws + L.dycs, kofs, s)) != MOE_OK) return st;

@@ -37,8 +37,11 @@ moe_status launch_mx_scales_step_major(const uint8_t* const* src, uint8_t* const
 // offsets NULL: one expert of R rows; kofs NULL: the padded offsets are not written.
 // The caller guarantees C % 64 == 0, pad % 32 == 0, kcap % 32 == 0, kcap >= the padded
 // row total, 16-byte aligned x and codes.
+// step_major: scales in the step-major layout of launch_mxfp8_quantize_step_major over
+// the transposed [C, kcap] output (word (k / 128) * C + c; kcap % 128 == 0).
 moe_status launch_mxfp8_colwise(const void* x_bf16, int64_t R, int C, int E, const int32_t* offsets, int pad,
-                                int64_t kcap, uint8_t* codes, uint8_t* scales, int32_t* kofs, hipStream_t s);
+                                int64_t kcap, uint8_t* codes, uint8_t* scales, int32_t* kofs, hipStream_t s,
+                                bool step_major = false);
 
 // per-tensor FP8 (one float32 scale per tensor). A tensor's word holds the float bits
 // of its amax between fp8t_amax and fp8t_finalize (cleared first by fp8t_zero), and

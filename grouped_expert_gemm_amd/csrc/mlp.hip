@@ -39,8 +39,9 @@ moe_status validate_desc(const moe_mlp_desc& d, bool backward) {
   }
   if (backward && d.compute == MOE_FP8)
     return fail(MOE_ERR_UNSUPPORTED, "grouped MLP backward: per-tensor FP8 backward is not implemented (use MXFP8 or BF16)");
-  if (backward && d.compute == MOE_MXFP8 && (d.act != MOE_BF16 || d.wt != MOE_BF16))
-    return fail(MOE_ERR_INVALID_ARG, "grouped MLP backward: MXFP8 takes bf16 activations and bf16 master weights");
+  if (backward && d.compute == MOE_MXFP8 && d.act != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "grouped MLP backward: MXFP8 takes bf16 activations (and bf16 master weights or "
+                                     "weights packed by mxfp8_pack_weight_bwd)");
   return MOE_OK;
 }
 

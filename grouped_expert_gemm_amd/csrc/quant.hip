@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
                                                                      int C, int E, const int32_t* __restrict__ offsets,
                                                                      int pad, int64_t kcap, uint8_t* __restrict__ codes,
                                                                      uint8_t* __restrict__ scales,
-                                                                     int32_t* __restrict__ kofs_out) {
+                                                                     int32_t* __restrict__ kofs_out, int step_major) {
   __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int32_t s_kofs[MOE_MAX_EXPERTS + 1];
   __shared__ int32_t s_item[MOE_MAX_EXPERTS + 1];
@@ -233,7 +233,9 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
       uint4* dst = reinterpret_cast<uint4*>(codes + col * kcap + k);
       dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
       dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
-      scales[col * (kcap / 32) + k / 32] = (uint8_t)(sx + 127);
+      // step-major (the wide-step GEMM's operand layout): word (k / 128) * C + col
+      const int64_t at = step_major ? ((k >> 7) * C + col) * 4 + ((k >> 5) & 3) : col * (kcap / 32) + k / 32;
+      scales[at] = (uint8_t)(sx + 127);
     }
     __syncthreads();  // the tile is reused by the next item
   }
@@ -244,13 +246,15 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
 using namespace moe;
 
 moe_status moe::launch_mxfp8_colwise(const void* x_bf16, int64_t R, int C, int E, const int32_t* offsets, int pad,
-                                int64_t kcap, uint8_t* codes, uint8_t* scales, int32_t* kofs, hipStream_t s) {
+                                int64_t kcap, uint8_t* codes, uint8_t* scales, int32_t* kofs, hipStream_t s,
+                                bool step_major) {
+  if (step_major && kcap % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "mxfp8 step-major scales need kcap % 128 == 0");
   const int64_t items = (kcap / 32 + 3 * E) / 4 * (C / 64) + E * (C / 64);
   int64_t grid = (int64_t)num_cus() * 32;  // ~4 resident per CU (33 KB of LDS each), the rest balance the tail
   if (items < grid) grid = items;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(mxfp8_quantize_colwise_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const uint16_t*)x_bf16,
-                     R, C, E, offsets, pad, kcap, codes, scales, kofs);
+                     R, C, E, offsets, pad, kcap, codes, scales, kofs, (int)step_major);
   return check_launch("mxfp8_quantize_colwise");
 }
 
@@ -269,6 +273,22 @@ extern "C" moe_status mxfp8_quantize_colwise(const void* x_bf16, int64_t R, int6
   if (!aligned(offsets, 4) || !aligned(kofs, 4) || (x_bf16 && !aligned(x_bf16, 16)) || (e4m3_t && !aligned(e4m3_t, 16)))
     return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_colwise: x and codes must be 16-byte and offsets 4-byte aligned");
   return launch_mxfp8_colwise(x_bf16, R, (int)C, E, offsets, pad, kcap, e4m3_t, e8m0_t, kofs, as_stream(stream));
+}
+
+extern "C" moe_status mxfp8_pack_weight_bwd(const void* w_bf16, int64_t rows, int64_t cols, void* packed,
+                                            void* stream) {
+  if (rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "mxfp8_pack_weight_bwd: negative size");
+  if (rows % 128 != 0 || cols % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "mxfp8_pack_weight_bwd: needs rows % 128 == 0 and cols % 64 == 0");
+  if (rows > 0x7FFFFFFF || rows * cols > 0x7FFFFFFFLL)
+    return fail(MOE_ERR_UNSUPPORTED, "mxfp8_pack_weight_bwd: weight exceeds 2^31 elements");
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!w_bf16 || !packed) return fail(MOE_ERR_INVALID_ARG, "mxfp8_pack_weight_bwd: NULL pointer");
+  if (!aligned(w_bf16, 16) || !aligned(packed, 16))
+    return fail(MOE_ERR_INVALID_ARG, "mxfp8_pack_weight_bwd: w and packed must be 16-byte aligned");
+  uint8_t* codes = reinterpret_cast<uint8_t*>(packed);
+  return launch_mxfp8_colwise(w_bf16, rows, (int)cols, 1, nullptr, 32, rows, codes, codes + rows * cols, nullptr,
+                              as_stream(stream), true);
 }
 
 extern "C" moe_status mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,

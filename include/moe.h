@@ -217,6 +217,22 @@ moe_status mxfp8_quantize_colwise(const void* x_bf16, int64_t R, int64_t C, int 
                                   int64_t kcap, uint8_t* e4m3_t, uint8_t* e8m0_t, int32_t* kofs, void* stream);
 
 /*
+ * MXFP8 packing of one bf16 weight for moe_grouped_mlp_bwd (the MXFP8 backward's data
+ * gradients take each weight quantised along the axis they reduce over: W2_e [H, I]
+ * along H, W1_e [2I, H] along 2I). Source: Challenge 2 (32-value blocks) and Challenge 3
+ * (quantisation as separate ops is the overhead the fused recipe removes: a training
+ * loop packs each weight once per optimizer step instead of once per call).
+ *   w [rows, cols] bf16 (16-byte aligned)
+ *   packed (out, 16-byte aligned, rows * cols * 33 / 32 bytes): the E4M3 codes of the
+ *     transpose, [cols][rows] (element (c, r) is w[r, c] quantised in blocks of 32
+ *     along r by the rule of mxfp8_quantize), then at byte rows * cols the E8M0 scales,
+ *     "step-major": the 4 scales of rows [128 k, 128 k + 128) of column c are one 32-bit
+ *     word (lowest byte first) at word index k * cols + c.
+ * Limits: rows % 128 == 0, cols % 64 == 0, rows * cols < 2^31.
+ */
+moe_status mxfp8_pack_weight_bwd(const void* w_bf16, int64_t rows, int64_t cols, void* packed, void* stream);
+
+/*
  * Per-tensor FP8 quantisation of a bf16 tensor. Source: Challenge 2 (FP8 with one
  * scaling factor for a whole tensor, the contrast to MXFP8's factor per 32 values).
  * The pages give no scale rule; the one implemented ("current scaling"):
@@ -294,9 +310,11 @@ moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, const void* 
  *   dG       = dA * U * sig(G) * (1 + G * (1 - sig(G))),  dU = dA * silu(G)
  *   dx_perm  = [dG, dU] W1_e                         -> dx_perm       [R, H]
  *   dW1_e    = [dG, dU]^T x_perm                     -> dw_gate_up[e] [2I, H]
- * Experts without rows get all-zero weight gradients. Weight gradients have the
- * weights' dtype (bf16 or float32) and are overwritten, not accumulated.
- * compute = MXFP8 (act and wt BF16: every tensor in and out is bf16): each of the four
+ * Experts without rows get all-zero weight gradients. Weight gradients are bf16 (float32
+ * with compute = F32) and are overwritten, not accumulated.
+ * compute = MXFP8 (act BF16; wt BF16, or MXFP8 for weights packed by mxfp8_pack_weight_bwd:
+ * w_gate_up[e] the packing of W1_e (rows 2I, cols H), w_down[e] that of W2_e (rows H,
+ * cols I), bit-identical to quantising the bf16 weights in the call): each of the four
  * GEMMs takes both operands as MXFP8 along its own reduction axis (Challenge 2's
  * 32-value blocks, Challenge 3's recipe): dY and dZ = [dG, dU] by rows, W2_e along H,
  * W1_e along 2I, and dY, h_save, dZ, x_perm along each expert's rows (blocks starting
@@ -304,9 +322,9 @@ moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, const void* 
  * the recipe returns a low-precision GEMM's result to bf16. Needs H % 256 == 0,
  * I % 256 == 0, E <= 128. Its workspace (moe_workspace_size(MOE_OP_MLP_BWD, ...))
  * holds every quantised operand, the column-wise weight copies and dH, dZ in bf16:
- * about R (3.1 H + 11.2 I) + 3.1 E H I bytes, plus (2H + 3I) bytes per padding row
- * of the token-axis layouts (3.0 GB at R = 8192, H = 4096, I = 14336, E = 8). Calls
- * sharing a workspace must not overlap.
+ * about R (3.1 H + 11.2 I) + 3.1 E H I bytes (the last term only for bf16 weights),
+ * plus (2H + 3I) bytes per padding row of the token-axis layouts (3.0 GB at R = 8192,
+ * H = 4096, I = 14336, E = 8, bf16 weights). Calls sharing a workspace must not overlap.
  */
 moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, const void* dy_perm,
                                const void* x_perm, const void* z_save, const void* h_save,

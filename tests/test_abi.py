@@ -157,3 +157,12 @@ def test_noalloc_permute_rejects_sizes_beyond_its_scratch(L):
     assert b"8 MiB" in L.moe_last_error()
     assert L.moe_permute_noalloc(dummy, None, 1, 10, 64, 0, 1, dummy, dummy, 0, dummy, None, dummy, dummy, dummy,
                                  dummy, dummy, None) == _lib.MOE_ERR_INVALID_ARG     # E = 0
+
+
+def test_pack_weight_argument_checks(L):
+    from grouped_expert_gemm_amd import _lib
+    dummy = ctypes.c_void_p(256)
+    assert L.mxfp8_pack_weight_bwd(dummy, 100, 64, dummy, None) == _lib.MOE_ERR_UNSUPPORTED   # rows % 128
+    assert L.mxfp8_pack_weight_bwd(dummy, 128, 96, dummy, None) == _lib.MOE_ERR_UNSUPPORTED   # cols % 64
+    assert L.mxfp8_pack_weight_bwd(None, 128, 64, dummy, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.mxfp8_pack_weight_bwd(None, 0, 64, None, None) == 0                             # empty: no-op

@@ -173,3 +173,49 @@ def test_mxfp8_backward_degenerate(moe):
         assert err <= MX_TOL, k2
     for e in (0, 1, 3):
         assert not host(dw1)[e].any() and not host(dw2)[e].any()
+
+
+@pytest.mark.parametrize("rows,cols", [(512, 384), (128, 64), (1024, 1536)])
+def test_mxfp8_pack_weight_bwd_bits(moe, rows, cols):
+    """mxfp8_pack_weight_bwd: the codes of w^T quantised along w's rows (32-value blocks)
+    and the step-major scales, bit for bit against the oracle's column-wise quantiser
+    (one expert of `rows` rows, 32-row padding, which is none here)."""
+    rng = np.random.default_rng(rows + cols)
+    w = (rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-6, 6, (rows // 32, 1)).repeat(32, 0))).astype(np.float32)
+    w[:32, :5] = 0.0                              # all-zero blocks
+    wb = _bits(w)
+    print(f"pack weight rows={rows} cols={cols}", flush=True)
+    packed = moe.mxfp8_pack_weight_bwd(dev_bf16(wb)).cpu().numpy()
+    codes, scales, _ = oracle.mxfp8_quantize_colwise(bf16_bits_to_f32(wb), np.array([0, rows]), 32, rows)
+    assert np.array_equal(packed[:rows * cols].reshape(cols, rows), codes)
+    # step-major: the 4 scales of rows [128 k, 128 k + 128) of column c form word k * cols + c
+    sm = scales.reshape(cols, rows // 128, 4).transpose(1, 0, 2).reshape(-1)
+    assert np.array_equal(packed[rows * cols:], sm)
+
+
+def test_mxfp8_backward_with_packed_weights(moe):
+    """The MXFP8 backward on weights packed once (mxfp8_pack_weight_bwd) gives the same
+    bits as on the bf16 master weights quantised inside the call."""
+    T, H, I, E, k = 700, 512, 256, 6, 2
+    w = scaled(WORKLOADS["mixtral_fwd_bwd"], T=T, H=H, I=I, E=E, k=k, zipf=1.2, seed=44)
+    inp = make_inputs(w)
+    inp.logits[:, [2]] -= 100.0
+    idx, p, m, pp = oracle_perm(inp, k, E)
+    assert m["split_sizes"][2] == 0
+    R = T * k
+    xp = dev_bf16(inp.bits["x"][m["src_token"]])
+    gen = np.random.default_rng(9)
+    z = dev_bf16(_bits(gen.standard_normal((R, 2 * I))))
+    h = dev_bf16(_bits(0.3 * gen.standard_normal((R, I))))
+    dy = dev_bf16(_bits(gen.standard_normal((R, H))))
+    off = torch.from_numpy(m["offsets"].astype(np.int32)).cuda()
+    prob = dev_f32(pp.astype(np.float32))
+    w1, w2 = dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"])
+    print(f"mxfp8 bwd with packed weights: R={R} H={H} I={I} E={E}", flush=True)
+    ref = moe.moe_grouped_mlp_bwd(dy, xp, z, h, prob, w1, w2, off, compute="mxfp8")
+    p1 = [moe.mxfp8_pack_weight_bwd(w1[e]) for e in range(E)]
+    p2 = [moe.mxfp8_pack_weight_bwd(w2[e]) for e in range(E)]
+    got = moe.moe_grouped_mlp_bwd(dy, xp, z, h, prob, p1, p2, off, compute="mxfp8")
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dx", "dw_gate_up", "dw_down", "dprob"), got, ref):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
