@@ -405,53 +405,6 @@ def memory_bound_measure(w, inp, reps=20):
     return recs
 
 
-def route_permute_measure(w, inp, reps=20):
-    """Routing followed by the permutation, as two calls (moe_route_topk, then moe_permute:
-    route, count, scan and scatter kernels) and as the fused moe_route_permute (routing
-    inside the count kernel), each timed call by call after a cache flush."""
-    import numpy as np
-    import torch
-
-    import grouped_expert_gemm_amd as moe
-    from grouped_expert_gemm_amd import _lib
-
-    T, H, E, k = w.T, w.H, w.E, w.k
-    R = T * k
-    x = dev_bf16(torch, np, inp.bits["x"])
-    logits = torch.from_numpy(inp.logits).cuda()
-    dev = x.device
-    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    prob = torch.empty((T, k), dtype=torch.float32, device=dev)
-    xp = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
-    pp = torch.empty(R, dtype=torch.float32, device=dev)
-    split = torch.empty(E, dtype=torch.int32, device=dev)
-    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    rmap = torch.empty(R, dtype=torch.int32, device=dev)
-    src = torch.empty(R, dtype=torch.int32, device=dev)
-    ws = torch.empty(max(1, moe.workspace_size(_lib.MOE_OP_PERMUTE, None, 0, T, E, k)), dtype=torch.uint8,
-                     device=dev)
-    L = moe.lib()
-    vp = lambda t: ctypes.c_void_p(t.data_ptr())
-    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-
-    def separate():
-        _lib.check("route", L.moe_route_topk(vp(logits), T, E, k, 1, vp(idx), vp(prob), s))
-        _lib.check("permute", L.moe_permute(vp(x), None, _lib.MOE_BF16, T, H, E, k, vp(idx), vp(prob), 0, vp(xp),
-                                            None, vp(pp), vp(split), vp(off), vp(rmap), vp(src), vp(ws),
-                                            ws.numel(), s))
-
-    def fused():
-        _lib.check("route_permute", L.moe_route_permute(vp(logits), T, E, k, 1, vp(x), None, _lib.MOE_BF16, H,
-                                                        vp(idx), vp(prob), vp(xp), None, vp(pp), vp(split), vp(off),
-                                                        vp(rmap), vp(src), vp(ws), ws.numel(), s))
-
-    rec = {"workload": w.name, "T": T, "E": E, "k": k, "cache": "flushed (512 MB write) before each call"}
-    for name, f in (("separate_ms", separate), ("fused_ms", fused)):
-        rec[name] = round(timed_flushed(f, reps), 4)
-    log(f"route+permute {w.name}: separate {rec['separate_ms']:.4f} ms, fused {rec['fused_ms']:.4f} ms")
-    return rec
-
-
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -607,9 +560,6 @@ def only_measurement(which, steps, warmup):
                 extra_forward(w8, inp, steps, warmup, compute="mxfp8", prequant=True)]
     if which == "colwise":
         return colwise_measure(steps)
-    if which == "route_permute":
-        wq = WORKLOADS["qwen3_fwd"]
-        return [route_permute_measure(w, inp, steps), route_permute_measure(wq, make_inputs(wq, want_float=False), steps)]
     if which == "permute":
         wq = WORKLOADS["qwen3_fwd"]
         return [memory_bound_measure(w, inp, steps), memory_bound_measure(wq, make_inputs(wq, want_float=False), steps)]
@@ -630,7 +580,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip the MXFP8 and Qwen3 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["fwd_bwd", "mx_fwd_bwd", "mx_fwd_bwd_pre", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise", "permute", "route_permute"],
+    ap.add_argument("--only", choices=["fwd_bwd", "mx_fwd_bwd", "mx_fwd_bwd_pre", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise", "permute"],
                     help="run one measurement and print its record (kernel traces of that workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
@@ -709,7 +659,6 @@ def main():
         result["qwen3_fwd"] = extra_forward(wq, inpq, max(3, args.steps // 2), args.warmup)
         result["router"] = [router_measure(w, inp), router_measure(wq, inpq)]
         result["permute_combine"] = [memory_bound_measure(w, inp), memory_bound_measure(wq, inpq)]
-        result["route_permute"] = [route_permute_measure(w, inp), route_permute_measure(wq, inpq)]
         result["mxfp8_colwise"] = colwise_measure()
         del inpq
         torch.cuda.empty_cache()

@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import MOE_BF16, MOE_F32, MOE_FP8, MOE_MXFP8, MlpDesc, MoeError, check, lib, ptr_table
 
 __all__ = [
-    "moe_route_topk", "moe_route_permute", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
+    "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
     "fp8_tensor_quantize", "mxfp8_quantize_colwise", "mxfp8_pack_weight_bwd",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu", "gemm_workspace",
     "workspace_size", "MoeError", "lib",
@@ -144,33 +144,6 @@ def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torch.Tensor
                                            _p(src), _p(ws), ws.numel(), _stream(dev)))
     return dict(x_perm=x_perm, x_perm_scale=xps, prob_perm=prob_perm, split_sizes=split, offsets=offsets,
                 row_id_map=rmap, src_token=src)
-
-
-def moe_route_permute(logits: torch.Tensor, x: torch.Tensor, k: int, renormalize: bool = True,
-                      x_scale: torch.Tensor | None = None):
-    """Routing fused with the permutation: logits [T, E] float32 and x [T, H] -> dict with
-    topk_idx [T, k], topk_prob [T, k] and moe_permute's outputs (bit-identical to the two calls)."""
-    _need_cuda(logits, x, x_scale)
-    T, E = logits.shape
-    H = x.shape[1]
-    R = T * k
-    dt = _DT[x.dtype]
-    dev = x.device
-    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    prob = torch.empty((T, k), dtype=torch.float32, device=dev)
-    x_perm = torch.empty((R, H), dtype=x.dtype, device=dev)
-    xps = torch.empty((R, H // 32), dtype=torch.uint8, device=dev) if dt == MOE_MXFP8 else None
-    prob_perm = torch.empty(R, dtype=torch.float32, device=dev)
-    split = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    rmap = torch.empty(R, dtype=torch.int32, device=dev)
-    src = torch.empty(R, dtype=torch.int32, device=dev)
-    ws = _workspace(workspace_size(_lib.MOE_OP_PERMUTE, None, 0, T, E, k), dev)
-    check("moe_route_permute", lib().moe_route_permute(
-        _p(logits), T, E, k, int(renormalize), _p(x), _p(x_scale), dt, H, _p(idx), _p(prob), _p(x_perm), _p(xps),
-        _p(prob_perm), _p(split), _p(offsets), _p(rmap), _p(src), _p(ws), ws.numel(), _stream(dev)))
-    return dict(topk_idx=idx, topk_prob=prob, x_perm=x_perm, x_perm_scale=xps, prob_perm=prob_perm,
-                split_sizes=split, offsets=offsets, row_id_map=rmap, src_token=src)
 
 
 def moe_unpermute_combine(y_perm: torch.Tensor, row_id_map: torch.Tensor, T: int, k: int,

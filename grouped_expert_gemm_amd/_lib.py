@@ -19,7 +19,7 @@ MOE_MAX_EXPERTS = 256
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd",
-    "moe_permute", "moe_permute_noalloc", "moe_route_permute", "moe_unpermute_combine", "mxfp8_quantize", "fp8_tensor_quantize", "mxfp8_quantize_colwise",
+    "moe_permute", "moe_permute_noalloc", "moe_unpermute_combine", "mxfp8_quantize", "fp8_tensor_quantize", "mxfp8_quantize_colwise",
     "mxfp8_pack_weight_bwd",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu",
     "moe_workspace_size",
@@ -58,8 +58,6 @@ def _declare(lib):
         "moe_router_bwd": [vp, vp, vp, vp, i64, c_int, c_int, vp, vp, vp, sz, vp],
         "moe_permute": [vp, vp, c_int, i64, c_int, c_int, c_int, vp, vp, c_int, vp, vp, vp, vp, vp, vp, vp,
                         vp, sz, vp],
-        "moe_route_permute": [vp, i64, c_int, c_int, c_int, vp, vp, c_int, c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                              vp, sz, vp],
         "moe_permute_noalloc": [vp, vp, c_int, i64, c_int, c_int, c_int, vp, vp, c_int, vp, vp, vp, vp, vp, vp,
                                 vp, vp],
         "moe_unpermute_combine": [vp, c_int, vp, vp, i64, c_int, c_int, vp, vp],

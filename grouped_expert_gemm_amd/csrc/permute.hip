@@ -17,7 +17,6 @@
 
 #include "common.h"
 #include "internal.h"
-#include "route_select.h"
 
 namespace moe {
 
@@ -83,63 +82,6 @@ __global__ __launch_bounds__(kPermBlock) void permute_count_kernel(const int32_t
     }
   }
   for (int e = tid; e < E; e += kPermBlock) {
-    int c = 0;
-#pragma unroll
-    for (int ww = 0; ww < kPermBlock / 32; ++ww) c += __popc(flags[e * (kPermBlock / 32) + ww]);
-    counts[(int64_t)blockIdx.x * E + e] = c;
-  }
-}
-
-// Routing fused with the count pass (the DeepEP dispatcher's optional permute fusion in
-// the PyTorch-native MoE library article): one workgroup of 1024 lanes per 256-token
-// count block selects every token's k experts (route_select), writes topk_idx and
-// topk_prob, and marks the block's per-expert LDS bit sets in the same pass; the ranks
-// and counts then come from the bit sets exactly as in permute_count_kernel. Replaces
-// the routing launch and the count launch (and the count pass's re-read of topk_idx).
-template <int L, int V>
-__global__ __launch_bounds__(1024) void route_count_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
-                                                           int renorm, int32_t* __restrict__ topk_idx,
-                                                           float* __restrict__ topk_prob,
-                                                           int32_t* __restrict__ counts,
-                                                           int32_t* __restrict__ rank_local) {
-  constexpr int G = 64 / L;                 // tokens per wavefront and pass
-  constexpr int kPass = 16 * G;             // tokens per pass of the 16 wavefronts
-  __shared__ uint32_t flags[MOE_MAX_EXPERTS * (kPermBlock / 32)];
-  __shared__ int8_t s_exp[kPermBlock][kMaxK];  // the block's chosen experts (E <= 256 fits after the shift)
-  const int tid = threadIdx.x;
-  for (int i = tid; i < E * (kPermBlock / 32); i += 1024) flags[i] = 0;
-  __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6;
-  const int j = lane % L;
-  const int64_t t0 = (int64_t)blockIdx.x * kPermBlock;
-  for (int base = 0; base < kPermBlock; base += kPass) {  // (E <= 2: one pass covers more than the block)
-    const int tl = base + wave * G + lane / L;  // token within the block
-    const int64_t t = t0 + tl;
-    const bool live = tl < kPermBlock && t < T;
-    int oid;
-    float op;
-    route_select<L, V>(logits, t, live, E, k, renorm, j, oid, op);
-    if (live && j < k) {
-      topk_idx[t * k + j] = oid;
-      topk_prob[t * k + j] = op;
-      s_exp[tl][j] = (int8_t)(oid - 128);
-      atomicOr(&flags[oid * (kPermBlock / 32) + (tl >> 5)], 1u << (tl & 31));
-    }
-  }
-  __syncthreads();
-  if (tid < kPermBlock && t0 + tid < T) {
-    const int w = tid >> 5;
-    const uint32_t bit = 1u << (tid & 31);
-    for (int jj = 0; jj < k; ++jj) {
-      const int e = (int)s_exp[tid][jj] + 128;
-      const uint32_t* f = &flags[e * (kPermBlock / 32)];
-      int r = 0;
-      for (int ww = 0; ww < w; ++ww) r += __popc(f[ww]);
-      r += __popc(f[w] & (bit - 1u));
-      rank_local[(t0 + tid) * k + jj] = r;
-    }
-  }
-  for (int e = tid; e < E; e += 1024) {
     int c = 0;
 #pragma unroll
     for (int ww = 0; ww < kPermBlock / 32; ++ww) c += __popc(flags[e * (kPermBlock / 32) + ww]);
@@ -345,13 +287,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 
 using namespace moe;
 
-// moe_permute, and with route_logits != NULL the fused moe_route_permute (topk_idx and
-// topk_prob are then written by the first kernel)
-static moe_status permute_impl(const float* route_logits, int route_renorm, const void* x, const uint8_t* x_scale,
-                               moe_dtype dt, int64_t T, int H, int E, int k, const int32_t* topk_idx,
-                               const float* topk_prob, int reuse_map, void* x_perm, uint8_t* x_perm_scale,
-                               float* prob_perm, int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
-                               int32_t* src_token, void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" moe_status moe_permute(const void* x, const uint8_t* x_scale, moe_dtype dt, int64_t T, int H,
+                                  int E, int k, const int32_t* topk_idx, const float* topk_prob,
+                                  int reuse_map, void* x_perm, uint8_t* x_perm_scale, float* prob_perm,
+                                  int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
+                                  int32_t* src_token, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   if (T < 0 || H < 1) return fail(MOE_ERR_INVALID_ARG, "moe_permute: T < 0 or H < 1");
   if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "moe_permute: E out of [1, 256]");
   if (k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "moe_permute: k out of [1, E]");
@@ -405,16 +346,8 @@ static moe_status permute_impl(const float* route_logits, int route_renorm, cons
   int32_t* rank_local = (int32_t*)ws;
 
   if (T > 0) {
-    if (route_logits) {  // fused routing: topk_idx / topk_prob are outputs of this call
-      route_dispatch(E, [&](auto Lc, auto Vc) {
-        constexpr int L = decltype(Lc)::value, V = decltype(Vc)::value;
-        hipLaunchKernelGGL((route_count_kernel<L, V>), dim3((unsigned)nb), dim3(1024), 0, s, route_logits, T, E, k,
-                           route_renorm, (int32_t*)topk_idx, (float*)topk_prob, counts, rank_local);
-      });
-    } else {
-      hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)nb), dim3(kPermBlock), 0, s, topk_idx, T, E, k,
-                         counts, rank_local);
-    }
+    hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)nb), dim3(kPermBlock), 0, s, topk_idx, T, E, k,
+                       counts, rank_local);
   }
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, counts, nb, E, base, split_sizes, offsets);
   if (T > 0) {
@@ -424,33 +357,7 @@ static moe_status permute_impl(const float* route_logits, int route_renorm, cons
                        rank_local, T, E, k, 0, unit, sunit, (uint8_t*)x_perm, dt == MOE_MXFP8 ? x_perm_scale : nullptr,
                        prob_perm, row_id_map, src_token);
   }
-  return check_launch(route_logits ? "moe_route_permute" : "moe_permute");
-}
-
-extern "C" moe_status moe_permute(const void* x, const uint8_t* x_scale, moe_dtype dt, int64_t T, int H,
-                                  int E, int k, const int32_t* topk_idx, const float* topk_prob,
-                                  int reuse_map, void* x_perm, uint8_t* x_perm_scale, float* prob_perm,
-                                  int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
-                                  int32_t* src_token, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
-  return permute_impl(nullptr, 0, x, x_scale, dt, T, H, E, k, topk_idx, topk_prob, reuse_map, x_perm, x_perm_scale,
-                      prob_perm, split_sizes, offsets, row_id_map, src_token, workspace, workspace_bytes, stream);
-}
-
-extern "C" moe_status moe_route_permute(const float* logits, int64_t T, int E, int k, int renormalize,
-                                        const void* x, const uint8_t* x_scale, moe_dtype dt, int H,
-                                        int32_t* topk_idx, float* topk_prob, void* x_perm, uint8_t* x_perm_scale,
-                                        float* prob_perm, int32_t* split_sizes, int32_t* offsets,
-                                        int32_t* row_id_map, int32_t* src_token, void* workspace,
-                                        size_t workspace_bytes, void* stream) {
-  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_route_permute: T < 0");
-  if (k > kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "moe_route_permute: k > 16");
-  if (T > 0 && (!logits || !topk_idx || !topk_prob))
-    return fail(MOE_ERR_INVALID_ARG, "moe_route_permute: NULL logits / topk_idx / topk_prob");
-  if (T > 0 && (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_prob, 4)))
-    return fail(MOE_ERR_INVALID_ARG, "moe_route_permute: misaligned pointer");
-  return permute_impl(logits, renormalize, x, x_scale, dt, T, H, E, k, topk_idx, topk_prob, 0, x_perm, x_perm_scale,
-                      prob_perm, split_sizes, offsets, row_id_map, src_token, workspace, workspace_bytes, stream);
+  return check_launch("moe_permute");
 }
 
 extern "C" moe_status moe_unpermute_combine(const void* y_perm, moe_dtype dt, const int32_t* row_id_map,

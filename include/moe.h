@@ -152,21 +152,6 @@ moe_status moe_permute(const void* x, const uint8_t* x_scale, moe_dtype dt, int6
                        void* stream);
 
 /*
- * Routing and permutation in one call: moe_route_topk followed by moe_permute on its
- * result, with the routing fused into the permutation's counting pass (the token
- * dispatcher's optional permute fusion named in the PyTorch-native MoE library
- * article; routing as in Challenge 1). topk_idx and topk_prob are OUTPUTS ([T, k]);
- * every other argument, output, the workspace (moe_workspace_size(MOE_OP_PERMUTE,
- * ...)) and the limits are those of moe_route_topk and moe_permute (reuse_map = 0).
- * The outputs are bit-identical to the two calls.
- */
-moe_status moe_route_permute(const float* logits, int64_t T, int E, int k, int renormalize, const void* x,
-                             const uint8_t* x_scale, moe_dtype dt, int H, int32_t* topk_idx, float* topk_prob,
-                             void* x_perm, uint8_t* x_perm_scale, float* prob_perm, int32_t* split_sizes,
-                             int32_t* offsets, int32_t* row_id_map, int32_t* src_token, void* workspace,
-                             size_t workspace_bytes, void* stream);
-
-/*
  * moe_permute without a workspace argument, for callers that cannot allocate device
  * memory (code under HIP graph capture, serving loops or harnesses that forbid
  * hipMalloc). Same arguments (minus the workspace), semantics and outputs as

@@ -314,58 +314,3 @@ def test_mxfp8_quantize_weight_shape(moe):
     assert np.array_equal(scales.cpu().numpy(), rs)
     assert np.array_equal(codes.cpu().numpy(), rc)
 
-
-ROUTE_PERMUTE_CASES = [
-    # T, E, k, renormalize, dtype, ties
-    (1, 1, 1, True, "bf16", False),
-    (300, 2, 2, True, "f32", False),
-    (257, 3, 2, False, "bf16", True),
-    (8192, 8, 2, True, "bf16", False),      # the Mixtral layer's routing
-    (1000, 65, 6, True, "bf16", True),
-    (16384, 128, 8, True, "bf16", False),   # the Qwen3 layer's routing (Zipf-skewed)
-    (700, 200, 16, False, "bf16", False),
-    (513, 256, 4, True, "mxfp8", True),
-]
-
-
-@pytest.mark.parametrize("case", ROUTE_PERMUTE_CASES, ids=[f"T{c[0]}-E{c[1]}-k{c[2]}" for c in ROUTE_PERMUTE_CASES])
-def test_route_permute_fused(moe, case):
-    """moe_route_permute (routing fused into the permutation's count pass) against the
-    oracle's routing and permutation, bit for bit, and against the two separate calls."""
-    T, E, k, renorm, dtype, ties = case
-    rng = np.random.default_rng(T * 7 + E)
-    logits = rng.standard_normal((T, E)).astype(np.float32)
-    if E == 128:
-        logits += (-1.2 * np.log(rng.permutation(E) + 1)).astype(np.float32)[None, :]
-    if ties:  # coarse values: many equal logits within a row
-        logits = np.round(logits * 2) / 2
-    H = 64
-    if dtype == "bf16":
-        xb = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
-        x, xs = dev_bf16(xb), None
-    elif dtype == "f32":
-        xf = rng.standard_normal((T, H)).astype(np.float32)
-        x, xs = dev_f32(xf), None
-    else:
-        x = torch.from_numpy(rng.integers(0, 255, (T, H), dtype=np.uint8)).cuda()
-        xs = torch.from_numpy(rng.integers(0, 255, (T, H // 32), dtype=np.uint8)).cuda()
-    print(f"route+permute fused: T={T} E={E} k={k} renorm={renorm} {dtype}", flush=True)
-    lg = dev_f32(logits)
-    f = moe.moe_route_permute(lg, x, k, renormalize=renorm, x_scale=xs)
-    idx, prob = moe.moe_route_topk(lg, k, renormalize=renorm)
-    sep = moe.moe_permute(x, idx, prob, E, x_scale=xs)
-    torch.cuda.synchronize()
-    ridx, rp = oracle.route_topk(logits, k, renormalize=renorm)
-    assert np.array_equal(f["topk_idx"].cpu().numpy(), ridx)
-    assert np.abs(f["topk_prob"].cpu().numpy() - rp).max() <= 1e-6
-    m = oracle.permute(ridx, E)
-    for key in ("split_sizes", "offsets", "row_id_map", "src_token"):
-        assert np.array_equal(f[key].cpu().numpy(), m[key]), key
-    assert torch.equal(f["topk_idx"], idx) and torch.equal(f["topk_prob"], prob)
-    for key in ("x_perm", "prob_perm", "split_sizes", "offsets", "row_id_map", "src_token"):
-        a, b = f[key], sep[key]
-        if a.dtype == torch.bfloat16:
-            a, b = a.view(torch.int16), b.view(torch.int16)
-        assert torch.equal(a, b), key
-    if xs is not None:
-        assert torch.equal(f["x_perm_scale"], sep["x_perm_scale"])
