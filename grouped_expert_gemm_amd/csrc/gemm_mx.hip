@@ -13,7 +13,12 @@
 // of a 64-value slice, and supplies the E8M0 scale of K block g (values [32g, 32g + 32))
 // of its row.
 //
-// grouped_gemm_mx_kernel (MXFP8): 256 x 256 tiles, 4 wavefronts of 128 x 128, a 4-slot
+// grouped_gemm_mxw_kernel (MXFP8, every GEMM of the MLP's forward and backward): the
+// per-tensor kernel's wide-step pipeline below plus E8M0 scales in a step-major layout
+// (described at the kernel).
+//
+// grouped_gemm_mx_kernel (MXFP8 with the public row-major scale layout, the stand-alone
+// gate_up entry point): 256 x 256 tiles, 4 wavefronts of 128 x 128, a 4-slot
 // LDS ring filled by global -> LDS copies four K steps ahead, a barrier in the middle
 // of each step. One K step is 64 fp8 values = 64 bytes per row (the two 16-byte chunks
 // a lane reads). Scales: per 4-step group each lane loads 8 bytes (blocks 8g..8g+7) of
@@ -64,7 +69,8 @@ struct MxParams {
 // MX_WGRAD (a weight gradient per expert, K = the expert's padded token count): P =
 // tab[0] and Q = q are token-axis (column-wise) layouts [N][ld] and [R][ld] whose expert
 // e occupies columns [kofs[e], kofs[e+1]); the result goes to ctab[e] [R][N] in bf16,
-// all zeros for an expert without rows. Only this kernel takes the larger argument block.
+// all zeros for an expert without rows. Only the weight-gradient instantiation takes
+// this larger argument block.
 struct MxWgradParams : MxParams {
   int ld;  // row stride of both token-axis code layouts (scales: ld / 32)
   const int32_t* kofs;
@@ -74,9 +80,9 @@ struct MxWgradParams : MxParams {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-template <int EP, typename Params>
+template <int EP>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_mx_kernel(const Params prm) {
+void grouped_gemm_mx_kernel(const MxParams prm) {
   __shared__ __attribute__((aligned(1024))) uint8_t sP0[kTileBytes], sP1[kTileBytes], sP2[kTileBytes], sP3[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sQ0[kTileBytes], sQ1[kTileBytes], sQ2[kTileBytes], sQ3[kTileBytes];
   __shared__ int32_t s_off[kMaxE + 1];
@@ -90,16 +96,9 @@ void grouped_gemm_mx_kernel(const Params prm) {
   const int E = prm.E;
   const int l32 = lane & 31, lhi = lane >> 5;
 
-  for (int e = tid; e <= E; e += 256) {
-    if constexpr (EP == MX_WGRAD) s_off[e] = prm.kofs[e];
-    else s_off[e] = prm.offsets[e];
-  }
+  for (int e = tid; e <= E; e += 256) s_off[e] = prm.offsets[e];
   __syncthreads();
-  if (EP == MX_WGRAD && tid == 0) {  // every expert: the whole [R, N] output; s_off holds the K offsets
-    const int per = (int)(prm.R / kBM) * prm.n_tiles;
-    for (int e = 0; e <= E; ++e) s_tstart[e] = e * per;
-  }
-  if (EP != MX_WGRAD && tid == 0) {  // nondecreasing offsets inside [0, R]; per-expert tile starts
+  if (tid == 0) {  // nondecreasing offsets inside [0, R]; per-expert tile starts
     int prev = 0, run = 0;
     for (int e = 0; e <= E; ++e) {
       int v = s_off[e];
@@ -133,8 +132,7 @@ void grouped_gemm_mx_kernel(const Params prm) {
     else return sQ3;
   };
 
-  int ld = prm.K;  // code row stride of P and Q (K-contiguous operands)
-  if constexpr (EP == MX_WGRAD) ld = prm.ld;
+  const int ld = prm.K;  // code row stride of P and Q (K-contiguous operands)
   const int64_t kscale = ld / 32;
   const int nk_all = prm.K / kStepK;  // a multiple of 4 (K % 256 == 0)
 
@@ -145,37 +143,22 @@ void grouped_gemm_mx_kernel(const Params prm) {
       if (s_tstart[mid] <= t) lo = mid; else hi = mid - 1;
     }
     int e = lo;
-    const int me = (EP == MX_WGRAD) ? (int)prm.R : s_off[e + 1] - s_off[e];
+    const int me = s_off[e + 1] - s_off[e];
     const int mte = (me + kBM - 1) / kBM;
     const int local = t - s_tstart[e];
-    int mt, nt;
-    if constexpr (EP == MX_WGRAD) {
-      // groups of 8 m-tiles, n fastest over the group: the 32 consecutive tiles one XCD
-      // runs at a time form an 8 x 4 block whose operand slabs (~3.4 MB at K = 1100)
-      // stay in its L2; m fastest over all m-tiles re-read every Q slab once per n-tile
-      constexpr int GM = 8;
-      const int span = GM * prm.n_tiles;
-      const int grp = local / span, rem = local - grp * span;
-      const int gm = min(GM, mte - grp * GM);
-      mt = grp * GM + rem % gm;
-      nt = rem / gm;
-    } else {
-      mt = local % mte;
-      nt = local / mte;
-    }
+    int mt = local % mte;
+    int nt = local / mte;
     e = __builtin_amdgcn_readfirstlane(e);
     mt = __builtin_amdgcn_readfirstlane(mt);
     nt = __builtin_amdgcn_readfirstlane(nt);
-    const int row_beg = (EP == MX_WGRAD) ? 0 : __builtin_amdgcn_readfirstlane(s_off[e]);
-    const int row_end = (EP == MX_WGRAD) ? (int)prm.R : __builtin_amdgcn_readfirstlane(s_off[e + 1]);
+    const int row_beg = __builtin_amdgcn_readfirstlane(s_off[e]);
+    const int row_end = __builtin_amdgcn_readfirstlane(s_off[e + 1]);
     const int tile_row = row_beg + mt * kBM;
-    // K steps of 64 values, a multiple of 4 (K % 256 == 0; the expert's padded rows for MX_WGRAD)
-    const int nk = (EP == MX_WGRAD) ? __builtin_amdgcn_readfirstlane((s_off[e + 1] - s_off[e]) / kStepK) : nk_all;
-    const int k_beg = (EP == MX_WGRAD) ? __builtin_amdgcn_readfirstlane(s_off[e]) : 0;
+    const int nk = nk_all;  // K steps of 64 values, a multiple of 4 (K % 256 == 0)
 
     // P row of local tile row r (SWIGLU: gate rows then up rows of the same columns)
     auto p_row = [&](int r) -> int {
-      if constexpr (EP == MX_SWIGLU || EP == MX_SWIGLU_SAVE) return (r < 128) ? nt * 128 + r : prm.I + nt * 128 + (r - 128);
+      if constexpr (EP == MX_SWIGLU) return (r < 128) ? nt * 128 + r : prm.I + nt * 128 + (r - 128);
       else return nt * kBN + r;
     };
     auto q_row = [&](int r) -> int {
@@ -185,9 +168,9 @@ void grouped_gemm_mx_kernel(const Params prm) {
 
     // ---- copies: identical lane mapping to the bf16 kernel (64-byte rows) ----
     const int dma_row0 = wave * 16 + (lane >> 2);
-    const uint8_t* pbase = ((EP == MX_WGRAD) ? prm.tab[0] : prm.tab[e]) + k_beg;
+    const uint8_t* pbase = prm.tab[e];
     uint32_t p_off[4], q_off[4];
-    const uint8_t* q_tile = prm.q + (int64_t)tile_row * ld + k_beg;
+    const uint8_t* q_tile = prm.q + (int64_t)tile_row * ld;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = i * 64 + dma_row0;
@@ -210,8 +193,8 @@ void grouped_gemm_mx_kernel(const Params prm) {
     constexpr int kDma = 8;
 
     // ---- scales: per sub-tile, this lane's row; 8 bytes per 4-step group ----
-    const uint8_t* ps_base = ((EP == MX_WGRAD) ? prm.tab_s[0] : prm.tab_s[e]) + k_beg / 32;
-    const uint8_t* qs_base = prm.q_s + (int64_t)tile_row * kscale + k_beg / 32;
+    const uint8_t* ps_base = prm.tab_s[e];
+    const uint8_t* qs_base = prm.q_s + (int64_t)tile_row * kscale;
     uint32_t ps_off[4], qs_off[4];
 #pragma unroll
     for (int t2 = 0; t2 < 4; ++t2) {
@@ -260,8 +243,8 @@ void grouped_gemm_mx_kernel(const Params prm) {
     };
     i32x8_t QA[4], QB[4], P01[2], P23[2];
 
-    // prologue (none for an expert without rows in MX_WGRAD: its gradient is zero)
-    if (EP != MX_WGRAD || nk > 0) {
+    // prologue
+    {
       load_scales(0);
       issue_dma(0, S0{});
       if (nk > 1) issue_dma(1, S1{});
@@ -419,11 +402,8 @@ void grouped_gemm_mx_kernel(const Params prm) {
     };
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    if constexpr (EP == MX_STORE || EP == MX_WGRAD) {
-      void* cbase;
-      if constexpr (EP == MX_WGRAD) cbase = prm.ctab[e];
-      else cbase = prm.c;
-      bf16_t* c0 = reinterpret_cast<bf16_t*>(cbase) + (int64_t)nt * kBN;
+    if constexpr (EP == MX_STORE) {
+      bf16_t* c0 = reinterpret_cast<bf16_t*>(prm.c) + (int64_t)nt * kBN;
       put_acc(B0{});
       put_acc(B1{});
       lds_barrier();
@@ -431,15 +411,6 @@ void grouped_gemm_mx_kernel(const Params prm) {
       drain(B1{}, c0 + 128, prm.N);
       lds_barrier();  // read out before the next tile's copies land
     } else {
-    if constexpr (EP == MX_SWIGLU_SAVE) {  // z: gate columns (block 0), up columns (block 1)
-      bf16_t* z0 = reinterpret_cast<bf16_t*>(prm.z_save) + (int64_t)nt * 128;
-      put_acc(B0{});
-      put_acc(B1{});
-      lds_barrier();
-      drain(B0{}, z0, 2 * prm.I);
-      drain(B1{}, z0 + prm.I, 2 * prm.I);
-      lds_barrier();
-    }
 #pragma unroll
     for (int sm = 0; sm < 4; ++sm) {
       const int64_t mg = (int64_t)tile_row + wm * 128 + sm * 32 + l32;
@@ -459,12 +430,6 @@ void grouped_gemm_mx_kernel(const Params prm) {
           amax = fmaxf(amax, __shfl_xor(amax, 32));
           const int sx = mx_scale_exponent(amax);
           const int64_t col0 = (int64_t)nt * 128 + wn * 64 + sn * 32;
-          if constexpr (EP == MX_SWIGLU_SAVE) {  // h in bf16, block-0 layout (its 128 columns)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4)
-              put(B0{}, sm, sn, i4,
-                  make_uint2(pack_bf16x2(h[i4 * 4 + 0], h[i4 * 4 + 1]), pack_bf16x2(h[i4 * 4 + 2], h[i4 * 4 + 3])));
-          }
           if (valid) {
             uint8_t* C = reinterpret_cast<uint8_t*>(prm.c) + mg * prm.I + col0;
 #pragma unroll
@@ -477,11 +442,6 @@ void grouped_gemm_mx_kernel(const Params prm) {
           }
         }
       }
-    }
-    if constexpr (EP == MX_SWIGLU_SAVE) {
-      lds_barrier();
-      drain(B0{}, reinterpret_cast<bf16_t*>(prm.h_save) + (int64_t)nt * 128, prm.I);
-      lds_barrier();  // read out before the next tile's copies land
     }
     }
   }
@@ -852,9 +812,21 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
 // Epilogues: MX_STORE (bf16 rows through LDS), MX_SWIGLU (h = silu(G) U p quantised to
 // MXFP8 along I: a 32-value block is one sub-tile column span of a row, 16 values in
 // lane l and 16 in lane l ^ 32) and MX_SWIGLU_SAVE (also z and h in bf16, through LDS).
-template <int EP>
+// MX_WGRAD (MxWgradParams): the weight gradients on token-axis operands, as in the
+// 64-value-step kernel, with step-major scales: step s of expert e is step
+// kofs[e] / 128 + s of the padded token axis, whose words start at that step times the
+// operand's row count.
+// The K loop has no guarded steps: steps that skip copies past the end would make
+// control-flow joins, where the compiler drains every copy in flight before the next LDS
+// reads (such a step cost 2-4 times a full one; a weight gradient has only about 8 steps
+// at 1000 tokens per expert). It runs whole groups of 5 full steps instead, the first
+// (5 - nk % 5) % 5 of them zero steps: their copies have an empty buffer range (they
+// land as zeros in LDS), their scale words are those of a real step, and their products
+// are exact zeros, which leave the +0 accumulators unchanged. The zero steps run while
+// the first real copies are in flight.
+template <int EP, typename Params = MxParams>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_mxw_kernel(const MxParams prm) {
+void grouped_gemm_mxw_kernel(const Params prm) {
   __shared__ __attribute__((aligned(1024))) uint8_t sH0[kXTile], sH1[kXTile], sH2[kXTile];
   __shared__ __attribute__((aligned(1024))) uint8_t sH3[kXTile], sH4[kXTile];
 
@@ -886,21 +858,25 @@ void grouped_gemm_mxw_kernel(const MxParams prm) {
     v = v < prev ? prev : v;
     return v > R ? R : v;
   };
+  constexpr bool wgrad = EP == MX_WGRAD;
   int total = 0;
-  {
+  int e_w = 0, ob = 0, oe = 0, ts_w = 0, nt_w = 0;
+  if constexpr (wgrad) {  // every expert owns the whole [R, N] output
+    total = E * (R / kBM) * prm.n_tiles;
+  } else {
     int prev = 0;
     for (int x = 0; x < E; ++x) {
       const int en = clamp_off(prm.offsets[x + 1], prev);
       total += ((en - prev + kBM - 1) / kBM) * prm.n_tiles;
       prev = en;
     }
+    oe = clamp_off(prm.offsets[1], 0);
+    nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
   }
-  int e_w = 0;
-  int ob = 0;
-  int oe = clamp_off(prm.offsets[1], 0);
-  int ts_w = 0;
-  int nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
-  const int nk = K / kXBK;
+  // row stride of both code arrays: K for K-contiguous operands, the padded token axis
+  // for the weight gradients
+  int ld = K;
+  if constexpr (wgrad) ld = prm.ld;
 
   const uint32_t fragP = (uint32_t)((wn * 64 + l32) * 128);
   const uint32_t fragQ = (uint32_t)((wm * 128 + l32) * 128);
@@ -914,22 +890,44 @@ void grouped_gemm_mxw_kernel(const MxParams prm) {
 
   for (int t = logical; t < total; t += nwg) {
     // ---------------- tile decode ----------------
-    while (e_w < E && t >= ts_w + nt_w) {
-      ts_w += nt_w;
-      ++e_w;
-      ob = oe;
-      if (e_w < E) {
-        oe = clamp_off(prm.offsets[e_w + 1], ob);
-        nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
+    int e, mt, nt, nk, k_beg = 0, pad = 0;
+    if constexpr (wgrad) {
+      // groups of 8 m-tiles, n fastest over the group: the 32 consecutive tiles one XCD
+      // runs at a time form an 8 x 4 block whose operand slabs stay in its L2
+      constexpr int GM = 8;
+      const int mte = R / kBM;
+      const int per = mte * prm.n_tiles;
+      e = t / per;
+      const int local = t - e * per;
+      const int span = GM * prm.n_tiles;
+      const int grp = local / span, rem = local - grp * span;
+      const int gm = min(GM, mte - grp * GM);
+      mt = grp * GM + rem % gm;
+      nt = rem / gm;
+      e = __builtin_amdgcn_readfirstlane(e);
+      k_beg = __builtin_amdgcn_readfirstlane(prm.kofs[e]);
+      nk = __builtin_amdgcn_readfirstlane((prm.kofs[e + 1] - k_beg) / kXBK);
+      pad = (5 - nk % 5) % 5;
+      ob = 0;
+      oe = R;
+    } else {
+      while (e_w < E && t >= ts_w + nt_w) {
+        ts_w += nt_w;
+        ++e_w;
+        ob = oe;
+        if (e_w < E) {
+          oe = clamp_off(prm.offsets[e_w + 1], ob);
+          nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
+        }
       }
-    }
-    if (e_w >= E) break;
-    int e = e_w, mt, nt;
-    {
+      if (e_w >= E) break;
+      e = e_w;
       const int local = t - ts_w;
       const int mte = (oe - ob + kBM - 1) / kBM;
       mt = local % mte;
       nt = local / mte;
+      nk = K / kXBK;
+      pad = (5 - nk % 5) % 5;
     }
     e = __builtin_amdgcn_readfirstlane(e);
     mt = __builtin_amdgcn_readfirstlane(mt);
@@ -944,21 +942,26 @@ void grouped_gemm_mxw_kernel(const MxParams prm) {
     };
 
     // ---------------- operands ----------------
-    const uint8_t* p_tile = prm.tab[e] + (int64_t)p_row(0) * K;
-    const uint8_t* q_tile = prm.q + (int64_t)tile_row * K;
-    const uint32_t off0 = (uint32_t)((int64_t)kc_row0 * K + kc_chunk * 16);
-    const int64_t q_extent = (int64_t)(row_end - tile_row) * K;
+    const uint8_t* p_tile = prm.tab[wgrad ? 0 : e] + (int64_t)p_row(0) * ld + k_beg;
+    const uint8_t* q_tile = prm.q + (int64_t)tile_row * ld + k_beg;
+    const uint32_t off0 = (uint32_t)((int64_t)kc_row0 * ld + kc_chunk * 16);
+    const int64_t q_extent = wgrad ? kAll : (int64_t)(row_end - tile_row) * ld;
     const int p_up = (EP == MX_SWIGLU || EP == MX_SWIGLU_SAVE) ? prm.I - 128 : 0;
+    // step kt of the loop is step kt - pad of the operands: an empty range (zeros) outside [0, nk)
     auto copy_op = [&](const uint8_t* tile, int up, int64_t extent, int kt, uint8_t* dst) {
-      const int64_t at = (int64_t)kt * kXBK;
-      int64_t nrec = extent - at;
-      nrec = nrec < 0 ? 0 : (nrec > kAll ? kAll : nrec);
+      const int ks = kt - pad;
+      const int64_t at = (int64_t)ks * kXBK;
+      int64_t lim = extent - at;
+      lim = lim < 0 ? 0 : (lim > kAll ? kAll : lim);
+      // read back as a wavefront-uniform value: a select left in a vector register would
+      // make the whole descriptor a vector operand and every copy a waterfall loop
+      const int64_t nrec = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ks < (uint32_t)nk ? (int)(uint32_t)lim : 0);
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)(tile + at), (short)0, (int)(uint32_t)nrec, kBufferFlags);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t rows = (uint32_t)(i * 32 + (i >= 4 ? up : 0));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 4096), 16, off0, (int)(rows * (uint32_t)K),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 4096), 16, off0, (int)(rows * (uint32_t)ld),
                                                  0, 0);
       }
     };
@@ -968,11 +971,12 @@ void grouped_gemm_mxw_kernel(const MxParams prm) {
     // scale words (step-major): P sub-tile sn is tile rows sub_n(sn, wn) + [0, 32); Q
     // sub-tile sm is wm * 128 + sm * 32 + [0, 32), rows past the expert clamped to its
     // last row (their products are discarded). Step kt's words start kt * rows words in.
-    const __amdgpu_buffer_rsrc_t ps_rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)prm.tab_s[e], (short)0, (int)0xFFFFFFFF, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t qs_rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)prm.q_s, (short)0, (int)0xFFFFFFFF, kBufferFlags);
     const int p_step = 4 * prm.N, q_step = 4 * R;  // bytes per K step of the two scale arrays
+    const int k_step0 = k_beg / kXBK;               // the expert's first step (weight gradients)
+    const __amdgpu_buffer_rsrc_t ps_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(prm.tab_s[wgrad ? 0 : e] + (int64_t)k_step0 * p_step), (short)0, (int)0xFFFFFFFF, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t qs_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(prm.q_s + (int64_t)k_step0 * q_step), (short)0, (int)0xFFFFFFFF, kBufferFlags);
     // One load serves two sub-tiles: lanes 0-31 read the row of sub-tile 2j, lanes 32-63
     // that of sub-tile 2j + 1 (the same row index l32); raw word j of a step holds them.
     uint32_t ps_off[2], qs_off[2];
@@ -984,6 +988,8 @@ void grouped_gemm_mxw_kernel(const MxParams prm) {
     }
     // raw words of a step: [0, 1] P sub-tile pairs, [2, 3] Q sub-tile pairs
     auto load_scales = [&](int kt, uint32_t* w) {
+      kt -= pad;  // a zero step takes the words of the nearest real step
+      kt = kt < 0 ? 0 : (kt >= nk ? nk - 1 : kt);
 #pragma unroll
       for (int j = 0; j < 2; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(ps_rs, ps_off[j], kt * p_step, 0);
 #pragma unroll
@@ -1060,9 +1066,8 @@ void grouped_gemm_mxw_kernel(const MxParams prm) {
     // per-tensor kernel. The scale loads are ordinary buffer loads, which the scheduler
     // could otherwise move between the copies (those stay ordered among themselves
     // through M0) and so break that count: a scheduling barrier keeps them ahead.
-    auto kstep = [&](int kt, auto V, auto FULL) {
+    auto kstep = [&](int kt, auto V) {
       constexpr int v = decltype(V)::value;
-      constexpr bool full = decltype(FULL)::value;
       using HP = std::integral_constant<int, (2 * v) % 5>;
       using HQ = std::integral_constant<int, (2 * v + 1) % 5>;
       using HPn = std::integral_constant<int, (2 * v + 2) % 5>;
@@ -1072,17 +1077,15 @@ void grouped_gemm_mxw_kernel(const MxParams prm) {
       read_q(HQ{}, 1, fb1);
       mfma_slice(fb0, sc, std::integral_constant<int, 0>{}, true, HP{}, 1);
       interleave_a();
-      if (full) wait_vm<8>();
-      else wait_vm_le(kt + 2 < nk ? 8 : 0);
-      lds_barrier();                                  // also waits for every read of step kt
+      wait_vm<8>();
+      lds_barrier();                  // also waits for every read of step kt
       uint32_t r2[4];
-      if (full || kt + 2 < nk) load_scales(kt + 2, r2);
+      load_scales(kt + 2, r2);
       __builtin_amdgcn_sched_barrier(0);
-      if (full || kt + 2 < nk) copy_Q(kt + 2, HP{});  // Q of step kt+2: half-slot 2(kt+2)+1 = 2kt mod 5
-      if (full || kt + 3 < nk) copy_P(kt + 3, HQ{});  // P of step kt+3: half-slot 2(kt+3) = 2kt+1 mod 5
-      const bool next = full || kt + 1 < nk;
-      if (next) read_q(HQn{}, 0, fb0);
-      mfma_slice(fb1, sc, std::integral_constant<int, 1>{}, next, HPn{}, 0);
+      copy_Q(kt + 2, HP{});           // Q of step kt+2: half-slot 2(kt+2)+1 = 2kt mod 5
+      copy_P(kt + 3, HQ{});           // P of step kt+3: half-slot 2(kt+3) = 2kt+1 mod 5
+      read_q(HQn{}, 0, fb0);          // (past the last step: zeros or in-flight data, never used)
+      mfma_slice(fb1, sc, std::integral_constant<int, 1>{}, true, HPn{}, 0);
       interleave_b();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1100,21 +1103,14 @@ void grouped_gemm_mxw_kernel(const MxParams prm) {
     using H2 = std::integral_constant<int, 2>;
     using H3 = std::integral_constant<int, 3>;
     using H4 = std::integral_constant<int, 4>;
-    using Full = std::true_type;
-    using Tail = std::false_type;
-    auto steps5 = [&](int kt0, auto FULL) {
-      static_for<5>([&](auto V) {
-        constexpr int v = decltype(V)::value;
-        if (decltype(FULL)::value || kt0 + v < nk) kstep(kt0 + v, V, FULL);
-      });
-    };
+    auto steps5 = [&](int kt0) { static_for<5>([&](auto V) { kstep(kt0 + decltype(V)::value, V); }); };
     // Prologue: the scale words of steps 0 and 1 ahead of every copy, then the copies of
-    // steps 0-2, so that step 0's wait sees the steady state's pattern.
-    int kt = 0;
-    load_scales(0, r0);
-    if (nk > 1) load_scales(1, r1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (nk >= 8) {
+    // steps 0-2, so that step 0's wait sees the steady state's pattern. (A weight
+    // gradient of an expert without rows has no steps: its tile is zeros.)
+    if (nk > 0) {
+      load_scales(0, r0);
+      load_scales(1, r1);
+      __builtin_amdgcn_sched_barrier(0);
       copy_P(0, H0{});
       copy_Q(0, H1{});
       copy_P(1, H2{});
@@ -1123,20 +1119,10 @@ void grouped_gemm_mxw_kernel(const MxParams prm) {
       wait_vm<24>();  // the scale words and step 0's copies complete
       lds_barrier();
       read_first(H0{}, H1{});
-      for (; kt + 7 < nk; kt += 5) steps5(kt, Full{});  // the copies of all five steps exist
-    } else {
-      copy_P(0, H0{});
-      copy_Q(0, H1{});
-      if (nk > 1) {
-        copy_P(1, H2{});
-        copy_Q(1, H3{});
-      }
-      if (nk > 2) copy_P(2, H4{});
-      wait_vm_le((nk > 1) * 16 + (nk > 2) * 8);  // step 0 complete
-      lds_barrier();
-      read_first(H0{}, H1{});
+      const int n_run = nk + pad;
+      for (int kt = 0; kt < n_run; kt += 5) steps5(kt);
+      wait_vm<0>();   // the zero copies issued past the last step land before LDS is reused
     }
-    for (; kt < nk; kt += 5) steps5(kt, Tail{});
     // every wavefront is done with every half-slot before the epilogue uses LDS
     lds_barrier();
 
@@ -1181,11 +1167,14 @@ void grouped_gemm_mxw_kernel(const MxParams prm) {
                            pack_bf16x2(acc[sn][sm][i4 * 4 + 2], acc[sn][sm][i4 * 4 + 3])));
           }
     };
-    if constexpr (EP == MX_STORE) {
+    if constexpr (EP == MX_STORE || EP == MX_WGRAD) {
       acc_block(0, sH0, sH1);
       acc_block(1, sH2, sH3);
       lds_barrier();
-      bf16_t* c0 = reinterpret_cast<bf16_t*>(prm.c) + (int64_t)nt * kBN;
+      void* cbase;
+      if constexpr (wgrad) cbase = prm.ctab[e];
+      else cbase = prm.c;
+      bf16_t* c0 = reinterpret_cast<bf16_t*>(cbase) + (int64_t)nt * kBN;
       drain(wv < 2 ? sH0 : sH1, c0, prm.N);
       drain(wv < 2 ? sH2 : sH3, c0 + 128, prm.N);
       lds_barrier();  // read out before the next tile's copies land
@@ -1259,9 +1248,8 @@ static moe_status launch(int ep, bool pt, const MxParams& p, int64_t max_tiles, 
     else if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_mxw_kernel<MX_SWIGLU>), g, b, 0, s, p);
     else hipLaunchKernelGGL((grouped_gemm_mxw_kernel<MX_STORE>), g, b, 0, s, p);
   } else {
-    if (ep == MX_SWIGLU && p.z_save) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU_SAVE, MxParams>), g, b, 0, s, p);
-    else if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU, MxParams>), g, b, 0, s, p);
-    else hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_STORE, MxParams>), g, b, 0, s, p);
+    if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_SWIGLU>), g, b, 0, s, p);
+    else hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_STORE>), g, b, 0, s, p);
   }
   return check_launch(what);
 }
@@ -1270,7 +1258,7 @@ static moe_status launch_wgrad(const MxWgradParams& p, int64_t max_tiles, hipStr
   if (max_tiles <= 0) return MOE_OK;
   int64_t grid = num_cus();
   if (max_tiles < grid) grid = max_tiles;
-  hipLaunchKernelGGL((grouped_gemm_mx_kernel<MX_WGRAD, MxWgradParams>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((grouped_gemm_mxw_kernel<MX_WGRAD, MxWgradParams>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return check_launch(what);
 }
 
@@ -1683,9 +1671,11 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
   p.n_tiles = H / kBN;
   if ((st = launch(MX_STORE, false, p, mtiles * p.n_tiles, s, "MXFP8 gate_up dgrad", true)) != MOE_OK) return st;
 
-  // weight gradients on the token-axis layouts
-  if ((st = launch_mxfp8_colwise(dy, R, H, E, offsets, 256, kc, ws + L.dyc, ws + L.dycs, kofs, s)) != MOE_OK) return st;
-  if ((st = launch_mxfp8_colwise(h, R, I, E, offsets, 256, kc, ws + L.hc, ws + L.hcs, nullptr, s)) != MOE_OK) return st;
+  // weight gradients on the token-axis layouts (wide-step kernel: step-major scales)
+  if ((st = launch_mxfp8_colwise(dy, R, H, E, offsets, 256, kc, ws + L.dyc, ws + L.dycs, kofs, s, true)) != MOE_OK)
+    return st;
+  if ((st = launch_mxfp8_colwise(h, R, I, E, offsets, 256, kc, ws + L.hc, ws + L.hcs, nullptr, s, true)) != MOE_OK)
+    return st;
   MxWgradParams w;
   std::memset(&w, 0, sizeof(w));
   w.kofs = kofs;
@@ -1701,9 +1691,11 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
   w.I = I;
   w.n_tiles = I / kBN;
   if ((st = launch_wgrad(w, (int64_t)E * (H / kBM) * w.n_tiles, s, "MXFP8 down wgrad")) != MOE_OK) return st;
-  if ((st = launch_mxfp8_colwise(dz, R, 2 * I, E, offsets, 256, kc, ws + L.dzc, ws + L.dzcs, nullptr, s)) != MOE_OK)
+  if ((st = launch_mxfp8_colwise(dz, R, 2 * I, E, offsets, 256, kc, ws + L.dzc, ws + L.dzcs, nullptr, s, true)) !=
+      MOE_OK)
     return st;
-  if ((st = launch_mxfp8_colwise(x, R, H, E, offsets, 256, kc, ws + L.xc, ws + L.xcs, nullptr, s)) != MOE_OK) return st;
+  if ((st = launch_mxfp8_colwise(x, R, H, E, offsets, 256, kc, ws + L.xc, ws + L.xcs, nullptr, s, true)) != MOE_OK)
+    return st;
   w.q = ws + L.dzc;
   w.q_s = ws + L.dzcs;
   w.tab[0] = ws + L.xc;
