@@ -509,6 +509,7 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
   int ts_w = 0;
   int nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
   const int nk = K / kXBK;
+  const int pad = (5 - nk % 5) % 5;  // zero steps ahead of the K loop (as in the MXFP8 kernel below)
 
   // fragment addresses: sub-tile rows start at multiples of 32, where swz8 depends on
   // the lane's row within the sub-tile only; half h of slice s is logical chunk
@@ -564,10 +565,13 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
     const uint32_t off0 = (uint32_t)((int64_t)kc_row0 * K + kc_chunk * 16);
     const int64_t q_extent = (int64_t)(row_end - tile_row) * K;
     const int p_up = (EP == MX_SWIGLU) ? prm.I - 128 : 0;
+    // step kt of the loop is step kt - pad of the operands: an empty range (zeros) outside [0, nk)
     auto copy_op = [&](const uint8_t* tile, int up, int64_t extent, int kt, uint8_t* dst) {
-      const int64_t at = (int64_t)kt * kXBK;
-      int64_t nrec = extent - at;
-      nrec = nrec < 0 ? 0 : (nrec > kAll ? kAll : nrec);
+      const int ks = kt - pad;
+      const int64_t at = (int64_t)ks * kXBK;
+      int64_t lim = extent - at;
+      lim = lim < 0 ? 0 : (lim > kAll ? kAll : lim);
+      const int64_t nrec = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ks < (uint32_t)nk ? (int)(uint32_t)lim : 0);
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)(tile + at), (short)0, (int)(uint32_t)nrec, kBufferFlags);
 #pragma unroll
@@ -644,9 +648,8 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
     // Per step the copies are issued in the order Q of step kt+2, P of step kt+3, so
     // when step kt+1 must have landed only P of step kt+2 (the 8 most recent) may be
     // in flight.
-    auto kstep = [&](int kt, auto V, auto FULL) {
+    auto kstep = [&](int kt, auto V) {
       constexpr int v = decltype(V)::value;
-      constexpr bool full = decltype(FULL)::value;
       using HP = std::integral_constant<int, (2 * v) % 5>;
       using HQ = std::integral_constant<int, (2 * v + 1) % 5>;
       using HPn = std::integral_constant<int, (2 * v + 2) % 5>;
@@ -654,14 +657,12 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
       read_q(HQ{}, 1, fb1);
       mfma_slice(fb0, std::integral_constant<int, 0>{}, true, HP{}, 1);
       interleave_a();
-      if (full) wait_vm<8>();
-      else wait_vm_le(kt + 2 < nk ? 8 : 0);
-      lds_barrier();                                  // also waits for every read of step kt
-      if (full || kt + 2 < nk) copy_Q(kt + 2, HP{});  // Q of step kt+2: half-slot 2(kt+2)+1 = 2kt mod 5
-      if (full || kt + 3 < nk) copy_P(kt + 3, HQ{});  // P of step kt+3: half-slot 2(kt+3) = 2kt+1 mod 5
-      const bool next = full || kt + 1 < nk;
-      if (next) read_q(HQn{}, 0, fb0);
-      mfma_slice(fb1, std::integral_constant<int, 0>{}, next, HPn{}, 0);
+      wait_vm<8>();
+      lds_barrier();                  // also waits for every read of step kt
+      copy_Q(kt + 2, HP{});           // Q of step kt+2: half-slot 2(kt+2)+1 = 2kt mod 5
+      copy_P(kt + 3, HQ{});           // P of step kt+3: half-slot 2(kt+3) = 2kt+1 mod 5
+      read_q(HQn{}, 0, fb0);          // (past the last step: never used)
+      mfma_slice(fb1, std::integral_constant<int, 0>{}, true, HPn{}, 0);
       interleave_b();
     };
     auto read_first = [&](auto HP, auto HQ) {
@@ -674,38 +675,17 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
     using H2 = std::integral_constant<int, 2>;
     using H3 = std::integral_constant<int, 3>;
     using H4 = std::integral_constant<int, 4>;
-    using Full = std::true_type;
-    using Tail = std::false_type;
-    auto steps5 = [&](int kt0, auto FULL) {
-      static_for<5>([&](auto V) {
-        constexpr int v = decltype(V)::value;
-        if (decltype(FULL)::value || kt0 + v < nk) kstep(kt0 + v, V, FULL);
-      });
-    };
-    int kt = 0;
-    if (nk >= 8) {
-      copy_P(0, H0{});
-      copy_Q(0, H1{});
-      copy_P(1, H2{});
-      copy_Q(1, H3{});
-      copy_P(2, H4{});
-      wait_vm<24>();  // step 0 complete
-      lds_barrier();
-      read_first(H0{}, H1{});
-      for (; kt + 7 < nk; kt += 5) steps5(kt, Full{});  // the copies of all five steps exist
-    } else {
-      copy_P(0, H0{});
-      copy_Q(0, H1{});
-      if (nk > 1) {
-        copy_P(1, H2{});
-        copy_Q(1, H3{});
-      }
-      if (nk > 2) copy_P(2, H4{});
-      wait_vm_le((nk > 1) * 16 + (nk > 2) * 8);  // step 0 complete
-      lds_barrier();
-      read_first(H0{}, H1{});
-    }
-    for (; kt < nk; kt += 5) steps5(kt, Tail{});
+    copy_P(0, H0{});
+    copy_Q(0, H1{});
+    copy_P(1, H2{});
+    copy_Q(1, H3{});
+    copy_P(2, H4{});
+    wait_vm<24>();  // step 0 complete
+    lds_barrier();
+    read_first(H0{}, H1{});
+    const int n_run = nk + pad;
+    for (int kt = 0; kt < n_run; kt += 5) static_for<5>([&](auto V) { kstep(kt + decltype(V)::value, V); });
+    wait_vm<0>();   // the zero copies issued past the last step land before LDS is reused
     // every wavefront is done with every half-slot before the epilogue uses LDS
     lds_barrier();
 
