@@ -29,7 +29,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .fp8_tensor import bf16_round
+from .fp8_tensor import bf16_round, fp8_tensor_qdq
 from .mxfp8 import mxfp8_qdq
 
 __all__ = [
@@ -37,6 +37,7 @@ __all__ = [
     "grouped_mlp_forward",
     "grouped_linear", "grouped_mlp_forward_mxfp8", "unpermute_combine",
     "grouped_mlp_backward", "moe_ffn_backward", "gather_rows", "grouped_mlp_backward_mxfp8",
+    "grouped_mlp_backward_fp8_tensor",
 ]
 
 f64 = np.float64
@@ -385,3 +386,66 @@ def grouped_mlp_backward_mxfp8(dy_perm, x_perm, z_save, h_save, w_gate_up, w_dow
         dw2[e] = qt(dy, a, b).T @ qt(h, a, b)
         dw1[e] = qt(dZ, 0, b - a).T @ qt(x, a, b)
     return dict(dx_perm=dx, dw_gate_up=dw1, dw_down=dw2, dprob_perm=dprob)
+
+
+def grouped_mlp_backward_fp8_tensor(dy_perm, x_perm, z_save, h_save, w_gate_up, w_down, offsets, prob_perm,
+                                    quantize=True, round_bf16=True):
+    """The grouped MLP backward with every GEMM operand quantised per tensor (Challenge
+    2's FP8: one scaling factor for a whole tensor; the factor is amax / 448 as in
+    fp8_tensor_quantize). The tensors are those of the forward: dY, dZ, h and x each over
+    all routed rows, W1_e and W2_e each per expert.
+
+      dH_e  = Q(dY)_e Q(W2_e)
+      dprob, dA, dG, dU from dH, the saved z = [G, U] and prob, as in grouped_mlp_backward
+      dx_e  = Q(dZ)_e Q(W1_e)
+      dW2_e = Q(dY)_e^T Q(h)_e
+      dW1_e = Q(dZ)_e^T Q(x)_e
+
+    One factor per tensor does not depend on the axis a GEMM reduces over, so each
+    tensor is quantised once and serves both GEMMs it enters; dZ's factor needs every
+    expert's dZ first. As in the MXFP8 backward, dH and dZ are rounded to bf16 (the
+    recipe keeps activations and their gradients in bf16) unless round_bf16 is False.
+    z_save [R, 2I] and h_save [R, I] are the forward's saved tensors, taken as given.
+    quantize=False drops every Q and both roundings. Also returns dz_perm, the dZ that
+    was quantised (bf16-rounded when round_bf16)."""
+    q = fp8_tensor_qdq if quantize else (lambda t: np.asarray(t, dtype=f64))
+    rnd = bf16_round if (quantize and round_bf16) else (lambda t: t)
+    dy = np.asarray(dy_perm, dtype=f64)
+    x = np.asarray(x_perm, dtype=f64)
+    z = np.asarray(z_save, dtype=f64)
+    h = np.asarray(h_save, dtype=f64)
+    p = np.asarray(prob_perm, dtype=f64)
+    off = np.asarray(offsets, dtype=np.int64)
+    E, twoI, H = w_gate_up.shape
+    I = twoI // 2
+    R = x.shape[0]
+    dx = np.zeros((R, H), f64)
+    dw1 = np.zeros((E, twoI, H), f64)
+    dw2 = np.zeros((E, H, I), f64)
+    dprob = np.zeros(R, f64)
+    dz = np.zeros((R, twoI), f64)
+    if R == 0:
+        return dict(dx_perm=dx, dw_gate_up=dw1, dw_down=dw2, dprob_perm=dprob, dz_perm=dz)
+    dyq, hq, xq = q(dy), q(h), q(x)
+    for e in range(E):           # dH, dprob, dZ; the down weight gradient
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        W2 = q(np.asarray(w_down[e], dtype=f64))
+        G, U = z[a:b, :I], z[a:b, I:]
+        sg = _sigmoid(G)
+        A = G * sg * U
+        dHs = rnd(dyq[a:b] @ W2)
+        dprob[a:b] = (dHs * A).sum(axis=1)
+        dA = dHs * p[a:b, None]
+        dz[a:b] = rnd(np.concatenate([dA * U * sg * (1.0 + G * (1.0 - sg)), dA * G * sg], axis=1))
+        dw2[e] = dyq[a:b].T @ hq[a:b]
+    dzq = q(dz)                   # one factor over every expert's rows
+    for e in range(E):           # dx and the gate_up weight gradient
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        W1 = q(np.asarray(w_gate_up[e], dtype=f64))
+        dx[a:b] = dzq[a:b] @ W1
+        dw1[e] = dzq[a:b].T @ xq[a:b]
+    return dict(dx_perm=dx, dw_gate_up=dw1, dw_down=dw2, dprob_perm=dprob, dz_perm=dz)
