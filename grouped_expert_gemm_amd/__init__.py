@@ -21,7 +21,7 @@ from ._lib import MOE_BF16, MOE_F32, MOE_FP8, MOE_MXFP8, MlpDesc, MoeError, chec
 
 __all__ = [
     "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
-    "fp8_tensor_quantize", "mxfp8_quantize_colwise", "mxfp8_pack_weight_bwd",
+    "fp8_tensor_quantize", "mxfp8_quantize_colwise", "fp8_tensor_quantize_colwise", "mxfp8_pack_weight_bwd",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu", "gemm_workspace",
     "workspace_size", "MoeError", "lib",
     "MOE_F32", "MOE_BF16", "MOE_MXFP8", "MOE_FP8",
@@ -202,6 +202,26 @@ def mxfp8_quantize_colwise(x: torch.Tensor, offsets: torch.Tensor, pad: int = 32
     check("mxfp8_quantize_colwise", lib().mxfp8_quantize_colwise(_p(x), R, C, E, _p(offsets), pad, kcap, _p(codes),
                                                                  _p(scales), _p(kofs), _stream(x.device)))
     return codes, scales, kofs
+
+
+def fp8_tensor_quantize_colwise(x: torch.Tensor, offsets: torch.Tensor, pad: int = 256):
+    """bf16 [R, C] with expert row offsets [E+1] -> (E4M3 codes [C, kcap], float32 scale
+    [1], padded offsets kofs [E+1]) with kcap = R + E * (pad - 1) rounded up to 128: the
+    per-tensor FP8 codes of x, each expert's rows zero-padded to a multiple of pad and
+    transposed to columns [kofs[e], kofs[e+1])."""
+    _need_cuda(x, offsets)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("fp8_tensor_quantize_colwise takes bfloat16")
+    x = x.contiguous()
+    R, C = x.shape
+    E = offsets.numel() - 1
+    kcap = (R + E * (pad - 1) + 127) // 128 * 128
+    codes = torch.zeros((C, kcap), dtype=torch.uint8, device=x.device)
+    scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    kofs = torch.empty(E + 1, dtype=torch.int32, device=x.device)
+    check("fp8_tensor_quantize_colwise", lib().fp8_tensor_quantize_colwise(
+        _p(x), R, C, E, _p(offsets), pad, kcap, _p(codes), _p(scale), _p(kofs), _stream(x.device)))
+    return codes, scale, kofs
 
 
 def mxfp8_pack_weight_bwd(w: torch.Tensor) -> torch.Tensor:

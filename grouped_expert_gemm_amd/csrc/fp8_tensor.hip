@@ -106,6 +106,105 @@ __global__ __launch_bounds__(256) void fp8t_finalize_kernel(uint32_t* words, int
   if (i < n) words[i] = __float_as_uint(scale_of_amax(words[i]));
 }
 
+// Transposed codes of x [R, C] (bf16, rows grouped by expert): out [C, kcap], expert
+// e's rows at columns [kofs[e], kofs[e] + m_e) of every output row, zero-padded to a
+// multiple of pad (the weight-gradient GEMMs' token-axis operand). One factor per
+// tensor means the codes are those of the row-major quantiser, only transposed. A
+// workgroup takes 128 rows x 64 columns of one expert's padded range through LDS
+// (16-byte loads, rows past the expert read as zeros); lane (q, c) encodes rows
+// 32q .. 32q + 31 of column c and stores them as two 16-byte stores. Tensor
+// blockIdx.y of the table; words: the tensors' amax bits (before fp8t_finalize).
+struct Fp8TTab {
+  const uint16_t* in[kTab];
+  uint8_t* out[kTab];
+};
+
+template <bool kRecip>
+__device__ __forceinline__ uint32_t encode4(const float* t, float s, float r) {
+  return e4m3_encode(quotient<kRecip>(t[0], s, r)) | (e4m3_encode(quotient<kRecip>(t[65], s, r)) << 8) |
+         (e4m3_encode(quotient<kRecip>(t[130], s, r)) << 16) | (e4m3_encode(quotient<kRecip>(t[195], s, r)) << 24);
+}
+
+__global__ __launch_bounds__(256) void fp8t_transpose_kernel(const Fp8TTab tab, int64_t R, int C, int E,
+                                                             const int32_t* __restrict__ offsets, int pad,
+                                                             int64_t kcap, const uint32_t* __restrict__ words,
+                                                             int32_t* __restrict__ kofs_out) {
+  __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int32_t s_kofs[MOE_MAX_EXPERTS + 1];
+  __shared__ int32_t s_item[MOE_MAX_EXPERTS + 1];
+  __shared__ float tile[128][65];
+  const int tid = threadIdx.x;
+  const int ncb = C / 64;
+  const uint16_t* __restrict__ x = tab.in[blockIdx.y];
+  uint8_t* __restrict__ codes = tab.out[blockIdx.y];
+  const float s = scale_of_amax(words[blockIdx.y]);
+  const float rcp = __fdiv_rn(1.f, s);
+  const bool fast = s >= 1.17549435e-38f && rcp >= 1.17549435e-38f && rcp <= 3.40282347e+38f;
+  if (tid == 0) {  // offsets made nondecreasing inside [0, R] (none: one expert of R rows); padded offsets
+    int prev = 0, kacc = 0, iacc = 0;
+    for (int e = 0; e <= E; ++e) {
+      int v = e == 0 ? 0 : (offsets ? offsets[e] : (int)R);
+      v = v < prev ? prev : v;
+      v = v > (int)R ? (int)R : v;
+      if (e > 0) {
+        const int m = v - prev;
+        const int kp = (m + pad - 1) / pad * pad;
+        s_kofs[e - 1] = kacc;
+        s_item[e - 1] = iacc;
+        kacc += kp;
+        iacc += ((kp / 32 + 3) / 4) * ncb;
+      }
+      s_off[e] = v;
+      prev = v;
+    }
+    s_kofs[E] = kacc;
+    s_item[E] = iacc;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && blockIdx.y == 0 && kofs_out)
+    for (int e = tid; e <= E; e += 256) kofs_out[e] = s_kofs[e];
+  const int total = s_item[E];
+  const int r = tid >> 3, c8 = (tid & 7) * 8;  // load: rows r + 32i, columns c8 .. c8 + 7
+  const int cc = tid & 63, q = tid >> 6;        // encode: rows 32q .. 32q + 31 of column cc
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_item[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int local = item - s_item[e];
+    const int j = local / ncb, cb = local - (local / ncb) * ncb;
+    const int64_t row0 = (int64_t)s_off[e] + 128 * j;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = row0 + r + 32 * i;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < s_off[e + 1]) v = *reinterpret_cast<const uint4*>(x + row * C + cb * 64 + c8);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        tile[r + 32 * i][c8 + 2 * h] = bf16_to_f32(w[h] & 0xFFFFu);
+        tile[r + 32 * i][c8 + 2 * h + 1] = bf16_to_f32(w[h] >> 16);
+      }
+    }
+    __syncthreads();
+    const int nblk = (s_kofs[e + 1] - s_kofs[e]) / 32;        // 32-row groups in the expert's padded range
+    if (q < nblk - 4 * j) {
+      uint32_t wd[8];
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        wd[g] = fast ? encode4<true>(&tile[32 * q + 4 * g][cc], s, rcp) : encode4<false>(&tile[32 * q + 4 * g][cc], s, rcp);
+      const int64_t col = (int64_t)cb * 64 + cc;
+      const int64_t k = (int64_t)s_kofs[e] + 128 * j + 32 * q;
+      uint4* dst = reinterpret_cast<uint4*>(codes + col * kcap + k);
+      dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+    }
+    __syncthreads();  // the tile is reused by the next item
+  }
+}
+
 unsigned grid_x(int64_t n8, int ntensors) {
   int64_t want = (n8 + 255) / 256;
   int64_t cap = (int64_t)num_cus() * 8 / ntensors;
@@ -115,6 +214,30 @@ unsigned grid_x(int64_t n8, int ntensors) {
 }
 
 }  // namespace
+
+moe_status fp8t_transpose(const void* const* in, uint8_t* const* out, int ntensors, int64_t R, int C, int E,
+                          const int32_t* offsets, int pad, int64_t kcap, const float* words, int32_t* kofs,
+                          hipStream_t s) {
+  if (ntensors <= 0 || C == 0) return MOE_OK;
+  // room for every expert's rows padded to a multiple of pad (one expert: R rounded up)
+  const int64_t room = offsets ? R + (int64_t)E * (pad - 1) : (R + pad - 1) / pad * pad;
+  if (C % 64 != 0 || pad <= 0 || pad % 32 != 0 || kcap % 32 != 0 || kcap < room || E < 1 || E > MOE_MAX_EXPERTS ||
+      (!offsets && E != 1) || ntensors > kTab || R > 0x7FFFFFFF)
+    return fail(MOE_ERR_UNSUPPORTED, "per-tensor FP8 transpose: unsupported shape");
+  Fp8TTab tab = {};
+  for (int t = 0; t < ntensors; ++t) {
+    tab.in[t] = (const uint16_t*)in[t];
+    tab.out[t] = out[t];
+  }
+  const int64_t items = (kcap / 32 + 3 * E) / 4 * (C / 64) + E * (C / 64);
+  int64_t grid = (int64_t)num_cus() * 16 / ntensors;
+  if (grid < 4) grid = 4;
+  if (items < grid) grid = items;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(fp8t_transpose_kernel, dim3((unsigned)grid, ntensors), dim3(256), 0, s, tab, R, C, E, offsets,
+                     pad, kcap, (const uint32_t*)words, kofs);
+  return check_launch("per-tensor FP8: transposed codes");
+}
 
 moe_status fp8t_zero(float* words, int n, hipStream_t s) {
   if (n <= 0) return MOE_OK;
@@ -182,5 +305,34 @@ extern "C" moe_status fp8_tensor_quantize(const void* in_bf16, int64_t n, uint8_
   uint8_t* out_tab[1] = {e4m3};
   if ((st = fp8t_amax(in_tab, 1, n, scale, s)) != MOE_OK) return st;
   if ((st = fp8t_quantize(in_tab, out_tab, 1, n, scale, s)) != MOE_OK) return st;
+  return fp8t_finalize(scale, 1, s);
+}
+
+extern "C" moe_status fp8_tensor_quantize_colwise(const void* x_bf16, int64_t R, int64_t C, int E,
+                                                  const int32_t* offsets, int pad, int64_t kcap, uint8_t* e4m3_t,
+                                                  float* scale, int32_t* kofs, void* stream) {
+  if (R < 0 || C < 0) return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_quantize_colwise: negative size");
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_quantize_colwise: E out of [1, 256]");
+  if (pad <= 0 || pad % 32 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_quantize_colwise: pad must be a positive multiple of 32");
+  if (C % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "fp8_tensor_quantize_colwise: C % 64 != 0");
+  if (kcap % 32 != 0 || kcap < R + (int64_t)E * (pad - 1))
+    return fail(MOE_ERR_INVALID_ARG,
+                "fp8_tensor_quantize_colwise: kcap must be a multiple of 32 and >= R + E * (pad - 1)");
+  if (R > 0x7FFFFFFF || kcap > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "fp8_tensor_quantize_colwise: R or kcap >= 2^31");
+  if (!offsets || !kofs || !scale || (C > 0 && !e4m3_t) || (R > 0 && C > 0 && !x_bf16))
+    return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_quantize_colwise: NULL pointer");
+  if (!aligned(offsets, 4) || !aligned(kofs, 4) || !aligned(scale, 4) || (x_bf16 && !aligned(x_bf16, 16)) ||
+      (e4m3_t && !aligned(e4m3_t, 16)))
+    return fail(MOE_ERR_INVALID_ARG,
+                "fp8_tensor_quantize_colwise: x and codes must be 16-byte, offsets, kofs and scale 4-byte aligned");
+  const hipStream_t s = as_stream(stream);
+  moe_status st;
+  if ((st = fp8t_zero(scale, 1, s)) != MOE_OK) return st;
+  const void* in[1] = {x_bf16};
+  uint8_t* out[1] = {e4m3_t};
+  if ((st = fp8t_amax(in, 1, R * C, scale, s)) != MOE_OK) return st;
+  if (C > 0 && (st = fp8t_transpose(in, out, 1, R, (int)C, E, offsets, pad, kcap, scale, kofs, s)) != MOE_OK)
+    return st;
   return fp8t_finalize(scale, 1, s);
 }

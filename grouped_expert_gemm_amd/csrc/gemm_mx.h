@@ -36,5 +36,13 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
                     const int32_t* offsets, bf16_t* dx, void* const* dw_gate_up, void* const* dw_down, float* dprob,
                     uint8_t* ws, hipStream_t s);
 
+// per-tensor FP8 backward (bf16 inputs and outputs, one factor per tensor: dY, dZ, h,
+// x over all rows, each expert's W1 and W2)
+size_t fp8_bwd_workspace_bytes(const moe_mlp_desc& d, int64_t R);
+moe_status backward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf16_t* x, const bf16_t* z,
+                               const bf16_t* h, const float* prob, const void* const* w_gate_up,
+                               const void* const* w_down, const int32_t* offsets, bf16_t* dx, void* const* dw_gate_up,
+                               void* const* dw_down, float* dprob, uint8_t* ws, hipStream_t s);
+
 }  // namespace mx
 }  // namespace moe

@@ -457,12 +457,12 @@ constexpr int kXTile = kBM * kXBK;        // one operand of one step: a half-slo
 // 64-value MFMA slices per step with the barrier between them. The MFMA runs with unit
 // block scales; the products are scaled by (Q's scale x the expert's P scale) in the
 // epilogue, and the SwiGLU epilogue writes h in bf16 and raises h's amax word (its
-// scale needs all of h). (An MX-scaled instantiation of this pipeline needs ~30 more
-// registers for the scales and spills inside the K loop; MXFP8 keeps the 64-byte-step
-// kernel above.)
-template <int EP>
+// scale needs all of h). MX_WGRAD (MxWgradParams): the backward's weight gradients on
+// token-axis codes (as in the MXFP8 kernel below), scaled by the two tensors' factors
+// q_s[0] x tab_s[0][0].
+template <int EP, typename Params = MxParams>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_fp8t_kernel(const MxParams prm) {
+void grouped_gemm_fp8t_kernel(const Params prm) {
   __shared__ __attribute__((aligned(1024))) uint8_t sH0[kXTile], sH1[kXTile], sH2[kXTile];
   __shared__ __attribute__((aligned(1024))) uint8_t sH3[kXTile], sH4[kXTile];
 
@@ -494,22 +494,24 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
     v = v < prev ? prev : v;
     return v > R ? R : v;
   };
+  constexpr bool wgrad = EP == MX_WGRAD;
   int total = 0;
-  {
+  int e_w = 0, ob = 0, oe = 0, ts_w = 0, nt_w = 0;
+  if constexpr (wgrad) {  // every expert owns the whole [R, N] output
+    total = E * (R / kBM) * prm.n_tiles;
+  } else {
     int prev = 0;
     for (int x = 0; x < E; ++x) {
       const int en = clamp_off(prm.offsets[x + 1], prev);
       total += ((en - prev + kBM - 1) / kBM) * prm.n_tiles;
       prev = en;
     }
+    oe = clamp_off(prm.offsets[1], 0);
+    nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
   }
-  int e_w = 0;
-  int ob = 0;
-  int oe = clamp_off(prm.offsets[1], 0);
-  int ts_w = 0;
-  int nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
-  const int nk = K / kXBK;
-  const int pad = (5 - nk % 5) % 5;  // zero steps ahead of the K loop (as in the MXFP8 kernel below)
+  // row stride of both code arrays: K, or the padded token axis for the weight gradients
+  int ld = K;
+  if constexpr (wgrad) ld = prm.ld;
 
   // fragment addresses: sub-tile rows start at multiples of 32, where swz8 depends on
   // the lane's row within the sub-tile only; half h of slice s is logical chunk
@@ -527,23 +529,43 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
 
   for (int t = logical; t < total; t += nwg) {
     // ---------------- tile decode ----------------
-    while (e_w < E && t >= ts_w + nt_w) {
-      ts_w += nt_w;
-      ++e_w;
-      ob = oe;
-      if (e_w < E) {
-        oe = clamp_off(prm.offsets[e_w + 1], ob);
-        nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
+    int e, mt, nt, nk, k_beg = 0;
+    if constexpr (wgrad) {
+      // groups of 8 m-tiles, n fastest over the group (as in the MXFP8 kernel below)
+      constexpr int GM = 8;
+      const int mte = R / kBM;
+      const int per = mte * prm.n_tiles;
+      e = t / per;
+      const int local = t - e * per;
+      const int span = GM * prm.n_tiles;
+      const int grp = local / span, rem = local - grp * span;
+      const int gm = min(GM, mte - grp * GM);
+      mt = grp * GM + rem % gm;
+      nt = rem / gm;
+      e = __builtin_amdgcn_readfirstlane(e);
+      k_beg = __builtin_amdgcn_readfirstlane(prm.kofs[e]);
+      nk = __builtin_amdgcn_readfirstlane((prm.kofs[e + 1] - k_beg) / kXBK);
+      ob = 0;
+      oe = R;
+    } else {
+      while (e_w < E && t >= ts_w + nt_w) {
+        ts_w += nt_w;
+        ++e_w;
+        ob = oe;
+        if (e_w < E) {
+          oe = clamp_off(prm.offsets[e_w + 1], ob);
+          nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
+        }
       }
-    }
-    if (e_w >= E) break;
-    int e = e_w, mt, nt;
-    {
+      if (e_w >= E) break;
+      e = e_w;
       const int local = t - ts_w;
       const int mte = (oe - ob + kBM - 1) / kBM;
       mt = local % mte;
       nt = local / mte;
+      nk = K / kXBK;
     }
+    const int pad = (5 - nk % 5) % 5;  // zero steps ahead of the K loop (as in the MXFP8 kernel below)
     e = __builtin_amdgcn_readfirstlane(e);
     mt = __builtin_amdgcn_readfirstlane(mt);
     nt = __builtin_amdgcn_readfirstlane(nt);
@@ -560,10 +582,10 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
     // ---------------- operands ----------------
     // Q's record count ends at the expert's last row: rows past it fail the range check
     // and land as zero codes, discarded in the epilogue.
-    const uint8_t* p_tile = prm.tab[e] + (int64_t)p_row(0) * K;
-    const uint8_t* q_tile = prm.q + (int64_t)tile_row * K;
-    const uint32_t off0 = (uint32_t)((int64_t)kc_row0 * K + kc_chunk * 16);
-    const int64_t q_extent = (int64_t)(row_end - tile_row) * K;
+    const uint8_t* p_tile = prm.tab[wgrad ? 0 : e] + (int64_t)p_row(0) * ld + k_beg;
+    const uint8_t* q_tile = prm.q + (int64_t)tile_row * ld + k_beg;
+    const uint32_t off0 = (uint32_t)((int64_t)kc_row0 * ld + kc_chunk * 16);
+    const int64_t q_extent = wgrad ? kAll : (int64_t)(row_end - tile_row) * ld;
     const int p_up = (EP == MX_SWIGLU) ? prm.I - 128 : 0;
     // step kt of the loop is step kt - pad of the operands: an empty range (zeros) outside [0, nk)
     auto copy_op = [&](const uint8_t* tile, int up, int64_t extent, int kt, uint8_t* dst) {
@@ -577,7 +599,7 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t rows = (uint32_t)(i * 32 + (i >= 4 ? up : 0));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 4096), 16, off0, (int)(rows * (uint32_t)K),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 4096), 16, off0, (int)(rows * (uint32_t)ld),
                                                  0, 0);
       }
     };
@@ -675,24 +697,27 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
     using H2 = std::integral_constant<int, 2>;
     using H3 = std::integral_constant<int, 3>;
     using H4 = std::integral_constant<int, 4>;
-    copy_P(0, H0{});
-    copy_Q(0, H1{});
-    copy_P(1, H2{});
-    copy_Q(1, H3{});
-    copy_P(2, H4{});
-    wait_vm<24>();  // step 0 complete
-    lds_barrier();
-    read_first(H0{}, H1{});
-    const int n_run = nk + pad;
-    for (int kt = 0; kt < n_run; kt += 5) static_for<5>([&](auto V) { kstep(kt + decltype(V)::value, V); });
-    wait_vm<0>();   // the zero copies issued past the last step land before LDS is reused
+    if (nk > 0) {  // (a weight gradient of an expert without rows: no steps, its tile is zeros)
+      copy_P(0, H0{});
+      copy_Q(0, H1{});
+      copy_P(1, H2{});
+      copy_Q(1, H3{});
+      copy_P(2, H4{});
+      wait_vm<24>();  // step 0 complete
+      lds_barrier();
+      read_first(H0{}, H1{});
+      const int n_run = nk + pad;
+      for (int kt = 0; kt < n_run; kt += 5) static_for<5>([&](auto V) { kstep(kt + decltype(V)::value, V); });
+      wait_vm<0>();   // the zero copies issued past the last step land before LDS is reused
+    }
     // every wavefront is done with every half-slot before the epilogue uses LDS
     lds_barrier();
 
     // ---------------- epilogue ----------------
     // the product of the two tensors' scales
-    const float alpha = *reinterpret_cast<const float*>(prm.q_s) * *reinterpret_cast<const float*>(prm.tab_s[e]);
-    if constexpr (EP == MX_STORE) {
+    const float alpha =
+        *reinterpret_cast<const float*>(prm.q_s) * *reinterpret_cast<const float*>(prm.tab_s[wgrad ? 0 : e]);
+    if constexpr (EP == MX_STORE || EP == MX_WGRAD) {
       // bf16 rows through LDS (idle after the K loop), as in the bf16 forward kernel:
       // blocks of 256 rows x 128 columns, 256-byte rows, chunk c of row r at
       // c ^ (r & 15), rows 0-127 in the first array of a pair and 128-255 in the second;
@@ -737,7 +762,10 @@ void grouped_gemm_fp8t_kernel(const MxParams prm) {
       acc_block(0, sH0, sH1);
       acc_block(1, sH2, sH3);
       lds_barrier();
-      bf16_t* c0 = reinterpret_cast<bf16_t*>(prm.c) + (int64_t)nt * kBN;
+      void* cbase;
+      if constexpr (wgrad) cbase = prm.ctab[e];
+      else cbase = prm.c;
+      bf16_t* c0 = reinterpret_cast<bf16_t*>(cbase) + (int64_t)nt * kBN;
       drain(wv < 2 ? sH0 : sH1, c0, prm.N);
       drain(wv < 2 ? sH2 : sH3, c0 + 128, prm.N);
       lds_barrier();  // read out before the next tile's copies land
@@ -1234,11 +1262,14 @@ static moe_status launch(int ep, bool pt, const MxParams& p, int64_t max_tiles, 
   return check_launch(what);
 }
 
-static moe_status launch_wgrad(const MxWgradParams& p, int64_t max_tiles, hipStream_t s, const char* what) {
+// pt: per-tensor FP8 (factors q_s[0] and tab_s[0][0]); else MXFP8 with step-major scales
+static moe_status launch_wgrad(const MxWgradParams& p, int64_t max_tiles, hipStream_t s, const char* what,
+                               bool pt = false) {
   if (max_tiles <= 0) return MOE_OK;
   int64_t grid = num_cus();
   if (max_tiles < grid) grid = max_tiles;
-  hipLaunchKernelGGL((grouped_gemm_mxw_kernel<MX_WGRAD, MxWgradParams>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  if (pt) hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_WGRAD, MxWgradParams>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((grouped_gemm_mxw_kernel<MX_WGRAD, MxWgradParams>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return check_launch(what);
 }
 
@@ -1685,6 +1716,178 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
   w.N = H;
   w.n_tiles = H / kBN;
   return launch_wgrad(w, (int64_t)E * (2 * I / kBM) * w.n_tiles, s, "MXFP8 gate_up wgrad");
+}
+
+
+// ---------------------------------------------------------------------------------
+// Per-tensor FP8 backward: every GEMM operand is one tensor with one factor (amax /
+// 448): dY, dZ, h and x over all routed rows, W1_e and W2_e per expert. A factor per
+// tensor does not depend on the axis a GEMM reduces over, so each tensor is quantised
+// once: row-major codes of dY and dZ for the data gradients, their transposed
+// token-axis codes (experts padded to whole 256-row K steps) and those of h and x for
+// the weight gradients, the weights' transposed codes for the data gradients.
+//   dH = dY W2_e, dSwiGLU -> dZ (bf16), dprob, dx = dZ W1_e, dW2 = dY^T h, dW1 = dZ^T x
+// Factor words: [dY, h, x, W1_0 .. W1_E-1, W2_0 .. W2_E-1, dZ] (amax bits, then scales).
+// ---------------------------------------------------------------------------------
+
+namespace {
+
+struct Fp8BwdLayout {
+  size_t words, dyq, dyc, w2t, w1t, dh, dz, dzq, dzc, hc, xc, kofs, total;
+};
+
+Fp8BwdLayout fp8_bwd_layout(const moe_mlp_desc& d, int64_t R) {
+  const size_t H = d.H, I = d.I, E = d.E, kc = (size_t)bwd_kcap(R, d.E);
+  Fp8BwdLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += a256(bytes); return at; };
+  L.words = take((4 + 2 * E) * 4);
+  L.dyq = take(R * H);
+  L.dyc = take(H * kc);
+  L.w2t = take(E * I * H);
+  L.w1t = take(E * H * 2 * I);
+  L.dh = take(R * I * 2);
+  L.dz = take(R * 2 * I * 2);
+  L.dzq = take(R * 2 * I);
+  L.dzc = take(2 * I * kc);
+  L.hc = take(I * kc);
+  L.xc = take(H * kc);
+  L.kofs = take((E + 1) * 4);
+  L.total = o;
+  return L;
+}
+
+// transposed codes of E tensors of one shape, in launches of at most 64 tensors
+moe_status transpose_each(const void* const* in, uint8_t* base, size_t stride, int E, int64_t rows, int cols,
+                          float* words, hipStream_t s) {
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int n = E - e0 < 64 ? E - e0 : 64;
+    uint8_t* out[64];
+    for (int i = 0; i < n; ++i) out[i] = base + (size_t)(e0 + i) * stride;
+    const moe_status st = fp8t_transpose(in + e0, out, n, rows, cols, 1, nullptr, 32, rows, words + e0, nullptr, s);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+size_t fp8_bwd_workspace_bytes(const moe_mlp_desc& d, int64_t R) { return fp8_bwd_layout(d, R).total; }
+
+moe_status backward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf16_t* x, const bf16_t* z,
+                               const bf16_t* h, const float* prob, const void* const* w_gate_up,
+                               const void* const* w_down, const int32_t* offsets, bf16_t* dx, void* const* dw_gate_up,
+                               void* const* dw_down, float* dprob, uint8_t* ws, hipStream_t s) {
+  const int E = d.E, H = d.H, I = d.I;
+  moe_status st = check_mx_shape(E, H, I, "moe_grouped_mlp_bwd");
+  if (st != MOE_OK) return st;
+  const int64_t kc = bwd_kcap(R, E);
+  if ((int64_t)2 * I * kc > 0x7FFFFFFFLL || (int64_t)H * kc > 0x7FFFFFFFLL)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_mlp_bwd: FP8 token-axis operands exceed 2^31 bytes");
+  const Fp8BwdLayout L = fp8_bwd_layout(d, R);
+  float* words = reinterpret_cast<float*>(ws + L.words);
+  float *w_dy = words, *w_h = words + 1, *w_x = words + 2, *w_w1 = words + 3, *w_w2 = words + 3 + E,
+        *w_dz = words + 3 + 2 * E;
+  uint8_t *dyq = ws + L.dyq, *dyc = ws + L.dyc, *w2t = ws + L.w2t, *w1t = ws + L.w1t, *dzq = ws + L.dzq,
+          *dzc = ws + L.dzc, *hc = ws + L.hc, *xc = ws + L.xc;
+  bf16_t *dh = (bf16_t*)(ws + L.dh), *dz = (bf16_t*)(ws + L.dz);
+  int32_t* kofs = (int32_t*)(ws + L.kofs);
+  const size_t w2n = (size_t)I * H, w1n = (size_t)H * 2 * I;
+  const int64_t mtiles = (R + kBM - 1) / kBM + E;
+
+  // factors of dY, h, x and the weights; every code array but dZ's
+  if ((st = fp8t_zero(words, 4 + 2 * E, s)) != MOE_OK) return st;
+  const void* t_dy[1] = {dy};
+  const void* t_h[1] = {h};
+  const void* t_x[1] = {x};
+  if ((st = fp8t_amax(t_dy, 1, R * H, w_dy, s)) != MOE_OK) return st;
+  if ((st = fp8t_amax(t_h, 1, R * I, w_h, s)) != MOE_OK) return st;
+  if ((st = fp8t_amax(t_x, 1, R * H, w_x, s)) != MOE_OK) return st;
+  if ((st = fp8t_amax(w_gate_up, E, (int64_t)2 * I * H, w_w1, s)) != MOE_OK) return st;
+  if ((st = fp8t_amax(w_down, E, (int64_t)H * I, w_w2, s)) != MOE_OK) return st;
+  uint8_t* o_dyq[1] = {dyq};
+  uint8_t* o_dyc[1] = {dyc};
+  uint8_t* o_hc[1] = {hc};
+  uint8_t* o_xc[1] = {xc};
+  if ((st = fp8t_quantize(t_dy, o_dyq, 1, R * H, w_dy, s)) != MOE_OK) return st;
+  if ((st = fp8t_transpose(t_dy, o_dyc, 1, R, H, E, offsets, 256, kc, w_dy, kofs, s)) != MOE_OK) return st;
+  if ((st = fp8t_transpose(t_h, o_hc, 1, R, I, E, offsets, 256, kc, w_h, nullptr, s)) != MOE_OK) return st;
+  if ((st = fp8t_transpose(t_x, o_xc, 1, R, H, E, offsets, 256, kc, w_x, nullptr, s)) != MOE_OK) return st;
+  // W2_e [H][I] -> [I][H] (K = H for dH); W1_e [2I][H] -> [H][2I] (K = 2I for dx)
+  if ((st = transpose_each(w_down, w2t, w2n, E, H, I, w_w2, s)) != MOE_OK) return st;
+  if ((st = transpose_each(w_gate_up, w1t, w1n, E, 2 * I, H, w_w1, s)) != MOE_OK) return st;
+  if ((st = fp8t_finalize(words, 3 + 2 * E, s)) != MOE_OK) return st;
+
+  // dH = dY W2_e
+  MxParams p;
+  std::memset(&p, 0, sizeof(p));
+  for (int e = 0; e < E; ++e) {
+    p.tab[e] = w2t + e * w2n;
+    p.tab_s[e] = reinterpret_cast<const uint8_t*>(w_w2 + e);
+  }
+  p.q = dyq;
+  p.q_s = reinterpret_cast<const uint8_t*>(w_dy);
+  p.c = dh;
+  p.offsets = offsets;
+  p.R = R;
+  p.K = H;
+  p.N = I;
+  p.E = E;
+  p.I = I;
+  p.n_tiles = I / kBN;
+  if ((st = launch(MX_STORE, true, p, mtiles * p.n_tiles, s, "FP8 down dgrad")) != MOE_OK) return st;
+
+  // dZ, dprob; then dZ's factor and codes
+  if (R > 0) {
+    hipLaunchKernelGGL(mx_dswiglu_kernel, dim3((unsigned)R), dim3(256), 0, s, dh, z, prob, dz, dprob, I);
+    if ((st = check_launch("FP8 dSwiGLU")) != MOE_OK) return st;
+  }
+  const void* t_dz[1] = {dz};
+  uint8_t* o_dzq[1] = {dzq};
+  uint8_t* o_dzc[1] = {dzc};
+  if ((st = fp8t_amax(t_dz, 1, R * 2 * I, w_dz, s)) != MOE_OK) return st;
+  if ((st = fp8t_quantize(t_dz, o_dzq, 1, R * 2 * I, w_dz, s)) != MOE_OK) return st;
+  if ((st = fp8t_transpose(t_dz, o_dzc, 1, R, 2 * I, E, offsets, 256, kc, w_dz, nullptr, s)) != MOE_OK) return st;
+  if ((st = fp8t_finalize(w_dz, 1, s)) != MOE_OK) return st;
+
+  // dx = dZ W1_e
+  for (int e = 0; e < E; ++e) {
+    p.tab[e] = w1t + e * w1n;
+    p.tab_s[e] = reinterpret_cast<const uint8_t*>(w_w1 + e);
+  }
+  p.q = dzq;
+  p.q_s = reinterpret_cast<const uint8_t*>(w_dz);
+  p.c = dx;
+  p.K = 2 * I;
+  p.N = H;
+  p.n_tiles = H / kBN;
+  if ((st = launch(MX_STORE, true, p, mtiles * p.n_tiles, s, "FP8 gate_up dgrad")) != MOE_OK) return st;
+
+  // weight gradients on the token-axis codes
+  MxWgradParams w;
+  std::memset(&w, 0, sizeof(w));
+  w.kofs = kofs;
+  w.E = E;
+  w.ld = (int)kc;
+  w.q = dyc;
+  w.q_s = reinterpret_cast<const uint8_t*>(w_dy);
+  w.tab[0] = hc;
+  w.tab_s[0] = reinterpret_cast<const uint8_t*>(w_h);
+  for (int e = 0; e < E; ++e) w.ctab[e] = dw_down[e];
+  w.R = H;
+  w.N = I;
+  w.I = I;
+  w.n_tiles = I / kBN;
+  if ((st = launch_wgrad(w, (int64_t)E * (H / kBM) * w.n_tiles, s, "FP8 down wgrad", true)) != MOE_OK) return st;
+  w.q = dzc;
+  w.q_s = reinterpret_cast<const uint8_t*>(w_dz);
+  w.tab[0] = xc;
+  w.tab_s[0] = reinterpret_cast<const uint8_t*>(w_x);
+  for (int e = 0; e < E; ++e) w.ctab[e] = dw_gate_up[e];
+  w.R = 2 * I;
+  w.N = H;
+  w.n_tiles = H / kBN;
+  return launch_wgrad(w, (int64_t)E * (2 * I / kBM) * w.n_tiles, s, "FP8 gate_up wgrad", true);
 }
 
 }  // namespace mx

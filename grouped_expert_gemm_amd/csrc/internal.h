@@ -52,5 +52,15 @@ moe_status fp8t_amax(const void* const* in, int ntensors, int64_t n, float* word
 moe_status fp8t_quantize(const void* const* in, uint8_t* const* out, int ntensors, int64_t n, const float* words,
                          hipStream_t s);
 moe_status fp8t_finalize(float* words, int n, hipStream_t s);
+// Transposed per-tensor FP8 codes of x [R, C] (bf16, rows grouped into E experts by
+// offsets; offsets NULL: one expert of R rows): out [C, kcap], expert e's rows at
+// columns kofs[e] .. (padded to a multiple of pad, zeros in the padding), with the
+// factor of words[t] (amax bits, between fp8t_amax and fp8t_finalize) for tensor t of
+// in/out. kofs (E + 1 padded offsets) is written when not NULL. C % 64 == 0, pad and
+// kcap multiples of 32, kcap >= R + E * (pad - 1) (without offsets: R rounded up to a
+// multiple of pad), at most 64 tensors.
+moe_status fp8t_transpose(const void* const* in, uint8_t* const* out, int ntensors, int64_t R, int C, int E,
+                          const int32_t* offsets, int pad, int64_t kcap, const float* words, int32_t* kofs,
+                          hipStream_t s);
 
 }  // namespace moe

@@ -37,8 +37,8 @@ moe_status validate_desc(const moe_mlp_desc& d, bool backward) {
     if (backward && d.I % 256 != 0)
       return fail(MOE_ERR_UNSUPPORTED, "grouped MLP backward: bf16 kernels need I % 256 == 0");
   }
-  if (backward && d.compute == MOE_FP8)
-    return fail(MOE_ERR_UNSUPPORTED, "grouped MLP backward: per-tensor FP8 backward is not implemented (use MXFP8 or BF16)");
+  if (backward && d.compute == MOE_FP8 && (d.act != MOE_BF16 || d.wt != MOE_BF16))
+    return fail(MOE_ERR_INVALID_ARG, "grouped MLP backward: per-tensor FP8 takes bf16 activations and bf16 weights");
   if (backward && d.compute == MOE_MXFP8 && d.act != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "grouped MLP backward: MXFP8 takes bf16 activations (and bf16 master weights or "
                                      "weights packed by mxfp8_pack_weight_bwd)");
@@ -71,6 +71,7 @@ size_t mlp_bwd_workspace_bytes(const moe_mlp_desc& d, int64_t R) {
   const size_t I = d.I;
   if (d.compute == MOE_F32) return a256(4 * R * I * 4);
   if (d.compute == MOE_MXFP8) return mx::bwd_workspace_bytes(d, R);
+  if (d.compute == MOE_FP8) return mx::fp8_bwd_workspace_bytes(d, R);
   return a256(R * 2 * I * 2) + a256((size_t)2 * (I / 256) * R * 4) + grouped_gemm_workspace_bytes();
 }
 
@@ -365,6 +366,11 @@ extern "C" moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, c
     return mx::backward(d, R, (const bf16_t*)dy_perm, (const bf16_t*)x_perm, (const bf16_t*)z_save,
                         (const bf16_t*)h_save, prob_perm, w_gate_up, w_down, offsets, (bf16_t*)dx_perm, dw_gate_up,
                         dw_down, dprob_perm, (uint8_t*)workspace, s);
+  }
+  if (d.compute == MOE_FP8) {
+    return mx::backward_fp8_tensor(d, R, (const bf16_t*)dy_perm, (const bf16_t*)x_perm, (const bf16_t*)z_save,
+                                   (const bf16_t*)h_save, prob_perm, w_gate_up, w_down, offsets, (bf16_t*)dx_perm,
+                                   dw_gate_up, dw_down, dprob_perm, (uint8_t*)workspace, s);
   }
 
   const int64_t H = d.H, I = d.I;

@@ -247,6 +247,26 @@ moe_status mxfp8_pack_weight_bwd(const void* w_bf16, int64_t rows, int64_t cols,
  */
 moe_status fp8_tensor_quantize(const void* in_bf16, int64_t n, uint8_t* e4m3, float* scale, void* stream);
 
+/*
+ * Per-tensor FP8 codes laid out along the token axis, expert by expert: the operand
+ * layout of the weight-gradient GEMMs of the per-tensor FP8 backward. Source:
+ * Challenge 2 (FP8: one scaling factor for a whole tensor). One factor for the whole
+ * tensor means the codes are those of fp8_tensor_quantize on x, transposed: expert e's
+ * rows [offsets[e], offsets[e+1]) of x, zero-padded to a multiple of `pad`, become
+ * columns [kofs[e], kofs[e+1]) of the output (padding is code 0).
+ *   x       [R, C] bf16 (16-byte aligned), offsets [E+1] int32 (device)
+ *   e4m3_t  [C, kcap] uint8 (out, 16-byte aligned); columns at and past kofs[E] are
+ *           not written
+ *   scale   ONE float32 in device memory (out, 4-byte aligned): x's factor, by the rule
+ *           of fp8_tensor_quantize (also the amax accumulator while the call runs)
+ *   kofs    [E+1] int32 (out, device): the padded column offsets
+ * Limits: C % 64 == 0, pad a positive multiple of 32, kcap a multiple of 32 with
+ * kcap >= R + E * (pad - 1), 1 <= E <= MOE_MAX_EXPERTS, R < 2^31.
+ */
+moe_status fp8_tensor_quantize_colwise(const void* x_bf16, int64_t R, int64_t C, int E, const int32_t* offsets,
+                                       int pad, int64_t kcap, uint8_t* e4m3_t, float* scale, int32_t* kofs,
+                                       void* stream);
+
 /* Description of one grouped MLP layer (the experts' shapes and precisions). */
 typedef struct {
   int E;             /* experts, 1..MOE_MAX_EXPERTS */

@@ -79,8 +79,13 @@ def test_mlp_descriptor_checks(L):
     assert n.value >= 8192 * (4096 + 2 * 14336 + 14336 * 2 + 2 * 14336 * 2)     # its quantised operands
     assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, 2, 2, 1, 0)), 1, 0, 0, 0,
                                 ctypes.byref(n)) == _lib.MOE_ERR_INVALID_ARG    # MXFP8 backward: bf16 activations
-    assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, 3, 1, 1, 0)), 1, 0, 0, 0,
-                                ctypes.byref(n)) == _lib.MOE_ERR_UNSUPPORTED    # per-tensor FP8 backward
+    assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, 3, 1, 1, 0)), 8192, 0, 0, 0,
+                                ctypes.byref(n)) == 0                           # per-tensor FP8 backward
+    assert n.value >= 8192 * (4096 + 2 * 14336 + 14336 * 2 + 2 * 14336 * 2)     # its quantised operands
+    assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, 3, 3, 1, 0)), 1, 0, 0, 0,
+                                ctypes.byref(n)) == _lib.MOE_ERR_INVALID_ARG    # FP8 backward: bf16 activations
+    assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, 3, 1, 3, 0)), 1, 0, 0, 0,
+                                ctypes.byref(n)) == _lib.MOE_ERR_INVALID_ARG    # ... and bf16 weights
     assert L.moe_workspace_size(1, ctypes.byref(D(0, 256, 128, 1, 1, 1, 0)), 1, 0, 0, 0,
                                 ctypes.byref(n)) == _lib.MOE_ERR_INVALID_ARG
     assert L.moe_workspace_size(1, ctypes.byref(D(8, 256, 128, 1, 0, 1, 0)), 1, 0, 0, 0,
@@ -99,7 +104,8 @@ def test_mlp_descriptor_checks(L):
 
 def test_fp8_tensor_argument_checks(L):
     """Per-tensor FP8: size and pointer checks before any launch; descriptor rules of the
-    FP8 forward (storage matching the compute dtype, no backward, no saved tensors)."""
+    FP8 forward (storage matching the compute dtype, no saved tensors) and backward
+    (bf16 activations and weights)."""
     from grouped_expert_gemm_amd import _lib
     INV, UNS = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED
     scale = ctypes.c_void_p(4096)
@@ -118,7 +124,9 @@ def test_fp8_tensor_argument_checks(L):
     assert L.moe_workspace_size(1, ctypes.byref(D(8, 4096, 14336, FP8, MX, BF16, 0)), 1, 0, 0, 0,
                                 ctypes.byref(n)) == INV                                # MXFP8 storage, FP8 compute
     assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, FP8, BF16, BF16, 0)), 1, 0, 0, 0,
-                                ctypes.byref(n)) == UNS                                # FP8 backward
+                                ctypes.byref(n)) == 0                                  # FP8 backward
+    assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, FP8, FP8, BF16, 0)), 1, 0, 0, 0,
+                                ctypes.byref(n)) == INV                                # ... on bf16 activations
     ptrs = (ctypes.c_void_p * 8)(*([4096] * 8))
     pp = ctypes.cast(ptrs, _lib.PP)
     d = D(8, 256, 256, FP8, BF16, BF16, 1)
@@ -144,6 +152,13 @@ def test_mxfp8_colwise_argument_checks(L):
     assert L.mxfp8_quantize_colwise(d, 100, 64, 0, d, 32, 256, d, d, d, None) == INV     # E = 0
     assert L.mxfp8_quantize_colwise(d, 100, 64, 4, None, 32, 256, d, d, d, None) == INV  # NULL offsets
     assert b"kcap" in L.moe_last_error() or b"NULL" in L.moe_last_error()
+    f = L.fp8_tensor_quantize_colwise
+    assert f(d, 100, 96, 4, d, 32, 256, d, d, d, None) == UNS      # C % 64
+    assert f(d, 100, 64, 4, d, 48, 256, d, d, d, None) == INV      # pad % 32
+    assert f(d, 100, 64, 4, d, 32, 192, d, d, d, None) == INV      # kcap < R + E (pad - 1)
+    assert f(d, 100, 64, 0, d, 32, 256, d, d, d, None) == INV      # E = 0
+    assert f(d, 100, 64, 4, d, 32, 256, d, None, d, None) == INV   # NULL scale
+    assert f(d, -1, 64, 4, d, 32, 256, d, d, d, None) == INV       # negative R
 
 
 def test_noalloc_permute_rejects_sizes_beyond_its_scratch(L):
