@@ -44,7 +44,7 @@ def dev_bf16(torch, np, bits):
 class Layer:
     """Device buffers and the C calls of one forward (and optionally backward) step."""
 
-    def __init__(self, w, inp, backward: bool, mx: bool = False, prequant: bool = False):
+    def __init__(self, w, inp, backward: bool, mx: bool = False, prequant: bool = False, fp8: bool = False):
         import numpy as np
         import torch
 
@@ -91,13 +91,17 @@ class Layer:
             self.dprob = torch.empty(R, dtype=torch.float32, device=dev)
             self.d1, self._k3 = _lib.ptr_table([self.dw1[e].data_ptr() for e in range(E)])
             self.d2, self._k4 = _lib.ptr_table([self.dw2[e].data_ptr() for e in range(E)])
-            comp = _lib.MOE_MXFP8 if mx else _lib.MOE_BF16
+            comp = _lib.MOE_FP8 if fp8 else (_lib.MOE_MXFP8 if mx else _lib.MOE_BF16)
             self.desc = _lib.MlpDesc(E, H, I, comp, _lib.MOE_BF16, _lib.MOE_BF16, 1)
             self.ws_bwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_BWD, self.desc, R), dtype=torch.uint8,
                                       device=dev)
-        self.mx = mx
+        self.mx = mx or fp8
         self.fs1 = self.fs2 = None
-        if mx:  # the whole grouped MLP forward in MXFP8 (one call), saving z and h when backward
+        if fp8:  # the whole grouped MLP forward in per-tensor FP8 (one call), saving z and h when backward
+            self.desc_fwd = _lib.MlpDesc(E, H, I, _lib.MOE_FP8, _lib.MOE_BF16, _lib.MOE_BF16, int(backward))
+            self.ws_fwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_FWD, self.desc_fwd, R), dtype=torch.uint8,
+                                      device=dev)
+        elif mx:  # the whole grouped MLP forward in MXFP8 (one call), saving z and h when backward
             wt = _lib.MOE_BF16
             if prequant:
                 # weights quantised once, outside the timed steps (as a training loop would once
@@ -465,26 +469,36 @@ def cpu_baseline(inp, w, seconds):
                       f"H={w.H}, I={w.I}); {t_all:.1f} s of oracle time, {os.cpu_count()} host CPUs visible"}
 
 
-def fwd_bwd_measure(steps, warmup, mx=False, prequant=False):
+_FWD_BWD_INPUTS = None
+
+
+def fwd_bwd_measure(steps, warmup, mx=False, prequant=False, fp8=False):
     """The whole layer forward + backward step (route ... combine, dOut gather, grouped
     MLP backward, dx combine, dprob gather) at the Mixtral fwd+bwd shape; mx: the grouped
     MLP forward and backward in MXFP8 (the forward saving z and h in bf16); prequant: the
-    MXFP8 weights quantised once outside the timed steps."""
+    MXFP8 weights quantised once outside the timed steps; fp8: forward and backward in
+    per-tensor FP8 (bf16 master weights quantised inside every step)."""
+    global _FWD_BWD_INPUTS
     from moe_inputs import WORKLOADS, make_inputs
 
     wb = WORKLOADS["mixtral_fwd_bwd"]
-    t0 = time.perf_counter()
-    inpb = make_inputs(wb, want_float=False)
-    log(f"inputs {wb.name}: {time.perf_counter() - t0:.1f} s")
-    lb = Layer(wb, inpb, backward=True, mx=mx, prequant=prequant)
+    if _FWD_BWD_INPUTS is None:   # the same seeded inputs for every fwd+bwd measurement
+        t0 = time.perf_counter()
+        _FWD_BWD_INPUTS = make_inputs(wb, want_float=False)
+        log(f"inputs {wb.name}: {time.perf_counter() - t0:.1f} s")
+    lb = Layer(wb, _FWD_BWD_INPUTS, backward=True, mx=mx, prequant=prequant, fp8=fp8)
     msb = time_steps(lb, steps, warmup)
     flopb = 3.0 * wb.gemm_flop_fwd()
     vb = flopb / (msb * 1e-3) / 1e12
-    peak = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
-    log(f"fwd+bwd step{' (MXFP8)' if mx else ''}{' prequant' if prequant else ''} {msb:.3f} ms -> {vb:.1f} TFLOP/s")
+    peak = FP8_PEAK_TFLOPS if (mx or fp8) else BF16_PEAK_TFLOPS
+    tag = " (FP8)" if fp8 else (" (MXFP8)" if mx else "")
+    log(f"fwd+bwd step{tag}{' prequant' if prequant else ''} {msb:.3f} ms -> {vb:.1f} TFLOP/s")
     rec = {"workload": "mixtral_fwd_bwd", "T": wb.T, "value": round(vb, 2), "unit": "TFLOP/s",
            "ms_per_step": round(msb, 4), "flop_per_step": flopb}
-    if mx:
+    if fp8:
+        rec.update(compute="fp8", pct_of_fp8_peak=round(100 * vb / peak, 2),
+                   weights="bf16 master weights, quantised inside every step (one factor per tensor)")
+    elif mx:
         rec.update(compute="mxfp8", pct_of_fp8_peak=round(100 * vb / peak, 2),
                    weights=("MXFP8, quantised once outside the step (row-wise for the forward, packed for the "
                             "backward)" if prequant else "bf16 master weights, quantised inside every step"))
@@ -509,7 +523,7 @@ def bwd_measure(reps=10):
     p = lambda t: ctypes.c_void_p(t.data_ptr())
     flop = 2.0 * wb.gemm_flop_fwd()
     out = []
-    for name, comp in (("bf16", _lib.MOE_BF16), ("mxfp8", _lib.MOE_MXFP8)):
+    for name, comp in (("bf16", _lib.MOE_BF16), ("mxfp8", _lib.MOE_MXFP8), ("fp8", _lib.MOE_FP8)):
         desc = _lib.MlpDesc(wb.E, wb.H, wb.I, comp, _lib.MOE_BF16, _lib.MOE_BF16, 1)
         ws = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_BWD, desc, lb.R), dtype=torch.uint8, device="cuda")
 
@@ -547,6 +561,8 @@ def only_measurement(which, steps, warmup):
         return fwd_bwd_measure(steps, warmup, mx=True)
     if which == "mx_fwd_bwd_pre":
         return fwd_bwd_measure(steps, warmup, mx=True, prequant=True)
+    if which == "fp8_fwd_bwd":
+        return fwd_bwd_measure(steps, warmup, fp8=True)
     if which == "bwd":
         return bwd_measure(steps)
     if which == "qwen3":
@@ -580,7 +596,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip the MXFP8 and Qwen3 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["fwd_bwd", "mx_fwd_bwd", "mx_fwd_bwd_pre", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise", "permute"],
+    ap.add_argument("--only", choices=["fwd_bwd", "mx_fwd_bwd", "mx_fwd_bwd_pre", "fp8_fwd_bwd", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise", "permute"],
                     help="run one measurement and print its record (kernel traces of that workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
@@ -670,6 +686,8 @@ def main():
         torch.cuda.empty_cache()
         result["mxfp8_fwd_bwd_prequantised"] = fwd_bwd_measure(max(3, args.steps // 2), args.warmup, mx=True,
                                                                prequant=True)
+        torch.cuda.empty_cache()
+        result["fp8_tensor_fwd_bwd"] = fwd_bwd_measure(max(3, args.steps // 2), args.warmup, fp8=True)
         torch.cuda.empty_cache()
         result["mlp_bwd"] = bwd_measure()
         torch.cuda.empty_cache()

@@ -22,12 +22,14 @@ moe_status gate_up(int E, int64_t R, int H, int I, const uint8_t* x, const uint8
                    bool step_major = false);
 
 // per-tensor FP8 forward (E4M3 with one float32 scale per tensor: x_perm, each expert's
-// W1 and W2, and h, which is stored in bf16 before its scale is known)
+// W1 and W2, and h, which is stored in bf16 before its scale is known: into h_save when
+// given, and z = [G, U] into z_save when given)
 size_t fp8_tensor_workspace_bytes(const moe_mlp_desc& d, int64_t R);
 moe_status forward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const void* x_perm, const float* x_scale,
                               const void* const* w_gate_up, const void* const* w_down, const float* const* w_gate_up_scale,
                               const float* const* w_down_scale, const int32_t* offsets, const float* prob_perm,
-                              void* y_perm, uint8_t* ws, hipStream_t s);
+                              void* y_perm, uint8_t* ws, hipStream_t s, void* z_save = nullptr,
+                              void* h_save = nullptr);
 
 // MXFP8 backward (bf16 inputs and outputs, every GEMM operand quantised along its K axis)
 size_t bwd_workspace_bytes(const moe_mlp_desc& d, int64_t R);

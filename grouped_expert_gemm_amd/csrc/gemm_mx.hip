@@ -457,7 +457,7 @@ constexpr int kXTile = kBM * kXBK;        // one operand of one step: a half-slo
 // 64-value MFMA slices per step with the barrier between them. The MFMA runs with unit
 // block scales; the products are scaled by (Q's scale x the expert's P scale) in the
 // epilogue, and the SwiGLU epilogue writes h in bf16 and raises h's amax word (its
-// scale needs all of h). MX_WGRAD (MxWgradParams): the backward's weight gradients on
+// scale needs all of h); MX_SWIGLU_SAVE also writes z = [G, U] in bf16. MX_WGRAD (MxWgradParams): the backward's weight gradients on
 // token-axis codes (as in the MXFP8 kernel below), scaled by the two tensors' factors
 // q_s[0] x tab_s[0][0].
 template <int EP, typename Params = MxParams>
@@ -495,6 +495,7 @@ void grouped_gemm_fp8t_kernel(const Params prm) {
     return v > R ? R : v;
   };
   constexpr bool wgrad = EP == MX_WGRAD;
+  constexpr bool swiglu = EP == MX_SWIGLU || EP == MX_SWIGLU_SAVE;
   int total = 0;
   int e_w = 0, ob = 0, oe = 0, ts_w = 0, nt_w = 0;
   if constexpr (wgrad) {  // every expert owns the whole [R, N] output
@@ -575,7 +576,7 @@ void grouped_gemm_fp8t_kernel(const Params prm) {
 
     // P row of local tile row r (SWIGLU: gate rows, then the up rows of the same columns)
     auto p_row = [&](int r) -> int {
-      if constexpr (EP == MX_SWIGLU) return (r < 128) ? nt * 128 + r : prm.I + nt * 128 + (r - 128);
+      if constexpr (swiglu) return (r < 128) ? nt * 128 + r : prm.I + nt * 128 + (r - 128);
       else return nt * kBN + r;
     };
 
@@ -586,7 +587,7 @@ void grouped_gemm_fp8t_kernel(const Params prm) {
     const uint8_t* q_tile = prm.q + (int64_t)tile_row * ld + k_beg;
     const uint32_t off0 = (uint32_t)((int64_t)kc_row0 * ld + kc_chunk * 16);
     const int64_t q_extent = wgrad ? kAll : (int64_t)(row_end - tile_row) * ld;
-    const int p_up = (EP == MX_SWIGLU) ? prm.I - 128 : 0;
+    const int p_up = swiglu ? prm.I - 128 : 0;
     // step kt of the loop is step kt - pad of the operands: an empty range (zeros) outside [0, nk)
     auto copy_op = [&](const uint8_t* tile, int up, int64_t extent, int kt, uint8_t* dst) {
       const int ks = kt - pad;
@@ -791,6 +792,19 @@ void grouped_gemm_fp8t_kernel(const Params prm) {
             for (int i4 = 0; i4 < 4; ++i4)
               *reinterpret_cast<uint2*>(C + i4 * 8 + lhi * 4) =
                   make_uint2(pack_bf16x2(h[i4 * 4 + 0], h[i4 * 4 + 1]), pack_bf16x2(h[i4 * 4 + 2], h[i4 * 4 + 3]));
+            if constexpr (EP == MX_SWIGLU_SAVE) {  // z = [G, U] of the row, scaled products in bf16
+              bf16_t* Z = reinterpret_cast<bf16_t*>(prm.z_save) + mg * 2 * prm.I + col0;
+#pragma unroll
+              for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x16& G = acc[sn][sm];
+                const f32x16& U = acc[sn + 2][sm];
+                const int i = i4 * 4;
+                *reinterpret_cast<uint2*>(Z + i4 * 8 + lhi * 4) = make_uint2(
+                    pack_bf16x2(G[i] * alpha, G[i + 1] * alpha), pack_bf16x2(G[i + 2] * alpha, G[i + 3] * alpha));
+                *reinterpret_cast<uint2*>(Z + prm.I + i4 * 8 + lhi * 4) = make_uint2(
+                    pack_bf16x2(U[i] * alpha, U[i + 1] * alpha), pack_bf16x2(U[i + 2] * alpha, U[i + 3] * alpha));
+              }
+            }
           }
         }
       }
@@ -1249,7 +1263,8 @@ static moe_status launch(int ep, bool pt, const MxParams& p, int64_t max_tiles, 
   if (max_tiles < grid) grid = max_tiles;
   const dim3 g((unsigned)grid), b(256);
   if (pt) {
-    if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_SWIGLU>), g, b, 0, s, p);
+    if (ep == MX_SWIGLU && p.z_save) hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_SWIGLU_SAVE>), g, b, 0, s, p);
+    else if (ep == MX_SWIGLU) hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_SWIGLU>), g, b, 0, s, p);
     else hipLaunchKernelGGL((grouped_gemm_fp8t_kernel<MX_STORE>), g, b, 0, s, p);
   } else if (sm) {
     if (ep == MX_SWIGLU && p.z_save) hipLaunchKernelGGL((grouped_gemm_mxw_kernel<MX_SWIGLU_SAVE>), g, b, 0, s, p);
@@ -1415,7 +1430,7 @@ size_t fp8_tensor_workspace_bytes(const moe_mlp_desc& d, int64_t R) {
 moe_status forward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const void* x_perm, const float* x_scale,
                               const void* const* w_gate_up, const void* const* w_down, const float* const* w_gate_up_scale,
                               const float* const* w_down_scale, const int32_t* offsets, const float* prob_perm,
-                              void* y_perm, uint8_t* ws, hipStream_t s) {
+                              void* y_perm, uint8_t* ws, hipStream_t s, void* z_save, void* h_save) {
   const int E = d.E, H = d.H, I = d.I;
   moe_status st = check_mx_shape(E, H, I, "moe_grouped_mlp_fwd");
   if (st != MOE_OK) return st;
@@ -1471,7 +1486,8 @@ moe_status forward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const void* x_pe
   // amax words of x and the weights -> scales (h's word stays an amax accumulator)
   if ((st = fp8t_finalize(words, 1 + 2 * E, s)) != MOE_OK) return st;
 
-  bf16_t* h = reinterpret_cast<bf16_t*>(ws);
+  // h in bf16 (its factor needs all of it first): the caller's h_save when saving
+  bf16_t* h = h_save ? reinterpret_cast<bf16_t*>(h_save) : reinterpret_cast<bf16_t*>(ws);
   ws += a256((size_t)R * I * 2);
   uint8_t* hq = ws;
   const int64_t mtiles = (R + kBM - 1) / kBM + E;
@@ -1479,6 +1495,7 @@ moe_status forward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const void* x_pe
   g.q = xq;
   g.q_s = reinterpret_cast<const uint8_t*>(xs);
   g.c = h;
+  g.z_save = z_save;
   g.c_s = reinterpret_cast<uint8_t*>(h_word);
   g.offsets = offsets;
   g.prob = prob_perm;

@@ -205,8 +205,6 @@ extern "C" moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, c
   if (!aligned(x_perm, align) || !aligned(y_perm, align))
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_mlp_fwd: x_perm / y_perm misaligned");
   if (d.save_for_bwd) {
-    if (d.compute == MOE_FP8)
-      return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_mlp_fwd: save_for_bwd needs BF16, F32 or MXFP8");
     if (!z_save || !h_save) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_mlp_fwd: save_for_bwd needs z_save and h_save");
     if (!aligned(z_save, align) || !aligned(h_save, align))
       return fail(MOE_ERR_INVALID_ARG, "moe_grouped_mlp_fwd: z_save / h_save misaligned");
@@ -241,7 +239,8 @@ extern "C" moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, c
     return mx::forward_fp8_tensor(d, R, x_perm, reinterpret_cast<const float*>(x_perm_scale), w_gate_up, w_down,
                                   reinterpret_cast<const float* const*>(w_gate_up_scale),
                                   reinterpret_cast<const float* const*>(w_down_scale), offsets, prob_perm, y_perm,
-                                  (uint8_t*)workspace, s);
+                                  (uint8_t*)workspace, s, d.save_for_bwd ? z_save : nullptr,
+                                  d.save_for_bwd ? h_save : nullptr);
   }
   if (d.compute == MOE_MXFP8) {
     return mx::forward(d, R, x_perm, x_perm_scale, w_gate_up, w_down, w_gate_up_scale, w_down_scale, offsets,

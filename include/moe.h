@@ -303,8 +303,9 @@ typedef struct {
  * -> one float each (wt = FP8). Outputs: y_perm [R, H] (bf16, or
  * float32 when compute = F32). With save_for_bwd: z_save [R, 2I] and h_save [R, I]
  * (bf16, or float32 when compute = F32; with MXFP8, z is the gate_up product of the
- * MXFP8 operands and h its ScaledSwiGLU before quantisation, both rounded to bf16);
- * otherwise both may be NULL. save_for_bwd is not available with compute = FP8.
+ * MXFP8 operands and h its ScaledSwiGLU before quantisation, both rounded to bf16;
+ * with FP8, z is the gate_up product of the FP8 operands times the two scales and h
+ * the bf16 value that is then quantised); otherwise both may be NULL.
  *   w_gate_up [host] E pointers to [2I, H]; w_down [host] E pointers to [H, I]
  *   w_gate_up_scale / w_down_scale [host] E pointers to [2I, H/32] / [H, I/32]
  *       E8M0 scales, only when wt = MXFP8 (else NULL)

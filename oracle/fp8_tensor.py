@@ -72,9 +72,11 @@ def bf16_round(a):
     return out
 
 
-def grouped_mlp_forward_fp8_tensor(x_perm, w_gate_up, w_down, offsets, prob_perm, x_scale=None):
+def grouped_mlp_forward_fp8_tensor(x_perm, w_gate_up, w_down, offsets, prob_perm, x_scale=None, return_zh=False):
     """y_perm [R, H] of the grouped MLP with every GEMM operand quantised per tensor.
-    x_scale: x_perm's scale when x_perm is part of a larger tensor (default: its own)."""
+    x_scale: x_perm's scale when x_perm is part of a larger tensor (default: its own).
+    return_zh: also return z [R, 2I] (the gate_up product of the quantised operands)
+    and h [R, I] (the bf16 value of h that is quantised), as (y, z, h)."""
     x = np.asarray(x_perm, np.float64)
     w1 = np.asarray(w_gate_up, np.float64)
     w2 = np.asarray(w_down, np.float64)
@@ -84,17 +86,20 @@ def grouped_mlp_forward_fp8_tensor(x_perm, w_gate_up, w_down, offsets, prob_perm
     R = x.shape[0]
     xq = fp8_tensor_qdq(x, x_scale)
     h = np.zeros((R, I))
+    z_all = np.zeros((R, 2 * I))
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b == a:
             continue
         z = xq[a:b] @ fp8_tensor_qdq(w1[e]).T
+        z_all[a:b] = z
         g, u = z[:, :I], z[:, I:]
         h[a:b] = g / (1.0 + np.exp(-g)) * u * p[a:b, None]
-    hq = fp8_tensor_qdq(bf16_round(h))
+    hb = bf16_round(h)
+    hq = fp8_tensor_qdq(hb)
     y = np.zeros((R, H))
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b > a:
             y[a:b] = hq[a:b] @ fp8_tensor_qdq(w2[e]).T
-    return y
+    return (y, z_all, hb) if return_zh else y

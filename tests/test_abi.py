@@ -104,8 +104,8 @@ def test_mlp_descriptor_checks(L):
 
 def test_fp8_tensor_argument_checks(L):
     """Per-tensor FP8: size and pointer checks before any launch; descriptor rules of the
-    FP8 forward (storage matching the compute dtype, no saved tensors) and backward
-    (bf16 activations and weights)."""
+    FP8 forward (storage matching the compute dtype, both saved tensors when saving) and
+    backward (bf16 activations and weights)."""
     from grouped_expert_gemm_amd import _lib
     INV, UNS = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED
     scale = ctypes.c_void_p(4096)
@@ -129,11 +129,12 @@ def test_fp8_tensor_argument_checks(L):
                                 ctypes.byref(n)) == INV                                # ... on bf16 activations
     ptrs = (ctypes.c_void_p * 8)(*([4096] * 8))
     pp = ctypes.cast(ptrs, _lib.PP)
+    # FP8 saves z and h for the backward too, and needs both buffers to do it
     d = D(8, 256, 256, FP8, BF16, BF16, 1)
     st = L.moe_grouped_mlp_fwd(ctypes.byref(d), 64, ctypes.c_void_p(4096), None, pp, pp, None, None,
                                ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
-                               ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096), 1 << 40, None)
-    assert st == UNS and b"save_for_bwd" in L.moe_last_error()
+                               None, ctypes.c_void_p(4096), ctypes.c_void_p(4096), 1 << 40, None)
+    assert st == INV and b"save_for_bwd" in L.moe_last_error()
     # MXFP8 saves z and h for the backward, and needs both buffers to do it
     d = D(8, 256, 256, MX, BF16, BF16, 1)
     st = L.moe_grouped_mlp_fwd(ctypes.byref(d), 64, ctypes.c_void_p(4096), None, pp, pp, None, None,
