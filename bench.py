@@ -98,7 +98,27 @@ class Layer:
         self.mx = mx or fp8
         self.fs1 = self.fs2 = None
         if fp8:  # the whole grouped MLP forward in per-tensor FP8 (one call), saving z and h when backward
-            self.desc_fwd = _lib.MlpDesc(E, H, I, _lib.MOE_FP8, _lib.MOE_BF16, _lib.MOE_BF16, int(backward))
+            wt = _lib.MOE_BF16
+            if prequant:
+                # weights quantised once, outside the timed steps: codes and one factor per expert
+                # weight for the forward, transposed packs for the backward
+                wt = _lib.MOE_FP8
+                q1 = [moe.fp8_tensor_quantize(self.w1[e]) for e in range(E)]
+                q2 = [moe.fp8_tensor_quantize(self.w2[e]) for e in range(E)]
+                self._q = (q1, q2)
+                self.t1, self._k1 = _lib.ptr_table([c.data_ptr() for c, _ in q1])
+                self.t2, self._k2 = _lib.ptr_table([c.data_ptr() for c, _ in q2])
+                self.fs1, self._k5 = _lib.ptr_table([f.data_ptr() for _, f in q1])
+                self.fs2, self._k6 = _lib.ptr_table([f.data_ptr() for _, f in q2])
+                if backward:
+                    self.pk1 = [moe.fp8_tensor_pack_weight_bwd(self.w1[e]) for e in range(E)]
+                    self.pk2 = [moe.fp8_tensor_pack_weight_bwd(self.w2[e]) for e in range(E)]
+                    self.b1, self._k7 = _lib.ptr_table([t.data_ptr() for t in self.pk1])
+                    self.b2, self._k8 = _lib.ptr_table([t.data_ptr() for t in self.pk2])
+                    self.desc = _lib.MlpDesc(E, H, I, _lib.MOE_FP8, _lib.MOE_BF16, _lib.MOE_FP8, 1)
+                    self.ws_bwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_BWD, self.desc, R),
+                                              dtype=torch.uint8, device=dev)
+            self.desc_fwd = _lib.MlpDesc(E, H, I, _lib.MOE_FP8, _lib.MOE_BF16, wt, int(backward))
             self.ws_fwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_FWD, self.desc_fwd, R), dtype=torch.uint8,
                                       device=dev)
         elif mx:  # the whole grouped MLP forward in MXFP8 (one call), saving z and h when backward
@@ -124,7 +144,7 @@ class Layer:
             self.desc_fwd = _lib.MlpDesc(E, H, I, _lib.MOE_MXFP8, _lib.MOE_BF16, wt, int(backward))
             self.ws_fwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_FWD, self.desc_fwd, R), dtype=torch.uint8,
                                       device=dev)
-        if not (mx and prequant and backward):
+        if not ((mx or fp8) and prequant and backward):
             self.b1, self.b2 = self.t1, self.t2
         self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self.ev = []
@@ -497,7 +517,9 @@ def fwd_bwd_measure(steps, warmup, mx=False, prequant=False, fp8=False):
            "ms_per_step": round(msb, 4), "flop_per_step": flopb}
     if fp8:
         rec.update(compute="fp8", pct_of_fp8_peak=round(100 * vb / peak, 2),
-                   weights="bf16 master weights, quantised inside every step (one factor per tensor)")
+                   weights=("FP8, quantised once outside the step (codes and factors for the forward, transposed "
+                            "packs for the backward)" if prequant else
+                            "bf16 master weights, quantised inside every step (one factor per tensor)"))
     elif mx:
         rec.update(compute="mxfp8", pct_of_fp8_peak=round(100 * vb / peak, 2),
                    weights=("MXFP8, quantised once outside the step (row-wise for the forward, packed for the "
@@ -563,6 +585,8 @@ def only_measurement(which, steps, warmup):
         return fwd_bwd_measure(steps, warmup, mx=True, prequant=True)
     if which == "fp8_fwd_bwd":
         return fwd_bwd_measure(steps, warmup, fp8=True)
+    if which == "fp8_fwd_bwd_pre":
+        return fwd_bwd_measure(steps, warmup, fp8=True, prequant=True)
     if which == "bwd":
         return bwd_measure(steps)
     if which == "qwen3":
@@ -596,7 +620,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip the MXFP8 and Qwen3 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["fwd_bwd", "mx_fwd_bwd", "mx_fwd_bwd_pre", "fp8_fwd_bwd", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise", "permute"],
+    ap.add_argument("--only", choices=["fwd_bwd", "mx_fwd_bwd", "mx_fwd_bwd_pre", "fp8_fwd_bwd", "fp8_fwd_bwd_pre", "bwd", "qwen3", "mxfp8", "fp8", "router", "colwise", "permute"],
                     help="run one measurement and print its record (kernel traces of that workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
@@ -688,6 +712,9 @@ def main():
                                                                prequant=True)
         torch.cuda.empty_cache()
         result["fp8_tensor_fwd_bwd"] = fwd_bwd_measure(max(3, args.steps // 2), args.warmup, fp8=True)
+        torch.cuda.empty_cache()
+        result["fp8_tensor_fwd_bwd_prequantised"] = fwd_bwd_measure(max(3, args.steps // 2), args.warmup,
+                                                                    fp8=True, prequant=True)
         torch.cuda.empty_cache()
         result["mlp_bwd"] = bwd_measure()
         torch.cuda.empty_cache()

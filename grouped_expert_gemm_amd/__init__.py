@@ -22,6 +22,7 @@ from ._lib import MOE_BF16, MOE_F32, MOE_FP8, MOE_MXFP8, MlpDesc, MoeError, chec
 __all__ = [
     "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
     "fp8_tensor_quantize", "mxfp8_quantize_colwise", "fp8_tensor_quantize_colwise", "mxfp8_pack_weight_bwd",
+    "fp8_tensor_pack_weight_bwd",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu", "gemm_workspace",
     "workspace_size", "MoeError", "lib",
     "MOE_F32", "MOE_BF16", "MOE_MXFP8", "MOE_FP8",
@@ -224,6 +225,20 @@ def fp8_tensor_quantize_colwise(x: torch.Tensor, offsets: torch.Tensor, pad: int
     return codes, scale, kofs
 
 
+def fp8_tensor_pack_weight_bwd(w: torch.Tensor) -> torch.Tensor:
+    """bf16 weight [rows, cols] -> packed per-tensor FP8 for moe_grouped_mlp_bwd (uint8,
+    rows * cols + 4 bytes: the codes of w^T, then the float32 factor)."""
+    _need_cuda(w)
+    if w.dtype != torch.bfloat16 or w.dim() != 2:
+        raise ValueError("fp8_tensor_pack_weight_bwd takes a 2-D bfloat16 weight")
+    w = w.contiguous()
+    rows, cols = w.shape
+    packed = torch.empty(rows * cols + 16, dtype=torch.uint8, device=w.device)
+    check("fp8_tensor_pack_weight_bwd", lib().fp8_tensor_pack_weight_bwd(_p(w), rows, cols, _p(packed),
+                                                                         _stream(w.device)))
+    return packed
+
+
 def mxfp8_pack_weight_bwd(w: torch.Tensor) -> torch.Tensor:
     """bf16 weight [rows, cols] -> packed MXFP8 for moe_grouped_mlp_bwd (uint8, rows * cols
     * 33 / 32 bytes: the codes of w^T quantised along rows, then the step-major scales)."""
@@ -295,7 +310,8 @@ def moe_grouped_mlp_bwd(dy_perm, x_perm, z, h, prob_perm, w_gate_up, w_down, off
                         dw_gate_up=None, dw_down=None, workspace: torch.Tensor | None = None):
     """Grouped MLP backward. Returns (dx_perm, dw_gate_up [E, 2I, H], dw_down [E, H, I], dprob_perm [R]).
 
-    With compute="mxfp8" the weights may be bf16 or packed by mxfp8_pack_weight_bwd (uint8)."""
+    With compute="mxfp8" the weights may be bf16 or packed by mxfp8_pack_weight_bwd (uint8); with
+    compute="fp8", bf16 or packed by fp8_tensor_pack_weight_bwd (uint8)."""
     w1 = _experts(w_gate_up)
     w2 = _experts(w_down)
     E = len(w1)
@@ -307,7 +323,8 @@ def moe_grouped_mlp_bwd(dy_perm, x_perm, z, h, prob_perm, w_gate_up, w_down, off
     _need_cuda(dy_perm, x_perm, z, h, prob_perm, offsets, *w1, *w2)
     c = _COMPUTE[compute]
     dt = torch.float32 if c == MOE_F32 else torch.bfloat16
-    desc = MlpDesc(E, H, I, c, _DT[x_perm.dtype], _DT[w1[0].dtype], 1)
+    wt = c if w1[0].dtype == torch.uint8 else _DT[w1[0].dtype]    # uint8: the compute dtype's packs
+    desc = MlpDesc(E, H, I, c, _DT[x_perm.dtype], wt, 1)
     dx = torch.empty((R, H), dtype=dt, device=dev)
     dw1 = dw_gate_up if dw_gate_up is not None else torch.empty((E, twoI, H), dtype=dt, device=dev)
     dw2 = dw_down if dw_down is not None else torch.empty((E, H, I), dtype=dt, device=dev)

@@ -20,7 +20,7 @@ MOE_MAX_EXPERTS = 256
 EXPORTS = (
     "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd",
     "moe_permute", "moe_permute_noalloc", "moe_unpermute_combine", "mxfp8_quantize", "fp8_tensor_quantize", "mxfp8_quantize_colwise",
-    "fp8_tensor_quantize_colwise",
+    "fp8_tensor_quantize_colwise", "fp8_tensor_pack_weight_bwd",
     "mxfp8_pack_weight_bwd",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu",
     "moe_workspace_size",
@@ -66,6 +66,7 @@ def _declare(lib):
         "fp8_tensor_quantize": [vp, i64, vp, vp, vp],
         "mxfp8_quantize_colwise": [vp, i64, i64, c_int, vp, c_int, i64, vp, vp, vp, vp],
         "fp8_tensor_quantize_colwise": [vp, i64, i64, c_int, vp, c_int, i64, vp, vp, vp, vp],
+        "fp8_tensor_pack_weight_bwd": [vp, i64, i64, vp, vp],
         "mxfp8_pack_weight_bwd": [vp, i64, i64, vp, vp],
         "moe_grouped_mlp_fwd": [ctypes.POINTER(MlpDesc), i64, vp, vp, PP, PP, PP, PP, vp, vp, vp, vp, vp, vp,
                                 sz, vp],

@@ -111,9 +111,13 @@ __global__ __launch_bounds__(256) void fp8t_finalize_kernel(uint32_t* words, int
 // multiple of pad (the weight-gradient GEMMs' token-axis operand). One factor per
 // tensor means the codes are those of the row-major quantiser, only transposed. A
 // workgroup takes 128 rows x 64 columns of one expert's padded range through LDS
-// (16-byte loads, rows past the expert read as zeros); lane (q, c) encodes rows
-// 32q .. 32q + 31 of column c and stores them as two 16-byte stores. Tensor
-// blockIdx.y of the table; words: the tensors' amax bits (before fp8t_finalize).
+// (16-byte loads, rows past the expert read as zeros; the next item's rows are loaded
+// while the current one is encoded); lane (q, c) encodes rows 32q .. 32q + 31 of column
+// c and stores them as two 16-byte stores. The codes come from gfx950's E4M3 conversion
+// (round to nearest even) of the correctly rounded quotient, as in the row-major
+// quantiser's software encoder for every quotient below 464: the largest is
+// amax / s = 448 (1 + at most a few ulps). Tensor blockIdx.y of the table; words: the
+// tensors' amax bits (before fp8t_finalize).
 struct Fp8TTab {
   const uint16_t* in[kTab];
   uint8_t* out[kTab];
@@ -121,8 +125,8 @@ struct Fp8TTab {
 
 template <bool kRecip>
 __device__ __forceinline__ uint32_t encode4(const float* t, float s, float r) {
-  return e4m3_encode(quotient<kRecip>(t[0], s, r)) | (e4m3_encode(quotient<kRecip>(t[65], s, r)) << 8) |
-         (e4m3_encode(quotient<kRecip>(t[130], s, r)) << 16) | (e4m3_encode(quotient<kRecip>(t[195], s, r)) << 24);
+  return e4m3_pack4(quotient<kRecip>(t[0], s, r), quotient<kRecip>(t[65], s, r), quotient<kRecip>(t[130], s, r),
+                    quotient<kRecip>(t[195], s, r));
 }
 
 __global__ __launch_bounds__(256) void fp8t_transpose_kernel(const Fp8TTab tab, int64_t R, int C, int E,
@@ -166,22 +170,37 @@ __global__ __launch_bounds__(256) void fp8t_transpose_kernel(const Fp8TTab tab, 
   const int total = s_item[E];
   const int r = tid >> 3, c8 = (tid & 7) * 8;  // load: rows r + 32i, columns c8 .. c8 + 7
   const int cc = tid & 63, q = tid >> 6;        // encode: rows 32q .. 32q + 31 of column cc
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  // item -> expert, 128-row group j, 64-column block cb
+  auto locate = [&](int item, int& e, int& j, int& cb) {
     int lo = 0, hi = E - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_item[mid] <= item) lo = mid; else hi = mid - 1;
     }
-    const int e = lo;
+    e = lo;
     const int local = item - s_item[e];
-    const int j = local / ncb, cb = local - (local / ncb) * ncb;
+    j = local / ncb;
+    cb = local - j * ncb;
+  };
+  uint4 v[4];  // an item's rows (rows past the expert as zeros)
+  auto fetch = [&](int item) {
+    int e, j, cb;
+    locate(item, e, j, cb);
     const int64_t row0 = (int64_t)s_off[e] + 128 * j;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = row0 + r + 32 * i;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < s_off[e + 1]) v = *reinterpret_cast<const uint4*>(x + row * C + cb * 64 + c8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (row < s_off[e + 1]) v[i] = *reinterpret_cast<const uint4*>(x + row * C + cb * 64 + c8);
+    }
+  };
+  if ((int)blockIdx.x < total) fetch(blockIdx.x);
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    int e, j, cb;
+    locate(item, e, j, cb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         tile[r + 32 * i][c8 + 2 * h] = bf16_to_f32(w[h] & 0xFFFFu);
@@ -189,6 +208,7 @@ __global__ __launch_bounds__(256) void fp8t_transpose_kernel(const Fp8TTab tab, 
       }
     }
     __syncthreads();
+    if (item + (int)gridDim.x < total) fetch(item + gridDim.x);
     const int nblk = (s_kofs[e + 1] - s_kofs[e]) / 32;        // 32-row groups in the expert's padded range
     if (q < nblk - 4 * j) {
       uint32_t wd[8];
@@ -335,4 +355,28 @@ extern "C" moe_status fp8_tensor_quantize_colwise(const void* x_bf16, int64_t R,
   if (C > 0 && (st = fp8t_transpose(in, out, 1, R, (int)C, E, offsets, pad, kcap, scale, kofs, s)) != MOE_OK)
     return st;
   return fp8t_finalize(scale, 1, s);
+}
+
+extern "C" moe_status fp8_tensor_pack_weight_bwd(const void* w_bf16, int64_t rows, int64_t cols, void* packed,
+                                                 void* stream) {
+  if (rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_pack_weight_bwd: negative size");
+  if (rows % 32 != 0 || cols % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "fp8_tensor_pack_weight_bwd: needs rows % 32 == 0 and cols % 64 == 0");
+  if (rows > 0x7FFFFFFF || rows * cols > 0x7FFFFFFFLL)
+    return fail(MOE_ERR_UNSUPPORTED, "fp8_tensor_pack_weight_bwd: weight exceeds 2^31 elements");
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!w_bf16 || !packed) return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_pack_weight_bwd: NULL pointer");
+  if (!aligned(w_bf16, 16) || !aligned(packed, 16))
+    return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_pack_weight_bwd: w and packed must be 16-byte aligned");
+  const hipStream_t s = as_stream(stream);
+  uint8_t* codes = reinterpret_cast<uint8_t*>(packed);
+  float* factor = reinterpret_cast<float*>(codes + rows * cols);  // rows * cols is a multiple of 4
+  moe_status st;
+  if ((st = fp8t_zero(factor, 1, s)) != MOE_OK) return st;
+  const void* in[1] = {w_bf16};
+  uint8_t* out[1] = {codes};
+  if ((st = fp8t_amax(in, 1, rows * cols, factor, s)) != MOE_OK) return st;
+  if ((st = fp8t_transpose(in, out, 1, rows, (int)cols, 1, nullptr, 32, rows, factor, nullptr, s)) != MOE_OK)
+    return st;
+  return fp8t_finalize(factor, 1, s);
 }

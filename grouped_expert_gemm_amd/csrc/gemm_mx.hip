@@ -1745,6 +1745,8 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
 // the weight gradients, the weights' transposed codes for the data gradients.
 //   dH = dY W2_e, dSwiGLU -> dZ (bf16), dprob, dx = dZ W1_e, dW2 = dY^T h, dW1 = dZ^T x
 // Factor words: [dY, h, x, W1_0 .. W1_E-1, W2_0 .. W2_E-1, dZ] (amax bits, then scales).
+// Weights packed by fp8_tensor_pack_weight_bwd (wt = FP8) bring their transposed codes
+// and factor: codes at the pointer, the float32 factor rows * cols bytes further.
 // ---------------------------------------------------------------------------------
 
 namespace {
@@ -1761,8 +1763,10 @@ Fp8BwdLayout fp8_bwd_layout(const moe_mlp_desc& d, int64_t R) {
   L.words = take((4 + 2 * E) * 4);
   L.dyq = take(R * H);
   L.dyc = take(H * kc);
-  L.w2t = take(E * I * H);
-  L.w1t = take(E * H * 2 * I);
+  if (d.wt == MOE_BF16) {  // transposed weight codes (packed weights bring their own)
+    L.w2t = take(E * I * H);
+    L.w1t = take(E * H * 2 * I);
+  }
   L.dh = take(R * I * 2);
   L.dz = take(R * 2 * I * 2);
   L.dzq = take(R * 2 * I);
@@ -1820,8 +1824,11 @@ moe_status backward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const bf16_t* d
   if ((st = fp8t_amax(t_dy, 1, R * H, w_dy, s)) != MOE_OK) return st;
   if ((st = fp8t_amax(t_h, 1, R * I, w_h, s)) != MOE_OK) return st;
   if ((st = fp8t_amax(t_x, 1, R * H, w_x, s)) != MOE_OK) return st;
-  if ((st = fp8t_amax(w_gate_up, E, (int64_t)2 * I * H, w_w1, s)) != MOE_OK) return st;
-  if ((st = fp8t_amax(w_down, E, (int64_t)H * I, w_w2, s)) != MOE_OK) return st;
+  const bool packed = d.wt == MOE_FP8;
+  if (!packed) {
+    if ((st = fp8t_amax(w_gate_up, E, (int64_t)2 * I * H, w_w1, s)) != MOE_OK) return st;
+    if ((st = fp8t_amax(w_down, E, (int64_t)H * I, w_w2, s)) != MOE_OK) return st;
+  }
   uint8_t* o_dyq[1] = {dyq};
   uint8_t* o_dyc[1] = {dyc};
   uint8_t* o_hc[1] = {hc};
@@ -1831,16 +1838,31 @@ moe_status backward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const bf16_t* d
   if ((st = fp8t_transpose(t_h, o_hc, 1, R, I, E, offsets, 256, kc, w_h, nullptr, s)) != MOE_OK) return st;
   if ((st = fp8t_transpose(t_x, o_xc, 1, R, H, E, offsets, 256, kc, w_x, nullptr, s)) != MOE_OK) return st;
   // W2_e [H][I] -> [I][H] (K = H for dH); W1_e [2I][H] -> [H][2I] (K = 2I for dx)
-  if ((st = transpose_each(w_down, w2t, w2n, E, H, I, w_w2, s)) != MOE_OK) return st;
-  if ((st = transpose_each(w_gate_up, w1t, w1n, E, 2 * I, H, w_w1, s)) != MOE_OK) return st;
-  if ((st = fp8t_finalize(words, 3 + 2 * E, s)) != MOE_OK) return st;
+  if (!packed) {
+    if ((st = transpose_each(w_down, w2t, w2n, E, H, I, w_w2, s)) != MOE_OK) return st;
+    if ((st = transpose_each(w_gate_up, w1t, w1n, E, 2 * I, H, w_w1, s)) != MOE_OK) return st;
+  }
+  if ((st = fp8t_finalize(words, 3, s)) != MOE_OK) return st;
+  if (!packed && (st = fp8t_finalize(w_w1, 2 * E, s)) != MOE_OK) return st;
+  auto w2_codes = [&](int e) -> const uint8_t* {
+    return packed ? reinterpret_cast<const uint8_t*>(w_down[e]) : w2t + e * w2n;
+  };
+  auto w1_codes = [&](int e) -> const uint8_t* {
+    return packed ? reinterpret_cast<const uint8_t*>(w_gate_up[e]) : w1t + e * w1n;
+  };
+  auto w2_factor = [&](int e) -> const uint8_t* {
+    return packed ? w2_codes(e) + w2n : reinterpret_cast<const uint8_t*>(w_w2 + e);
+  };
+  auto w1_factor = [&](int e) -> const uint8_t* {
+    return packed ? w1_codes(e) + w1n : reinterpret_cast<const uint8_t*>(w_w1 + e);
+  };
 
   // dH = dY W2_e
   MxParams p;
   std::memset(&p, 0, sizeof(p));
   for (int e = 0; e < E; ++e) {
-    p.tab[e] = w2t + e * w2n;
-    p.tab_s[e] = reinterpret_cast<const uint8_t*>(w_w2 + e);
+    p.tab[e] = w2_codes(e);
+    p.tab_s[e] = w2_factor(e);
   }
   p.q = dyq;
   p.q_s = reinterpret_cast<const uint8_t*>(w_dy);
@@ -1869,8 +1891,8 @@ moe_status backward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const bf16_t* d
 
   // dx = dZ W1_e
   for (int e = 0; e < E; ++e) {
-    p.tab[e] = w1t + e * w1n;
-    p.tab_s[e] = reinterpret_cast<const uint8_t*>(w_w1 + e);
+    p.tab[e] = w1_codes(e);
+    p.tab_s[e] = w1_factor(e);
   }
   p.q = dzq;
   p.q_s = reinterpret_cast<const uint8_t*>(w_dz);

@@ -37,8 +37,9 @@ moe_status validate_desc(const moe_mlp_desc& d, bool backward) {
     if (backward && d.I % 256 != 0)
       return fail(MOE_ERR_UNSUPPORTED, "grouped MLP backward: bf16 kernels need I % 256 == 0");
   }
-  if (backward && d.compute == MOE_FP8 && (d.act != MOE_BF16 || d.wt != MOE_BF16))
-    return fail(MOE_ERR_INVALID_ARG, "grouped MLP backward: per-tensor FP8 takes bf16 activations and bf16 weights");
+  if (backward && d.compute == MOE_FP8 && d.act != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "grouped MLP backward: per-tensor FP8 takes bf16 activations (and bf16 master "
+                                     "weights or weights packed by fp8_tensor_pack_weight_bwd)");
   if (backward && d.compute == MOE_MXFP8 && d.act != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "grouped MLP backward: MXFP8 takes bf16 activations (and bf16 master weights or "
                                      "weights packed by mxfp8_pack_weight_bwd)");

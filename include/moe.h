@@ -267,6 +267,20 @@ moe_status fp8_tensor_quantize_colwise(const void* x_bf16, int64_t R, int64_t C,
                                        int pad, int64_t kcap, uint8_t* e4m3_t, float* scale, int32_t* kofs,
                                        void* stream);
 
+/*
+ * Per-tensor FP8 packing of one bf16 weight for moe_grouped_mlp_bwd (the FP8 backward's
+ * data gradients take each weight transposed, K-contiguous: W2_e [H, I] as [I, H], W1_e
+ * [2I, H] as [H, 2I]). Source: Challenge 2 (FP8: one scaling factor for a whole tensor)
+ * and Challenge 3 (quantisation as separate ops is the overhead the fused recipe
+ * removes: a training loop packs each weight once per optimizer step).
+ *   w [rows, cols] bf16 (16-byte aligned)
+ *   packed (out, 16-byte aligned, rows * cols + 4 bytes): the E4M3 codes of the
+ *     transpose, [cols][rows] (element (c, r) is the code of w[r, c] under the rule of
+ *     fp8_tensor_quantize), then at byte rows * cols the tensor's float32 factor.
+ * Limits: rows % 32 == 0, cols % 64 == 0, rows * cols < 2^31.
+ */
+moe_status fp8_tensor_pack_weight_bwd(const void* w_bf16, int64_t rows, int64_t cols, void* packed, void* stream);
+
 /* Description of one grouped MLP layer (the experts' shapes and precisions). */
 typedef struct {
   int E;             /* experts, 1..MOE_MAX_EXPERTS */
@@ -322,7 +336,7 @@ moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, const void* 
 
 /*
  * Grouped MLP backward (the "matching fused backward" of Challenge 3), compute
- * BF16, F32 or MXFP8. With dY = dy_perm (gradient of y_perm), G, U = the halves of z_save,
+ * BF16, F32, MXFP8 or FP8. With dY = dy_perm (gradient of y_perm), G, U = the halves of z_save,
  * A = silu(G) * U, p = prob_perm, per expert e:
  *   dW2_e    = dY^T h_save                          -> dw_down[e]    [H, I]
  *   dH       = dY W2_e
@@ -346,6 +360,13 @@ moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, const void* 
  * about R (3.1 H + 11.2 I) + 3.1 E H I bytes (the last term only for bf16 weights),
  * plus (2H + 3I) bytes per padding row of the token-axis layouts (3.0 GB at R = 8192,
  * H = 4096, I = 14336, E = 8, bf16 weights). Calls sharing a workspace must not overlap.
+ * compute = FP8 (act BF16; wt BF16, or FP8 for weights packed by
+ * fp8_tensor_pack_weight_bwd, laid out as for MXFP8 above): every GEMM operand is one
+ * tensor quantised by the rule of fp8_tensor_quantize (Challenge 2's FP8: one factor per
+ * tensor): dY, dZ, h_save and x_perm each over all R rows, W1_e and W2_e each per
+ * expert; a product is scaled by its two tensors' factors. dH and dZ are rounded to
+ * bf16 before use, as for MXFP8. Same shape limits; the workspace holds the same
+ * operands with one code per element and no scales.
  */
 moe_status moe_grouped_mlp_bwd(const moe_mlp_desc* desc, int64_t R, const void* dy_perm,
                                const void* x_perm, const void* z_save, const void* h_save,

@@ -85,7 +85,7 @@ def test_mlp_descriptor_checks(L):
     assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, 3, 3, 1, 0)), 1, 0, 0, 0,
                                 ctypes.byref(n)) == _lib.MOE_ERR_INVALID_ARG    # FP8 backward: bf16 activations
     assert L.moe_workspace_size(2, ctypes.byref(D(8, 4096, 14336, 3, 1, 3, 0)), 1, 0, 0, 0,
-                                ctypes.byref(n)) == _lib.MOE_ERR_INVALID_ARG    # ... and bf16 weights
+                                ctypes.byref(n)) == 0                           # ... packed FP8 weights
     assert L.moe_workspace_size(1, ctypes.byref(D(0, 256, 128, 1, 1, 1, 0)), 1, 0, 0, 0,
                                 ctypes.byref(n)) == _lib.MOE_ERR_INVALID_ARG
     assert L.moe_workspace_size(1, ctypes.byref(D(8, 256, 128, 1, 0, 1, 0)), 1, 0, 0, 0,
@@ -182,3 +182,9 @@ def test_pack_weight_argument_checks(L):
     assert L.mxfp8_pack_weight_bwd(dummy, 128, 96, dummy, None) == _lib.MOE_ERR_UNSUPPORTED   # cols % 64
     assert L.mxfp8_pack_weight_bwd(None, 128, 64, dummy, None) == _lib.MOE_ERR_INVALID_ARG
     assert L.mxfp8_pack_weight_bwd(None, 0, 64, None, None) == 0                             # empty: no-op
+    f = L.fp8_tensor_pack_weight_bwd
+    assert f(dummy, 100, 64, dummy, None) == _lib.MOE_ERR_UNSUPPORTED    # rows % 32
+    assert f(dummy, 128, 96, dummy, None) == _lib.MOE_ERR_UNSUPPORTED    # cols % 64
+    assert f(None, 128, 64, dummy, None) == _lib.MOE_ERR_INVALID_ARG
+    assert f(dummy, 128, 64, ctypes.c_void_p(264), None) == _lib.MOE_ERR_INVALID_ARG  # packed misaligned
+    assert f(None, 0, 64, None, None) == 0                               # empty: no-op

@@ -194,3 +194,45 @@ def test_fp8_colwise_codes_bit_exact(moe, sizes, C, mag):
         block = got[:, kofs[e]:kofs[e + 1]]
         assert np.array_equal(block[:, :m], ref_codes[a:a + m].T), e
         assert not block[:, m:].any(), e
+
+
+@pytest.mark.parametrize("rows,cols", [(512, 384), (32, 64), (1024, 1536)])
+def test_fp8_pack_weight_bwd_bits(moe, rows, cols):
+    """fp8_tensor_pack_weight_bwd: the oracle's per-tensor codes of w, transposed, then
+    its float32 factor, bit for bit."""
+    rng = np.random.default_rng(rows + cols)
+    w = 0.05 * rng.standard_normal((rows, cols))
+    w[:3, :5] = 0.0
+    wb = _bits(w)
+    packed = moe.fp8_tensor_pack_weight_bwd(dev_bf16(wb))
+    torch.cuda.synchronize()
+    got = packed.cpu().numpy()
+    codes, factor = oracle.fp8_tensor_quantize(bf16_bits_to_f32(wb))
+    assert np.array_equal(got[:rows * cols].reshape(cols, rows), codes.T)
+    assert got[rows * cols:rows * cols + 4].view(np.float32)[0] == factor
+
+
+def test_fp8_backward_with_packed_weights(moe):
+    """The FP8 backward on weights packed once by fp8_tensor_pack_weight_bwd gives the
+    same bits as on the bf16 master weights quantised inside the call."""
+    T, H, I, E, k = 700, 512, 256, 4, 2
+    w = scaled(WORKLOADS["mixtral_fwd_bwd"], T=T, H=H, I=I, E=E, k=k, seed=57)
+    inp = make_inputs(w)
+    idx, p, m, pp = oracle_perm(inp, k, E)
+    R = T * k
+    xp_bits = inp.bits["x"][m["src_token"]]
+    rng = np.random.default_rng(8)
+    zb = _bits(rng.standard_normal((R, 2 * I)))
+    hb = _bits(0.3 * rng.standard_normal((R, I)))
+    dyf, dyb = make_grad((R, H), 89)
+    off = torch.from_numpy(m["offsets"].astype(np.int32)).cuda()
+    w1, w2 = dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"])
+    args = (dev_bf16(dyb), dev_bf16(xp_bits), dev_bf16(zb), dev_bf16(hb), dev_f32(pp.astype(np.float32)))
+    print("fp8 bwd: packed weights", flush=True)
+    a = moe.moe_grouped_mlp_bwd(*args, w1, w2, off, compute="fp8")
+    p1 = [moe.fp8_tensor_pack_weight_bwd(w1[e]) for e in range(E)]
+    p2 = [moe.fp8_tensor_pack_weight_bwd(w2[e]) for e in range(E)]
+    b = moe.moe_grouped_mlp_bwd(*args, p1, p2, off, compute="fp8")
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
