@@ -41,9 +41,28 @@ def fp8_tensor_quantize(x, scale=None):
     return e4m3_encode(q.astype(np.float64)), s
 
 
-def fp8_tensor_qdq(x, scale=None) -> np.ndarray:
-    codes, s = fp8_tensor_quantize(x, scale)
-    return e4m3_decode(codes) * np.float64(s)
+def fp8_tensor_qdq(x, scale=None, chunk: int = 1 << 22) -> np.ndarray:
+    """Quantise then dequantise a whole tensor. The factor needs the whole tensor; the
+    codes are elementwise, so tensors of more than `chunk` elements are encoded in
+    chunks on host threads (numpy releases the interpreter lock in its array loops):
+    the same bits as one call on the whole tensor."""
+    a = np.asarray(x, np.float32)
+    if a.size <= chunk:
+        codes, s = fp8_tensor_quantize(a, scale)
+        return e4m3_decode(codes) * np.float64(s)
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    s = fp8_tensor_scale(a) if scale is None else np.float32(scale)
+    flat = a.reshape(-1)
+    out = np.empty(flat.size, np.float64)
+
+    def one(i):
+        codes, _ = fp8_tensor_quantize(flat[i:i + chunk], s)
+        out[i:i + chunk] = e4m3_decode(codes) * np.float64(s)
+
+    with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
+        list(ex.map(one, range(0, flat.size, chunk)))
+    return out.reshape(a.shape)
 
 
 BF16_MAX = float.fromhex("0x1.fep127")   # largest finite bfloat16: (2 - 2^-7) * 2^127
@@ -58,8 +77,26 @@ def bf16_round(a):
     power of two), rounded half to even by np.rint, and scaled back (exact). Results
     beyond the largest finite value become +-inf (IEEE rounding of an overflow);
     zeros, infinities and NaN pass through. There is no float32 step in between, so
-    no double rounding."""
+    no double rounding. Large inputs are rounded in chunks on host threads (the
+    rounding is elementwise: the same bits)."""
     a = np.asarray(a, np.float64)
+    if a.size > (1 << 22):
+        import os
+        from concurrent.futures import ThreadPoolExecutor
+        flat = a.reshape(-1)
+        res = np.empty_like(flat)
+        step = 1 << 22
+
+        def one(i):
+            res[i:i + step] = _bf16_round_flat(flat[i:i + step])
+
+        with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
+            list(ex.map(one, range(0, flat.size, step)))
+        return res.reshape(a.shape)
+    return _bf16_round_flat(a)
+
+
+def _bf16_round_flat(a):
     out = np.array(a, dtype=np.float64, copy=True)
     fin = np.isfinite(a) & (a != 0)
     v = a[fin]

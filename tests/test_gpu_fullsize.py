@@ -6,7 +6,9 @@ GPU's combine.
 
   * routing indices and the permutation: bit-exact for all tokens;
   * bf16 outputs: max|a-b| / max|b| <= 2e-2 per expert and over all tokens;
-  * MXFP8 outputs: <= 6e-2 against the oracle's quantise/dequantise reference;
+  * MXFP8 and per-tensor FP8 outputs: <= 6e-2 against the oracle's
+    quantise/dequantise reference (per-tensor FP8: one test over all rows, since a
+    tensor's factor spans every expert);
   * backward: y, dx and dprob rows and both weight gradients of every expert; dx and the
     GPU's dprob gather ([T, k], the gradient w.r.t. the routing probabilities) over all
     tokens.
@@ -24,6 +26,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 BF16_TOL = 2e-2
 MX_TOL = 6e-2
+FP8_TOL = 6e-2
 
 
 @pytest.fixture(scope="module")
@@ -276,9 +279,10 @@ def _mx_fwd_bwd_run(moe):
 @pytest.mark.parametrize("e", range(8))
 def test_mxfp8_forward_backward_full_size_expert(moe, e):
     """Expert e of the MXFP8 training step: y, and the saved z and h, against the
-    oracle's MXFP8 forward; dx, dprob, dW1, dW2 against the oracle's MXFP8 backward on
-    the GPU's saved z and h (the backward's inputs, taken as given), both with the bf16
-    roundings of dH and dZ that the recipe's return to bf16 implies and without them."""
+    oracle's MXFP8 forward; dx, dprob, dW1, dW2 (the GPU backward ran on the GPU's saved
+    z and h) against the oracle's MXFP8 backward on the oracle forward's own z and h
+    rounded to bf16, both with the bf16 roundings of dH and dZ that the recipe's return
+    to bf16 implies and without them."""
     run = _mx_fwd_bwd_run(moe)
     a, b, x, pe, W1, W2 = _expert(run, e)
     offs = np.array([0, b - a])
@@ -286,7 +290,7 @@ def test_mxfp8_forward_backward_full_size_expert(moe, e):
     fwd = {"y": max_rel_err(run["y"][a:b], y), "z": max_rel_err(bf16_bits_to_f32(run["z"][a:b]), z_ref),
            "h": max_rel_err(bf16_bits_to_f32(run["h"][a:b]), h_ref)}
     dy = bf16_bits_to_f32(run["inp"].bits["dout"][run["m"]["src_token"][a:b]])
-    zs, hs = bf16_bits_to_f32(run["z"][a:b]), bf16_bits_to_f32(run["h"][a:b])
+    zs, hs = oracle.bf16_round(z_ref), oracle.bf16_round(h_ref)
     got = {"dx_perm": run["dxp"][a:b], "dprob_perm": run["dprob_perm"][a:b],
            "dw_gate_up": bf16_bits_to_f32(run["dw1"][e]), "dw_down": bf16_bits_to_f32(run["dw2"][e])}
     errs = {}
@@ -317,9 +321,11 @@ def test_mxfp8_forward_backward_full_size_tokens(moe):
     for e in range(w.E):
         a, b, x, pe, W1, W2 = _expert(run, e)
         if e not in run["ref"]:
+            offs = np.array([0, b - a])
             dy = bf16_bits_to_f32(run["inp"].bits["dout"][m["src_token"][a:b]])
-            g = oracle.grouped_mlp_backward_mxfp8(dy, x, bf16_bits_to_f32(run["z"][a:b]),
-                                                  bf16_bits_to_f32(run["h"][a:b]), W1, W2, np.array([0, b - a]), pe)
+            _, h_ref, z_ref = oracle.grouped_mlp_forward_mxfp8(x, W1, W2, offs, pe, return_z=True)
+            g = oracle.grouped_mlp_backward_mxfp8(dy, x, oracle.bf16_round(z_ref), oracle.bf16_round(h_ref), W1, W2,
+                                                  offs, pe)
             run["ref"][e] = dict(dx_perm=g["dx_perm"])
         ref_dxp[a:b] = run["ref"][e]["dx_perm"]
     err = max_rel_err(run["dx"], oracle.unpermute_combine(ref_dxp, m["row_id_map"], w.T, w.k))
@@ -327,4 +333,57 @@ def test_mxfp8_forward_backward_full_size_tokens(moe):
     record_parity("full size mixtral_fwd_bwd MXFP8 all tokens", dx=err)
     assert err <= MX_TOL
     _RUNS.clear()
+    _INPUTS.clear()
+
+
+# ---------------------------------------------------------------------------
+# Mixtral forward + backward (T = 4096), grouped MLP in per-tensor FP8
+# ---------------------------------------------------------------------------
+
+def test_fp8_forward_backward_full_size(moe):
+    """The per-tensor FP8 training step at the full Mixtral fwd+bwd size, every expert
+    and every token: y, the saved z and h against the oracle's FP8 forward over all rows;
+    dx (per row and after the GPU combine), dprob, dW1, dW2 (the GPU backward ran on the
+    GPU's saved z and h) against the oracle's FP8 backward on the oracle forward's own z
+    (rounded to bf16) and bf16 h, with dH and dZ rounded to bf16 (the reading without
+    those roundings is checked at the small shapes of test_gpu_fp8_bwd.py). One factor
+    per tensor spans all experts, so the oracle runs on all rows at once."""
+    w = WORKLOADS["mixtral_fwd_bwd"]
+    inp = _inputs("mixtral_fwd_bwd")
+    _RUNS.clear()
+    print(f"mixtral_fwd_bwd: T={w.T} H={w.H} I={w.I}, GPU layer forward + backward (per-tensor FP8)", flush=True)
+    idx, r, m, pp = _route_and_permute(moe, inp, w)
+    w1, w2 = dev_bf16(inp.bits["w1"]), dev_bf16(inp.bits["w2"])
+    y, z, h = moe.moe_grouped_mlp_fwd(r["x_perm"], w1, w2, r["offsets"], r["prob_perm"], compute="fp8",
+                                      save_for_bwd=True)
+    dyp = moe.moe_permute(dev_bf16(inp.bits["dout"]), idx, None, w.E, row_id_map=r["row_id_map"])["x_perm"]
+    dxp, dw1, dw2, dprob = moe.moe_grouped_mlp_bwd(dyp, r["x_perm"], z, h, r["prob_perm"], w1, w2, r["offsets"],
+                                                   compute="fp8")
+    dx = moe.moe_unpermute_combine(dxp, r["row_id_map"], w.T, w.k)
+    got = dict(y=_h32(y), z=_h32(z), h=_h32(h), dx_perm=_h32(dxp), dx=_h32(dx), dprob_perm=dprob.cpu().numpy(),
+               dw_gate_up=_h32(dw1), dw_down=_h32(dw2))
+    del idx, r, w1, w2, y, z, h, dyp, dxp, dw1, dw2, dprob, dx
+    _done_with_gpu()
+    off, src = m["offsets"], m["src_token"]
+    x = bf16_bits_to_f32(inp.bits["x"][src])
+    W1, W2 = bf16_bits_to_f32(inp.bits["w1"]), bf16_bits_to_f32(inp.bits["w2"])
+    y_ref, z_ref, h_ref = oracle.grouped_mlp_forward_fp8_tensor(x, W1, W2, off, pp, return_zh=True)
+    fwd = {"y": max_rel_err(got["y"], y_ref), "z": max_rel_err(got["z"], z_ref), "h": max_rel_err(got["h"], h_ref)}
+    print("  forward " + ", ".join(f"{k} {v:.2e}" for k, v in fwd.items()), flush=True)
+    dy = bf16_bits_to_f32(inp.bits["dout"][src])
+    g = oracle.grouped_mlp_backward_fp8_tensor(dy, x, oracle.bf16_round(z_ref), h_ref, W1, W2, off, pp)
+    errs = {k: max_rel_err(got[k], g[k]) for k in ("dx_perm", "dprob_perm", "dw_gate_up", "dw_down")}
+    errs["dx"] = max_rel_err(got["dx"], oracle.unpermute_combine(g["dx_perm"], m["row_id_map"], w.T, w.k))
+    for e in range(w.E):   # every expert's weight gradients on their own scale
+        errs[f"dw_gate_up[{e}]"] = max_rel_err(got["dw_gate_up"][e], g["dw_gate_up"][e])
+        errs[f"dw_down[{e}]"] = max_rel_err(got["dw_down"][e], g["dw_down"][e])
+    print("  backward " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items() if "[" not in k)
+          + f"; worst expert dW1 {max(v for k, v in errs.items() if k.startswith('dw_gate_up[')):.2e}, "
+          f"dW2 {max(v for k, v in errs.items() if k.startswith('dw_down[')):.2e}", flush=True)
+    record_parity("full size mixtral_fwd_bwd FP8 forward", **fwd)
+    record_parity("full size mixtral_fwd_bwd FP8 backward, dH/dZ rounded to bf16",
+                  **{k: v for k, v in errs.items() if "[" not in k})
+    assert fwd["y"] <= FP8_TOL and fwd["z"] <= 1e-2 and fwd["h"] <= 1e-2
+    for k, v in errs.items():
+        assert v <= FP8_TOL, k
     _INPUTS.clear()

@@ -91,3 +91,13 @@ def test_float32_inputs_agree_with_the_input_generator():
     x = (rng.standard_normal(100000) * np.exp2(rng.uniform(-130, 120, 100000))).astype(np.float32)
     want = (f32_to_bf16_bits(x).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert np.array_equal(oracle.bf16_round(x.astype(np.float64)), want)
+
+
+def test_large_inputs_round_in_chunks_to_the_same_bits():
+    # above 2^22 elements the rounding runs in chunks on threads: the same values
+    rng = np.random.default_rng(21)
+    v = rng.standard_normal((1 << 22) + 12345) * np.exp(rng.uniform(-30, 30, (1 << 22) + 12345))
+    big = oracle.bf16_round(v)
+    for i in (0, 1 << 21, (1 << 22) + 100):
+        part = v[i:i + 5000]
+        assert np.array_equal(oracle.bf16_round(part), big[i:i + 5000])

@@ -235,3 +235,13 @@ def test_fp8_backward_matches_brute_force_quantisation_on_generic_operands():
             continue
         np.testing.assert_allclose(got["dx_perm"][a:b], dzq[a:b] @ qw1[e], rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(got["dw_gate_up"][e], dzq[a:b].T @ qx[a:b], rtol=1e-12, atol=1e-14)
+
+
+def test_qdq_chunks_give_the_same_bits():
+    # the factor is the whole tensor's; the threaded chunked encoding equals one call
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((300, 70)) * np.exp(rng.uniform(-8, 4, (300, 70)))).astype(np.float32)
+    whole = oracle.fp8_tensor_qdq(x)
+    assert np.array_equal(oracle.fp8_tensor_qdq(x, chunk=1000), whole)
+    assert np.array_equal(oracle.fp8_tensor_qdq(x, scale=np.float32(0.5), chunk=777),
+                          oracle.fp8_tensor_qdq(x, scale=np.float32(0.5)))
