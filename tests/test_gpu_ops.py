@@ -153,10 +153,11 @@ def test_permute_drops_repeated_and_out_of_range_ids(moe):
     pp = p.ravel()[m["src_token"][:n] * k + m["src_slot"][:n]]
     assert np.array_equal(r["prob_perm"].cpu().numpy()[:n], pp)
     # the combine adds only the kept pairs of each token
+    yh = rng.standard_normal((n, H)).astype(np.float32)
     y = torch.zeros((T * k, H), dtype=torch.float32, device="cuda")
-    y[:n] = torch.from_numpy(rng.standard_normal((n, H)).astype(np.float32)).cuda()
+    y[:n] = torch.from_numpy(yh).cuda()
     out = moe.moe_unpermute_combine(y, r["row_id_map"], T, k).cpu().numpy()
-    ref = oracle.unpermute_combine(np.concatenate([y[:n].cpu().numpy(), np.zeros((1, H))]),
+    ref = oracle.unpermute_combine(np.concatenate([yh, np.zeros((1, H), np.float32)]),
                                    np.where(m["row_id_map"] < 0, n, m["row_id_map"]), T, k)
     assert np.abs(out - ref).max() <= 1e-6 * np.abs(ref).max()
 
