@@ -1581,6 +1581,174 @@ __global__ __launch_bounds__(256) void mx_dswiglu_kernel(const bf16_t* __restric
   if (threadIdx.x == 0) dprob[r] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// dSwiGLU fused with both MXFP8 quantisations of dZ, so dZ never goes through HBM in
+// bf16: dZ = [dG, dU] is formed as mx_dswiglu_kernel forms it (the same float32
+// operations, then rounded to bf16), quantised by rows (K = 2I of the dx GEMM; the rule
+// and step-major layout of launch_mxfp8_quantize_step_major) and along each expert's
+// tokens (K of the dW1 GEMM; the rule and step-major layout of launch_mxfp8_colwise
+// with pad 256), so the codes are those of the separate kernels bit for bit. An item is
+// 128 rows of one expert's 256-padded row range (rows past the expert are zeros) by 64
+// columns of I, i.e. 64 gate and 64 up columns of dZ: thread t loads rows t / 8 + 32 i
+// (i < 4), columns 8 (t % 8) .. + 8 of dH, G and U (16-byte loads); 4 threads own a
+// 32-value row block; the token-axis blocks go through an LDS tile as in the
+// column-wise quantiser. dprob: one partial per row and item, part[r * I / 64 + cb],
+// summed in order by mx_dprob_sum_kernel.
+__global__ __launch_bounds__(256) void mx_dswiglu_quant_kernel(
+    const bf16_t* __restrict__ dh, const bf16_t* __restrict__ z, const float* __restrict__ prob,
+    const int32_t* __restrict__ offsets, int E, int R, int I, int64_t kcap, uint8_t* __restrict__ dzq,
+    uint8_t* __restrict__ dzs, uint8_t* __restrict__ dzc, uint8_t* __restrict__ dzcs, float* __restrict__ part) {
+  __shared__ int32_t s_off[kMaxE + 1];
+  __shared__ int32_t s_kofs[kMaxE + 1];
+  __shared__ int32_t s_item[kMaxE + 1];
+  __shared__ float tile[128][65];
+  const int tid = threadIdx.x;
+  const int ncb = I / 64;
+  const int64_t I2 = 2 * (int64_t)I;
+  if (tid == 0) {  // offsets made nondecreasing inside [0, R]; experts padded to 256 rows
+    int prev = 0, kacc = 0, iacc = 0;
+    for (int e = 0; e <= E; ++e) {
+      int v = e == 0 ? 0 : offsets[e];
+      v = v < prev ? prev : v;
+      v = v > R ? R : v;
+      if (e > 0) {
+        const int kp = (v - prev + 255) / 256 * 256;
+        s_kofs[e - 1] = kacc;
+        s_item[e - 1] = iacc;
+        kacc += kp;
+        iacc += kp / 128 * ncb;
+      }
+      s_off[e] = v;
+      prev = v;
+    }
+    s_kofs[E] = kacc;
+    s_item[E] = iacc;
+  }
+  __syncthreads();
+  const int total = s_item[E];
+  const int r = tid >> 3, c8 = (tid & 7) * 8;  // load and row blocks: rows r + 32 i, columns c8 .. c8 + 7
+  const int cc = tid & 63, q = tid >> 6;        // token blocks: rows 32 q .. 32 q + 31 of column cc
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_item[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int local = item - s_item[e];
+    const int j = local / ncb, cb = local - (local / ncb) * ncb;
+    const int row_end = s_off[e + 1];
+    const int64_t k0 = (int64_t)s_kofs[e] + 128 * j;
+    uint32_t g_bits[4][4], u_bits[4][4];  // dG, dU of this thread's 4 rows x 8 columns, bf16 pairs
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = s_off[e] + 128 * j + r + 32 * i;
+      const bool live = row < row_end;
+      uint4 dv = make_uint4(0, 0, 0, 0), gv = dv, uv = dv;
+      float p = 0.f;
+      if (live) {
+        dv = *reinterpret_cast<const uint4*>(dh + (int64_t)row * I + cb * 64 + c8);
+        gv = *reinterpret_cast<const uint4*>(z + (int64_t)row * I2 + cb * 64 + c8);
+        uv = *reinterpret_cast<const uint4*>(z + (int64_t)row * I2 + I + cb * 64 + c8);
+        p = prob[row];
+      }
+      const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w},
+                     uw[4] = {uv.x, uv.y, uv.z, uv.w};
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float dg2[2], du2[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float d = bf16_to_f32(hh ? dw[w] >> 16 : dw[w] & 0xFFFFu);
+          const float G = bf16_to_f32(hh ? gw[w] >> 16 : gw[w] & 0xFFFFu);
+          const float U = bf16_to_f32(hh ? uw[w] >> 16 : uw[w] & 0xFFFFu);
+          const float sg = 1.f / (1.f + expf(-G));
+          acc += d * (G * sg * U);
+          const float dA = d * p;
+          dg2[hh] = dA * U * sg * (1.f + G * (1.f - sg));
+          du2[hh] = dA * G * sg;
+        }
+        g_bits[i][w] = pack_bf16x2(dg2[0], dg2[1]);
+        u_bits[i][w] = pack_bf16x2(du2[0], du2[1]);
+      }
+      // dprob partial of the row: the 8 threads of a row, in a fixed order
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      acc += __shfl_xor(acc, 4);
+      if (live && (tid & 7) == 0) part[(int64_t)row * ncb + cb] = acc;
+      // row blocks of 32 values (4 threads each), gate then up
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint32_t* b = half ? u_bits[i] : g_bits[i];
+        float f[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          f[2 * w] = bf16_to_f32(b[w] & 0xFFFFu);
+          f[2 * w + 1] = bf16_to_f32(b[w] >> 16);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) amax = fmaxf(amax, fabsf(f[w]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        const int sx = mx_scale_exponent(amax);
+        if (live) {
+          const int64_t col = (int64_t)half * I + cb * 64 + c8;
+          *reinterpret_cast<uint2*>(dzq + (int64_t)row * I2 + col) =
+              make_uint2(e4m3_pack4(ldexpf(f[0], -sx), ldexpf(f[1], -sx), ldexpf(f[2], -sx), ldexpf(f[3], -sx)),
+                         e4m3_pack4(ldexpf(f[4], -sx), ldexpf(f[5], -sx), ldexpf(f[6], -sx), ldexpf(f[7], -sx)));
+          if ((tid & 3) == 0) {  // step-major: block bc = col / 32 of row `row`
+            const int64_t bc = col >> 5;
+            dzs[((bc >> 2) * R + row) * 4 + (bc & 3)] = (uint8_t)(sx + 127);
+          }
+        }
+      }
+    }
+    // token blocks: gate columns, then up columns, through the LDS tile
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t* b = half ? u_bits[i] : g_bits[i];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          tile[r + 32 * i][c8 + 2 * w] = bf16_to_f32(b[w] & 0xFFFFu);
+          tile[r + 32 * i][c8 + 2 * w + 1] = bf16_to_f32(b[w] >> 16);
+        }
+      }
+      __syncthreads();
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(tile[32 * q + i][cc]));
+      const int sx = mx_scale_exponent(amax);
+      uint32_t wd[8];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const float* t = &tile[32 * q + 4 * g][cc];
+        wd[g] = e4m3_pack4(ldexpf(t[0], -sx), ldexpf(t[65], -sx), ldexpf(t[130], -sx), ldexpf(t[195], -sx));
+      }
+      const int64_t col = (int64_t)half * I + cb * 64 + cc;
+      const int64_t k = k0 + 32 * q;
+      uint4* dst = reinterpret_cast<uint4*>(dzc + col * kcap + k);
+      dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+      dzcs[((k >> 7) * I2 + col) * 4 + ((k >> 5) & 3)] = (uint8_t)(sx + 127);
+      __syncthreads();  // the tile is rewritten next
+    }
+  }
+}
+
+// dprob[r] = the sum of the row's I / 64 partials, in column-block order
+__global__ __launch_bounds__(256) void mx_dprob_sum_kernel(const float* __restrict__ part, int R, int ncb,
+                                                           float* __restrict__ dprob) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= R) return;
+  const float* pr = part + (int64_t)r * ncb;
+  float acc = 0.f;
+  for (int c = 0; c < ncb; ++c) acc += pr[c];
+  dprob[r] = acc;
+}
+
 // token-axis layout: every expert padded to whole 256-row K steps of the GEMM
 int64_t bwd_kcap(int64_t R, int E) { return (R + (int64_t)E * 255 + 255) / 256 * 256; }
 
@@ -1602,7 +1770,7 @@ BwdLayout bwd_layout(const moe_mlp_desc& d, int64_t R) {
     L.w1s = take(E * H * 2 * I / 32);
   }
   L.dh = take(R * I * 2);
-  L.dz = take(R * 2 * I * 2);
+  L.dz = take(R * (I / 64) * 4);  // dprob partials (dZ itself is only stored as MXFP8)
   L.dzq = take(R * 2 * I);
   L.dzs = take(R * 2 * I / 32);
   L.dyc = take(H * kc);
@@ -1634,7 +1802,8 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
     return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_mlp_bwd: MXFP8 token-axis operands exceed 2^31 bytes");
   const BwdLayout L = bwd_layout(d, R);
   uint8_t *dyq = ws + L.dyq, *dys = ws + L.dys, *dzq = ws + L.dzq, *dzs = ws + L.dzs;
-  bf16_t *dh = (bf16_t*)(ws + L.dh), *dz = (bf16_t*)(ws + L.dz);
+  bf16_t* dh = (bf16_t*)(ws + L.dh);
+  float* part = (float*)(ws + L.dz);
   int32_t* kofs = (int32_t*)(ws + L.kofs);
   const size_t w2n = (size_t)I * H, w1n = (size_t)H * 2 * I;
   const int64_t mtiles = (R + kBM - 1) / kBM + E;
@@ -1674,14 +1843,20 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
   p.n_tiles = I / kBN;
   if ((st = launch(MX_STORE, false, p, mtiles * p.n_tiles, s, "MXFP8 down dgrad", true)) != MOE_OK) return st;
 
-  // dZ, dprob
+  // dZ (never stored in bf16: quantised by rows for dx and along the tokens for dW1 in
+  // the same kernel) and dprob (partials per 64 columns, then summed in order)
   if (R > 0) {
-    hipLaunchKernelGGL(mx_dswiglu_kernel, dim3((unsigned)R), dim3(256), 0, s, dh, z, prob, dz, dprob, I);
-    if ((st = check_launch("MXFP8 dSwiGLU")) != MOE_OK) return st;
+    const int64_t items = (kc / 128) * (I / 64);
+    const int64_t grid = items < (int64_t)num_cus() * 8 ? items : (int64_t)num_cus() * 8;
+    hipLaunchKernelGGL(mx_dswiglu_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, dh, z, prob, offsets, E,
+                       (int)R, I, kc, dzq, dzs, ws + L.dzc, ws + L.dzcs, part);
+    if ((st = check_launch("MXFP8 dSwiGLU + dZ quantisation")) != MOE_OK) return st;
+    hipLaunchKernelGGL(mx_dprob_sum_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, part, (int)R, I / 64,
+                       dprob);
+    if ((st = check_launch("MXFP8 dprob")) != MOE_OK) return st;
   }
 
   // dx = dZ W1_e
-  if ((st = launch_mxfp8_quantize_step_major(dz, R, 2 * I, dzq, dzs, s)) != MOE_OK) return st;
   if (!packed)
     for (int e = 0; e < E; ++e)
       if ((st = launch_mxfp8_colwise(w_gate_up[e], 2 * I, H, 1, nullptr, 32, 2 * I, ws + L.w1c + e * w1n,
@@ -1719,9 +1894,6 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
   w.I = I;
   w.n_tiles = I / kBN;
   if ((st = launch_wgrad(w, (int64_t)E * (H / kBM) * w.n_tiles, s, "MXFP8 down wgrad")) != MOE_OK) return st;
-  if ((st = launch_mxfp8_colwise(dz, R, 2 * I, E, offsets, 256, kc, ws + L.dzc, ws + L.dzcs, nullptr, s, true)) !=
-      MOE_OK)
-    return st;
   if ((st = launch_mxfp8_colwise(x, R, H, E, offsets, 256, kc, ws + L.xc, ws + L.xcs, nullptr, s, true)) != MOE_OK)
     return st;
   w.q = ws + L.dzc;

@@ -356,10 +356,11 @@ moe_status moe_grouped_mlp_fwd(const moe_mlp_desc* desc, int64_t R, const void* 
  * at the expert's first row, zero-padded). dH and dZ are rounded to bf16 before use, as
  * the recipe returns a low-precision GEMM's result to bf16. Needs H % 256 == 0,
  * I % 256 == 0, E <= 128. Its workspace (moe_workspace_size(MOE_OP_MLP_BWD, ...))
- * holds every quantised operand, the column-wise weight copies and dH, dZ in bf16:
- * about R (3.1 H + 11.2 I) + 3.1 E H I bytes (the last term only for bf16 weights),
- * plus (2H + 3I) bytes per padding row of the token-axis layouts (3.0 GB at R = 8192,
- * H = 4096, I = 14336, E = 8, bf16 weights). Calls sharing a workspace must not overlap.
+ * holds every quantised operand, the column-wise weight copies and dH in bf16 (dZ is
+ * only stored quantised): about R (3.1 H + 7.3 I) + 3.1 E H I bytes (the last term only
+ * for bf16 weights), plus (2H + 3I) bytes per padding row of the token-axis layouts
+ * (2.5 GB at R = 8192, H = 4096, I = 14336, E = 8, bf16 weights). Calls sharing a
+ * workspace must not overlap.
  * compute = FP8 (act BF16; wt BF16, or FP8 for weights packed by
  * fp8_tensor_pack_weight_bwd, laid out as for MXFP8 above): every GEMM operand is one
  * tensor quantised by the rule of fp8_tensor_quantize (Challenge 2's FP8: one factor per
