@@ -121,6 +121,7 @@ __global__ __launch_bounds__(256) void fp8t_finalize_kernel(uint32_t* words, int
 struct Fp8TTab {
   const uint16_t* in[kTab];
   uint8_t* out[kTab];
+  uint8_t* rows[kTab];  // NULL, or the row-major codes [R, C] of the same tensor, written too
 };
 
 template <bool kRecip>
@@ -141,6 +142,7 @@ __global__ __launch_bounds__(256) void fp8t_transpose_kernel(const Fp8TTab tab, 
   const int ncb = C / 64;
   const uint16_t* __restrict__ x = tab.in[blockIdx.y];
   uint8_t* __restrict__ codes = tab.out[blockIdx.y];
+  uint8_t* __restrict__ row_codes = tab.rows[blockIdx.y];
   const float s = scale_of_amax(words[blockIdx.y]);
   const float rcp = __fdiv_rn(1.f, s);
   const bool fast = s >= 1.17549435e-38f && rcp >= 1.17549435e-38f && rcp <= 3.40282347e+38f;
@@ -201,10 +203,29 @@ __global__ __launch_bounds__(256) void fp8t_transpose_kernel(const Fp8TTab tab, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      float f[8];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        tile[r + 32 * i][c8 + 2 * h] = bf16_to_f32(w[h] & 0xFFFFu);
-        tile[r + 32 * i][c8 + 2 * h + 1] = bf16_to_f32(w[h] >> 16);
+        f[2 * h] = bf16_to_f32(w[h] & 0xFFFFu);
+        f[2 * h + 1] = bf16_to_f32(w[h] >> 16);
+        tile[r + 32 * i][c8 + 2 * h] = f[2 * h];
+        tile[r + 32 * i][c8 + 2 * h + 1] = f[2 * h + 1];
+      }
+      const int64_t row = (int64_t)s_off[e] + 128 * j + r + 32 * i;
+      if (row_codes && row < s_off[e + 1]) {  // the same codes, row-major: 8 bytes of the row
+        uint32_t c0, c1;
+        if (fast) {
+          c0 = e4m3_pack4(quotient<true>(f[0], s, rcp), quotient<true>(f[1], s, rcp), quotient<true>(f[2], s, rcp),
+                          quotient<true>(f[3], s, rcp));
+          c1 = e4m3_pack4(quotient<true>(f[4], s, rcp), quotient<true>(f[5], s, rcp), quotient<true>(f[6], s, rcp),
+                          quotient<true>(f[7], s, rcp));
+        } else {
+          c0 = e4m3_pack4(quotient<false>(f[0], s, rcp), quotient<false>(f[1], s, rcp),
+                          quotient<false>(f[2], s, rcp), quotient<false>(f[3], s, rcp));
+          c1 = e4m3_pack4(quotient<false>(f[4], s, rcp), quotient<false>(f[5], s, rcp),
+                          quotient<false>(f[6], s, rcp), quotient<false>(f[7], s, rcp));
+        }
+        *reinterpret_cast<uint2*>(row_codes + row * C + cb * 64 + c8) = make_uint2(c0, c1);
       }
     }
     __syncthreads();
@@ -237,7 +258,7 @@ unsigned grid_x(int64_t n8, int ntensors) {
 
 moe_status fp8t_transpose(const void* const* in, uint8_t* const* out, int ntensors, int64_t R, int C, int E,
                           const int32_t* offsets, int pad, int64_t kcap, const float* words, int32_t* kofs,
-                          hipStream_t s) {
+                          hipStream_t s, uint8_t* const* rows_out) {
   if (ntensors <= 0 || C == 0) return MOE_OK;
   // room for every expert's rows padded to a multiple of pad (one expert: R rounded up)
   const int64_t room = offsets ? R + (int64_t)E * (pad - 1) : (R + pad - 1) / pad * pad;
@@ -248,6 +269,7 @@ moe_status fp8t_transpose(const void* const* in, uint8_t* const* out, int ntenso
   for (int t = 0; t < ntensors; ++t) {
     tab.in[t] = (const uint16_t*)in[t];
     tab.out[t] = out[t];
+    tab.rows[t] = rows_out ? rows_out[t] : nullptr;
   }
   const int64_t items = (kcap / 32 + 3 * E) / 4 * (C / 64) + E * (C / 64);
   int64_t grid = (int64_t)num_cus() * 16 / ntensors;

@@ -1538,15 +1538,19 @@ namespace {
 
 // dH [R, I] and z = [G, U] [R, 2I] (bf16) -> dZ = [dG, dU] (bf16), dprob[r] = sum dH * A
 // with A = silu(G) U (the probability's gradient), dA = dH p. One workgroup per row.
+// amax (optional): raised to the float bits of max |dZ| over the stored bf16 values (an
+// integer max of non-negative float bits, as fp8t_amax computes it).
 __global__ __launch_bounds__(256) void mx_dswiglu_kernel(const bf16_t* __restrict__ dh, const bf16_t* __restrict__ z,
                                                          const float* __restrict__ prob, bf16_t* __restrict__ dz,
-                                                         float* __restrict__ dprob, int I) {
+                                                         float* __restrict__ dprob, int I,
+                                                         uint32_t* __restrict__ amax) {
   const int64_t r = blockIdx.x;
   const float p = prob[r];
   const bf16_t* dhr = dh + r * I;
   const bf16_t* zr = z + r * 2 * I;
   bf16_t* dzr = dz + r * 2 * I;
   float acc = 0.f;
+  uint32_t mbits = 0;  // max bf16 magnitude bits of the stored dZ
   for (int c = threadIdx.x * 8; c < I; c += 256 * 8) {
     const uint4 dv = *reinterpret_cast<const uint4*>(dhr + c);
     const uint4 gv = *reinterpret_cast<const uint4*>(zr + c);
@@ -1569,6 +1573,7 @@ __global__ __launch_bounds__(256) void mx_dswiglu_kernel(const bf16_t* __restric
       }
       og[j] = pack_bf16x2(dg2[0], dg2[1]);
       ou[j] = pack_bf16x2(du2[0], du2[1]);
+      mbits = max(mbits, max(max(og[j] & 0x7FFFu, (og[j] >> 16) & 0x7FFFu), max(ou[j] & 0x7FFFu, (ou[j] >> 16) & 0x7FFFu)));
     }
     *reinterpret_cast<uint4*>(dzr + c) = make_uint4(og[0], og[1], og[2], og[3]);
     *reinterpret_cast<uint4*>(dzr + I + c) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
@@ -1576,9 +1581,21 @@ __global__ __launch_bounds__(256) void mx_dswiglu_kernel(const bf16_t* __restric
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   __shared__ float red[4];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __shared__ uint32_t mred[4];
+  if (amax) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, off));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = acc;
+    mred[threadIdx.x >> 6] = mbits;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) dprob[r] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (threadIdx.x == 0) {
+    dprob[r] = (red[0] + red[1]) + (red[2] + red[3]);
+    const uint32_t m = max(max(mred[0], mred[1]), max(mred[2], mred[3]));
+    if (amax && m) atomicMax(amax, m << 16);
+  }
 }
 
 // dSwiGLU fused with both MXFP8 quantisations of dZ, so dZ never goes through HBM in
@@ -2048,17 +2065,18 @@ moe_status backward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const bf16_t* d
   p.n_tiles = I / kBN;
   if ((st = launch(MX_STORE, true, p, mtiles * p.n_tiles, s, "FP8 down dgrad")) != MOE_OK) return st;
 
-  // dZ, dprob; then dZ's factor and codes
+  // dZ, dprob and dZ's amax in one pass; then its row-major and token-axis codes from
+  // one read of dZ
   if (R > 0) {
-    hipLaunchKernelGGL(mx_dswiglu_kernel, dim3((unsigned)R), dim3(256), 0, s, dh, z, prob, dz, dprob, I);
+    hipLaunchKernelGGL(mx_dswiglu_kernel, dim3((unsigned)R), dim3(256), 0, s, dh, z, prob, dz, dprob, I,
+                       reinterpret_cast<uint32_t*>(w_dz));
     if ((st = check_launch("FP8 dSwiGLU")) != MOE_OK) return st;
   }
   const void* t_dz[1] = {dz};
   uint8_t* o_dzq[1] = {dzq};
   uint8_t* o_dzc[1] = {dzc};
-  if ((st = fp8t_amax(t_dz, 1, R * 2 * I, w_dz, s)) != MOE_OK) return st;
-  if ((st = fp8t_quantize(t_dz, o_dzq, 1, R * 2 * I, w_dz, s)) != MOE_OK) return st;
-  if ((st = fp8t_transpose(t_dz, o_dzc, 1, R, 2 * I, E, offsets, 256, kc, w_dz, nullptr, s)) != MOE_OK) return st;
+  if ((st = fp8t_transpose(t_dz, o_dzc, 1, R, 2 * I, E, offsets, 256, kc, w_dz, nullptr, s, o_dzq)) != MOE_OK)
+    return st;
   if ((st = fp8t_finalize(w_dz, 1, s)) != MOE_OK) return st;
 
   // dx = dZ W1_e

@@ -58,9 +58,10 @@ moe_status fp8t_finalize(float* words, int n, hipStream_t s);
 // factor of words[t] (amax bits, between fp8t_amax and fp8t_finalize) for tensor t of
 // in/out. kofs (E + 1 padded offsets) is written when not NULL. C % 64 == 0, pad and
 // kcap multiples of 32, kcap >= R + E * (pad - 1) (without offsets: R rounded up to a
-// multiple of pad), at most 64 tensors.
+// multiple of pad), at most 64 tensors. rows_out (optional): per tensor, also the
+// row-major codes [R, C] (those of fp8t_quantize), from the same loads.
 moe_status fp8t_transpose(const void* const* in, uint8_t* const* out, int ntensors, int64_t R, int C, int E,
                           const int32_t* offsets, int pad, int64_t kcap, const float* words, int32_t* kofs,
-                          hipStream_t s);
+                          hipStream_t s, uint8_t* const* rows_out = nullptr);
 
 }  // namespace moe
