@@ -2022,8 +2022,7 @@ moe_status backward_fp8_tensor(const moe_mlp_desc& d, int64_t R, const bf16_t* d
   uint8_t* o_dyc[1] = {dyc};
   uint8_t* o_hc[1] = {hc};
   uint8_t* o_xc[1] = {xc};
-  if ((st = fp8t_quantize(t_dy, o_dyq, 1, R * H, w_dy, s)) != MOE_OK) return st;
-  if ((st = fp8t_transpose(t_dy, o_dyc, 1, R, H, E, offsets, 256, kc, w_dy, kofs, s)) != MOE_OK) return st;
+  if ((st = fp8t_transpose(t_dy, o_dyc, 1, R, H, E, offsets, 256, kc, w_dy, kofs, s, o_dyq)) != MOE_OK) return st;
   if ((st = fp8t_transpose(t_h, o_hc, 1, R, I, E, offsets, 256, kc, w_h, nullptr, s)) != MOE_OK) return st;
   if ((st = fp8t_transpose(t_x, o_xc, 1, R, H, E, offsets, 256, kc, w_x, nullptr, s)) != MOE_OK) return st;
   // W2_e [H][I] -> [I][H] (K = H for dH); W1_e [2I][H] -> [H][2I] (K = 2I for dx)
