@@ -33,16 +33,18 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// round to nearest even; inputs are finite
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// Round to nearest even, by gfx950's v_cvt_pk_bf16_f32 (one instruction per pair; it
+// agrees with the integer rounding u + 0x7FFF + ((u >> 16) & 1) on every finite and
+// infinite float32, denormals included, and returns a quiet NaN for a NaN).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xFFFFu; }
 
 // E8M0 exponent for a block maximum: the smallest s with amax <= 448 * 2^s, in
 // [-127, 127]; amax == 0 gives -127. Exact integer work on the float32 bits.

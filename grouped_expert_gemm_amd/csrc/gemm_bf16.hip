@@ -534,7 +534,7 @@ void grouped_gemm_kernel(const Params prm) {
               for (int v = 0; v < 4; ++v) {
                 const float dh = acc[sn][sm][i4 * 4 + v];
                 const float gg = gv[v], u = uv[v];
-                const float sg = 1.f / (1.f + __expf(-gg));
+                const float sg = sigmoid_f(gg);
                 const float sl = gg * sg;
                 dpart[sm] += dh * sl * u;
                 const float da = dh * pr[sm];

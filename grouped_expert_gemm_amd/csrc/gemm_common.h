@@ -55,6 +55,23 @@ __device__ __forceinline__ void wait_vm() {
 // ones the next step reads (wait_vm_le), and the others must stay in flight, which
 // __syncthreads() would not allow (its fence drains every outstanding copy). The
 // signal fences keep the compiler from moving memory accesses across the barrier.
+// Entry i of a table the kernel only reads (expert offsets), through the constant
+// address space: with a wavefront-uniform index it becomes a scalar load, waited for
+// with lgkmcnt. A vector load's vmcnt wait would also wait for every store and copy
+// this wavefront still has in flight (vmcnt retires them in issue order).
+__device__ __forceinline__ int load_const(const int32_t* table, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)table)[i];
+}
+
+// This lane's number within its wavefront, computed (two mbcnt instructions) rather than
+// taken from a register held since the kernel's start: epilogues that run once per tile
+// call it so the value need not stay live, or be spilled, across the K loop.
+__device__ __forceinline__ int lane_number() {
+  unsigned base = 0;
+  asm volatile("" : "+v"(base));  // opaque: the count is not hoisted out of the tile loop
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, base));
+}
+
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -87,7 +104,12 @@ __device__ __forceinline__ void wait_vm_le(int n) {  // n: a multiple of 4 in [0
   }
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g), the quotient by the hardware reciprocal (v_rcp_f32, 1 ulp)
+// instead of the correctly rounded division's ten-instruction sequence: in the SwiGLU
+// epilogues, which run 128 of these per lane and tile, the division was most of the time.
+__device__ __forceinline__ float silu_f(float g) { return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
+// sigmoid(g) = 1 / (1 + e^-g), the same way
+__device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 
 
 }  // namespace gemm

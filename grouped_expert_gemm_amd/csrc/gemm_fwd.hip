@@ -78,7 +78,7 @@ void grouped_gemm_fwd_kernel(const Params prm) {
   };
   int e_w = 0;
   int ob = 0;
-  int oe = clamp_off(prm.offsets[1], 0);
+  int oe = clamp_off(load_const(prm.offsets, 1), 0);
   int ts_w = 0;
   int nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
   const int nk = prm.K / kWBK;
@@ -91,7 +91,7 @@ void grouped_gemm_fwd_kernel(const Params prm) {
   {
     int prev = 0;
     for (int x = 0; x < E; ++x) {
-      const int en = clamp_off(prm.offsets[x + 1], prev);
+      const int en = clamp_off(load_const(prm.offsets, x + 1), prev);
       total += ((en - prev + kBM - 1) / kBM) * prm.n_tiles;
       prev = en;
     }
@@ -146,7 +146,7 @@ void grouped_gemm_fwd_kernel(const Params prm) {
       ++e_w;
       ob = oe;
       if (e_w < E) {
-        oe = clamp_off(prm.offsets[e_w + 1], ob);
+        oe = clamp_off(load_const(prm.offsets, e_w + 1), ob);
         nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
       }
     }
@@ -363,7 +363,7 @@ void grouped_gemm_fwd_kernel(const Params prm) {
       // barrier reads back and stores 4 whole rows per instruction, 16 bytes per lane,
       // skipping rows past the expert. Column block b of the accumulators is sub-tiles
       // 2b and 2b + 1: chunk wn * 8 + (sn & 1) * 4 + i4 of the block.
-      int ln = lane, wv = __builtin_amdgcn_readfirstlane(wave);
+      int ln = lane_number(), wv = wave_u;
       asm volatile("" : "+v"(ln));  // keep the lane offsets inside the epilogue
       const int em = wv >> 1, en = wv & 1, e32 = ln & 31, ehi = ln >> 5;
       const int valid = min(row_end - tile_row, kBM);
@@ -413,10 +413,17 @@ void grouped_gemm_fwd_kernel(const Params prm) {
         lds_barrier();  // read out before the next tile's copies land
       } else {  // EPI_SWIGLU: gate columns in block 0, the matching up columns in block 1
         uint8_t* harr = em ? sH1 : sH0;
+        // the lane's four routing weights, loaded together: one memory round trip, not four
+        float pw[4];
 #pragma unroll
         for (int sm = 0; sm < 4; ++sm) {
           const int mr = tile_row + em * 128 + sm * 32 + e32;
-          const float p = prm.prob[mr < row_end ? mr : row_end - 1];  // rows past the expert: not stored
+          pw[sm] = prm.prob[mr < row_end ? mr : row_end - 1];  // rows past the expert: not stored
+        }
+        asm volatile("" : "+v"(pw[0]), "+v"(pw[1]), "+v"(pw[2]), "+v"(pw[3]));
+#pragma unroll
+        for (int sm = 0; sm < 4; ++sm) {
+          const float p = pw[sm];
 #pragma unroll
           for (int sq = 0; sq < 2; ++sq)
 #pragma unroll

@@ -503,11 +503,11 @@ void grouped_gemm_fp8t_kernel(const Params prm) {
   } else {
     int prev = 0;
     for (int x = 0; x < E; ++x) {
-      const int en = clamp_off(prm.offsets[x + 1], prev);
+      const int en = clamp_off(load_const(prm.offsets, x + 1), prev);
       total += ((en - prev + kBM - 1) / kBM) * prm.n_tiles;
       prev = en;
     }
-    oe = clamp_off(prm.offsets[1], 0);
+    oe = clamp_off(load_const(prm.offsets, 1), 0);
     nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
   }
   // row stride of both code arrays: K, or the padded token axis for the weight gradients
@@ -554,7 +554,7 @@ void grouped_gemm_fp8t_kernel(const Params prm) {
         ++e_w;
         ob = oe;
         if (e_w < E) {
-          oe = clamp_off(prm.offsets[e_w + 1], ob);
+          oe = clamp_off(load_const(prm.offsets, e_w + 1), ob);
           nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
         }
       }
@@ -888,11 +888,11 @@ void grouped_gemm_mxw_kernel(const Params prm) {
   } else {
     int prev = 0;
     for (int x = 0; x < E; ++x) {
-      const int en = clamp_off(prm.offsets[x + 1], prev);
+      const int en = clamp_off(load_const(prm.offsets, x + 1), prev);
       total += ((en - prev + kBM - 1) / kBM) * prm.n_tiles;
       prev = en;
     }
-    oe = clamp_off(prm.offsets[1], 0);
+    oe = clamp_off(load_const(prm.offsets, 1), 0);
     nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
   }
   // row stride of both code arrays: K for K-contiguous operands, the padded token axis
@@ -938,7 +938,7 @@ void grouped_gemm_mxw_kernel(const Params prm) {
         ++e_w;
         ob = oe;
         if (e_w < E) {
-          oe = clamp_off(prm.offsets[e_w + 1], ob);
+          oe = clamp_off(load_const(prm.offsets, e_w + 1), ob);
           nt_w = ((oe - ob + kBM - 1) / kBM) * prm.n_tiles;
         }
       }
