@@ -458,71 +458,86 @@ void grouped_gemm_kernel(const Params prm) {
 
     // ---------------- epilogue ----------------
     if constexpr (EP == EPI_DSWIGLU) {
-      // dSwiGLU through LDS (free after the K loop), in two passes over 128 of the 256
-      // columns: z's gate and up halves are copied in with coalesced 16-byte copies
-      // (rows of 256 bytes, chunk c of row r at c ^ (r & 15); gate rows r in sP[r / 64],
-      // up rows in sQ[r / 64]; rows past the expert read as zeros), every lane turns its
-      // accumulators and z values into dG, dU in place, and the tile leaves with
-      // coalesced 16-byte stores. In the accumulator layout each load would touch 32
-      // rows x 16 bytes, one latency-bound round trip per 8 bytes a lane needs.
+      // dSwiGLU through LDS (free after the K loop) in four passes. Pass (a, b) takes the
+      // accumulator rows of sub-tiles sm = 2a, 2a + 1 of every wavefront and the tile's
+      // columns 128b .. 128b + 127, so all four wavefronts work in every pass. Its z values
+      // (gate and up halves) are copied in with coalesced 16-byte copies while the pass
+      // before it computes: passes alternate between two LDS buffers of 64 KiB (the sP
+      // and the sQ arrays), and each wait counts the copies and stores issued after the
+      // pass's own copies (16 per lane each), so the copies' latency and the previous
+      // pass's store drain overlap the arithmetic. In a buffer, rows are 256 bytes (128
+      // columns), chunk c of row r at c ^ (r & 15); pass row rho = 64 (sm & 1) + 32 wm +
+      // (lane & 31) sits in array rho >> 6 (gate: [0], [1]; up: [2], [3]), which every LDS
+      // access names at compile time. Rows past the expert read as zeros and are not
+      // stored: the buffer descriptors' record counts end at the expert's last row. In
+      // the accumulator layout each load would touch 32 rows x 16 bytes, one
+      // latency-bound round trip per 8 bytes a lane needs.
       // The lane offsets below do not change from tile to tile; computed from opaque
       // copies of the lane and wavefront numbers they stay inside the epilogue instead
       // of being hoisted out of the tile loop and held across the K loop, which has no
       // registers to spare.
-      int ln = lane, wv = __builtin_amdgcn_readfirstlane(wave);
+      int ln = lane_number(), wv = wave_u;
       asm volatile("" : "+v"(ln));
       asm volatile("" : "+s"(wv));
       const int em = wv >> 1, en = wv & 1, e32 = ln & 31, ehi = ln >> 5;
       const int tile_row = row_beg + mt * kBM;
       const int valid_rows = min(row_end - tile_row, kBM);
       const int64_t I = prm.I;
-      const int64_t zld = 2 * I;  // z and dz row length
+      const int64_t zld = 2 * I;  // z row length
       float pr[4], dpart[4];
 #pragma unroll
       for (int sm = 0; sm < 4; ++sm) {
         const int64_t mg = (int64_t)tile_row + em * 128 + sm * 32 + e32;
-        pr[sm] = mg < row_end ? prm.prob[mg] : 0.f;
+        pr[sm] = prm.prob[mg < row_end ? mg : row_end - 1];  // rows past the expert: not stored
         dpart[sm] = 0.f;
       }
-      auto arrP = [&](int a) -> uint8_t* { return a == 0 ? sP0 : a == 1 ? sP1 : a == 2 ? sP2 : sP3; };
-      auto arrQ = [&](int a) -> uint8_t* { return a == 0 ? sQ0 : a == 1 ? sQ1 : a == 2 ? sQ2 : sQ3; };
       const char* zt = reinterpret_cast<const char*>(prm.zin + (int64_t)tile_row * zld);
       char* dzt = reinterpret_cast<char*>(prm.c + (int64_t)tile_row * prm.c_ld);
-      static_for<2>([&](auto CC) {
-        constexpr int c = decltype(CC)::value;
-        const int64_t col0 = (int64_t)nt * kBN + c * 128;  // first z column of the pass (gate half)
-        // copy in: wavefront w takes rows [64w, 64w + 64) of both halves, 4 rows per copy
+      const uint32_t zrow = (uint32_t)(zld * 2), crow = (uint32_t)(prm.c_ld * 2);  // row bytes
+      // copy / store instruction i (0..7) of wavefront w covers pass rows 16i + 4w .. +3,
+      // lane l row 16i + 4w + (l >> 4) and physical chunk l & 15; that pass row is tile row
+      // 128 ((i & 3) >> 1) + 32 (2a + (i >> 2)) + 16 (i & 1) + 4w + (l >> 4)
+      const int lrow = ln >> 4, pch = ln & 15;
+      const int lch = pch ^ ((4 * wv + lrow) & 15);  // logical chunk at physical chunk pch
+      auto tile_row_of = [&](int a, int i) -> uint32_t {
+        return (uint32_t)(128 * ((i & 3) >> 1) + 32 * (2 * a + (i >> 2)) + 16 * (i & 1) + 4 * wv);
+      };
+      auto buf = [&](auto B, int k) -> uint8_t* {  // array k of buffer B
+        if constexpr (B.value == 0) return k == 0 ? sP0 : k == 1 ? sP1 : k == 2 ? sP2 : sP3;
+        else return k == 0 ? sQ0 : k == 1 ? sQ1 : k == 2 ? sQ2 : sQ3;
+      };
+      auto copy_in = [&](auto A, auto BB, auto B) {
+        constexpr int a = decltype(A)::value, b = decltype(BB)::value;
+        const int64_t col0 = (int64_t)nt * kBN + b * 128;  // first z column of the pass (gate half)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int64_t colb = (col0 + half * I) * 2;
           const int64_t nrec = (int64_t)valid_rows * zld * 2 - colb;
           const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
               (void*)(zt + colb), (short)0, (int)(uint32_t)(nrec < 0 ? 0 : nrec), kBufferFlags);
-          uint8_t* dst = (half ? arrQ(wv) : arrP(wv));
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int rr = wv * 64 + 4 * i + (ln >> 4);
-            const int g = (ln & 15) ^ (rr & 15);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 1024), 16,
-                                                     (uint32_t)((ln >> 4) * zld * 2 + g * 16),
-                                                     (int)((uint32_t)(wv * 64 + 4 * i) * (uint32_t)(zld * 2)), 0, 0);
+          for (int i = 0; i < 8; ++i) {
+            uint8_t* dst = buf(B, 2 * half + (i >> 2)) + (16 * (i & 3) + 4 * wv) * 256;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, (uint32_t)(lrow * zrow + lch * 16),
+                                                     (int)(tile_row_of(a, i) * zrow), 0, 0);
           }
         }
-        wait_vm<0>();
-        lds_barrier();
-        // dG, dU in place
+      };
+      auto compute = [&](auto A, auto BB, auto B) {  // dG, dU in place
+        constexpr int a = decltype(A)::value, b = decltype(BB)::value;
+        const int rr = em * 32 + e32;  // row within the arrays
 #pragma unroll
-        for (int sm = 0; sm < 4; ++sm) {
-          const int r = em * 128 + sm * 32 + e32;
-          uint8_t* gP = arrP(r >> 6) + (r & 63) * 256;
-          uint8_t* gQ = arrQ(r >> 6) + (r & 63) * 256;
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int sm = 2 * a + s2;
+          uint8_t* gP = buf(B, s2) + rr * 256;
+          uint8_t* gQ = buf(B, 2 + s2) + rr * 256;
 #pragma unroll
           for (int sq = 0; sq < 2; ++sq) {
-            const int sn = 2 * c + sq;
+            const int sn = 2 * b + sq;
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
               const int ch = en * 8 + sq * 4 + i4;
-              const uint32_t off = (uint32_t)(((ch ^ (r & 15)) << 4) + ehi * 8);
+              const uint32_t off = (uint32_t)(((ch ^ (rr & 15)) << 4) + ehi * 8);
               const uint2 gz = *reinterpret_cast<const uint2*>(gP + off);
               const uint2 uz = *reinterpret_cast<const uint2*>(gQ + off);
               const float gv[4] = {bf16_to_f32(gz.x & 0xFFFFu), bf16_to_f32(gz.x >> 16),
@@ -532,14 +547,16 @@ void grouped_gemm_kernel(const Params prm) {
               float dg[4], du[4];
 #pragma unroll
               for (int v = 0; v < 4; ++v) {
+                // dG = p dh u sg (1 + g (1 - sg)) = p (dh u) (sg + sl - sl sg), dU = p dh sl,
+                // dprob += dh u sl, with sl = g sg
                 const float dh = acc[sn][sm][i4 * 4 + v];
                 const float gg = gv[v], u = uv[v];
                 const float sg = sigmoid_f(gg);
                 const float sl = gg * sg;
-                dpart[sm] += dh * sl * u;
-                const float da = dh * pr[sm];
-                dg[v] = da * u * sg * (1.f + gg * (1.f - sg));
-                du[v] = da * sl;
+                const float q = dh * u;
+                dpart[sm] = __builtin_fmaf(q, sl, dpart[sm]);
+                dg[v] = (pr[sm] * q) * __builtin_fmaf(-sl, sg, sg + sl);
+                du[v] = (pr[sm] * dh) * sl;
               }
               *reinterpret_cast<uint2*>(gP + off) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
               *reinterpret_cast<uint2*>(gQ + off) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
@@ -549,23 +566,46 @@ void grouped_gemm_kernel(const Params prm) {
           // with every product it needs kept live
           asm volatile("" : "+v"(dpart[sm]));
         }
-        lds_barrier();
-        // store out: wavefront w stores rows [64w, 64w + 64) of both halves
+      };
+      auto store_out = [&](auto A, auto BB, auto B) {
+        constexpr int a = decltype(A)::value, b = decltype(BB)::value;
+        const int64_t col0 = (int64_t)nt * kBN + b * 128;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const uint8_t* src = half ? arrQ(wv) : arrP(wv);
           const int64_t colb = (col0 + half * I) * 2;
+          const int64_t nrec = (int64_t)valid_rows * crow - colb;
+          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(dzt + colb), (short)0, (int)(uint32_t)(nrec < 0 ? 0 : nrec), kBufferFlags);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int rl = 4 * i + (ln >> 4);  // row within the wavefront's 64
-            const int rr = wv * 64 + rl;
-            const int pch = ln & 15;
-            const uint4 v = *reinterpret_cast<const uint4*>(src + rl * 256 + ((pch ^ (rr & 15)) << 4));
-            if (rr < valid_rows)
-              *reinterpret_cast<uint4*>(dzt + (int64_t)rr * prm.c_ld * 2 + colb + pch * 16) = v;
+          for (int i = 0; i < 8; ++i) {
+            const uint8_t* src = buf(B, 2 * half + (i >> 2)) + (16 * (i & 3) + 4 * wv + lrow) * 256;
+            const v4u32 v = *reinterpret_cast<const v4u32*>(src + (lch << 4));  // logical chunk pch
+            __builtin_amdgcn_raw_buffer_store_b128(v, rs, (uint32_t)(lrow * crow + pch * 16),
+                                                   (int)(tile_row_of(a, i) * crow), 0);
           }
         }
-        lds_barrier();  // every read of the staging area is done before it is reused
+      };
+      using C0 = std::integral_constant<int, 0>;
+      using C1 = std::integral_constant<int, 1>;
+      copy_in(C0{}, C0{}, C0{});
+      static_for<4>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        using A = std::integral_constant<int, j / 2>;
+        using BB = std::integral_constant<int, j % 2>;
+        using B = std::integral_constant<int, j % 2>;  // buffer
+        if constexpr (j < 3) {
+          copy_in(std::integral_constant<int, (j + 1) / 2>{}, std::integral_constant<int, (j + 1) % 2>{},
+                  std::integral_constant<int, (j + 1) % 2>{});
+        }
+        // this pass's copies landed: after them only the previous pass's stores and the
+        // next pass's copies were issued
+        if constexpr (j == 0 || j == 3) wait_vm<16>();
+        else wait_vm<32>();
+        lds_barrier();
+        compute(A{}, BB{}, B{});
+        lds_barrier();
+        store_out(A{}, BB{}, B{});
+        lds_barrier();  // every read of the buffer is done before it is refilled
       });
       // dprob partial of each row: the 64 columns of this wavefront, both lanes of the row
 #pragma unroll

@@ -1565,7 +1565,7 @@ __global__ __launch_bounds__(256) void mx_dswiglu_kernel(const bf16_t* __restric
         const float d = bf16_to_f32(h ? dw[j] >> 16 : dw[j] & 0xFFFFu);
         const float G = bf16_to_f32(h ? gw[j] >> 16 : gw[j] & 0xFFFFu);
         const float U = bf16_to_f32(h ? uw[j] >> 16 : uw[j] & 0xFFFFu);
-        const float sg = 1.f / (1.f + expf(-G));
+        const float sg = sigmoid_f(G);
         acc += d * (G * sg * U);
         const float dA = d * p;
         dg2[h] = dA * U * sg * (1.f + G * (1.f - sg));
@@ -1679,7 +1679,7 @@ __global__ __launch_bounds__(256) void mx_dswiglu_quant_kernel(
           const float d = bf16_to_f32(hh ? dw[w] >> 16 : dw[w] & 0xFFFFu);
           const float G = bf16_to_f32(hh ? gw[w] >> 16 : gw[w] & 0xFFFFu);
           const float U = bf16_to_f32(hh ? uw[w] >> 16 : uw[w] & 0xFFFFu);
-          const float sg = 1.f / (1.f + expf(-G));
+          const float sg = sigmoid_f(G);
           acc += d * (G * sg * U);
           const float dA = d * p;
           dg2[hh] = dA * U * sg * (1.f + G * (1.f - sg));
