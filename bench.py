@@ -30,7 +30,9 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector, published
 METRIC = "grouped-MLP TFLOP/s fwd and fwd+bwd, Mixtral-8x7B layer; % MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "grouped_expert_gemm_amd", "csrc", "gemm_fwd.hip")
+# the gate_up kernel's source: its file and the headers whose device code it inlines
+KERNEL_SRCS = [os.path.join(ROOT, "grouped_expert_gemm_amd", "csrc", f)
+               for f in ("gemm_fwd.hip", "gemm_common.h", "common.h", "gemm_bf16.h")]
 
 
 def log(*a):
@@ -439,12 +441,20 @@ def cpu_model():
     return "unknown"
 
 
+def kernel_sha256():
+    """sha256 over the gate_up kernel's source files, in a fixed order."""
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def traffic_record():
     """HBM bytes per gate_up launch from the committed rocprofv3 counter runs, or None
     if they were taken on a different version of the kernel source."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        sha = kernel_sha256()
         if rec.get("kernel_sha256") != sha:
             return None
         return rec.get("bytes_per_launch")

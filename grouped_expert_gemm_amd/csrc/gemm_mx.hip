@@ -1609,7 +1609,7 @@ __global__ __launch_bounds__(256) void mx_dswiglu_kernel(const bf16_t* __restric
 // (i < 4), columns 8 (t % 8) .. + 8 of dH, G and U (16-byte loads); 4 threads own a
 // 32-value row block; the token-axis blocks go through an LDS tile as in the
 // column-wise quantiser. dprob: one partial per row and item, part[r * I / 64 + cb],
-// summed in order by mx_dprob_sum_kernel.
+// summed in a fixed order by mx_dprob_sum_kernel.
 __global__ __launch_bounds__(256) void mx_dswiglu_quant_kernel(
     const bf16_t* __restrict__ dh, const bf16_t* __restrict__ z, const float* __restrict__ prob,
     const int32_t* __restrict__ offsets, int E, int R, int I, int64_t kcap, uint8_t* __restrict__ dzq,
@@ -1656,18 +1656,26 @@ __global__ __launch_bounds__(256) void mx_dswiglu_quant_kernel(
     const int row_end = s_off[e + 1];
     const int64_t k0 = (int64_t)s_kofs[e] + 128 * j;
     uint32_t g_bits[4][4], u_bits[4][4];  // dG, dU of this thread's 4 rows x 8 columns, bf16 pairs
+    // all four rows' loads first, so they are in flight together (an item has at least
+    // one live row: rows past the expert read the expert's last row and count as zeros)
+    uint4 dvs[4], gvs[4], uvs[4];
+    float ps[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int row = s_off[e] + 128 * j + r + 32 * i;
+      row = row < row_end ? row : row_end - 1;
+      dvs[i] = *reinterpret_cast<const uint4*>(dh + (int64_t)row * I + cb * 64 + c8);
+      gvs[i] = *reinterpret_cast<const uint4*>(z + (int64_t)row * I2 + cb * 64 + c8);
+      uvs[i] = *reinterpret_cast<const uint4*>(z + (int64_t)row * I2 + I + cb * 64 + c8);
+      ps[i] = prob[row];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = s_off[e] + 128 * j + r + 32 * i;
       const bool live = row < row_end;
-      uint4 dv = make_uint4(0, 0, 0, 0), gv = dv, uv = dv;
-      float p = 0.f;
-      if (live) {
-        dv = *reinterpret_cast<const uint4*>(dh + (int64_t)row * I + cb * 64 + c8);
-        gv = *reinterpret_cast<const uint4*>(z + (int64_t)row * I2 + cb * 64 + c8);
-        uv = *reinterpret_cast<const uint4*>(z + (int64_t)row * I2 + I + cb * 64 + c8);
-        p = prob[row];
-      }
+      const uint4 zero = make_uint4(0, 0, 0, 0);
+      const uint4 dv = live ? dvs[i] : zero, gv = live ? gvs[i] : zero, uv = live ? uvs[i] : zero;
+      const float p = live ? ps[i] : 0.f;
       const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w},
                      uw[4] = {uv.x, uv.y, uv.z, uv.w};
       float acc = 0.f;
@@ -1755,15 +1763,19 @@ __global__ __launch_bounds__(256) void mx_dswiglu_quant_kernel(
   }
 }
 
-// dprob[r] = the sum of the row's I / 64 partials, in column-block order
+// dprob[r] = the sum of the row's I / 64 partials: one wavefront per row, lane l adds
+// blocks l, l + 64, ... in order, then a butterfly over the lanes (a fixed order, so
+// the result does not change from run to run)
 __global__ __launch_bounds__(256) void mx_dprob_sum_kernel(const float* __restrict__ part, int R, int ncb,
                                                            float* __restrict__ dprob) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (r >= R) return;
   const float* pr = part + (int64_t)r * ncb;
   float acc = 0.f;
-  for (int c = 0; c < ncb; ++c) acc += pr[c];
-  dprob[r] = acc;
+  for (int c = lane; c < ncb; c += 64) acc += pr[c];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) dprob[r] = acc;
 }
 
 // token-axis layout: every expert padded to whole 256-row K steps of the GEMM
@@ -1868,7 +1880,7 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
     hipLaunchKernelGGL(mx_dswiglu_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, dh, z, prob, offsets, E,
                        (int)R, I, kc, dzq, dzs, ws + L.dzc, ws + L.dzcs, part);
     if ((st = check_launch("MXFP8 dSwiGLU + dZ quantisation")) != MOE_OK) return st;
-    hipLaunchKernelGGL(mx_dprob_sum_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, part, (int)R, I / 64,
+    hipLaunchKernelGGL(mx_dprob_sum_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, part, (int)R, I / 64,
                        dprob);
     if ((st = check_launch("MXFP8 dprob")) != MOE_OK) return st;
   }

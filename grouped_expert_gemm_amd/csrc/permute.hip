@@ -15,6 +15,8 @@
 //             it to its k destination rows, plus the maps and the row weights.
 #include <mutex>
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -164,7 +166,20 @@ __device__ __forceinline__ void copy_row_to_k(const uint8_t* __restrict__ src, i
                                               int k, int lane) {
   const int64_t n = bytes / (int64_t)sizeof(U);
   const U* s = reinterpret_cast<const U*>(src);
-  for (int64_t c = lane; c < n; c += 64) {
+  int64_t c = lane;
+  // four chunks' loads in flight together, then their stores
+  for (; c + 192 < n; c += 256) {
+    U v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = s[c + 64 * q];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j < k && rows[j] >= 0) reinterpret_cast<U*>(dst_base + (int64_t)rows[j] * bytes)[c + 64 * q] = v[q];
+      }
+  }
+  for (; c < n; c += 64) {
     U v = s[c];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
@@ -225,7 +240,9 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
 // combine: out[t] = sum_j w[t, j] * y_perm[row_id_map[t*k + j]], float32 sums in slot order
 // ---------------------------------------------------------------------------
 
-template <bool kBF16, int VEC>
+// KM: an upper bound of k (2, 4, 8 or 16) that sizes the per-slot arrays of the
+// batched path, so the registers it holds scale with k; 0: any k, one slot at a time
+template <bool kBF16, int VEC, int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y, const int32_t* __restrict__ rmap,
                                                       const float* __restrict__ w, int64_t T, int H, int k,
                                                       void* __restrict__ out) {
@@ -234,6 +251,88 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   if (t >= T) return;
   const int64_t R = T * k;
   const int nchunk = H / VEC;
+  if constexpr (KM > 0) {
+    // the token's row ids and weights once; per chunk all k loads in flight together
+    // (a dropped slot reads row 0 and is left out of the sum), then the sums in slot order
+    int32_t rr[KM];
+    float ww[KM];
+    bool ok[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const int32_t r = j < k ? rmap[t * k + j] : -1;
+      ok[j] = r >= 0 && r < R;
+      rr[j] = ok[j] ? r : 0;
+      ww[j] = (j < k && w) ? w[t * k + j] : 1.f;
+    }
+    for (int c = lane; c < nchunk; c += 64) {
+      float acc[VEC];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+      if constexpr (kBF16 && VEC == 8) {
+        uint4 q[KM];
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          if (j < k)
+            q[j] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(y) + (int64_t)rr[j] * H +
+                                                   (int64_t)c * VEC);
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+          if (j < k && ok[j]) {
+            const uint32_t u[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              acc[2 * v] += ww[j] * bf16_to_f32(u[v] & 0xFFFFu);
+              acc[2 * v + 1] += ww[j] * bf16_to_f32(u[v] >> 16);
+            }
+          }
+        }
+        uint4 o;
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * H + (int64_t)c * VEC) = o;
+      } else if constexpr (!kBF16 && VEC == 4) {
+        float4 q[KM];
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          if (j < k)
+            q[j] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(y) + (int64_t)rr[j] * H +
+                                                    (int64_t)c * VEC);
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+          if (j < k && ok[j]) {
+            acc[0] += ww[j] * q[j].x;
+            acc[1] += ww[j] * q[j].y;
+            acc[2] += ww[j] * q[j].z;
+            acc[3] += ww[j] * q[j].w;
+          }
+        }
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + t * H + (int64_t)c * VEC) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
+      } else {
+        float vals[KM][VEC];
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          if (j < k)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v)
+              vals[j][v] = kBF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(y)[(int64_t)rr[j] * H + (int64_t)c * VEC + v])
+                                 : reinterpret_cast<const float*>(y)[(int64_t)rr[j] * H + (int64_t)c * VEC + v];
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          if (j < k && ok[j])
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] += ww[j] * vals[j][v];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          if constexpr (kBF16) reinterpret_cast<uint16_t*>(out)[t * H + (int64_t)c * VEC + v] = (uint16_t)f32_to_bf16(acc[v]);
+          else reinterpret_cast<float*>(out)[t * H + (int64_t)c * VEC + v] = acc[v];
+        }
+      }
+    }
+    return;
+  }
   for (int c = lane; c < nchunk; c += 64) {
     float acc[VEC];
 #pragma unroll
@@ -369,19 +468,31 @@ extern "C" moe_status moe_unpermute_combine(const void* y_perm, moe_dtype dt, co
   if (!y_perm || !row_id_map || !out) return fail(MOE_ERR_INVALID_ARG, "moe_unpermute_combine: NULL pointer");
   const hipStream_t s = as_stream(stream);
   const int64_t blocks = (T + 3) / 4;
+  // the batched kernel sized for the smallest of 4, 8, 16 slots that holds k (at k <= 2
+  // the one-slot-at-a-time loop measured as fast or faster: Mixtral's top-2 combine)
+  auto launch = [&](auto BF, auto V) {
+    constexpr bool bf = decltype(BF)::value;
+    constexpr int vec = decltype(V)::value;
+    const dim3 g((unsigned)blocks), b(256);
+    if (k <= 2) hipLaunchKernelGGL((combine_kernel<bf, vec, 0>), g, b, 0, s, y_perm, row_id_map, weights, T, H, k, out);
+    else if (k <= 4) hipLaunchKernelGGL((combine_kernel<bf, vec, 4>), g, b, 0, s, y_perm, row_id_map, weights, T, H, k, out);
+    else if (k <= 8) hipLaunchKernelGGL((combine_kernel<bf, vec, 8>), g, b, 0, s, y_perm, row_id_map, weights, T, H, k, out);
+    else if (k <= 16) hipLaunchKernelGGL((combine_kernel<bf, vec, 16>), g, b, 0, s, y_perm, row_id_map, weights, T, H, k, out);
+    else hipLaunchKernelGGL((combine_kernel<bf, vec, 0>), g, b, 0, s, y_perm, row_id_map, weights, T, H, k, out);
+  };
+  using BF16 = std::true_type;
+  using F32 = std::false_type;
   if (dt == MOE_BF16) {
     if (H % 8 == 0 && aligned(y_perm, 16) && aligned(out, 16))
-      hipLaunchKernelGGL((combine_kernel<true, 8>), dim3((unsigned)blocks), dim3(256), 0, s, y_perm, row_id_map,
-                         weights, T, H, k, out);
+      launch(BF16{}, std::integral_constant<int, 8>{});
     else
-      hipLaunchKernelGGL((combine_kernel<true, 1>), dim3((unsigned)blocks), dim3(256), 0, s, y_perm, row_id_map,
+      hipLaunchKernelGGL((combine_kernel<true, 1, 0>), dim3((unsigned)blocks), dim3(256), 0, s, y_perm, row_id_map,
                          weights, T, H, k, out);
   } else {
     if (H % 4 == 0 && aligned(y_perm, 16) && aligned(out, 16))
-      hipLaunchKernelGGL((combine_kernel<false, 4>), dim3((unsigned)blocks), dim3(256), 0, s, y_perm, row_id_map,
-                         weights, T, H, k, out);
+      launch(F32{}, std::integral_constant<int, 4>{});
     else
-      hipLaunchKernelGGL((combine_kernel<false, 1>), dim3((unsigned)blocks), dim3(256), 0, s, y_perm, row_id_map,
+      hipLaunchKernelGGL((combine_kernel<false, 1, 0>), dim3((unsigned)blocks), dim3(256), 0, s, y_perm, row_id_map,
                          weights, T, H, k, out);
   }
   return check_launch("moe_unpermute_combine");

@@ -23,7 +23,11 @@ def test_traffic_record_follows_the_kernel_source(tmp_path, monkeypatch):
     assert rec["read_bytes"] + rec["write_bytes"] == rec["bytes_per_launch"]
     # reported only while the kernel source hashes to the one the counters were taken on
     assert bench.traffic_record() in (None, rec["bytes_per_launch"])
-    other = tmp_path / "gemm_fwd.hip"
-    other.write_text("// another version of the kernel\n")
-    monkeypatch.setattr(bench, "KERNEL_SRC", str(other))
-    assert bench.traffic_record() is None
+    # a change to the kernel file or to a header whose device code it inlines
+    for i, name in enumerate(("gemm_fwd.hip", "common.h")):
+        other = tmp_path / name
+        other.write_text("// another version\n")
+        srcs = list(bench.KERNEL_SRCS)
+        srcs[[os.path.basename(f) for f in srcs].index(name)] = str(other)
+        monkeypatch.setattr(bench, "KERNEL_SRCS", srcs)
+        assert bench.traffic_record() is None
