@@ -227,6 +227,43 @@ def test_combine(moe):
                                rtol=1e-6, atol=1e-6)
 
 
+def test_combine_rounds_to_nearest_bf16(moe):
+    """The kernels round a float32 result to bf16 once, to nearest with ties to even (the
+    packed conversion of gfx950). With k = 1 and weights of at most 16 significant bits,
+    every product w * y of a bf16 value y is exact in float32, so the combine's output is
+    that one rounding of the exact product: it must equal the oracle's bf16 rounding bit
+    for bit. Half of the rows hold powers of two, which the weights 1 + 2^-8, 1 + 3 2^-8,
+    1 + 5 2^-8 put exactly half-way between two bf16 values, and 1 + 2^-8 -+ 2^-16 just
+    below and above; the other rows are normal draws times 16-bit weights."""
+    rng = np.random.default_rng(11)
+    T, H = 1024, 256
+    y = rng.standard_normal((T, H)).astype(np.float32)
+    pw = rng.choice([-1.0, 1.0], size=(T // 2, H)) * np.exp2(rng.integers(-20, 21, size=(T // 2, H)))
+    y[: T // 2] = pw
+    yb = f32_to_bf16_bits(y)
+    w_ties = [1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 5 * 2.0 ** -8, 1 + 2.0 ** -8 - 2.0 ** -16,
+              1 + 2.0 ** -8 + 2.0 ** -16, 1 - 2.0 ** -9, 0.75 + 2.0 ** -10, -(1 + 2.0 ** -8)]
+    w = np.empty(T)
+    for t in range(T):
+        if t < T // 2:
+            w[t] = w_ties[t % len(w_ties)]
+        else:  # 16 significant bits
+            w[t] = rng.integers(1 << 15, 1 << 16) * 2.0 ** (-15 + int(rng.integers(-3, 4))) * rng.choice([-1.0, 1.0])
+    assert np.all(w.astype(np.float32).astype(np.float64) == w)
+    exact = bf16_bits_to_f32(yb).astype(np.float64) * w[:, None]
+    ref = oracle.bf16_round(exact)
+    # how many products sit exactly half-way between two bf16 values (the case that
+    # tells round-half-even from other rules)
+    e = np.floor(np.log2(np.abs(exact)))
+    frac = np.abs(exact) / np.exp2(e - 7)
+    ties = int(np.sum(frac - np.floor(frac) == 0.5))
+    assert ties > 1000, ties
+    rmap = torch.arange(T, dtype=torch.int32).cuda()
+    print(f"combine rounding T={T} H={H} ties={ties}", flush=True)
+    out = moe.moe_unpermute_combine(dev_bf16(yb), rmap, T, 1, dev_f32(w.astype(np.float32)))
+    assert np.array_equal(bf16_bits(out), f32_to_bf16_bits(ref.astype(np.float32)))
+
+
 # ---------------------------------------------------------------------------
 # MXFP8 quantisation: bit-exact
 # ---------------------------------------------------------------------------
