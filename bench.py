@@ -99,11 +99,47 @@ class Layer:
                                       device=dev)
         self.mx = mx or fp8
         self.fs1 = self.fs2 = None
-        if fp8:  # the whole grouped MLP forward in per-tensor FP8 (one call), saving z and h when backward
+        self.wq_step = None
+        if (mx or fp8) and backward:
+            # the forward's and the backward's weight layouts from one two-layout call per
+            # weight tensor: once outside the timed steps (prequant), or at the start of
+            # every step from the bf16 master weights (as a step after an optimizer update)
+            quant = moe.fp8_tensor_quantize_weights if fp8 else moe.mxfp8_quantize_weights
+            self.q1, qs1, self.pk1 = quant(self.w1)
+            self.q2, qs2, self.pk2 = quant(self.w2)
+            self.qs1, self.qs2 = qs1, qs2
+            t = lambda ts: _lib.ptr_table([x.data_ptr() for x in ts])
+            self.t1, self._k1 = t([self.q1[e] for e in range(E)])
+            self.t2, self._k2 = t([self.q2[e] for e in range(E)])
+            if fp8:
+                self.fs1, self._k5 = _lib.ptr_table([qs1.data_ptr() + 4 * e for e in range(E)])
+                self.fs2, self._k6 = _lib.ptr_table([qs2.data_ptr() + 4 * e for e in range(E)])
+            else:
+                self.fs1, self._k5 = t([qs1[e] for e in range(E)])
+                self.fs2, self._k6 = t([qs2[e] for e in range(E)])
+            self.b1, self._k7 = t([self.pk1[e] for e in range(E)])
+            self.b2, self._k8 = t([self.pk2[e] for e in range(E)])
+            if not prequant:
+                w1t, k9 = t([self.w1[e] for e in range(E)])
+                w2t, k10 = t([self.w2[e] for e in range(E)])
+                self._k9 = (k9, k10)
+                if fp8:
+                    self.wq_step = [(self.L.fp8_tensor_quantize_weights, E, w1t, 2 * I, H, self.t1, qs1, self.b1),
+                                    (self.L.fp8_tensor_quantize_weights, E, w2t, H, I, self.t2, qs2, self.b2)]
+                else:
+                    self.wq_step = [(self.L.mxfp8_quantize_weights, E, w1t, 2 * I, H, self.t1, self.fs1, self.b1),
+                                    (self.L.mxfp8_quantize_weights, E, w2t, H, I, self.t2, self.fs2, self.b2)]
+            comp = _lib.MOE_FP8 if fp8 else _lib.MOE_MXFP8
+            self.desc = _lib.MlpDesc(E, H, I, comp, _lib.MOE_BF16, comp, 1)
+            self.ws_bwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_BWD, self.desc, R), dtype=torch.uint8,
+                                      device=dev)
+            self.desc_fwd = _lib.MlpDesc(E, H, I, comp, _lib.MOE_BF16, comp, 1)
+            self.ws_fwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_FWD, self.desc_fwd, R), dtype=torch.uint8,
+                                      device=dev)
+        elif fp8:  # the grouped MLP forward in per-tensor FP8 (one call)
             wt = _lib.MOE_BF16
             if prequant:
                 # weights quantised once, outside the timed steps: codes and one factor per expert
-                # weight for the forward, transposed packs for the backward
                 wt = _lib.MOE_FP8
                 q1 = [moe.fp8_tensor_quantize(self.w1[e]) for e in range(E)]
                 q2 = [moe.fp8_tensor_quantize(self.w2[e]) for e in range(E)]
@@ -112,22 +148,13 @@ class Layer:
                 self.t2, self._k2 = _lib.ptr_table([c.data_ptr() for c, _ in q2])
                 self.fs1, self._k5 = _lib.ptr_table([f.data_ptr() for _, f in q1])
                 self.fs2, self._k6 = _lib.ptr_table([f.data_ptr() for _, f in q2])
-                if backward:
-                    self.pk1 = [moe.fp8_tensor_pack_weight_bwd(self.w1[e]) for e in range(E)]
-                    self.pk2 = [moe.fp8_tensor_pack_weight_bwd(self.w2[e]) for e in range(E)]
-                    self.b1, self._k7 = _lib.ptr_table([t.data_ptr() for t in self.pk1])
-                    self.b2, self._k8 = _lib.ptr_table([t.data_ptr() for t in self.pk2])
-                    self.desc = _lib.MlpDesc(E, H, I, _lib.MOE_FP8, _lib.MOE_BF16, _lib.MOE_FP8, 1)
-                    self.ws_bwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_BWD, self.desc, R),
-                                              dtype=torch.uint8, device=dev)
-            self.desc_fwd = _lib.MlpDesc(E, H, I, _lib.MOE_FP8, _lib.MOE_BF16, wt, int(backward))
+            self.desc_fwd = _lib.MlpDesc(E, H, I, _lib.MOE_FP8, _lib.MOE_BF16, wt, 0)
             self.ws_fwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_FWD, self.desc_fwd, R), dtype=torch.uint8,
                                       device=dev)
-        elif mx:  # the whole grouped MLP forward in MXFP8 (one call), saving z and h when backward
+        elif mx:  # the grouped MLP forward in MXFP8 (one call)
             wt = _lib.MOE_BF16
             if prequant:
-                # weights quantised once, outside the timed steps (as a training loop would once
-                # per optimizer step): row-wise for the forward, packed for the backward
+                # weights quantised once, outside the timed steps, by rows (the forward's layout)
                 wt = _lib.MOE_MXFP8
                 self.q1, self.qs1 = moe.mxfp8_quantize(self.w1)
                 self.q2, self.qs2 = moe.mxfp8_quantize(self.w2)
@@ -135,18 +162,10 @@ class Layer:
                 self.t2, self._k2 = _lib.ptr_table([self.q2[e].data_ptr() for e in range(E)])
                 self.fs1, self._k5 = _lib.ptr_table([self.qs1[e].data_ptr() for e in range(E)])
                 self.fs2, self._k6 = _lib.ptr_table([self.qs2[e].data_ptr() for e in range(E)])
-                if backward:
-                    self.pk1 = [moe.mxfp8_pack_weight_bwd(self.w1[e]) for e in range(E)]
-                    self.pk2 = [moe.mxfp8_pack_weight_bwd(self.w2[e]) for e in range(E)]
-                    self.b1, self._k7 = _lib.ptr_table([t.data_ptr() for t in self.pk1])
-                    self.b2, self._k8 = _lib.ptr_table([t.data_ptr() for t in self.pk2])
-                    self.desc = _lib.MlpDesc(E, H, I, _lib.MOE_MXFP8, _lib.MOE_BF16, _lib.MOE_MXFP8, 1)
-                    self.ws_bwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_BWD, self.desc, R),
-                                              dtype=torch.uint8, device=dev)
-            self.desc_fwd = _lib.MlpDesc(E, H, I, _lib.MOE_MXFP8, _lib.MOE_BF16, wt, int(backward))
+            self.desc_fwd = _lib.MlpDesc(E, H, I, _lib.MOE_MXFP8, _lib.MOE_BF16, wt, 0)
             self.ws_fwd = torch.empty(moe.workspace_size(_lib.MOE_OP_MLP_FWD, self.desc_fwd, R), dtype=torch.uint8,
                                       device=dev)
-        if not ((mx or fp8) and prequant and backward):
+        if not ((mx or fp8) and backward):
             self.b1, self.b2 = self.t1, self.t2
         self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self.ev = []
@@ -161,6 +180,10 @@ class Layer:
         c("permute", L.moe_permute(p(self.x), None, BF, T, H, E, k, p(self.idx), p(self.prob), 0, p(self.x_perm),
                                    None, p(self.prob_perm), p(self.split), p(self.offsets), p(self.rmap),
                                    p(self.src), p(self.ws_perm), self.ws_perm.numel(), s))
+        if self.wq_step:  # bf16 master weights -> both layouts, every step
+            for fn, n, src, rows, cols, codes, scales, packed in self.wq_step:
+                sc = ctypes.c_void_p(scales.data_ptr()) if hasattr(scales, "data_ptr") else scales
+                c("weight quantisation", fn(n, src, rows, cols, codes, sc, packed, s))
         if self.mx:
             c("mlp fwd", L.moe_grouped_mlp_fwd(ctypes.byref(self.desc_fwd), R, p(self.x_perm), None, self.t1, self.t2,
                                                self.fs1, self.fs2, p(self.offsets), p(self.prob_perm), p(self.y),
@@ -505,9 +528,10 @@ _FWD_BWD_INPUTS = None
 def fwd_bwd_measure(steps, warmup, mx=False, prequant=False, fp8=False):
     """The whole layer forward + backward step (route ... combine, dOut gather, grouped
     MLP backward, dx combine, dprob gather) at the Mixtral fwd+bwd shape; mx: the grouped
-    MLP forward and backward in MXFP8 (the forward saving z and h in bf16); prequant: the
-    MXFP8 weights quantised once outside the timed steps; fp8: forward and backward in
-    per-tensor FP8 (bf16 master weights quantised inside every step)."""
+    MLP forward and backward in MXFP8 (the forward saving z and h in bf16); fp8: the same
+    in per-tensor FP8. The low-precision steps start from the bf16 master weights: one
+    call per weight tensor writes the forward's and the backward's layouts at the start
+    of every step, or once outside the timed steps with prequant."""
     global _FWD_BWD_INPUTS
     from moe_inputs import WORKLOADS, make_inputs
 
@@ -529,11 +553,14 @@ def fwd_bwd_measure(steps, warmup, mx=False, prequant=False, fp8=False):
         rec.update(compute="fp8", pct_of_fp8_peak=round(100 * vb / peak, 2),
                    weights=("FP8, quantised once outside the step (codes and factors for the forward, transposed "
                             "packs for the backward)" if prequant else
-                            "bf16 master weights, quantised inside every step (one factor per tensor)"))
+                            "bf16 master weights, quantised inside every step (one factor per tensor; "
+                            "fp8_tensor_quantize_weights: the forward's codes and the backward's packs together)"))
     elif mx:
         rec.update(compute="mxfp8", pct_of_fp8_peak=round(100 * vb / peak, 2),
                    weights=("MXFP8, quantised once outside the step (row-wise for the forward, packed for the "
-                            "backward)" if prequant else "bf16 master weights, quantised inside every step"))
+                            "backward)" if prequant else
+                            "bf16 master weights, quantised inside every step (mxfp8_quantize_weights: row-wise "
+                            "for the forward and packed for the backward from one read)"))
     else:
         rec["pct_of_bf16_peak"] = round(100 * vb / peak, 2)
     return rec

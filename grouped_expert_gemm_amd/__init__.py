@@ -22,7 +22,7 @@ from ._lib import MOE_BF16, MOE_F32, MOE_FP8, MOE_MXFP8, MlpDesc, MoeError, chec
 __all__ = [
     "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd", "moe_permute", "moe_unpermute_combine", "mxfp8_quantize",
     "fp8_tensor_quantize", "mxfp8_quantize_colwise", "fp8_tensor_quantize_colwise", "mxfp8_pack_weight_bwd",
-    "fp8_tensor_pack_weight_bwd",
+    "fp8_tensor_pack_weight_bwd", "mxfp8_quantize_weights", "fp8_tensor_quantize_weights",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu", "gemm_workspace",
     "workspace_size", "MoeError", "lib",
     "MOE_F32", "MOE_BF16", "MOE_MXFP8", "MOE_FP8",
@@ -249,6 +249,48 @@ def mxfp8_pack_weight_bwd(w: torch.Tensor) -> torch.Tensor:
     packed = torch.empty(rows * cols + rows * cols // 32, dtype=torch.uint8, device=w.device)
     check("mxfp8_pack_weight_bwd", lib().mxfp8_pack_weight_bwd(_p(w), rows, cols, _p(packed), _stream(w.device)))
     return packed
+
+
+def _weight_stack(w, fn):
+    _need_cuda(w)
+    if w.dtype != torch.bfloat16 or w.dim() != 3:
+        raise ValueError(f"{fn} takes bfloat16 weights [n, rows, cols]")
+    return w.contiguous()
+
+
+def mxfp8_quantize_weights(w: torch.Tensor):
+    """bf16 weights [n, rows, cols] -> (E4M3 codes uint8 [n, rows, cols], E8M0 scales uint8
+    [n, rows, cols/32], packed uint8 [n, rows * cols * 33 / 32]): for each weight the
+    outputs of mxfp8_quantize and of mxfp8_pack_weight_bwd, from one read of it."""
+    w = _weight_stack(w, "mxfp8_quantize_weights")
+    n, rows, cols = w.shape
+    codes = torch.empty((n, rows, cols), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, rows, cols // 32), dtype=torch.uint8, device=w.device)
+    packed = torch.empty((n, rows * cols + rows * cols // 32), dtype=torch.uint8, device=w.device)
+    tw, kw = _lib.ptr_table([w[i].data_ptr() for i in range(n)])
+    tc, kc = _lib.ptr_table([codes[i].data_ptr() for i in range(n)])
+    ts, ks = _lib.ptr_table([scales[i].data_ptr() for i in range(n)])
+    tp, kp = _lib.ptr_table([packed[i].data_ptr() for i in range(n)])
+    check("mxfp8_quantize_weights", lib().mxfp8_quantize_weights(n, tw, rows, cols, tc, ts, tp, _stream(w.device)))
+    return codes, scales, packed
+
+
+def fp8_tensor_quantize_weights(w: torch.Tensor):
+    """bf16 weights [n, rows, cols] -> (E4M3 codes uint8 [n, rows, cols], float32 scales [n],
+    packed uint8 [n, rows * cols + 16]): for each weight the outputs of
+    fp8_tensor_quantize and of fp8_tensor_pack_weight_bwd (in the first rows * cols + 4
+    bytes of its packed row), from one pass for the maxima and one for the codes."""
+    w = _weight_stack(w, "fp8_tensor_quantize_weights")
+    n, rows, cols = w.shape
+    codes = torch.empty((n, rows, cols), dtype=torch.uint8, device=w.device)
+    scale = torch.empty(n, dtype=torch.float32, device=w.device)
+    packed = torch.empty((n, rows * cols + 16), dtype=torch.uint8, device=w.device)
+    tw, kw = _lib.ptr_table([w[i].data_ptr() for i in range(n)])
+    tc, kc = _lib.ptr_table([codes[i].data_ptr() for i in range(n)])
+    tp, kp = _lib.ptr_table([packed[i].data_ptr() for i in range(n)])
+    check("fp8_tensor_quantize_weights", lib().fp8_tensor_quantize_weights(n, tw, rows, cols, tc, _p(scale), tp,
+                                                                           _stream(w.device)))
+    return codes, scale, packed
 
 
 def _experts(w):

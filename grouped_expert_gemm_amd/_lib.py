@@ -21,7 +21,7 @@ EXPORTS = (
     "moe_route_topk", "moe_router_logits", "moe_route_topk_bwd", "moe_router_bwd",
     "moe_permute", "moe_permute_noalloc", "moe_unpermute_combine", "mxfp8_quantize", "fp8_tensor_quantize", "mxfp8_quantize_colwise",
     "fp8_tensor_quantize_colwise", "fp8_tensor_pack_weight_bwd",
-    "mxfp8_pack_weight_bwd",
+    "mxfp8_pack_weight_bwd", "mxfp8_quantize_weights", "fp8_tensor_quantize_weights",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "moe_grouped_linear", "moe_grouped_gate_up_swiglu",
     "moe_workspace_size",
     "moe_status_str", "moe_last_error",
@@ -68,6 +68,8 @@ def _declare(lib):
         "fp8_tensor_quantize_colwise": [vp, i64, i64, c_int, vp, c_int, i64, vp, vp, vp, vp],
         "fp8_tensor_pack_weight_bwd": [vp, i64, i64, vp, vp],
         "mxfp8_pack_weight_bwd": [vp, i64, i64, vp, vp],
+        "mxfp8_quantize_weights": [c_int, PP, i64, i64, PP, PP, PP, vp],
+        "fp8_tensor_quantize_weights": [c_int, PP, i64, i64, PP, vp, PP, vp],
         "moe_grouped_mlp_fwd": [ctypes.POINTER(MlpDesc), i64, vp, vp, PP, PP, PP, PP, vp, vp, vp, vp, vp, vp,
                                 sz, vp],
         "moe_grouped_mlp_bwd": [ctypes.POINTER(MlpDesc), i64, vp, vp, vp, vp, vp, PP, PP, vp, vp, PP, PP, vp,

@@ -66,13 +66,15 @@ __device__ __forceinline__ float scale_of_amax(uint32_t bits) {
 // q1 + residual * r (one fma) is the correctly rounded quotient (Markstein's theorem;
 // it needs s and r in the normal range, checked per tensor). Quotients below the
 // float32 normal range, where the theorem does not hold, are far below E4M3's smallest
-// step and get code 0 either way.
+// step and get code 0 either way. The residual step alone would turn x = -0 into +0
+// (q1 = -0, residual +0, and +0 + -0 rounds to +0); the quotient has x's sign (s > 0),
+// so x's sign is put back, which keeps the sign of zero as the division does.
 template <bool kRecip>
 __device__ __forceinline__ float quotient(float x, float s, float r) {
   if constexpr (!kRecip) return __fdiv_rn(x, s);
   const float q1 = x * r;
   const float e = __builtin_fmaf(-q1, s, x);
-  return __builtin_fmaf(e, r, q1);
+  return __builtin_copysignf(__builtin_fmaf(e, r, q1), x);
 }
 
 template <bool kRecip>
@@ -246,6 +248,15 @@ __global__ __launch_bounds__(256) void fp8t_transpose_kernel(const Fp8TTab tab, 
   }
 }
 
+// copies of the finished scales into per-tensor destinations (the weight packs' factors)
+struct Fp8Dst {
+  float* p[kTab];
+};
+__global__ __launch_bounds__(64) void fp8t_scatter_kernel(const float* __restrict__ words, const Fp8Dst dst, int n) {
+  const int i = threadIdx.x;
+  if (i < n) *dst.p[i] = words[i];
+}
+
 unsigned grid_x(int64_t n8, int ntensors) {
   int64_t want = (n8 + 255) / 256;
   int64_t cap = (int64_t)num_cus() * 8 / ntensors;
@@ -401,4 +412,46 @@ extern "C" moe_status fp8_tensor_pack_weight_bwd(const void* w_bf16, int64_t row
   if ((st = fp8t_transpose(in, out, 1, rows, (int)cols, 1, nullptr, 32, rows, factor, nullptr, s)) != MOE_OK)
     return st;
   return fp8t_finalize(factor, 1, s);
+}
+
+extern "C" moe_status fp8_tensor_quantize_weights(int n, const void* const* w_bf16, int64_t rows, int64_t cols,
+                                                  uint8_t* const* e4m3, float* scale, void* const* packed,
+                                                  void* stream) {
+  if (n < 1 || n > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_quantize_weights: n out of [1, 256]");
+  if (rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_quantize_weights: negative size");
+  if (rows % 32 != 0 || cols % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "fp8_tensor_quantize_weights: needs rows % 32 == 0 and cols % 64 == 0");
+  if (rows > 0x7FFFFFFF || rows * cols > 0x7FFFFFFFLL)
+    return fail(MOE_ERR_UNSUPPORTED, "fp8_tensor_quantize_weights: weight exceeds 2^31 elements");
+  if (!scale) return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_quantize_weights: NULL scale");
+  if (!aligned(scale, 4)) return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_quantize_weights: scale not 4-byte aligned");
+  if (!w_bf16 || !e4m3 || !packed) return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_quantize_weights: NULL table");
+  const bool empty = rows == 0 || cols == 0;
+  for (int i = 0; i < n; ++i) {
+    if (!packed[i] || (!empty && (!w_bf16[i] || !e4m3[i])))
+      return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_quantize_weights: NULL pointer");
+    if (!aligned(packed[i], 16) || (!empty && (!aligned(w_bf16[i], 16) || !aligned(e4m3[i], 8))))
+      return fail(MOE_ERR_INVALID_ARG, "fp8_tensor_quantize_weights: w and packed must be 16-byte, e4m3 8-byte aligned");
+  }
+  const hipStream_t s = as_stream(stream);
+  moe_status st;
+  if ((st = fp8t_zero(scale, n, s)) != MOE_OK) return st;
+  if ((st = fp8t_amax(w_bf16, n, rows * cols, scale, s)) != MOE_OK) return st;
+  for (int t0 = 0; !empty && t0 < n; t0 += kTab) {
+    const int cnt = n - t0 < kTab ? n - t0 : kTab;
+    uint8_t* codes[kTab];
+    for (int t = 0; t < cnt; ++t) codes[t] = reinterpret_cast<uint8_t*>(packed[t0 + t]);
+    if ((st = fp8t_transpose(w_bf16 + t0, codes, cnt, rows, (int)cols, 1, nullptr, 32, rows, scale + t0, nullptr, s,
+                             e4m3 + t0)) != MOE_OK)
+      return st;
+  }
+  if ((st = fp8t_finalize(scale, n, s)) != MOE_OK) return st;
+  for (int t0 = 0; t0 < n; t0 += kTab) {  // each pack carries its factor after the codes
+    const int cnt = n - t0 < kTab ? n - t0 : kTab;
+    Fp8Dst dst = {};
+    for (int t = 0; t < cnt; ++t) dst.p[t] = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(packed[t0 + t]) + rows * cols);
+    hipLaunchKernelGGL(fp8t_scatter_kernel, dim3(1), dim3(64), 0, s, scale + t0, dst, cnt);
+    if ((st = check_launch("fp8_tensor_quantize_weights: factors")) != MOE_OK) return st;
+  }
+  return MOE_OK;
 }

@@ -1847,13 +1847,24 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
   auto w1_codes = [&](int e) -> const uint8_t* {
     return packed ? reinterpret_cast<const uint8_t*>(w_gate_up[e]) : ws + L.w1c + e * w1n;
   };
-  // dH = dY W2_e (the data gradients run on the wide-step kernel: step-major scales)
-  if ((st = launch_mxfp8_quantize_step_major(dy, R, H, dyq, dys, s)) != MOE_OK) return st;
-  if (!packed)
-    for (int e = 0; e < E; ++e)
-      if ((st = launch_mxfp8_colwise(w_down[e], H, I, 1, nullptr, 32, H, ws + L.w2c + e * w2n,
-                                     ws + L.w2s + e * w2n / 32, nullptr, s, true)) != MOE_OK)
-        return st;
+  // dH = dY W2_e (the data gradients run on the wide-step kernel: step-major scales).
+  // dY is quantised by rows (for dH) and along the tokens (for dW2) from one read.
+  if ((st = launch_mxfp8_colwise(dy, R, H, E, offsets, 256, kc, ws + L.dyc, ws + L.dycs, kofs, s, true, dyq, dys,
+                                 R)) != MOE_OK)
+    return st;
+  const void* wsrc[kMaxE];
+  uint8_t* wcodes[kMaxE];
+  uint8_t* wscales[kMaxE];
+  if (!packed) {
+    for (int e = 0; e < E; ++e) {
+      wsrc[e] = w_down[e];
+      wcodes[e] = ws + L.w2c + e * w2n;
+      wscales[e] = ws + L.w2s + e * w2n / 32;
+    }
+    if ((st = launch_mxfp8_colwise_multi(E, wsrc, H, I, 1, nullptr, 32, H, wcodes, wscales, nullptr, s, true)) !=
+        MOE_OK)
+      return st;
+  }
   MxParams p;
   std::memset(&p, 0, sizeof(p));
   for (int e = 0; e < E; ++e) {
@@ -1886,11 +1897,16 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
   }
 
   // dx = dZ W1_e
-  if (!packed)
-    for (int e = 0; e < E; ++e)
-      if ((st = launch_mxfp8_colwise(w_gate_up[e], 2 * I, H, 1, nullptr, 32, 2 * I, ws + L.w1c + e * w1n,
-                                     ws + L.w1s + e * w1n / 32, nullptr, s, true)) != MOE_OK)
-        return st;
+  if (!packed) {
+    for (int e = 0; e < E; ++e) {
+      wsrc[e] = w_gate_up[e];
+      wcodes[e] = ws + L.w1c + e * w1n;
+      wscales[e] = ws + L.w1s + e * w1n / 32;
+    }
+    if ((st = launch_mxfp8_colwise_multi(E, wsrc, 2 * I, H, 1, nullptr, 32, 2 * I, wcodes, wscales, nullptr, s,
+                                         true)) != MOE_OK)
+      return st;
+  }
   for (int e = 0; e < E; ++e) {
     p.tab[e] = w1_codes(e);
     p.tab_s[e] = packed ? w1_codes(e) + w1n : ws + L.w1s + e * w1n / 32;
@@ -1904,8 +1920,6 @@ moe_status backward(const moe_mlp_desc& d, int64_t R, const bf16_t* dy, const bf
   if ((st = launch(MX_STORE, false, p, mtiles * p.n_tiles, s, "MXFP8 gate_up dgrad", true)) != MOE_OK) return st;
 
   // weight gradients on the token-axis layouts (wide-step kernel: step-major scales)
-  if ((st = launch_mxfp8_colwise(dy, R, H, E, offsets, 256, kc, ws + L.dyc, ws + L.dycs, kofs, s, true)) != MOE_OK)
-    return st;
   if ((st = launch_mxfp8_colwise(h, R, I, E, offsets, 256, kc, ws + L.hc, ws + L.hcs, nullptr, s, true)) != MOE_OK)
     return st;
   MxWgradParams w;

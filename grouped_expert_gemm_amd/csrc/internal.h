@@ -39,9 +39,21 @@ moe_status launch_mx_scales_step_major(const uint8_t* const* src, uint8_t* const
 // row total, 16-byte aligned x and codes.
 // step_major: scales in the step-major layout of launch_mxfp8_quantize_step_major over
 // the transposed [C, kcap] output (word (k / 128) * C + c; kcap % 128 == 0).
+// rcodes (optional): also the row-wise codes [R, C] of x (those of mxfp8_quantize) from
+// the same loads, with the scales in rscales: [R][C / 32] for rstep == 0, else
+// step-major over rstep rows (launch_mxfp8_quantize_step_major's layout; C % 128 == 0);
+// rcodes 8-byte aligned.
 moe_status launch_mxfp8_colwise(const void* x_bf16, int64_t R, int C, int E, const int32_t* offsets, int pad,
                                 int64_t kcap, uint8_t* codes, uint8_t* scales, int32_t* kofs, hipStream_t s,
-                                bool step_major = false);
+                                bool step_major = false, uint8_t* rcodes = nullptr, uint8_t* rscales = nullptr,
+                                int64_t rstep = 0);
+// the same for n tensors of one shape (host arrays of device pointers), as few launches
+// as possible; kofs, when not NULL, is written once (it depends only on offsets)
+moe_status launch_mxfp8_colwise_multi(int n, const void* const* x_bf16, int64_t R, int C, int E,
+                                      const int32_t* offsets, int pad, int64_t kcap, uint8_t* const* codes,
+                                      uint8_t* const* scales, int32_t* kofs, hipStream_t s, bool step_major,
+                                      uint8_t* const* rcodes = nullptr, uint8_t* const* rscales = nullptr,
+                                      int64_t rstep = 0);
 
 // per-tensor FP8 (one float32 scale per tensor). A tensor's word holds the float bits
 // of its amax between fp8t_amax and fp8t_finalize (cleared first by fp8t_zero), and

@@ -137,15 +137,32 @@ moe_status launch_mx_scales_step_major(const uint8_t* const* src, uint8_t* const
 // expert read as zeros) into an LDS tile; lane (q, c) then owns block q of column c:
 // its maximum, scale byte and 32 codes, stored as two 16-byte stores, so the four
 // blocks of a column leave as one whole 128-byte line of the output row.
-__global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint16_t* __restrict__ x, int64_t R,
-                                                                     int C, int E, const int32_t* __restrict__ offsets,
-                                                                     int pad, int64_t kcap, uint8_t* __restrict__ codes,
-                                                                     uint8_t* __restrict__ scales,
-                                                                     int32_t* __restrict__ kofs_out, int step_major) {
+// Several tensors of one shape go through one launch (blockIdx.y indexes the table).
+// A tensor with row-wise outputs also gets the quantisation along its rows from the
+// same loads: the 8 values a lane holds are a quarter of a 32-value row block, so four
+// lanes reduce the block maximum with two xor-shuffles, as the row-wise quantiser does.
+constexpr int kColTab = 16;  // tensors per launch
+struct MxColTab {
+  const uint16_t* x[kColTab];
+  uint8_t* codes[kColTab];
+  uint8_t* scales[kColTab];
+  uint2* rcodes[kColTab];     // NULL, or the row-wise codes [R, C] of the same tensor
+  uint8_t* rscales[kColTab];  // its row-wise scales (layout chosen by rstep)
+};
+
+__global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const MxColTab tab, int64_t R, int C, int E,
+                                                                     const int32_t* __restrict__ offsets, int pad,
+                                                                     int64_t kcap, int32_t* __restrict__ kofs_out,
+                                                                     int step_major, int64_t rstep) {
   __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int32_t s_kofs[MOE_MAX_EXPERTS + 1];
   __shared__ int32_t s_item[MOE_MAX_EXPERTS + 1];
   __shared__ float tile[128][65];
+  const uint16_t* __restrict__ x = tab.x[blockIdx.y];
+  uint8_t* __restrict__ codes = tab.codes[blockIdx.y];
+  uint8_t* __restrict__ scales = tab.scales[blockIdx.y];
+  uint2* __restrict__ rcodes = tab.rcodes[blockIdx.y];
+  uint8_t* __restrict__ rscales = tab.rscales[blockIdx.y];
   const int tid = threadIdx.x;
   const int ncb = C / 64;
   if (tid == 0) {  // offsets made nondecreasing inside [0, R] (none: one expert of R rows); padded offsets
@@ -169,7 +186,7 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
     s_item[E] = iacc;
   }
   __syncthreads();
-  if (blockIdx.x == 0 && kofs_out)
+  if (blockIdx.x == 0 && blockIdx.y == 0 && kofs_out)
     for (int e = tid; e <= E; e += 256) kofs_out[e] = s_kofs[e];
   const int total = s_item[E];
   const int r = tid >> 3, c8 = (tid & 7) * 8;  // load: rows r + 32i, columns c8 .. c8 + 7
@@ -186,10 +203,9 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
     j = local / ncb;
     cb = local - j * ncb;
   };
-  // an item's rows in registers (rows past the expert as zeros): the next item's loads
-  // are in flight while the current one is encoded
-  uint4 v[4];
-  auto fetch = [&](int item) {
+  // an item's rows in registers (rows past the expert as zeros). Two register sets: the
+  // loads of the next two items are in flight while the current one is encoded
+  auto fetch = [&](uint4 (&v)[4], int item) {
     int e, j, cb;
     locate(item, e, j, cb);
     const int64_t row0 = (int64_t)s_off[e] + 128 * j;
@@ -200,8 +216,8 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
       if (row < s_off[e + 1]) v[i] = *reinterpret_cast<const uint4*>(x + row * C + cb * 64 + c8);
     }
   };
-  if ((int)blockIdx.x < total) fetch(blockIdx.x);
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  // encode item from v, then refill v with item `next` (if any)
+  auto encode = [&](uint4 (&v)[4], int item, int next) {
     int e, j, cb;
     locate(item, e, j, cb);
     const int nblk = (s_kofs[e + 1] - s_kofs[e]) / 32;        // blocks in the expert's padded range
@@ -209,14 +225,37 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      float f[8];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        tile[r + 32 * i][c8 + 2 * h] = bf16_to_f32(w[h] & 0xFFFFu);
-        tile[r + 32 * i][c8 + 2 * h + 1] = bf16_to_f32(w[h] >> 16);
+        f[2 * h] = bf16_to_f32(w[h] & 0xFFFFu);
+        f[2 * h + 1] = bf16_to_f32(w[h] >> 16);
+        tile[r + 32 * i][c8 + 2 * h] = f[2 * h];
+        tile[r + 32 * i][c8 + 2 * h + 1] = f[2 * h + 1];
+      }
+      if (rcodes) {  // uniform over the launch's tensor: every lane reaches the shuffles
+        float amax = 0.f;
+#pragma unroll
+        for (int h = 0; h < 8; ++h) amax = fmaxf(amax, fabsf(f[h]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        const int sr = mx_scale_exponent(amax);
+        const int64_t row = (int64_t)s_off[e] + 128 * j + r + 32 * i;
+        if (row < s_off[e + 1]) {
+          const int64_t col = (int64_t)cb * 64 + c8;
+          rcodes[(row * C + col) >> 3] =
+              make_uint2(e4m3_pack4(ldexpf(f[0], -sr), ldexpf(f[1], -sr), ldexpf(f[2], -sr), ldexpf(f[3], -sr)),
+                         e4m3_pack4(ldexpf(f[4], -sr), ldexpf(f[5], -sr), ldexpf(f[6], -sr), ldexpf(f[7], -sr)));
+          if ((tid & 3) == 0) {
+            const int64_t b = col >> 5;  // block of the row
+            const int64_t at = rstep ? ((b >> 2) * rstep + row) * 4 + (b & 3) : row * (C / 32) + b;
+            rscales[at] = (uint8_t)(sr + 127);
+          }
+        }
       }
     }
     __syncthreads();
-    if (item + (int)gridDim.x < total) fetch(item + gridDim.x);
+    if (next < total) fetch(v, next);
     if (q < blocks) {
       float amax = 0.f;
 #pragma unroll
@@ -238,6 +277,18 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
       scales[at] = (uint8_t)(sx + 127);
     }
     __syncthreads();  // the tile is reused by the next item
+  };
+  // a workgroup takes items in pairs (2p, 2p + 1): neighbouring 64-column blocks, whose
+  // row-wise codes are the two halves of the same 128-byte lines, leave through one L2
+  const int G = gridDim.x;
+  const int npairs = (total + 1) / 2;
+  uint4 va[4], vb[4];
+  int p = blockIdx.x;
+  if (2 * p < total) fetch(va, 2 * p);
+  if (2 * p + 1 < total) fetch(vb, 2 * p + 1);
+  for (; p < npairs; p += G) {  // block-uniform trip count and branches
+    encode(va, 2 * p, 2 * (p + G));
+    if (2 * p + 1 < total) encode(vb, 2 * p + 1, 2 * (p + G) + 1);
   }
 }
 
@@ -245,17 +296,45 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_colwise_kernel(const uint1
 
 using namespace moe;
 
-moe_status moe::launch_mxfp8_colwise(const void* x_bf16, int64_t R, int C, int E, const int32_t* offsets, int pad,
-                                int64_t kcap, uint8_t* codes, uint8_t* scales, int32_t* kofs, hipStream_t s,
-                                bool step_major) {
+moe_status moe::launch_mxfp8_colwise_multi(int n, const void* const* x_bf16, int64_t R, int C, int E,
+                                           const int32_t* offsets, int pad, int64_t kcap, uint8_t* const* codes,
+                                           uint8_t* const* scales, int32_t* kofs, hipStream_t s, bool step_major,
+                                           uint8_t* const* rcodes, uint8_t* const* rscales, int64_t rstep) {
   if (step_major && kcap % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "mxfp8 step-major scales need kcap % 128 == 0");
+  if (rcodes && rstep && C % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "mxfp8 step-major scales need cols % 128 == 0");
+  if (n < 1) return MOE_OK;
   const int64_t items = (kcap / 32 + 3 * E) / 4 * (C / 64) + E * (C / 64);
-  int64_t grid = (int64_t)num_cus() * 32;  // ~4 resident per CU (33 KB of LDS each), the rest balance the tail
-  if (items < grid) grid = items;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(mxfp8_quantize_colwise_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const uint16_t*)x_bf16,
-                     R, C, E, offsets, pad, kcap, codes, scales, kofs, (int)step_major);
-  return check_launch("mxfp8_quantize_colwise");
+  const int64_t pairs = (items + 1) / 2;
+  for (int t0 = 0; t0 < n; t0 += kColTab) {
+    const int cnt = n - t0 < kColTab ? n - t0 : kColTab;
+    MxColTab tab = {};
+    for (int t = 0; t < cnt; ++t) {
+      tab.x[t] = (const uint16_t*)x_bf16[t0 + t];
+      tab.codes[t] = codes[t0 + t];
+      tab.scales[t] = scales[t0 + t];
+      tab.rcodes[t] = rcodes ? (uint2*)rcodes[t0 + t] : nullptr;
+      tab.rscales[t] = rcodes ? rscales[t0 + t] : nullptr;
+    }
+    // ~4 resident per CU (33 KB of LDS each), the rest balance the tail
+    int64_t grid = (int64_t)num_cus() * 32 / cnt;
+    if (grid < 4) grid = 4;
+    if (pairs < grid) grid = pairs;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(mxfp8_quantize_colwise_kernel, dim3((unsigned)grid, (unsigned)cnt), dim3(256), 0, s, tab, R,
+                       C, E, offsets, pad, kcap, t0 == 0 ? kofs : nullptr, (int)step_major, rstep);
+    moe_status st = check_launch("mxfp8_quantize_colwise");
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+moe_status moe::launch_mxfp8_colwise(const void* x_bf16, int64_t R, int C, int E, const int32_t* offsets, int pad,
+                                     int64_t kcap, uint8_t* codes, uint8_t* scales, int32_t* kofs, hipStream_t s,
+                                     bool step_major, uint8_t* rcodes, uint8_t* rscales, int64_t rstep) {
+  uint8_t* const rc[1] = {rcodes};
+  uint8_t* const rs[1] = {rscales};
+  return launch_mxfp8_colwise_multi(1, &x_bf16, R, C, E, offsets, pad, kcap, &codes, &scales, kofs, s, step_major,
+                                    rcodes ? rc : nullptr, rcodes ? rs : nullptr, rstep);
 }
 
 extern "C" moe_status mxfp8_quantize_colwise(const void* x_bf16, int64_t R, int64_t C, int E, const int32_t* offsets,
@@ -289,6 +368,31 @@ extern "C" moe_status mxfp8_pack_weight_bwd(const void* w_bf16, int64_t rows, in
   uint8_t* codes = reinterpret_cast<uint8_t*>(packed);
   return launch_mxfp8_colwise(w_bf16, rows, (int)cols, 1, nullptr, 32, rows, codes, codes + rows * cols, nullptr,
                               as_stream(stream), true);
+}
+
+extern "C" moe_status mxfp8_quantize_weights(int n, const void* const* w_bf16, int64_t rows, int64_t cols,
+                                             uint8_t* const* e4m3, uint8_t* const* e8m0, void* const* packed,
+                                             void* stream) {
+  if (n < 1 || n > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_weights: n out of [1, 256]");
+  if (rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_weights: negative size");
+  if (rows % 128 != 0 || cols % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "mxfp8_quantize_weights: needs rows % 128 == 0 and cols % 64 == 0");
+  if (rows > 0x7FFFFFFF || rows * cols > 0x7FFFFFFFLL)
+    return fail(MOE_ERR_UNSUPPORTED, "mxfp8_quantize_weights: weight exceeds 2^31 elements");
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!w_bf16 || !e4m3 || !e8m0 || !packed) return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_weights: NULL table");
+  uint8_t* codes[MOE_MAX_EXPERTS];
+  uint8_t* scales[MOE_MAX_EXPERTS];
+  for (int i = 0; i < n; ++i) {
+    if (!w_bf16[i] || !e4m3[i] || !e8m0[i] || !packed[i])
+      return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_weights: NULL pointer");
+    if (!aligned(w_bf16[i], 16) || !aligned(packed[i], 16) || !aligned(e4m3[i], 8))
+      return fail(MOE_ERR_INVALID_ARG, "mxfp8_quantize_weights: w and packed must be 16-byte, e4m3 8-byte aligned");
+    codes[i] = reinterpret_cast<uint8_t*>(packed[i]);
+    scales[i] = codes[i] + rows * cols;
+  }
+  return launch_mxfp8_colwise_multi(n, w_bf16, rows, (int)cols, 1, nullptr, 32, rows, codes, scales, nullptr,
+                                    as_stream(stream), true, e4m3, e8m0, 0);
 }
 
 extern "C" moe_status mxfp8_quantize(const void* in_bf16, int64_t rows, int64_t cols, uint8_t* e4m3,

@@ -281,6 +281,44 @@ moe_status fp8_tensor_quantize_colwise(const void* x_bf16, int64_t R, int64_t C,
  */
 moe_status fp8_tensor_pack_weight_bwd(const void* w_bf16, int64_t rows, int64_t cols, void* packed, void* stream);
 
+/*
+ * MXFP8 quantisation of n bf16 weights of one shape into both layouts a training step
+ * takes, from one read of each weight. Source: Challenge 2 (32-value blocks) and
+ * Challenge 3 (quantisation as separate ops is the overhead the fused recipe removes: a
+ * step that updates its bf16 master weights needs the forward's and the backward's
+ * operand once per step, and one pass over each weight makes both).
+ * For weight i (w_bf16, e4m3, e8m0, packed: host arrays of n device pointers):
+ *   w_bf16[i] [rows, cols] bf16 (16-byte aligned)
+ *   e4m3[i] [rows, cols] uint8 (out, 8-byte aligned), e8m0[i] [rows, cols/32] uint8 (out):
+ *     byte for byte the output of mxfp8_quantize on w_bf16[i] (the forward's operand,
+ *     moe_grouped_mlp_fwd with wt = MXFP8)
+ *   packed[i] (out, 16-byte aligned, rows * cols * 33 / 32 bytes): byte for byte the
+ *     output of mxfp8_pack_weight_bwd on w_bf16[i] (the backward's operand)
+ * Limits: 1 <= n <= MOE_MAX_EXPERTS and those of mxfp8_pack_weight_bwd (rows % 128 == 0,
+ * cols % 64 == 0, rows * cols < 2^31). rows == 0 or cols == 0 is a no-op.
+ */
+moe_status mxfp8_quantize_weights(int n, const void* const* w_bf16, int64_t rows, int64_t cols, uint8_t* const* e4m3,
+                                  uint8_t* const* e8m0, void* const* packed, void* stream);
+
+/*
+ * Per-tensor FP8 quantisation of n bf16 weights of one shape into both layouts a
+ * training step takes: one pass for the maxima, one that writes both codes. Source:
+ * Challenge 2 (FP8: one scaling factor for a whole tensor) and Challenge 3 (quantisation
+ * as separate ops is the overhead the fused recipe removes).
+ * For weight i (w_bf16, e4m3, packed: host arrays of n device pointers):
+ *   w_bf16[i] [rows, cols] bf16 (16-byte aligned)
+ *   e4m3[i] [rows, cols] uint8 (out, 8-byte aligned) and scale[i] (scale: a device array
+ *     of n float32, out, 4-byte aligned): the codes and factor of fp8_tensor_quantize on
+ *     w_bf16[i] (the forward's operand, moe_grouped_mlp_fwd with wt = FP8)
+ *   packed[i] (out, 16-byte aligned, rows * cols + 4 bytes): byte for byte the output
+ *     of fp8_tensor_pack_weight_bwd on w_bf16[i] (the backward's operand)
+ * scale also holds the maxima while the call's kernels run. Limits: 1 <= n <=
+ * MOE_MAX_EXPERTS, rows % 32 == 0, cols % 64 == 0, rows * cols < 2^31. rows == 0 or
+ * cols == 0 writes only the factors (1, the factor of an empty tensor).
+ */
+moe_status fp8_tensor_quantize_weights(int n, const void* const* w_bf16, int64_t rows, int64_t cols,
+                                       uint8_t* const* e4m3, float* scale, void* const* packed, void* stream);
+
 /* Description of one grouped MLP layer (the experts' shapes and precisions). */
 typedef struct {
   int E;             /* experts, 1..MOE_MAX_EXPERTS */

@@ -188,3 +188,32 @@ def test_pack_weight_argument_checks(L):
     assert f(None, 128, 64, dummy, None) == _lib.MOE_ERR_INVALID_ARG
     assert f(dummy, 128, 64, ctypes.c_void_p(264), None) == _lib.MOE_ERR_INVALID_ARG  # packed misaligned
     assert f(None, 0, 64, None, None) == 0                               # empty: no-op
+
+
+def test_weight_quantisers_argument_checks(L):
+    """mxfp8_quantize_weights / fp8_tensor_quantize_weights reject bad counts, shapes,
+    NULL tables and entries, and misaligned pointers before any GPU work."""
+    from grouped_expert_gemm_amd import _lib
+    d = ctypes.c_void_p(256)
+    one = _lib.ptr_table([256])[0]
+    odd = _lib.ptr_table([264])[0]
+    nul = _lib.ptr_table([None])[0]
+    INV, UNS = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED
+    m = L.mxfp8_quantize_weights
+    assert m(0, one, 128, 64, one, one, one, None) == INV          # n < 1
+    assert m(257, one, 128, 64, one, one, one, None) == INV        # n > 256
+    assert m(1, one, 100, 64, one, one, one, None) == UNS          # rows % 128
+    assert m(1, one, 128, 96, one, one, one, None) == UNS          # cols % 64
+    assert m(1, None, 128, 64, one, one, one, None) == INV         # NULL table
+    assert m(1, nul, 128, 64, one, one, one, None) == INV          # NULL entry
+    assert m(1, one, 128, 64, one, one, odd, None) == INV          # packed misaligned
+    assert m(1, None, 0, 64, None, None, None, None) == 0          # empty: no-op
+    f = L.fp8_tensor_quantize_weights
+    assert f(0, one, 32, 64, one, d, one, None) == INV             # n < 1
+    assert f(1, one, 48, 64, one, d, one, None) == UNS             # rows % 32
+    assert f(1, one, 32, 96, one, d, one, None) == UNS             # cols % 64
+    assert f(1, one, 32, 64, one, None, one, None) == INV          # NULL scale
+    assert f(1, one, 32, 64, one, ctypes.c_void_p(258), one, None) == INV   # scale misaligned
+    assert f(1, None, 32, 64, one, d, one, None) == INV            # NULL table
+    assert f(1, one, 32, 64, nul, d, one, None) == INV             # NULL entry
+    assert f(1, one, 32, 64, _lib.ptr_table([260])[0], d, one, None) == INV   # codes not 8-byte aligned

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from conftest import max_rel_err
-from moe_inputs import WORKLOADS, bf16_bits_to_f32, make_inputs, scaled
+from moe_inputs import WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs, scaled
 
 pytestmark = pytest.mark.gpu
 
@@ -55,6 +55,32 @@ def test_quantize_zero_and_empty(moe):
     codes, scale = moe.fp8_tensor_quantize(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"))
     torch.cuda.synchronize()
     assert scale.item() == 1.0 and codes.numel() == 0
+
+
+def test_quantize_keeps_sign_of_zero(moe):
+    """-0 inputs get code 0x80 (the E4M3 code of the quotient -0 / s, sign kept) in every
+    per-tensor FP8 quantiser: by rows, along the token axis and in the weight packs; also
+    in a tensor that is all -0 (factor 1)."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((64, 128)).astype(np.float32)
+    x[::3, ::5] = -0.0
+    x[5] = -0.0
+    bits = f32_to_bf16_bits(x)
+    rc, rs = oracle.fp8_tensor_quantize(bf16_bits_to_f32(bits))
+    assert (rc[5] == 0x80).all()
+    xd = dev_bf16(bits)
+    codes, scale = moe.fp8_tensor_quantize(xd)
+    packed = moe.fp8_tensor_pack_weight_bwd(xd)
+    off = torch.tensor([0, 64], dtype=torch.int32, device="cuda")
+    tcodes, tscale, _ = moe.fp8_tensor_quantize_colwise(xd, off, 32)
+    neg = dev_bf16(f32_to_bf16_bits(np.full((32, 64), -0.0, np.float32)))
+    ncodes, nscale = moe.fp8_tensor_quantize(neg)
+    torch.cuda.synchronize()
+    assert scale.item() == rs and tscale.item() == rs
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(packed.cpu().numpy()[:64 * 128].reshape(128, 64), rc.T)
+    assert np.array_equal(tcodes.cpu().numpy()[:, :64], rc.T)
+    assert nscale.item() == 1.0 and (ncodes.cpu().numpy() == 0x80).all()
 
 
 SHAPES = [
