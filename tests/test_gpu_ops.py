@@ -272,6 +272,7 @@ COLWISE = [
     # name, expert sizes, C, pad
     ("ragged_idle", [37, 0, 100, 1, 162], 128, 32),
     ("gemm_pad", [300, 5, 0, 257], 64, 256),
+    ("odd_blocks", [130, 0, 260, 7], 192, 32),   # three 64-column blocks: item pairs straddle row groups
     ("mixtral_bwd_dY", None, 4096, 256),   # the T=4096 backward's dY: 8192 rows, 8 experts
 ]
 

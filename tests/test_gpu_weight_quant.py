@@ -47,8 +47,9 @@ def _weights(n, rows, cols, seed):
     return _bits(w)
 
 
-# (n, rows, cols): one weight; several; more than one tensor table (16 per launch)
-MX_CASES = [(1, 128, 64), (3, 512, 384), (17, 256, 128)]
+# (n, rows, cols): one weight; several; more than one tensor table (16 per launch); an
+# odd number of 64-column blocks (a workgroup's item pairs straddle row groups)
+MX_CASES = [(1, 128, 64), (3, 512, 384), (17, 256, 128), (2, 384, 192)]
 
 
 @pytest.mark.parametrize("n,rows,cols", MX_CASES)
@@ -75,8 +76,9 @@ def test_mxfp8_quantize_weights_bits(moe, n, rows, cols):
         assert torch.equal(moe.mxfp8_pack_weight_bwd(w[i]), packed[i])
 
 
-# (n, rows, cols): one weight; several; more than one tensor table (64 per launch)
-FP8_CASES = [(1, 32, 64), (3, 512, 384), (65, 64, 128)]
+# (n, rows, cols): one weight; several; more than one tensor table (64 per launch); an
+# odd number of 64-column blocks
+FP8_CASES = [(1, 32, 64), (3, 512, 384), (65, 64, 128), (2, 96, 192)]
 
 
 @pytest.mark.parametrize("n,rows,cols", FP8_CASES)
