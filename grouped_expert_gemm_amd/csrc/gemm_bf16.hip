@@ -33,9 +33,9 @@
 //   MNCONTIG tiles are 32 rows of 512 bytes with their own chunk swizzle (mnswz).
 // Scheduling: one workgroup per CU loops over tiles (persistent); tile ids are
 //   remapped so that each XCD (workgroup id mod 8) works on a contiguous run of
-//   tiles. Inside an expert, tiles run m-fastest, so a run covers a few weight
-//   panels and all of the expert's token panels, and concurrent runs share them
-//   through L2 and the Infinity Cache.
+//   tiles. Inside an expert, row (m) tiles run fastest within groups of at most 16
+//   (tile_in_expert), so a run covers a few weight panels and a few token panels, and
+//   concurrent runs share them through L2 and the Infinity Cache.
 #include <type_traits>
 
 #include "common.h"
@@ -152,8 +152,7 @@ void grouped_gemm_kernel(const Params prm) {
       const int me = s_off[e + 1] - s_off[e];
       const int mte = (me + kBM - 1) / kBM;
       const int local = t - s_tstart[e];
-      mt = local % mte;
-      nt = local / mte;
+      tile_in_expert(local, mte, prm.n_tiles, mt, nt);
     } else {
       const int mtiles = prm.M / kBM;
       const int per = mtiles * prm.n_tiles;

@@ -72,6 +72,24 @@ __device__ __forceinline__ int lane_number() {
   return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, base));
 }
 
+// Order of one expert's mte x ntiles tiles (row tiles by column tiles): the row tiles
+// form groups of at most kMaxGroupRows (equal sizes but the last), row tiles fastest
+// inside a group. Consecutive tiles (an XCD's concurrent run) then cover a few row
+// panels and a few column panels of the expert and share both through its L2; with row
+// tiles fastest over a long expert, every tile of a run would bring its own row panel
+// and the row operand would be fetched once per column tile. A bijection of
+// [0, mte * ntiles) onto the tiles for every group size.
+constexpr int kMaxGroupRows = 16;
+__device__ __forceinline__ void tile_in_expert(int local, int mte, int ntiles, int& mt, int& nt) {
+  const int ng = (mte + kMaxGroupRows - 1) / kMaxGroupRows;
+  const int g = (mte + ng - 1) / ng;
+  const int grp = local / (g * ntiles);
+  const int rem = local - grp * g * ntiles;
+  const int gm = mte - grp * g < g ? mte - grp * g : g;
+  mt = grp * g + rem % gm;
+  nt = rem / gm;
+}
+
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
   __atomic_signal_fence(__ATOMIC_SEQ_CST);

@@ -69,7 +69,7 @@ void grouped_gemm_fwd_kernel(const Params prm) {
   };
 
   // Tile order: expert-major, ceil(rows_e / 256) row tiles x n_tiles per expert, row
-  // tiles fastest. A workgroup's tiles only move forward, so it walks the expert
+  // tiles fastest within groups of at most 16 (tile_in_expert). A workgroup's tiles only move forward, so it walks the expert
   // offsets once (wavefront-uniform loads), making them a nondecreasing sequence inside
   // [0, R] on the way: no access leaves the tensors.
   auto clamp_off = [&](int v, int prev) -> int {
@@ -155,8 +155,7 @@ void grouped_gemm_fwd_kernel(const Params prm) {
     {
       const int local = t - ts_w;
       const int mte = (oe - ob + kBM - 1) / kBM;
-      mt = local % mte;
-      nt = local / mte;
+      tile_in_expert(local, mte, prm.n_tiles, mt, nt);
     }
     e = __builtin_amdgcn_readfirstlane(e);
     mt = __builtin_amdgcn_readfirstlane(mt);

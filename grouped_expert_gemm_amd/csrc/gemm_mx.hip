@@ -146,8 +146,8 @@ void grouped_gemm_mx_kernel(const MxParams prm) {
     const int me = s_off[e + 1] - s_off[e];
     const int mte = (me + kBM - 1) / kBM;
     const int local = t - s_tstart[e];
-    int mt = local % mte;
-    int nt = local / mte;
+    int mt, nt;
+    tile_in_expert(local, mte, prm.n_tiles, mt, nt);
     e = __builtin_amdgcn_readfirstlane(e);
     mt = __builtin_amdgcn_readfirstlane(mt);
     nt = __builtin_amdgcn_readfirstlane(nt);
@@ -488,8 +488,9 @@ void grouped_gemm_fp8t_kernel(const Params prm) {
   };
 
   // Tiles: expert-major, ceil(rows_e / 256) row tiles x n_tiles per expert, row tiles
-  // fastest. Expert offsets are walked once with wavefront-uniform loads and made a
-  // nondecreasing sequence inside [0, R] on the way.
+  // fastest within groups of at most 16 (tile_in_expert). Expert offsets are walked
+  // once with wavefront-uniform loads and made a nondecreasing sequence inside [0, R]
+  // on the way.
   auto clamp_off = [&](int v, int prev) -> int {
     v = v < prev ? prev : v;
     return v > R ? R : v;
@@ -562,8 +563,7 @@ void grouped_gemm_fp8t_kernel(const Params prm) {
       e = e_w;
       const int local = t - ts_w;
       const int mte = (oe - ob + kBM - 1) / kBM;
-      mt = local % mte;
-      nt = local / mte;
+      tile_in_expert(local, mte, prm.n_tiles, mt, nt);
       nk = K / kXBK;
     }
     const int pad = (5 - nk % 5) % 5;  // zero steps ahead of the K loop (as in the MXFP8 kernel below)
@@ -874,8 +874,9 @@ void grouped_gemm_mxw_kernel(const Params prm) {
   };
 
   // Tiles: expert-major, ceil(rows_e / 256) row tiles x n_tiles per expert, row tiles
-  // fastest. Expert offsets are walked once with wavefront-uniform loads and made a
-  // nondecreasing sequence inside [0, R] on the way.
+  // fastest within groups of at most 16 (tile_in_expert). Expert offsets are walked
+  // once with wavefront-uniform loads and made a nondecreasing sequence inside [0, R]
+  // on the way.
   auto clamp_off = [&](int v, int prev) -> int {
     v = v < prev ? prev : v;
     return v > R ? R : v;
@@ -946,8 +947,7 @@ void grouped_gemm_mxw_kernel(const Params prm) {
       e = e_w;
       const int local = t - ts_w;
       const int mte = (oe - ob + kBM - 1) / kBM;
-      mt = local % mte;
-      nt = local / mte;
+      tile_in_expert(local, mte, prm.n_tiles, mt, nt);
       nk = K / kXBK;
       pad = (5 - nk % 5) % 5;
     }
