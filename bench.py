@@ -123,9 +123,10 @@ class Layer:
                 w1t, k9 = t([self.w1[e] for e in range(E)])
                 w2t, k10 = t([self.w2[e] for e in range(E)])
                 self._k9 = (k9, k10)
-                if fp8:
-                    self.wq_step = [(self.L.fp8_tensor_quantize_weights, E, w1t, 2 * I, H, self.t1, qs1, self.b1),
-                                    (self.L.fp8_tensor_quantize_weights, E, w2t, H, I, self.t2, qs2, self.b2)]
+                if fp8:  # the factors: one float32 array per weight tensor
+                    f1, f2 = ctypes.c_void_p(qs1.data_ptr()), ctypes.c_void_p(qs2.data_ptr())
+                    self.wq_step = [(self.L.fp8_tensor_quantize_weights, E, w1t, 2 * I, H, self.t1, f1, self.b1),
+                                    (self.L.fp8_tensor_quantize_weights, E, w2t, H, I, self.t2, f2, self.b2)]
                 else:
                     self.wq_step = [(self.L.mxfp8_quantize_weights, E, w1t, 2 * I, H, self.t1, self.fs1, self.b1),
                                     (self.L.mxfp8_quantize_weights, E, w2t, H, I, self.t2, self.fs2, self.b2)]
@@ -181,9 +182,8 @@ class Layer:
                                    None, p(self.prob_perm), p(self.split), p(self.offsets), p(self.rmap),
                                    p(self.src), p(self.ws_perm), self.ws_perm.numel(), s))
         if self.wq_step:  # bf16 master weights -> both layouts, every step
-            for fn, n, src, rows, cols, codes, scales, packed in self.wq_step:
-                sc = ctypes.c_void_p(scales.data_ptr()) if hasattr(scales, "data_ptr") else scales
-                c("weight quantisation", fn(n, src, rows, cols, codes, sc, packed, s))
+            for fn, *args in self.wq_step:
+                c("weight quantisation", fn(*args, s))
         if self.mx:
             c("mlp fwd", L.moe_grouped_mlp_fwd(ctypes.byref(self.desc_fwd), R, p(self.x_perm), None, self.t1, self.t2,
                                                self.fs1, self.fs2, p(self.offsets), p(self.prob_perm), p(self.y),
