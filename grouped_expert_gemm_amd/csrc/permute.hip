@@ -465,6 +465,7 @@ extern "C" moe_status moe_unpermute_combine(const void* y_perm, moe_dtype dt, co
   if (T < 0 || H < 1 || k < 1) return fail(MOE_ERR_INVALID_ARG, "moe_unpermute_combine: bad T/H/k");
   if (dt != MOE_F32 && dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "moe_unpermute_combine: dtype must be F32 or BF16");
   if (T == 0) return MOE_OK;
+  if ((T + 3) / 4 > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "moe_unpermute_combine: T too large");
   if (!y_perm || !row_id_map || !out) return fail(MOE_ERR_INVALID_ARG, "moe_unpermute_combine: NULL pointer");
   const hipStream_t s = as_stream(stream);
   const int64_t blocks = (T + 3) / 4;

@@ -56,6 +56,8 @@ def test_argument_errors_before_launch(L):
     assert b"NULL" in L.moe_last_error()
     assert L.mxfp8_quantize(None, 4, 33, None, None, None) == INV              # cols % 32
     assert L.moe_unpermute_combine(None, 2, None, None, 4, 8, 2, None, None) == UNS  # MXFP8 rows
+    assert L.moe_unpermute_combine(None, 1, None, None, 1 << 34, 8, 2, None, None) == UNS  # grid past 2^31 blocks
+    assert L.moe_unpermute_combine(None, 1, None, None, 4, 8, 2, None, None) == INV  # NULL
     # permute: undersized workspace is reported before any launch
     dummy = ctypes.c_void_p(256)
     assert L.moe_permute(dummy, None, 1, 1000, 64, 8, 2, dummy, dummy, 0, dummy, None, dummy, dummy, dummy,
