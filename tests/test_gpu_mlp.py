@@ -133,6 +133,49 @@ def test_tiny_layer_f32_forward_and_backward(moe):
     assert max_rel_err(dprob.cpu().numpy(), g["drouting_weights"]) <= F32_TOL
 
 
+# (T, H, I, E, k): H and I off the 32 and 64 grids of the float32 tiles (64 x 64, K in
+# steps of 32), experts spanning several 64-row tiles with ragged ends, the last
+# expert idle
+F32_RAGGED = [(300, 100, 72, 5, 2), (400, 33, 130, 3, 1)]
+
+
+@pytest.mark.parametrize("T,H,I,E,k", F32_RAGGED)
+def test_f32_ragged_shapes(moe, T, H, I, E, k):
+    """The float32 grouped GEMMs at sizes that are not multiples of their tiles: the
+    MLP forward and backward, the grouped linear and the fused gate_up, against the
+    oracle."""
+    w = scaled(WORKLOADS["tiny"], T=T, H=H, I=I, E=E, k=k, seed=T + H + I)
+    inp = make_inputs(w)
+    inp.logits[:, E - 1] -= 100.0
+    idx, p, m, pp = oracle_perm(inp, k, E)
+    assert m["split_sizes"][E - 1] == 0 and max(m["split_sizes"]) > 128
+    xf = inp.x[m["src_token"]]
+    xp = dev_f32(xf)
+    w1, w2 = dev_f32(inp.w1), dev_f32(inp.w2)
+    off = torch.from_numpy(m["offsets"].astype(np.int32)).cuda()
+    prob = dev_f32(pp)
+    R = T * k
+    dyf = np.random.default_rng(5).standard_normal((R, H)).astype(np.float32)
+    print(f"f32 ragged: T={T} H={H} I={I} E={E} k={k} rows per expert {m['split_sizes'].tolist()}", flush=True)
+    y, z, h = moe.moe_grouped_mlp_fwd(xp, w1, w2, off, prob, compute="f32", save_for_bwd=True)
+    dx, dw1, dw2, dprob = moe.moe_grouped_mlp_bwd(dev_f32(dyf), xp, z, h, prob, w1, w2, off, compute="f32")
+    lin = moe.moe_grouped_linear(xp, w1, off)
+    h2, z2 = moe.moe_grouped_gate_up_swiglu(xp, w1, off, prob, save_z=True)
+    torch.cuda.synchronize()
+    ry, rz, rh = oracle.grouped_mlp_forward(xf, inp.w1, inp.w2, m["offsets"], pp)
+    assert max_rel_err(host(y), ry) <= F32_TOL
+    assert max_rel_err(host(z), rz) <= F32_TOL
+    assert max_rel_err(host(h), rh) <= F32_TOL
+    assert np.array_equal(host(h2), host(h)) and np.array_equal(host(z2), host(z))
+    assert max_rel_err(host(lin), oracle.grouped_linear(xf, inp.w1, m["offsets"])) <= F32_TOL
+    ref = oracle.grouped_mlp_backward(dyf, xf, inp.w1, inp.w2, m["offsets"], pp)
+    assert max_rel_err(host(dx), ref["dx_perm"]) <= F32_TOL
+    assert max_rel_err(host(dw1), ref["dw_gate_up"]) <= F32_TOL
+    assert max_rel_err(host(dw2), ref["dw_down"]) <= F32_TOL
+    assert max_rel_err(dprob.cpu().numpy(), ref["dprob_perm"]) <= F32_TOL
+    assert not host(dw1)[E - 1].any() and not host(dw2)[E - 1].any(), "idle expert must get zero weight gradients"
+
+
 def test_layer_bf16_end_to_end(moe):
     """route -> permute -> grouped MLP -> combine in bf16 against the per-expert loop."""
     w = scaled(WORKLOADS["qwen3_fwd"], T=2000, H=512, I=256, E=32, k=4, seed=21)
