@@ -78,9 +78,10 @@ __device__ __forceinline__ int lane_number() {
 // panels and a few column panels of the expert and share both through its L2; with row
 // tiles fastest over a long expert, every tile of a run would bring its own row panel
 // and the row operand would be fetched once per column tile. A bijection of
-// [0, mte * ntiles) onto the tiles for every group size.
+// [0, mte * ntiles) onto the tiles for every group size (also compiled for the host,
+// where a CPU check enumerates it for many expert shapes).
 constexpr int kMaxGroupRows = 16;
-__device__ __forceinline__ void tile_in_expert(int local, int mte, int ntiles, int& mt, int& nt) {
+__host__ __device__ __forceinline__ void tile_in_expert(int local, int mte, int ntiles, int& mt, int& nt) {
   const int ng = (mte + kMaxGroupRows - 1) / kMaxGroupRows;
   const int g = (mte + ng - 1) / ng;
   const int grp = local / (g * ntiles);
