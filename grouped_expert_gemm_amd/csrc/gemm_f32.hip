@@ -11,83 +11,14 @@
 
 #include "common.h"
 #include "gemm_f32.h"
+#include "tile_f32.h"
 
 namespace moe {
 namespace f32 {
 
-constexpr int kT = 64;   // output tile edge
-constexpr int kKS = 32;  // K per LDS stage
-constexpr int kLd = kT + 1;  // LDS row pitch (floats): k-fastest writes fall in distinct banks
+using namespace tf32;
 
 __device__ __forceinline__ float sigmoid(float g) { return 1.f / (1.f + expf(-g)); }
-
-// Strided view of an operand: element (i, k) at p[i * si + k * sk], valid for i < ni,
-// k < nk (zero outside).
-struct View {
-  const float* p;
-  int64_t si, sk;
-  int ni, nk;
-};
-
-// Stage a 64 x 32 block (i0 .. i0+63, k0 .. k0+31) of v into LDS as s[k][i]. Threads
-// run along whichever of i and k is contiguous in memory.
-__device__ __forceinline__ void stage(const View& v, int k0, float* s, int tid) {
-  const bool kfast = v.sk == 1;
-#pragma unroll
-  for (int j = 0; j < (kT * kKS) / 256; ++j) {
-    const int idx = tid + 256 * j;
-    const int i = kfast ? idx / kKS : idx % kT;
-    const int k = kfast ? idx % kKS : idx / kT;
-    float x = 0.f;
-    if (i < v.ni && k0 + k < v.nk) x = v.p[(int64_t)i * v.si + (int64_t)(k0 + k) * v.sk];
-    s[k * kLd + i] = x;
-  }
-}
-
-// acc[b] += A (64 x K) times B_b (K x 64) for NB operands B sharing A; wavefront
-// (wm, wn) holds the 32 x 32 block at rows 32 wm, columns 32 wn, in the matrix-core
-// layout: lane l, register v is row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
-template <int NB>
-__device__ __forceinline__ void tile_product(const View& a, const View (&b)[NB], f32x16 (&acc)[NB], float* sA,
-                                             float* sB, int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int x = 0; x < NB; ++x)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[x][v] = 0.f;
-  for (int k0 = 0; k0 < a.nk; k0 += kKS) {
-    __syncthreads();  // the previous stage's reads are done
-    stage(a, k0, sA, tid);
-#pragma unroll
-    for (int x = 0; x < NB; ++x) stage(b[x], k0, sB + x * kKS * kLd, tid);
-    __syncthreads();
-    // one k pair per instruction: lane l supplies k = kp + l / 32 of row / column l % 32
-#pragma unroll
-    for (int kp = 0; kp < kKS; kp += 2) {
-      const int k = kp + (lane >> 5);
-      const float av = sA[k * kLd + wm * 32 + (lane & 31)];
-#pragma unroll
-      for (int x = 0; x < NB; ++x) {
-        const float bv = sB[x * kKS * kLd + k * kLd + wn * 32 + (lane & 31)];
-        acc[x] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[x], 0, 0, 0);
-      }
-    }
-  }
-}
-
-// Calls f(row, col, v) for this lane's outputs of the tile that fall inside (m, n).
-template <typename F>
-__device__ __forceinline__ void for_outputs(int tid, int m, int n, F&& f) {
-  const int lane = tid & 63, wave = tid >> 6;
-  const int col = (wave & 1) * 32 + (lane & 31);
-  if (col >= n) return;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int row = (wave >> 1) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    if (row < m) f(row, col, v);
-  }
-}
 
 // Row tile `rt` of the experts' row tiles in order (ceil(rows_e / 64) each): its expert,
 // first row and row count, or false past the last. Offsets are read as a nondecreasing
@@ -117,14 +48,14 @@ __global__ __launch_bounds__(256) void grouped_rows(const float* __restrict__ a,
                                                     int64_t sbk, int64_t sbn, const int32_t* __restrict__ off,
                                                     int64_t R, int E, int N, int K, float* __restrict__ y,
                                                     int64_t ldy) {
-  __shared__ float sA[kKS * kLd], sB[kKS * kLd];
+  __shared__ float sA[kStage], sB[kStage];
   int e, rows;
   int64_t r0;
   if (!find_row_tile(off, E, R, blockIdx.x, e, r0, rows)) return;
   const int n0 = blockIdx.y * kT;
   const int tid = threadIdx.x;
-  const View av{a + r0 * lda, lda, 1, rows, K};
-  const View bv[1] = {{reinterpret_cast<const float*>(w.p[e]) + (int64_t)n0 * sbn, sbn, sbk, N - n0, K}};
+  const View<float> av{a + r0 * lda, lda, 1, rows, K};
+  const View<float> bv[1] = {{reinterpret_cast<const float*>(w.p[e]) + (int64_t)n0 * sbn, sbn, sbk, N - n0, K}};
   f32x16 acc[1];
   tile_product<1>(av, bv, acc, sA, sB, tid);
   for_outputs(tid, rows, N - n0, [&](int r, int c, int v) { y[(r0 + r) * ldy + n0 + c] = acc[0][v]; });
@@ -136,15 +67,15 @@ __global__ __launch_bounds__(256) void grouped_gate_up(const float* __restrict__
                                                        const int32_t* __restrict__ off,
                                                        const float* __restrict__ prob, int64_t R, int E, int H,
                                                        int I, float* __restrict__ h, float* __restrict__ z) {
-  __shared__ float sA[kKS * kLd], sB[2 * kKS * kLd];
+  __shared__ float sA[kStage], sB[2 * kStage];
   int e, rows;
   int64_t r0;
   if (!find_row_tile(off, E, R, blockIdx.x, e, r0, rows)) return;
   const int i0 = blockIdx.y * kT;
   const int tid = threadIdx.x;
   const float* W = reinterpret_cast<const float*>(w1.p[e]);
-  const View av{x + r0 * H, H, 1, rows, H};
-  const View bv[2] = {{W + (int64_t)i0 * H, H, 1, I - i0, H}, {W + (int64_t)(I + i0) * H, H, 1, I - i0, H}};
+  const View<float> av{x + r0 * H, H, 1, rows, H};
+  const View<float> bv[2] = {{W + (int64_t)i0 * H, H, 1, I - i0, H}, {W + (int64_t)(I + i0) * H, H, 1, I - i0, H}};
   f32x16 acc[2];
   tile_product<2>(av, bv, acc, sA, sB, tid);
   for_outputs(tid, rows, I - i0, [&](int r, int c, int v) {
@@ -164,7 +95,7 @@ __global__ __launch_bounds__(256) void grouped_wgrad(const float* __restrict__ a
                                                      const float* __restrict__ b, int64_t ldb,
                                                      const int32_t* __restrict__ off, int64_t R, int E, int M, int N,
                                                      PtrTab dw) {
-  __shared__ float sA[kKS * kLd], sB[kKS * kLd];
+  __shared__ float sA[kStage], sB[kStage];
   const int e = blockIdx.z;
   int64_t r0 = 0, r1 = 0;
   for (int x = 0; x <= e; ++x) {  // the same clamped, nondecreasing offsets as the row tiles
@@ -175,8 +106,8 @@ __global__ __launch_bounds__(256) void grouped_wgrad(const float* __restrict__ a
   const int rows = (int)(r1 - r0);
   const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
   const int tid = threadIdx.x;
-  const View av{a + r0 * lda + m0, 1, lda, M - m0, rows};
-  const View bv[1] = {{b + r0 * ldb + n0, 1, ldb, N - n0, rows}};
+  const View<float> av{a + r0 * lda + m0, 1, lda, M - m0, rows};
+  const View<float> bv[1] = {{b + r0 * ldb + n0, 1, ldb, N - n0, rows}};
   f32x16 acc[1];
   tile_product<1>(av, bv, acc, sA, sB, tid);
   float* out = reinterpret_cast<float*>(const_cast<void*>(dw.p[e]));

@@ -90,6 +90,9 @@ ROUTER_BWD = [
     (2500, 128, 128, True),  # three token chunks of the weight gradient
     (1, 64, 3, False),
     (1025, 4096, 8, True),   # Mixtral width, two chunks
+    (333, 264, 72, False),   # 9 expert groups of 8, ragged columns and tokens
+    (70, 8, 64, True),       # one column block of 8
+    (5000, 2048, 128, False),  # the Qwen3 width, several token chunks
 ]
 
 
