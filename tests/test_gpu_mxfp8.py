@@ -86,13 +86,21 @@ def test_mxfp8_prequantised_operands_and_h(moe):
     # Elements that nearly cancel carry a sum error that is large next to themselves but
     # tiny next to their block's maximum, which sets the block's scale: so codes may
     # differ (rarely), and each difference stays within one E4M3 step of the top binade
-    # of its block (2^-3 of the block maximum).
-    assert (g_scales != rhs).mean() < 1e-2
+    # of its block (2^-3 of the block maximum). A block's scale follows its maximum, on
+    # which both sums agree except at a power-of-two boundary. The differences come from
+    # rounding order, so they fall above and below the oracle alike; a systematic
+    # rounding bias would put them all on one side.
     diff = g_codes != rhq
     print(f"  h codes differing: {diff.mean():.2e}, scales differing: {(g_scales != rhs).mean():.2e}")
-    assert diff.mean() < 1e-2
+    assert (g_scales != rhs).mean() <= 1e-3
+    assert diff.mean() <= 5e-3
     gv = oracle.mxfp8_dequantize(g_codes, g_scales)
     rv = oracle.mxfp8_dequantize(rhq, rhs)
+    d = (gv - rv)[diff]
+    if d.size >= 50:
+        above = (d > 0).mean()
+        print(f"  differing codes above the oracle: {above:.2f} of {d.size}")
+        assert 0.3 <= above <= 0.7
     R = gv.shape[0]
     bmax = np.abs(rv).reshape(R, -1, 32).max(axis=2)
     bdiff = np.abs(gv - rv).reshape(R, -1, 32).max(axis=2)
