@@ -122,6 +122,14 @@ int main() {
                                                          nullptr, 0, nullptr), INV);
   }
 
+  {
+    // float32 sizes whose launch grid would not fit: refused before any launch
+    alignas(256) static float f[64];
+    const void* tab[1] = {f};
+    expect("linear f32 grid", moe_grouped_linear(1, 4, 1, 65535 * 64 + 1, MOE_F32, f, tab, (const int32_t*)f, f,
+                                                 nullptr, 0, nullptr), UNS);
+  }
+
   // workspace sizes (pure host arithmetic) and a workspace that is too small
   size_t bytes = 0;
   expect("ws NULL out", moe_workspace_size(MOE_OP_PERMUTE, nullptr, 0, 16, 8, 2, nullptr), INV);

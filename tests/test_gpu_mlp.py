@@ -176,6 +176,33 @@ def test_f32_ragged_shapes(moe, T, H, I, E, k):
     assert not host(dw1)[E - 1].any() and not host(dw2)[E - 1].any(), "idle expert must get zero weight gradients"
 
 
+def test_f32_one_row_tiny_sizes(moe):
+    """The float32 path at its smallest: one routed row, H = 5 and I = 3 (K below one
+    32-wide stage, one partial tile everywhere), the second expert idle."""
+    T, H, I, E, k = 1, 5, 3, 2, 1
+    w = scaled(WORKLOADS["tiny"], T=T, H=H, I=I, E=E, k=k, seed=77)
+    inp = make_inputs(w)
+    inp.logits[:, 1] -= 100.0
+    idx, p, m, pp = oracle_perm(inp, k, E)
+    assert list(m["split_sizes"]) == [1, 0]
+    xf = inp.x[m["src_token"]]
+    xp, w1, w2 = dev_f32(xf), dev_f32(inp.w1), dev_f32(inp.w2)
+    off = torch.from_numpy(m["offsets"].astype(np.int32)).cuda()
+    prob = dev_f32(pp)
+    dyf = np.random.default_rng(6).standard_normal((T * k, H)).astype(np.float32)
+    print("f32 one row: H=5 I=3 E=2", flush=True)
+    y, z, h = moe.moe_grouped_mlp_fwd(xp, w1, w2, off, prob, compute="f32", save_for_bwd=True)
+    dx, dw1, dw2, dprob = moe.moe_grouped_mlp_bwd(dev_f32(dyf), xp, z, h, prob, w1, w2, off, compute="f32")
+    torch.cuda.synchronize()
+    ry, _, rh = oracle.grouped_mlp_forward(xf, inp.w1, inp.w2, m["offsets"], pp)
+    assert max_rel_err(host(y), ry) <= F32_TOL and max_rel_err(host(h), rh) <= F32_TOL
+    ref = oracle.grouped_mlp_backward(dyf, xf, inp.w1, inp.w2, m["offsets"], pp)
+    assert max_rel_err(host(dx), ref["dx_perm"]) <= F32_TOL
+    assert max_rel_err(host(dw1), ref["dw_gate_up"]) <= F32_TOL
+    assert max_rel_err(host(dw2), ref["dw_down"]) <= F32_TOL
+    assert max_rel_err(dprob.cpu().numpy(), ref["dprob_perm"]) <= F32_TOL
+
+
 def test_layer_bf16_end_to_end(moe):
     """route -> permute -> grouped MLP -> combine in bf16 against the per-expert loop."""
     w = scaled(WORKLOADS["qwen3_fwd"], T=2000, H=512, I=256, E=32, k=4, seed=21)
