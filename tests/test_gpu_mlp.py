@@ -50,6 +50,7 @@ FWD_SHAPES = [
     ("skewed", 1200, 256, 128, 16, 4, 1.2, (3, 9)),
     ("one_expert", 300, 256, 256, 1, 1, 0.0, ()),
     ("tiny_groups", 37, 256, 128, 8, 2, 0.0, (0,)),
+    ("max_experts", 300, 256, 256, 256, 2, 0.0, ()),   # E = 256: experts of 0-3 rows, many idle
 ]
 
 
@@ -77,6 +78,7 @@ BWD_SHAPES = [
     # runs several, issuing the next tile's first copies before its stores; skewed
     # expert sizes give both long and short K loops, and idle experts in the chain
     ("many_tiles", 1200, 1024, 1024, 16, 2, 1.2, (4, 11)),
+    ("max_experts", 300, 256, 256, 256, 2, 0.0, ()),   # E = 256, many idle experts
 ]
 
 
