@@ -219,3 +219,21 @@ def test_weight_quantisers_argument_checks(L):
     assert f(1, None, 32, 64, one, d, one, None) == INV            # NULL table
     assert f(1, one, 32, 64, nul, d, one, None) == INV             # NULL entry
     assert f(1, one, 32, 64, _lib.ptr_table([260])[0], d, one, None) == INV   # codes not 8-byte aligned
+
+
+def test_mx_and_fp8_reject_more_than_128_experts(L):
+    """The MXFP8 and per-tensor FP8 kernels take at most 128 experts per call (their
+    pointer tables travel in the kernel arguments): more is refused before any launch."""
+    from grouped_expert_gemm_amd import _lib
+    E = 129
+    D = _lib.MlpDesc
+    ptrs = (ctypes.c_void_p * E)(*([4096] * E))
+    pp = ctypes.cast(ptrs, _lib.PP)
+    p = ctypes.c_void_p(4096)
+    for compute in (_lib.MOE_MXFP8, _lib.MOE_FP8):
+        d = D(E, 256, 256, compute, 1, 1, 0)   # bf16 activations and weights, quantised inside
+        st = L.moe_grouped_mlp_fwd(ctypes.byref(d), 64, p, None, pp, pp, None, None, p, p, p, None, None,
+                                   p, 1 << 40, None)
+        assert st == _lib.MOE_ERR_UNSUPPORTED and b"128" in L.moe_last_error(), (compute, st, L.moe_last_error())
+        st = L.moe_grouped_mlp_bwd(ctypes.byref(d), 64, p, p, p, p, p, pp, pp, p, p, pp, pp, p, p, 1 << 40, None)
+        assert st == _lib.MOE_ERR_UNSUPPORTED and b"128" in L.moe_last_error(), (compute, st, L.moe_last_error())
